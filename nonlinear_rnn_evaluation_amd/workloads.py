@@ -1,0 +1,228 @@
+"""Seeded synthetic inputs shared by the HIP path's tests, the benchmark and the oracle.
+
+This module draws random numbers and rounds them to the storage precision of each
+workload.  It contains none of the method's arithmetic (no cell, no Jacobian, no
+projection, no solve); both the GPU path and the CPU oracle receive the arrays it
+returns.
+
+Recipe (the same for every workload):
+  * one ``numpy.random.default_rng(seed)`` (PCG64) stream, drawn in this order:
+      1. W as a single [G*D, D_in] array,
+      2. the recurrent weights: U as [G*D, D] (dense GRU) or u as [G, D]
+         (diagonal-recurrence cells),
+      3. x as [B, T, D_in];
+  * weights are drawn in float64; x is drawn in float64 when the input precision is
+    fp32/fp64 and with ``standard_normal(dtype=float32)`` when it is bf16;
+  * values are then rounded to the storage precision (fp64, fp32, or bf16 with
+    round-to-nearest-even via torch) -- the oracle reads the rounded values.
+
+Distribution notation: ``N(0, v)`` names the variance v; Glorot-uniform uses one
+limit sqrt(6 / (fan_in + D)) per gate block (fan_in = D_in for W, D for U).
+
+The five named workloads are synthetic stand-ins for the pages' "untrained GRU
+evaluation" timing workload (Towards Scalable and Stable Parallelization of
+Nonlinear RNNs, experimental setup) and for ParaRNN's diagonal-recurrence
+LSTM/GRU adaptations (ParaRNN abstract); no dataset is read.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+# Cell kinds and Jacobian modes use the same integer codes as the C ABI.
+CELL_GRU = 0        # dense recurrent matrix U, gates (r, z, n)
+CELL_GRU_DIAG = 1   # elementwise recurrent weights u, gates (r, z, n)
+CELL_LSTM_DIAG = 2  # elementwise recurrent weights u, gates (i, f, o, g), state (c, h)
+
+JAC_FULL = 0
+JAC_DIAG = 1
+JAC_ZERO = 2
+
+DT_F64 = 0
+DT_F32 = 1
+DT_BF16 = 2
+
+_TORCH_DT = {DT_F64: torch.float64, DT_F32: torch.float32, DT_BF16: torch.bfloat16}
+
+
+def gates_of(cell: int) -> int:
+    return 4 if cell == CELL_LSTM_DIAG else 3
+
+
+def state_size(cell: int, D: int) -> int:
+    return 2 * D if cell == CELL_LSTM_DIAG else D
+
+
+@dataclasses.dataclass
+class Workload:
+    """One synthetic problem: shapes, precisions, solver settings and the draw rule."""
+    name: str
+    cell: int
+    B: int
+    T: int
+    D: int
+    D_in: int
+    x_dtype: int
+    state_dtype: int
+    w_init: str            # "normal" or "glorot"
+    w_var: float = 0.0     # variance for "normal"
+    u_init: str = "same"   # "same" (as W), "uniform1" (U(-1, 1) elementwise)
+    u_scale: float = 1.0   # multiplies the recurrent weights after the draw (stiff variant)
+    forget_bias: float = 0.0
+    jac_modes: tuple = (JAC_FULL,)
+    jac_every: int = 1
+    tol: float = 1e-5
+    max_iters: int = 64
+    seed: int = 0
+
+    @property
+    def G(self) -> int:
+        return gates_of(self.cell)
+
+    @property
+    def S(self) -> int:
+        return state_size(self.cell, self.D)
+
+    def describe(self) -> dict:
+        return {
+            "workload": self.name, "cell": ["gru", "gru_diag", "lstm_diag"][self.cell],
+            "B": self.B, "T": self.T, "D": self.D, "D_in": self.D_in,
+            "x_dtype": ["f64", "f32", "bf16"][self.x_dtype],
+            "state_dtype": ["f64", "f32", "bf16"][self.state_dtype],
+            "jac_modes": [["full", "diag", "zero"][m] for m in self.jac_modes],
+            "jac_every": self.jac_every, "tol": self.tol, "max_iters": self.max_iters,
+        }
+
+
+def named_workloads() -> dict:
+    """The five workloads (plus the stiff variant of the long LSTM one)."""
+    w = {}
+    w["tiny_gru"] = Workload(
+        "tiny_gru", CELL_GRU, B=1, T=64, D=4, D_in=2, x_dtype=DT_F64, state_dtype=DT_F64,
+        w_init="normal", w_var=1.0 / 4, jac_modes=(JAC_FULL, JAC_DIAG), tol=1e-10, max_iters=64)
+    w["gru_quasi"] = Workload(
+        "gru_quasi", CELL_GRU, B=8, T=4096, D=64, D_in=64, x_dtype=DT_F32, state_dtype=DT_F32,
+        w_init="glorot", jac_modes=(JAC_DIAG,), tol=1e-5, max_iters=64)
+    w["gru_full"] = Workload(
+        "gru_full", CELL_GRU, B=16, T=16384, D=16, D_in=16, x_dtype=DT_F32, state_dtype=DT_F32,
+        w_init="normal", w_var=0.5 / 16, jac_modes=(JAC_FULL,), tol=1e-5, max_iters=64)
+    w["gru_diag_long"] = Workload(
+        "gru_diag_long", CELL_GRU_DIAG, B=4, T=8192, D=2048, D_in=2048, x_dtype=DT_BF16,
+        state_dtype=DT_F32, w_init="glorot", u_init="uniform1", jac_modes=(JAC_FULL,),
+        tol=1e-4, max_iters=64)
+    w["lstm_diag_long"] = Workload(
+        "lstm_diag_long", CELL_LSTM_DIAG, B=1, T=131072, D=4096, D_in=4096, x_dtype=DT_BF16,
+        state_dtype=DT_F32, w_init="glorot", u_init="uniform1", forget_bias=1.0,
+        jac_modes=(JAC_FULL,), jac_every=2, tol=1e-4, max_iters=64)
+    w["lstm_diag_long_stiff"] = dataclasses.replace(
+        w["lstm_diag_long"], name="lstm_diag_long_stiff", u_scale=3.0, max_iters=256)
+    return w
+
+
+#: The workloads in the order they are listed for this method (index 0 is the tiny one).
+WORKLOAD_ORDER = ["tiny_gru", "gru_quasi", "gru_full", "gru_diag_long", "lstm_diag_long"]
+
+
+def get_workload(name_or_index, **overrides) -> Workload:
+    ws = named_workloads()
+    if isinstance(name_or_index, int):
+        name_or_index = WORKLOAD_ORDER[name_or_index]
+    w = ws[name_or_index]
+    return dataclasses.replace(w, **overrides) if overrides else w
+
+
+def _round(a: np.ndarray, dt: int) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to(_TORCH_DT[dt])
+
+
+def generate(w: Workload) -> dict:
+    """Draw the workload's tensors (CPU torch tensors in their storage precision).
+
+    Returns W [G*D, D_in] (x precision), U [G*D, D] or u [G, D] (state precision),
+    b_x [G*D] (state precision), b_h (None: every workload has zero recurrent bias),
+    x [B, T, D_in] (x precision), h0 [B, S] zeros (state precision).
+    """
+    rng = np.random.default_rng(w.seed)
+    G, D, D_in = w.G, w.D, w.D_in
+    # 1. W
+    if w.w_init == "normal":
+        W = rng.normal(0.0, math.sqrt(w.w_var), size=(G * D, D_in))
+    elif w.w_init == "glorot":
+        lim = math.sqrt(6.0 / (D_in + D))
+        W = rng.uniform(-lim, lim, size=(G * D, D_in))
+    else:
+        raise ValueError(w.w_init)
+    # 2. recurrent weights
+    if w.cell == CELL_GRU:
+        if w.w_init == "normal":
+            U = rng.normal(0.0, math.sqrt(w.w_var), size=(G * D, D))
+        else:
+            lim = math.sqrt(6.0 / (D + D))
+            U = rng.uniform(-lim, lim, size=(G * D, D))
+    else:
+        if w.u_init != "uniform1":
+            raise ValueError("diagonal-recurrence cells draw u ~ U(-1, 1)")
+        U = rng.uniform(-1.0, 1.0, size=(G, D))
+    U = U * w.u_scale
+    # 3. x
+    if w.x_dtype == DT_BF16:
+        x = rng.standard_normal(size=(w.B, w.T, D_in), dtype=np.float32)
+    else:
+        x = rng.standard_normal(size=(w.B, w.T, D_in))
+    b_x = np.zeros(G * D)
+    if w.forget_bias != 0.0:
+        if w.cell != CELL_LSTM_DIAG:
+            raise ValueError("forget bias only applies to the LSTM cell")
+        b_x[D:2 * D] = w.forget_bias   # gate order (i, f, o, g): f is block 1
+    return {
+        "W": _round(W, w.x_dtype),
+        "U": _round(U, w.state_dtype),
+        "b_x": _round(b_x, w.state_dtype),
+        "b_h": None,
+        "x": _round(x, w.x_dtype),
+        "h0": torch.zeros(w.B, w.S, dtype=_TORCH_DT[w.state_dtype]),
+    }
+
+
+def random_problem(cell: int, B: int, T: int, D: int, D_in: int, *, seed: int = 0,
+                   x_dtype: int = DT_F64, state_dtype: int = DT_F64, w_std: Optional[float] = None,
+                   u_scale: float = 1.0, bias_std: float = 0.0, h0_std: float = 0.0) -> dict:
+    """A small random problem for parity tests: same draw order, optional random biases/h0.
+
+    Biases and h0 (drawn after x, in the order b_x, b_h, h0) exercise the terms that the
+    named workloads leave at zero.
+    """
+    rng = np.random.default_rng(seed)
+    G = gates_of(cell)
+    S = state_size(cell, D)
+    std = w_std if w_std is not None else 1.0 / math.sqrt(max(D, D_in))
+    W = rng.normal(0.0, std, size=(G * D, D_in))
+    if cell == CELL_GRU:
+        U = rng.normal(0.0, 1.0 / math.sqrt(D), size=(G * D, D))
+    else:
+        U = rng.uniform(-1.0, 1.0, size=(G, D))
+    U = U * u_scale
+    x = rng.standard_normal(size=(B, T, D_in))
+    b_x = rng.normal(0.0, bias_std, size=(G * D,)) if bias_std > 0 else np.zeros(G * D)
+    b_h = rng.normal(0.0, bias_std, size=(G * D,)) if bias_std > 0 else None
+    h0 = rng.normal(0.0, h0_std, size=(B, S)) if h0_std > 0 else np.zeros((B, S))
+    return {
+        "W": _round(W, x_dtype),
+        "U": _round(U, state_dtype),
+        "b_x": _round(b_x, state_dtype),
+        "b_h": None if b_h is None else _round(b_h, state_dtype),
+        "x": _round(x, x_dtype),
+        "h0": _round(h0, state_dtype),
+    }
+
+
+def as_f64(t: Optional[torch.Tensor]) -> Optional[np.ndarray]:
+    """Exact widening of a stored tensor to float64 numpy (bf16 and fp32 embed exactly)."""
+    if t is None:
+        return None
+    return t.detach().to("cpu").to(torch.float64).numpy()

@@ -1,0 +1,97 @@
+"""Naive Newton evaluation with a dense block-bidiagonal solve (oracle; test infrastructure only).
+
+The T-step recurrence is unfolded into one system of equations, one per timestep's
+state (ParaRNN overview, "Core Idea"; DEER poses the states as the solution of a
+fixed-point problem, "Towards Scalable and Stable Parallelization of Nonlinear
+RNNs", abstract):
+
+    R_t(H) = f(H_{t-1}, x_t) - H_t = 0,   t = 1..T,   H_0 = h0.
+
+Each Newton iteration computes the residual and the Jacobian at every step, then
+solves the linearised system (ParaRNN overview, "Core Idea" step 2 and "Newton's
+Iteration").  The system matrix is block lower-bidiagonal: identity blocks on the
+diagonal and -J_t = -df(H_{t-1}, x_t)/dH_{t-1} just below it, because each step
+depends only on its input and the previous state.  Here it is assembled densely
+(T*S x T*S per batch element) and handed to LAPACK -- slow on purpose, so that the
+HIP path's scan has an independent check.
+
+Options:
+* jac_mode: FULL (exact Jacobian), DIAG (its diagonal: quasi-DEER), ZERO (no
+  Jacobian; a fixed-point sweep, test only).
+* jac_every: the Jacobian is recomputed only when k % jac_every == 0 and reused
+  otherwise (ParaRNN overview, "Newton's Iteration": recomputing the Jacobian only
+  every few steps).  The residual is always fresh.
+
+Readings where the pages are silent: initial guess H = 0; stop when the max-abs
+residual (NaN counted as +inf) is <= tol, testing *before* each update so the
+returned iterate is the one whose residual was checked; one shared loop for all
+batch elements; tol < 0 never stops early.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .cells import approx_jacobian, cell_jacobian, cell_step
+from .sequential import project
+
+STATUS_OK = 0
+STATUS_NOT_CONVERGED = 1
+STATUS_NONFINITE = 2
+
+
+def max_abs(r) -> float:
+    """max |r| over all entries; any NaN makes it +inf; an empty array gives 0."""
+    a = np.abs(np.asarray(r, dtype=np.float64))
+    if a.size == 0:
+        return 0.0
+    if np.isnan(a).any():
+        return float("inf")
+    return float(a.max())
+
+
+def _previous_states(h0, H):
+    """P_t = H_{t-1} (with H_0 = h0) for every step: [B, T, S]."""
+    return np.concatenate([h0[:, None, :], H[:, :-1, :]], axis=1)
+
+
+def newton_dense(cell: int, W, U, b_x, b_h, x, h0, max_iters: int, tol: float,
+                 jac_mode: int, jac_every: int = 1, gx=None):
+    """Returns dict(states [B,T,S], iters, status, rhos[list], jac_evals)."""
+    if jac_every < 1:
+        raise ValueError("jac_every must be >= 1")
+    U = np.asarray(U, dtype=np.float64)
+    b_h = None if b_h is None else np.asarray(b_h, dtype=np.float64)
+    h0 = np.asarray(h0, dtype=np.float64)
+    if gx is None:
+        gx = project(W, x, b_x)
+    B, T, GD = gx.shape
+    S = h0.shape[1]
+    H = np.zeros((B, T, S))
+    rhos = []
+    Jhat = None
+    jac_evals = 0
+    k = 0
+    while True:
+        P = _previous_states(h0, H)
+        F = cell_step(cell, U, b_h, P.reshape(B * T, S), gx.reshape(B * T, GD)).reshape(B, T, S)
+        r = F - H
+        rho = max_abs(r)
+        rhos.append(rho)
+        if not np.isfinite(rho):
+            return dict(states=H, iters=k, status=STATUS_NONFINITE, rhos=rhos, jac_evals=jac_evals)
+        if rho <= tol:
+            return dict(states=H, iters=k, status=STATUS_OK, rhos=rhos, jac_evals=jac_evals)
+        if k == max_iters:
+            return dict(states=H, iters=k, status=STATUS_NOT_CONVERGED, rhos=rhos,
+                        jac_evals=jac_evals)
+        if k % jac_every == 0:
+            J = cell_jacobian(cell, U, b_h, P.reshape(B * T, S), gx.reshape(B * T, GD))
+            Jhat = approx_jacobian(J, jac_mode).reshape(B, T, S, S)
+            jac_evals += 1
+        for b in range(B):
+            A = np.eye(T * S)
+            for t in range(1, T):
+                A[t * S:(t + 1) * S, (t - 1) * S:t * S] = -Jhat[b, t]
+            delta = np.linalg.solve(A, r[b].reshape(T * S))
+            H[b] = H[b] + delta.reshape(T, S)
+        k += 1
