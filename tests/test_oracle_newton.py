@@ -254,3 +254,21 @@ def test_golden_tiny_gru_matches_stored_oracle_output():
         res = _newton(w.cell, p, 64, 1e-10, {"full": O.JAC_FULL, "diag": O.JAC_DIAG}[mode])
         assert res["iters"] == g[mode]["iters"]
         np.testing.assert_allclose(res["rhos"], g[mode]["rhos"], rtol=1e-9, atol=1e-300)
+
+
+@pytest.mark.parametrize("cell", CELLS)
+def test_stale_jacobian_reuses_the_refresh_point(cell):
+    """jac_every=2: update 2 uses J from the states of update 1's start and a fresh residual."""
+    p = _problem(cell, B=1, T=9)
+    S = p["h0"].shape[1]
+    gx = O.project(p["W"], p["x"], p["b_x"])[0]
+    h1 = _newton(cell, p, 1, -1.0, O.JAC_FULL, 2)["states"][0]
+    r2 = _newton(cell, p, 2, -1.0, O.JAC_FULL, 2)
+    assert r2["jac_evals"] == 1
+    P0 = np.concatenate([p["h0"], np.zeros((8, S))], 0)
+    P1 = np.concatenate([p["h0"], h1[:-1]], 0)
+    F1 = O.cell_step(cell, p["U"], p["b_h"], P1, gx)
+    J0 = O.cell_jacobian(cell, p["U"], p["b_h"], P0, gx)
+    np.testing.assert_allclose(r2["states"][0], h1 + O.scan_loop(J0, F1 - h1), rtol=0, atol=1e-13)
+    fresh = _newton(cell, p, 2, -1.0, O.JAC_FULL, 1)["states"][0]
+    assert np.abs(fresh - r2["states"][0]).max() > 1e-8
