@@ -1,0 +1,168 @@
+/*
+ * pnr.h -- C ABI of libpnr: parallel-in-time Newton evaluation of a nonlinear RNN
+ * on one AMD MI355X (gfx950).
+ *
+ * The operation.  Given inputs x_1..x_T, an initial state s_0 = h0 and a cell f, the
+ * library returns the states s_t = f(s_{t-1}, x_t), t = 1..T.  Instead of stepping
+ * through time it unfolds the recurrence into one system of nonlinear equations, one
+ * per step (ParaRNN overview page, "Core Idea"; DEER poses the states as the solution
+ * of a fixed-point problem: "Towards Scalable and Stable Parallelization of Nonlinear
+ * RNNs", abstract) and solves it with Newton iterations (ParaRNN overview, "Newton's
+ * Iteration").  One iteration k:
+ *   r_t   = f(s_{t-1}^(k), x_t) - s_t^(k)                       residual, every t at once
+ *   J_t   = df/ds evaluated at s_{t-1}                          Jacobian (mode below)
+ *   rho_k = max_{b,t,i} |r|   (NaN counts as +inf)              two-level reduction
+ *           stop if rho_k <= tol or rho_k is not finite          (ParaRNN overview, "Parallel Reduction")
+ *   d_t   = J_t d_{t-1} + r_t, d_0 = 0                          block lower-bidiagonal solve,
+ *                                                                done as a parallel scan of
+ *                                                                affine maps
+ *   s^(k+1) = s^(k) + d
+ * The converged states equal sequential evaluation ("Parallelizing non-linear
+ * sequential models over the sequence length", abstract).  The initial guess is
+ * s^(0) = 0.  The Newton loop runs on the device: no host synchronisation happens
+ * between iterations; the call synchronises once at its end.
+ *
+ * Cells (the pages print no equations; these are the readings implemented):
+ *   PNR_CELL_GRU        GRU, dense recurrent matrix U [3D, D], gate blocks (r, z, n),
+ *                       "linear before reset": n = tanh(gx_n + r*(U_n h + b_hn)),
+ *                       h' = (1-z) n + z h.  State size S = D.
+ *   PNR_CELL_GRU_DIAG   the same GRU with elementwise recurrent weights u [3, D]
+ *                       (diagonal recurrence, as in ParaRNN's GRU adaptation).  S = D.
+ *   PNR_CELL_LSTM_DIAG  LSTM with elementwise recurrent weights u [4, D], gate blocks
+ *                       (i, f, o, g); state (c, h), S = 2D, c first.
+ *
+ * Jacobian modes (jac_mode):
+ *   PNR_JAC_FULL  exact Jacobian in the cell's own structure: dense D x D (GRU),
+ *                 diagonal (GRU_DIAG), one 2x2 block per channel (LSTM_DIAG).
+ *   PNR_JAC_DIAG  its diagonal: quasi-Newton ("quasi-DEER"; "Towards Scalable and
+ *                 Stable Parallelization of Nonlinear RNNs", abstract).
+ *   PNR_JAC_ZERO  no Jacobian: a fixed-point (Picard) sweep.  Test mode.
+ * pnr_cell.jac_every = e >= 1 recomputes the Jacobian only on iterations k with
+ * k % e == 0 and reuses it otherwise (ParaRNN overview, "Newton's Iteration": the
+ * Jacobian recomputed only every few steps); the residual is always fresh.
+ *
+ * Memory and layout.  Every tensor argument is a DEVICE pointer, row-major, owned by
+ * the caller and not retained after the call returns:
+ *   x      [B, T, D_in]            x_dtype
+ *   h0     [B, S]                  state_dtype (may be NULL: zeros)
+ *   h_out  [B, T, S]               state_dtype; h_out[b, t] = s_{t+1}; h0 excluded
+ *   W      [G*D, D_in]             x_dtype     (G = 3 for GRU cells, 4 for LSTM)
+ *   U      GRU: [3D, D]; GRU_DIAG: [3, D]; LSTM_DIAG: [4, D]     state_dtype
+ *   b_x    [G*D] (NULL = 0)        state_dtype; added to W x
+ *   b_h    [G*D] (NULL = 0)        state_dtype; added to the recurrent term (for
+ *                                  the GRU candidate gate it sits inside r*(...))
+ * The library allocates no device memory: all scratch comes from pnr_cell.workspace,
+ * at least pnr_workspace_bytes() bytes, 256-byte aligned.  Work is enqueued on
+ * pnr_cell.stream (a hipStream_t; NULL = the default stream).
+ *
+ * Supported combinations (others return PNR_E_UNSUPPORTED):
+ *   GRU:        (x, state) in {(f64, f64), (f32, f32), (bf16, f32)}, 1 <= D <= 64
+ *   GRU_DIAG,
+ *   LSTM_DIAG:  (x, state) in {(f32, f32), (bf16, f32)}
+ *
+ * Errors.  Functions never abort and never print.  Negative return codes mean no
+ * result was produced; the text of the last error of the calling thread is
+ * available from pnr_last_error().  Argument validation happens before any HIP call.
+ */
+#ifndef PNR_H
+#define PNR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum pnr_cell_kind { PNR_CELL_GRU = 0, PNR_CELL_GRU_DIAG = 1, PNR_CELL_LSTM_DIAG = 2 };
+enum pnr_jac_mode { PNR_JAC_FULL = 0, PNR_JAC_DIAG = 1, PNR_JAC_ZERO = 2 };
+enum pnr_dtype { PNR_F64 = 0, PNR_F32 = 1, PNR_BF16 = 2 };
+enum pnr_status {
+  PNR_OK = 0,             /* converged: rho <= tol                                   */
+  PNR_NOT_CONVERGED = 1,  /* max_iters updates applied, rho > tol; h_out = last iterate */
+  PNR_NONFINITE = 2,      /* a residual was NaN/Inf; h_out = the iterate that made it   */
+  PNR_E_INVALID = -1,     /* bad pointer, size, enum or combination                   */
+  PNR_E_UNSUPPORTED = -2, /* valid request outside the supported set above            */
+  PNR_E_WORKSPACE = -3,   /* workspace NULL, misaligned or smaller than required      */
+  PNR_E_HIP = -4          /* a HIP runtime call failed                                */
+};
+
+/* Problem description.  All sizes must be >= 1 (T may be 0: nothing to do). */
+typedef struct pnr_cell {
+  int32_t kind;          /* pnr_cell_kind                                   */
+  int32_t D;             /* channels (hidden size)                          */
+  int32_t D_in;          /* input features                                  */
+  int32_t T;             /* sequence length                                 */
+  int32_t B;             /* batch                                           */
+  int32_t x_dtype;       /* pnr_dtype of x and W                            */
+  int32_t state_dtype;   /* pnr_dtype of h0, h_out, U, b_x, b_h             */
+  int32_t jac_every;     /* >= 1                                            */
+  void* stream;          /* hipStream_t, NULL = default stream              */
+  void* workspace;       /* device scratch, >= pnr_workspace_bytes(...)     */
+  size_t workspace_bytes;
+} pnr_cell;
+
+typedef struct pnr_params {
+  const void* W;    /* [G*D, D_in]        x_dtype                       */
+  const void* U;    /* see the cell list   state_dtype                   */
+  const void* b_x;  /* [G*D] or NULL       state_dtype                   */
+  const void* b_h;  /* [G*D] or NULL       state_dtype                   */
+} pnr_params;
+
+/*
+ * Scratch bytes pnr_eval needs for this problem and Jacobian mode (0 on invalid
+ * input; the reason is in pnr_last_error()).  Pure host arithmetic; no HIP call.
+ * The Jacobian itself is never stored: it is rebuilt from the stored states inside
+ * the scan, so the dense mode needs no O(T D^2) buffer (the memory argument behind
+ * quasi-DEER in "Towards Scalable and Stable Parallelization of Nonlinear RNNs",
+ * scime summary "Approach", is thereby moot here; both modes use O(T D)).
+ */
+size_t pnr_workspace_bytes(const pnr_cell* cell, int jac_mode);
+
+/*
+ * Evaluate the RNN by parallel Newton iterations (see the top of this file).
+ *   max_iters  >= 0: at most this many Newton updates; 0 returns the initial guess.
+ *   tol        stop when rho_k <= tol; tol < 0 never stops early (exactly max_iters
+ *              updates are applied).
+ * Returns a pnr_status.  On PNR_OK / PNR_NOT_CONVERGED / PNR_NONFINITE, h_out holds
+ * the iterate s^(k) whose residual rho_k was checked last, and the call has
+ * synchronised the stream.  Thread-safe for distinct workspaces.
+ */
+int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0,
+             void* h_out, int max_iters, double tol, int jac_mode);
+
+/* Newton updates applied by the calling thread's last pnr_eval (-1 if it failed before). */
+int pnr_iters_used(void);
+
+/* rho of the state returned by the calling thread's last pnr_eval (NaN if none). */
+double pnr_last_residual(void);
+
+/*
+ * Copies the residual history rho_0..rho_iters of the last pnr_eval (at most max_n
+ * values) into host memory `out`; returns how many values that history has.
+ */
+int pnr_last_residual_history(double* out, int max_n);
+
+/* Text of the calling thread's last error ("" if none).  Valid until the next call. */
+const char* pnr_last_error(void);
+
+/*
+ * Standalone linear solve used inside every Newton iteration, exposed for testing
+ * the scan on its own: d_t = A_t d_{t-1} + b_t, d_0 = 0 along t, for R independent
+ * rows (ParaRNN overview, "Newton's Iteration": forward substitution on the block
+ * lower-triangular system).  fp32, device pointers:
+ *   kind 1 (diagonal):  A, b, d are [R, T]
+ *   kind 2 (2x2 block): A is [R, 4, T] (a00, a01, a10, a11 planes), b and d [R, 2, T]
+ * tile_len (0 = library default) sets the per-block tile along T; smaller tiles mean
+ * more blocks linked by the decoupled look-back.  workspace as for pnr_eval, size
+ * from pnr_scan_workspace_bytes.  Synchronises the stream before returning.
+ */
+size_t pnr_scan_workspace_bytes(int kind, int R, int T, int tile_len);
+int pnr_scan(int kind, int R, int T, const float* A, const float* b, float* d, int tile_len,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PNR_H */

@@ -1,0 +1,344 @@
+// Host side of the C ABI declared in include/pnr.h.
+//
+// pnr_eval validates its arguments without touching HIP, carves the caller's workspace,
+// then enqueues on the caller's stream:
+//   init -> input projection GEMM -> max_iters fused Newton iterations -> one
+//   residual-only pass -> output layout conversion -> one control read-back.
+// Every iteration kernel reads the device control block first and returns at once
+// when an earlier iteration has already decided, so the host never waits between
+// iterations (ParaRNN overview page, "Technical Implementation": Newton iterations
+// with a residual check; the check runs on the device).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "kernels.h"
+
+using namespace pnr;
+
+namespace {
+
+struct LastCall {
+  int iters = -1;
+  double residual = NAN;
+  std::vector<double> hist;
+  std::string err;
+};
+thread_local LastCall g_last;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last.err = buf;
+  return code;
+}
+
+size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
+size_t dsize(int dt) { return dt == PNR_F64 ? 8 : (dt == PNR_F32 ? 4 : 2); }
+
+bool is_diag_cell(int kind) { return kind == PNR_CELL_GRU_DIAG || kind == PNR_CELL_LSTM_DIAG; }
+int gates(int kind) { return kind == PNR_CELL_LSTM_DIAG ? 4 : 3; }
+int states(int kind, int D) { return kind == PNR_CELL_LSTM_DIAG ? 2 * D : D; }
+
+struct Layout {
+  size_t ctrl = 0, hist = 0, partials = 0, slots = 0, gx = 0, h[3] = {0, 0, 0}, total = 0;
+  size_t slot_words = 0;
+  int nbuf = 2, tiles_per_row = 0, n_tiles = 0, L = 0;
+  bool dense_full = false;
+};
+
+// Validate the request; returns 0 or a negative status with the reason recorded.
+int validate(const pnr_cell* c, int jac_mode) {
+  if (!c) return fail(PNR_E_INVALID, "cell descriptor is NULL");
+  if (c->kind < PNR_CELL_GRU || c->kind > PNR_CELL_LSTM_DIAG) return fail(PNR_E_INVALID, "unknown cell kind %d", c->kind);
+  if (jac_mode < PNR_JAC_FULL || jac_mode > PNR_JAC_ZERO) return fail(PNR_E_INVALID, "unknown jac_mode %d", jac_mode);
+  if (c->D < 1 || c->D_in < 1 || c->B < 1 || c->T < 0)
+    return fail(PNR_E_INVALID, "sizes must satisfy D, D_in, B >= 1 and T >= 0 (got D=%d D_in=%d B=%d T=%d)", c->D,
+                c->D_in, c->B, c->T);
+  if (c->jac_every < 1) return fail(PNR_E_INVALID, "jac_every must be >= 1 (got %d)", c->jac_every);
+  for (int dt : {c->x_dtype, c->state_dtype})
+    if (dt < PNR_F64 || dt > PNR_BF16) return fail(PNR_E_INVALID, "unknown dtype %d", dt);
+  const int xd = c->x_dtype, sd = c->state_dtype;
+  if (c->kind == PNR_CELL_GRU) {
+    const bool ok = (xd == PNR_F64 && sd == PNR_F64) || (xd == PNR_F32 && sd == PNR_F32) ||
+                    (xd == PNR_BF16 && sd == PNR_F32);
+    if (!ok) return fail(PNR_E_UNSUPPORTED, "GRU supports (x, state) dtypes (f64,f64), (f32,f32), (bf16,f32)");
+    const int full = jac_mode == PNR_JAC_FULL;
+    if (!dense_supported(c->D, full, sd == PNR_F64))
+      return fail(PNR_E_UNSUPPORTED, "GRU with D=%d is not supported in this mode (%s, %s)", c->D,
+                  full ? "dense Jacobian: D <= 32" : "diagonal Jacobian: D <= 64 (fp32) / 32 (fp64)",
+                  sd == PNR_F64 ? "fp64" : "fp32");
+  } else {
+    const bool ok = (xd == PNR_F32 || xd == PNR_BF16) && sd == PNR_F32;
+    if (!ok) return fail(PNR_E_UNSUPPORTED, "diagonal-recurrence cells support x in {f32, bf16} with f32 state");
+  }
+  const double elems = (double)c->B * c->T * states(c->kind, c->D);
+  if (elems * gates(c->kind) > 9.0e18 || (double)c->T * 4 > 2.0e9)
+    return fail(PNR_E_INVALID, "problem too large for this library's index range");
+  return 0;
+}
+
+Layout make_layout(const pnr_cell* c, int jac_mode) {
+  Layout l;
+  const int G = gates(c->kind), S = states(c->kind, c->D);
+  const size_t B = c->B, T = c->T, D = c->D;
+  const size_t es = dsize(c->state_dtype);
+  l.nbuf = c->jac_every > 1 ? 3 : 2;
+  size_t off = 0;
+  l.ctrl = off; off = align_up(off + sizeof(Ctrl));
+  l.hist = off; off = align_up(off + sizeof(double) * (PNR_MAX_ITERS + 1));
+  l.partials = off; off = align_up(off + sizeof(uint64_t) * kMaxGrid);
+  if (is_diag_cell(c->kind)) {
+    const int tile = PNR_BLOCK * diag_items_per_thread(c->kind);
+    l.tiles_per_row = (int)((T + tile - 1) / tile);
+    l.n_tiles = (int)(B * D * l.tiles_per_row);
+    l.slot_words = (size_t)l.n_tiles * diag_slot_words(c->kind);
+  } else {
+    l.dense_full = jac_mode == PNR_JAC_FULL;
+    l.L = dense_tile_len(c->D, l.dense_full, c->state_dtype == PNR_F64);
+    l.tiles_per_row = (int)((T + l.L - 1) / l.L);
+    l.n_tiles = (int)(B * l.tiles_per_row);
+    l.slot_words = (size_t)l.n_tiles * dense_slot_words(c->D, l.dense_full, c->state_dtype == PNR_F64);
+  }
+  l.slots = off; off = align_up(off + sizeof(uint64_t) * (l.slot_words ? l.slot_words : 1));
+  l.gx = off; off = align_up(off + es * B * T * (size_t)G * D);
+  for (int i = 0; i < l.nbuf; ++i) { l.h[i] = off; off = align_up(off + es * B * T * (size_t)S); }
+  l.total = off;
+  return l;
+}
+
+struct DevInfo { int dev = -1; int num_cu = 0; };
+thread_local DevInfo g_dev;
+
+int device_info(int* num_cu) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PNR_E_HIP, "hipGetDevice failed");
+  if (g_dev.dev != dev) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      return fail(PNR_E_HIP, "cannot query the compute-unit count");
+    g_dev.dev = dev;
+    g_dev.num_cu = n;
+  }
+  *num_cu = g_dev.num_cu;
+  return 0;
+}
+
+#define PNR_HIP(call)                                                                     \
+  do {                                                                                    \
+    hipError_t e_ = (call);                                                               \
+    if (e_ != hipSuccess) return fail(PNR_E_HIP, "%s failed: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t pnr_workspace_bytes(const pnr_cell* cell, int jac_mode) {
+  if (validate(cell, jac_mode) != 0) return 0;
+  return make_layout(cell, jac_mode).total;
+}
+
+const char* pnr_last_error(void) { return g_last.err.c_str(); }
+int pnr_iters_used(void) { return g_last.iters; }
+double pnr_last_residual(void) { return g_last.residual; }
+int pnr_last_residual_history(double* out, int max_n) {
+  const int n = (int)g_last.hist.size();
+  if (out)
+    for (int i = 0; i < n && i < max_n; ++i) out[i] = g_last.hist[i];
+  return n;
+}
+
+int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, void* h_out,
+             int max_iters, double tol, int jac_mode) {
+  g_last = LastCall();
+  int rc = validate(cell, jac_mode);
+  if (rc) return rc;
+  if (!params) return fail(PNR_E_INVALID, "params is NULL");
+  if (!x || !h_out || !params->W || !params->U) return fail(PNR_E_INVALID, "x, h_out, W and U must be non-NULL");
+  if (max_iters < 0 || max_iters >= PNR_MAX_ITERS)
+    return fail(PNR_E_INVALID, "max_iters must be in [0, %d)", PNR_MAX_ITERS);
+  if (isnan(tol)) return fail(PNR_E_INVALID, "tol is NaN");
+  const Layout l = make_layout(cell, jac_mode);
+  if (!cell->workspace) return fail(PNR_E_WORKSPACE, "workspace is NULL (%zu bytes required)", l.total);
+  if ((uintptr_t)cell->workspace % 256) return fail(PNR_E_WORKSPACE, "workspace must be 256-byte aligned");
+  if (cell->workspace_bytes < l.total)
+    return fail(PNR_E_WORKSPACE, "workspace has %zu bytes, %zu required", cell->workspace_bytes, l.total);
+  if (cell->T == 0) {
+    g_last.iters = 0;
+    g_last.residual = 0.0;
+    g_last.hist.assign(1, 0.0);
+    return PNR_OK;
+  }
+
+  int num_cu = 0;
+  if ((rc = device_info(&num_cu))) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(cell->stream);
+  char* ws = static_cast<char*>(cell->workspace);
+  Ctrl* ctrl = reinterpret_cast<Ctrl*>(ws + l.ctrl);
+  double* hist = reinterpret_cast<double*>(ws + l.hist);
+  uint64_t* slots = reinterpret_cast<uint64_t*>(ws + l.slots);
+  void* gx = ws + l.gx;
+  void* H[3] = {ws + l.h[0], ws + l.h[1], l.nbuf > 2 ? ws + l.h[2] : nullptr};
+
+  const int kind = cell->kind, D = cell->D, T = cell->T, B = cell->B, Din = cell->D_in;
+  const int G = gates(kind), S = states(kind, D);
+
+  PNR_HIP(launch_init(ctrl, slots, l.slot_words, st));
+
+  // ---- input projection ----
+  GemmArgs g{};
+  if (is_diag_cell(kind)) {
+    // gx[b][m][t] = sum_k W[m][k] x[b][t][k] + b_x[m]
+    g = GemmArgs{params->W, x, params->b_x, gx, G * D, T, Din, 0, (long long)T * Din, (long long)G * D * T,
+                 Din, Din, T, B, 1};
+  } else {
+    // gx[(b,t)][m] = sum_k x[(b,t)][k] W[m][k] + b_x[m]
+    g = GemmArgs{x, params->W, params->b_x, gx, B * T, G * D, Din, 0, 0, 0, Din, Din, G * D, 1, 0};
+  }
+  PNR_HIP(launch_gemm(cell->x_dtype, cell->state_dtype, g, st));
+
+  // ---- Newton loop: every launch is enqueued up front; the device decides when to stop ----
+  int cur = -1, jac = -1;   // buffer indices; -1 = the zero initial guess
+  auto pick_next = [&](int a, int b) {
+    for (int i = 0; i < l.nbuf; ++i)
+      if (i != a && i != b) return i;
+    return -1;
+  };
+  for (int k = 0; k <= max_iters; ++k) {
+    const bool resid_only = k == max_iters;
+    if (!resid_only && k % cell->jac_every == 0) jac = cur;
+    const int next = resid_only ? cur : pick_next(cur, jac);
+    if (is_diag_cell(kind)) {
+      DiagIterArgs a{};
+      a.gx = static_cast<const float*>(gx);
+      a.u = static_cast<const float*>(params->U);
+      a.bh = static_cast<const float*>(params->b_h);
+      a.h0 = static_cast<const float*>(h0);
+      a.Hcur = cur >= 0 ? static_cast<const float*>(H[cur]) : nullptr;
+      a.Hjac = jac >= 0 ? static_cast<const float*>(H[jac]) : nullptr;
+      a.Hnext = next >= 0 ? static_cast<float*>(H[next]) : nullptr;
+      a.slots = slots;
+      a.partials = reinterpret_cast<uint32_t*>(ws + l.partials);
+      a.ctrl = ctrl;
+      a.rho_hist = hist;
+      a.cur_zero = cur < 0;
+      a.jac_zero = jac < 0;
+      a.B = B; a.D = D; a.T = T;
+      a.tiles_per_row = l.tiles_per_row;
+      a.n_tiles = l.n_tiles;
+      a.k = k; a.cur_buf = cur; a.max_iters = max_iters; a.tol = tol;
+      a.jac_mode = jac_mode;
+      a.resid_only = resid_only;
+      PNR_HIP(launch_diag_iter(kind, a, num_cu, st, nullptr));
+    } else if (cell->state_dtype == PNR_F32) {
+      DenseIterArgs<float> a{};
+      a.gx = static_cast<const float*>(gx);
+      a.U = static_cast<const float*>(params->U);
+      a.bh = static_cast<const float*>(params->b_h);
+      a.h0 = static_cast<const float*>(h0);
+      a.Hcur = cur >= 0 ? static_cast<const float*>(H[cur]) : nullptr;
+      a.Hjac = jac >= 0 ? static_cast<const float*>(H[jac]) : nullptr;
+      a.Hnext = next >= 0 ? static_cast<float*>(H[next]) : nullptr;
+      a.slots = slots; a.partials = reinterpret_cast<uint64_t*>(ws + l.partials);
+      a.ctrl = ctrl; a.rho_hist = hist;
+      a.cur_zero = cur < 0; a.jac_zero = jac < 0;
+      a.B = B; a.D = D; a.T = T; a.L = l.L;
+      a.tiles_per_row = l.tiles_per_row; a.n_tiles = l.n_tiles;
+      a.k = k; a.cur_buf = cur; a.max_iters = max_iters; a.tol = tol;
+      a.jac_mode = jac_mode; a.resid_only = resid_only;
+      PNR_HIP(launch_dense_iter_f32(a, l.dense_full, num_cu, st));
+    } else {
+      DenseIterArgs<double> a{};
+      a.gx = static_cast<const double*>(gx);
+      a.U = static_cast<const double*>(params->U);
+      a.bh = static_cast<const double*>(params->b_h);
+      a.h0 = static_cast<const double*>(h0);
+      a.Hcur = cur >= 0 ? static_cast<const double*>(H[cur]) : nullptr;
+      a.Hjac = jac >= 0 ? static_cast<const double*>(H[jac]) : nullptr;
+      a.Hnext = next >= 0 ? static_cast<double*>(H[next]) : nullptr;
+      a.slots = slots; a.partials = reinterpret_cast<uint64_t*>(ws + l.partials);
+      a.ctrl = ctrl; a.rho_hist = hist;
+      a.cur_zero = cur < 0; a.jac_zero = jac < 0;
+      a.B = B; a.D = D; a.T = T; a.L = l.L;
+      a.tiles_per_row = l.tiles_per_row; a.n_tiles = l.n_tiles;
+      a.k = k; a.cur_buf = cur; a.max_iters = max_iters; a.tol = tol;
+      a.jac_mode = jac_mode; a.resid_only = resid_only;
+      PNR_HIP(launch_dense_iter_f64(a, l.dense_full, num_cu, st));
+    }
+    cur = next;
+  }
+
+  // ---- returned iterate -> caller layout ----
+  if (is_diag_cell(kind)) {
+    const float* bufs[3] = {static_cast<const float*>(H[0]), static_cast<const float*>(H[1]),
+                            static_cast<const float*>(H[2])};
+    PNR_HIP(launch_diag_output(bufs, ctrl, static_cast<float*>(h_out), B, S, T, st));
+  } else if (cell->state_dtype == PNR_F32) {
+    const float* bufs[3] = {static_cast<const float*>(H[0]), static_cast<const float*>(H[1]),
+                            static_cast<const float*>(H[2])};
+    PNR_HIP(launch_dense_output<float>(bufs, ctrl, static_cast<float*>(h_out), (size_t)B * T * S, st));
+  } else {
+    const double* bufs[3] = {static_cast<const double*>(H[0]), static_cast<const double*>(H[1]),
+                             static_cast<const double*>(H[2])};
+    PNR_HIP(launch_dense_output<double>(bufs, ctrl, static_cast<double*>(h_out), (size_t)B * T * S, st));
+  }
+
+  // ---- the one device -> host crossing of the call ----
+  Ctrl hc;
+  std::vector<double> hh(max_iters + 1);
+  PNR_HIP(hipMemcpyAsync(&hc, ctrl, sizeof(Ctrl), hipMemcpyDeviceToHost, st));
+  PNR_HIP(hipMemcpyAsync(hh.data(), hist, sizeof(double) * (max_iters + 1), hipMemcpyDeviceToHost, st));
+  PNR_HIP(hipStreamSynchronize(st));
+  if (!hc.done || hc.iters < 0) return fail(PNR_E_HIP, "device loop did not record a decision");
+  g_last.iters = hc.iters;
+  g_last.residual = hc.rho;
+  g_last.hist.assign(hh.begin(), hh.begin() + hc.iters + 1);
+  return hc.status;
+}
+
+size_t pnr_scan_workspace_bytes(int kind, int R, int T, int tile_len) {
+  if ((kind != 1 && kind != 2) || R < 0 || T < 0) {
+    fail(PNR_E_INVALID, "bad scan arguments");
+    return 0;
+  }
+  if (tile_len == 0) tile_len = scan_default_tile(kind);
+  const size_t tiles = (size_t)R * ((T + tile_len - 1) / (tile_len > 0 ? tile_len : 1));
+  return align_up(sizeof(Ctrl)) + align_up(sizeof(uint64_t) * (tiles * scan_slot_words(kind) + 1));
+}
+
+int pnr_scan(int kind, int R, int T, const float* A, const float* b, float* d, int tile_len, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  g_last = LastCall();
+  if (kind != 1 && kind != 2) return fail(PNR_E_INVALID, "scan kind must be 1 (diagonal) or 2 (2x2)");
+  if (R < 0 || T < 0) return fail(PNR_E_INVALID, "R and T must be >= 0");
+  if (tile_len == 0) tile_len = scan_default_tile(kind);
+  if (tile_len != PNR_BLOCK && tile_len != 2 * PNR_BLOCK && tile_len != 4 * PNR_BLOCK && tile_len != 8 * PNR_BLOCK)
+    return fail(PNR_E_INVALID, "tile_len must be 0, 256, 512, 1024 or 2048");
+  if (R == 0 || T == 0) return PNR_OK;
+  if (!A || !b || !d) return fail(PNR_E_INVALID, "A, b and d must be non-NULL");
+  const size_t need = pnr_scan_workspace_bytes(kind, R, T, tile_len);
+  if (!workspace || (uintptr_t)workspace % 256 || workspace_bytes < need)
+    return fail(PNR_E_WORKSPACE, "workspace must be 256-byte aligned and hold %zu bytes", need);
+  int num_cu = 0, rc;
+  if ((rc = device_info(&num_cu))) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  Ctrl* ctrl = reinterpret_cast<Ctrl*>(workspace);
+  uint64_t* slots = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + align_up(sizeof(Ctrl)));
+  const size_t tiles = (size_t)R * ((T + tile_len - 1) / tile_len);
+  PNR_HIP(launch_init(ctrl, slots, tiles * scan_slot_words(kind), st));
+  PNR_HIP(launch_scan(kind, R, T, A, b, d, tile_len, slots, ctrl, num_cu, st));
+  PNR_HIP(hipStreamSynchronize(st));
+  return PNR_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,175 @@
+// Shared device/host definitions for libpnr (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pnr.h"
+
+#define PNR_BLOCK 256          // threads per block for every iteration kernel (4 waves)
+#define PNR_WAVES (PNR_BLOCK / 64)
+#define PNR_MAX_ITERS 4096     // residual history capacity
+
+namespace pnr {
+
+// ---------------------------------------------------------------------------------
+// Control block written only on the device during a call; read back once at the end.
+struct Ctrl {
+  int32_t done;        // 1 once the loop has decided (converged, non-finite, or exhausted)
+  int32_t status;      // pnr_status
+  int32_t iters;       // Newton updates applied to the returned iterate
+  int32_t result_buf;  // index of the state buffer holding the result (-1 = the zero guess)
+  double rho;          // residual of the returned iterate
+  uint32_t ticket;     // dynamic tile counter of the running iteration kernel
+  uint32_t finished;   // blocks of the running iteration kernel that have finished
+  uint32_t pad[2];
+};
+
+// ---------------------------------------------------------------------------------
+// Elementwise math.  sigmoid(a) = 1 / (1 + e^-a); tanh(a) = 2 sigmoid(2a) - 1.  fp32
+// uses the hardware exp2/rcp (a few ulp; far below the fp32 conditioning floor of the
+// recurrences), fp64 uses the device math library.
+__device__ __forceinline__ float fast_exp(float a) { return __expf(a); }
+__device__ __forceinline__ float sigm(float a) { return __frcp_rn(1.0f + fast_exp(-a)); }
+__device__ __forceinline__ float tanh_(float a) {
+  return 1.0f - 2.0f * __frcp_rn(1.0f + fast_exp(2.0f * a));
+}
+__device__ __forceinline__ double sigm(double a) { return 1.0 / (1.0 + exp(-a)); }
+__device__ __forceinline__ double tanh_(double a) { return tanh(a); }
+
+// |r| as ordered unsigned bits: for non-negative floats the bit patterns order like the
+// values, and every NaN pattern sorts above +inf, so an integer max keeps NaN.
+__device__ __forceinline__ uint32_t abs_bits(float r) { return __float_as_uint(r) & 0x7fffffffu; }
+__device__ __forceinline__ uint64_t abs_bits(double r) {
+  return (uint64_t)__double_as_longlong(r) & 0x7fffffffffffffffull;
+}
+__host__ __device__ inline double bits_to_rho(uint32_t b) {
+  if (b >= 0x7f800000u) return __builtin_inf();
+  union { uint32_t u; float f; } c; c.u = b; return (double)c.f;
+}
+__host__ __device__ inline double bits_to_rho64(uint64_t b) {
+  if (b >= 0x7ff0000000000000ull) return __builtin_inf();
+  union { uint64_t u; double f; } c; c.u = b; return c.f;
+}
+
+// ---------------------------------------------------------------------------------
+// Cross-lane helpers (wave64).  DPP row_shr:n moves a value n lanes up inside each row
+// of 16 lanes; lanes with no source keep `old`.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL,
+                                                    0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+__device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
+
+// max over the 64 lanes (all lanes get the result)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u<0x111>(0u, v));   // row_shr:1
+  v = max(v, dpp_u<0x112>(0u, v));   // row_shr:2
+  v = max(v, dpp_u<0x114>(0u, v));   // row_shr:4
+  v = max(v, dpp_u<0x118>(0u, v));   // row_shr:8
+  uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+  uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+  uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+  uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+// ---------------------------------------------------------------------------------
+// Affine maps d -> A d + b.  compose(later, earlier) = later o earlier.
+struct Aff1 {  // one channel (diagonal Jacobian)
+  float a, b;
+};
+__device__ __forceinline__ Aff1 compose(const Aff1& l, const Aff1& e) {
+  return Aff1{l.a * e.a, fmaf(l.a, e.b, l.b)};
+}
+__device__ __forceinline__ Aff1 aff_identity1() { return Aff1{1.0f, 0.0f}; }
+
+struct Aff2 {  // one channel of the (c, h) LSTM state: 2x2 block
+  float a00, a01, a10, a11, b0, b1;
+};
+__device__ __forceinline__ Aff2 compose(const Aff2& l, const Aff2& e) {
+  Aff2 r;
+  r.a00 = fmaf(l.a00, e.a00, l.a01 * e.a10);
+  r.a01 = fmaf(l.a00, e.a01, l.a01 * e.a11);
+  r.a10 = fmaf(l.a10, e.a00, l.a11 * e.a10);
+  r.a11 = fmaf(l.a10, e.a01, l.a11 * e.a11);
+  r.b0 = fmaf(l.a00, e.b0, fmaf(l.a01, e.b1, l.b0));
+  r.b1 = fmaf(l.a10, e.b0, fmaf(l.a11, e.b1, l.b1));
+  return r;
+}
+__device__ __forceinline__ Aff2 aff_identity2() { return Aff2{1.f, 0.f, 0.f, 1.f, 0.f, 0.f}; }
+
+// Inclusive scan over the 64 lanes of a wave, in lane order (lane 0 earliest):
+// after it, lane l holds e_l o e_{l-1} o ... o e_0.  Within each 16-lane row a
+// Hillis-Steele pass with DPP row_shr:1,2,4,8; across rows the row totals are
+// broadcast with readlane and folded in.
+__device__ __forceinline__ Aff1 shfl_row_shr_aff(const Aff1& v, const Aff1& id, int s) {
+  Aff1 o;
+  switch (s) {
+    case 1: o.a = dpp_f<0x111>(id.a, v.a); o.b = dpp_f<0x111>(id.b, v.b); break;
+    case 2: o.a = dpp_f<0x112>(id.a, v.a); o.b = dpp_f<0x112>(id.b, v.b); break;
+    case 4: o.a = dpp_f<0x114>(id.a, v.a); o.b = dpp_f<0x114>(id.b, v.b); break;
+    default: o.a = dpp_f<0x118>(id.a, v.a); o.b = dpp_f<0x118>(id.b, v.b); break;
+  }
+  return o;
+}
+__device__ __forceinline__ Aff2 shfl_row_shr_aff(const Aff2& v, const Aff2& id, int s) {
+  Aff2 o;
+#define PNR_DPP6(C)                                                     \
+  o.a00 = dpp_f<C>(id.a00, v.a00); o.a01 = dpp_f<C>(id.a01, v.a01);     \
+  o.a10 = dpp_f<C>(id.a10, v.a10); o.a11 = dpp_f<C>(id.a11, v.a11);     \
+  o.b0 = dpp_f<C>(id.b0, v.b0); o.b1 = dpp_f<C>(id.b1, v.b1);
+  switch (s) {
+    case 1: PNR_DPP6(0x111) break;
+    case 2: PNR_DPP6(0x112) break;
+    case 4: PNR_DPP6(0x114) break;
+    default: PNR_DPP6(0x118) break;
+  }
+#undef PNR_DPP6
+  return o;
+}
+__device__ __forceinline__ Aff1 readlane_aff(const Aff1& v, int l) {
+  return Aff1{readlane_f(v.a, l), readlane_f(v.b, l)};
+}
+__device__ __forceinline__ Aff2 readlane_aff(const Aff2& v, int l) {
+  return Aff2{readlane_f(v.a00, l), readlane_f(v.a01, l), readlane_f(v.a10, l),
+              readlane_f(v.a11, l), readlane_f(v.b0, l), readlane_f(v.b1, l)};
+}
+
+template <class E>
+__device__ __forceinline__ E wave_inclusive_scan(E v, const E& id) {
+#pragma unroll
+  for (int s = 1; s <= 8; s <<= 1) v = compose(v, shfl_row_shr_aff(v, id, s));
+  const int row = (int)(lane_id() >> 4);
+  E r0 = readlane_aff(v, 15), r1 = readlane_aff(v, 31), r2 = readlane_aff(v, 47);
+  E p1 = r0;
+  E p2 = compose(r1, r0);
+  E p3 = compose(r2, p2);
+  E pre = row == 1 ? p1 : (row == 2 ? p2 : p3);
+  if (row > 0) v = compose(v, pre);
+  return v;
+}
+
+// ---------------------------------------------------------------------------------
+// Look-back slots.  A slot word carries 32 value bits and the epoch (iteration + 1) that
+// wrote it, in one 64-bit word written by a single relaxed agent-scope atomic store, so a
+// reader needs no fence: a word is either from this iteration (epoch matches) or not.
+__device__ __forceinline__ void slot_put(uint64_t* w, uint32_t epoch, float v) {
+  uint64_t x = ((uint64_t)epoch << 32) | (uint64_t)__float_as_uint(v);
+  __hip_atomic_store(w, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool slot_get(const uint64_t* w, uint32_t epoch, float& v) {
+  uint64_t x = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  v = __uint_as_float((uint32_t)x);
+  return (uint32_t)(x >> 32) == epoch;
+}
+
+}  // namespace pnr

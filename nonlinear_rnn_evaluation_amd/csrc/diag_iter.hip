@@ -1,0 +1,583 @@
+// One Newton iteration for the diagonal-recurrence cells (GRU_DIAG, LSTM_DIAG), fused:
+// cell + Jacobian + residual (every step at once), residual max (wave -> LDS -> block
+// partial -> last block), and the linear solve d_t = J_t d_{t-1} + r_t as a scan of
+// affine maps (thread-serial -> wave DPP -> LDS -> decoupled look-back across tiles),
+// followed by the update s <- s + d.
+//
+// Method: ParaRNN overview page, "Technical Implementation" (Newton's Iteration: a
+// Jacobian per iteration, block lower-triangular system, Jacobian reuse; Parallel
+// Reduction: block-local reduction, results to global memory, a final block merges);
+// quasi-DEER diagonal Jacobian from "Towards Scalable and Stable Parallelization of
+// Nonlinear RNNs" (abstract).  With elementwise recurrent weights the exact Jacobian
+// of GRU_DIAG is diagonal and that of LSTM_DIAG is one 2x2 block per channel ((c, h)
+// of the same channel), so every channel is an independent row.
+//
+// Layout (time-contiguous rows): gx [B][G][D][T], states [B][S][T] with S = D (GRU) or
+// 2D (LSTM: c rows 0..D-1, h rows D..2D-1).  A row (b, d) is cut into tiles of
+// PNR_BLOCK*N steps; each thread owns N consecutive steps, loaded as float4s.
+//
+// The Jacobian is never stored.  A reused (stale) Jacobian is rebuilt from the state
+// it was taken at (Hjac), which costs one extra state read instead of a Jacobian
+// write + read.
+#include "common.h"
+#include "kernels.h"
+
+namespace pnr {
+
+template <int CELL> struct DiagCell;
+
+// ---- GRU with elementwise recurrent weights: state h, gates (r, z, n) ----------------
+template <> struct DiagCell<PNR_CELL_GRU_DIAG> {
+  static constexpr int G = 3, SP = 1;        // gates, state planes per channel
+  static constexpr int AGG_WORDS = 2, PRE_WORDS = 1;
+  using E = Aff1;
+  struct Par { float ur, uz, un, br, bz, bn; };
+  struct Vec { float v0; };                  // one state component
+  __device__ static Par load_par(const float* u, const float* bh, int D, int d) {
+    Par p;
+    p.ur = u[d]; p.uz = u[D + d]; p.un = u[2 * D + d];
+    p.br = bh ? bh[d] : 0.f; p.bz = bh ? bh[D + d] : 0.f; p.bn = bh ? bh[2 * D + d] : 0.f;
+    return p;
+  }
+  // residual at (prev p, current h) and, when want_j, the Jacobian there
+  __device__ static void eval(const Par& q, const float* g, float p, float h, int jmode,
+                              bool want_j, float& res, float& ja) {
+    float ghr = fmaf(q.ur, p, q.br), ghz = fmaf(q.uz, p, q.bz), ghn = fmaf(q.un, p, q.bn);
+    float r = sigm(g[0] + ghr), z = sigm(g[1] + ghz);
+    float n = tanh_(fmaf(r, ghn, g[2]));
+    float f = fmaf(z, p - n, n);
+    res = f - h;
+    if (want_j) {
+      if (jmode == PNR_JAC_ZERO) {
+        ja = 0.f;
+      } else {
+        float omz = 1.f - z;
+        float cn = omz * (1.f - n * n);
+        ja = z + (p - n) * z * omz * q.uz + cn * r * fmaf(ghn * (1.f - r), q.ur, q.un);
+      }
+    }
+  }
+  __device__ static float jac_only(const Par& q, const float* g, float p, int jmode) {
+    float res, ja;
+    eval(q, g, p, 0.f, jmode, true, res, ja);
+    return ja;
+  }
+};
+
+// ---- LSTM with elementwise recurrent weights: state (c, h), gates (i, f, o, g) ------
+template <> struct DiagCell<PNR_CELL_LSTM_DIAG> {
+  static constexpr int G = 4, SP = 2;
+  static constexpr int AGG_WORDS = 6, PRE_WORDS = 2;
+  using E = Aff2;
+  struct Par { float ui, uf, uo, ug, bi, bf, bo, bg; };
+  __device__ static Par load_par(const float* u, const float* bh, int D, int d) {
+    Par p;
+    p.ui = u[d]; p.uf = u[D + d]; p.uo = u[2 * D + d]; p.ug = u[3 * D + d];
+    p.bi = bh ? bh[d] : 0.f; p.bf = bh ? bh[D + d] : 0.f;
+    p.bo = bh ? bh[2 * D + d] : 0.f; p.bg = bh ? bh[3 * D + d] : 0.f;
+    return p;
+  }
+  __device__ static void eval(const Par& q, const float* gx, float cp, float hp, float c, float h,
+                              int jmode, bool want_j, float& rc, float& rh, Aff2& J) {
+    float i = sigm(gx[0] + fmaf(q.ui, hp, q.bi));
+    float f = sigm(gx[1] + fmaf(q.uf, hp, q.bf));
+    float o = sigm(gx[2] + fmaf(q.uo, hp, q.bo));
+    float g = tanh_(gx[3] + fmaf(q.ug, hp, q.bg));
+    float cn = fmaf(f, cp, i * g);
+    float tau = tanh_(cn);
+    rc = cn - c;
+    rh = o * tau - h;
+    if (want_j) {
+      if (jmode == PNR_JAC_ZERO) {
+        J = Aff2{0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      } else {
+        // c' = f c + i g:  dc'/dc = f,  dc'/dh = kappa
+        float kappa = cp * f * (1.f - f) * q.uf + g * i * (1.f - i) * q.ui + i * (1.f - g * g) * q.ug;
+        // h' = o tanh(c'):  dh'/dc = o (1 - tau^2) f,  dh'/dh = tau o (1-o) u_o + o (1 - tau^2) kappa
+        float dt = o * (1.f - tau * tau);
+        J.a00 = f;
+        J.a11 = fmaf(tau * o * (1.f - o), q.uo, dt * kappa);
+        if (jmode == PNR_JAC_DIAG) {
+          J.a01 = 0.f; J.a10 = 0.f;
+        } else {
+          J.a01 = kappa; J.a10 = dt * f;
+        }
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------------
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void load_n(const float* __restrict__ row, int tb, int T, bool vec,
+                                       int N, float* out) {
+  if (vec && tb + N <= T) {
+    const f4_t* p = reinterpret_cast<const f4_t*>(row + tb);
+    for (int v = 0; v < N / 4; ++v) {
+      f4_t x = __builtin_nontemporal_load(p + v);
+      out[4 * v] = x[0]; out[4 * v + 1] = x[1]; out[4 * v + 2] = x[2]; out[4 * v + 3] = x[3];
+    }
+  } else {
+    for (int i = 0; i < N; ++i) out[i] = (tb + i < T) ? row[tb + i] : 0.f;
+  }
+}
+__device__ __forceinline__ void store_n(float* __restrict__ row, int tb, int T, bool vec, int N,
+                                        const float* in) {
+  if (vec && tb + N <= T) {
+    f4_t* p = reinterpret_cast<f4_t*>(row + tb);
+    for (int v = 0; v < N / 4; ++v) {
+      f4_t x = {in[4 * v], in[4 * v + 1], in[4 * v + 2], in[4 * v + 3]};
+      __builtin_nontemporal_store(x, p + v);
+    }
+  } else {
+    for (int i = 0; i < N; ++i)
+      if (tb + i < T) row[tb + i] = in[i];
+  }
+}
+
+// Apply an affine map to a state increment.
+__device__ __forceinline__ float apply(const Aff1& e, float d) { return fmaf(e.a, d, e.b); }
+__device__ __forceinline__ float2 apply(const Aff2& e, float2 d) {
+  return make_float2(fmaf(e.a00, d.x, fmaf(e.a01, d.y, e.b0)), fmaf(e.a10, d.x, fmaf(e.a11, d.y, e.b1)));
+}
+
+// slot I/O for the two element kinds
+__device__ __forceinline__ void put_agg(uint64_t* s, uint32_t ep, const Aff1& e) {
+  slot_put(s, ep, e.a); slot_put(s + 1, ep, e.b);
+}
+__device__ __forceinline__ bool get_agg(const uint64_t* s, uint32_t ep, Aff1& e) {
+  bool ok = slot_get(s, ep, e.a);
+  ok &= slot_get(s + 1, ep, e.b);
+  return ok;
+}
+__device__ __forceinline__ void put_agg(uint64_t* s, uint32_t ep, const Aff2& e) {
+  slot_put(s, ep, e.a00); slot_put(s + 1, ep, e.a01); slot_put(s + 2, ep, e.a10);
+  slot_put(s + 3, ep, e.a11); slot_put(s + 4, ep, e.b0); slot_put(s + 5, ep, e.b1);
+}
+__device__ __forceinline__ bool get_agg(const uint64_t* s, uint32_t ep, Aff2& e) {
+  bool ok = slot_get(s, ep, e.a00);
+  ok &= slot_get(s + 1, ep, e.a01);
+  ok &= slot_get(s + 2, ep, e.a10);
+  ok &= slot_get(s + 3, ep, e.a11);
+  ok &= slot_get(s + 4, ep, e.b0);
+  ok &= slot_get(s + 5, ep, e.b1);
+  return ok;
+}
+__device__ __forceinline__ void put_pre(uint64_t* s, uint32_t ep, float d) { slot_put(s, ep, d); }
+__device__ __forceinline__ bool get_pre(const uint64_t* s, uint32_t ep, float& d) { return slot_get(s, ep, d); }
+__device__ __forceinline__ void put_pre(uint64_t* s, uint32_t ep, float2 d) {
+  slot_put(s, ep, d.x); slot_put(s + 1, ep, d.y);
+}
+__device__ __forceinline__ bool get_pre(const uint64_t* s, uint32_t ep, float2& d) {
+  bool ok = slot_get(s, ep, d.x);
+  ok &= slot_get(s + 1, ep, d.y);
+  return ok;
+}
+
+template <class E> struct DeltaOf;
+template <> struct DeltaOf<Aff1> { using T = float; __device__ static float zero() { return 0.f; } };
+template <> struct DeltaOf<Aff2> { using T = float2; __device__ static float2 zero() { return make_float2(0.f, 0.f); } };
+
+template <class E> __device__ __forceinline__ E identity_of();
+template <> __device__ __forceinline__ Aff1 identity_of<Aff1>() { return aff_identity1(); }
+template <> __device__ __forceinline__ Aff2 identity_of<Aff2>() { return aff_identity2(); }
+
+__device__ __forceinline__ float wave_shr1(float v, float lane0) { return dpp_f<0x138>(lane0, v); }
+__device__ __forceinline__ float2 wave_shr1(float2 v, float2 lane0) {
+  return make_float2(dpp_f<0x138>(lane0.x, v.x), dpp_f<0x138>(lane0.y, v.y));
+}
+
+// Decoupled look-back by one thread: returns the increment d entering tile `tile`.
+template <class CellT>
+__device__ typename DeltaOf<typename CellT::E>::T lookback(uint64_t* slots, int tile, int seg,
+                                                         uint32_t ep, const typename CellT::E& tot) {
+  using E = typename CellT::E;
+  using Dl = typename DeltaOf<E>::T;
+  constexpr int SW = CellT::AGG_WORDS + CellT::PRE_WORDS;
+  uint64_t* mine = slots + (size_t)tile * SW;
+  if (seg == 0) {
+    put_pre(mine + CellT::AGG_WORDS, ep, apply(tot, DeltaOf<E>::zero()));
+    return DeltaOf<E>::zero();
+  }
+  put_agg(mine, ep, tot);
+  E acc = identity_of<E>();
+  int j = tile - 1;
+  Dl din;
+  while (true) {
+    const uint64_t* s = slots + (size_t)j * SW;
+    Dl pre;
+    if (get_pre(s + CellT::AGG_WORDS, ep, pre)) {
+      din = apply(acc, pre);
+      break;
+    }
+    E agg;
+    if (get_agg(s, ep, agg)) {
+      acc = compose(acc, agg);
+      --j;
+      continue;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  put_pre(mine + CellT::AGG_WORDS, ep, apply(tot, din));
+  return din;
+}
+
+// ---------------------------------------------------------------------------------
+template <int CELL, int N, bool RESID_ONLY>
+__global__ void __launch_bounds__(PNR_BLOCK) diag_iter_kernel(DiagIterArgs a) {
+  using C = DiagCell<CELL>;
+  using E = typename C::E;
+  using Dl = typename DeltaOf<E>::T;
+  constexpr int G = C::G;
+  constexpr int TILE = PNR_BLOCK * N;
+
+  __shared__ int s_tile;
+  __shared__ E s_wtot[PNR_WAVES];
+  __shared__ Dl s_din;
+  __shared__ uint32_t s_wmax[PNR_WAVES];
+  __shared__ int s_last;
+
+  Ctrl* ctrl = a.ctrl;
+  if (__hip_atomic_load(&ctrl->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return;
+
+  const int tid = threadIdx.x;
+  const int wid = tid >> 6;
+  const int lane = tid & 63;
+  const int D = a.D, T = a.T;
+  const int S = D * C::SP;
+  const bool vec = (T & 3) == 0;
+  const uint32_t ep = (uint32_t)a.k + 1u;
+  const bool stale = (a.Hjac != a.Hcur) || a.jac_zero != a.cur_zero;
+  uint32_t blk_max = 0;
+
+  while (true) {
+    if (tid == 0) s_tile = (int)atomicAdd(&ctrl->ticket, 1u);
+    __syncthreads();
+    const int tile = s_tile;
+    if (tile >= a.n_tiles) break;
+    const int row = tile / a.tiles_per_row;      // (b, d)
+    const int seg = tile - row * a.tiles_per_row;
+    const int b = row / D, d = row - b * D;
+    const int tb = seg * TILE + tid * N;         // first step of this thread
+
+    const typename C::Par q = C::load_par(a.u, a.bh, D, d);
+    // gate pre-activations from the input projection
+    float g[G][N];
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg)
+      load_n(a.gx + ((size_t)(b * G + gg) * D + d) * T, tb, T, vec, N, g[gg]);
+
+    uint32_t tmax = 0;
+    E e[N];
+    float hc[C::SP][N];   // current state values (for the update)
+    if constexpr (CELL == PNR_CELL_GRU_DIAG) {
+      const size_t roff = ((size_t)b * S + d) * T;
+      float h[N], pj[N];
+      if (a.cur_zero) { for (int i = 0; i < N; ++i) h[i] = 0.f; }
+      else load_n(a.Hcur + roff, tb, T, vec, N, h);
+      float p0;
+      if (tb == 0) p0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
+      else p0 = (a.cur_zero || tb > T) ? 0.f : a.Hcur[roff + tb - 1];
+      if (stale && !RESID_ONLY) {
+        float pj0;
+        if (tb == 0) pj0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
+        else pj0 = (a.jac_zero || tb > T) ? 0.f : a.Hjac[roff + tb - 1];
+        float hj[N];
+        if (a.jac_zero) { for (int i = 0; i < N; ++i) hj[i] = 0.f; }
+        else load_n(a.Hjac + roff, tb, T, vec, N, hj);
+        pj[0] = pj0;
+        for (int i = 1; i < N; ++i) pj[i] = hj[i - 1];
+      }
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const float p = i == 0 ? p0 : h[i - 1];
+        float gi[3] = {g[0][i], g[1][i], g[2][i]};
+        float res, ja;
+        C::eval(q, gi, p, h[i], a.jac_mode, !stale && !RESID_ONLY, res, ja);
+        if (stale && !RESID_ONLY) ja = C::jac_only(q, gi, pj[i], a.jac_mode);
+        const bool valid = tb + i < T;
+        if (!valid) { res = 0.f; ja = 1.f; }
+        tmax = max(tmax, abs_bits(res));
+        e[i] = Aff1{ja, res};
+        hc[0][i] = h[i];
+      }
+    } else {
+      const size_t coff = ((size_t)b * S + d) * T, hoff = ((size_t)b * S + D + d) * T;
+      float c[N], h[N];
+      if (a.cur_zero) { for (int i = 0; i < N; ++i) { c[i] = 0.f; h[i] = 0.f; } }
+      else { load_n(a.Hcur + coff, tb, T, vec, N, c); load_n(a.Hcur + hoff, tb, T, vec, N, h); }
+      float cp0, hp0;
+      if (tb == 0) {
+        cp0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
+        hp0 = a.h0 ? a.h0[(size_t)b * S + D + d] : 0.f;
+      } else if (a.cur_zero || tb > T) {
+        cp0 = 0.f; hp0 = 0.f;
+      } else {
+        cp0 = a.Hcur[coff + tb - 1]; hp0 = a.Hcur[hoff + tb - 1];
+      }
+      float cj[N], hj[N], cpj0 = 0.f, hpj0 = 0.f;
+      if (stale && !RESID_ONLY) {
+        if (tb == 0) {
+          cpj0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
+          hpj0 = a.h0 ? a.h0[(size_t)b * S + D + d] : 0.f;
+        } else if (!(a.jac_zero || tb > T)) {
+          cpj0 = a.Hjac[coff + tb - 1]; hpj0 = a.Hjac[hoff + tb - 1];
+        }
+        if (a.jac_zero) { for (int i = 0; i < N; ++i) { cj[i] = 0.f; hj[i] = 0.f; } }
+        else { load_n(a.Hjac + coff, tb, T, vec, N, cj); load_n(a.Hjac + hoff, tb, T, vec, N, hj); }
+      }
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const float cp = i == 0 ? cp0 : c[i - 1];
+        const float hp = i == 0 ? hp0 : h[i - 1];
+        float gi[4] = {g[0][i], g[1][i], g[2][i], g[3][i]};
+        float rc, rh;
+        Aff2 J;
+        C::eval(q, gi, cp, hp, c[i], h[i], a.jac_mode, !stale && !RESID_ONLY, rc, rh, J);
+        if (stale && !RESID_ONLY) {
+          float dc, dh;
+          const float cpj = i == 0 ? cpj0 : cj[i - 1];
+          const float hpj = i == 0 ? hpj0 : hj[i - 1];
+          C::eval(q, gi, cpj, hpj, 0.f, 0.f, a.jac_mode, true, dc, dh, J);
+        }
+        const bool valid = tb + i < T;
+        if (!valid) { rc = 0.f; rh = 0.f; J = aff_identity2(); }
+        tmax = max(tmax, max(abs_bits(rc), abs_bits(rh)));
+        J.b0 = rc; J.b1 = rh;
+        e[i] = J;
+        hc[0][i] = c[i];
+        hc[1][i] = h[i];
+      }
+    }
+    blk_max = max(blk_max, tmax);
+    if constexpr (RESID_ONLY) {
+      __syncthreads();   // s_tile is rewritten by the next ticket
+      continue;
+    }
+
+    // ---- scan: thread-serial, then wave (DPP), then block (LDS), then look-back ----
+    E agg = e[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) agg = compose(e[i], agg);
+    const E idn = identity_of<E>();
+    E incl = wave_inclusive_scan(agg, idn);
+    if (lane == 63) s_wtot[wid] = incl;
+    __syncthreads();
+    if (tid == 0) {
+      E tot = s_wtot[0];
+      for (int w = 1; w < PNR_WAVES; ++w) tot = compose(s_wtot[w], tot);
+      s_din = lookback<C>(a.slots, tile, seg, ep, tot);
+    }
+    __syncthreads();
+    Dl dw = s_din;
+    for (int w = 0; w < wid; ++w) dw = apply(s_wtot[w], dw);
+    Dl dout = apply(incl, dw);
+    Dl dl = wave_shr1(dout, dw);   // increment entering this thread's first step
+
+    // ---- fix-up: d_t = J_t d_{t-1} + r_t along the thread's steps, s <- s + d ----
+    if constexpr (CELL == PNR_CELL_GRU_DIAG) {
+      float out[N];
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        dl = apply(e[i], dl);
+        out[i] = hc[0][i] + dl;
+      }
+      store_n(a.Hnext + ((size_t)b * S + d) * T, tb, T, vec, N, out);
+    } else {
+      float oc[N], oh[N];
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        dl = apply(e[i], dl);
+        oc[i] = hc[0][i] + dl.x;
+        oh[i] = hc[1][i] + dl.y;
+      }
+      store_n(a.Hnext + ((size_t)b * S + d) * T, tb, T, vec, N, oc);
+      store_n(a.Hnext + ((size_t)b * S + D + d) * T, tb, T, vec, N, oh);
+    }
+    __syncthreads();   // LDS (s_wtot, s_din, s_tile) is reused by the next tile
+  }
+
+  // ---- level 2 of the residual max: block partial -> global -> the last block merges ----
+  blk_max = wave_max_u32(blk_max);
+  if (lane == 0) s_wmax[wid] = blk_max;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t m = s_wmax[0];
+    for (int w = 1; w < PNR_WAVES; ++w) m = max(m, s_wmax[w]);
+    __hip_atomic_store(&a.partials[blockIdx.x], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __threadfence();
+    const uint32_t prev = atomicAdd(&ctrl->finished, 1u);
+    s_last = prev == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  uint32_t m = 0;
+  for (int i = tid; i < (int)gridDim.x; i += PNR_BLOCK)
+    m = max(m, __hip_atomic_load(&a.partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  m = wave_max_u32(m);
+  if (lane == 0) s_wmax[wid] = m;
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < PNR_WAVES; ++w) m = max(m, s_wmax[w]);
+    m = max(m, s_wmax[0]);
+    finish_iteration(ctrl, a.rho_hist, bits_to_rho(m), a.k, a.cur_buf, a.max_iters, a.tol);
+  }
+}
+
+// ---------------------------------------------------------------------------------
+template <int CELL, int N, bool R>
+static int occupancy_grid(int n_tiles, int num_cu) {
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int v = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, diag_iter_kernel<CELL, N, R>, PNR_BLOCK, 0) !=
+            hipSuccess || v < 1)
+      v = 1;
+    per_cu = v;
+  }
+  long g = (long)per_cu * num_cu;
+  if (g > kMaxGrid) g = kMaxGrid;
+  if (g > n_tiles) g = n_tiles;
+  return (int)(g < 1 ? 1 : g);
+}
+
+template <int CELL, int N>
+static hipError_t launch_cell(const DiagIterArgs& a, int num_cu, hipStream_t st, int* grid_out) {
+  int grid;
+  if (a.resid_only) {
+    grid = occupancy_grid<CELL, N, true>(a.n_tiles, num_cu);
+    hipLaunchKernelGGL((diag_iter_kernel<CELL, N, true>), dim3(grid), dim3(PNR_BLOCK), 0, st, a);
+  } else {
+    grid = occupancy_grid<CELL, N, false>(a.n_tiles, num_cu);
+    hipLaunchKernelGGL((diag_iter_kernel<CELL, N, false>), dim3(grid), dim3(PNR_BLOCK), 0, st, a);
+  }
+  if (grid_out) *grid_out = grid;
+  return hipGetLastError();
+}
+
+constexpr int kDiagN = 8;   // consecutive steps per thread (two float4 per state row)
+
+int diag_items_per_thread(int) { return kDiagN; }
+int diag_slot_words(int cell) {
+  return cell == PNR_CELL_LSTM_DIAG ? DiagCell<PNR_CELL_LSTM_DIAG>::AGG_WORDS + DiagCell<PNR_CELL_LSTM_DIAG>::PRE_WORDS
+                                    : DiagCell<PNR_CELL_GRU_DIAG>::AGG_WORDS + DiagCell<PNR_CELL_GRU_DIAG>::PRE_WORDS;
+}
+
+hipError_t launch_diag_iter(int cell, const DiagIterArgs& a, int num_cu, hipStream_t st, int* grid_out) {
+  if (cell == PNR_CELL_GRU_DIAG) return launch_cell<PNR_CELL_GRU_DIAG, kDiagN>(a, num_cu, st, grid_out);
+  return launch_cell<PNR_CELL_LSTM_DIAG, kDiagN>(a, num_cu, st, grid_out);
+}
+
+// ---------------------------------------------------------------------------------
+// Standalone scan d_t = A_t d_{t-1} + b_t over R independent rows: the same thread /
+// wave / block / look-back machinery as the fused iteration, with the elements read
+// from memory.  KIND 1: A, b, d are [R][T]; KIND 2: A [R][4][T], b and d [R][2][T].
+struct ScanArgs {
+  const float* A; const float* b; float* d;
+  uint64_t* slots; Ctrl* ctrl;
+  int R, T, tiles_per_row, n_tiles;
+};
+
+template <int KIND, int N>
+__global__ void __launch_bounds__(PNR_BLOCK) scan_kernel(ScanArgs a) {
+  using C = DiagCell<KIND == 1 ? PNR_CELL_GRU_DIAG : PNR_CELL_LSTM_DIAG>;
+  using E = typename C::E;
+  using Dl = typename DeltaOf<E>::T;
+  constexpr int TILE = PNR_BLOCK * N;
+  __shared__ int s_tile;
+  __shared__ E s_wtot[PNR_WAVES];
+  __shared__ Dl s_din;
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int T = a.T;
+  while (true) {
+    if (tid == 0) s_tile = (int)atomicAdd(&a.ctrl->ticket, 1u);
+    __syncthreads();
+    const int tile = s_tile;
+    if (tile >= a.n_tiles) break;
+    const int row = tile / a.tiles_per_row, seg = tile - row * a.tiles_per_row;
+    const int tb = seg * TILE + tid * N;
+    E e[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int t = tb + i;
+      if (t < T) {
+        if constexpr (KIND == 1) {
+          e[i] = Aff1{a.A[(size_t)row * T + t], a.b[(size_t)row * T + t]};
+        } else {
+          const float* Ar = a.A + (size_t)row * 4 * T;
+          const float* br = a.b + (size_t)row * 2 * T;
+          e[i] = Aff2{Ar[t], Ar[T + t], Ar[2 * T + t], Ar[3 * T + t], br[t], br[T + t]};
+        }
+      } else {
+        e[i] = identity_of<E>();
+      }
+    }
+    E agg = e[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) agg = compose(e[i], agg);
+    E incl = wave_inclusive_scan(agg, identity_of<E>());
+    if (lane == 63) s_wtot[wid] = incl;
+    __syncthreads();
+    if (tid == 0) {
+      E tot = s_wtot[0];
+      for (int w = 1; w < PNR_WAVES; ++w) tot = compose(s_wtot[w], tot);
+      s_din = lookback<C>(a.slots, tile, seg, 1u, tot);
+    }
+    __syncthreads();
+    Dl dw = s_din;
+    for (int w = 0; w < wid; ++w) dw = apply(s_wtot[w], dw);
+    Dl dl = wave_shr1(apply(incl, dw), dw);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      dl = apply(e[i], dl);
+      const int t = tb + i;
+      if (t < T) {
+        if constexpr (KIND == 1) {
+          a.d[(size_t)row * T + t] = dl;
+        } else {
+          a.d[(size_t)row * 2 * T + t] = dl.x;
+          a.d[(size_t)row * 2 * T + T + t] = dl.y;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+int scan_default_tile(int) { return PNR_BLOCK * kDiagN; }
+int scan_slot_words(int kind) { return diag_slot_words(kind == 1 ? PNR_CELL_GRU_DIAG : PNR_CELL_LSTM_DIAG); }
+
+template <int KIND, int N>
+static hipError_t launch_scan_n(const ScanArgs& a, int num_cu, hipStream_t st) {
+  int v = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, scan_kernel<KIND, N>, PNR_BLOCK, 0) != hipSuccess || v < 1)
+    v = 1;
+  long g = (long)v * num_cu;
+  if (g > kMaxGrid) g = kMaxGrid;
+  if (g > a.n_tiles) g = a.n_tiles;
+  if (g < 1) g = 1;
+  hipLaunchKernelGGL((scan_kernel<KIND, N>), dim3((int)g), dim3(PNR_BLOCK), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(int kind, int R, int T, const float* A, const float* b, float* d, int tile_len,
+                       uint64_t* slots, Ctrl* ctrl, int num_cu, hipStream_t st) {
+  const int n = tile_len / PNR_BLOCK;
+  ScanArgs a{A, b, d, slots, ctrl, R, T, (T + tile_len - 1) / tile_len, 0};
+  a.n_tiles = R * a.tiles_per_row;
+  if (a.n_tiles == 0) return hipSuccess;
+#define PNR_SCAN_CASE(NN) \
+  case NN: return kind == 1 ? launch_scan_n<1, NN>(a, num_cu, st) : launch_scan_n<2, NN>(a, num_cu, st);
+  switch (n) {
+    PNR_SCAN_CASE(1)
+    PNR_SCAN_CASE(2)
+    PNR_SCAN_CASE(4)
+    PNR_SCAN_CASE(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef PNR_SCAN_CASE
+}
+
+}  // namespace pnr

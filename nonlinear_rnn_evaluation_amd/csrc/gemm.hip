@@ -1,0 +1,193 @@
+// Input projection, computed once per call: gx = W x + b_x for every step.  Each step
+// depends only on its input and the previous state (ParaRNN overview page, "Newton's
+// Iteration"), so the input half of every gate pre-activation is one dense product over
+// all steps -- a plain GEMM, done before the Newton loop.
+//
+//   C[z][i][j] = sum_k A[z][i][k] * Bm[z][j][k] + bias[i or j]      (fp32 or fp64 out)
+//
+// Both operands are K-contiguous.  bf16 inputs run on MFMA (v_mfma_f32_32x32x16_bf16,
+// fp32 accumulate); fp32/fp64 inputs use an LDS-tiled VALU kernel (the dense-GRU
+// projections are a few GFLOP).
+#include "common.h"
+#include "kernels.h"
+
+namespace pnr {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16_t;
+
+// ---------------------------------------------------------------------------------
+// bf16 MFMA GEMM.  Block tile 128 x 128, K step 32, 256 threads = 4 waves in 2 x 2,
+// each wave 64 x 64 = 2 x 2 MFMA tiles of 32 x 32.  LDS double buffered; rows padded
+// by 8 bf16 to spread ds_read_b128 over banks.
+constexpr int GB_M = 128, GB_N = 128, GB_K = 32, GB_LD = GB_K + 8;
+
+__global__ void __launch_bounds__(256) gemm_bf16_mfma(GemmArgs g) {
+  __shared__ __align__(16) __bf16 As[2][GB_M * GB_LD];
+  __shared__ __align__(16) __bf16 Bs[2][GB_N * GB_LD];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  const int z = blockIdx.z;
+  const int i0 = blockIdx.y * GB_M, j0 = blockIdx.x * GB_N;
+  const __bf16* A = reinterpret_cast<const __bf16*>(g.A) + (size_t)z * g.sA;
+  const __bf16* Bm = reinterpret_cast<const __bf16*>(g.Bm) + (size_t)z * g.sB;
+  float* C = reinterpret_cast<float*>(g.C) + (size_t)z * g.sC;
+
+  // global -> register staging: each thread moves 2 x 16 B of A and of B per K step
+  const int lr = tid >> 2;          // 0..63
+  const int lk = (tid & 3) * 8;     // 0, 8, 16, 24
+  uint4 ra[2], rb[2];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = lr + 64 * h;
+      const int ia = i0 + r, jb = j0 + r, kk = k0 + lk;
+      uint4 va = make_uint4(0, 0, 0, 0), vb = make_uint4(0, 0, 0, 0);
+      if (ia < g.M && kk < g.K) va = *reinterpret_cast<const uint4*>(A + (size_t)ia * g.lda + kk);
+      if (jb < g.N && kk < g.K) vb = *reinterpret_cast<const uint4*>(Bm + (size_t)jb * g.ldb + kk);
+      ra[h] = va; rb[h] = vb;
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = lr + 64 * h;
+      *reinterpret_cast<uint4*>(&As[buf][r * GB_LD + lk]) = ra[h];
+      *reinterpret_cast<uint4*>(&Bs[buf][r * GB_LD + lk]) = rb[h];
+    }
+  };
+
+  floatx16_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+  const int nk = (g.K + GB_K - 1) / GB_K;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * GB_K);
+#pragma unroll
+    for (int ks = 0; ks < GB_K / 16; ++ks) {
+      bf16x8_t fa[2], fb[2];
+      const int kofs = ks * 16 + (lane >> 5) * 8;
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        const int r = wm * 64 + mi * 32 + (lane & 31);
+        fa[mi] = *reinterpret_cast<const bf16x8_t*>(&As[buf][r * GB_LD + kofs]);
+      }
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const int r = wn * 64 + ni * 32 + (lane & 31);
+        fb[ni] = *reinterpret_cast<const bf16x8_t*>(&Bs[buf][r * GB_LD + kofs]);
+      }
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+    }
+    if (kt + 1 < nk) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds column (lane & 31) and rows 8*q + 4*(lane >> 5) + e
+  const float* bias = reinterpret_cast<const float*>(g.bias);
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+      const int j = j0 + wn * 64 + ni * 32 + (lane & 31);
+      if (j >= g.N) continue;
+      const float bj = (bias && !g.bias_on_i) ? bias[j] : 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = i0 + wm * 64 + mi * 32 + 8 * q + 4 * (lane >> 5) + e;
+          if (i < g.M) {
+            const float bi = (bias && g.bias_on_i) ? bias[i] : 0.f;
+            __builtin_nontemporal_store(acc[mi][ni][4 * q + e] + bi + bj, &C[(size_t)i * g.ldc + j]);
+          }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// Generic LDS-tiled GEMM: 64 x 64 block tile, K step 16, 256 threads with 4 x 4 outputs.
+template <typename Tin> __device__ __forceinline__ float to_acc(Tin v, float) { return (float)v; }
+template <typename Tin> __device__ __forceinline__ double to_acc(Tin v, double) { return (double)v; }
+__device__ __forceinline__ float to_acc(__bf16 v, float) { return (float)v; }
+
+template <typename Tin, typename Tout>
+__global__ void __launch_bounds__(256) gemm_generic(GemmArgs g) {
+  __shared__ Tout As[16][64 + 1];
+  __shared__ Tout Bs[16][64 + 1];
+  const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;
+  const int z = blockIdx.z;
+  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  const Tin* A = reinterpret_cast<const Tin*>(g.A) + (size_t)z * g.sA;
+  const Tin* Bm = reinterpret_cast<const Tin*>(g.Bm) + (size_t)z * g.sB;
+  Tout* C = reinterpret_cast<Tout*>(g.C) + (size_t)z * g.sC;
+  Tout acc[4][4];
+  for (int a = 0; a < 4; ++a)
+    for (int b = 0; b < 4; ++b) acc[a][b] = Tout(0);
+  for (int k0 = 0; k0 < g.K; k0 += 16) {
+    for (int e = tid; e < 64 * 16; e += 256) {
+      const int r = e >> 4, kk = e & 15;
+      const int ia = i0 + r, jb = j0 + r, k = k0 + kk;
+      As[kk][r] = (ia < g.M && k < g.K) ? to_acc(A[(size_t)ia * g.lda + k], Tout(0)) : Tout(0);
+      Bs[kk][r] = (jb < g.N && k < g.K) ? to_acc(Bm[(size_t)jb * g.ldb + k], Tout(0)) : Tout(0);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      Tout av[4], bv[4];
+      for (int a = 0; a < 4; ++a) av[a] = As[kk][ty * 4 + a];
+      for (int b = 0; b < 4; ++b) bv[b] = Bs[kk][tx + 16 * b];
+      for (int a = 0; a < 4; ++a)
+        for (int b = 0; b < 4; ++b) acc[a][b] += av[a] * bv[b];
+    }
+    __syncthreads();
+  }
+  const Tout* bias = reinterpret_cast<const Tout*>(g.bias);
+  for (int a = 0; a < 4; ++a) {
+    const int i = i0 + ty * 4 + a;
+    if (i >= g.M) continue;
+    for (int b = 0; b < 4; ++b) {
+      const int j = j0 + tx + 16 * b;
+      if (j >= g.N) continue;
+      Tout v = acc[a][b];
+      if (bias) v += g.bias_on_i ? bias[i] : bias[j];
+      C[(size_t)i * g.ldc + j] = v;
+    }
+  }
+}
+
+hipError_t launch_gemm(int in_dtype, int out_dtype, const GemmArgs& g, hipStream_t st) {
+  if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
+  if (in_dtype == PNR_BF16 && out_dtype == PNR_F32 && (g.K % 8) == 0 && (g.lda % 8) == 0 &&
+      (g.ldb % 8) == 0 && (g.sA % 8) == 0 && (g.sB % 8) == 0) {
+    dim3 grid((g.N + GB_N - 1) / GB_N, (g.M + GB_M - 1) / GB_M, g.batch);
+    hipLaunchKernelGGL(gemm_bf16_mfma, grid, dim3(256), 0, st, g);
+    return hipGetLastError();
+  }
+  dim3 grid((g.N + 63) / 64, (g.M + 63) / 64, g.batch);
+  if (in_dtype == PNR_BF16 && out_dtype == PNR_F32)
+    hipLaunchKernelGGL((gemm_generic<__bf16, float>), grid, dim3(256), 0, st, g);
+  else if (in_dtype == PNR_F32 && out_dtype == PNR_F32)
+    hipLaunchKernelGGL((gemm_generic<float, float>), grid, dim3(256), 0, st, g);
+  else if (in_dtype == PNR_F64 && out_dtype == PNR_F64)
+    hipLaunchKernelGGL((gemm_generic<double, double>), grid, dim3(256), 0, st, g);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace pnr

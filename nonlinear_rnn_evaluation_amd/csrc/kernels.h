@@ -1,0 +1,129 @@
+// Internal launch interface between the host driver and the HIP kernels of libpnr.
+#pragma once
+
+#include "common.h"
+
+namespace pnr {
+
+// Upper bound on the grid of any persistent iteration kernel (sizes the partials array).
+constexpr int kMaxGrid = 16384;
+
+// ---------------------------------------------------------------------------------
+// Decision taken by the block that merges the residual partials of iteration k (the
+// "final block" of the two-level reduction): record rho_k and stop when it is within
+// tol, not finite, or when k is the residual-only pass after max_iters updates.
+__device__ inline void finish_iteration(Ctrl* c, double* hist, double rho, int k, int cur_buf,
+                                        int max_iters, double tol) {
+  hist[k] = rho;
+  c->rho = rho;
+  int done = 0, status = PNR_NOT_CONVERGED;
+  if (!(rho < __builtin_inf())) {
+    done = 1; status = PNR_NONFINITE;
+  } else if (rho <= tol) {
+    done = 1; status = PNR_OK;
+  } else if (k >= max_iters) {
+    done = 1; status = PNR_NOT_CONVERGED;
+  }
+  if (done) {
+    c->status = status;
+    c->iters = k;
+    c->result_buf = cur_buf;
+    c->done = 1;
+  }
+  c->ticket = 0;
+  c->finished = 0;
+}
+
+// ---------------------------------------------------------------------------------
+struct DiagIterArgs {
+  const float* gx;     // [B][G][D][T]
+  const float* u;      // [G][D]
+  const float* bh;     // [G*D] or nullptr
+  const float* h0;     // [B][S] or nullptr
+  const float* Hcur;   // [B][S][T]
+  const float* Hjac;   // [B][S][T]: the state the Jacobian is taken at (== Hcur when fresh)
+  float* Hnext;        // [B][S][T]
+  uint64_t* slots;     // look-back slots, n_tiles * slot words
+  uint32_t* partials;  // per-block residual maxima
+  Ctrl* ctrl;
+  double* rho_hist;
+  int cur_zero;        // Hcur is the zero initial guess (not read)
+  int jac_zero;        // Hjac is the zero initial guess
+  int B, D, T;
+  int tiles_per_row;
+  int n_tiles;
+  int k;
+  int cur_buf;
+  int max_iters;
+  double tol;
+  int jac_mode;
+  int resid_only;
+};
+
+int diag_items_per_thread(int cell);
+int diag_slot_words(int cell);
+hipError_t launch_diag_iter(int cell, const DiagIterArgs& a, int num_cu, hipStream_t st, int* grid_out);
+
+// ---------------------------------------------------------------------------------
+template <typename Tt>
+struct DenseIterArgs {
+  const Tt* gx;        // [B][T][3D]
+  const Tt* U;         // [3D][D]
+  const Tt* bh;        // [3D] or nullptr
+  const Tt* h0;        // [B][D] or nullptr
+  const Tt* Hcur;      // [B][T][D]
+  const Tt* Hjac;
+  Tt* Hnext;
+  uint64_t* slots;
+  uint64_t* partials;
+  Ctrl* ctrl;
+  double* rho_hist;
+  int cur_zero, jac_zero;
+  int B, D, T;
+  int L;               // steps per tile
+  int tiles_per_row;
+  int n_tiles;
+  int k, cur_buf, max_iters;
+  double tol;
+  int jac_mode;
+  int resid_only;
+};
+
+// Tile length and look-back slot words per tile for the dense GRU path.
+int dense_tile_len(int D, int full, int is_f64);
+int dense_slot_words(int D, int full, int is_f64);
+size_t dense_lds_bytes(int D, int full, int is_f64, int stale);
+int dense_supported(int D, int full, int is_f64);
+hipError_t launch_dense_iter_f32(const DenseIterArgs<float>& a, int full, int num_cu, hipStream_t st);
+hipError_t launch_dense_iter_f64(const DenseIterArgs<double>& a, int full, int num_cu, hipStream_t st);
+
+// ---------------------------------------------------------------------------------
+// Input projection C[z][i][j] = sum_k A[z][i][k] * Bm[z][j][k] + bias, both operands
+// K-contiguous; bias indexed by i (bias_on_i) or j.  C row-major with leading dim ldc.
+struct GemmArgs {
+  const void* A; const void* Bm; const void* bias; void* C;
+  int M, N, K;
+  long long sA, sB, sC;   // batch strides in elements (0 = shared)
+  int lda, ldb, ldc;
+  int batch;
+  int bias_on_i;
+};
+hipError_t launch_gemm(int in_dtype, int out_dtype, const GemmArgs& g, hipStream_t st);
+
+// ---------------------------------------------------------------------------------
+// Misc: control/slot initialisation and the output layout conversion.
+hipError_t launch_init(Ctrl* ctrl, uint64_t* slots, size_t slot_words, hipStream_t st);
+// diag layout [B][S][T] -> h_out [B][T][S] (or zeros when the result is the zero guess)
+hipError_t launch_diag_output(const float* const* bufs, const Ctrl* ctrl, float* h_out, int B, int S,
+                              int T, hipStream_t st);
+template <typename Tt>
+hipError_t launch_dense_output(const Tt* const* bufs, const Ctrl* ctrl, Tt* h_out, size_t n,
+                               hipStream_t st);
+
+// Standalone scan (testing entry point)
+hipError_t launch_scan(int kind, int R, int T, const float* A, const float* b, float* d, int tile_len,
+                       uint64_t* slots, Ctrl* ctrl, int num_cu, hipStream_t st);
+int scan_default_tile(int kind);
+int scan_slot_words(int kind);
+
+}  // namespace pnr

@@ -1,0 +1,86 @@
+// Small kernels around the Newton loop: per-call initialisation of the control block
+// and look-back slots, and the conversion of the returned iterate to the caller's
+// [B, T, S] layout.
+#include "common.h"
+#include "kernels.h"
+
+namespace pnr {
+
+__global__ void init_kernel(Ctrl* ctrl, uint64_t* slots, size_t n) {
+  const size_t i0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i0 == 0) {
+    ctrl->done = 0;
+    ctrl->status = PNR_NOT_CONVERGED;
+    ctrl->iters = -1;
+    ctrl->result_buf = -1;
+    ctrl->rho = 0.0;
+    ctrl->ticket = 0;
+    ctrl->finished = 0;
+  }
+  // epoch 0 is never a live epoch, so zeroed words read as "not yet written"
+  for (size_t i = i0; i < n; i += (size_t)gridDim.x * blockDim.x) slots[i] = 0;
+}
+
+hipError_t launch_init(Ctrl* ctrl, uint64_t* slots, size_t slot_words, hipStream_t st) {
+  size_t blocks = (slot_words + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(init_kernel, dim3((unsigned)blocks), dim3(256), 0, st, ctrl, slots, slot_words);
+  return hipGetLastError();
+}
+
+struct Bufs3f { const float* p[3]; };
+
+// [B][S][T] -> [B][T][S] through a 32 x 32 LDS tile; zeros when the result is the zero guess.
+__global__ void __launch_bounds__(256) diag_output_kernel(Bufs3f bufs, const Ctrl* ctrl, float* out, int S,
+                                                          int T) {
+  __shared__ float tile[32][33];
+  const int rb = ctrl->result_buf;
+  const float* src = rb >= 0 ? bufs.p[rb] : nullptr;
+  const int b = blockIdx.z;
+  const int t0 = blockIdx.x * 32, s0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8
+  for (int r = ty; r < 32; r += 8) {
+    const int s = s0 + r, t = t0 + tx;
+    float v = 0.f;
+    if (src && s < S && t < T) v = src[((size_t)b * S + s) * T + t];
+    tile[r][tx] = v;
+  }
+  __syncthreads();
+  for (int r = ty; r < 32; r += 8) {
+    const int t = t0 + r, s = s0 + tx;
+    if (t < T && s < S) out[((size_t)b * T + t) * S + s] = tile[tx][r];
+  }
+}
+
+hipError_t launch_diag_output(const float* const* bufs, const Ctrl* ctrl, float* h_out, int B, int S, int T,
+                              hipStream_t st) {
+  Bufs3f bb{{bufs[0], bufs[1], bufs[2]}};
+  dim3 grid((T + 31) / 32, (S + 31) / 32, B);
+  hipLaunchKernelGGL(diag_output_kernel, grid, dim3(256), 0, st, bb, ctrl, h_out, S, T);
+  return hipGetLastError();
+}
+
+template <typename Tt> struct Bufs3 { const Tt* p[3]; };
+
+template <typename Tt>
+__global__ void dense_output_kernel(Bufs3<Tt> bufs, const Ctrl* ctrl, Tt* out, size_t n) {
+  const int rb = ctrl->result_buf;
+  const Tt* src = rb >= 0 ? bufs.p[rb] : nullptr;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    out[i] = src ? src[i] : Tt(0);
+}
+
+template <typename Tt>
+hipError_t launch_dense_output(const Tt* const* bufs, const Ctrl* ctrl, Tt* h_out, size_t n, hipStream_t st) {
+  Bufs3<Tt> bb{{bufs[0], bufs[1], bufs[2]}};
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL((dense_output_kernel<Tt>), dim3((unsigned)blocks), dim3(256), 0, st, bb, ctrl, h_out, n);
+  return hipGetLastError();
+}
+template hipError_t launch_dense_output<float>(const float* const*, const Ctrl*, float*, size_t, hipStream_t);
+template hipError_t launch_dense_output<double>(const double* const*, const Ctrl*, double*, size_t, hipStream_t);
+
+}  // namespace pnr

@@ -1,0 +1,186 @@
+"""ctypes binding of libpnr (include/pnr.h): argument marshalling only.
+
+Every step of the evaluation runs in the HIP library; this module turns torch tensors
+into device pointers and the C structs, passes torch's current stream, and allocates
+the output and workspace tensors (PyTorch is used only for device memory and streams).
+If ``libpnr.so`` has not been built, loading raises -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpnr.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "pnr.h")
+
+CELL_GRU, CELL_GRU_DIAG, CELL_LSTM_DIAG = 0, 1, 2
+JAC_FULL, JAC_DIAG, JAC_ZERO = 0, 1, 2
+F64, F32, BF16 = 0, 1, 2
+OK, NOT_CONVERGED, NONFINITE = 0, 1, 2
+E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP = -1, -2, -3, -4
+
+_DT = {torch.float64: F64, torch.float32: F32, torch.bfloat16: BF16}
+
+
+class PnrCell(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("D", ctypes.c_int32), ("D_in", ctypes.c_int32),
+                ("T", ctypes.c_int32), ("B", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
+                ("state_dtype", ctypes.c_int32), ("jac_every", ctypes.c_int32),
+                ("stream", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+class PnrParams(ctypes.Structure):
+    _fields_ = [("W", ctypes.c_void_p), ("U", ctypes.c_void_p), ("b_x", ctypes.c_void_p),
+                ("b_h", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libpnr.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libpnr.so not found at {LIB_PATH}; build it with "
+                           "`python -m nonlinear_rnn_evaluation_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    lib.pnr_workspace_bytes.argtypes = [P(PnrCell), ctypes.c_int]
+    lib.pnr_workspace_bytes.restype = ctypes.c_size_t
+    lib.pnr_eval.argtypes = [P(PnrCell), P(PnrParams), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                             ctypes.c_int, ctypes.c_double, ctypes.c_int]
+    lib.pnr_eval.restype = ctypes.c_int
+    lib.pnr_iters_used.argtypes = []
+    lib.pnr_iters_used.restype = ctypes.c_int
+    lib.pnr_last_residual.argtypes = []
+    lib.pnr_last_residual.restype = ctypes.c_double
+    lib.pnr_last_residual_history.argtypes = [P(ctypes.c_double), ctypes.c_int]
+    lib.pnr_last_residual_history.restype = ctypes.c_int
+    lib.pnr_last_error.argtypes = []
+    lib.pnr_last_error.restype = ctypes.c_char_p
+    lib.pnr_scan_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.pnr_scan_workspace_bytes.restype = ctypes.c_size_t
+    lib.pnr_scan.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                             ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.pnr_scan.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def header_functions() -> list:
+    """Names of the functions declared in include/pnr.h."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"\b(pnr_[a-z_]+)\s*\(", text)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libpnr takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libpnr takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def make_cell(kind: int, D: int, D_in: int, T: int, B: int, x_dtype: int, state_dtype: int,
+              jac_every: int = 1, stream: Optional[int] = None, workspace: Optional[int] = None,
+              workspace_bytes: int = 0) -> PnrCell:
+    return PnrCell(kind, D, D_in, T, B, x_dtype, state_dtype, jac_every, stream, workspace, workspace_bytes)
+
+
+# ---- the C entry points under their own names ------------------------------------------
+def pnr_workspace_bytes(cell: PnrCell, jac_mode: int) -> int:
+    return load().pnr_workspace_bytes(ctypes.byref(cell), jac_mode)
+
+
+def pnr_eval(cell: PnrCell, params: PnrParams, x: int, h0: Optional[int], h_out: int, max_iters: int,
+             tol: float, jac_mode: int) -> int:
+    return load().pnr_eval(ctypes.byref(cell), ctypes.byref(params), x, h0, h_out, max_iters, tol, jac_mode)
+
+
+def pnr_iters_used() -> int:
+    return load().pnr_iters_used()
+
+
+def pnr_last_residual() -> float:
+    return load().pnr_last_residual()
+
+
+def pnr_last_residual_history() -> list:
+    lib = load()
+    n = lib.pnr_last_residual_history(None, 0)
+    buf = (ctypes.c_double * max(n, 1))()
+    lib.pnr_last_residual_history(buf, n)
+    return list(buf[:n])
+
+
+def pnr_last_error() -> str:
+    return load().pnr_last_error().decode()
+
+
+def pnr_scan_workspace_bytes(kind: int, R: int, T: int, tile_len: int = 0) -> int:
+    return load().pnr_scan_workspace_bytes(kind, R, T, tile_len)
+
+
+def pnr_scan(kind: int, R: int, T: int, A: int, b: int, d: int, tile_len: int, workspace: int,
+             workspace_bytes: int, stream: Optional[int]) -> int:
+    return load().pnr_scan(kind, R, T, A, b, d, tile_len, workspace, workspace_bytes, stream)
+
+
+# ---- torch-level conveniences (allocation + marshalling) ---------------------------------
+class PnrError(RuntimeError):
+    pass
+
+
+def evaluate(kind: int, W: torch.Tensor, U: torch.Tensor, x: torch.Tensor, *, b_x=None, b_h=None,
+             h0=None, max_iters: int = 64, tol: float = 1e-5, jac_mode: int = JAC_FULL,
+             jac_every: int = 1, h_out: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None) -> dict:
+    """Run pnr_eval on device tensors; returns dict(h=[B,T,S], status, iters, residual, history)."""
+    B, T, D_in = x.shape
+    D = U.shape[1]
+    S = 2 * D if kind == CELL_LSTM_DIAG else D
+    xdt, sdt = _DT[x.dtype], _DT[U.dtype]
+    cell = make_cell(kind, D, D_in, T, B, xdt, sdt, jac_every, _stream())
+    need = pnr_workspace_bytes(cell, jac_mode)
+    if need == 0:
+        raise PnrError(pnr_last_error())
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    cell.workspace = workspace.data_ptr()
+    cell.workspace_bytes = workspace.numel()
+    if h_out is None:
+        h_out = torch.empty(B, T, S, dtype=U.dtype, device=x.device)
+    params = PnrParams(_ptr(W), _ptr(U), _ptr(b_x), _ptr(b_h))
+    rc = pnr_eval(cell, params, _ptr(x), _ptr(h0), _ptr(h_out), max_iters, tol, jac_mode)
+    if rc < 0:
+        raise PnrError(f"pnr_eval returned {rc}: {pnr_last_error()}")
+    return {"h": h_out, "status": rc, "iters": pnr_iters_used(), "residual": pnr_last_residual(),
+            "history": pnr_last_residual_history(), "workspace": workspace}
+
+
+def scan(kind: int, A: torch.Tensor, b: torch.Tensor, tile_len: int = 0) -> torch.Tensor:
+    """Standalone linear scan d_t = A_t d_{t-1} + b_t (kind 1: [R,T]; kind 2: A [R,4,T], b [R,2,T])."""
+    R, T = b.shape[0], b.shape[-1]
+    d = torch.empty_like(b)
+    need = pnr_scan_workspace_bytes(kind, R, T, tile_len)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=b.device)
+    rc = pnr_scan(kind, R, T, _ptr(A), _ptr(b), _ptr(d), tile_len, ws.data_ptr(), ws.numel(), _stream())
+    if rc < 0:
+        raise PnrError(f"pnr_scan returned {rc}: {pnr_last_error()}")
+    return d

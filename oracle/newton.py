@@ -32,6 +32,7 @@ from __future__ import annotations
 import numpy as np
 
 from .cells import approx_jacobian, cell_jacobian, cell_step
+from .scan import scan_loop
 from .sequential import project
 
 STATUS_OK = 0
@@ -55,8 +56,13 @@ def _previous_states(h0, H):
 
 
 def newton_dense(cell: int, W, U, b_x, b_h, x, h0, max_iters: int, tol: float,
-                 jac_mode: int, jac_every: int = 1, gx=None):
-    """Returns dict(states [B,T,S], iters, status, rhos[list], jac_evals)."""
+                 jac_mode: int, jac_every: int = 1, gx=None, solver: str = "dense"):
+    """Returns dict(states [B,T,S], iters, status, rhos[list], jac_evals).
+
+    solver="dense" assembles the block-bidiagonal matrix and calls LAPACK (only for
+    T*S up to a few thousand); solver="loop" solves the same system by forward
+    substitution (``scan_loop``), which the tests pin to the dense solve.
+    """
     if jac_every < 1:
         raise ValueError("jac_every must be >= 1")
     U = np.asarray(U, dtype=np.float64)
@@ -89,6 +95,9 @@ def newton_dense(cell: int, W, U, b_x, b_h, x, h0, max_iters: int, tol: float,
             Jhat = approx_jacobian(J, jac_mode).reshape(B, T, S, S)
             jac_evals += 1
         for b in range(B):
+            if solver == "loop":
+                H[b] = H[b] + scan_loop(Jhat[b], r[b])
+                continue
             A = np.eye(T * S)
             for t in range(1, T):
                 A[t * S:(t + 1) * S, (t - 1) * S:t * S] = -Jhat[b, t]

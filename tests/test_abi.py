@@ -1,0 +1,98 @@
+"""C-ABI checks that need no GPU: the library loads, exports what include/pnr.h declares,
+and rejects bad requests before touching HIP (no compute call is made here)."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+from nonlinear_rnn_evaluation_amd import pnr
+
+pytestmark = pytest.mark.skipif(not os.path.exists(pnr.LIB_PATH), reason="libpnr.so not built")
+
+
+def test_library_exports_every_declared_function():
+    lib = pnr.load()
+    names = pnr.header_functions()
+    assert {"pnr_eval", "pnr_iters_used", "pnr_workspace_bytes", "pnr_last_residual",
+            "pnr_last_error", "pnr_scan"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", pnr.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    assert set(names) <= exported
+
+
+def _cell(**kw):
+    base = dict(kind=pnr.CELL_GRU_DIAG, D=64, D_in=32, T=1000, B=2, x_dtype=pnr.F32, state_dtype=pnr.F32,
+                jac_every=1)
+    base.update(kw)
+    return pnr.make_cell(**base)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(kind=7), pnr.E_INVALID),
+    (dict(D=0), pnr.E_INVALID),
+    (dict(B=0), pnr.E_INVALID),
+    (dict(T=-1), pnr.E_INVALID),
+    (dict(jac_every=0), pnr.E_INVALID),
+    (dict(x_dtype=9), pnr.E_INVALID),
+    (dict(x_dtype=pnr.F64, state_dtype=pnr.F64), pnr.E_UNSUPPORTED),
+    (dict(kind=pnr.CELL_GRU, D=48), pnr.E_UNSUPPORTED),          # dense Jacobian needs D <= 32
+    (dict(kind=pnr.CELL_GRU, x_dtype=pnr.BF16, state_dtype=pnr.F64), pnr.E_UNSUPPORTED),
+])
+def test_invalid_requests_are_rejected_without_a_gpu(bad, code):
+    cell = _cell(**bad)
+    assert pnr.pnr_workspace_bytes(cell, pnr.JAC_FULL) == 0
+    assert pnr.pnr_last_error() != ""
+    params = pnr.PnrParams(1024, 2048, None, None)
+    rc = pnr.pnr_eval(cell, params, 4096, None, 8192, 10, 1e-5, pnr.JAC_FULL)
+    assert rc == code, pnr.pnr_last_error()
+    assert pnr.pnr_iters_used() == -1
+
+
+def test_argument_errors_before_any_hip_call():
+    cell = _cell()
+    need = pnr.pnr_workspace_bytes(cell, pnr.JAC_FULL)
+    assert need > 0
+    params = pnr.PnrParams(1024, 2048, None, None)
+    assert pnr.pnr_eval(cell, params, None, None, 8192, 10, 1e-5, pnr.JAC_FULL) == pnr.E_INVALID
+    assert pnr.pnr_eval(cell, params, 4096, None, 8192, 10, 1e-5, 5) == pnr.E_INVALID
+    assert pnr.pnr_eval(cell, params, 4096, None, 8192, -1, 1e-5, pnr.JAC_FULL) == pnr.E_INVALID
+    assert pnr.pnr_eval(cell, params, 4096, None, 8192, 10, float("nan"), pnr.JAC_FULL) == pnr.E_INVALID
+    # workspace: missing, misaligned, too small
+    assert pnr.pnr_eval(cell, params, 4096, None, 8192, 10, 1e-5, pnr.JAC_FULL) == pnr.E_WORKSPACE
+    cell.workspace, cell.workspace_bytes = 4096 + 8, need
+    assert pnr.pnr_eval(cell, params, 4096, None, 8192, 10, 1e-5, pnr.JAC_FULL) == pnr.E_WORKSPACE
+    cell.workspace, cell.workspace_bytes = 4096, need - 1
+    assert pnr.pnr_eval(cell, params, 4096, None, 8192, 10, 1e-5, pnr.JAC_FULL) == pnr.E_WORKSPACE
+    assert "required" in pnr.pnr_last_error()
+    # T == 0 is a valid, empty problem: no device work, converged with zero updates
+    cell = _cell(T=0)
+    cell.workspace, cell.workspace_bytes = 4096, pnr.pnr_workspace_bytes(cell, pnr.JAC_FULL)
+    assert pnr.pnr_eval(cell, params, 4096, None, 8192, 10, 1e-5, pnr.JAC_FULL) == pnr.OK
+    assert pnr.pnr_iters_used() == 0 and pnr.pnr_last_residual() == 0.0
+
+
+def test_workspace_scales_with_states_not_with_dense_jacobians():
+    """The Jacobian is rebuilt inside the scan, so the dense mode needs no O(T D^2) buffer."""
+    full = _cell(kind=pnr.CELL_GRU, D=16, D_in=16, T=16384, B=16)
+    diag = _cell(kind=pnr.CELL_GRU, D=16, D_in=16, T=16384, B=16)
+    wf = pnr.pnr_workspace_bytes(full, pnr.JAC_FULL)
+    wd = pnr.pnr_workspace_bytes(diag, pnr.JAC_DIAG)
+    states = 16 * 16384 * 16 * 4
+    assert wd >= 5 * states            # gx (3 planes) + two state buffers
+    assert wf < 8 * states             # far below the 16 * states a stored 16x16 Jacobian would add
+    # jac_every > 1 keeps the state the Jacobian was taken at: one more state buffer
+    e2 = _cell(kind=pnr.CELL_LSTM_DIAG, D=64, T=4096, B=1, jac_every=2)
+    e1 = _cell(kind=pnr.CELL_LSTM_DIAG, D=64, T=4096, B=1, jac_every=1)
+    extra = pnr.pnr_workspace_bytes(e2, pnr.JAC_FULL) - pnr.pnr_workspace_bytes(e1, pnr.JAC_FULL)
+    assert extra == 1 * 4096 * 128 * 4
+
+
+def test_scan_argument_checks():
+    assert pnr.pnr_scan_workspace_bytes(3, 4, 100, 0) == 0
+    assert pnr.pnr_scan(3, 4, 100, 1, 2, 3, 0, 256, 1 << 20, None) == pnr.E_INVALID
+    assert pnr.pnr_scan(1, 4, 100, 1, 2, 3, 300, 256, 1 << 20, None) == pnr.E_INVALID
+    assert pnr.pnr_scan(1, 4, 100, 1, 2, 3, 0, None, 0, None) == pnr.E_WORKSPACE
+    assert pnr.pnr_scan(1, 0, 100, 1, 2, 3, 0, None, 0, None) == pnr.OK

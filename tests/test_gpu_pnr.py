@@ -1,0 +1,224 @@
+"""GPU parity tests: the HIP path (through the C ABI) against the CPU oracle.
+
+Tolerances: fp64 paths 1e-10 (rounding only); fp32 paths are compared against the fp64
+oracle at max-abs 1e-4, the bar stated for fp32 state, and per-iteration parity at 1e-4
+as well (the fp32 conditioning floor of these small problems is ~1e-6).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from nonlinear_rnn_evaluation_amd import pnr
+from nonlinear_rnn_evaluation_amd import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _np(t):
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def _to_dev(p):
+    return {k: (None if v is None else v.to(DEV)) for k, v in p.items()}
+
+
+def _run(cell, p, max_iters, tol, mode, every=1):
+    d = _to_dev(p)
+    return pnr.evaluate(cell, d["W"], d["U"], d["x"], b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"],
+                        max_iters=max_iters, tol=tol, jac_mode=mode, jac_every=every)
+
+
+def _f64(p):
+    return {k: WL.as_f64(v) for k, v in p.items()}
+
+
+# ---------------------------------------------------------------------------------
+# Scan primitive: d_t = A_t d_{t-1} + b_t, thread / wave / block / look-back
+@pytest.mark.parametrize("T", [1, 5, 63, 64, 65, 255, 256, 257, 2047, 2048, 2049, 6000])
+@pytest.mark.parametrize("tile", [256, 2048])
+def test_scan_diagonal_matches_loop(T, tile):
+    rng = np.random.default_rng(T + tile)
+    R = 5
+    A = rng.uniform(-1.0, 1.0, size=(R, T)).astype(np.float32)
+    b = rng.standard_normal(size=(R, T)).astype(np.float32)
+    d = _np(pnr.scan(1, torch.from_numpy(A).to(DEV), torch.from_numpy(b).to(DEV), tile))
+    for r in range(R):
+        ref = O.scan_loop(A[r].astype(np.float64)[:, None], b[r].astype(np.float64)[:, None])[:, 0]
+        np.testing.assert_allclose(d[r], ref, rtol=0, atol=2e-5 * max(1.0, np.abs(ref).max()))
+
+
+@pytest.mark.parametrize("T", [1, 64, 257, 2049, 5000])
+@pytest.mark.parametrize("tile", [256, 1024])
+def test_scan_2x2_matches_loop(T, tile):
+    rng = np.random.default_rng(7 * T + tile)
+    R = 3
+    A = rng.uniform(-0.6, 0.6, size=(R, 4, T)).astype(np.float32)
+    b = rng.standard_normal(size=(R, 2, T)).astype(np.float32)
+    d = _np(pnr.scan(2, torch.from_numpy(A).to(DEV), torch.from_numpy(b).to(DEV), tile))
+    for r in range(R):
+        Am = A[r].astype(np.float64).transpose(1, 0).reshape(T, 2, 2)
+        ref = O.scan_loop(Am, b[r].astype(np.float64).T)
+        np.testing.assert_allclose(d[r].T, ref, rtol=0, atol=2e-5 * max(1.0, np.abs(ref).max()))
+
+
+def test_scan_lookback_stress_many_tiles():
+    """200+ tiles per row linked only by the decoupled look-back."""
+    rng = np.random.default_rng(11)
+    R, T = 4, 60000
+    A = rng.uniform(0.0, 1.0, size=(R, T)).astype(np.float32)
+    b = rng.standard_normal(size=(R, T)).astype(np.float32) * 0.1
+    At, bt = torch.from_numpy(A).to(DEV), torch.from_numpy(b).to(DEV)
+    ref = np.stack([O.scan_loop(A[r].astype(np.float64)[:, None], b[r].astype(np.float64)[:, None])[:, 0]
+                    for r in range(R)])
+    for _ in range(3):
+        d = _np(pnr.scan(1, At, bt, 256))
+        np.testing.assert_allclose(d, ref, rtol=0, atol=1e-4)
+
+
+# ---------------------------------------------------------------------------------
+# One or a few Newton iterations: same iterate as the dense-solve oracle
+CASES = [
+    # cell, D, D_in, x dtype, state dtype, mode, every
+    (WL.CELL_GRU, 4, 3, WL.DT_F64, WL.DT_F64, WL.JAC_FULL, 1),
+    (WL.CELL_GRU, 4, 3, WL.DT_F64, WL.DT_F64, WL.JAC_DIAG, 1),
+    (WL.CELL_GRU, 5, 2, WL.DT_F64, WL.DT_F64, WL.JAC_ZERO, 1),
+    (WL.CELL_GRU, 6, 4, WL.DT_F64, WL.DT_F64, WL.JAC_FULL, 2),
+    (WL.CELL_GRU, 8, 5, WL.DT_F32, WL.DT_F32, WL.JAC_FULL, 1),
+    (WL.CELL_GRU, 8, 5, WL.DT_F32, WL.DT_F32, WL.JAC_DIAG, 3),
+    (WL.CELL_GRU, 3, 4, WL.DT_BF16, WL.DT_F32, WL.JAC_DIAG, 1),
+    (WL.CELL_GRU_DIAG, 5, 3, WL.DT_F32, WL.DT_F32, WL.JAC_FULL, 1),
+    (WL.CELL_GRU_DIAG, 5, 3, WL.DT_F32, WL.DT_F32, WL.JAC_ZERO, 1),
+    (WL.CELL_GRU_DIAG, 4, 8, WL.DT_BF16, WL.DT_F32, WL.JAC_FULL, 2),
+    (WL.CELL_LSTM_DIAG, 3, 3, WL.DT_F32, WL.DT_F32, WL.JAC_FULL, 1),
+    (WL.CELL_LSTM_DIAG, 3, 3, WL.DT_F32, WL.DT_F32, WL.JAC_DIAG, 1),
+    (WL.CELL_LSTM_DIAG, 4, 8, WL.DT_BF16, WL.DT_F32, WL.JAC_FULL, 2),
+    (WL.CELL_LSTM_DIAG, 2, 5, WL.DT_F32, WL.DT_F32, WL.JAC_FULL, 3),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "cell%d_D%d_x%d_s%d_m%d_e%d" % (c[0], c[1], c[3], c[4], c[5], c[6]))
+@pytest.mark.parametrize("T", [37, 150])
+def test_fixed_iterations_match_dense_newton_oracle(case, T):
+    cell, D, Din, xd, sd, mode, every = case
+    p = WL.random_problem(cell, 2, T, D, Din, seed=D * 31 + T, x_dtype=xd, state_dtype=sd,
+                          bias_std=0.3, h0_std=0.5)
+    q = _f64(p)
+    tol_abs = 1e-10 if sd == WL.DT_F64 else 1e-4
+    for k in (1, 2, 4):
+        got = _run(cell, p, k, -1.0, mode, every)
+        ref = O.newton_dense(cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], k, -1.0, mode, every,
+                             solver="loop")
+        assert got["status"] == pnr.NOT_CONVERGED and got["iters"] == k
+        np.testing.assert_allclose(_np(got["h"]), ref["states"], rtol=0, atol=tol_abs)
+        np.testing.assert_allclose(got["history"], ref["rhos"], rtol=1e-3 if sd != WL.DT_F64 else 1e-9,
+                                   atol=tol_abs)
+
+
+@pytest.mark.parametrize("cell", [WL.CELL_GRU_DIAG, WL.CELL_LSTM_DIAG])
+@pytest.mark.parametrize("T", [4096 + 2048 + 123, 2 * 2048, 4099])
+def test_fixed_iterations_multi_tile_diag(cell, T):
+    """Several 2048-step tiles per row plus a ragged tail (and T % 4 != 0: scalar loads)."""
+    p = WL.random_problem(cell, 2, T, 3, 4, seed=T, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32,
+                          bias_std=0.2, h0_std=0.3)
+    q = _f64(p)
+    for k, every in ((1, 1), (3, 1), (3, 2)):
+        got = _run(cell, p, k, -1.0, WL.JAC_FULL, every)
+        ref = O.newton_dense(cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], k, -1.0, WL.JAC_FULL,
+                             every, solver="loop")
+        np.testing.assert_allclose(_np(got["h"]), ref["states"], rtol=0, atol=1e-4)
+
+
+@pytest.mark.parametrize("mode", [WL.JAC_FULL, WL.JAC_DIAG])
+@pytest.mark.parametrize("D,sd", [(4, WL.DT_F64), (16, WL.DT_F32), (7, WL.DT_F32)])
+def test_fixed_iterations_multi_tile_dense(mode, D, sd):
+    T = 700
+    p = WL.random_problem(WL.CELL_GRU, 3, T, D, 5, seed=D + T, x_dtype=sd, state_dtype=sd,
+                          bias_std=0.2, h0_std=0.3)
+    q = _f64(p)
+    got = _run(WL.CELL_GRU, p, 3, -1.0, mode)
+    ref = O.newton_dense(WL.CELL_GRU, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], 3, -1.0, mode,
+                         solver="loop")
+    np.testing.assert_allclose(_np(got["h"]), ref["states"], rtol=0, atol=1e-10 if sd == WL.DT_F64 else 1e-4)
+
+
+# ---------------------------------------------------------------------------------
+# Converged result = sequential evaluation
+@pytest.mark.parametrize("cell,D,mode", [(WL.CELL_GRU, 8, WL.JAC_FULL), (WL.CELL_GRU, 32, WL.JAC_DIAG),
+                                         (WL.CELL_GRU_DIAG, 16, WL.JAC_FULL),
+                                         (WL.CELL_LSTM_DIAG, 16, WL.JAC_FULL),
+                                         (WL.CELL_LSTM_DIAG, 16, WL.JAC_DIAG)])
+def test_converged_matches_sequential(cell, D, mode):
+    T = 5000
+    p = WL.random_problem(cell, 2, T, D, 8, seed=3 + D, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32,
+                          bias_std=0.2, h0_std=0.3)
+    q = _f64(p)
+    got = _run(cell, p, 200, 1e-6, mode)
+    assert got["status"] == pnr.OK, (got["status"], got["history"][-3:])
+    ref = O.sequential(cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"])
+    assert np.abs(_np(got["h"]) - ref).max() < 1e-4
+
+
+def test_tiny_gru_fp64_iteration_counts_and_states():
+    w = WL.get_workload("tiny_gru")
+    p = WL.generate(w)
+    q = _f64(p)
+    seq = O.sequential(w.cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"])
+    for mode in w.jac_modes:
+        got = _run(w.cell, p, w.max_iters, w.tol, mode)
+        ref = O.newton_dense(w.cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], w.max_iters, w.tol, mode)
+        assert got["status"] == pnr.OK
+        assert got["iters"] == ref["iters"]
+        np.testing.assert_allclose(got["history"], ref["rhos"], rtol=1e-6, atol=1e-14)
+        assert np.abs(_np(got["h"]) - seq).max() < 1e-9
+
+
+# ---------------------------------------------------------------------------------
+# Edge cases and status codes
+def test_nonfinite_input_reports_nonfinite_at_first_residual():
+    for cell in (WL.CELL_GRU, WL.CELL_GRU_DIAG, WL.CELL_LSTM_DIAG):
+        p = WL.random_problem(cell, 2, 300, 4, 3, seed=1, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32)
+        p["x"][1, 123, 2] = float("nan")
+        got = _run(cell, p, 10, 1e-6, WL.JAC_FULL)
+        assert got["status"] == pnr.NONFINITE and got["iters"] == 0
+        assert math.isinf(got["residual"])
+
+
+def test_zero_iterations_returns_initial_guess_and_its_residual():
+    p = WL.random_problem(WL.CELL_LSTM_DIAG, 2, 100, 4, 3, seed=2, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32,
+                          h0_std=0.5)
+    q = _f64(p)
+    got = _run(WL.CELL_LSTM_DIAG, p, 0, 1e-6, WL.JAC_FULL)
+    assert got["status"] == pnr.NOT_CONVERGED and got["iters"] == 0
+    assert torch.all(got["h"] == 0)
+    ref = O.newton_dense(WL.CELL_LSTM_DIAG, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], 0, 1e-6,
+                         WL.JAC_FULL, solver="loop")
+    assert got["residual"] == pytest.approx(ref["rhos"][0], rel=1e-5)
+
+
+def test_one_iteration_not_converged_and_short_sequences():
+    for T in (1, 2, 3):
+        p = WL.random_problem(WL.CELL_GRU_DIAG, 1, T, 3, 2, seed=T, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32)
+        q = _f64(p)
+        got = _run(WL.CELL_GRU_DIAG, p, 64, 1e-7, WL.JAC_FULL)
+        assert got["status"] == pnr.OK and got["iters"] <= T
+        ref = O.sequential(WL.CELL_GRU_DIAG, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"])
+        assert np.abs(_np(got["h"]) - ref).max() < 1e-5
+    p = WL.random_problem(WL.CELL_GRU, 1, 300, 4, 2, seed=9, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32)
+    got = _run(WL.CELL_GRU, p, 1, 1e-12, WL.JAC_FULL)
+    assert got["status"] == pnr.NOT_CONVERGED and got["iters"] == 1
+
+
+def test_repeated_calls_reuse_workspace():
+    p = WL.random_problem(WL.CELL_LSTM_DIAG, 2, 3000, 8, 4, seed=5, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32)
+    d = _to_dev(p)
+    first = pnr.evaluate(WL.CELL_LSTM_DIAG, d["W"], d["U"], d["x"], max_iters=50, tol=1e-6)
+    ws = first["workspace"]
+    for _ in range(3):
+        again = pnr.evaluate(WL.CELL_LSTM_DIAG, d["W"], d["U"], d["x"], max_iters=50, tol=1e-6, workspace=ws)
+        assert again["iters"] == first["iters"]
+        assert torch.allclose(again["h"], first["h"], atol=1e-6, rtol=0)

@@ -272,3 +272,15 @@ def test_stale_jacobian_reuses_the_refresh_point(cell):
     np.testing.assert_allclose(r2["states"][0], h1 + O.scan_loop(J0, F1 - h1), rtol=0, atol=1e-13)
     fresh = _newton(cell, p, 2, -1.0, O.JAC_FULL, 1)["states"][0]
     assert np.abs(fresh - r2["states"][0]).max() > 1e-8
+
+
+@pytest.mark.parametrize("cell", CELLS)
+def test_loop_solver_matches_dense_solver(cell):
+    """Forward substitution and LAPACK on the assembled system give the same iterates."""
+    p = _problem(cell, T=11)
+    for mode, every in ((O.JAC_FULL, 1), (O.JAC_DIAG, 2)):
+        a = O.newton_dense(cell, p["W"], p["U"], p["b_x"], p["b_h"], p["x"], p["h0"], 3, -1.0, mode, every)
+        b = O.newton_dense(cell, p["W"], p["U"], p["b_x"], p["b_h"], p["x"], p["h0"], 3, -1.0, mode, every,
+                           solver="loop")
+        np.testing.assert_allclose(b["states"], a["states"], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(b["rhos"], a["rhos"], rtol=1e-12, atol=1e-14)
