@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark of parallel Newton evaluation of nonlinear RNNs on one MI355X.
+
+One step = one pnr_eval call over one batch of synthetic input: input projection, the
+on-device Newton loop to convergence, and the output layout conversion, with the inputs
+already resident in HBM.  The reported value is converged B*T per second per layer.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--others a,b,..]
+
+Prints ONE JSON line.  Besides the primary workload (the 64-channel GRU with diagonal
+quasi-Newton Jacobians, B=8, T=4096) it reports the other named workloads under
+"others", each with its own roofline and parity numbers.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "converged timesteps·batch/sec (B·T/s) per layer; Newton iters; scan HBM GB/s"
+UNIT = "timesteps*batch/s"
+HBM_PEAK_GBS = 8000.0
+PRIMARY = "gru_quasi"
+DEFAULT_OTHERS = "tiny_gru,gru_full,gru_diag_long,lstm_diag_long,lstm_diag_long_stiff"
+KERNEL_SRC = {"diag": "nonlinear_rnn_evaluation_amd/csrc/diag_iter.hip",
+              "dense": "nonlinear_rnn_evaluation_amd/csrc/dense_iter.hip"}
+
+
+def src_hash(path):
+    with open(os.path.join(ROOT, path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def iteration_bytes(w, k, iters_total, resid=False):
+    """Algorithmic HBM bytes of one fused iteration kernel launch that did work.
+
+    Per element the kernel must read the gate pre-activations and the current iterate
+    (not at k=0: the zero guess is never stored), write the next iterate, and -- when
+    the Jacobian is reused -- read the state it was taken at (unless that is the zero
+    guess).  The residual-only pass reads and does not write.
+    """
+    from nonlinear_rnn_evaluation_amd import workloads as WL
+    es = 8 if w.state_dtype == WL.DT_F64 else 4
+    G, S = w.G, w.S
+    n_bt = w.B * w.T
+    gx = n_bt * G * w.D * es
+    h = n_bt * S * es
+    cur = h if k > 0 else 0
+    if resid:
+        return gx + cur
+    jk = k - (k % w.jac_every)
+    jac = h if (jk != k and jk > 0) else 0
+    return gx + cur + h + jac
+
+
+def run_workload(name, steps, warmup, mode=None, with_cpu=True, cpu_budget=12.0, parity=True):
+    import numpy as np
+    import torch
+
+    from nonlinear_rnn_evaluation_amd import pnr
+    from nonlinear_rnn_evaluation_amd import workloads as WL
+
+    w = WL.get_workload(name)
+    mode = w.jac_modes[0] if mode is None else mode
+    t_gen = time.perf_counter()
+    p = WL.generate(w)
+    dev = torch.device("cuda:0")
+    d = {k: (None if v is None else v.to(dev)) for k, v in p.items()}
+    t_gen = time.perf_counter() - t_gen
+    stream = torch.cuda.current_stream()
+
+    def call(ws=None, out=None):
+        return pnr.evaluate(w.cell, d["W"], d["U"], d["x"], b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"],
+                            max_iters=w.max_iters, tol=w.tol, jac_mode=mode, jac_every=w.jac_every,
+                            workspace=ws, h_out=out)
+
+    first = call()
+    ws, out = first["workspace"], first["h"]
+    for _ in range(max(0, warmup - 1)):
+        call(ws, out)
+    # ---- timed region: K steps between a barrier + synchronize on both sides ----
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    results = []
+    for _ in range(steps):
+        results.append(call(ws, out))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    last = results[-1]
+    iters = last["iters"]
+    status = last["status"]
+
+    # ---- live per-kernel timing: HIP events around each launch, on the launch stream ----
+    pnr.pnr_profile_enable(True)
+    profs = []
+    for _ in range(steps):
+        call(ws, out)
+        profs.append(pnr.pnr_last_profile())
+    pnr.pnr_profile_enable(False)
+    newton_ms = sum(pp["newton_ms"] for pp in profs) / steps
+    passes = profs[-1]["passes"]
+    resid_last = profs[-1]["resid_only"]
+    bytes_call = sum(iteration_bytes(w, k, iters, resid=(resid_last and k == passes - 1)) for k in range(passes))
+    achieved = bytes_call / (newton_ms * 1e-3) / 1e9 if newton_ms > 0 else 0.0
+    family = "diag" if w.cell in (WL.CELL_GRU_DIAG, WL.CELL_LSTM_DIAG) else "dense"
+    kname = "pnr::diag_newton_kernel" if family == "diag" else "pnr::dense_newton_kernel"
+    traffic = None
+    pmc_path = os.path.join(ROOT, "profiles", f"newton_kernel_{name}_pmc.json")
+    if os.path.exists(pmc_path):
+        with open(pmc_path) as f:
+            pmc = json.load(f)
+        if pmc.get("kernel_src_sha") == src_hash(KERNEL_SRC[family]):
+            traffic = pmc.get("bytes_per_launch")
+    roof = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "avg_launch_us": round(newton_ms * 1e3, 3), "launches_per_step": 1, "passes_per_launch": passes,
+            "algorithmic_bytes_per_launch": bytes_call,
+            "us_per_pass": round(newton_ms * 1e3 / max(passes, 1), 3)}
+    phases = {k: round(sum(pp[k] for pp in profs) / steps, 4)
+              for k in ("total_ms", "proj_ms", "newton_ms", "out_ms")}
+    proj_flops = 2.0 * w.B * w.T * w.D_in * w.G * w.D
+    phases["proj_tflops"] = round(proj_flops / (phases["proj_ms"] * 1e-3) / 1e12, 2) if phases["proj_ms"] else None
+
+    rec = {"workload": name, "status": int(status), "iters": int(iters), "ms_per_step": round(ms, 4),
+           "value": (w.B * w.T) / (ms * 1e-3) if status == 0 else None,
+           "wall_s": round(wall, 3), "gen_s": round(t_gen, 2), "roofline": roof, "phases_ms": phases,
+           "residual": last["residual"], "jac_mode": ["full", "diag", "zero"][mode],
+           "config": w.describe()}
+
+    # ---- parity and the CPU oracle baseline (same inputs) ----
+    if parity or with_cpu:
+        rec.update(oracle_leg(w, p, out, with_cpu, cpu_budget))
+    del ws, out, results, first, d
+    torch.cuda.empty_cache()
+    return rec
+
+
+def oracle_leg(w, p, out, with_cpu, budget):
+    """Sequential fp64 oracle on the same inputs: timed (bounded sample) and compared."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+    from oracle.sequential import output_channel_columns
+    from nonlinear_rnn_evaluation_amd import workloads as WL
+
+    res = {}
+    diag = w.cell in (WL.CELL_GRU_DIAG, WL.CELL_LSTM_DIAG)
+    W = WL.as_f64(p["W"])
+    U = WL.as_f64(p["U"])
+    bx = WL.as_f64(p["b_x"])
+    h0 = WL.as_f64(p["h0"])
+    xs = p["x"].float().numpy() if p["x"].dtype == torch.bfloat16 else p["x"].numpy()
+    if diag:
+        # channels are independent: a sample of channels is an exact sub-problem
+        n_ch = min(w.D, 16 if w.T * w.B > 100000 else 64)
+        ch = np.linspace(0, w.D - 1, n_ch).round().astype(int)
+        Wc, Uc, bxc, _, h0c, _ = O.restrict_channels(w.cell, w.D, W, U, bx, None, h0, ch)
+        t0 = time.perf_counter()
+        ref = O.sequential(w.cell, Wc, Uc, bxc, None, xs, h0c)
+        el = time.perf_counter() - t0
+        cols = output_channel_columns(w.cell, w.D, ch)
+        got = out[:, :, torch.from_numpy(cols).to(out.device)].double().cpu().numpy()
+        frac = n_ch / w.D
+        sample = f"{n_ch} of {w.D} channels (evenly spaced), all {w.B}x{w.T} steps; time scaled by {w.D}/{n_ch}"
+        reps = 1
+    else:
+        reps, el = 0, 0.0
+        while True:
+            t0 = time.perf_counter()
+            ref = O.sequential(w.cell, W, U, bx, None, xs, h0)
+            el += time.perf_counter() - t0
+            reps += 1
+            if not with_cpu or el >= budget or reps >= 50:
+                break
+        got = out.double().cpu().numpy()
+        frac = 1.0
+        sample = f"the full workload, {reps} run(s)"
+    err = np.abs(got - ref)
+    res["parity"] = {"max_abs": float(err.max()), "mean_abs": float(err.mean()),
+                     "vs": "fp64 sequential oracle", "sample": sample}
+    if with_cpu:
+        try:
+            from threadpoolctl import threadpool_info
+            blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            blas = 1
+        value = w.B * w.T * reps * frac / el
+        res["cpu_baseline"] = {"value": value, "unit": UNIT, "cores": int(blas), "kind": "oracle",
+                               "sample": sample + f"; {el:.1f} s of oracle time",
+                               "host_cpus": len(os.sched_getaffinity(0))}
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default=PRIMARY)
+    ap.add_argument("--others", default=DEFAULT_OTHERS, help="comma list, or 'none'")
+    ap.add_argument("--other-steps", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    prim = run_workload(args.workload, args.steps, args.warmup, with_cpu=not args.no_cpu_baseline,
+                        cpu_budget=args.cpu_budget)
+    others = []
+    if args.others and args.others != "none":
+        for name in args.others.split(","):
+            from nonlinear_rnn_evaluation_amd import workloads as WL
+            w = WL.get_workload(name)
+            for mode in w.jac_modes:
+                print(f"# bench: {name} mode {mode}", file=sys.stderr, flush=True)
+                r = run_workload(name, args.other_steps, 1, mode=mode, with_cpu=False)
+                others.append(r)
+    line = {
+        "metric": METRIC, "value": prim["value"], "unit": UNIT, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": prim["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": dict({"workload": prim["workload"]}, **{k: v for k, v in prim["config"].items() if k != "workload"}),
+        "newton_iters": prim["iters"], "status": prim["status"],
+        "roofline": prim["roofline"], "cpu_baseline": prim.get("cpu_baseline"), "parity": prim.get("parity"),
+        "phases_ms": prim["phases_ms"], "others": others,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -56,7 +56,8 @@
  * pnr_cell.stream (a hipStream_t; NULL = the default stream).
  *
  * Supported combinations (others return PNR_E_UNSUPPORTED):
- *   GRU:        (x, state) in {(f64, f64), (f32, f32), (bf16, f32)}, 1 <= D <= 64
+ *   GRU:        (x, state) in {(f64, f64), (f32, f32), (bf16, f32)}; D <= 32 with
+ *               PNR_JAC_FULL, D <= 64 (fp32 state) or 32 (fp64 state) otherwise
  *   GRU_DIAG,
  *   LSTM_DIAG:  (x, state) in {(f32, f32), (bf16, f32)}
  *
@@ -112,10 +113,9 @@ typedef struct pnr_params {
 /*
  * Scratch bytes pnr_eval needs for this problem and Jacobian mode (0 on invalid
  * input; the reason is in pnr_last_error()).  Pure host arithmetic; no HIP call.
- * The Jacobian itself is never stored: it is rebuilt from the stored states inside
- * the scan, so the dense mode needs no O(T D^2) buffer (the memory argument behind
- * quasi-DEER in "Towards Scalable and Stable Parallelization of Nonlinear RNNs",
- * scime summary "Approach", is thereby moot here; both modes use O(T D)).
+ * The Jacobian itself is never stored: it is rebuilt inside the iteration kernel from
+ * the stored states (and, for the dense GRU, from U), so the dense mode needs no
+ * O(T D^2) buffer and both Jacobian modes use O(T D) workspace.
  */
 size_t pnr_workspace_bytes(const pnr_cell* cell, int jac_mode);
 
@@ -160,6 +160,27 @@ const char* pnr_last_error(void);
 size_t pnr_scan_workspace_bytes(int kind, int R, int T, int tile_len);
 int pnr_scan(int kind, int R, int T, const float* A, const float* b, float* d, int tile_len,
              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Per-phase timing of the calling thread's pnr_eval calls, for measurement only.  When
+ * enabled (pnr_profile_enable(1)), pnr_eval records a HIP event before and after each
+ * of its kernel launches on the caller's stream and, after its final synchronisation,
+ * fills the record below (milliseconds of GPU time between those events).  The whole
+ * Newton loop is one launch; `passes` counts the fused passes it ran (one per
+ * residual evaluated: iters + 1).  Disabled by default; enabling it adds one event pair
+ * per launch.  pnr_last_profile returns 0, or -1 if no profiled call completed.
+ */
+typedef struct pnr_profile {
+  double total_ms;       /* first launch to last launch of the call                    */
+  double proj_ms;        /* input projection                                            */
+  double newton_ms;      /* the persistent Newton-loop kernel                           */
+  double out_ms;         /* conversion of the returned iterate to h_out                 */
+  int32_t passes;        /* fused passes of the Newton kernel (iters + 1)               */
+  int32_t resid_only;    /* 1 if the last pass only evaluated the residual (max_iters)  */
+} pnr_profile;
+
+int pnr_profile_enable(int on);
+int pnr_last_profile(pnr_profile* out);
 
 #ifdef __cplusplus
 }

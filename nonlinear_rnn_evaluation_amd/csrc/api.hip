@@ -11,6 +11,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <string>
@@ -116,6 +117,54 @@ Layout make_layout(const pnr_cell* c, int jac_mode) {
   return l;
 }
 
+// ---- optional per-launch timing (measurement mode) ----
+struct Prof {
+  bool on = false;
+  bool valid = false;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  pnr_profile last{};
+  hipEvent_t next() {
+    if (used == pool.size()) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      pool.push_back(e);
+    }
+    return pool[used++];
+  }
+};
+thread_local Prof g_prof;
+
+// Event pair around one launch group; no-op when profiling is off.
+struct Mark {
+  hipEvent_t a = nullptr, b = nullptr;
+};
+Mark mark_begin(hipStream_t st) {
+  Mark m;
+  if (!g_prof.on) return m;
+  m.a = g_prof.next();
+  if (m.a) hipEventRecord(m.a, st);
+  return m;
+}
+void mark_end(Mark& m, hipStream_t st) {
+  if (!g_prof.on || !m.a) return;
+  m.b = g_prof.next();
+  if (m.b) hipEventRecord(m.b, st);
+}
+double mark_ms(const Mark& m) {
+  float ms = 0.f;
+  if (!m.a || !m.b || hipEventElapsedTime(&ms, m.a, m.b) != hipSuccess) return 0.0;
+  return ms;
+}
+
+// Row walk (no look-back) when the rows alone fill the resident grid evenly enough;
+// PNR_DIAG_WALK=0/1 forces either organisation (used by the tests to cover both).
+int walk_mode(int rows, int capacity) {
+  const char* e = getenv("PNR_DIAG_WALK");
+  if (e && (e[0] == '0' || e[0] == '1')) return e[0] == '1';
+  return rows >= capacity && (rows % capacity == 0 || rows >= 4 * capacity);
+}
+
 struct DevInfo { int dev = -1; int num_cu = 0; };
 thread_local DevInfo g_dev;
 
@@ -149,6 +198,16 @@ size_t pnr_workspace_bytes(const pnr_cell* cell, int jac_mode) {
 }
 
 const char* pnr_last_error(void) { return g_last.err.c_str(); }
+
+int pnr_profile_enable(int on) {
+  g_prof.on = on != 0;
+  return 0;
+}
+int pnr_last_profile(pnr_profile* out) {
+  if (!g_prof.valid || !out) return -1;
+  *out = g_prof.last;
+  return 0;
+}
 int pnr_iters_used(void) { return g_last.iters; }
 double pnr_last_residual(void) { return g_last.residual; }
 int pnr_last_residual_history(double* out, int max_n) {
@@ -161,6 +220,8 @@ int pnr_last_residual_history(double* out, int max_n) {
 int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, void* h_out,
              int max_iters, double tol, int jac_mode) {
   g_last = LastCall();
+  g_prof.valid = false;
+  g_prof.used = 0;
   int rc = validate(cell, jac_mode);
   if (rc) return rc;
   if (!params) return fail(PNR_E_INVALID, "params is NULL");
@@ -193,6 +254,7 @@ int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, cons
   const int kind = cell->kind, D = cell->D, T = cell->T, B = cell->B, Din = cell->D_in;
   const int G = gates(kind), S = states(kind, D);
 
+  Mark m_first = mark_begin(st);
   PNR_HIP(launch_init(ctrl, slots, l.slot_words, st));
 
   // ---- input projection ----
@@ -205,80 +267,70 @@ int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, cons
     // gx[(b,t)][m] = sum_k x[(b,t)][k] W[m][k] + b_x[m]
     g = GemmArgs{x, params->W, params->b_x, gx, B * T, G * D, Din, 0, 0, 0, Din, Din, G * D, 1, 0};
   }
+  Mark m_proj = mark_begin(st);
   PNR_HIP(launch_gemm(cell->x_dtype, cell->state_dtype, g, st));
+  mark_end(m_proj, st);
 
-  // ---- Newton loop: every launch is enqueued up front; the device decides when to stop ----
-  int cur = -1, jac = -1;   // buffer indices; -1 = the zero initial guess
-  auto pick_next = [&](int a, int b) {
-    for (int i = 0; i < l.nbuf; ++i)
-      if (i != a && i != b) return i;
-    return -1;
-  };
-  for (int k = 0; k <= max_iters; ++k) {
-    const bool resid_only = k == max_iters;
-    if (!resid_only && k % cell->jac_every == 0) jac = cur;
-    const int next = resid_only ? cur : pick_next(cur, jac);
-    if (is_diag_cell(kind)) {
-      DiagIterArgs a{};
-      a.gx = static_cast<const float*>(gx);
-      a.u = static_cast<const float*>(params->U);
-      a.bh = static_cast<const float*>(params->b_h);
-      a.h0 = static_cast<const float*>(h0);
-      a.Hcur = cur >= 0 ? static_cast<const float*>(H[cur]) : nullptr;
-      a.Hjac = jac >= 0 ? static_cast<const float*>(H[jac]) : nullptr;
-      a.Hnext = next >= 0 ? static_cast<float*>(H[next]) : nullptr;
-      a.slots = slots;
-      a.partials = reinterpret_cast<uint32_t*>(ws + l.partials);
-      a.ctrl = ctrl;
-      a.rho_hist = hist;
-      a.cur_zero = cur < 0;
-      a.jac_zero = jac < 0;
-      a.B = B; a.D = D; a.T = T;
-      a.tiles_per_row = l.tiles_per_row;
-      a.n_tiles = l.n_tiles;
-      a.k = k; a.cur_buf = cur; a.max_iters = max_iters; a.tol = tol;
-      a.jac_mode = jac_mode;
-      a.resid_only = resid_only;
-      PNR_HIP(launch_diag_iter(kind, a, num_cu, st, nullptr));
-    } else if (cell->state_dtype == PNR_F32) {
-      DenseIterArgs<float> a{};
-      a.gx = static_cast<const float*>(gx);
-      a.U = static_cast<const float*>(params->U);
-      a.bh = static_cast<const float*>(params->b_h);
-      a.h0 = static_cast<const float*>(h0);
-      a.Hcur = cur >= 0 ? static_cast<const float*>(H[cur]) : nullptr;
-      a.Hjac = jac >= 0 ? static_cast<const float*>(H[jac]) : nullptr;
-      a.Hnext = next >= 0 ? static_cast<float*>(H[next]) : nullptr;
-      a.slots = slots; a.partials = reinterpret_cast<uint64_t*>(ws + l.partials);
-      a.ctrl = ctrl; a.rho_hist = hist;
-      a.cur_zero = cur < 0; a.jac_zero = jac < 0;
-      a.B = B; a.D = D; a.T = T; a.L = l.L;
-      a.tiles_per_row = l.tiles_per_row; a.n_tiles = l.n_tiles;
-      a.k = k; a.cur_buf = cur; a.max_iters = max_iters; a.tol = tol;
-      a.jac_mode = jac_mode; a.resid_only = resid_only;
-      PNR_HIP(launch_dense_iter_f32(a, l.dense_full, num_cu, st));
-    } else {
-      DenseIterArgs<double> a{};
-      a.gx = static_cast<const double*>(gx);
-      a.U = static_cast<const double*>(params->U);
-      a.bh = static_cast<const double*>(params->b_h);
-      a.h0 = static_cast<const double*>(h0);
-      a.Hcur = cur >= 0 ? static_cast<const double*>(H[cur]) : nullptr;
-      a.Hjac = jac >= 0 ? static_cast<const double*>(H[jac]) : nullptr;
-      a.Hnext = next >= 0 ? static_cast<double*>(H[next]) : nullptr;
-      a.slots = slots; a.partials = reinterpret_cast<uint64_t*>(ws + l.partials);
-      a.ctrl = ctrl; a.rho_hist = hist;
-      a.cur_zero = cur < 0; a.jac_zero = jac < 0;
-      a.B = B; a.D = D; a.T = T; a.L = l.L;
-      a.tiles_per_row = l.tiles_per_row; a.n_tiles = l.n_tiles;
-      a.k = k; a.cur_buf = cur; a.max_iters = max_iters; a.tol = tol;
-      a.jac_mode = jac_mode; a.resid_only = resid_only;
-      PNR_HIP(launch_dense_iter_f64(a, l.dense_full, num_cu, st));
-    }
-    cur = next;
+  // ---- the Newton loop: one persistent launch; the device decides when to stop ----
+  Mark m_newton = mark_begin(st);
+  if (is_diag_cell(kind)) {
+    DiagLoopArgs a{};
+    a.gx = static_cast<const float*>(gx);
+    a.u = static_cast<const float*>(params->U);
+    a.bh = static_cast<const float*>(params->b_h);
+    a.h0 = static_cast<const float*>(h0);
+    for (int i = 0; i < 3; ++i) a.H[i] = static_cast<float*>(H[i]);
+    a.nbuf = l.nbuf;
+    a.slots = slots;
+    a.partials = reinterpret_cast<uint32_t*>(ws + l.partials);
+    a.ctrl = ctrl;
+    a.rho_hist = hist;
+    a.B = B; a.D = D; a.T = T;
+    a.tiles_per_row = l.tiles_per_row;
+    a.n_tiles = l.n_tiles;
+    a.n_rows = B * D;
+    a.max_iters = max_iters; a.jac_every = cell->jac_every; a.jac_mode = jac_mode;
+    a.tol = tol;
+    const int cap = diag_grid_capacity(kind, num_cu);
+    // A block walks whole rows (no look-back) when there are enough rows to fill the
+    // grid; otherwise rows are cut into tiles linked by the decoupled look-back.
+    a.walk = walk_mode(a.n_rows, cap);
+    const int items = a.walk ? a.n_rows : a.n_tiles;
+    const int grid = items < cap ? items : cap;
+    PNR_HIP(launch_diag_newton(kind, a, grid, st));
+  } else if (cell->state_dtype == PNR_F32) {
+    DenseLoopArgs<float> a{};
+    a.gx = static_cast<const float*>(gx);
+    a.U = static_cast<const float*>(params->U);
+    a.bh = static_cast<const float*>(params->b_h);
+    a.h0 = static_cast<const float*>(h0);
+    for (int i = 0; i < 3; ++i) a.H[i] = static_cast<float*>(H[i]);
+    a.nbuf = l.nbuf;
+    a.slots = slots; a.partials = reinterpret_cast<uint64_t*>(ws + l.partials);
+    a.ctrl = ctrl; a.rho_hist = hist;
+    a.B = B; a.D = D; a.T = T; a.L = l.L;
+    a.tiles_per_row = l.tiles_per_row; a.n_tiles = l.n_tiles;
+    a.max_iters = max_iters; a.jac_every = cell->jac_every; a.jac_mode = jac_mode; a.tol = tol;
+    PNR_HIP(launch_dense_newton_f32(a, l.dense_full, num_cu, st));
+  } else {
+    DenseLoopArgs<double> a{};
+    a.gx = static_cast<const double*>(gx);
+    a.U = static_cast<const double*>(params->U);
+    a.bh = static_cast<const double*>(params->b_h);
+    a.h0 = static_cast<const double*>(h0);
+    for (int i = 0; i < 3; ++i) a.H[i] = static_cast<double*>(H[i]);
+    a.nbuf = l.nbuf;
+    a.slots = slots; a.partials = reinterpret_cast<uint64_t*>(ws + l.partials);
+    a.ctrl = ctrl; a.rho_hist = hist;
+    a.B = B; a.D = D; a.T = T; a.L = l.L;
+    a.tiles_per_row = l.tiles_per_row; a.n_tiles = l.n_tiles;
+    a.max_iters = max_iters; a.jac_every = cell->jac_every; a.jac_mode = jac_mode; a.tol = tol;
+    PNR_HIP(launch_dense_newton_f64(a, l.dense_full, num_cu, st));
   }
+  mark_end(m_newton, st);
 
   // ---- returned iterate -> caller layout ----
+  Mark m_out = mark_begin(st);
   if (is_diag_cell(kind)) {
     const float* bufs[3] = {static_cast<const float*>(H[0]), static_cast<const float*>(H[1]),
                             static_cast<const float*>(H[2])};
@@ -293,16 +345,33 @@ int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, cons
     PNR_HIP(launch_dense_output<double>(bufs, ctrl, static_cast<double*>(h_out), (size_t)B * T * S, st));
   }
 
+  mark_end(m_out, st);
+  mark_end(m_first, st);
+
   // ---- the one device -> host crossing of the call ----
   Ctrl hc;
   std::vector<double> hh(max_iters + 1);
   PNR_HIP(hipMemcpyAsync(&hc, ctrl, sizeof(Ctrl), hipMemcpyDeviceToHost, st));
   PNR_HIP(hipMemcpyAsync(hh.data(), hist, sizeof(double) * (max_iters + 1), hipMemcpyDeviceToHost, st));
   PNR_HIP(hipStreamSynchronize(st));
+  if (hc.fault)
+    return fail(PNR_E_HIP, "device loop gave up waiting (%s); results are not valid",
+                hc.fault == 1 ? "look-back" : "grid barrier");
   if (!hc.done || hc.iters < 0) return fail(PNR_E_HIP, "device loop did not record a decision");
   g_last.iters = hc.iters;
   g_last.residual = hc.rho;
   g_last.hist.assign(hh.begin(), hh.begin() + hc.iters + 1);
+  if (g_prof.on) {
+    pnr_profile p{};
+    p.total_ms = mark_ms(m_first);
+    p.proj_ms = mark_ms(m_proj);
+    p.newton_ms = mark_ms(m_newton);
+    p.out_ms = mark_ms(m_out);
+    p.passes = hc.iters + 1;
+    p.resid_only = hc.iters == max_iters;
+    g_prof.last = p;
+    g_prof.valid = true;
+  }
   return hc.status;
 }
 

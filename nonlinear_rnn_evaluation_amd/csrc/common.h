@@ -20,10 +20,76 @@ struct Ctrl {
   int32_t iters;       // Newton updates applied to the returned iterate
   int32_t result_buf;  // index of the state buffer holding the result (-1 = the zero guess)
   double rho;          // residual of the returned iterate
-  uint32_t ticket;     // dynamic tile counter of the running iteration kernel
-  uint32_t finished;   // blocks of the running iteration kernel that have finished
-  uint32_t pad[2];
+  uint32_t ticket;     // dynamic tile counter (standalone scan)
+  int32_t fault;       // a bounded device wait ran out (1 = look-back, 2 = barrier)
+  uint32_t pad0[24];
+  // the grid-barrier words sit on cache lines of their own: every block polls bar_gen
+  uint32_t bar_count;  // grid barrier: blocks arrived
+  uint32_t pad1[63];
+  uint32_t bar_gen;    // grid barrier: generation, bumped by the last block to arrive
+  uint32_t pad2[63];
 };
+
+// Bound on every device-side wait (polls of a look-back slot or of the grid barrier).
+// With the back-off below a full count is a few seconds: far above any
+// legitimate wait, and it guarantees that every wave reaches the end of the kernel.
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+// Sleep between polls of a shared word, growing from ~64 to ~2048 clocks, so that
+// thousands of waiting waves do not saturate the memory side with polls.
+__device__ __forceinline__ void backoff(uint32_t spins) {
+  if (spins < 8) __builtin_amdgcn_s_sleep(1);
+  else if (spins < 64) __builtin_amdgcn_s_sleep(8);
+  else __builtin_amdgcn_s_sleep(32);
+}
+
+__device__ __forceinline__ void record_fault(Ctrl* c, int code) {
+  __hip_atomic_store(&c->fault, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool has_fault(const Ctrl* c) {
+  return __hip_atomic_load(&c->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+}
+
+// Grid-wide barrier for a persistent, co-resident grid.  The last block to arrive runs
+// `merge` (the whole block, after an acquire fence) before it releases the others --
+// the "final block" of a two-level reduction.  Global writes before the barrier are
+// released with an agent-scope fence and acquired after it, so blocks on other XCDs
+// (each with its own L2) see them.  The wait is bounded (kSpinLimit).
+template <class Merge>
+__device__ __forceinline__ void grid_barrier(Ctrl* c, Merge merge) {
+  __shared__ int s_last;
+  __shared__ uint32_t s_gen;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t gen = __hip_atomic_load(&c->bar_gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __threadfence();
+    const uint32_t prev = atomicAdd(&c->bar_count, 1u);
+    s_last = prev == gridDim.x - 1;
+    s_gen = gen;
+  }
+  __syncthreads();
+  if (s_last) {
+    __threadfence();
+    merge();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      __hip_atomic_store(&c->bar_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __threadfence();
+      __hip_atomic_store(&c->bar_gen, s_gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else if (threadIdx.x == 0) {
+    uint32_t spins = 0;
+    while (__hip_atomic_load(&c->bar_gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == s_gen) {
+      backoff(spins);
+      if (++spins > kSpinLimit) {
+        record_fault(c, 2);
+        break;
+      }
+    }
+    __threadfence();
+  }
+  __syncthreads();
+}
 
 // ---------------------------------------------------------------------------------
 // Elementwise math.  sigmoid(a) = 1 / (1 + e^-a); tanh(a) = 2 sigmoid(2a) - 1.  fp32

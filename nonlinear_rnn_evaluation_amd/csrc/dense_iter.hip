@@ -1,7 +1,9 @@
-// One Newton iteration for the GRU with a dense recurrent matrix U (D <= 64), fused:
-// recurrent product U s_{t-1} for every step of a tile, gates, residual, Jacobian
-// factors, the linear solve d_t = J_t d_{t-1} + r_t (scan of affine maps with a
-// decoupled look-back across tiles) and the update s <- s + d.
+// The Newton loop for the GRU with a dense recurrent matrix U (D <= 64), one fused pass
+// per iteration: recurrent product U s_{t-1} for every step of a tile, gates, residual,
+// Jacobian factors, the linear solve d_t = J_t d_{t-1} + r_t (scan of affine maps with
+// a decoupled look-back across tiles) and the update s <- s + d.  All iterations run
+// inside one persistent, co-resident grid; the residual max is finished by the last
+// block to reach the grid barrier.
 //
 // Method: ParaRNN overview page, "Technical Implementation / Newton's Iteration" and
 // "Parallel Reduction"; DEER's dense Jacobian and quasi-DEER's diagonal one from
@@ -10,21 +12,23 @@
 // The dense Jacobian of the linear-before-reset GRU factors as
 //   J_t = diag(z) + diag(al) U_z + diag(be) U_r + diag(ga) U_n
 //   al = (s - n) z (1 - z),  be = (1 - z)(1 - n^2) gh_n r (1 - r),  ga = (1 - z)(1 - n^2) r
-// so it is never formed: the scan applies it to a vector with three products by the
-// blocks of U (resident in LDS) and an elementwise combination.  Only four D-vectors
-// per step live in LDS.
+// so it is never formed: the scan applies it with three products by the blocks of U
+// (resident in LDS) and an elementwise combination.  Only four D-vectors per step live
+// in LDS.
 //
 // Layout: gx [B][T][3D], states [B][T][D] (channel-contiguous).  A tile is L steps of
-// one batch element; blocks are persistent and take tiles from a ticket counter.
+// one batch element; blocks take tiles from a ticket counter.
 //
 // Scan organisation inside a tile:
 //  * DIAG: thread (p, i) = part p of the tile, channel i; each part is a run of
-//    consecutive steps composed serially; parts are combined in LDS; the look-back is
-//    per channel.
+//    consecutive steps composed serially; parts are combined in LDS.
 //  * FULL: a group of D+1 lanes (inside one wave) owns one part.  Lane j < D carries
 //    column j of the part's matrix product, lane D carries the vector part.  The block
-//    total and the per-part prefixes are composed serially; the look-back moves a
-//    (D*D + D)-value aggregate and a D-value prefix.
+//    total and the per-part prefixes are composed serially.
+// Across tiles: the tile publishes its aggregate, reads the slots of up to WMAX
+// predecessors in one cooperative round trip, and resolves its incoming increment
+// from the nearest published prefix by applying the aggregates in between to it
+// (matrix-vector products only).
 #include "common.h"
 #include "kernels.h"
 
@@ -32,10 +36,14 @@ namespace pnr {
 
 template <typename Tt> struct WordsOf { static constexpr int W = sizeof(Tt) / 4; };
 
-// look-back slot words per tile: FULL holds the (D*D + D)-value aggregate then the
-// D-value prefix; DIAG holds D values of a, D of b, then D prefixes.  W words per value.
-__host__ __device__ inline int dense_slot_words_dev(int D, bool full, int W) {
-  return full ? (D * D + 2 * D) * W : 3 * D * W;
+// look-back slot values per tile: FULL holds the (D*D + D)-value aggregate then the
+// D-value prefix; DIAG holds D values of a, D of b, then D prefixes.
+__host__ __device__ inline int dense_slot_values(int D, bool full) { return full ? D * D + 2 * D : 3 * D; }
+__host__ __device__ inline int dense_agg_values(int D, bool full) { return full ? D * D + D : 2 * D; }
+// predecessors inspected per look-back round trip (bounded by the LDS it takes)
+__host__ __device__ inline int dense_window(int D, bool full, int es) {
+  int w = (24 * 1024) / (dense_slot_values(D, full) * es);
+  return w < 2 ? 2 : (w > 16 ? 16 : w);
 }
 
 __device__ __forceinline__ void vput(uint64_t* s, uint32_t ep, float v) { slot_put(s, ep, v); }
@@ -72,50 +80,48 @@ __device__ __forceinline__ float mul_add(float a, float b, float c) { return fma
 __device__ __forceinline__ double mul_add(double a, double b, double c) { return fma(a, b, c); }
 
 // ---------------------------------------------------------------------------------
-// LDS layout (dynamic shared memory), all in units of Tt:
-//   Us   [3D][D]     recurrent matrix
-//   Bh   [3D]        recurrent bias
+// LDS layout (dynamic shared memory), in units of Tt:
+//   Us   [D][3D]     recurrent matrix, transposed   Bh   [3D]   recurrent bias
 //   Hx   [L+1][D]    Hx[0] = s_{t0-1}, Hx[1+s] = current iterate at step t0+s
-//   Hj   [L+1][D]    same for the state the Jacobian is taken at (only when stale)
+//   Hj   [L+1][D]    same for the state the Jacobian is taken at (Jacobian reuse only)
 //   R    [L][D]      residuals
-//   Jd   [L][D]      diagonal Jacobian            (DIAG)
-//   Z, Al, Be, Ga [L][D] Jacobian factors          (FULL)
-//   scan scratch (see the two scan paths)
-template <typename Tt>
+//   Jd   [L][D]      diagonal Jacobian (DIAG)  |  Z, Al, Be, Ga [L][D] factors (FULL)
+//   Pagg             per-part aggregates: DIAG [2][parts][D]; FULL [parts][D*D + D]
+//   Tot  [D*D + D]   FULL: block total
+//   Pin  [parts+1][D] FULL: increment entering each part
+//   Fx   [2][parts][D] FULL: fix-up double buffer (also look-back scratch)
+//   Win  [WMAX][slot values]  look-back window
+//   Din  [D]         increment entering the tile
 struct DenseLds {
-  int D, L, full, stale, parts;
+  int D, L, full, reuse, parts, wmax;
   __host__ __device__ size_t count() const {
-    size_t n = (size_t)3 * D * D + 3 * D + (size_t)(L + 1) * D * (stale ? 2 : 1) + (size_t)L * D;
+    size_t n = (size_t)3 * D * D + 3 * D + (size_t)(L + 1) * D * (reuse ? 2 : 1) + (size_t)L * D;
     if (full) {
-      n += (size_t)4 * L * D;
-      n += (size_t)parts * (D * D + D);   // per-part aggregates
-      n += (size_t)2 * (D * D + D);       // block total, look-back accumulator
-      n += (size_t)(D * D + D);           // look-back scratch (predecessor aggregate)
-      n += (size_t)(parts + 1) * D;       // per-part incoming increments
-      n += (size_t)2 * parts * D;         // fix-up double buffer
-      n += (size_t)D;                     // tile incoming increment
+      n += (size_t)4 * L * D + (size_t)parts * (D * D + D) + (D * D + D) + (size_t)(parts + 1) * D +
+           (size_t)2 * parts * D;
     } else {
-      n += (size_t)L * D;                 // Jd
-      n += (size_t)2 * parts * D;         // per-part aggregates (a, b)
-      n += (size_t)D;                     // tile incoming increment
+      n += (size_t)L * D + (size_t)2 * parts * D;
     }
+    n += (size_t)wmax * dense_slot_values(D, full) + D;
     return n;
   }
 };
 
+// Ut is U transposed, [D][3D] (Ut[k][g*D + i] = U[g*D + i][k]): lanes that compute
+// consecutive channels i read consecutive LDS words, so the product is bank-conflict
+// free; the state row p is a broadcast.
 template <typename Tt>
-__device__ __forceinline__ void gru_gates(const Tt* __restrict__ Us, const Tt* __restrict__ Bh,
+__device__ __forceinline__ void gru_gates(const Tt* __restrict__ Ut, const Tt* __restrict__ Bh,
                                           const Tt* __restrict__ p, const Tt* __restrict__ g, int D,
                                           int i, Tt& r, Tt& z, Tt& n, Tt& ghn) {
   Tt ar = Bh[i], az = Bh[D + i], an = Bh[2 * D + i];
-  const Tt* ur = Us + (size_t)i * D;
-  const Tt* uz = Us + (size_t)(D + i) * D;
-  const Tt* un = Us + (size_t)(2 * D + i) * D;
+  const int G3 = 3 * D;
   for (int k = 0; k < D; ++k) {
     const Tt pk = p[k];
-    ar = mul_add(ur[k], pk, ar);
-    az = mul_add(uz[k], pk, az);
-    an = mul_add(un[k], pk, an);
+    const Tt* u = Ut + (size_t)k * G3;
+    ar = mul_add(u[i], pk, ar);
+    az = mul_add(u[D + i], pk, az);
+    an = mul_add(u[2 * D + i], pk, an);
   }
   r = sigm(g[i] + ar);
   z = sigm(g[D + i] + az);
@@ -123,420 +129,413 @@ __device__ __forceinline__ void gru_gates(const Tt* __restrict__ Us, const Tt* _
   n = tanh_(mul_add(r, an, g[2 * D + i]));
 }
 
-template <typename Tt, int DM, bool FULL, bool RESID_ONLY>
-__global__ void __launch_bounds__(PNR_BLOCK) dense_iter_kernel(DenseIterArgs<Tt> a) {
+__device__ __forceinline__ int pick_next_dense(int cur, int jac, int nbuf) {
+  for (int i = 0; i < nbuf; ++i)
+    if (i != cur && i != jac) return i;
+  return -1;
+}
+
+template <typename Tt, int DM, bool FULL>
+__global__ void __launch_bounds__(PNR_BLOCK) dense_newton_kernel(DenseLoopArgs<Tt> a) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
   Tt* lds = reinterpret_cast<Tt*>(lds_raw);
-  __shared__ int s_tile;
-  __shared__ int s_flag;
+  __shared__ int s_p;
+  __shared__ int s_ok[16][2];
   __shared__ uint64_t s_wmax[PNR_WAVES];
-  __shared__ int s_last;
 
   Ctrl* ctrl = a.ctrl;
-  if (__hip_atomic_load(&ctrl->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return;
-
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int D = a.D, T = a.T, L = a.L;
-  const bool stale = !RESID_ONLY && ((a.Hjac != a.Hcur) || a.jac_zero != a.cur_zero);
+  const bool reuse = a.nbuf > 2;
   const int GS = D + 1;                       // FULL: lanes per group
   const int GPW = FULL ? 64 / GS : 0;         // FULL: groups per wave
   const int parts = FULL ? GPW * PNR_WAVES : PNR_BLOCK / D;
   constexpr int W = WordsOf<Tt>::W;
-  const uint32_t ep = (uint32_t)a.k + 1u;
+  const int SV = dense_slot_values(D, FULL), SA = dense_agg_values(D, FULL);
+  const int WMAX = dense_window(D, FULL, (int)sizeof(Tt));
+  const int DD = D * D + D;
 
   // carve LDS
   Tt* Us = lds;
   Tt* Bh = Us + 3 * D * D;
   Tt* Hx = Bh + 3 * D;
   Tt* Hj = Hx + (L + 1) * D;
-  Tt* R = Hj + (stale ? (L + 1) * D : 0);
+  Tt* R = Hj + (reuse ? (L + 1) * D : 0);
   Tt* Jd = R + L * D;            // DIAG
   Tt* Zv = R + L * D;            // FULL factors
   Tt* Al = Zv + L * D;
   Tt* Be = Al + L * D;
   Tt* Ga = Be + L * D;
-  Tt* Pagg = FULL ? Ga + L * D : Jd + L * D;   // FULL: [parts][D*D + D]; DIAG: [2][parts][D]
-  Tt* Tot = Pagg + (FULL ? parts * (D * D + D) : 2 * parts * D);   // FULL: [D*D + D]
-  Tt* Acc = Tot + (FULL ? (D * D + D) : 0);                          // FULL: [D*D + D]
-  Tt* Prd = Acc + (FULL ? (D * D + D) : 0);                          // FULL: [D*D + D]
-  Tt* Pin = Prd + (FULL ? (D * D + D) : 0);                          // FULL: [parts + 1][D]
-  Tt* Fx = Pin + (FULL ? (parts + 1) * D : 0);                       // FULL: [2][parts][D]
-  Tt* Din = Fx + (FULL ? 2 * parts * D : 0);                         // [D]
+  Tt* Pagg = FULL ? Ga + L * D : Jd + L * D;
+  Tt* Tot = Pagg + (FULL ? parts * DD : 2 * parts * D);
+  Tt* Pin = Tot + (FULL ? DD : 0);
+  Tt* Fx = Pin + (FULL ? (parts + 1) * D : 0);
+  Tt* Win = Fx + (FULL ? 2 * parts * D : 0);
+  Tt* Din = Win + WMAX * SV;
 
-  for (int idx = tid; idx < 3 * D * D; idx += PNR_BLOCK) Us[idx] = a.U[idx];
+  for (int idx = tid; idx < 3 * D * D; idx += PNR_BLOCK) {
+    const int row = idx / D, k = idx - row * D;     // U[row][k] -> Ut[k][row]
+    Us[(size_t)k * 3 * D + row] = a.U[idx];
+  }
   for (int idx = tid; idx < 3 * D; idx += PNR_BLOCK) Bh[idx] = a.bh ? a.bh[idx] : Tt(0);
+  __syncthreads();
 
-  uint64_t blk_max = 0;
-  while (true) {
-    if (tid == 0) s_tile = (int)atomicAdd(&ctrl->ticket, 1u);
-    __syncthreads();
-    const int tile = s_tile;
-    if (tile >= a.n_tiles) break;
-    const int b = tile / a.tiles_per_row;
-    const int seg = tile - b * a.tiles_per_row;
-    const int t0 = seg * L;
-    const int Lv = min(L, T - t0);
-    const Tt* gxb = a.gx + (size_t)b * T * 3 * D;
+  int cur = -1, jac = -1;
+  for (int k = 0; k <= a.max_iters; ++k) {
+    const bool resid_only = k == a.max_iters;
+    if (!resid_only && k % a.jac_every == 0) jac = cur;
+    const int next = resid_only ? cur : pick_next_dense(cur, jac, a.nbuf);
+    const Tt* Hcur = cur >= 0 ? a.H[cur] : nullptr;
+    const Tt* Hjac = jac >= 0 ? a.H[jac] : nullptr;
+    Tt* Hnext = next >= 0 ? a.H[next] : nullptr;
+    const bool stale = !resid_only && jac != cur;
+    const uint32_t ep = (uint32_t)k + 1u;
+    uint64_t blk_max = 0;
 
-    // ---- stage states: Hx[0] = s_{t0-1}; Hx[1+s] = iterate at t0+s ----
-    for (int idx = tid; idx < (L + 1) * D; idx += PNR_BLOCK) {
-      const int s = idx / D, c = idx - s * D;
-      const int t = t0 + s - 1;
-      Tt v = Tt(0);
-      if (t < 0) v = a.h0 ? a.h0[(size_t)b * D + c] : Tt(0);
-      else if (t < T && !a.cur_zero) v = a.Hcur[((size_t)b * T + t) * D + c];
-      Hx[idx] = v;
-      if (stale) {
-        Tt w = Tt(0);
-        if (t < 0) w = a.h0 ? a.h0[(size_t)b * D + c] : Tt(0);
-        else if (t < T && !a.jac_zero) w = a.Hjac[((size_t)b * T + t) * D + c];
-        Hj[idx] = w;
-      }
-    }
-    __syncthreads();
+    // Static assignment, tiles in increasing order per block (co-resident grid): the
+    // lowest unfinished tile never waits, so every look-back ends.
+    for (int tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+      if (has_fault(ctrl)) break;
+      const int b = tile / a.tiles_per_row;
+      const int seg = tile - b * a.tiles_per_row;
+      const int t0 = seg * L;
+      const int Lv = min(L, T - t0);
+      const Tt* gxb = a.gx + (size_t)b * T * 3 * D;
 
-    // ---- cell: gates, residual, Jacobian (diagonal or factors) ----
-    uint64_t tmax = 0;
-    for (int idx = tid; idx < L * D; idx += PNR_BLOCK) {
-      const int s = idx / D, i = idx - s * D;
-      if (s >= Lv) {
-        R[idx] = Tt(0);
-        if (!RESID_ONLY) {
-          if (FULL) { Zv[idx] = Tt(1); Al[idx] = Tt(0); Be[idx] = Tt(0); Ga[idx] = Tt(0); }
-          else Jd[idx] = Tt(1);
+      // ---- stage states: Hx[0] = s_{t0-1}; Hx[1+s] = iterate at t0+s ----
+      for (int idx = tid; idx < (L + 1) * D; idx += PNR_BLOCK) {
+        const int s = idx / D, c = idx - s * D;
+        const int t = t0 + s - 1;
+        Tt v = Tt(0);
+        if (t < 0) v = a.h0 ? a.h0[(size_t)b * D + c] : Tt(0);
+        else if (t < T && Hcur) v = Hcur[((size_t)b * T + t) * D + c];
+        Hx[idx] = v;
+        if (stale) {
+          Tt w = Tt(0);
+          if (t < 0) w = a.h0 ? a.h0[(size_t)b * D + c] : Tt(0);
+          else if (t < T && Hjac) w = Hjac[((size_t)b * T + t) * D + c];
+          Hj[idx] = w;
         }
-        continue;
-      }
-      const Tt* g = gxb + (size_t)(t0 + s) * 3 * D;
-      const Tt* p = Hx + s * D;
-      Tt r, z, n, ghn;
-      gru_gates(Us, Bh, p, g, D, i, r, z, n, ghn);
-      const Tt f = mul_add(z, p[i] - n, n);
-      const Tt res = f - Hx[(s + 1) * D + i];
-      R[idx] = res;
-      tmax = max(tmax, abs_bits64(res));
-      if (RESID_ONLY) continue;
-      const Tt* pj = p;
-      if (stale) {
-        pj = Hj + s * D;
-        gru_gates(Us, Bh, pj, g, D, i, r, z, n, ghn);
-      }
-      const Tt omz = Tt(1) - z;
-      const Tt cn = omz * (Tt(1) - n * n);
-      const Tt al = (pj[i] - n) * z * omz;
-      const Tt be = cn * ghn * r * (Tt(1) - r);
-      const Tt ga = cn * r;
-      if (a.jac_mode == PNR_JAC_ZERO) {
-        if (FULL) { Zv[idx] = Tt(0); Al[idx] = Tt(0); Be[idx] = Tt(0); Ga[idx] = Tt(0); }
-        else Jd[idx] = Tt(0);
-      } else if (FULL) {
-        Zv[idx] = z; Al[idx] = al; Be[idx] = be; Ga[idx] = ga;
-      } else {
-        Jd[idx] = z + al * Us[(size_t)(D + i) * D + i] + be * Us[(size_t)i * D + i] +
-                  ga * Us[(size_t)(2 * D + i) * D + i];
-      }
-    }
-    blk_max = max(blk_max, tmax);
-    __syncthreads();
-    if (RESID_ONLY) continue;
-
-    uint64_t* myslot = a.slots + (size_t)tile * dense_slot_words_dev(D, FULL, W);
-
-    if constexpr (!FULL) {
-      // ================= DIAG: per-channel scalar scan =================
-      const int p = tid / D, i = tid - p * D;
-      const int lp = (L + parts - 1) / parts;
-      Tt* Sa = Pagg;
-      Tt* Sb = Pagg + parts * D;
-      if (p < parts) {
-        Tt ea = Tt(1), eb = Tt(0);
-        for (int s = p * lp; s < min(L, (p + 1) * lp); ++s) {
-          const Tt ja = Jd[s * D + i];
-          eb = mul_add(ja, eb, R[s * D + i]);
-          ea = ja * ea;
-        }
-        Sa[p * D + i] = ea; Sb[p * D + i] = eb;
       }
       __syncthreads();
-      if (tid < D) {
-        // block total for channel i and the look-back on that channel
-        Tt ta = Sa[tid], tb = Sb[tid];
-        for (int q = 1; q < parts; ++q) {
-          const Tt qa = Sa[q * D + tid], qb = Sb[q * D + tid];
-          tb = mul_add(qa, tb, qb);
-          ta = qa * ta;
+
+      // ---- cell: gates, residual, Jacobian (diagonal or factors) ----
+      uint64_t tmax = 0;
+      for (int idx = tid; idx < L * D; idx += PNR_BLOCK) {
+        const int s = idx / D, i = idx - s * D;
+        if (s >= Lv) {
+          R[idx] = Tt(0);
+          if (!resid_only) {
+            if (FULL) { Zv[idx] = Tt(1); Al[idx] = Tt(0); Be[idx] = Tt(0); Ga[idx] = Tt(0); }
+            else Jd[idx] = Tt(1);
+          }
+          continue;
         }
-        uint64_t* aggA = myslot + (size_t)tid * W;
-        uint64_t* aggB = myslot + (size_t)(D + tid) * W;
-        uint64_t* pre = myslot + (size_t)(2 * D + tid) * W;
-        Tt din = Tt(0);
-        if (seg == 0) {
-          vput(pre, ep, tb);
+        const Tt* g = gxb + (size_t)(t0 + s) * 3 * D;
+        const Tt* p = Hx + s * D;
+        Tt r, z, n, ghn;
+        gru_gates(Us, Bh, p, g, D, i, r, z, n, ghn);
+        const Tt f = mul_add(z, p[i] - n, n);
+        const Tt res = f - Hx[(s + 1) * D + i];
+        R[idx] = res;
+        tmax = max(tmax, abs_bits64(res));
+        if (resid_only) continue;
+        const Tt* pj = p;
+        if (stale) {
+          pj = Hj + s * D;
+          gru_gates(Us, Bh, pj, g, D, i, r, z, n, ghn);
+        }
+        const Tt omz = Tt(1) - z;
+        const Tt cn = omz * (Tt(1) - n * n);
+        const Tt al = (pj[i] - n) * z * omz;
+        const Tt be = cn * ghn * r * (Tt(1) - r);
+        const Tt ga = cn * r;
+        if (a.jac_mode == PNR_JAC_ZERO) {
+          if (FULL) { Zv[idx] = Tt(0); Al[idx] = Tt(0); Be[idx] = Tt(0); Ga[idx] = Tt(0); }
+          else Jd[idx] = Tt(0);
+        } else if (FULL) {
+          Zv[idx] = z; Al[idx] = al; Be[idx] = be; Ga[idx] = ga;
         } else {
-          vput(aggA, ep, ta);
-          vput(aggB, ep, tb);
-          Tt acc_a = Tt(1), acc_b = Tt(0);
-          int j = tile - 1;
-          const size_t sw = (size_t)dense_slot_words_dev(D, FULL, W);
-          while (true) {
-            const uint64_t* js = a.slots + (size_t)j * sw;
-            Tt pv;
-            if (vget(js + (size_t)(2 * D + tid) * W, ep, pv)) {
-              din = mul_add(acc_a, pv, acc_b);
-              break;
-            }
-            Tt qa, qb;
-            bool ok = vget(js + (size_t)tid * W, ep, qa);
-            ok &= vget(js + (size_t)(D + tid) * W, ep, qb);
-            if (ok) {
-              acc_b = mul_add(acc_a, qb, acc_b);
-              acc_a = acc_a * qa;
-              --j;
-              continue;
-            }
-            __builtin_amdgcn_s_sleep(1);
-          }
-          vput(pre, ep, mul_add(ta, din, tb));
-        }
-        Din[tid] = din;
-      }
-      __syncthreads();
-      if (p < parts) {
-        Tt dl = Din[i];
-        for (int q = 0; q < p; ++q) dl = mul_add(Sa[q * D + i], dl, Sb[q * D + i]);
-        for (int s = p * lp; s < min(Lv, (p + 1) * lp); ++s) {
-          dl = mul_add(Jd[s * D + i], dl, R[s * D + i]);
-          a.Hnext[((size_t)b * T + t0 + s) * D + i] = Hx[(s + 1) * D + i] + dl;
+          const Tt* ud = Us + (size_t)i * 3 * D;   // U[g*D + i][i] = Ut[i][g*D + i]
+          Jd[idx] = z + al * ud[D + i] + be * ud[i] + ga * ud[2 * D + i];
         }
       }
+      blk_max = max(blk_max, tmax);
       __syncthreads();
-    } else {
-      // ================= FULL: dense D x D scan =================
-      const int gi = lane / GS;                // group inside the wave
-      const int j = lane - gi * GS;            // lane inside the group
-      const bool in_group = gi < GPW;
+      if (resid_only) continue;
+
+      uint64_t* myslot = a.slots + (size_t)tile * SV * W;
+      const int p = tid / D, ci = tid - p * D;                    // DIAG thread layout
+      const int lpd = (L + parts - 1) / parts;                    // DIAG steps per part
+      const int gi = lane / GS, jl = lane - gi * GS;              // FULL group layout
+      const bool in_group = FULL && gi < GPW;
       const int part = wid * GPW + gi;
-      const int lp = (L + parts - 1) / parts;
-      const int DD = D * D + D;
-      // (1) part aggregates: lane j < D carries column j of the matrix product, lane D the vector
-      if (in_group) {
-        Tt col[DM];
-#pragma unroll
-        for (int m = 0; m < DM; ++m) col[m] = (j < D && m == j) ? Tt(1) : Tt(0);
-        for (int s = part * lp; s < min(L, (part + 1) * lp); ++s) {
-          const Tt* zr = Zv + s * D; const Tt* ar = Al + s * D;
-          const Tt* br = Be + s * D; const Tt* gr = Ga + s * D;
-          Tt nw[DM];
-#pragma unroll
-          for (int m = 0; m < DM; ++m) {
-            Tt ur = 0, uz = 0, un = 0;
-            if (m < D) {
-              const Tt* rr = Us + (size_t)m * D;
-              const Tt* rz = Us + (size_t)(D + m) * D;
-              const Tt* rn = Us + (size_t)(2 * D + m) * D;
-#pragma unroll
-              for (int k = 0; k < DM; ++k) {
-                if (k < D) {
-                  ur = mul_add(rr[k], col[k], ur);
-                  uz = mul_add(rz[k], col[k], uz);
-                  un = mul_add(rn[k], col[k], un);
-                }
-              }
-            }
-            Tt v = m < D ? zr[m] * col[m] + ar[m] * uz + br[m] * ur + gr[m] * un : Tt(0);
-            if (j == D && m < D) v += R[s * D + m];
-            nw[m] = v;
+      const int lpf = (L + parts - 1) / parts;
+      Tt keep_a = Tt(1), keep_b = Tt(0);   // DIAG: this tile's total (a, b) for channel tid
+
+      // ---- (1) part aggregates and (2) the block total, published for the successors ----
+      if constexpr (!FULL) {
+        Tt* Sa = Pagg;
+        Tt* Sb = Pagg + parts * D;
+        if (p < parts) {
+          Tt ea = Tt(1), eb = Tt(0);
+          for (int s = p * lpd; s < min(L, (p + 1) * lpd); ++s) {
+            const Tt ja = Jd[s * D + ci];
+            eb = mul_add(ja, eb, R[s * D + ci]);
+            ea = ja * ea;
           }
-#pragma unroll
-          for (int m = 0; m < DM; ++m) col[m] = nw[m];
-        }
-        Tt* ag = Pagg + (size_t)part * DD;     // [D][D] row-major, then [D]
-#pragma unroll
-        for (int m = 0; m < DM; ++m) {
-          if (m < D) {
-            if (j < D) ag[m * D + j] = col[m];
-            else ag[D * D + m] = col[m];
-          }
-        }
-      }
-      __syncthreads();
-      // (2) block total = agg_{parts-1} o ... o agg_0 (one group, column per lane)
-      if (tid < GS) {
-        Tt col[DM];
-#pragma unroll
-        for (int m = 0; m < DM; ++m) col[m] = m < D ? (tid < D ? Pagg[m * D + tid] : Pagg[D * D + m]) : Tt(0);
-        for (int q = 1; q < parts; ++q) {
-          const Tt* ag = Pagg + (size_t)q * DD;
-          Tt nw[DM];
-#pragma unroll
-          for (int m = 0; m < DM; ++m) {
-            Tt v = (tid == D && m < D) ? ag[D * D + m] : Tt(0);
-            if (m < D) {
-#pragma unroll
-              for (int k = 0; k < DM; ++k)
-                if (k < D) v = mul_add(ag[m * D + k], col[k], v);
-            }
-            nw[m] = v;
-          }
-#pragma unroll
-          for (int m = 0; m < DM; ++m) col[m] = nw[m];
-        }
-#pragma unroll
-        for (int m = 0; m < DM; ++m) {
-          if (m < D) {
-            if (tid < D) Tot[m * D + tid] = col[m];
-            else Tot[D * D + m] = col[m];
-          }
-        }
-      }
-      __syncthreads();
-      // (3) decoupled look-back over whole tiles (all threads poll together)
-      const size_t sw = (size_t)dense_slot_words_dev(D, true, W);
-      uint64_t* mpre = myslot + (size_t)DD * W;
-      if (seg == 0) {
-        for (int m = tid; m < D; m += PNR_BLOCK) {
-          Din[m] = Tt(0);
-          vput(mpre + (size_t)m * W, ep, Tot[D * D + m]);
+          Sa[p * D + ci] = ea;
+          Sb[p * D + ci] = eb;
         }
         __syncthreads();
-      } else {
-        for (int e = tid; e < DD; e += PNR_BLOCK) {
-          vput(myslot + (size_t)e * W, ep, Tot[e]);
-          Acc[e] = (e < D * D) ? ((e / D == e % D) ? Tt(1) : Tt(0)) : Tt(0);
+        if (tid < D) {
+          Tt ta = Sa[tid], tb = Sb[tid];
+          for (int q = 1; q < parts; ++q) {
+            const Tt qa = Sa[q * D + tid], qb = Sb[q * D + tid];
+            tb = mul_add(qa, tb, qb);
+            ta = qa * ta;
+          }
+          keep_a = ta;
+          keep_b = tb;
+          if (seg == 0) {
+            vput(myslot + (size_t)(2 * D + tid) * W, ep, tb);
+            Din[tid] = Tt(0);
+          } else {
+            vput(myslot + (size_t)tid * W, ep, ta);
+            vput(myslot + (size_t)(D + tid) * W, ep, tb);
+          }
         }
-        int jt = tile - 1;
-        while (true) {
-          const uint64_t* js = a.slots + (size_t)jt * sw;
-          if (tid == 0) s_flag = 1;
-          __syncthreads();
-          // predecessor's inclusive prefix?
+      } else {
+        if (in_group) {
+          Tt col[DM];
+#pragma unroll
+          for (int m = 0; m < DM; ++m) col[m] = (jl < D && m == jl) ? Tt(1) : Tt(0);
+          for (int s = part * lpf; s < min(L, (part + 1) * lpf); ++s) {
+            const Tt* zr = Zv + s * D; const Tt* ar = Al + s * D;
+            const Tt* br = Be + s * D; const Tt* gr = Ga + s * D;
+            Tt nw[DM];
+#pragma unroll
+            for (int m = 0; m < DM; ++m) {
+              Tt ur = 0, uz = 0, un = 0;
+              if (m < D) {
+#pragma unroll
+                for (int kk = 0; kk < DM; ++kk) {
+                  if (kk < D) {
+                    const Tt* u = Us + (size_t)kk * 3 * D;
+                    ur = mul_add(u[m], col[kk], ur);
+                    uz = mul_add(u[D + m], col[kk], uz);
+                    un = mul_add(u[2 * D + m], col[kk], un);
+                  }
+                }
+              }
+              Tt v = m < D ? zr[m] * col[m] + ar[m] * uz + br[m] * ur + gr[m] * un : Tt(0);
+              if (jl == D && m < D) v += R[s * D + m];
+              nw[m] = v;
+            }
+#pragma unroll
+            for (int m = 0; m < DM; ++m) col[m] = nw[m];
+          }
+          Tt* ag = Pagg + (size_t)part * DD;     // [D][D] row-major, then [D]
+#pragma unroll
+          for (int m = 0; m < DM; ++m) {
+            if (m < D) {
+              if (jl < D) ag[m * D + jl] = col[m];
+              else ag[D * D + m] = col[m];
+            }
+          }
+        }
+        __syncthreads();
+        if (tid < GS) {
+          Tt col[DM];
+#pragma unroll
+          for (int m = 0; m < DM; ++m) col[m] = m < D ? (tid < D ? Pagg[m * D + tid] : Pagg[D * D + m]) : Tt(0);
+          for (int q = 1; q < parts; ++q) {
+            const Tt* ag = Pagg + (size_t)q * DD;
+            Tt nw[DM];
+#pragma unroll
+            for (int m = 0; m < DM; ++m) {
+              Tt v = (tid == D && m < D) ? ag[D * D + m] : Tt(0);
+              if (m < D) {
+#pragma unroll
+                for (int kk = 0; kk < DM; ++kk)
+                  if (kk < D) v = mul_add(ag[m * D + kk], col[kk], v);
+              }
+              nw[m] = v;
+            }
+#pragma unroll
+            for (int m = 0; m < DM; ++m) col[m] = nw[m];
+          }
+#pragma unroll
+          for (int m = 0; m < DM; ++m) {
+            if (m < D) {
+              if (tid < D) Tot[m * D + tid] = col[m];
+              else Tot[D * D + m] = col[m];
+            }
+          }
+        }
+        __syncthreads();
+        if (seg == 0) {
           for (int m = tid; m < D; m += PNR_BLOCK) {
+            Din[m] = Tt(0);
+            vput(myslot + (size_t)(SA + m) * W, ep, Tot[D * D + m]);
+          }
+        } else {
+          for (int e = tid; e < SA; e += PNR_BLOCK) vput(myslot + (size_t)e * W, ep, Tot[e]);
+        }
+      }
+      __syncthreads();
+
+      // ---- (3) decoupled look-back over a window of predecessors (block-uniform loop) ----
+      if (seg > 0) {
+        uint32_t spins = 0;
+        while (true) {
+          const int Wn = min(seg, WMAX);
+          if (tid < Wn) { s_ok[tid][0] = 1; s_ok[tid][1] = 1; }
+          __syncthreads();
+          for (int idx = tid; idx < Wn * SV; idx += PNR_BLOCK) {
+            const int w = idx / SV, e = idx - w * SV;
+            const uint64_t* js = a.slots + (size_t)(tile - 1 - w) * SV * W;
             Tt v;
-            if (!vget(js + (size_t)(DD + m) * W, ep, v)) s_flag = 0;
-            Prd[m] = v;
+            if (!vget(js + (size_t)e * W, ep, v)) s_ok[w][e < SA ? 0 : 1] = 0;
+            Win[w * SV + e] = v;
           }
           __syncthreads();
-          if (s_flag) {
-            for (int m = tid; m < D; m += PNR_BLOCK) {
-              Tt v = Acc[D * D + m];
-              for (int k = 0; k < D; ++k) v = mul_add(Acc[m * D + k], Prd[k], v);
-              Din[m] = v;
+          if (tid == 0) {
+            int pp = -1;
+            for (int w = 0; w < Wn; ++w) {
+              if (s_ok[w][1]) { pp = w; break; }
+              if (!s_ok[w][0]) break;
+            }
+            s_p = pp;
+          }
+          __syncthreads();
+          const int pp = s_p;
+          if (pp >= 0) {
+            if constexpr (!FULL) {
+              if (tid < D) {
+                Tt dl = Win[pp * SV + 2 * D + tid];
+                for (int w = pp - 1; w >= 0; --w) dl = mul_add(Win[w * SV + tid], dl, Win[w * SV + D + tid]);
+                Din[tid] = dl;
+              }
+            } else {
+              // d <- M_w d + v_w for w = pp-1 .. 0, starting from the prefix of tile pp
+              Tt* vec = Fx;                 // scratch: two D-vectors
+              if (tid < D) vec[tid] = Win[pp * SV + SA + tid];
+              __syncthreads();
+              int src = 0;
+              for (int w = pp - 1; w >= 0; --w) {
+                if (tid < D) {
+                  const Tt* M = Win + w * SV;
+                  Tt v = M[D * D + tid];
+                  for (int kk = 0; kk < D; ++kk) v = mul_add(M[tid * D + kk], vec[src * D + kk], v);
+                  vec[(1 - src) * D + tid] = v;
+                }
+                __syncthreads();
+                src = 1 - src;
+              }
+              if (tid < D) Din[tid] = vec[src * D + tid];
             }
             __syncthreads();
             break;
           }
-          __syncthreads();
-          if (tid == 0) s_flag = 1;
-          __syncthreads();
-          for (int e = tid; e < DD; e += PNR_BLOCK) {
-            Tt v;
-            if (!vget(js + (size_t)e * W, ep, v)) s_flag = 0;
-            Prd[e] = v;
+          if (++spins > kSpinLimit) {
+            if (tid == 0) record_fault(ctrl, 1);
+            for (int m = tid; m < D; m += PNR_BLOCK) Din[m] = Tt(0);
+            __syncthreads();
+            break;
+          }
+          backoff(spins);
+        }
+        // publish this tile's inclusive prefix
+        if constexpr (!FULL) {
+          if (tid < D) vput(myslot + (size_t)(2 * D + tid) * W, ep, mul_add(keep_a, Din[tid], keep_b));
+        } else {
+          for (int m = tid; m < D; m += PNR_BLOCK) {
+            Tt v = Tot[D * D + m];
+            for (int kk = 0; kk < D; ++kk) v = mul_add(Tot[m * D + kk], Din[kk], v);
+            vput(myslot + (size_t)(SA + m) * W, ep, v);
+          }
+        }
+      }
+      __syncthreads();
+
+      // ---- (4) fix-up: walk each part from its incoming increment, s <- s + d ----
+      if constexpr (!FULL) {
+        Tt* Sa = Pagg;
+        Tt* Sb = Pagg + parts * D;
+        if (p < parts) {
+          Tt dl = Din[ci];
+          for (int q = 0; q < p; ++q) dl = mul_add(Sa[q * D + ci], dl, Sb[q * D + ci]);
+          for (int s = p * lpd; s < min(Lv, (p + 1) * lpd); ++s) {
+            dl = mul_add(Jd[s * D + ci], dl, R[s * D + ci]);
+            Hnext[((size_t)b * T + t0 + s) * D + ci] = Hx[(s + 1) * D + ci] + dl;
+          }
+        }
+        __syncthreads();
+      } else {
+        for (int m = tid; m < D; m += PNR_BLOCK) Pin[m] = Din[m];
+        __syncthreads();
+        for (int q = 0; q < parts; ++q) {
+          if (tid < D) {
+            const Tt* ag = Pagg + (size_t)q * DD;
+            Tt v = ag[D * D + tid];
+            for (int kk = 0; kk < D; ++kk) v = mul_add(ag[tid * D + kk], Pin[q * D + kk], v);
+            Pin[(q + 1) * D + tid] = v;
           }
           __syncthreads();
-          if (s_flag) {
-            // Acc <- Acc o Prd = (Acc_M Prd_M, Acc_M Prd_v + Acc_v); new values staged in Tot's
-            // tail is not safe, so compute into registers per entry first.
-            Tt vals[(DM * DM + DM + PNR_BLOCK - 1) / PNR_BLOCK];
-            int c = 0;
-            for (int e = tid; e < DD; e += PNR_BLOCK, ++c) {
-              Tt v;
-              if (e < D * D) {
-                const int m = e / D, n = e - m * D;
-                v = Tt(0);
-                for (int k = 0; k < D; ++k) v = mul_add(Acc[m * D + k], Prd[k * D + n], v);
-              } else {
-                const int m = e - D * D;
-                v = Acc[D * D + m];
-                for (int k = 0; k < D; ++k) v = mul_add(Acc[m * D + k], Prd[D * D + k], v);
-              }
-              vals[c] = v;
+        }
+        Tt* cb = Fx;
+        Tt* nb = Fx + parts * D;
+        if (in_group && jl < D) cb[part * D + jl] = Pin[part * D + jl];
+        __syncthreads();
+        for (int st = 0; st < lpf; ++st) {
+          const int s = part * lpf + st;
+          if (in_group && jl < D && s < L) {
+            const Tt* dv = cb + part * D;
+            Tt ur = 0, uz = 0, un = 0;
+            for (int kk = 0; kk < D; ++kk) {
+              const Tt* u = Us + (size_t)kk * 3 * D;
+              ur = mul_add(u[jl], dv[kk], ur);
+              uz = mul_add(u[D + jl], dv[kk], uz);
+              un = mul_add(u[2 * D + jl], dv[kk], un);
             }
-            __syncthreads();
-            c = 0;
-            for (int e = tid; e < DD; e += PNR_BLOCK, ++c) Acc[e] = vals[c];
-            __syncthreads();
-            --jt;
-            continue;
+            const int qi = s * D + jl;
+            const Tt v = Zv[qi] * dv[jl] + Al[qi] * uz + Be[qi] * ur + Ga[qi] * un + R[qi];
+            nb[part * D + jl] = v;
+            if (s < Lv) Hnext[((size_t)b * T + t0 + s) * D + jl] = Hx[(s + 1) * D + jl] + v;
           }
-          __syncthreads();   // every thread has read s_flag before thread 0 resets it
-          __builtin_amdgcn_s_sleep(1);
+          __syncthreads();
+          Tt* tmp = cb; cb = nb; nb = tmp;
         }
-        // publish this tile's inclusive prefix: Tot applied to Din
-        for (int m = tid; m < D; m += PNR_BLOCK) {
-          Tt v = Tot[D * D + m];
-          for (int k = 0; k < D; ++k) v = mul_add(Tot[m * D + k], Din[k], v);
-          vput(mpre + (size_t)m * W, ep, v);
-        }
-      }
-      // (4) increments entering each part: Pin[0] = Din, Pin[q+1] = agg_q(Pin[q])
-      for (int m = tid; m < D; m += PNR_BLOCK) Pin[m] = Din[m];
-      __syncthreads();
-      for (int q = 0; q < parts; ++q) {
-        if (tid < D) {
-          const Tt* ag = Pagg + (size_t)q * DD;
-          Tt v = ag[D * D + tid];
-          for (int k = 0; k < D; ++k) v = mul_add(ag[tid * D + k], Pin[q * D + k], v);
-          Pin[(q + 1) * D + tid] = v;
-        }
-        __syncthreads();
-      }
-      // (5) fix-up: each group walks its part with the dense J applied to its increment
-      Tt* cur = Fx;
-      Tt* nxt = Fx + parts * D;
-      if (in_group && j < D) cur[part * D + j] = Pin[part * D + j];
-      __syncthreads();
-      for (int st = 0; st < lp; ++st) {
-        const int s = part * lp + st;
-        if (in_group && j < D && s < L) {
-          const Tt* dv = cur + part * D;
-          Tt ur = 0, uz = 0, un = 0;
-          const Tt* rr = Us + (size_t)j * D;
-          const Tt* rz = Us + (size_t)(D + j) * D;
-          const Tt* rn = Us + (size_t)(2 * D + j) * D;
-          for (int k = 0; k < D; ++k) {
-            ur = mul_add(rr[k], dv[k], ur);
-            uz = mul_add(rz[k], dv[k], uz);
-            un = mul_add(rn[k], dv[k], un);
-          }
-          const int q = s * D + j;
-          const Tt v = Zv[q] * dv[j] + Al[q] * uz + Be[q] * ur + Ga[q] * un + R[q];
-          nxt[part * D + j] = v;
-          if (s < Lv) a.Hnext[((size_t)b * T + t0 + s) * D + j] = Hx[(s + 1) * D + j] + v;
-        }
-        __syncthreads();
-        Tt* tmp = cur; cur = nxt; nxt = tmp;
       }
     }
-  }
 
-  // ---- level 2 of the residual max: block partial -> global -> the last block merges ----
-  blk_max = wave_max_u64(blk_max);
-  if (lane == 0) s_wmax[wid] = blk_max;
-  __syncthreads();
-  if (tid == 0) {
-    uint64_t m = s_wmax[0];
-    for (int w = 1; w < PNR_WAVES; ++w) m = max(m, s_wmax[w]);
-    __hip_atomic_store(&a.partials[blockIdx.x], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __threadfence();
-    const uint32_t prev = atomicAdd(&ctrl->finished, 1u);
-    s_last = prev == gridDim.x - 1;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  uint64_t m = 0;
-  for (int i = tid; i < (int)gridDim.x; i += PNR_BLOCK) {
-    const uint64_t v = __hip_atomic_load(&a.partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    m = max(m, v);
-  }
-  m = wave_max_u64(m);
-  __syncthreads();
-  if (lane == 0) s_wmax[wid] = m;
-  __syncthreads();
-  if (tid == 0) {
-    for (int w = 0; w < PNR_WAVES; ++w) m = max(m, s_wmax[w]);
-    finish_iteration(ctrl, a.rho_hist, rho_of<Tt>(m), a.k, a.cur_buf, a.max_iters, a.tol);
+    // ---- two-level residual max: block partial -> global; the barrier's last block merges ----
+    blk_max = wave_max_u64(blk_max);
+    if (lane == 0) s_wmax[wid] = blk_max;
+    __syncthreads();
+    if (tid == 0) {
+      uint64_t m = s_wmax[0];
+      for (int w = 1; w < PNR_WAVES; ++w) m = max(m, s_wmax[w]);
+      __hip_atomic_store(&a.partials[blockIdx.x], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    grid_barrier(ctrl, [&]() {
+      uint64_t m = 0;
+      for (int i = tid; i < (int)gridDim.x; i += PNR_BLOCK) {
+        const uint64_t v = __hip_atomic_load(&a.partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        m = max(m, v);
+      }
+      m = wave_max_u64(m);
+      __syncthreads();
+      if (lane == 0) s_wmax[wid] = m;
+      __syncthreads();
+      if (tid == 0) {
+        for (int w = 0; w < PNR_WAVES; ++w) m = max(m, s_wmax[w]);
+        finish_iteration(ctrl, a.rho_hist, rho_of<Tt>(m), k, cur, a.max_iters, a.tol);
+      }
+    });
+    if (__hip_atomic_load(&ctrl->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) || has_fault(ctrl)) break;
+    cur = next;
   }
 }
 
@@ -558,53 +557,52 @@ int dense_tile_len(int D, int full, int) {
 
 static int dense_parts(int D, int full) { return full ? (64 / (D + 1)) * PNR_WAVES : PNR_BLOCK / D; }
 
-int dense_slot_words(int D, int full, int is_f64) { return dense_slot_words_dev(D, full, is_f64 ? 2 : 1); }
+int dense_slot_words(int D, int full, int is_f64) { return dense_slot_values(D, full) * (is_f64 ? 2 : 1); }
 
-size_t dense_lds_bytes(int D, int full, int is_f64, int stale) {
-  DenseLds<float> l{D, dense_tile_len(D, full, is_f64), full, stale, dense_parts(D, full)};
-  return l.count() * (is_f64 ? 8 : 4);
-}
-
-template <typename Tt, int DM, bool FULL, bool R>
-static hipError_t launch_one(const DenseIterArgs<Tt>& a, int num_cu, hipStream_t st, size_t lds) {
-  auto fn = dense_iter_kernel<Tt, DM, FULL, R>;
-  static size_t attr_set = 0;
-  if (lds > 65536 && lds > attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = lds;
-  }
-  int v = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, fn, PNR_BLOCK, lds) != hipSuccess || v < 1) v = 1;
-  long g = (long)v * num_cu;
-  if (g > kMaxGrid) g = kMaxGrid;
-  if (g > a.n_tiles) g = a.n_tiles;
-  if (g < 1) g = 1;
-  hipLaunchKernelGGL(fn, dim3((int)g), dim3(PNR_BLOCK), lds, st, a);
-  return hipGetLastError();
+size_t dense_lds_bytes(int D, int full, int is_f64, int reuse) {
+  const int es = is_f64 ? 8 : 4;
+  DenseLds l{D, dense_tile_len(D, full, is_f64), full, reuse, dense_parts(D, full), dense_window(D, full != 0, es)};
+  return l.count() * es;
 }
 
 template <typename Tt, int DM, bool FULL>
-static hipError_t launch_dm(const DenseIterArgs<Tt>& a, int num_cu, hipStream_t st) {
-  const bool stale = !a.resid_only && ((a.Hjac != a.Hcur) || a.jac_zero != a.cur_zero);
-  const size_t lds = dense_lds_bytes(a.D, FULL, sizeof(Tt) == 8, stale);
-  return a.resid_only ? launch_one<Tt, DM, FULL, true>(a, num_cu, st, lds)
-                      : launch_one<Tt, DM, FULL, false>(a, num_cu, st, lds);
+static int dense_capacity_t(int num_cu, size_t lds) {
+  auto fn = dense_newton_kernel<Tt, DM, FULL>;
+  if (lds > 65536) {
+    if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return 0;
+  }
+  int v = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, fn, PNR_BLOCK, lds) != hipSuccess) return 0;
+  long g = (long)v * num_cu;
+  return (int)(g > kMaxGrid ? kMaxGrid : g);
+}
+
+template <typename Tt, int DM, bool FULL>
+static hipError_t launch_t(const DenseLoopArgs<Tt>& a, int num_cu, hipStream_t st) {
+  const size_t lds = dense_lds_bytes(a.D, FULL, sizeof(Tt) == 8, a.nbuf > 2);
+  const int cap = dense_capacity_t<Tt, DM, FULL>(num_cu, lds);
+  if (cap < 1) return hipErrorInvalidConfiguration;
+  int grid = a.n_tiles < cap ? a.n_tiles : cap;
+  if (grid < 1) grid = 1;
+  void* args[] = {const_cast<DenseLoopArgs<Tt>*>(&a)};
+  return hipLaunchCooperativeKernel((const void*)dense_newton_kernel<Tt, DM, FULL>, dim3(grid), dim3(PNR_BLOCK),
+                                    args, (unsigned)lds, st);
 }
 
 template <typename Tt>
-static hipError_t launch_dense_t(const DenseIterArgs<Tt>& a, int full, int num_cu, hipStream_t st) {
-  if (!full) return launch_dm<Tt, 1, false>(a, num_cu, st);
-  if (a.D <= 4) return launch_dm<Tt, 4, true>(a, num_cu, st);
-  if (a.D <= 8) return launch_dm<Tt, 8, true>(a, num_cu, st);
-  if (a.D <= 16) return launch_dm<Tt, 16, true>(a, num_cu, st);
-  return launch_dm<Tt, 32, true>(a, num_cu, st);
+static hipError_t launch_dense_t(const DenseLoopArgs<Tt>& a, int full, int num_cu, hipStream_t st) {
+  if (!full) return launch_t<Tt, 1, false>(a, num_cu, st);
+  if (a.D <= 4) return launch_t<Tt, 4, true>(a, num_cu, st);
+  if (a.D <= 8) return launch_t<Tt, 8, true>(a, num_cu, st);
+  if (a.D <= 16) return launch_t<Tt, 16, true>(a, num_cu, st);
+  return launch_t<Tt, 32, true>(a, num_cu, st);
 }
 
-hipError_t launch_dense_iter_f32(const DenseIterArgs<float>& a, int full, int num_cu, hipStream_t st) {
+hipError_t launch_dense_newton_f32(const DenseLoopArgs<float>& a, int full, int num_cu, hipStream_t st) {
   return launch_dense_t<float>(a, full, num_cu, st);
 }
-hipError_t launch_dense_iter_f64(const DenseIterArgs<double>& a, int full, int num_cu, hipStream_t st) {
+hipError_t launch_dense_newton_f64(const DenseLoopArgs<double>& a, int full, int num_cu, hipStream_t st) {
   return launch_dense_t<double>(a, full, num_cu, st);
 }
 

@@ -1,8 +1,9 @@
-// One Newton iteration for the diagonal-recurrence cells (GRU_DIAG, LSTM_DIAG), fused:
-// cell + Jacobian + residual (every step at once), residual max (wave -> LDS -> block
-// partial -> last block), and the linear solve d_t = J_t d_{t-1} + r_t as a scan of
-// affine maps (thread-serial -> wave DPP -> LDS -> decoupled look-back across tiles),
-// followed by the update s <- s + d.
+// The Newton loop for the diagonal-recurrence cells (GRU_DIAG, LSTM_DIAG), one fused
+// pass per iteration: cell + Jacobian + residual (every step at once), residual max
+// (wave -> LDS -> block partial -> the last block at the grid barrier), and the linear
+// solve d_t = J_t d_{t-1} + r_t as a scan of affine maps (thread-serial -> wave DPP ->
+// LDS -> carry along a row, or a decoupled look-back across tiles), followed by the
+// update s <- s + d.  All iterations run inside one persistent, co-resident grid.
 //
 // Method: ParaRNN overview page, "Technical Implementation" (Newton's Iteration: a
 // Jacobian per iteration, block lower-triangular system, Jacobian reuse; Parallel
@@ -188,190 +189,224 @@ __device__ __forceinline__ float2 wave_shr1(float2 v, float2 lane0) {
   return make_float2(dpp_f<0x138>(lane0.x, v.x), dpp_f<0x138>(lane0.y, v.y));
 }
 
-// Decoupled look-back by one thread: returns the increment d entering tile `tile`.
+__device__ __forceinline__ float shfl_down_f(float v, int off) { return __shfl_down(v, off, 64); }
+__device__ __forceinline__ Aff1 shfl_down_e(const Aff1& v, int off) {
+  return Aff1{shfl_down_f(v.a, off), shfl_down_f(v.b, off)};
+}
+__device__ __forceinline__ Aff2 shfl_down_e(const Aff2& v, int off) {
+  return Aff2{shfl_down_f(v.a00, off), shfl_down_f(v.a01, off), shfl_down_f(v.a10, off),
+              shfl_down_f(v.a11, off), shfl_down_f(v.b0, off), shfl_down_f(v.b1, off)};
+}
+__device__ __forceinline__ float readlane_d(float v, int l) { return readlane_f(v, l); }
+__device__ __forceinline__ float2 readlane_d(float2 v, int l) {
+  return make_float2(readlane_f(v.x, l), readlane_f(v.y, l));
+}
+
+// Decoupled look-back over a window of 64 predecessors, run by one whole wave: lane w
+// inspects tile (tile-1-w).  The nearest predecessor that has published its inclusive
+// prefix, with every tile after it having published its aggregate, resolves the
+// increment entering this tile: d_in = agg_{tile-1} o ... o agg_{p+1} (prefix_p).  If no
+// prefix is visible in the window yet, the wave waits and reads the window again; tiles
+// publish prefixes in order from the start of each row, so a resolved prefix moves up
+// to 64 tiles per round trip.  Returns d_in in every lane.  The wait is bounded.
 template <class CellT>
-__device__ typename DeltaOf<typename CellT::E>::T lookback(uint64_t* slots, int tile, int seg,
-                                                         uint32_t ep, const typename CellT::E& tot) {
+__device__ typename DeltaOf<typename CellT::E>::T lookback_window(uint64_t* slots, int tile, int seg,
+                                                                uint32_t ep, const typename CellT::E& tot,
+                                                                Ctrl* ctrl) {
   using E = typename CellT::E;
   using Dl = typename DeltaOf<E>::T;
-  constexpr int SW = CellT::AGG_WORDS + CellT::PRE_WORDS;
+  constexpr int AW = CellT::AGG_WORDS, SW = CellT::AGG_WORDS + CellT::PRE_WORDS;
+  const int lane = (int)lane_id();
   uint64_t* mine = slots + (size_t)tile * SW;
+  const E idn = identity_of<E>();
   if (seg == 0) {
-    put_pre(mine + CellT::AGG_WORDS, ep, apply(tot, DeltaOf<E>::zero()));
+    if (lane == 0) put_pre(mine + AW, ep, apply(tot, DeltaOf<E>::zero()));
     return DeltaOf<E>::zero();
   }
-  put_agg(mine, ep, tot);
-  E acc = identity_of<E>();
-  int j = tile - 1;
-  Dl din;
+  if (lane == 0) put_agg(mine, ep, tot);
+  uint32_t spins = 0;
   while (true) {
-    const uint64_t* s = slots + (size_t)j * SW;
-    Dl pre;
-    if (get_pre(s + CellT::AGG_WORDS, ep, pre)) {
-      din = apply(acc, pre);
-      break;
+    const bool valid = lane < seg;
+    int st = 0;
+    E e = idn;
+    Dl pre = DeltaOf<E>::zero();
+    if (valid) {
+      const uint64_t* s = slots + (size_t)(tile - 1 - lane) * SW;
+      if (get_pre(s + AW, ep, pre)) st = 2;
+      else if (get_agg(s, ep, e)) st = 1;
     }
-    E agg;
-    if (get_agg(s, ep, agg)) {
-      acc = compose(acc, agg);
-      --j;
-      continue;
+    const uint64_t pm = __ballot(st == 2);
+    const uint64_t bad = __ballot(valid && st == 0);
+    if (pm) {
+      const int p = __ffsll((long long)pm) - 1;
+      const uint64_t before = p == 0 ? 0ull : ((1ull << p) - 1ull);
+      if ((bad & before) == 0) {
+        E x = lane < p ? e : idn;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          E o = shfl_down_e(x, off);
+          if (lane + off >= 64) o = idn;
+          x = compose(x, o);
+        }
+        const E x0 = readlane_aff(x, 0);
+        const Dl din = apply(x0, readlane_d(pre, p));
+        if (lane == 0) put_pre(mine + AW, ep, apply(tot, din));
+        return din;
+      }
     }
-    __builtin_amdgcn_s_sleep(1);
+    if (++spins > kSpinLimit) {
+      if (lane == 0) record_fault(ctrl, 1);
+      return DeltaOf<E>::zero();
+    }
+    backoff(spins);
   }
-  put_pre(mine + CellT::AGG_WORDS, ep, apply(tot, din));
-  return din;
 }
 
 // ---------------------------------------------------------------------------------
+// One tile (PNR_BLOCK*N consecutive steps of one row): residuals and Jacobians, the
+// scan, and the update.  d_in comes from the caller's carry (row walk) or from the
+// look-back.  Returns the increment at the tile's last step (the next tile's carry).
+template <int CELL>
+struct TileShared {
+  typename DiagCell<CELL>::E wtot[PNR_WAVES];
+  typename DeltaOf<typename DiagCell<CELL>::E>::T din;
+};
+
+struct IterView {
+  const float* Hcur;
+  const float* Hjac;
+  float* Hnext;
+  bool cur_zero, jac_zero, stale;
+  uint32_t ep;
+};
+
 template <int CELL, int N, bool RESID_ONLY>
-__global__ void __launch_bounds__(PNR_BLOCK) diag_iter_kernel(DiagIterArgs a) {
+__device__ __forceinline__ typename DeltaOf<typename DiagCell<CELL>::E>::T diag_tile(
+    const DiagLoopArgs& a, TileShared<CELL>& sh, int row, int seg, int tile, bool walk,
+    typename DeltaOf<typename DiagCell<CELL>::E>::T carry, const IterView& v, uint32_t& blk_max) {
   using C = DiagCell<CELL>;
   using E = typename C::E;
   using Dl = typename DeltaOf<E>::T;
   constexpr int G = C::G;
   constexpr int TILE = PNR_BLOCK * N;
-
-  __shared__ int s_tile;
-  __shared__ E s_wtot[PNR_WAVES];
-  __shared__ Dl s_din;
-  __shared__ uint32_t s_wmax[PNR_WAVES];
-  __shared__ int s_last;
-
-  Ctrl* ctrl = a.ctrl;
-  if (__hip_atomic_load(&ctrl->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return;
-
-  const int tid = threadIdx.x;
-  const int wid = tid >> 6;
-  const int lane = tid & 63;
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int D = a.D, T = a.T;
   const int S = D * C::SP;
   const bool vec = (T & 3) == 0;
-  const uint32_t ep = (uint32_t)a.k + 1u;
-  const bool stale = (a.Hjac != a.Hcur) || a.jac_zero != a.cur_zero;
-  uint32_t blk_max = 0;
+  const int b = row / D, d = row - b * D;
+  const int tb = seg * TILE + tid * N;
+  const bool stale = v.stale && !RESID_ONLY;
+  const int jac_mode = a.jac_mode;
 
-  while (true) {
-    if (tid == 0) s_tile = (int)atomicAdd(&ctrl->ticket, 1u);
-    __syncthreads();
-    const int tile = s_tile;
-    if (tile >= a.n_tiles) break;
-    const int row = tile / a.tiles_per_row;      // (b, d)
-    const int seg = tile - row * a.tiles_per_row;
-    const int b = row / D, d = row - b * D;
-    const int tb = seg * TILE + tid * N;         // first step of this thread
-
-    const typename C::Par q = C::load_par(a.u, a.bh, D, d);
-    // gate pre-activations from the input projection
-    float g[G][N];
+  const typename C::Par q = C::load_par(a.u, a.bh, D, d);
+  float g[G][N];
 #pragma unroll
-    for (int gg = 0; gg < G; ++gg)
-      load_n(a.gx + ((size_t)(b * G + gg) * D + d) * T, tb, T, vec, N, g[gg]);
+  for (int gg = 0; gg < G; ++gg) load_n(a.gx + ((size_t)(b * G + gg) * D + d) * T, tb, T, vec, N, g[gg]);
 
-    uint32_t tmax = 0;
-    E e[N];
-    float hc[C::SP][N];   // current state values (for the update)
-    if constexpr (CELL == PNR_CELL_GRU_DIAG) {
-      const size_t roff = ((size_t)b * S + d) * T;
-      float h[N], pj[N];
-      if (a.cur_zero) { for (int i = 0; i < N; ++i) h[i] = 0.f; }
-      else load_n(a.Hcur + roff, tb, T, vec, N, h);
-      float p0;
-      if (tb == 0) p0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
-      else p0 = (a.cur_zero || tb > T) ? 0.f : a.Hcur[roff + tb - 1];
-      if (stale && !RESID_ONLY) {
-        float pj0;
-        if (tb == 0) pj0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
-        else pj0 = (a.jac_zero || tb > T) ? 0.f : a.Hjac[roff + tb - 1];
-        float hj[N];
-        if (a.jac_zero) { for (int i = 0; i < N; ++i) hj[i] = 0.f; }
-        else load_n(a.Hjac + roff, tb, T, vec, N, hj);
-        pj[0] = pj0;
-        for (int i = 1; i < N; ++i) pj[i] = hj[i - 1];
-      }
+  uint32_t tmax = 0;
+  E e[N];
+  float hc[C::SP][N];
+  if constexpr (CELL == PNR_CELL_GRU_DIAG) {
+    const size_t roff = ((size_t)b * S + d) * T;
+    float h[N], pj[N];
+    if (v.cur_zero) { for (int i = 0; i < N; ++i) h[i] = 0.f; }
+    else load_n(v.Hcur + roff, tb, T, vec, N, h);
+    float p0;
+    if (tb == 0) p0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
+    else p0 = (v.cur_zero || tb > T) ? 0.f : v.Hcur[roff + tb - 1];
+    if (stale) {
+      float pj0;
+      if (tb == 0) pj0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
+      else pj0 = (v.jac_zero || tb > T) ? 0.f : v.Hjac[roff + tb - 1];
+      float hj[N];
+      if (v.jac_zero) { for (int i = 0; i < N; ++i) hj[i] = 0.f; }
+      else load_n(v.Hjac + roff, tb, T, vec, N, hj);
+      pj[0] = pj0;
+      for (int i = 1; i < N; ++i) pj[i] = hj[i - 1];
+    }
 #pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const float p = i == 0 ? p0 : h[i - 1];
-        float gi[3] = {g[0][i], g[1][i], g[2][i]};
-        float res, ja;
-        C::eval(q, gi, p, h[i], a.jac_mode, !stale && !RESID_ONLY, res, ja);
-        if (stale && !RESID_ONLY) ja = C::jac_only(q, gi, pj[i], a.jac_mode);
-        const bool valid = tb + i < T;
-        if (!valid) { res = 0.f; ja = 1.f; }
-        tmax = max(tmax, abs_bits(res));
-        e[i] = Aff1{ja, res};
-        hc[0][i] = h[i];
-      }
+    for (int i = 0; i < N; ++i) {
+      const float p = i == 0 ? p0 : h[i - 1];
+      float gi[3] = {g[0][i], g[1][i], g[2][i]};
+      float res, ja = 0.f;
+      C::eval(q, gi, p, h[i], jac_mode, !stale && !RESID_ONLY, res, ja);
+      if (stale) ja = C::jac_only(q, gi, pj[i], jac_mode);
+      if (tb + i >= T) { res = 0.f; ja = 1.f; }
+      tmax = max(tmax, abs_bits(res));
+      e[i] = Aff1{ja, res};
+      hc[0][i] = h[i];
+    }
+  } else {
+    const size_t coff = ((size_t)b * S + d) * T, hoff = ((size_t)b * S + D + d) * T;
+    float c[N], h[N];
+    if (v.cur_zero) { for (int i = 0; i < N; ++i) { c[i] = 0.f; h[i] = 0.f; } }
+    else { load_n(v.Hcur + coff, tb, T, vec, N, c); load_n(v.Hcur + hoff, tb, T, vec, N, h); }
+    float cp0, hp0;
+    if (tb == 0) {
+      cp0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
+      hp0 = a.h0 ? a.h0[(size_t)b * S + D + d] : 0.f;
+    } else if (v.cur_zero || tb > T) {
+      cp0 = 0.f; hp0 = 0.f;
     } else {
-      const size_t coff = ((size_t)b * S + d) * T, hoff = ((size_t)b * S + D + d) * T;
-      float c[N], h[N];
-      if (a.cur_zero) { for (int i = 0; i < N; ++i) { c[i] = 0.f; h[i] = 0.f; } }
-      else { load_n(a.Hcur + coff, tb, T, vec, N, c); load_n(a.Hcur + hoff, tb, T, vec, N, h); }
-      float cp0, hp0;
+      cp0 = v.Hcur[coff + tb - 1]; hp0 = v.Hcur[hoff + tb - 1];
+    }
+    float cj[N], hj[N], cpj0 = 0.f, hpj0 = 0.f;
+    if (stale) {
       if (tb == 0) {
-        cp0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
-        hp0 = a.h0 ? a.h0[(size_t)b * S + D + d] : 0.f;
-      } else if (a.cur_zero || tb > T) {
-        cp0 = 0.f; hp0 = 0.f;
-      } else {
-        cp0 = a.Hcur[coff + tb - 1]; hp0 = a.Hcur[hoff + tb - 1];
+        cpj0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
+        hpj0 = a.h0 ? a.h0[(size_t)b * S + D + d] : 0.f;
+      } else if (!(v.jac_zero || tb > T)) {
+        cpj0 = v.Hjac[coff + tb - 1]; hpj0 = v.Hjac[hoff + tb - 1];
       }
-      float cj[N], hj[N], cpj0 = 0.f, hpj0 = 0.f;
-      if (stale && !RESID_ONLY) {
-        if (tb == 0) {
-          cpj0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
-          hpj0 = a.h0 ? a.h0[(size_t)b * S + D + d] : 0.f;
-        } else if (!(a.jac_zero || tb > T)) {
-          cpj0 = a.Hjac[coff + tb - 1]; hpj0 = a.Hjac[hoff + tb - 1];
-        }
-        if (a.jac_zero) { for (int i = 0; i < N; ++i) { cj[i] = 0.f; hj[i] = 0.f; } }
-        else { load_n(a.Hjac + coff, tb, T, vec, N, cj); load_n(a.Hjac + hoff, tb, T, vec, N, hj); }
-      }
+      if (v.jac_zero) { for (int i = 0; i < N; ++i) { cj[i] = 0.f; hj[i] = 0.f; } }
+      else { load_n(v.Hjac + coff, tb, T, vec, N, cj); load_n(v.Hjac + hoff, tb, T, vec, N, hj); }
+    }
 #pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const float cp = i == 0 ? cp0 : c[i - 1];
-        const float hp = i == 0 ? hp0 : h[i - 1];
-        float gi[4] = {g[0][i], g[1][i], g[2][i], g[3][i]};
-        float rc, rh;
-        Aff2 J;
-        C::eval(q, gi, cp, hp, c[i], h[i], a.jac_mode, !stale && !RESID_ONLY, rc, rh, J);
-        if (stale && !RESID_ONLY) {
-          float dc, dh;
-          const float cpj = i == 0 ? cpj0 : cj[i - 1];
-          const float hpj = i == 0 ? hpj0 : hj[i - 1];
-          C::eval(q, gi, cpj, hpj, 0.f, 0.f, a.jac_mode, true, dc, dh, J);
-        }
-        const bool valid = tb + i < T;
-        if (!valid) { rc = 0.f; rh = 0.f; J = aff_identity2(); }
-        tmax = max(tmax, max(abs_bits(rc), abs_bits(rh)));
-        J.b0 = rc; J.b1 = rh;
-        e[i] = J;
-        hc[0][i] = c[i];
-        hc[1][i] = h[i];
+    for (int i = 0; i < N; ++i) {
+      const float cp = i == 0 ? cp0 : c[i - 1];
+      const float hp = i == 0 ? hp0 : h[i - 1];
+      float gi[4] = {g[0][i], g[1][i], g[2][i], g[3][i]};
+      float rc, rh;
+      Aff2 J = aff_identity2();
+      C::eval(q, gi, cp, hp, c[i], h[i], jac_mode, !stale && !RESID_ONLY, rc, rh, J);
+      if (stale) {
+        float dc, dh;
+        const float cpj = i == 0 ? cpj0 : cj[i - 1];
+        const float hpj = i == 0 ? hpj0 : hj[i - 1];
+        C::eval(q, gi, cpj, hpj, 0.f, 0.f, jac_mode, true, dc, dh, J);
       }
+      if (tb + i >= T) { rc = 0.f; rh = 0.f; J = aff_identity2(); }
+      tmax = max(tmax, max(abs_bits(rc), abs_bits(rh)));
+      J.b0 = rc; J.b1 = rh;
+      e[i] = J;
+      hc[0][i] = c[i];
+      hc[1][i] = h[i];
     }
-    blk_max = max(blk_max, tmax);
-    if constexpr (RESID_ONLY) {
-      __syncthreads();   // s_tile is rewritten by the next ticket
-      continue;
-    }
-
-    // ---- scan: thread-serial, then wave (DPP), then block (LDS), then look-back ----
+  }
+  blk_max = max(blk_max, tmax);
+  if constexpr (RESID_ONLY) {
+    return DeltaOf<E>::zero();
+  } else {
+    // ---- scan: thread-serial, then wave (DPP), then block (LDS), then carry / look-back ----
     E agg = e[0];
 #pragma unroll
     for (int i = 1; i < N; ++i) agg = compose(e[i], agg);
     const E idn = identity_of<E>();
     E incl = wave_inclusive_scan(agg, idn);
-    if (lane == 63) s_wtot[wid] = incl;
+    if (lane == 63) sh.wtot[wid] = incl;
     __syncthreads();
-    if (tid == 0) {
-      E tot = s_wtot[0];
-      for (int w = 1; w < PNR_WAVES; ++w) tot = compose(s_wtot[w], tot);
-      s_din = lookback<C>(a.slots, tile, seg, ep, tot);
+    E tot = sh.wtot[0];
+    for (int w = 1; w < PNR_WAVES; ++w) tot = compose(sh.wtot[w], tot);
+    if (walk) {
+      if (tid == 0) sh.din = carry;
+    } else if (wid == 0) {
+      const Dl din = lookback_window<C>(a.slots, tile, seg, v.ep, tot, a.ctrl);
+      if (lane == 0) sh.din = din;
     }
     __syncthreads();
-    Dl dw = s_din;
-    for (int w = 0; w < wid; ++w) dw = apply(s_wtot[w], dw);
+    const Dl din = sh.din;
+    Dl dw = din;
+    for (int w = 0; w < wid; ++w) dw = apply(sh.wtot[w], dw);
     Dl dout = apply(incl, dw);
     Dl dl = wave_shr1(dout, dw);   // increment entering this thread's first step
 
@@ -383,7 +418,7 @@ __global__ void __launch_bounds__(PNR_BLOCK) diag_iter_kernel(DiagIterArgs a) {
         dl = apply(e[i], dl);
         out[i] = hc[0][i] + dl;
       }
-      store_n(a.Hnext + ((size_t)b * S + d) * T, tb, T, vec, N, out);
+      store_n(v.Hnext + ((size_t)b * S + d) * T, tb, T, vec, N, out);
     } else {
       float oc[N], oh[N];
 #pragma unroll
@@ -392,82 +427,97 @@ __global__ void __launch_bounds__(PNR_BLOCK) diag_iter_kernel(DiagIterArgs a) {
         oc[i] = hc[0][i] + dl.x;
         oh[i] = hc[1][i] + dl.y;
       }
-      store_n(a.Hnext + ((size_t)b * S + d) * T, tb, T, vec, N, oc);
-      store_n(a.Hnext + ((size_t)b * S + D + d) * T, tb, T, vec, N, oh);
+      store_n(v.Hnext + ((size_t)b * S + d) * T, tb, T, vec, N, oc);
+      store_n(v.Hnext + ((size_t)b * S + D + d) * T, tb, T, vec, N, oh);
     }
-    __syncthreads();   // LDS (s_wtot, s_din, s_tile) is reused by the next tile
+    const Dl tile_out = apply(tot, din);
+    __syncthreads();   // sh is reused by the next tile
+    return tile_out;
   }
+}
 
-  // ---- level 2 of the residual max: block partial -> global -> the last block merges ----
-  blk_max = wave_max_u32(blk_max);
-  if (lane == 0) s_wmax[wid] = blk_max;
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t m = s_wmax[0];
-    for (int w = 1; w < PNR_WAVES; ++w) m = max(m, s_wmax[w]);
-    __hip_atomic_store(&a.partials[blockIdx.x], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __threadfence();
-    const uint32_t prev = atomicAdd(&ctrl->finished, 1u);
-    s_last = prev == gridDim.x - 1;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  uint32_t m = 0;
-  for (int i = tid; i < (int)gridDim.x; i += PNR_BLOCK)
-    m = max(m, __hip_atomic_load(&a.partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  m = wave_max_u32(m);
-  if (lane == 0) s_wmax[wid] = m;
-  __syncthreads();
-  if (tid == 0) {
-    for (int w = 1; w < PNR_WAVES; ++w) m = max(m, s_wmax[w]);
-    m = max(m, s_wmax[0]);
-    finish_iteration(ctrl, a.rho_hist, bits_to_rho(m), a.k, a.cur_buf, a.max_iters, a.tol);
-  }
+__device__ __forceinline__ int pick_next(int cur, int jac, int nbuf) {
+  for (int i = 0; i < nbuf; ++i)
+    if (i != cur && i != jac) return i;
+  return -1;
 }
 
 // ---------------------------------------------------------------------------------
-template <int CELL, int N, bool R>
-static int occupancy_grid(int n_tiles, int num_cu) {
-  static int per_cu = 0;
-  if (per_cu == 0) {
-    int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, diag_iter_kernel<CELL, N, R>, PNR_BLOCK, 0) !=
-            hipSuccess || v < 1)
-      v = 1;
-    per_cu = v;
-  }
-  long g = (long)per_cu * num_cu;
-  if (g > kMaxGrid) g = kMaxGrid;
-  if (g > n_tiles) g = n_tiles;
-  return (int)(g < 1 ? 1 : g);
-}
-
+// The whole Newton loop in one persistent, co-resident grid.  Iteration k: blocks take
+// work items from a ticket (a whole row in walk mode, one tile otherwise), then meet at
+// a grid barrier whose last block merges the residual partials and decides; after the
+// barrier every block reads the decision and either stops or starts iteration k+1.
+// The state buffers rotate exactly as the host would rotate them: the next iterate goes
+// to a buffer holding neither the current iterate nor the state the Jacobian is taken at.
 template <int CELL, int N>
-static hipError_t launch_cell(const DiagIterArgs& a, int num_cu, hipStream_t st, int* grid_out) {
-  int grid;
-  if (a.resid_only) {
-    grid = occupancy_grid<CELL, N, true>(a.n_tiles, num_cu);
-    hipLaunchKernelGGL((diag_iter_kernel<CELL, N, true>), dim3(grid), dim3(PNR_BLOCK), 0, st, a);
-  } else {
-    grid = occupancy_grid<CELL, N, false>(a.n_tiles, num_cu);
-    hipLaunchKernelGGL((diag_iter_kernel<CELL, N, false>), dim3(grid), dim3(PNR_BLOCK), 0, st, a);
+__global__ void __launch_bounds__(PNR_BLOCK) diag_newton_kernel(DiagLoopArgs a) {
+  using C = DiagCell<CELL>;
+  using E = typename C::E;
+  using Dl = typename DeltaOf<E>::T;
+  __shared__ TileShared<CELL> sh;
+  __shared__ uint32_t s_wmax[PNR_WAVES];
+  Ctrl* ctrl = a.ctrl;
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int n_items = a.walk ? a.n_rows : a.n_tiles;
+  int cur = -1, jac = -1;
+  for (int k = 0; k <= a.max_iters; ++k) {
+    const bool resid_only = k == a.max_iters;
+    if (!resid_only && k % a.jac_every == 0) jac = cur;
+    const int next = resid_only ? cur : pick_next(cur, jac, a.nbuf);
+    IterView v;
+    v.Hcur = cur >= 0 ? a.H[cur] : nullptr;
+    v.Hjac = jac >= 0 ? a.H[jac] : nullptr;
+    v.Hnext = next >= 0 ? a.H[next] : nullptr;
+    v.cur_zero = cur < 0;
+    v.jac_zero = jac < 0;
+    v.stale = jac != cur;
+    v.ep = (uint32_t)k + 1u;
+    uint32_t blk_max = 0;
+    // Static assignment, items in increasing order per block: with a co-resident grid
+    // the lowest unfinished tile never waits on anything, so the look-back always ends.
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+      if (a.walk) {
+        Dl carry = DeltaOf<E>::zero();
+        for (int seg = 0; seg < a.tiles_per_row; ++seg) {
+          if (resid_only)
+            diag_tile<CELL, N, true>(a, sh, item, seg, 0, true, carry, v, blk_max);
+          else
+            carry = diag_tile<CELL, N, false>(a, sh, item, seg, 0, true, carry, v, blk_max);
+        }
+      } else {
+        const int row = item / a.tiles_per_row, seg = item - row * a.tiles_per_row;
+        if (resid_only)
+          diag_tile<CELL, N, true>(a, sh, row, seg, item, false, DeltaOf<E>::zero(), v, blk_max);
+        else
+          diag_tile<CELL, N, false>(a, sh, row, seg, item, false, DeltaOf<E>::zero(), v, blk_max);
+      }
+      if (has_fault(ctrl)) break;
+    }
+    // ---- two-level residual max: block partial -> global; the barrier's last block merges ----
+    blk_max = wave_max_u32(blk_max);
+    if (lane == 0) s_wmax[wid] = blk_max;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t m = s_wmax[0];
+      for (int w = 1; w < PNR_WAVES; ++w) m = max(m, s_wmax[w]);
+      __hip_atomic_store(&a.partials[blockIdx.x], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    grid_barrier(ctrl, [&]() {
+      uint32_t m = 0;
+      for (int i = tid; i < (int)gridDim.x; i += PNR_BLOCK)
+        m = max(m, __hip_atomic_load(&a.partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      m = wave_max_u32(m);
+      __syncthreads();
+      if (lane == 0) s_wmax[wid] = m;
+      __syncthreads();
+      if (tid == 0) {
+        for (int w = 0; w < PNR_WAVES; ++w) m = max(m, s_wmax[w]);
+        finish_iteration(ctrl, a.rho_hist, bits_to_rho(m), k, cur, a.max_iters, a.tol);
+      }
+    });
+    if (__hip_atomic_load(&ctrl->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) || has_fault(ctrl)) break;
+    cur = next;
   }
-  if (grid_out) *grid_out = grid;
-  return hipGetLastError();
-}
-
-constexpr int kDiagN = 8;   // consecutive steps per thread (two float4 per state row)
-
-int diag_items_per_thread(int) { return kDiagN; }
-int diag_slot_words(int cell) {
-  return cell == PNR_CELL_LSTM_DIAG ? DiagCell<PNR_CELL_LSTM_DIAG>::AGG_WORDS + DiagCell<PNR_CELL_LSTM_DIAG>::PRE_WORDS
-                                    : DiagCell<PNR_CELL_GRU_DIAG>::AGG_WORDS + DiagCell<PNR_CELL_GRU_DIAG>::PRE_WORDS;
-}
-
-hipError_t launch_diag_iter(int cell, const DiagIterArgs& a, int num_cu, hipStream_t st, int* grid_out) {
-  if (cell == PNR_CELL_GRU_DIAG) return launch_cell<PNR_CELL_GRU_DIAG, kDiagN>(a, num_cu, st, grid_out);
-  return launch_cell<PNR_CELL_LSTM_DIAG, kDiagN>(a, num_cu, st, grid_out);
 }
 
 // ---------------------------------------------------------------------------------
@@ -495,7 +545,7 @@ __global__ void __launch_bounds__(PNR_BLOCK) scan_kernel(ScanArgs a) {
     if (tid == 0) s_tile = (int)atomicAdd(&a.ctrl->ticket, 1u);
     __syncthreads();
     const int tile = s_tile;
-    if (tile >= a.n_tiles) break;
+    if (tile >= a.n_tiles || has_fault(a.ctrl)) break;
     const int row = tile / a.tiles_per_row, seg = tile - row * a.tiles_per_row;
     const int tb = seg * TILE + tid * N;
     E e[N];
@@ -520,10 +570,11 @@ __global__ void __launch_bounds__(PNR_BLOCK) scan_kernel(ScanArgs a) {
     E incl = wave_inclusive_scan(agg, identity_of<E>());
     if (lane == 63) s_wtot[wid] = incl;
     __syncthreads();
-    if (tid == 0) {
+    if (wid == 0) {
       E tot = s_wtot[0];
       for (int w = 1; w < PNR_WAVES; ++w) tot = compose(s_wtot[w], tot);
-      s_din = lookback<C>(a.slots, tile, seg, 1u, tot);
+      const Dl din = lookback_window<C>(a.slots, tile, seg, 1u, tot, a.ctrl);
+      if (lane == 0) s_din = din;
     }
     __syncthreads();
     Dl dw = s_din;
@@ -545,6 +596,8 @@ __global__ void __launch_bounds__(PNR_BLOCK) scan_kernel(ScanArgs a) {
     __syncthreads();
   }
 }
+
+constexpr int kDiagN = 8;   // consecutive steps per thread (two float4 per state row)
 
 int scan_default_tile(int) { return PNR_BLOCK * kDiagN; }
 int scan_slot_words(int kind) { return diag_slot_words(kind == 1 ? PNR_CELL_GRU_DIAG : PNR_CELL_LSTM_DIAG); }
@@ -578,6 +631,39 @@ hipError_t launch_scan(int kind, int R, int T, const float* A, const float* b, f
     default: return hipErrorInvalidValue;
   }
 #undef PNR_SCAN_CASE
+}
+
+// ---------------------------------------------------------------------------------
+int diag_items_per_thread(int) { return kDiagN; }
+int diag_slot_words(int cell) {
+  return cell == PNR_CELL_LSTM_DIAG ? DiagCell<PNR_CELL_LSTM_DIAG>::AGG_WORDS + DiagCell<PNR_CELL_LSTM_DIAG>::PRE_WORDS
+                                    : DiagCell<PNR_CELL_GRU_DIAG>::AGG_WORDS + DiagCell<PNR_CELL_GRU_DIAG>::PRE_WORDS;
+}
+
+template <int CELL>
+static int diag_capacity(int num_cu) {
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int v = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, diag_newton_kernel<CELL, kDiagN>, PNR_BLOCK, 0) !=
+            hipSuccess || v < 1)
+      v = 1;
+    per_cu = v;
+  }
+  long g = (long)per_cu * num_cu;
+  return (int)(g > kMaxGrid ? kMaxGrid : g);
+}
+
+int diag_grid_capacity(int cell, int num_cu) {
+  return cell == PNR_CELL_GRU_DIAG ? diag_capacity<PNR_CELL_GRU_DIAG>(num_cu)
+                                   : diag_capacity<PNR_CELL_LSTM_DIAG>(num_cu);
+}
+
+hipError_t launch_diag_newton(int cell, const DiagLoopArgs& a, int grid, hipStream_t st) {
+  void* args[] = {const_cast<DiagLoopArgs*>(&a)};
+  const void* fn = cell == PNR_CELL_GRU_DIAG ? (const void*)diag_newton_kernel<PNR_CELL_GRU_DIAG, kDiagN>
+                                             : (const void*)diag_newton_kernel<PNR_CELL_LSTM_DIAG, kDiagN>;
+  return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(PNR_BLOCK), args, 0, st);
 }
 
 }  // namespace pnr

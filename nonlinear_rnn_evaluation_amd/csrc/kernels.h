@@ -31,71 +31,62 @@ __device__ inline void finish_iteration(Ctrl* c, double* hist, double rho, int k
     c->done = 1;
   }
   c->ticket = 0;
-  c->finished = 0;
 }
 
 // ---------------------------------------------------------------------------------
-struct DiagIterArgs {
+struct DiagLoopArgs {
   const float* gx;     // [B][G][D][T]
   const float* u;      // [G][D]
   const float* bh;     // [G*D] or nullptr
   const float* h0;     // [B][S] or nullptr
-  const float* Hcur;   // [B][S][T]
-  const float* Hjac;   // [B][S][T]: the state the Jacobian is taken at (== Hcur when fresh)
-  float* Hnext;        // [B][S][T]
+  float* H[3];         // state buffers [B][S][T]
+  int nbuf;            // 2, or 3 when the Jacobian is reused
   uint64_t* slots;     // look-back slots, n_tiles * slot words
   uint32_t* partials;  // per-block residual maxima
   Ctrl* ctrl;
   double* rho_hist;
-  int cur_zero;        // Hcur is the zero initial guess (not read)
-  int jac_zero;        // Hjac is the zero initial guess
   int B, D, T;
   int tiles_per_row;
-  int n_tiles;
-  int k;
-  int cur_buf;
-  int max_iters;
+  int n_tiles;         // B * D * tiles_per_row
+  int n_rows;          // B * D
+  int walk;            // 1: one block walks a whole row with a carry; 0: tiles + look-back
+  int max_iters, jac_every, jac_mode;
   double tol;
-  int jac_mode;
-  int resid_only;
 };
 
 int diag_items_per_thread(int cell);
 int diag_slot_words(int cell);
-hipError_t launch_diag_iter(int cell, const DiagIterArgs& a, int num_cu, hipStream_t st, int* grid_out);
+int diag_grid_capacity(int cell, int num_cu);
+hipError_t launch_diag_newton(int cell, const DiagLoopArgs& a, int grid, hipStream_t st);
 
 // ---------------------------------------------------------------------------------
 template <typename Tt>
-struct DenseIterArgs {
+struct DenseLoopArgs {
   const Tt* gx;        // [B][T][3D]
   const Tt* U;         // [3D][D]
   const Tt* bh;        // [3D] or nullptr
   const Tt* h0;        // [B][D] or nullptr
-  const Tt* Hcur;      // [B][T][D]
-  const Tt* Hjac;
-  Tt* Hnext;
+  Tt* H[3];            // state buffers [B][T][D]
+  int nbuf;
   uint64_t* slots;
   uint64_t* partials;
   Ctrl* ctrl;
   double* rho_hist;
-  int cur_zero, jac_zero;
   int B, D, T;
   int L;               // steps per tile
   int tiles_per_row;
   int n_tiles;
-  int k, cur_buf, max_iters;
+  int max_iters, jac_every, jac_mode;
   double tol;
-  int jac_mode;
-  int resid_only;
 };
 
 // Tile length and look-back slot words per tile for the dense GRU path.
 int dense_tile_len(int D, int full, int is_f64);
 int dense_slot_words(int D, int full, int is_f64);
-size_t dense_lds_bytes(int D, int full, int is_f64, int stale);
+size_t dense_lds_bytes(int D, int full, int is_f64, int reuse);
 int dense_supported(int D, int full, int is_f64);
-hipError_t launch_dense_iter_f32(const DenseIterArgs<float>& a, int full, int num_cu, hipStream_t st);
-hipError_t launch_dense_iter_f64(const DenseIterArgs<double>& a, int full, int num_cu, hipStream_t st);
+hipError_t launch_dense_newton_f32(const DenseLoopArgs<float>& a, int full, int num_cu, hipStream_t st);
+hipError_t launch_dense_newton_f64(const DenseLoopArgs<double>& a, int full, int num_cu, hipStream_t st);
 
 // ---------------------------------------------------------------------------------
 // Input projection C[z][i][j] = sum_k A[z][i][k] * Bm[z][j][k] + bias, both operands

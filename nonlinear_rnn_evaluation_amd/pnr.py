@@ -40,6 +40,11 @@ class PnrParams(ctypes.Structure):
                 ("b_h", ctypes.c_void_p)]
 
 
+class PnrProfile(ctypes.Structure):
+    _fields_ = [("total_ms", ctypes.c_double), ("proj_ms", ctypes.c_double), ("newton_ms", ctypes.c_double),
+                ("out_ms", ctypes.c_double), ("passes", ctypes.c_int32), ("resid_only", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -71,6 +76,10 @@ def load() -> ctypes.CDLL:
     lib.pnr_scan.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                              ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.pnr_scan.restype = ctypes.c_int
+    lib.pnr_profile_enable.argtypes = [ctypes.c_int]
+    lib.pnr_profile_enable.restype = ctypes.c_int
+    lib.pnr_last_profile.argtypes = [P(PnrProfile)]
+    lib.pnr_last_profile.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -140,6 +149,17 @@ def pnr_scan_workspace_bytes(kind: int, R: int, T: int, tile_len: int = 0) -> in
 def pnr_scan(kind: int, R: int, T: int, A: int, b: int, d: int, tile_len: int, workspace: int,
              workspace_bytes: int, stream: Optional[int]) -> int:
     return load().pnr_scan(kind, R, T, A, b, d, tile_len, workspace, workspace_bytes, stream)
+
+
+def pnr_profile_enable(on: bool) -> int:
+    return load().pnr_profile_enable(1 if on else 0)
+
+
+def pnr_last_profile() -> Optional[dict]:
+    p = PnrProfile()
+    if load().pnr_last_profile(ctypes.byref(p)) != 0:
+        return None
+    return {name: getattr(p, name) for name, _ in PnrProfile._fields_}
 
 
 # ---- torch-level conveniences (allocation + marshalling) ---------------------------------

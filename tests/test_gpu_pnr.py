@@ -119,10 +119,13 @@ def test_fixed_iterations_match_dense_newton_oracle(case, T):
                                    atol=tol_abs)
 
 
+@pytest.mark.parametrize("walk", ["0", "1"])
 @pytest.mark.parametrize("cell", [WL.CELL_GRU_DIAG, WL.CELL_LSTM_DIAG])
 @pytest.mark.parametrize("T", [4096 + 2048 + 123, 2 * 2048, 4099])
-def test_fixed_iterations_multi_tile_diag(cell, T):
-    """Several 2048-step tiles per row plus a ragged tail (and T % 4 != 0: scalar loads)."""
+def test_fixed_iterations_multi_tile_diag(cell, T, walk, monkeypatch):
+    """Several 2048-step tiles per row plus a ragged tail (and T % 4 != 0: scalar loads),
+    with rows cut into look-back tiles (walk=0) or walked whole by one block (walk=1)."""
+    monkeypatch.setenv("PNR_DIAG_WALK", walk)
     p = WL.random_problem(cell, 2, T, 3, 4, seed=T, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32,
                           bias_std=0.2, h0_std=0.3)
     q = _f64(p)
@@ -211,6 +214,20 @@ def test_one_iteration_not_converged_and_short_sequences():
     p = WL.random_problem(WL.CELL_GRU, 1, 300, 4, 2, seed=9, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32)
     got = _run(WL.CELL_GRU, p, 1, 1e-12, WL.JAC_FULL)
     assert got["status"] == pnr.NOT_CONVERGED and got["iters"] == 1
+
+
+@pytest.mark.parametrize("walk", ["0", "1"])
+def test_long_rows_lookback_and_walk_agree_with_sequential(walk, monkeypatch):
+    """One row of 150 tiles: the windowed look-back must resolve prefixes across many tiles."""
+    monkeypatch.setenv("PNR_DIAG_WALK", walk)
+    cell = WL.CELL_LSTM_DIAG
+    p = WL.random_problem(cell, 1, 150 * 2048 + 77, 1, 3, seed=4, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32,
+                          bias_std=0.2)
+    q = _f64(p)
+    got = _run(cell, p, 100, 1e-6, WL.JAC_FULL, 2)
+    assert got["status"] == pnr.OK
+    ref = O.sequential(cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"])
+    assert np.abs(_np(got["h"]) - ref).max() < 1e-4
 
 
 def test_repeated_calls_reuse_workspace():
