@@ -14,6 +14,8 @@ namespace pnr {
 
 // ---------------------------------------------------------------------------------
 // Control block written only on the device during a call; read back once at the end.
+constexpr int kBarGroups = 32;   // first-level arrival counters of the grid barrier
+
 struct Ctrl {
   int32_t done;        // 1 once the loop has decided (converged, non-finite, or exhausted)
   int32_t status;      // pnr_status
@@ -23,11 +25,14 @@ struct Ctrl {
   uint32_t ticket;     // dynamic tile counter (standalone scan)
   int32_t fault;       // a bounded device wait ran out (1 = look-back, 2 = barrier)
   uint32_t pad0[24];
-  // the grid-barrier words sit on cache lines of their own: every block polls bar_gen
-  uint32_t bar_count;  // grid barrier: blocks arrived
+  // Grid barrier.  Every counter sits on a 256-byte line of its own: blocks arrive on
+  // one of kBarGroups group counters, the last of each group on the top counter, and
+  // all blocks poll the generation word.
+  uint32_t bar_top;
   uint32_t pad1[63];
-  uint32_t bar_gen;    // grid barrier: generation, bumped by the last block to arrive
+  uint32_t bar_gen;
   uint32_t pad2[63];
+  struct { uint32_t count; uint32_t pad[63]; } bar_group[kBarGroups];
 };
 
 // Bound on every device-side wait (polls of a look-back slot or of the grid barrier).
@@ -50,11 +55,23 @@ __device__ __forceinline__ bool has_fault(const Ctrl* c) {
   return __hip_atomic_load(&c->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
 }
 
-// Grid-wide barrier for a persistent, co-resident grid.  The last block to arrive runs
-// `merge` (the whole block, after an acquire fence) before it releases the others --
-// the "final block" of a two-level reduction.  Global writes before the barrier are
-// released with an agent-scope fence and acquired after it, so blocks on other XCDs
-// (each with its own L2) see them.  The wait is bounded (kSpinLimit).
+// Wait until every memory operation this thread issued has completed.  Atomic (agent
+// scope) operations complete at the device's coherence point, so an atomic issued after
+// this wait is ordered after them for every observer -- without the L2 write-back and
+// invalidate that an agent-scope fence costs on a multi-XCD device.
+__device__ __forceinline__ void drain_memory_ops() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Grid-wide barrier for a persistent, co-resident grid whose blocks exchange data only
+// through agent-scope atomics (look-back slots, residual partials, the control block)
+// and whose other global data is private to a block across the barrier.  Arrival is
+// two-level (a group counter, then the top counter for the last of each group); the
+// last block to arrive runs `merge` -- the "final block" of the residual reduction --
+// then resets the counters and bumps the generation that the others poll.  The wait is
+// bounded (kSpinLimit) and records a fault instead of hanging.
 template <class Merge>
 __device__ __forceinline__ void grid_barrier(Ctrl* c, Merge merge) {
   __shared__ int s_last;
@@ -62,19 +79,28 @@ __device__ __forceinline__ void grid_barrier(Ctrl* c, Merge merge) {
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t gen = __hip_atomic_load(&c->bar_gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __threadfence();
-    const uint32_t prev = atomicAdd(&c->bar_count, 1u);
-    s_last = prev == gridDim.x - 1;
+    drain_memory_ops();
+    const uint32_t g = blockIdx.x % kBarGroups;
+    const uint32_t members = (gridDim.x - g + kBarGroups - 1) / kBarGroups;
+    int last = 0;
+    const uint32_t prev = atomicAdd(&c->bar_group[g].count, 1u);
+    if (prev == members - 1) {
+      __hip_atomic_store(&c->bar_group[g].count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      drain_memory_ops();
+      const uint32_t groups = gridDim.x < (unsigned)kBarGroups ? gridDim.x : (unsigned)kBarGroups;
+      const uint32_t top = atomicAdd(&c->bar_top, 1u);
+      last = top == groups - 1;
+    }
+    s_last = last;
     s_gen = gen;
   }
   __syncthreads();
   if (s_last) {
-    __threadfence();
     merge();
     __syncthreads();
     if (threadIdx.x == 0) {
-      __hip_atomic_store(&c->bar_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __threadfence();
+      __hip_atomic_store(&c->bar_top, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      drain_memory_ops();
       __hip_atomic_store(&c->bar_gen, s_gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   } else if (threadIdx.x == 0) {
@@ -86,9 +112,23 @@ __device__ __forceinline__ void grid_barrier(Ctrl* c, Merge merge) {
         break;
       }
     }
-    __threadfence();
   }
   __syncthreads();
+}
+
+// Coherent (agent-scope) scalar load of data another block may have written during this
+// kernel, e.g. the last state of the preceding tile.
+__device__ __forceinline__ float coherent_load(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double coherent_load(const double* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void coherent_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void coherent_store(double* p, double v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------------

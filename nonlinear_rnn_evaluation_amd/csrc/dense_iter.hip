@@ -39,12 +39,22 @@ template <typename Tt> struct WordsOf { static constexpr int W = sizeof(Tt) / 4;
 // look-back slot values per tile: FULL holds the (D*D + D)-value aggregate then the
 // D-value prefix; DIAG holds D values of a, D of b, then D prefixes.
 __host__ __device__ inline int dense_slot_values(int D, bool full) { return full ? D * D + 2 * D : 3 * D; }
+// dense-Jacobian scan: parts (one lane group of D+1 lanes each) per tile; few enough
+// that the serial composition of the part aggregates stays short
+__host__ __device__ inline int dense_full_parts(int D) {
+  const int groups = (64 / (D + 1)) * PNR_WAVES;
+  return groups < 8 ? groups : 8;
+}
 __host__ __device__ inline int dense_agg_values(int D, bool full) { return full ? D * D + D : 2 * D; }
 // predecessors inspected per look-back round trip (bounded by the LDS it takes)
-__host__ __device__ inline int dense_window(int D, bool full, int es) {
-  int w = (24 * 1024) / (dense_slot_values(D, full) * es);
-  return w < 2 ? 2 : (w > 16 ? 16 : w);
+constexpr int kWinPerThread = 16;
+constexpr int kBatch = 8;   // loads issued together before any is used
+__host__ __device__ inline int dense_window(int D, bool full, int) {
+  int w = (PNR_BLOCK * kWinPerThread) / dense_slot_values(D, full);
+  return w < 1 ? 1 : (w > 16 ? 16 : w);
 }
+// staged state values per thread: (L+1)*D <= PNR_BLOCK * kStagePerThread
+constexpr int kStagePerThread = 17;
 
 __device__ __forceinline__ void vput(uint64_t* s, uint32_t ep, float v) { slot_put(s, ep, v); }
 __device__ __forceinline__ bool vget(const uint64_t* s, uint32_t ep, float& v) { return slot_get(s, ep, v); }
@@ -81,9 +91,12 @@ __device__ __forceinline__ double mul_add(double a, double b, double c) { return
 
 // ---------------------------------------------------------------------------------
 // LDS layout (dynamic shared memory), in units of Tt:
-//   Us   [D][3D]     recurrent matrix, transposed   Bh   [3D]   recurrent bias
-//   Hx   [L+1][D]    Hx[0] = s_{t0-1}, Hx[1+s] = current iterate at step t0+s
-//   Hj   [L+1][D]    same for the state the Jacobian is taken at (Jacobian reuse only)
+//   Us   [D][3D]     recurrent matrix, transposed (absent when the cell runs on MFMA
+//                    and the scan is diagonal: U then lives in registers)
+//   Bh   [3D]        recurrent bias
+//   Hx   [L+1][LD]   Hx[0] = s_{t0-1}, Hx[1+s] = current iterate at step t0+s; rows
+//                    padded to LD = D+4 on the MFMA path (conflict-free operand reads)
+//   Hj   [L+1][LD]   same for the state the Jacobian is taken at (Jacobian reuse only)
 //   R    [L][D]      residuals
 //   Jd   [L][D]      diagonal Jacobian (DIAG)  |  Z, Al, Be, Ga [L][D] factors (FULL)
 //   Pagg             per-part aggregates: DIAG [2][parts][D]; FULL [parts][D*D + D]
@@ -93,9 +106,9 @@ __device__ __forceinline__ double mul_add(double a, double b, double c) { return
 //   Win  [WMAX][slot values]  look-back window
 //   Din  [D]         increment entering the tile
 struct DenseLds {
-  int D, L, full, reuse, parts, wmax;
+  int D, L, full, reuse, parts, wmax, ld, has_u;
   __host__ __device__ size_t count() const {
-    size_t n = (size_t)3 * D * D + 3 * D + (size_t)(L + 1) * D * (reuse ? 2 : 1) + (size_t)L * D;
+    size_t n = (has_u ? (size_t)3 * D * D : 0) + 3 * D + (size_t)(L + 1) * ld * (reuse ? 2 : 1) + (size_t)L * D;
     if (full) {
       n += (size_t)4 * L * D + (size_t)parts * (D * D + D) + (D * D + D) + (size_t)(parts + 1) * D +
            (size_t)2 * parts * D;
@@ -135,7 +148,29 @@ __device__ __forceinline__ int pick_next_dense(int cur, int jac, int nbuf) {
   return -1;
 }
 
-template <typename Tt, int DM, bool FULL>
+typedef float f4mf_t __attribute__((ext_vector_type(4)));
+
+// Gate pre-activations from the recurrent product on MFMA (fp32, D in {16, 32, 64}):
+// Gh[t][g*D + c] = sum_k Hp[t][k] U[g*D + c][k] for one 16-step x 16-channel block, as
+// D/4 chained v_mfma_f32_16x16x4_f32 per gate.  A = Hp rows from LDS (lane l: step l%16,
+// k = 4kk + l/16); B = U fragments held in registers for the whole kernel (lane l:
+// channel l%16, k = 4kk + l/16).  Result: lane l holds steps 4(l/16)+i, channel l%16.
+template <int DM>
+__device__ __forceinline__ void mfma_gates(const float* __restrict__ Hrows, int LD, int tb,
+                                           const float (&uf)[3][DM / 4], f4mf_t (&acc)[3]) {
+  const int l = (int)lane_id();
+  const float* arow = Hrows + (size_t)(tb * 16 + (l & 15)) * LD + (l >> 4);
+#pragma unroll
+  for (int g = 0; g < 3; ++g) acc[g] = f4mf_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < DM / 4; ++kk) {
+    const float av = arow[4 * kk];
+#pragma unroll
+    for (int g = 0; g < 3; ++g) acc[g] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, uf[g][kk], acc[g], 0, 0, 0);
+  }
+}
+
+template <typename Tt, int DM, bool FULL, bool MF>
 __global__ void __launch_bounds__(PNR_BLOCK) dense_newton_kernel(DenseLoopArgs<Tt> a) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
   Tt* lds = reinterpret_cast<Tt*>(lds_raw);
@@ -149,18 +184,20 @@ __global__ void __launch_bounds__(PNR_BLOCK) dense_newton_kernel(DenseLoopArgs<T
   const bool reuse = a.nbuf > 2;
   const int GS = D + 1;                       // FULL: lanes per group
   const int GPW = FULL ? 64 / GS : 0;         // FULL: groups per wave
-  const int parts = FULL ? GPW * PNR_WAVES : PNR_BLOCK / D;
+  const int parts = FULL ? dense_full_parts(D) : PNR_BLOCK / D;
   constexpr int W = WordsOf<Tt>::W;
   const int SV = dense_slot_values(D, FULL), SA = dense_agg_values(D, FULL);
   const int WMAX = dense_window(D, FULL, (int)sizeof(Tt));
   const int DD = D * D + D;
+  constexpr bool HAS_U = !MF || FULL;
+  const int LD = MF ? D + 4 : D;
 
   // carve LDS
   Tt* Us = lds;
-  Tt* Bh = Us + 3 * D * D;
+  Tt* Bh = Us + (HAS_U ? 3 * D * D : 0);
   Tt* Hx = Bh + 3 * D;
-  Tt* Hj = Hx + (L + 1) * D;
-  Tt* R = Hj + (reuse ? (L + 1) * D : 0);
+  Tt* Hj = Hx + (L + 1) * LD;
+  Tt* R = Hj + (reuse ? (L + 1) * LD : 0);
   Tt* Jd = R + L * D;            // DIAG
   Tt* Zv = R + L * D;            // FULL factors
   Tt* Al = Zv + L * D;
@@ -173,11 +210,29 @@ __global__ void __launch_bounds__(PNR_BLOCK) dense_newton_kernel(DenseLoopArgs<T
   Tt* Win = Fx + (FULL ? 2 * parts * D : 0);
   Tt* Din = Win + WMAX * SV;
 
-  for (int idx = tid; idx < 3 * D * D; idx += PNR_BLOCK) {
-    const int row = idx / D, k = idx - row * D;     // U[row][k] -> Ut[k][row]
-    Us[(size_t)k * 3 * D + row] = a.U[idx];
+  if constexpr (HAS_U) {
+    for (int idx = tid; idx < 3 * D * D; idx += PNR_BLOCK) {
+      const int row = idx / D, k = idx - row * D;     // U[row][k] -> Ut[k][row]
+      Us[(size_t)k * 3 * D + row] = a.U[idx];
+    }
   }
   for (int idx = tid; idx < 3 * D; idx += PNR_BLOCK) Bh[idx] = a.bh ? a.bh[idx] : Tt(0);
+  // MFMA path: this wave's U fragments and diagonal entries, in registers for the kernel
+  constexpr int KF = MF ? DM / 4 : 1;
+  float uf[3][KF];
+  float udg[3] = {0.f, 0.f, 0.f};
+  const int mf_cb = MF ? wid % (DM / 16) : 0;             // channel block of this wave
+  const int mf_tb0 = MF ? wid / (DM / 16) : 0;            // first step block of this wave
+  const int mf_tbs = MF ? PNR_WAVES / (DM / 16) : 1;      // step-block stride
+  if constexpr (MF) {
+    const int c = mf_cb * 16 + (lane & 15);
+#pragma unroll
+    for (int g = 0; g < 3; ++g) {
+#pragma unroll
+      for (int kk = 0; kk < KF; ++kk) uf[g][kk] = (float)a.U[(size_t)(g * D + c) * D + 4 * kk + (lane >> 4)];
+      udg[g] = (float)a.U[(size_t)(g * D + c) * D + c];
+    }
+  }
   __syncthreads();
 
   int cur = -1, jac = -1;
@@ -203,24 +258,106 @@ __global__ void __launch_bounds__(PNR_BLOCK) dense_newton_kernel(DenseLoopArgs<T
       const Tt* gxb = a.gx + (size_t)b * T * 3 * D;
 
       // ---- stage states: Hx[0] = s_{t0-1}; Hx[1+s] = iterate at t0+s ----
-      for (int idx = tid; idx < (L + 1) * D; idx += PNR_BLOCK) {
-        const int s = idx / D, c = idx - s * D;
-        const int t = t0 + s - 1;
-        Tt v = Tt(0);
-        if (t < 0) v = a.h0 ? a.h0[(size_t)b * D + c] : Tt(0);
-        else if (t < T && Hcur) v = Hcur[((size_t)b * T + t) * D + c];
-        Hx[idx] = v;
-        if (stale) {
-          Tt w = Tt(0);
-          if (t < 0) w = a.h0 ? a.h0[(size_t)b * D + c] : Tt(0);
-          else if (t < T && Hjac) w = Hjac[((size_t)b * T + t) * D + c];
-          Hj[idx] = w;
+      // All of a thread's loads are issued before any is used, so they overlap.  Row
+      // s = 0 is the last step of the previous tile, written by another block during
+      // this kernel: it is read coherently; the other rows are this block's own.
+      for (int j0 = 0; j0 < kStagePerThread; j0 += kBatch) {
+        Tt hv[kBatch], jv[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int idx = tid + (j0 + j) * PNR_BLOCK;
+          hv[j] = Tt(0);
+          jv[j] = Tt(0);
+          if (idx < (L + 1) * D) {
+            const int s = idx / D, c = idx - s * D;
+            const int t = t0 + s - 1;
+            const size_t gi = ((size_t)b * T + t) * D + c;
+            if (t < 0) {
+              hv[j] = a.h0 ? a.h0[(size_t)b * D + c] : Tt(0);
+              jv[j] = hv[j];
+            } else if (t < T) {
+              if (Hcur) hv[j] = s == 0 ? coherent_load(Hcur + gi) : Hcur[gi];
+              if (stale && Hjac) jv[j] = s == 0 ? coherent_load(Hjac + gi) : Hjac[gi];
+            }
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int idx = tid + (j0 + j) * PNR_BLOCK;
+          if (idx < (L + 1) * D) {
+            const int s = idx / D, c = idx - s * D;
+            Hx[s * LD + c] = hv[j];
+            if (stale) Hj[s * LD + c] = jv[j];
+          }
         }
       }
       __syncthreads();
 
       // ---- cell: gates, residual, Jacobian (diagonal or factors) ----
       uint64_t tmax = 0;
+      if constexpr (MF) {
+        // recurrent product on MFMA; lane l then owns steps tb*16 + 4(l/16) + i of
+        // channel c for its wave's blocks
+        const int c = mf_cb * 16 + (lane & 15);
+        const float bhr = Bh[c], bhz = Bh[D + c], bhn = Bh[2 * D + c];
+        for (int tb = mf_tb0; tb < L / 16; tb += mf_tbs) {
+          // input pre-activations of this lane's 4 steps, loaded before the MFMAs
+          float gxv[4][3];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int s = tb * 16 + 4 * (lane >> 4) + i;
+            const Tt* g = gxb + (size_t)(t0 + s) * 3 * D;
+#pragma unroll
+            for (int q = 0; q < 3; ++q) gxv[i][q] = s < Lv ? g[q * D + c] : 0.f;
+          }
+          f4mf_t acc[3], accj[3];
+          mfma_gates<DM>(Hx, LD, tb, uf, acc);
+          if (stale) mfma_gates<DM>(Hj, LD, tb, uf, accj);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int s = tb * 16 + 4 * (lane >> 4) + i;
+            const int idx = s * D + c;
+            if (s >= Lv) {
+              R[idx] = Tt(0);
+              if (!resid_only) {
+                if (FULL) { Zv[idx] = Tt(1); Al[idx] = Tt(0); Be[idx] = Tt(0); Ga[idx] = Tt(0); }
+                else Jd[idx] = Tt(1);
+              }
+              continue;
+            }
+            const float p = Hx[s * LD + c];
+            float r = sigm(gxv[i][0] + acc[0][i] + bhr);
+            float z = sigm(gxv[i][1] + acc[1][i] + bhz);
+            float ghn = acc[2][i] + bhn;
+            float n = tanh_(fmaf(r, ghn, gxv[i][2]));
+            const float res = fmaf(z, p - n, n) - Hx[(s + 1) * LD + c];
+            R[idx] = res;
+            tmax = max(tmax, abs_bits64(res));
+            if (resid_only) continue;
+            float pj = p;
+            if (stale) {
+              pj = Hj[s * LD + c];
+              r = sigm(gxv[i][0] + accj[0][i] + bhr);
+              z = sigm(gxv[i][1] + accj[1][i] + bhz);
+              ghn = accj[2][i] + bhn;
+              n = tanh_(fmaf(r, ghn, gxv[i][2]));
+            }
+            const float omz = 1.f - z;
+            const float cn = omz * (1.f - n * n);
+            const float al = (pj - n) * z * omz;
+            const float be = cn * ghn * r * (1.f - r);
+            const float ga = cn * r;
+            if (a.jac_mode == PNR_JAC_ZERO) {
+              if (FULL) { Zv[idx] = Tt(0); Al[idx] = Tt(0); Be[idx] = Tt(0); Ga[idx] = Tt(0); }
+              else Jd[idx] = Tt(0);
+            } else if (FULL) {
+              Zv[idx] = z; Al[idx] = al; Be[idx] = be; Ga[idx] = ga;
+            } else {
+              Jd[idx] = z + al * udg[1] + be * udg[0] + ga * udg[2];
+            }
+          }
+        }
+      } else {
       for (int idx = tid; idx < L * D; idx += PNR_BLOCK) {
         const int s = idx / D, i = idx - s * D;
         if (s >= Lv) {
@@ -232,17 +369,17 @@ __global__ void __launch_bounds__(PNR_BLOCK) dense_newton_kernel(DenseLoopArgs<T
           continue;
         }
         const Tt* g = gxb + (size_t)(t0 + s) * 3 * D;
-        const Tt* p = Hx + s * D;
+        const Tt* p = Hx + s * LD;
         Tt r, z, n, ghn;
         gru_gates(Us, Bh, p, g, D, i, r, z, n, ghn);
         const Tt f = mul_add(z, p[i] - n, n);
-        const Tt res = f - Hx[(s + 1) * D + i];
+        const Tt res = f - Hx[(s + 1) * LD + i];
         R[idx] = res;
         tmax = max(tmax, abs_bits64(res));
         if (resid_only) continue;
         const Tt* pj = p;
         if (stale) {
-          pj = Hj + s * D;
+          pj = Hj + s * LD;
           gru_gates(Us, Bh, pj, g, D, i, r, z, n, ghn);
         }
         const Tt omz = Tt(1) - z;
@@ -260,6 +397,7 @@ __global__ void __launch_bounds__(PNR_BLOCK) dense_newton_kernel(DenseLoopArgs<T
           Jd[idx] = z + al * ud[D + i] + be * ud[i] + ga * ud[2 * D + i];
         }
       }
+      }
       blk_max = max(blk_max, tmax);
       __syncthreads();
       if (resid_only) continue;
@@ -268,8 +406,8 @@ __global__ void __launch_bounds__(PNR_BLOCK) dense_newton_kernel(DenseLoopArgs<T
       const int p = tid / D, ci = tid - p * D;                    // DIAG thread layout
       const int lpd = (L + parts - 1) / parts;                    // DIAG steps per part
       const int gi = lane / GS, jl = lane - gi * GS;              // FULL group layout
-      const bool in_group = FULL && gi < GPW;
       const int part = wid * GPW + gi;
+      const bool in_group = FULL && gi < GPW && part < parts;
       const int lpf = (L + parts - 1) / parts;
       Tt keep_a = Tt(1), keep_b = Tt(0);   // DIAG: this tile's total (a, b) for channel tid
 
@@ -392,12 +530,29 @@ __global__ void __launch_bounds__(PNR_BLOCK) dense_newton_kernel(DenseLoopArgs<T
           const int Wn = min(seg, WMAX);
           if (tid < Wn) { s_ok[tid][0] = 1; s_ok[tid][1] = 1; }
           __syncthreads();
-          for (int idx = tid; idx < Wn * SV; idx += PNR_BLOCK) {
-            const int w = idx / SV, e = idx - w * SV;
-            const uint64_t* js = a.slots + (size_t)(tile - 1 - w) * SV * W;
-            Tt v;
-            if (!vget(js + (size_t)e * W, ep, v)) s_ok[w][e < SA ? 0 : 1] = 0;
-            Win[w * SV + e] = v;
+          for (int j0 = 0; j0 < kWinPerThread; j0 += kBatch) {
+            // issue a batch of slot reads, then consume them
+            Tt wv[kBatch];
+            bool wok[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+              const int idx = tid + (j0 + j) * PNR_BLOCK;
+              wok[j] = true;
+              wv[j] = Tt(0);
+              if (idx < Wn * SV) {
+                const int w = idx / SV, e = idx - w * SV;
+                wok[j] = vget(a.slots + ((size_t)(tile - 1 - w) * SV + e) * W, ep, wv[j]);
+              }
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+              const int idx = tid + (j0 + j) * PNR_BLOCK;
+              if (idx < Wn * SV) {
+                const int w = idx / SV, e = idx - w * SV;
+                if (!wok[j]) s_ok[w][e < SA ? 0 : 1] = 0;
+                Win[w * SV + e] = wv[j];
+              }
+            }
           }
           __syncthreads();
           if (tid == 0) {
@@ -468,7 +623,10 @@ __global__ void __launch_bounds__(PNR_BLOCK) dense_newton_kernel(DenseLoopArgs<T
           for (int q = 0; q < p; ++q) dl = mul_add(Sa[q * D + ci], dl, Sb[q * D + ci]);
           for (int s = p * lpd; s < min(Lv, (p + 1) * lpd); ++s) {
             dl = mul_add(Jd[s * D + ci], dl, R[s * D + ci]);
-            Hnext[((size_t)b * T + t0 + s) * D + ci] = Hx[(s + 1) * D + ci] + dl;
+            Tt* o = Hnext + ((size_t)b * T + t0 + s) * D + ci;
+            // the tile's last row is the next tile's halo, read by another block next pass
+            if (s == L - 1) coherent_store(o, Hx[(s + 1) * LD + ci] + dl);
+            else *o = Hx[(s + 1) * LD + ci] + dl;
           }
         }
         __syncthreads();
@@ -502,7 +660,11 @@ __global__ void __launch_bounds__(PNR_BLOCK) dense_newton_kernel(DenseLoopArgs<T
             const int qi = s * D + jl;
             const Tt v = Zv[qi] * dv[jl] + Al[qi] * uz + Be[qi] * ur + Ga[qi] * un + R[qi];
             nb[part * D + jl] = v;
-            if (s < Lv) Hnext[((size_t)b * T + t0 + s) * D + jl] = Hx[(s + 1) * D + jl] + v;
+            if (s < Lv) {
+              Tt* o = Hnext + ((size_t)b * T + t0 + s) * D + jl;
+              if (s == L - 1) coherent_store(o, Hx[(s + 1) * LD + jl] + v);   // next tile's halo
+              else *o = Hx[(s + 1) * LD + jl] + v;
+            }
           }
           __syncthreads();
           Tt* tmp = cb; cb = nb; nb = tmp;
@@ -546,28 +708,25 @@ int dense_supported(int D, int full, int is_f64) {
   return is_f64 ? D <= 32 : D <= 64;
 }
 
-int dense_tile_len(int D, int full, int) {
-  if (full) {
-    const int parts = (64 / (D + 1)) * PNR_WAVES;
-    const int lp = D <= 4 ? 2 : (D <= 8 ? 4 : 8);
-    return parts * lp;
-  }
-  return 64;
-}
+int dense_tile_len(int D, int full, int) { return full ? dense_full_parts(D) * 8 : 64; }
 
-static int dense_parts(int D, int full) { return full ? (64 / (D + 1)) * PNR_WAVES : PNR_BLOCK / D; }
+static int dense_parts(int D, int full) { return full ? dense_full_parts(D) : PNR_BLOCK / D; }
 
 int dense_slot_words(int D, int full, int is_f64) { return dense_slot_values(D, full) * (is_f64 ? 2 : 1); }
 
+static bool dense_use_mfma(int D, int is_f64) { return !is_f64 && (D == 16 || D == 32 || D == 64); }
+
 size_t dense_lds_bytes(int D, int full, int is_f64, int reuse) {
   const int es = is_f64 ? 8 : 4;
-  DenseLds l{D, dense_tile_len(D, full, is_f64), full, reuse, dense_parts(D, full), dense_window(D, full != 0, es)};
+  const bool mf = dense_use_mfma(D, is_f64);
+  DenseLds l{D, dense_tile_len(D, full, is_f64), full, reuse, dense_parts(D, full),
+             dense_window(D, full != 0, es), mf ? D + 4 : D, (!mf || full) ? 1 : 0};
   return l.count() * es;
 }
 
-template <typename Tt, int DM, bool FULL>
+template <typename Tt, int DM, bool FULL, bool MF>
 static int dense_capacity_t(int num_cu, size_t lds) {
-  auto fn = dense_newton_kernel<Tt, DM, FULL>;
+  auto fn = dense_newton_kernel<Tt, DM, FULL, MF>;
   if (lds > 65536) {
     if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return 0;
@@ -578,28 +737,37 @@ static int dense_capacity_t(int num_cu, size_t lds) {
   return (int)(g > kMaxGrid ? kMaxGrid : g);
 }
 
-template <typename Tt, int DM, bool FULL>
+template <typename Tt, int DM, bool FULL, bool MF>
 static hipError_t launch_t(const DenseLoopArgs<Tt>& a, int num_cu, hipStream_t st) {
   const size_t lds = dense_lds_bytes(a.D, FULL, sizeof(Tt) == 8, a.nbuf > 2);
-  const int cap = dense_capacity_t<Tt, DM, FULL>(num_cu, lds);
+  const int cap = dense_capacity_t<Tt, DM, FULL, MF>(num_cu, lds);
   if (cap < 1) return hipErrorInvalidConfiguration;
   int grid = a.n_tiles < cap ? a.n_tiles : cap;
   if (grid < 1) grid = 1;
   void* args[] = {const_cast<DenseLoopArgs<Tt>*>(&a)};
-  return hipLaunchCooperativeKernel((const void*)dense_newton_kernel<Tt, DM, FULL>, dim3(grid), dim3(PNR_BLOCK),
-                                    args, (unsigned)lds, st);
+  return hipLaunchCooperativeKernel((const void*)dense_newton_kernel<Tt, DM, FULL, MF>, dim3(grid),
+                                    dim3(PNR_BLOCK), args, (unsigned)lds, st);
 }
 
 template <typename Tt>
 static hipError_t launch_dense_t(const DenseLoopArgs<Tt>& a, int full, int num_cu, hipStream_t st) {
-  if (!full) return launch_t<Tt, 1, false>(a, num_cu, st);
-  if (a.D <= 4) return launch_t<Tt, 4, true>(a, num_cu, st);
-  if (a.D <= 8) return launch_t<Tt, 8, true>(a, num_cu, st);
-  if (a.D <= 16) return launch_t<Tt, 16, true>(a, num_cu, st);
-  return launch_t<Tt, 32, true>(a, num_cu, st);
+  if (!full) return launch_t<Tt, 1, false, false>(a, num_cu, st);
+  if (a.D <= 4) return launch_t<Tt, 4, true, false>(a, num_cu, st);
+  if (a.D <= 8) return launch_t<Tt, 8, true, false>(a, num_cu, st);
+  if (a.D <= 16) return launch_t<Tt, 16, true, false>(a, num_cu, st);
+  return launch_t<Tt, 32, true, false>(a, num_cu, st);
 }
 
 hipError_t launch_dense_newton_f32(const DenseLoopArgs<float>& a, int full, int num_cu, hipStream_t st) {
+  if (dense_use_mfma(a.D, 0)) {
+    if (!full) {
+      if (a.D == 16) return launch_t<float, 16, false, true>(a, num_cu, st);
+      if (a.D == 32) return launch_t<float, 32, false, true>(a, num_cu, st);
+      return launch_t<float, 64, false, true>(a, num_cu, st);
+    }
+    if (a.D == 16) return launch_t<float, 16, true, true>(a, num_cu, st);
+    if (a.D == 32) return launch_t<float, 32, true, true>(a, num_cu, st);
+  }
   return launch_dense_t<float>(a, full, num_cu, st);
 }
 hipError_t launch_dense_newton_f64(const DenseLoopArgs<double>& a, int full, int num_cu, hipStream_t st) {

@@ -231,9 +231,11 @@ __device__ typename DeltaOf<typename CellT::E>::T lookback_window(uint64_t* slot
     E e = idn;
     Dl pre = DeltaOf<E>::zero();
     if (valid) {
+      // both reads are issued before either is tested
       const uint64_t* s = slots + (size_t)(tile - 1 - lane) * SW;
-      if (get_pre(s + AW, ep, pre)) st = 2;
-      else if (get_agg(s, ep, e)) st = 1;
+      const bool has_pre = get_pre(s + AW, ep, pre);
+      const bool has_agg = get_agg(s, ep, e);
+      st = has_pre ? 2 : (has_agg ? 1 : 0);
     }
     const uint64_t pm = __ballot(st == 2);
     const uint64_t bad = __ballot(valid && st == 0);
@@ -311,13 +313,18 @@ __device__ __forceinline__ typename DeltaOf<typename DiagCell<CELL>::E>::T diag_
     float h[N], pj[N];
     if (v.cur_zero) { for (int i = 0; i < N; ++i) h[i] = 0.f; }
     else load_n(v.Hcur + roff, tb, T, vec, N, h);
+    // the state before a tile's first step was written by the block owning the
+    // previous tile: read it coherently (everything else here is this block's own)
+    const bool halo_other = tid == 0 && !walk;
     float p0;
     if (tb == 0) p0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
-    else p0 = (v.cur_zero || tb > T) ? 0.f : v.Hcur[roff + tb - 1];
+    else if (v.cur_zero || tb > T) p0 = 0.f;
+    else p0 = halo_other ? coherent_load(v.Hcur + roff + tb - 1) : v.Hcur[roff + tb - 1];
     if (stale) {
       float pj0;
       if (tb == 0) pj0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
-      else pj0 = (v.jac_zero || tb > T) ? 0.f : v.Hjac[roff + tb - 1];
+      else if (v.jac_zero || tb > T) pj0 = 0.f;
+      else pj0 = halo_other ? coherent_load(v.Hjac + roff + tb - 1) : v.Hjac[roff + tb - 1];
       float hj[N];
       if (v.jac_zero) { for (int i = 0; i < N; ++i) hj[i] = 0.f; }
       else load_n(v.Hjac + roff, tb, T, vec, N, hj);
@@ -341,12 +348,15 @@ __device__ __forceinline__ typename DeltaOf<typename DiagCell<CELL>::E>::T diag_
     float c[N], h[N];
     if (v.cur_zero) { for (int i = 0; i < N; ++i) { c[i] = 0.f; h[i] = 0.f; } }
     else { load_n(v.Hcur + coff, tb, T, vec, N, c); load_n(v.Hcur + hoff, tb, T, vec, N, h); }
+    const bool halo_other = tid == 0 && !walk;   // see the GRU branch
     float cp0, hp0;
     if (tb == 0) {
       cp0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
       hp0 = a.h0 ? a.h0[(size_t)b * S + D + d] : 0.f;
     } else if (v.cur_zero || tb > T) {
       cp0 = 0.f; hp0 = 0.f;
+    } else if (halo_other) {
+      cp0 = coherent_load(v.Hcur + coff + tb - 1); hp0 = coherent_load(v.Hcur + hoff + tb - 1);
     } else {
       cp0 = v.Hcur[coff + tb - 1]; hp0 = v.Hcur[hoff + tb - 1];
     }
@@ -356,7 +366,11 @@ __device__ __forceinline__ typename DeltaOf<typename DiagCell<CELL>::E>::T diag_
         cpj0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
         hpj0 = a.h0 ? a.h0[(size_t)b * S + D + d] : 0.f;
       } else if (!(v.jac_zero || tb > T)) {
-        cpj0 = v.Hjac[coff + tb - 1]; hpj0 = v.Hjac[hoff + tb - 1];
+        if (halo_other) {
+          cpj0 = coherent_load(v.Hjac + coff + tb - 1); hpj0 = coherent_load(v.Hjac + hoff + tb - 1);
+        } else {
+          cpj0 = v.Hjac[coff + tb - 1]; hpj0 = v.Hjac[hoff + tb - 1];
+        }
       }
       if (v.jac_zero) { for (int i = 0; i < N; ++i) { cj[i] = 0.f; hj[i] = 0.f; } }
       else { load_n(v.Hjac + coff, tb, T, vec, N, cj); load_n(v.Hjac + hoff, tb, T, vec, N, hj); }
@@ -418,7 +432,10 @@ __device__ __forceinline__ typename DeltaOf<typename DiagCell<CELL>::E>::T diag_
         dl = apply(e[i], dl);
         out[i] = hc[0][i] + dl;
       }
-      store_n(v.Hnext + ((size_t)b * S + d) * T, tb, T, vec, N, out);
+      float* orow = v.Hnext + ((size_t)b * S + d) * T;
+      store_n(orow, tb, T, vec, N, out);
+      // the tile's last state is the next tile's halo, read by another block next pass
+      if (!walk && tid == PNR_BLOCK - 1 && tb + N <= T) coherent_store(orow + tb + N - 1, out[N - 1]);
     } else {
       float oc[N], oh[N];
 #pragma unroll
@@ -427,8 +444,15 @@ __device__ __forceinline__ typename DeltaOf<typename DiagCell<CELL>::E>::T diag_
         oc[i] = hc[0][i] + dl.x;
         oh[i] = hc[1][i] + dl.y;
       }
-      store_n(v.Hnext + ((size_t)b * S + d) * T, tb, T, vec, N, oc);
-      store_n(v.Hnext + ((size_t)b * S + D + d) * T, tb, T, vec, N, oh);
+      float* crow = v.Hnext + ((size_t)b * S + d) * T;
+      float* hrow = v.Hnext + ((size_t)b * S + D + d) * T;
+      store_n(crow, tb, T, vec, N, oc);
+      store_n(hrow, tb, T, vec, N, oh);
+      // the tile's last state is the next tile's halo, read by another block next pass
+      if (!walk && tid == PNR_BLOCK - 1 && tb + N <= T) {
+        coherent_store(crow + tb + N - 1, oc[N - 1]);
+        coherent_store(hrow + tb + N - 1, oh[N - 1]);
+      }
     }
     const Dl tile_out = apply(tot, din);
     __syncthreads();   // sh is reused by the next tile
@@ -449,8 +473,9 @@ __device__ __forceinline__ int pick_next(int cur, int jac, int nbuf) {
 // barrier every block reads the decision and either stops or starts iteration k+1.
 // The state buffers rotate exactly as the host would rotate them: the next iterate goes
 // to a buffer holding neither the current iterate nor the state the Jacobian is taken at.
+// Registers capped at 128 VGPRs (four waves per SIMD) to keep enough loads in flight.
 template <int CELL, int N>
-__global__ void __launch_bounds__(PNR_BLOCK) diag_newton_kernel(DiagLoopArgs a) {
+__global__ void __launch_bounds__(PNR_BLOCK, 4) diag_newton_kernel(DiagLoopArgs a) {
   using C = DiagCell<CELL>;
   using E = typename C::E;
   using Dl = typename DeltaOf<E>::T;

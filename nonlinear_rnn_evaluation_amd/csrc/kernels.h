@@ -28,9 +28,9 @@ __device__ inline void finish_iteration(Ctrl* c, double* hist, double rho, int k
     c->status = status;
     c->iters = k;
     c->result_buf = cur_buf;
-    c->done = 1;
+    // every block reads `done` right after the barrier: publish it coherently
+    __hip_atomic_store(&c->done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  c->ticket = 0;
 }
 
 // ---------------------------------------------------------------------------------

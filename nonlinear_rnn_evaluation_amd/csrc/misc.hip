@@ -15,9 +15,10 @@ __global__ void init_kernel(Ctrl* ctrl, uint64_t* slots, size_t n) {
     ctrl->result_buf = -1;
     ctrl->rho = 0.0;
     ctrl->ticket = 0;
-    ctrl->bar_count = 0;
+    ctrl->bar_top = 0;
     ctrl->bar_gen = 0;
     ctrl->fault = 0;
+    for (int g = 0; g < kBarGroups; ++g) ctrl->bar_group[g].count = 0;
   }
   // epoch 0 is never a live epoch, so zeroed words read as "not yet written"
   for (size_t i = i0; i < n; i += (size_t)gridDim.x * blockDim.x) slots[i] = 0;
