@@ -708,19 +708,22 @@ int dense_supported(int D, int full, int is_f64) {
   return is_f64 ? D <= 32 : D <= 64;
 }
 
-int dense_tile_len(int D, int full, int) { return full ? dense_full_parts(D) * 8 : 64; }
+int dense_tile_len(int D, int full, int is_f64) {
+  if (dense_mfma_supported(D, full, is_f64)) return dense_mfma_tile_len();
+  return full ? dense_full_parts(D) * 8 : 64;
+}
 
 static int dense_parts(int D, int full) { return full ? dense_full_parts(D) : PNR_BLOCK / D; }
 
-int dense_slot_words(int D, int full, int is_f64) { return dense_slot_values(D, full) * (is_f64 ? 2 : 1); }
-
-static bool dense_use_mfma(int D, int is_f64) { return !is_f64 && (D == 16 || D == 32 || D == 64); }
+int dense_slot_words(int D, int full, int is_f64) {
+  if (dense_mfma_supported(D, full, is_f64)) return dense_mfma_slot_words(D, full);
+  return dense_slot_values(D, full) * (is_f64 ? 2 : 1);
+}
 
 size_t dense_lds_bytes(int D, int full, int is_f64, int reuse) {
   const int es = is_f64 ? 8 : 4;
-  const bool mf = dense_use_mfma(D, is_f64);
-  DenseLds l{D, dense_tile_len(D, full, is_f64), full, reuse, dense_parts(D, full),
-             dense_window(D, full != 0, es), mf ? D + 4 : D, (!mf || full) ? 1 : 0};
+  DenseLds l{D, full ? dense_full_parts(D) * 8 : 64, full, reuse, dense_parts(D, full),
+             dense_window(D, full != 0, es), D, 1};
   return l.count() * es;
 }
 
@@ -759,15 +762,7 @@ static hipError_t launch_dense_t(const DenseLoopArgs<Tt>& a, int full, int num_c
 }
 
 hipError_t launch_dense_newton_f32(const DenseLoopArgs<float>& a, int full, int num_cu, hipStream_t st) {
-  if (dense_use_mfma(a.D, 0)) {
-    if (!full) {
-      if (a.D == 16) return launch_t<float, 16, false, true>(a, num_cu, st);
-      if (a.D == 32) return launch_t<float, 32, false, true>(a, num_cu, st);
-      return launch_t<float, 64, false, true>(a, num_cu, st);
-    }
-    if (a.D == 16) return launch_t<float, 16, true, true>(a, num_cu, st);
-    if (a.D == 32) return launch_t<float, 32, true, true>(a, num_cu, st);
-  }
+  if (dense_mfma_supported(a.D, full, 0)) return launch_dense_mfma(a, full, num_cu, st);
   return launch_dense_t<float>(a, full, num_cu, st);
 }
 hipError_t launch_dense_newton_f64(const DenseLoopArgs<double>& a, int full, int num_cu, hipStream_t st) {

@@ -86,6 +86,11 @@ int dense_slot_words(int D, int full, int is_f64);
 size_t dense_lds_bytes(int D, int full, int is_f64, int reuse);
 int dense_supported(int D, int full, int is_f64);
 hipError_t launch_dense_newton_f32(const DenseLoopArgs<float>& a, int full, int num_cu, hipStream_t st);
+// MFMA kernels (fp32; diagonal Jacobian with D in {16, 32, 64}, dense Jacobian with D = 16)
+int dense_mfma_supported(int D, int full, int is_f64);
+int dense_mfma_tile_len();
+int dense_mfma_slot_words(int D, int full);
+hipError_t launch_dense_mfma(const DenseLoopArgs<float>& a, int full, int num_cu, hipStream_t st);
 hipError_t launch_dense_newton_f64(const DenseLoopArgs<double>& a, int full, int num_cu, hipStream_t st);
 
 // ---------------------------------------------------------------------------------

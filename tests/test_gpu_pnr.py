@@ -239,3 +239,27 @@ def test_repeated_calls_reuse_workspace():
         again = pnr.evaluate(WL.CELL_LSTM_DIAG, d["W"], d["U"], d["x"], max_iters=50, tol=1e-6, workspace=ws)
         assert again["iters"] == first["iters"]
         assert torch.allclose(again["h"], first["h"], atol=1e-6, rtol=0)
+
+
+@pytest.mark.parametrize("D,mode,every", [(16, WL.JAC_FULL, 1), (16, WL.JAC_FULL, 2), (16, WL.JAC_DIAG, 1),
+                                          (32, WL.JAC_DIAG, 2), (64, WL.JAC_DIAG, 1), (64, WL.JAC_ZERO, 1)])
+def test_mfma_dense_paths_match_newton_oracle(D, mode, every):
+    """fp32 dense-U GRU with D in {16, 32, 64}: the recurrent product (and, for the dense
+    Jacobian, the scan) run on MFMA; iterates must match the oracle's, over several
+    64-step tiles and a ragged tail."""
+    T = 3 * 64 + 17
+    p = WL.random_problem(WL.CELL_GRU, 2, T, D, 7, seed=D + every, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32,
+                          bias_std=0.2, h0_std=0.3, w_std=0.5 / math.sqrt(D))
+    q = _f64(p)
+    for k in (1, 2, 4):
+        got = _run(WL.CELL_GRU, p, k, -1.0, mode, every)
+        ref = O.newton_dense(WL.CELL_GRU, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], k, -1.0, mode,
+                             every, solver="loop")
+        np.testing.assert_allclose(_np(got["h"]), ref["states"], rtol=0, atol=1e-4)
+        np.testing.assert_allclose(got["history"], ref["rhos"], rtol=1e-3, atol=1e-5)
+    got = _run(WL.CELL_GRU, p, 100, 1e-6, mode, every)
+    if mode != WL.JAC_ZERO:
+        assert got["status"] == pnr.OK
+    ref = O.sequential(WL.CELL_GRU, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"])
+    if got["status"] == pnr.OK:
+        assert np.abs(_np(got["h"]) - ref).max() < 1e-4
