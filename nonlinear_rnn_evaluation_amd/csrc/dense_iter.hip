@@ -247,12 +247,15 @@ __global__ void __launch_bounds__(PNR_BLOCK) dense_newton_kernel(DenseLoopArgs<T
     const uint32_t ep = (uint32_t)k + 1u;
     uint64_t blk_max = 0;
 
-    // Static assignment, tiles in increasing order per block (co-resident grid): the
-    // lowest unfinished tile never waits, so every look-back ends.
-    for (int tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+    // Static assignment in increasing item order per block (co-resident grid): the
+    // lowest unfinished tile never waits, so every look-back ends.  Items go out
+    // time-segment-major (segment s of every batch row before segment
+    // s+1), so a tile's predecessor always has a smaller item index: it was handed out
+    // earlier, and prefixes are usually published before a successor looks back.
+    for (int item = blockIdx.x; item < a.n_tiles; item += gridDim.x) {
       if (has_fault(ctrl)) break;
-      const int b = tile / a.tiles_per_row;
-      const int seg = tile - b * a.tiles_per_row;
+      const int seg = item / a.B, b = item - seg * a.B;
+      const int tile = b * a.tiles_per_row + seg;   // slot index: row-major
       const int t0 = seg * L;
       const int Lv = min(L, T - t0);
       const Tt* gxb = a.gx + (size_t)b * T * 3 * D;

@@ -231,9 +231,13 @@ __global__ void __launch_bounds__(PNR_BLOCK) dense_diag_mfma_kernel(DenseLoopArg
     const bool stale = !resid_only && jac != cur;
     const uint32_t ep = (uint32_t)k + 1u;
     uint32_t blk_max = 0;
-    for (int tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+    // Items go out time-segment-major (segment s of every batch row before segment
+    // s+1), so a tile's predecessor always has a smaller item index: it was handed out
+    // earlier, and prefixes are usually published before a successor looks back.
+    for (int item = blockIdx.x; item < a.n_tiles; item += gridDim.x) {
       if (has_fault(ctrl)) break;
-      const int b = tile / a.tiles_per_row, seg = tile - b * a.tiles_per_row;
+      const int seg = item / a.B, b = item - seg * a.B;
+      const int tile = b * a.tiles_per_row + seg;   // slot index: row-major
       const int t0 = seg * kTL, Lv = min(kTL, T - t0);
       const float* gxb = a.gx + (size_t)b * T * 3 * D;
       stage_rows(X, Hcur, a.h0, b, t0, T, D, LD);
@@ -364,7 +368,7 @@ __global__ void __launch_bounds__(PNR_BLOCK) dense_diag_mfma_kernel(DenseLoopArg
 constexpr int kF = 16;
 constexpr int kFAgg = kF * kF + kF;      // aggregate values: M (row-major) then v
 constexpr int kFSlot = kFAgg + kF;       // slot values: aggregate, then prefix
-constexpr int kFWin = 8;
+constexpr int kFWin = 16;
 __host__ __device__ inline size_t mff_lds_floats(int reuse) {
   const int LD = kF + 4;
   return (size_t)3 * kF + (size_t)(kTL + 1) * LD * (reuse ? 2 : 1) + (size_t)5 * kTL * kF +
@@ -429,9 +433,13 @@ __global__ void __launch_bounds__(PNR_BLOCK) dense_full_mfma_kernel(DenseLoopArg
     const bool stale = !resid_only && jac != cur;
     const uint32_t ep = (uint32_t)k + 1u;
     uint32_t blk_max = 0;
-    for (int tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+    // Items go out time-segment-major (segment s of every batch row before segment
+    // s+1), so a tile's predecessor always has a smaller item index: it was handed out
+    // earlier, and prefixes are usually published before a successor looks back.
+    for (int item = blockIdx.x; item < a.n_tiles; item += gridDim.x) {
       if (has_fault(ctrl)) break;
-      const int b = tile / a.tiles_per_row, seg = tile - b * a.tiles_per_row;
+      const int seg = item / a.B, b = item - seg * a.B;
+      const int tile = b * a.tiles_per_row + seg;   // slot index: row-major
       const int t0 = seg * kTL, Lv = min(kTL, T - t0);
       const float* gxb = a.gx + (size_t)b * T * 3 * D;
       stage_rows(X, Hcur, a.h0, b, t0, T, D, LD);
