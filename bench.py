@@ -27,13 +27,29 @@ UNIT = "timesteps*batch/s"
 HBM_PEAK_GBS = 8000.0
 PRIMARY = "gru_quasi"
 DEFAULT_OTHERS = "tiny_gru,gru_full,gru_diag_long,lstm_diag_long,lstm_diag_long_stiff"
-KERNEL_SRC = {"diag": "nonlinear_rnn_evaluation_amd/csrc/diag_iter.hip",
-              "dense": "nonlinear_rnn_evaluation_amd/csrc/dense_iter.hip"}
+CSRC = "nonlinear_rnn_evaluation_amd/csrc/"
+
+
+def newton_kernel(w, mode):
+    """(kernel name as the profiler lists it, source file) of the Newton loop kernel."""
+    from nonlinear_rnn_evaluation_amd import workloads as WL
+    if w.cell in (WL.CELL_GRU_DIAG, WL.CELL_LSTM_DIAG):
+        return "pnr::diag_newton_kernel", CSRC + "diag_iter.hip"
+    full = mode == WL.JAC_FULL
+    if w.state_dtype == WL.DT_F32 and ((full and w.D == 16) or (not full and w.D in (16, 32, 64))):
+        if full:
+            return "pnr::dense_full_mfma_kernel", CSRC + "dense_mfma.hip"
+        return f"pnr::dense_diag_mfma_kernel<{w.D}>", CSRC + "dense_mfma.hip"
+    return "pnr::dense_newton_kernel", CSRC + "dense_iter.hip"
 
 
 def src_hash(path):
-    with open(os.path.join(ROOT, path), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel's source file and the two headers every kernel includes."""
+    h = hashlib.sha256()
+    for p in (path, CSRC + "common.h", CSRC + "kernels.h"):
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def iteration_bytes(w, k, iters_total, resid=False):
@@ -111,14 +127,13 @@ def run_workload(name, steps, warmup, mode=None, with_cpu=True, cpu_budget=12.0,
     resid_last = profs[-1]["resid_only"]
     bytes_call = sum(iteration_bytes(w, k, iters, resid=(resid_last and k == passes - 1)) for k in range(passes))
     achieved = bytes_call / (newton_ms * 1e-3) / 1e9 if newton_ms > 0 else 0.0
-    family = "diag" if w.cell in (WL.CELL_GRU_DIAG, WL.CELL_LSTM_DIAG) else "dense"
-    kname = "pnr::diag_newton_kernel" if family == "diag" else "pnr::dense_newton_kernel"
+    kname, ksrc = newton_kernel(w, mode)
     traffic = None
     pmc_path = os.path.join(ROOT, "profiles", f"newton_kernel_{name}_pmc.json")
     if os.path.exists(pmc_path):
         with open(pmc_path) as f:
             pmc = json.load(f)
-        if pmc.get("kernel_src_sha") == src_hash(KERNEL_SRC[family]):
+        if pmc.get("kernel_src_sha") == src_hash(ksrc) and pmc.get("jac_mode") == mode:
             traffic = pmc.get("bytes_per_launch")
     roof = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
