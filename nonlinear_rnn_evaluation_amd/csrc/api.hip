@@ -51,7 +51,7 @@ int gates(int kind) { return kind == PNR_CELL_LSTM_DIAG ? 4 : 3; }
 int states(int kind, int D) { return kind == PNR_CELL_LSTM_DIAG ? 2 * D : D; }
 
 struct Layout {
-  size_t ctrl = 0, hist = 0, partials = 0, slots = 0, gx = 0, h[3] = {0, 0, 0}, total = 0;
+  size_t ctrl = 0, hist = 0, partials = 0, slots = 0, gx = 0, h[4] = {0, 0, 0, 0}, total = 0;
   size_t slot_words = 0;
   int nbuf = 2, tiles_per_row = 0, n_tiles = 0, L = 0;
   bool dense_full = false;
@@ -94,10 +94,12 @@ Layout make_layout(const pnr_cell* c, int jac_mode) {
   const size_t B = c->B, T = c->T, D = c->D;
   const size_t es = dsize(c->state_dtype);
   l.nbuf = c->jac_every > 1 ? 3 : 2;
+  if (c->kind == PNR_CELL_GRU)
+    l.nbuf = dense_state_buffers(c->D, jac_mode == PNR_JAC_FULL, c->state_dtype == PNR_F64, c->jac_every > 1);
   size_t off = 0;
   l.ctrl = off; off = align_up(off + sizeof(Ctrl));
   l.hist = off; off = align_up(off + sizeof(double) * (PNR_MAX_ITERS + 1));
-  l.partials = off; off = align_up(off + sizeof(uint64_t) * kMaxGrid);
+  l.partials = off; off = align_up(off + sizeof(uint64_t) * kPartialWords);
   if (is_diag_cell(c->kind)) {
     const int tile = PNR_BLOCK * diag_items_per_thread(c->kind);
     l.tiles_per_row = (int)((T + tile - 1) / tile);
@@ -249,13 +251,13 @@ int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, cons
   double* hist = reinterpret_cast<double*>(ws + l.hist);
   uint64_t* slots = reinterpret_cast<uint64_t*>(ws + l.slots);
   void* gx = ws + l.gx;
-  void* H[3] = {ws + l.h[0], ws + l.h[1], l.nbuf > 2 ? ws + l.h[2] : nullptr};
+  void* H[4] = {ws + l.h[0], ws + l.h[1], l.nbuf > 2 ? ws + l.h[2] : nullptr, l.nbuf > 3 ? ws + l.h[3] : nullptr};
 
   const int kind = cell->kind, D = cell->D, T = cell->T, B = cell->B, Din = cell->D_in;
   const int G = gates(kind), S = states(kind, D);
 
   Mark m_first = mark_begin(st);
-  PNR_HIP(launch_init(ctrl, slots, l.slot_words, st));
+  PNR_HIP(launch_init(ctrl, slots, l.slot_words, reinterpret_cast<uint64_t*>(ws + l.partials), kPartialWords, st));
 
   // ---- input projection ----
   GemmArgs g{};
@@ -272,6 +274,7 @@ int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, cons
   mark_end(m_proj, st);
 
   // ---- the Newton loop: one persistent launch; the device decides when to stop ----
+  bool out_written = false;
   Mark m_newton = mark_begin(st);
   if (is_diag_cell(kind)) {
     DiagLoopArgs a{};
@@ -304,13 +307,23 @@ int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, cons
     a.U = static_cast<const float*>(params->U);
     a.bh = static_cast<const float*>(params->b_h);
     a.h0 = static_cast<const float*>(h0);
-    for (int i = 0; i < 3; ++i) a.H[i] = static_cast<float*>(H[i]);
+    for (int i = 0; i < 4; ++i) a.H[i] = static_cast<float*>(H[i]);
     a.nbuf = l.nbuf;
     a.slots = slots; a.partials = reinterpret_cast<uint64_t*>(ws + l.partials);
     a.ctrl = ctrl; a.rho_hist = hist;
     a.B = B; a.D = D; a.T = T; a.L = l.L;
     a.tiles_per_row = l.tiles_per_row; a.n_tiles = l.n_tiles;
     a.max_iters = max_iters; a.jac_every = cell->jac_every; a.jac_mode = jac_mode; a.tol = tol;
+    // resident variant: the loop kernel writes the returned iterate to h_out itself.  Its
+    // tiles are at least as long as the layout's, so the slot region suffices.
+    const int rtl = dense_mfma_resident_tile(D, l.dense_full, B, T, cell->jac_every > 1, num_cu);
+    if (rtl > 0) {
+      a.L = rtl;
+      a.tiles_per_row = (T + rtl - 1) / rtl;
+      a.n_tiles = B * a.tiles_per_row;
+      a.out = static_cast<float*>(h_out);
+      out_written = true;
+    }
     PNR_HIP(launch_dense_newton_f32(a, l.dense_full, num_cu, st));
   } else {
     DenseLoopArgs<double> a{};
@@ -318,7 +331,7 @@ int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, cons
     a.U = static_cast<const double*>(params->U);
     a.bh = static_cast<const double*>(params->b_h);
     a.h0 = static_cast<const double*>(h0);
-    for (int i = 0; i < 3; ++i) a.H[i] = static_cast<double*>(H[i]);
+    for (int i = 0; i < 4; ++i) a.H[i] = static_cast<double*>(H[i]);
     a.nbuf = l.nbuf;
     a.slots = slots; a.partials = reinterpret_cast<uint64_t*>(ws + l.partials);
     a.ctrl = ctrl; a.rho_hist = hist;
@@ -335,13 +348,15 @@ int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, cons
     const float* bufs[3] = {static_cast<const float*>(H[0]), static_cast<const float*>(H[1]),
                             static_cast<const float*>(H[2])};
     PNR_HIP(launch_diag_output(bufs, ctrl, static_cast<float*>(h_out), B, S, T, st));
+  } else if (out_written) {
+    // nothing to do
   } else if (cell->state_dtype == PNR_F32) {
-    const float* bufs[3] = {static_cast<const float*>(H[0]), static_cast<const float*>(H[1]),
-                            static_cast<const float*>(H[2])};
+    const float* bufs[4] = {static_cast<const float*>(H[0]), static_cast<const float*>(H[1]),
+                            static_cast<const float*>(H[2]), static_cast<const float*>(H[3])};
     PNR_HIP(launch_dense_output<float>(bufs, ctrl, static_cast<float*>(h_out), (size_t)B * T * S, st));
   } else {
-    const double* bufs[3] = {static_cast<const double*>(H[0]), static_cast<const double*>(H[1]),
-                             static_cast<const double*>(H[2])};
+    const double* bufs[4] = {static_cast<const double*>(H[0]), static_cast<const double*>(H[1]),
+                             static_cast<const double*>(H[2]), static_cast<const double*>(H[3])};
     PNR_HIP(launch_dense_output<double>(bufs, ctrl, static_cast<double*>(h_out), (size_t)B * T * S, st));
   }
 
@@ -349,18 +364,22 @@ int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, cons
   mark_end(m_first, st);
 
   // ---- the one device -> host crossing of the call ----
-  Ctrl hc;
-  std::vector<double> hh(max_iters + 1);
-  PNR_HIP(hipMemcpyAsync(&hc, ctrl, sizeof(Ctrl), hipMemcpyDeviceToHost, st));
-  PNR_HIP(hipMemcpyAsync(hh.data(), hist, sizeof(double) * (max_iters + 1), hipMemcpyDeviceToHost, st));
+  // control block and residual history are adjacent in the workspace: one copy
+  static thread_local std::vector<char> rb;
+  const size_t rb_bytes = (l.hist - l.ctrl) + sizeof(double) * (max_iters + 1);
+  if (rb.size() < rb_bytes) rb.resize(rb_bytes);
+  PNR_HIP(hipMemcpyAsync(rb.data(), ws + l.ctrl, rb_bytes, hipMemcpyDeviceToHost, st));
   PNR_HIP(hipStreamSynchronize(st));
+  Ctrl hc;
+  memcpy(&hc, rb.data(), sizeof(Ctrl));
+  const double* hh = reinterpret_cast<const double*>(rb.data() + (l.hist - l.ctrl));
   if (hc.fault)
     return fail(PNR_E_HIP, "device loop gave up waiting (%s); results are not valid",
                 hc.fault == 1 ? "look-back" : "grid barrier");
   if (!hc.done || hc.iters < 0) return fail(PNR_E_HIP, "device loop did not record a decision");
   g_last.iters = hc.iters;
   g_last.residual = hc.rho;
-  g_last.hist.assign(hh.begin(), hh.begin() + hc.iters + 1);
+  g_last.hist.assign(hh, hh + hc.iters + 1);
   if (g_prof.on) {
     pnr_profile p{};
     p.total_ms = mark_ms(m_first);
@@ -404,7 +423,7 @@ int pnr_scan(int kind, int R, int T, const float* A, const float* b, float* d, i
   Ctrl* ctrl = reinterpret_cast<Ctrl*>(workspace);
   uint64_t* slots = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + align_up(sizeof(Ctrl)));
   const size_t tiles = (size_t)R * ((T + tile_len - 1) / tile_len);
-  PNR_HIP(launch_init(ctrl, slots, tiles * scan_slot_words(kind), st));
+  PNR_HIP(launch_init(ctrl, slots, tiles * scan_slot_words(kind), nullptr, 0, st));
   PNR_HIP(launch_scan(kind, R, T, A, b, d, tile_len, slots, ctrl, num_cu, st));
   PNR_HIP(hipStreamSynchronize(st));
   return PNR_OK;

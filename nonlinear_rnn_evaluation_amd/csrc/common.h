@@ -33,6 +33,10 @@ struct Ctrl {
   uint32_t bar_gen;
   uint32_t pad2[63];
   struct { uint32_t count; uint32_t pad[63]; } bar_group[kBarGroups];
+  // Barrier-free loops: the decision on iteration k, tagged (k + 1) << 32 | flags
+  // (bit 0: stop).  Written by the merging block, polled by the others.
+  uint64_t dec;
+  uint32_t pad3[62];
 };
 
 // Bound on every device-side wait (polls of a look-back slot or of the grid barrier).
@@ -136,9 +140,11 @@ __device__ __forceinline__ void coherent_store(double* p, double v) {
 // uses the hardware exp2/rcp (a few ulp; far below the fp32 conditioning floor of the
 // recurrences), fp64 uses the device math library.
 __device__ __forceinline__ float fast_exp(float a) { return __expf(a); }
-__device__ __forceinline__ float sigm(float a) { return __frcp_rn(1.0f + fast_exp(-a)); }
+// v_rcp_f32 (1 ulp); rcp(+inf) = 0 gives the saturated ends of both functions
+__device__ __forceinline__ float fast_rcp(float a) { return __builtin_amdgcn_rcpf(a); }
+__device__ __forceinline__ float sigm(float a) { return fast_rcp(1.0f + fast_exp(-a)); }
 __device__ __forceinline__ float tanh_(float a) {
-  return 1.0f - 2.0f * __frcp_rn(1.0f + fast_exp(2.0f * a));
+  return 1.0f - 2.0f * fast_rcp(1.0f + fast_exp(2.0f * a));
 }
 __device__ __forceinline__ double sigm(double a) { return 1.0 / (1.0 + exp(-a)); }
 __device__ __forceinline__ double tanh_(double a) { return tanh(a); }

@@ -711,6 +711,11 @@ int dense_supported(int D, int full, int is_f64) {
   return is_f64 ? D <= 32 : D <= 64;
 }
 
+int dense_state_buffers(int D, int full, int is_f64, int reuse) {
+  (void)D; (void)full; (void)is_f64;
+  return reuse ? 3 : 2;   // the iterate being checked and the next (plus the reused one)
+}
+
 int dense_tile_len(int D, int full, int is_f64) {
   if (dense_mfma_supported(D, full, is_f64)) return dense_mfma_tile_len();
   return full ? dense_full_parts(D) * 8 : 64;

@@ -26,6 +26,8 @@
 // first column of a 16x16 operand, so it is the same MFMA chain.  J_t is never stored:
 // each lane forms the four entries it feeds to the MFMA from the factors and twelve
 // entries of U held in registers.
+#include <cstdlib>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -42,13 +44,14 @@ __device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Stage rows s = 0..kTL of the tile: row s holds the state before step t0+s.  Row 0 is
+// Stage rows s = 0..TL of the tile: row s holds the state before step t0+s.  Row 0 is
 // the previous tile's last step (another block's): read coherently.  Batched loads.
+template <int TL = kTL>
 __device__ __forceinline__ void stage_rows(float* __restrict__ X, const float* __restrict__ H,
                                            const float* __restrict__ h0, int b, int t0, int T, int D,
                                            int LD) {
   const int tid = threadIdx.x;
-  const int n = (kTL + 1) * D;
+  const int n = (TL + 1) * D;
   for (int j0 = 0; j0 < n; j0 += kLoadBatch * PNR_BLOCK) {
     float v[kLoadBatch];
 #pragma unroll
@@ -88,6 +91,29 @@ __device__ __forceinline__ void gates_block(const float* __restrict__ X, int LD,
     const float av = arow[4 * kk];
 #pragma unroll
     for (int g = 0; g < 3; ++g) acc[g] = mfma4(av, uf[g][kk], acc[g]);
+  }
+}
+
+// The same product with the K index split so that, in MFMA kk, lane group q = lane/16
+// contributes k = q*(D/4) + kk: a lane's A operands for one 16-step block are then D/4
+// consecutive floats of one LDS row, read as D/16 vectors before the MFMA chain starts.
+// The B fragments must follow the same split: ufp[g][kk] = U_g[c][q*(D/4) + kk].
+template <int DM>
+__device__ __forceinline__ void load_afrag(const float* __restrict__ X, int LD, int tb, v4f (&f)[DM / 16]) {
+  const int l = (int)lane_id();
+  const v4f* p = reinterpret_cast<const v4f*>(X + (size_t)(tb * 16 + (l & 15)) * LD + (l >> 4) * (DM / 4));
+#pragma unroll
+  for (int j = 0; j < DM / 16; ++j) f[j] = p[j];
+}
+template <int DM>
+__device__ __forceinline__ void gates_frag(const v4f (&f)[DM / 16], const float (&ufp)[3][DM / 4], v4f (&acc)[3]) {
+#pragma unroll
+  for (int g = 0; g < 3; ++g) acc[g] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < DM / 4; ++kk) {
+    const float av = f[kk >> 2][kk & 3];
+#pragma unroll
+    for (int g = 0; g < 3; ++g) acc[g] = mfma4(av, ufp[g][kk], acc[g]);
   }
 }
 
@@ -174,191 +200,507 @@ __device__ __forceinline__ int window_read(const uint64_t* __restrict__ slots, i
 }
 
 // =====================================================================================
-// Diagonal (quasi-Newton) Jacobian.  LDS: Bh[3D] | X[(kTL+1) LD] | Xj (reuse) | R[kTL D] |
-// Jd[kTL D] | Sa,Sb[parts D] | Win[W * 3D] | Din[D].
-__host__ __device__ inline int mfd_window(int D) {
-  const int w = (PNR_BLOCK * 16) / (3 * D);
-  return w > 16 ? 16 : w;
-}
-__host__ __device__ inline size_t mfd_lds_floats(int D, int reuse) {
-  const int LD = D + 4, parts = PNR_BLOCK / D;
-  return (size_t)3 * D + (size_t)(kTL + 1) * LD * (reuse ? 2 : 1) + (size_t)2 * kTL * D + (size_t)2 * parts * D +
-         (size_t)mfd_window(D) * 3 * D + D;
+// Diagonal (quasi-Newton) Jacobian, without a grid barrier.
+//
+// The only values that cross blocks are 64-bit words tagged with their pass (value |
+// epoch << 32), kept in three copies, one per pass modulo 3: the tile aggregates and
+// prefixes of the look-back, and each block's residual maximum.  A tile needs no state
+// of its predecessor: the state before its first step (the halo) starts at the initial
+// guess and every fix-up adds the increment entering the tile, which the look-back
+// delivers -- the same sum the predecessor forms for its last step, up to rounding.  A
+// tile starts pass k+1 right after its own fix-up of pass k.  The stopping test is off
+// the critical path: each block publishes its residual maximum of pass k right after
+// its cells; the block holding the last tile of the last row (no tile depends on it)
+// merges them, records rho_k and publishes the decision; every block reads the
+// decision on pass k-1 only before its fix-up of pass k, the first write over iterate
+// k-1.  If it says stop, the decided iterate (k-1 or k) is still held.
+//
+// Why three copies suffice: a word of pass k is rewritten in pass k+3, by a tile past
+// its fix-up of pass k+2, so after the decision on pass k+1, which was merged after every
+// block finished its cells of pass k+1 and hence its look-back of pass k (the last read
+// of the words of pass k).
+//
+// Two modes, chosen on the host:
+//  * streaming: a block may own several tiles of 64 steps; every pass stages the tile's
+//    states from HBM, streams its gate inputs, and writes the next iterate back;
+//  * resident (every tile owns a co-resident block): the tile's states stay in LDS for
+//    the whole launch, in two buffers (the iterate being checked, and the next one);
+//    the returned iterate is written to the caller's output once, at the end.  Tiles are
+//    64 steps, or 128 (D = 64 only) when there are more 64-step tiles than co-resident
+//    blocks.  The gate inputs are streamed a block of 16 steps ahead of their use; with
+//    every tile on the same CU in every pass they stay in that XCD's L2.
+//
+// LDS: Bh[3D] | X0[(TL+1) LD] | X1 (resident) | Xj (streaming with Jacobian reuse) |
+//      R[TL D] | Jd[TL D] | Sa, Sb[P D] | Agg[2 P D] | Din[D]          (P = 256 / D)
+// Slots per tile and pass modulo 3: A[D] | b[D] | prefix[D]; then per tile (streaming) the
+// halo and the refresh-point halo of a reused Jacobian (D floats each).
+
+// Predecessor tiles read per thread in the look-back (the window is 256 / D times this);
+// D >= 32 reads fewer to stay within two waves' registers.
+__host__ __device__ constexpr int mfd_lookback_per_thread(int D, bool resident) { return D >= 32 ? 8 : 16; }
+
+__host__ __device__ inline size_t mfd_lds_floats(int D, int TL, int reuse, int resident) {
+  const int LD = D + 4, P = PNR_BLOCK / D;
+  const size_t xs = (size_t)(TL + 1) * LD;
+  return (size_t)3 * D + xs * (1 + (resident ? 1 : 0) + (reuse ? 1 : 0)) + (size_t)2 * TL * D +
+         (size_t)4 * P * D + D;
 }
 
-template <int DM>
-__global__ void __launch_bounds__(PNR_BLOCK) dense_diag_mfma_kernel(DenseLoopArgs<float> a) {
+__device__ __forceinline__ uint64_t load_dec(Ctrl* c) {
+  return __hip_atomic_load(&c->dec, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void short_backoff(uint32_t spins) {
+  if (spins < 32) __builtin_amdgcn_s_sleep(1);
+  else __builtin_amdgcn_s_sleep(4);
+}
+
+// Bounded wait for ready(); every few polls it also looks for a published stop
+// decision (which makes the awaited value unnecessary) or a fault.  Returns 0 when
+// ready, 1 when stopped, 2 on a fault or when the spin budget ran out.
+template <class Ready>
+__device__ __forceinline__ int wait_for(Ready ready, Ctrl* c) {
+  uint32_t spins = 0;
+  while (!ready()) {
+    if ((++spins & 7) == 0) {
+      if (has_fault(c)) return 2;
+      if (load_dec(c) & 1ull) return 1;
+    }
+    if (spins > kSpinLimit) {
+      record_fault(c, 1);
+      return 2;
+    }
+    short_backoff(spins);
+  }
+  return 0;
+}
+
+// Increment entering tile `seg` of its row (valid in threads tid < DM).  Thread
+// (group g, channel c) covers the predecessors at distances g*kLBPer+1 .. g*kLBPer+kLBPer
+// of a window of min(seg, G*kLBPer) tiles: it reads their aggregates (A, b), except the
+// farthest tile of the window, whose inclusive prefix it reads instead, and composes
+// them far to near; the groups' maps are then composed in LDS.  Returns the wait
+// status (0 ok) through `st`, block-uniform.
+template <int DM, int kLBPer>
+__device__ __forceinline__ float lookback_regs(const uint64_t* __restrict__ slots, int tile, int seg, int km3,
+                                               uint32_t ep, float* __restrict__ Agg, Ctrl* ctrl, int& st) {
+  constexpr int G = PNR_BLOCK / DM, SVP = 3 * DM;
+  __shared__ int s_st;
+  const int tid = threadIdx.x, c = tid % DM, grp = tid / DM;
+  const int Wn = min(seg, G * kLBPer);
+  const int w_lo = grp * kLBPer + 1, w_hi = min(Wn, w_lo + kLBPer - 1);
+  if (tid == 0) s_st = 0;
+  float ga = 1.f, gb = 0.f;
+  __syncthreads();
+  if (w_lo <= w_hi) {
+    uint32_t spins = 0;
+    while (true) {
+      // All loads first (addresses clamped into the window, so every one is valid and
+      // none waits on another), then the tag checks: one memory round trip per poll.
+      uint64_t wa[kLBPer], wb[kLBPer];
+#pragma unroll
+      for (int j = 0; j < kLBPer; ++j) {
+        const int w = min(w_lo + j, Wn);
+        const uint64_t* sp = slots + ((size_t)(tile - w) * 3 + km3) * SVP;
+        wa[j] = __hip_atomic_load(sp + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        wb[j] = __hip_atomic_load(sp + (w == Wn ? 2 * DM : DM) + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      bool ok = true;
+#pragma unroll
+      for (int j = 0; j < kLBPer; ++j) {
+        const int w = w_lo + j;
+        const bool live = w <= w_hi, pre = w == Wn;
+        const bool tb_ok = (uint32_t)(wb[j] >> 32) == ep, ta_ok = pre || (uint32_t)(wa[j] >> 32) == ep;
+        ok = ok & (!live | (tb_ok & ta_ok));
+      }
+      if (ok) {
+#pragma unroll
+        for (int j = kLBPer - 1; j >= 0; --j) {
+          const int w = w_lo + j;
+          const bool live = w <= w_hi, pre = w == Wn;
+          const float va = live ? (pre ? 0.f : __uint_as_float((uint32_t)wa[j])) : 1.f;
+          const float vb = live ? __uint_as_float((uint32_t)wb[j]) : 0.f;
+          gb = fmaf(va, gb, vb);
+          ga *= va;
+        }
+        break;
+      }
+      // same policy as wait_for: give up on a published stop or a fault
+      if ((++spins & 7) == 0) {
+        const int w = has_fault(ctrl) ? 2 : ((load_dec(ctrl) & 1ull) ? 1 : 0);
+        if (w) {
+          atomicMax(&s_st, w);
+          break;
+        }
+      }
+      if (spins > kSpinLimit) {
+        record_fault(ctrl, 1);
+        atomicMax(&s_st, 2);
+        break;
+      }
+      short_backoff(spins);
+    }
+  }
+  Agg[grp * 2 * DM + c] = ga;
+  Agg[grp * 2 * DM + DM + c] = gb;
+  __syncthreads();
+  st = s_st;
+  float din = 0.f;
+  if (tid < DM)
+    for (int g2 = G - 1; g2 >= 0; --g2) din = fmaf(Agg[g2 * 2 * DM + tid], din, Agg[g2 * 2 * DM + DM + tid]);
+  return din;
+}
+
+template <int DM, int TL, bool RES, bool REUSE>
+__global__ void __launch_bounds__(PNR_BLOCK, (RES && TL > 64) ? 1 : 2)
+    dense_diag_mfma_kernel(DenseLoopArgs<float> a) {
+  static_assert(!(RES && REUSE), "the resident variant keeps no refresh-point iterate");
   extern __shared__ __align__(16) float lds[];
+  __shared__ uint32_t s_wmax[PNR_WAVES];
+  __shared__ int s_flag;
   Ctrl* ctrl = a.ctrl;
-  constexpr int D = DM, LD = DM + 4, P = PNR_BLOCK / DM, LP = kTL / P, SV = 3 * DM, SA = 2 * DM;
+  constexpr int D = DM, LD = DM + 4, P = PNR_BLOCK / DM, LP = TL / P, SVP = 3 * DM;
+  constexpr int NCB = D / 16, TBS = PNR_WAVES / NCB, NTB = (TL / 16) / TBS;   // MFMA work split
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int T = a.T;
-  const bool reuse = a.nbuf > 2;
-  const int WMAX = mfd_window(D);
+  constexpr size_t XS = (size_t)(TL + 1) * LD;
   float* Bh = lds;
-  float* X = Bh + 3 * D;
-  float* Xj = X + (kTL + 1) * LD;
-  float* R = Xj + (reuse ? (kTL + 1) * LD : 0);
-  float* Jd = R + kTL * D;
-  float* Sa = Jd + kTL * D;
+  float* Xb0 = Bh + 3 * D;
+  float* Xb1 = Xb0 + XS;
+  float* Xj = Xb1 + (RES ? XS : 0);
+  float* R = Xj + (REUSE ? XS : 0);
+  float* Jd = R + TL * D;
+  float* Sa = Jd + TL * D;
   float* Sb = Sa + P * D;
-  float* Win = Sb + P * D;
-  float* Din = Win + WMAX * SV;
+  float* Agg = Sb + P * D;
+  float* Din = Agg + 2 * P * D;
 
   for (int i = tid; i < 3 * D; i += PNR_BLOCK) Bh[i] = a.bh ? a.bh[i] : 0.f;
   // this wave's U fragments (recurrent product) and the diagonal of each gate block
-  const int cb = wid % (D / 16), tb0 = wid / (D / 16), tbs = PNR_WAVES / (D / 16);
+  const int cb = wid % NCB, tb0 = wid / NCB;
   const int c_mf = cb * 16 + (lane & 15);
   float uf[3][D / 4], udg[3];
 #pragma unroll
   for (int g = 0; g < 3; ++g) {
 #pragma unroll
-    for (int kk = 0; kk < D / 4; ++kk) uf[g][kk] = a.U[(size_t)(g * D + c_mf) * D + 4 * kk + (lane >> 4)];
+    for (int kk = 0; kk < D / 4; ++kk) uf[g][kk] = a.U[(size_t)(g * D + c_mf) * D + (lane >> 4) * (D / 4) + kk];
     udg[g] = a.U[(size_t)(g * D + c_mf) * D + c_mf];
   }
-  __syncthreads();
-  const float bhr = Bh[c_mf], bhz = Bh[D + c_mf], bhn = Bh[2 * D + c_mf];
+  const float bhr = a.bh ? a.bh[c_mf] : 0.f, bhz = a.bh ? a.bh[D + c_mf] : 0.f,
+              bhn = a.bh ? a.bh[2 * D + c_mf] : 0.f;
   const int pp_ = tid / D, ci = tid - pp_ * D;   // scan layout: part, channel
+  const int grid = (int)gridDim.x;
+  const bool merger = (a.n_tiles - 1) % grid == (int)blockIdx.x;
+
+  // Gate inputs of step tb*16 + 4(lane/16) + i, channel c_mf, of a tile.
+  auto load_gx = [&](float (&v)[4][3], int b, int t0, int Lv, int tb) {
+    const float* gxb = a.gx + (size_t)b * T * 3 * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = tb * 16 + 4 * (lane >> 4) + i;
+      const float* g = gxb + (size_t)(t0 + s) * 3 * D;
+#pragma unroll
+      for (int q = 0; q < 3; ++q) v[i][q] = s < Lv ? g[q * D + c_mf] : 0.f;
+    }
+  };
+
+  if (RES)
+    for (int i = tid; i < (int)XS; i += PNR_BLOCK) Xb1[i] = 0.f;
+  float* Xc = Xb0;   // iterate whose residual this pass checks
+  float* Xn = Xb1;   // the next iterate (resident mode)
+
+  // Leaves the loop once a stop decision is published.  Before the fix-up of pass k the
+  // decided iterate is k or k-1, both still in LDS: the resident variant writes its tile
+  // of it to the caller's output.
+  auto finish = [&](int k) {
+    if (RES && !has_fault(ctrl)) {
+      const int kd = (int)(load_dec(ctrl) >> 32) - 1;
+      const float* Xr = kd == k ? Xc : Xn;
+      const int seg = (int)blockIdx.x / a.B, b = (int)blockIdx.x - seg * a.B;
+      const int t0 = seg * TL, Lv = min(TL, T - t0);
+      for (int i = tid; i < Lv * D; i += PNR_BLOCK) {
+        const int s = i / D, c = i - s * D;
+        a.out[((size_t)b * T + t0 + s) * D + c] = Xr[(s + 1) * LD + c];
+      }
+    }
+  };
 
   int cur = -1, jac = -1;
+  __syncthreads();
   for (int k = 0; k <= a.max_iters; ++k) {
     const bool resid_only = k == a.max_iters;
     if (!resid_only && k % a.jac_every == 0) jac = cur;
-    const int next = resid_only ? cur : next_buffer(cur, jac, a.nbuf);
+    const int next = resid_only ? cur : next_buffer(cur, REUSE ? jac : -1, a.nbuf);
     const float* Hcur = cur >= 0 ? a.H[cur] : nullptr;
     const float* Hjac = jac >= 0 ? a.H[jac] : nullptr;
     float* Hnext = next >= 0 ? a.H[next] : nullptr;
-    const bool stale = !resid_only && jac != cur;
+    const bool stale = REUSE && !resid_only && jac != cur;
     const uint32_t ep = (uint32_t)k + 1u;
+    const int km3 = k % 3;
     uint32_t blk_max = 0;
+    bool dec_seen = k == 0;   // the decision on pass k-1 (none before pass 0)
+    int stop = 0;             // 1: a stop decision ended a wait; 2: fault
     // Items go out time-segment-major (segment s of every batch row before segment
-    // s+1), so a tile's predecessor always has a smaller item index: it was handed out
-    // earlier, and prefixes are usually published before a successor looks back.
-    for (int item = blockIdx.x; item < a.n_tiles; item += gridDim.x) {
-      if (has_fault(ctrl)) break;
+    // s+1), so a tile's predecessors have smaller item indices: they were handed out
+    // earlier, and their aggregates are usually published before a successor looks back.
+    for (int item = blockIdx.x; item < a.n_tiles && !stop; item += grid) {
+      const bool last_item = item + grid >= a.n_tiles;
       const int seg = item / a.B, b = item - seg * a.B;
       const int tile = b * a.tiles_per_row + seg;   // slot index: row-major
-      const int t0 = seg * kTL, Lv = min(kTL, T - t0);
-      const float* gxb = a.gx + (size_t)b * T * 3 * D;
-      stage_rows(X, Hcur, a.h0, b, t0, T, D, LD);
-      if (stale) stage_rows(Xj, Hjac, a.h0, b, t0, T, D, LD);
+      const int t0 = seg * TL, Lv = min(TL, T - t0);
+
+      // ---- stage the iterate: rows 1..TL (own writes of the previous pass) and the halo ----
+      if (!RES || k == 0) stage_rows<TL>(Xc, Hcur, a.h0, b, t0, T, D, LD);
+      if (stale) stage_rows<TL>(Xj, Hjac, a.h0, b, t0, T, D, LD);
+      if (tid == 0) s_flag = 0;
+      __syncthreads();
+      // The halo (the state before the tile's first step) is the tile's own: it starts
+      // at zero (the initial guess) and each fix-up adds the increment that enters the
+      // tile, which the look-back delivers.  No tile waits for its predecessor's states.
+      float* hal = reinterpret_cast<float*>(a.slots + (size_t)a.n_tiles * 3 * SVP) + (size_t)tile * 2 * D;
+      if (!RES && tid < D)
+        Xc[tid] = seg == 0 ? (a.h0 ? a.h0[(size_t)b * D + tid] : 0.f) : (k == 0 ? 0.f : hal[tid]);
+      if (REUSE && tid < D) {
+        // the halo of the refresh-point iterate, for the passes that reuse its Jacobian
+        if (!resid_only && k % a.jac_every == 0) hal[D + tid] = Xc[tid];
+        if (stale) Xj[tid] = hal[D + tid];
+      }
       __syncthreads();
 
       // ---- cell on MFMA: residual and diagonal Jacobian ----
       uint32_t tmax = 0;
-      for (int tb = tb0; tb < kTL / 16; tb += tbs) {
-        float gxv[4][3];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int s = tb * 16 + 4 * (lane >> 4) + i;
-          const float* g = gxb + (size_t)(t0 + s) * 3 * D;
-#pragma unroll
-          for (int q = 0; q < 3; ++q) gxv[i][q] = s < Lv ? g[q * D + c_mf] : 0.f;
+      // Residual and Jacobian diagonal of this lane's 4 steps of a block of 16, from the
+      // block's gate products.  Branch-free (steps past the end of the sequence are
+      // masked), so the compiler can interleave it with the next block's MFMAs.
+      auto cell_elem = [&](int tb, const v4f (&acc)[3], const float (&gv)[4][3]) {
+        v4f accj[3];
+        if (stale) {
+          v4f fj[D / 16];
+          load_afrag<D>(Xj, LD, tb, fj);
+          gates_frag<D>(fj, uf, accj);
         }
-        v4f acc[3], accj[3];
-        gates_block<D>(X, LD, tb, uf, acc);
-        if (stale) gates_block<D>(Xj, LD, tb, uf, accj);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int s = tb * 16 + 4 * (lane >> 4) + i;
           const int idx = s * D + c_mf;
-          if (s >= Lv) {
-            R[idx] = 0.f;
-            Jd[idx] = 1.f;
-            continue;
-          }
-          const float p = X[s * LD + c_mf];
-          float r = sigm(gxv[i][0] + acc[0][i] + bhr);
-          float z = sigm(gxv[i][1] + acc[1][i] + bhz);
+          const bool ok = s < Lv;
+          const float p = Xc[s * LD + c_mf];
+          float r = sigm(gv[i][0] + acc[0][i] + bhr);
+          float z = sigm(gv[i][1] + acc[1][i] + bhz);
           float ghn = acc[2][i] + bhn;
-          float n = tanh_(fmaf(r, ghn, gxv[i][2]));
-          const float res = fmaf(z, p - n, n) - X[(s + 1) * LD + c_mf];
+          float n = tanh_(fmaf(r, ghn, gv[i][2]));
+          float res = fmaf(z, p - n, n) - Xc[(s + 1) * LD + c_mf];
+          res = ok ? res : 0.f;
           R[idx] = res;
           tmax = max(tmax, abs_bits(res));
-          if (resid_only) continue;
           float pj = p;
           if (stale) {
             pj = Xj[s * LD + c_mf];
-            r = sigm(gxv[i][0] + accj[0][i] + bhr);
-            z = sigm(gxv[i][1] + accj[1][i] + bhz);
+            r = sigm(gv[i][0] + accj[0][i] + bhr);
+            z = sigm(gv[i][1] + accj[1][i] + bhz);
             ghn = accj[2][i] + bhn;
-            n = tanh_(fmaf(r, ghn, gxv[i][2]));
+            n = tanh_(fmaf(r, ghn, gv[i][2]));
           }
           const float omz = 1.f - z, cn = omz * (1.f - n * n);
-          Jd[idx] = a.jac_mode == PNR_JAC_ZERO
-                        ? 0.f
-                        : z + (pj - n) * z * omz * udg[1] + cn * ghn * r * (1.f - r) * udg[0] + cn * r * udg[2];
+          float jd = z + (pj - n) * z * omz * udg[1] + cn * ghn * r * (1.f - r) * udg[0] + cn * r * udg[2];
+          jd = a.jac_mode == PNR_JAC_ZERO ? 0.f : jd;
+          Jd[idx] = ok ? jd : 1.f;
         }
+      };
+      // Software pipeline over the blocks of 16 steps: block u's MFMAs are issued
+      // before block u-1's elementwise work, which does not depend on them.  The gate
+      // inputs are loaded a block ahead.
+      {
+        v4f fa[D / 16];
+        v4f accA[3], accB[3];
+        float gvA[4][3], gvB[4][3];
+        load_afrag<D>(Xc, LD, tb0, fa);
+        load_gx(gvA, b, t0, Lv, tb0);
+        gates_frag<D>(fa, uf, accA);
+        if (NTB > 1) load_afrag<D>(Xc, LD, tb0 + TBS, fa);
+#pragma unroll 1
+        for (int u = 1; u < NTB; ++u) {
+          load_gx(gvB, b, t0, Lv, tb0 + u * TBS);
+          gates_frag<D>(fa, uf, accB);
+          if (u + 1 < NTB) load_afrag<D>(Xc, LD, tb0 + (u + 1) * TBS, fa);
+          cell_elem(tb0 + (u - 1) * TBS, accA, gvA);
+#pragma unroll
+          for (int g = 0; g < 3; ++g) accA[g] = accB[g];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 3; ++q) gvA[i][q] = gvB[i][q];
+        }
+        cell_elem(tb0 + (NTB - 1) * TBS, accA, gvA);
       }
       blk_max = max(blk_max, tmax);
       __syncthreads();
+
+      // ---- the block's residual maximum of this pass; the merging block decides ----
+      if (last_item) {
+        uint32_t m = wave_max_u32(blk_max);
+        if (lane == 0) s_wmax[wid] = m;
+        __syncthreads();
+        if (tid == 0) {
+          for (int w2 = 0; w2 < PNR_WAVES; ++w2) m = max(m, s_wmax[w2]);
+          __hip_atomic_store(a.partials + (size_t)km3 * grid + blockIdx.x, ((uint64_t)ep << 32) | m,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (merger) {
+          uint32_t mm = 0;
+          int wst = 0;
+          for (int i = tid; i < grid; i += PNR_BLOCK) {
+            const uint64_t* pw = a.partials + (size_t)km3 * grid + i;
+            uint64_t x = 0;
+            const int w = wait_for([&]() {
+              x = __hip_atomic_load(pw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              return (uint32_t)(x >> 32) == ep;
+            }, ctrl);
+            if (w) wst = w;
+            mm = max(mm, (uint32_t)x);
+          }
+          mm = wave_max_u32(mm);
+          __syncthreads();
+          if (lane == 0) s_wmax[wid] = mm;
+          if (wst) atomicMax(&s_flag, wst);
+          __syncthreads();
+          if (s_flag) {
+            stop = s_flag;
+            break;
+          }
+          if (tid == 0) {
+            for (int w2 = 0; w2 < PNR_WAVES; ++w2) mm = max(mm, s_wmax[w2]);
+            finish_iteration(ctrl, a.rho_hist, bits_to_rho(mm), k, cur, a.max_iters, a.tol);
+            const int done = __hip_atomic_load(&ctrl->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            drain_memory_ops();   // rho, status and iters land before the decision word
+            __hip_atomic_store(&ctrl->dec, ((uint64_t)ep << 32) | (uint64_t)(done ? 1 : 0), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            s_flag = done ? 1 : 0;
+          }
+          __syncthreads();
+          if (s_flag) {   // this block just decided to stop
+            stop = s_flag;
+            break;
+          }
+        }
+      }
+
+      uint64_t* myslot = a.slots + ((size_t)tile * 3 + km3) * SVP;
+      float ta = 1.f, tbv = 0.f;
+      if (!resid_only) {
+        // ---- scan inside the tile: part aggregates, tile total, publication ----
+        float ea = 1.f, eb = 0.f;
+        {
+          float jv[LP], rv[LP];   // all loads of the part first, then the serial composition
+#pragma unroll
+          for (int j = 0; j < LP; ++j) {
+            jv[j] = Jd[(pp_ * LP + j) * D + ci];
+            rv[j] = R[(pp_ * LP + j) * D + ci];
+          }
+#pragma unroll
+          for (int j = 0; j < LP; ++j) {
+            eb = fmaf(jv[j], eb, rv[j]);
+            ea *= jv[j];
+          }
+        }
+        Sa[pp_ * D + ci] = ea;
+        Sb[pp_ * D + ci] = eb;
+        __syncthreads();
+        if (tid < D) {
+          for (int q = 0; q < P; ++q) {
+            tbv = fmaf(Sa[q * D + tid], tbv, Sb[q * D + tid]);
+            ta *= Sa[q * D + tid];
+          }
+          if (seg == 0) {
+            slot_put(myslot + 2 * D + tid, ep, tbv);
+          } else {
+            slot_put(myslot + tid, ep, ta);
+            slot_put(myslot + D + tid, ep, tbv);
+          }
+        }
+        // ---- decoupled look-back over the predecessors, in registers ----
+        if (seg > 0) {
+          int w = 0;
+          const float dl = lookback_regs<D, mfd_lookback_per_thread(DM, RES)>(a.slots, tile, seg, km3, ep, Agg,
+                                                                               ctrl, w);
+          if (w) {
+            stop = w;
+            break;
+          }
+          if (tid < D) {
+            Din[tid] = dl;
+            slot_put(myslot + 2 * D + tid, ep, fmaf(ta, dl, tbv));
+          }
+        } else if (tid < D) {
+          Din[tid] = 0.f;
+        }
+      }
+
       if (resid_only) continue;
 
-      // ---- scan inside the tile: part aggregates, tile total, publication ----
-      float ea = 1.f, eb = 0.f;
-      for (int s = pp_ * LP; s < (pp_ + 1) * LP; ++s) {
-        const float ja = Jd[s * D + ci];
-        eb = fmaf(ja, eb, R[s * D + ci]);
-        ea *= ja;
-      }
-      Sa[pp_ * D + ci] = ea;
-      Sb[pp_ * D + ci] = eb;
-      __syncthreads();
-      uint64_t* myslot = a.slots + (size_t)tile * SV;
-      float ta = 1.f, tbv = 0.f;
-      if (tid < D) {
-        for (int q = 0; q < P; ++q) {
-          tbv = fmaf(Sa[q * D + tid], tbv, Sb[q * D + tid]);
-          ta *= Sa[q * D + tid];
+      // ---- the decision on pass k-1 guards the first overwrite of iterate k-1 ----
+      if (!dec_seen) {
+        if (tid == 0) {
+          uint64_t d = 0;
+          const int w = wait_for([&]() {
+            d = load_dec(ctrl);
+            return (uint32_t)(d >> 32) >= (uint32_t)k;
+          }, ctrl);
+          s_flag = w ? w : (int)(d & 1ull);
         }
-        if (seg == 0) {
-          slot_put(myslot + 2 * D + tid, ep, tbv);
-          Din[tid] = 0.f;
-        } else {
-          slot_put(myslot + tid, ep, ta);
-          slot_put(myslot + D + tid, ep, tbv);
+        __syncthreads();
+        if (s_flag) {
+          stop = s_flag;
+          break;
         }
-      }
-      // ---- decoupled look-back over a window of predecessors ----
-      if (seg > 0) {
-        uint32_t spins = 0;
-        while (true) {
-          const int pw = window_read(a.slots, tile, min(seg, WMAX), SV, SA, ep, Win);
-          if (pw >= 0) {
-            if (tid < D) {
-              float dl = Win[pw * SV + 2 * D + tid];
-              for (int w = pw - 1; w >= 0; --w) dl = fmaf(Win[w * SV + tid], dl, Win[w * SV + D + tid]);
-              Din[tid] = dl;
-              slot_put(myslot + 2 * D + tid, ep, fmaf(ta, dl, tbv));
-            }
-            break;
-          }
-          if (++spins > kSpinLimit) {
-            if (tid == 0) record_fault(ctrl, 1);
-            if (tid < D) Din[tid] = 0.f;
-            break;
-          }
-          backoff(spins);
-        }
+        dec_seen = true;
       }
       __syncthreads();
       // ---- fix-up: each (part, channel) walks its steps from its incoming increment ----
       {
         float dl = Din[ci];
         for (int q = 0; q < pp_; ++q) dl = fmaf(Sa[q * D + ci], dl, Sb[q * D + ci]);
-        for (int s = pp_ * LP; s < min(Lv, (pp_ + 1) * LP); ++s) {
-          dl = fmaf(Jd[s * D + ci], dl, R[s * D + ci]);
-          float* o = Hnext + ((size_t)b * T + t0 + s) * D + ci;
-          const float v = X[(s + 1) * LD + ci] + dl;
-          if (s == kTL - 1) coherent_store(o, v);   // the next tile's halo
-          else *o = v;
+        if (tid < D) {   // the next iterate's halo
+          const float h = seg == 0 ? (a.h0 ? a.h0[(size_t)b * D + tid] : 0.f) : Xc[tid] + Din[tid];
+          if (RES) Xn[tid] = h;
+          else hal[tid] = h;
+        }
+        float jv[LP], rv[LP];
+#pragma unroll
+        for (int j = 0; j < LP; ++j) {
+          jv[j] = Jd[(pp_ * LP + j) * D + ci];
+          rv[j] = R[(pp_ * LP + j) * D + ci];
+        }
+#pragma unroll
+        for (int j = 0; j < LP; ++j) {
+          const int s = pp_ * LP + j;
+          dl = fmaf(jv[j], dl, rv[j]);
+          if (s >= Lv) continue;
+          const float v = Xc[(s + 1) * LD + ci] + dl;
+          if (RES) Xn[(s + 1) * LD + ci] = v;
+          else Hnext[((size_t)b * T + t0 + s) * D + ci] = v;
         }
       }
       __syncthreads();
     }
-    end_pass(a, blk_max, k, cur);
-    if (__hip_atomic_load(&ctrl->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) || has_fault(ctrl)) break;
+    if (stop == 0 && resid_only) {
+      // the last pass: wait for its (stopping) decision
+      if (tid == 0) {
+        const int w = wait_for([&]() { return (uint32_t)(load_dec(ctrl) >> 32) >= (uint32_t)(k + 1); }, ctrl);
+        s_flag = w == 2 ? 2 : 1;
+      }
+      __syncthreads();
+      stop = s_flag;
+    }
+    if (stop) {
+      finish(k);
+      return;
+    }
     cur = next;
+    if (RES) {
+      float* t = Xc;
+      Xc = Xn;
+      Xn = t;
+    }
   }
 }
 
@@ -695,32 +1037,70 @@ int dense_mfma_supported(int D, int full, int is_f64) {
   return full ? D == kF : (D == 16 || D == 32 || D == 64);
 }
 int dense_mfma_tile_len() { return kTL; }
-int dense_mfma_slot_words(int D, int full) { return full ? kFSlot : 3 * D; }
+int dense_mfma_slot_words(int D, int full) { return full ? kFSlot : 10 * D; }
 
-template <class F>
-static hipError_t coop_launch(F fn, const DenseLoopArgs<float>& a, size_t lds, int num_cu, hipStream_t st) {
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
+static int block_occupancy(const void* fn, size_t lds) {
+  if (lds > 65536 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+    return 0;
   int v = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, fn, PNR_BLOCK, lds) != hipSuccess || v < 1)
-    return hipErrorInvalidConfiguration;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, fn, PNR_BLOCK, lds) != hipSuccess) return 0;
+  return v;
+}
+
+// Cooperative launch of a persistent loop kernel: at most the co-resident grid, at most
+// one block per tile.
+static hipError_t coop_launch(const void* fn, const DenseLoopArgs<float>& a, size_t lds, int num_cu, hipStream_t st) {
+  const int v = block_occupancy(fn, lds);
+  if (v < 1) return hipErrorInvalidConfiguration;
   long g = (long)v * num_cu;
   if (g > kMaxGrid) g = kMaxGrid;
   if (g > a.n_tiles) g = a.n_tiles;
   if (g < 1) g = 1;
   void* args[] = {const_cast<DenseLoopArgs<float>*>(&a)};
-  return hipLaunchCooperativeKernel((const void*)fn, dim3((int)g), dim3(PNR_BLOCK), args, (unsigned)lds, st);
+  return hipLaunchCooperativeKernel(fn, dim3((int)g), dim3(PNR_BLOCK), args, (unsigned)lds, st);
+}
+
+template <int DM>
+static const void* diag_kernel(int res_tile, bool reuse) {
+  if (res_tile == 128) return DM == 64 ? (const void*)dense_diag_mfma_kernel<64, 128, true, false> : nullptr;
+  if (res_tile) return (const void*)dense_diag_mfma_kernel<DM, kTL, true, false>;
+  return reuse ? (const void*)dense_diag_mfma_kernel<DM, kTL, false, true>
+               : (const void*)dense_diag_mfma_kernel<DM, kTL, false, false>;
+}
+static const void* diag_kernel_for(int D, int res_tile, bool reuse) {
+  if (D == 16) return diag_kernel<16>(res_tile, reuse);
+  if (D == 32) return diag_kernel<32>(res_tile, reuse);
+  return diag_kernel<64>(res_tile, reuse);
+}
+
+// PNR_DENSE_RESIDENT: "0" never, "64" / "128" only that tile length (tests and tuning).
+int dense_mfma_resident_tile(int D, int full, int B, int T, int reuse, int num_cu) {
+  if (full || reuse || !dense_mfma_supported(D, 0, 0) || B < 1 || T < 1) return 0;
+  const char* env = getenv("PNR_DENSE_RESIDENT");
+  const int only = env ? atoi(env) : -1;
+  if (only == 0) return 0;
+  for (int tl : {64, 128}) {
+    if ((only > 0 && tl != only) || (tl == 128 && D != 64)) continue;
+    const long tiles = (long)B * ((T + tl - 1) / tl);
+    const int v = block_occupancy(diag_kernel_for(D, tl, false), mfd_lds_floats(D, tl, 0, 1) * 4);
+    if (v >= 1 && tiles <= kMaxGrid && (long)v * num_cu >= tiles) return tl;
+  }
+  return 0;
 }
 
 hipError_t launch_dense_mfma(const DenseLoopArgs<float>& a, int full, int num_cu, hipStream_t st) {
-  const int reuse = a.nbuf > 2;
-  if (full) return coop_launch(dense_full_mfma_kernel, a, mff_lds_floats(reuse) * 4, num_cu, st);
-  const size_t lds = mfd_lds_floats(a.D, reuse) * 4;
-  if (a.D == 16) return coop_launch(dense_diag_mfma_kernel<16>, a, lds, num_cu, st);
-  if (a.D == 32) return coop_launch(dense_diag_mfma_kernel<32>, a, lds, num_cu, st);
-  return coop_launch(dense_diag_mfma_kernel<64>, a, lds, num_cu, st);
+  const bool reuse = a.nbuf > 2;
+  if (full) return coop_launch((const void*)dense_full_mfma_kernel, a, mff_lds_floats(reuse) * 4, num_cu, st);
+  const bool res = a.out != nullptr;
+  const bool dreuse = a.jac_every > 1;
+  if (a.nbuf != (dreuse ? 3 : 2)) return hipErrorInvalidValue;
+  if (res && (dreuse || !(a.L == kTL || (a.L == 128 && a.D == 64)))) return hipErrorInvalidValue;
+  if (!res && a.L != kTL) return hipErrorInvalidValue;
+  const void* fn = diag_kernel_for(a.D, res ? a.L : 0, dreuse);
+  const size_t lds = mfd_lds_floats(a.D, a.L, dreuse, res) * 4;
+  // the resident variant needs one co-resident block per tile
+  if (res && (long)block_occupancy(fn, lds) * num_cu < a.n_tiles) return hipErrorInvalidValue;
+  return coop_launch(fn, a, lds, num_cu, st);
 }
 
 }  // namespace pnr

@@ -12,10 +12,14 @@ constexpr int kMaxGrid = 16384;
 // Decision taken by the block that merges the residual partials of iteration k (the
 // "final block" of the two-level reduction): record rho_k and stop when it is within
 // tol, not finite, or when k is the residual-only pass after max_iters updates.
+//
+// Every field of the control block is written with agent-scope (coherent) stores: the
+// merging block differs from pass to pass and may sit on another XCD, and plain stores
+// of one address from several XCDs' L2 caches reach memory in no defined order.
 __device__ inline void finish_iteration(Ctrl* c, double* hist, double rho, int k, int cur_buf,
                                         int max_iters, double tol) {
   hist[k] = rho;
-  c->rho = rho;
+  __hip_atomic_store(&c->rho, rho, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   int done = 0, status = PNR_NOT_CONVERGED;
   if (!(rho < __builtin_inf())) {
     done = 1; status = PNR_NONFINITE;
@@ -25,9 +29,9 @@ __device__ inline void finish_iteration(Ctrl* c, double* hist, double rho, int k
     done = 1; status = PNR_NOT_CONVERGED;
   }
   if (done) {
-    c->status = status;
-    c->iters = k;
-    c->result_buf = cur_buf;
+    __hip_atomic_store(&c->status, status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&c->iters, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&c->result_buf, cur_buf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // every block reads `done` right after the barrier: publish it coherently
     __hip_atomic_store(&c->done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -66,10 +70,11 @@ struct DenseLoopArgs {
   const Tt* U;         // [3D][D]
   const Tt* bh;        // [3D] or nullptr
   const Tt* h0;        // [B][D] or nullptr
-  Tt* H[3];            // state buffers [B][T][D]
+  Tt* H[4];            // state buffers [B][T][D] (dense_state_buffers of them)
+  Tt* out;             // resident mode only: the caller's h_out, written by the loop kernel
   int nbuf;
   uint64_t* slots;
-  uint64_t* partials;
+  uint64_t* partials;  // kPartialWords
   Ctrl* ctrl;
   double* rho_hist;
   int B, D, T;
@@ -80,7 +85,9 @@ struct DenseLoopArgs {
   double tol;
 };
 
-// Tile length and look-back slot words per tile for the dense GRU path.
+// Tile length, look-back slot words per tile and number of [B][T][D] state buffers for
+// the dense GRU path.
+int dense_state_buffers(int D, int full, int is_f64, int reuse);
 int dense_tile_len(int D, int full, int is_f64);
 int dense_slot_words(int D, int full, int is_f64);
 size_t dense_lds_bytes(int D, int full, int is_f64, int reuse);
@@ -91,6 +98,10 @@ int dense_mfma_supported(int D, int full, int is_f64);
 int dense_mfma_tile_len();
 int dense_mfma_slot_words(int D, int full);
 hipError_t launch_dense_mfma(const DenseLoopArgs<float>& a, int full, int num_cu, hipStream_t st);
+// Tile length of the resident variant when every tile can own a co-resident block (and
+// the variant applies), else 0.  The caller then sets DenseLoopArgs::L and ::out (the
+// loop kernel writes h_out itself) and skips the output kernel.
+int dense_mfma_resident_tile(int D, int full, int B, int T, int reuse, int num_cu);
 hipError_t launch_dense_newton_f64(const DenseLoopArgs<double>& a, int full, int num_cu, hipStream_t st);
 
 // ---------------------------------------------------------------------------------
@@ -108,12 +119,16 @@ hipError_t launch_gemm(int in_dtype, int out_dtype, const GemmArgs& g, hipStream
 
 // ---------------------------------------------------------------------------------
 // Misc: control/slot initialisation and the output layout conversion.
-hipError_t launch_init(Ctrl* ctrl, uint64_t* slots, size_t slot_words, hipStream_t st);
+// Per-block residual words: three per block (one per pass modulo 3) for the barrier-free
+// loops, which tag each word with its pass.
+constexpr size_t kPartialWords = 3 * (size_t)kMaxGrid;
+hipError_t launch_init(Ctrl* ctrl, uint64_t* slots, size_t slot_words, uint64_t* partials, size_t partial_words,
+                       hipStream_t st);
 // diag layout [B][S][T] -> h_out [B][T][S] (or zeros when the result is the zero guess)
 hipError_t launch_diag_output(const float* const* bufs, const Ctrl* ctrl, float* h_out, int B, int S,
                               int T, hipStream_t st);
 template <typename Tt>
-hipError_t launch_dense_output(const Tt* const* bufs, const Ctrl* ctrl, Tt* h_out, size_t n,
+hipError_t launch_dense_output(const Tt* const* bufs /* 4 */, const Ctrl* ctrl, Tt* h_out, size_t n,
                                hipStream_t st);
 
 // Standalone scan (testing entry point)

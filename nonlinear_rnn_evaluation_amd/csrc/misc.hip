@@ -6,7 +6,7 @@
 
 namespace pnr {
 
-__global__ void init_kernel(Ctrl* ctrl, uint64_t* slots, size_t n) {
+__global__ void init_kernel(Ctrl* ctrl, uint64_t* slots, size_t n, uint64_t* partials, size_t np) {
   const size_t i0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i0 == 0) {
     ctrl->done = 0;
@@ -19,16 +19,20 @@ __global__ void init_kernel(Ctrl* ctrl, uint64_t* slots, size_t n) {
     ctrl->bar_gen = 0;
     ctrl->fault = 0;
     for (int g = 0; g < kBarGroups; ++g) ctrl->bar_group[g].count = 0;
+    ctrl->dec = 0;
   }
   // epoch 0 is never a live epoch, so zeroed words read as "not yet written"
   for (size_t i = i0; i < n; i += (size_t)gridDim.x * blockDim.x) slots[i] = 0;
+  for (size_t i = i0; i < np; i += (size_t)gridDim.x * blockDim.x) partials[i] = 0;
 }
 
-hipError_t launch_init(Ctrl* ctrl, uint64_t* slots, size_t slot_words, hipStream_t st) {
-  size_t blocks = (slot_words + 255) / 256;
+hipError_t launch_init(Ctrl* ctrl, uint64_t* slots, size_t slot_words, uint64_t* partials, size_t partial_words,
+                       hipStream_t st) {
+  size_t blocks = ((slot_words > partial_words ? slot_words : partial_words) + 255) / 256;
   if (blocks < 1) blocks = 1;
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(init_kernel, dim3((unsigned)blocks), dim3(256), 0, st, ctrl, slots, slot_words);
+  hipLaunchKernelGGL(init_kernel, dim3((unsigned)blocks), dim3(256), 0, st, ctrl, slots, slot_words, partials,
+                     partial_words);
   return hipGetLastError();
 }
 
@@ -64,10 +68,10 @@ hipError_t launch_diag_output(const float* const* bufs, const Ctrl* ctrl, float*
   return hipGetLastError();
 }
 
-template <typename Tt> struct Bufs3 { const Tt* p[3]; };
+template <typename Tt> struct Bufs4 { const Tt* p[4]; };
 
 template <typename Tt>
-__global__ void dense_output_kernel(Bufs3<Tt> bufs, const Ctrl* ctrl, Tt* out, size_t n) {
+__global__ void dense_output_kernel(Bufs4<Tt> bufs, const Ctrl* ctrl, Tt* out, size_t n) {
   const int rb = ctrl->result_buf;
   const Tt* src = rb >= 0 ? bufs.p[rb] : nullptr;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
@@ -76,7 +80,7 @@ __global__ void dense_output_kernel(Bufs3<Tt> bufs, const Ctrl* ctrl, Tt* out, s
 
 template <typename Tt>
 hipError_t launch_dense_output(const Tt* const* bufs, const Ctrl* ctrl, Tt* h_out, size_t n, hipStream_t st) {
-  Bufs3<Tt> bb{{bufs[0], bufs[1], bufs[2]}};
+  Bufs4<Tt> bb{{bufs[0], bufs[1], bufs[2], bufs[3]}};
   size_t blocks = (n + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) blocks = 1;

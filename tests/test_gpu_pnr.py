@@ -241,13 +241,17 @@ def test_repeated_calls_reuse_workspace():
         assert torch.allclose(again["h"], first["h"], atol=1e-6, rtol=0)
 
 
+@pytest.mark.parametrize("resident", ["64", "128", "0"])
 @pytest.mark.parametrize("D,mode,every", [(16, WL.JAC_FULL, 1), (16, WL.JAC_FULL, 2), (16, WL.JAC_DIAG, 1),
-                                          (32, WL.JAC_DIAG, 2), (64, WL.JAC_DIAG, 1), (64, WL.JAC_ZERO, 1)])
-def test_mfma_dense_paths_match_newton_oracle(D, mode, every):
+                                          (32, WL.JAC_DIAG, 1), (32, WL.JAC_DIAG, 2), (64, WL.JAC_DIAG, 1),
+                                          (64, WL.JAC_ZERO, 1), (64, WL.JAC_DIAG, 3)])
+def test_mfma_dense_paths_match_newton_oracle(D, mode, every, resident, monkeypatch):
     """fp32 dense-U GRU with D in {16, 32, 64}: the recurrent product (and, for the dense
     Jacobian, the scan) run on MFMA; iterates must match the oracle's, over several
-    64-step tiles and a ragged tail."""
-    T = 3 * 64 + 17
+    tiles and a ragged tail, with the diagonal-Jacobian kernel resident (states in LDS
+    across iterations; 64- or, for D = 64, 128-step tiles) and streaming."""
+    monkeypatch.setenv("PNR_DENSE_RESIDENT", resident)
+    T = 3 * 128 + 17
     p = WL.random_problem(WL.CELL_GRU, 2, T, D, 7, seed=D + every, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32,
                           bias_std=0.2, h0_std=0.3, w_std=0.5 / math.sqrt(D))
     q = _f64(p)
@@ -263,3 +267,20 @@ def test_mfma_dense_paths_match_newton_oracle(D, mode, every):
     ref = O.sequential(WL.CELL_GRU, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"])
     if got["status"] == pnr.OK:
         assert np.abs(_np(got["h"]) - ref).max() < 1e-4
+
+
+@pytest.mark.parametrize("resident", ["64", "128", "0"])
+def test_mfma_dense_diag_long_row_chains_lookback_windows(resident, monkeypatch):
+    """One batch row much longer than the look-back window of the D = 64 kernel (32
+    tiles): tiles beyond the window resolve from a predecessor's published prefix."""
+    monkeypatch.setenv("PNR_DENSE_RESIDENT", resident)
+    D, T = 64, 64 * 128 + 300
+    p = WL.random_problem(WL.CELL_GRU, 1, T, D, 8, seed=11, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32,
+                          bias_std=0.2, h0_std=0.3, w_std=0.5 / math.sqrt(D))
+    q = _f64(p)
+    for k in (1, 3):
+        got = _run(WL.CELL_GRU, p, k, -1.0, WL.JAC_DIAG)
+        ref = O.newton_dense(WL.CELL_GRU, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], k, -1.0,
+                             WL.JAC_DIAG, 1, solver="loop")
+        np.testing.assert_allclose(_np(got["h"]), ref["states"], rtol=0, atol=1e-4)
+        np.testing.assert_allclose(got["history"], ref["rhos"], rtol=1e-3, atol=1e-5)
