@@ -39,7 +39,8 @@ def newton_kernel(w, mode):
     if w.state_dtype == WL.DT_F32 and ((full and w.D == 16) or (not full and w.D in (16, 32, 64))):
         if full:
             return "pnr::dense_full_mfma_kernel", CSRC + "dense_mfma.hip"
-        return f"pnr::dense_diag_mfma_kernel<{w.D}>", CSRC + "dense_mfma.hip"
+        # template arguments <D, tile, resident, reuse>: the library picks the variant
+        return f"pnr::dense_diag_mfma_kernel<{w.D}, *>", CSRC + "dense_mfma.hip"
     return "pnr::dense_newton_kernel", CSRC + "dense_iter.hip"
 
 

@@ -210,10 +210,11 @@ __device__ __forceinline__ int window_read(const uint64_t* __restrict__ slots, i
 // delivers -- the same sum the predecessor forms for its last step, up to rounding.  A
 // tile starts pass k+1 right after its own fix-up of pass k.  The stopping test is off
 // the critical path: each block publishes its residual maximum of pass k right after
-// its cells; the block holding the last tile of the last row (no tile depends on it)
-// merges them, records rho_k and publishes the decision; every block reads the
-// decision on pass k-1 only before its fix-up of pass k, the first write over iterate
-// k-1.  If it says stop, the decided iterate (k-1 or k) is still held.
+// its cells; block 0, the head of the first row and otherwise idle at that point,
+// merges them at its own fix-up of pass k+1, records rho_k and publishes the decision;
+// every block reads the decision on pass k-1 only before its fix-up of pass k, the
+// first write over iterate k-1.  If it says stop, the decided iterate (k-1 or k) is
+// still held.
 //
 // Why three copies suffice: a word of pass k is rewritten in pass k+3, by a tile past
 // its fix-up of pass k+2, so after the decision on pass k+1, which was merged after every
@@ -231,18 +232,23 @@ __device__ __forceinline__ int window_read(const uint64_t* __restrict__ slots, i
 //    every tile on the same CU in every pass they stay in that XCD's L2.
 //
 // LDS: Bh[3D] | X0[(TL+1) LD] | X1 (resident) | Xj (streaming with Jacobian reuse) |
-//      R[TL D] | Jd[TL D] | Sa, Sb[P D] | Agg[2 P D] | Din[D]          (P = 256 / D)
+//      R[D][TL+4] | Jd[D][TL+4] | Sa, Sb[P D] | Agg[2 P D] | Din[D]   (P = 256 / D;
+//      r and J channel-major, so that a lane's 4 or 16 consecutive steps are vectors)
 // Slots per tile and pass modulo 3: A[D] | b[D] | prefix[D]; then per tile (streaming) the
 // halo and the refresh-point halo of a reused Jacobian (D floats each).
 
-// Predecessor tiles read per thread in the look-back (the window is 256 / D times this);
-// D >= 32 reads fewer to stay within two waves' registers.
-__host__ __device__ constexpr int mfd_lookback_per_thread(int D, bool resident) { return D >= 32 ? 8 : 16; }
+// Look-back window: each thread reads mfd_lookback_chunks() chunks of
+// mfd_lookback_per_thread() predecessor tiles; the window is 256 / D times their product
+// (8 tiles for D = 64).  Measured on gru-shaped rows, short windows resolve sooner than
+// long ones: every poll of a long window waits for the slowest of many predecessors,
+// while a tile beyond a short window takes the published prefix of a nearer one.
+__host__ __device__ constexpr int mfd_lookback_per_thread(int D) { return D >= 32 ? 2 : 1; }
+__host__ __device__ constexpr int mfd_lookback_chunks(int D) { return 1; }
 
 __host__ __device__ inline size_t mfd_lds_floats(int D, int TL, int reuse, int resident) {
   const int LD = D + 4, P = PNR_BLOCK / D;
   const size_t xs = (size_t)(TL + 1) * LD;
-  return (size_t)3 * D + xs * (1 + (resident ? 1 : 0) + (reuse ? 1 : 0)) + (size_t)2 * TL * D +
+  return (size_t)3 * D + xs * (1 + (resident ? 1 : 0) + (reuse ? 1 : 0)) + (size_t)2 * D * (TL + 4) +
          (size_t)4 * P * D + D;
 }
 
@@ -275,24 +281,27 @@ __device__ __forceinline__ int wait_for(Ready ready, Ctrl* c) {
 }
 
 // Increment entering tile `seg` of its row (valid in threads tid < DM).  Thread
-// (group g, channel c) covers the predecessors at distances g*kLBPer+1 .. g*kLBPer+kLBPer
-// of a window of min(seg, G*kLBPer) tiles: it reads their aggregates (A, b), except the
-// farthest tile of the window, whose inclusive prefix it reads instead, and composes
-// them far to near; the groups' maps are then composed in LDS.  Returns the wait
-// status (0 ok) through `st`, block-uniform.
-template <int DM, int kLBPer>
+// (group g, channel c) covers a run of NCH * kLBPer consecutive predecessors of a window
+// of min(seg, G * NCH * kLBPer) tiles: it reads their aggregates (A, b) -- except the
+// farthest tile of the window, whose inclusive prefix it reads instead -- in NCH chunks,
+// far to near, and composes them; the groups' maps are then composed in LDS.  Returns
+// the wait status (0 ok) through `st`, block-uniform.
+template <int DM, int kLBPer, int NCH>
 __device__ __forceinline__ float lookback_regs(const uint64_t* __restrict__ slots, int tile, int seg, int km3,
                                                uint32_t ep, float* __restrict__ Agg, Ctrl* ctrl, int& st) {
-  constexpr int G = PNR_BLOCK / DM, SVP = 3 * DM;
+  constexpr int G = PNR_BLOCK / DM, SVP = 3 * DM, RUN = NCH * kLBPer;
   __shared__ int s_st;
   const int tid = threadIdx.x, c = tid % DM, grp = tid / DM;
-  const int Wn = min(seg, G * kLBPer);
-  const int w_lo = grp * kLBPer + 1, w_hi = min(Wn, w_lo + kLBPer - 1);
+  const int Wn = min(seg, G * RUN);
+  const int g_lo = grp * RUN + 1, g_hi = min(Wn, g_lo + RUN - 1);
   if (tid == 0) s_st = 0;
   float ga = 1.f, gb = 0.f;
   __syncthreads();
-  if (w_lo <= w_hi) {
+  for (int ch = NCH - 1; ch >= 0; --ch) {
+    const int w_lo = g_lo + ch * kLBPer, w_hi = min(g_hi, w_lo + kLBPer - 1);
+    if (w_lo > w_hi) continue;
     uint32_t spins = 0;
+    bool give_up = false;
     while (true) {
       // All loads first (addresses clamped into the window, so every one is valid and
       // none waits on another), then the tag checks: one memory round trip per poll.
@@ -329,16 +338,19 @@ __device__ __forceinline__ float lookback_regs(const uint64_t* __restrict__ slot
         const int w = has_fault(ctrl) ? 2 : ((load_dec(ctrl) & 1ull) ? 1 : 0);
         if (w) {
           atomicMax(&s_st, w);
+          give_up = true;
           break;
         }
       }
       if (spins > kSpinLimit) {
         record_fault(ctrl, 1);
         atomicMax(&s_st, 2);
+        give_up = true;
         break;
       }
       short_backoff(spins);
     }
+    if (give_up) break;
   }
   Agg[grp * 2 * DM + c] = ga;
   Agg[grp * 2 * DM + DM + c] = gb;
@@ -368,8 +380,9 @@ __global__ void __launch_bounds__(PNR_BLOCK, (RES && TL > 64) ? 1 : 2)
   float* Xb1 = Xb0 + XS;
   float* Xj = Xb1 + (RES ? XS : 0);
   float* R = Xj + (REUSE ? XS : 0);
-  float* Jd = R + TL * D;
-  float* Sa = Jd + TL * D;
+  constexpr int RLD = TL + 4;   // channel-major row length of R and Jd
+  float* Jd = R + D * RLD;
+  float* Sa = Jd + D * RLD;
   float* Sb = Sa + P * D;
   float* Agg = Sb + P * D;
   float* Din = Agg + 2 * P * D;
@@ -389,7 +402,7 @@ __global__ void __launch_bounds__(PNR_BLOCK, (RES && TL > 64) ? 1 : 2)
               bhn = a.bh ? a.bh[2 * D + c_mf] : 0.f;
   const int pp_ = tid / D, ci = tid - pp_ * D;   // scan layout: part, channel
   const int grid = (int)gridDim.x;
-  const bool merger = (a.n_tiles - 1) % grid == (int)blockIdx.x;
+  const bool merger = blockIdx.x == 0;
 
   // Gate inputs of step tb*16 + 4(lane/16) + i, channel c_mf, of a tile.
   auto load_gx = [&](float (&v)[4][3], int b, int t0, int Lv, int tb) {
@@ -424,7 +437,47 @@ __global__ void __launch_bounds__(PNR_BLOCK, (RES && TL > 64) ? 1 : 2)
     }
   };
 
-  int cur = -1, jac = -1;
+  // Block 0 -- the head of the first row, which otherwise idles at its gate -- merges
+  // the residual maxima of pass kk once every block has published its own, records
+  // rho_kk (finish_iteration) and publishes the decision.  Returns 0 (continue), 1 (stop)
+  // or 2 (fault).  Block-uniform.
+  auto merge = [&](int kk, int cur_kk) -> int {
+    const int m3 = kk % 3;
+    const uint32_t epk = (uint32_t)kk + 1u;
+    uint32_t mm = 0;
+    int wst = 0;
+    for (int i = tid; i < grid; i += PNR_BLOCK) {
+      const uint64_t* pw = a.partials + (size_t)m3 * grid + i;
+      uint64_t x = 0;
+      const int w = wait_for([&]() {
+        x = __hip_atomic_load(pw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return (uint32_t)(x >> 32) == epk;
+      }, ctrl);
+      if (w) wst = w;
+      mm = max(mm, (uint32_t)x);
+    }
+    mm = wave_max_u32(mm);
+    __syncthreads();
+    if (tid == 0) s_flag = 0;
+    __syncthreads();
+    if (lane == 0) s_wmax[wid] = mm;
+    if (wst) atomicMax(&s_flag, wst);
+    __syncthreads();
+    if (s_flag) return s_flag;
+    if (tid == 0) {
+      for (int w2 = 0; w2 < PNR_WAVES; ++w2) mm = max(mm, s_wmax[w2]);
+      finish_iteration(ctrl, a.rho_hist, bits_to_rho(mm), kk, cur_kk, a.max_iters, a.tol);
+      const int done = __hip_atomic_load(&ctrl->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      drain_memory_ops();   // rho, status and iters land before the decision word
+      __hip_atomic_store(&ctrl->dec, ((uint64_t)epk << 32) | (uint64_t)(done ? 1 : 0), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      s_flag = done ? 1 : 0;
+    }
+    __syncthreads();
+    return s_flag;
+  };
+
+  int cur = -1, prev = -1, jac = -1;
   __syncthreads();
   for (int k = 0; k <= a.max_iters; ++k) {
     const bool resid_only = k == a.max_iters;
@@ -448,16 +501,24 @@ __global__ void __launch_bounds__(PNR_BLOCK, (RES && TL > 64) ? 1 : 2)
       const int tile = b * a.tiles_per_row + seg;   // slot index: row-major
       const int t0 = seg * TL, Lv = min(TL, T - t0);
 
-      // ---- stage the iterate: rows 1..TL (own writes of the previous pass) and the halo ----
-      if (!RES || k == 0) stage_rows<TL>(Xc, Hcur, a.h0, b, t0, T, D, LD);
-      if (stale) stage_rows<TL>(Xj, Hjac, a.h0, b, t0, T, D, LD);
+      // ---- stage the iterate: rows 1..TL and the halo ----
+      // Thread (part, channel) loads exactly the rows its own fix-up stored in the pass
+      // before, so no other thread's global stores need to have landed.
+      auto stage_own = [&](float* X, const float* H) {
+#pragma unroll
+        for (int j = 0; j < LP; ++j) {
+          const int s2 = pp_ * LP + j;
+          X[(s2 + 1) * LD + ci] = (H && s2 < Lv) ? H[((size_t)b * T + t0 + s2) * D + ci] : 0.f;
+        }
+      };
+      if (!RES || k == 0) stage_own(Xc, RES ? nullptr : Hcur);
+      if (stale) stage_own(Xj, Hjac);
       if (tid == 0) s_flag = 0;
-      __syncthreads();
       // The halo (the state before the tile's first step) is the tile's own: it starts
       // at zero (the initial guess) and each fix-up adds the increment that enters the
       // tile, which the look-back delivers.  No tile waits for its predecessor's states.
       float* hal = reinterpret_cast<float*>(a.slots + (size_t)a.n_tiles * 3 * SVP) + (size_t)tile * 2 * D;
-      if (!RES && tid < D)
+      if ((!RES || k == 0) && tid < D)
         Xc[tid] = seg == 0 ? (a.h0 ? a.h0[(size_t)b * D + tid] : 0.f) : (k == 0 ? 0.f : hal[tid]);
       if (REUSE && tid < D) {
         // the halo of the refresh-point iterate, for the passes that reuse its Jacobian
@@ -478,10 +539,10 @@ __global__ void __launch_bounds__(PNR_BLOCK, (RES && TL > 64) ? 1 : 2)
           load_afrag<D>(Xj, LD, tb, fj);
           gates_frag<D>(fj, uf, accj);
         }
+        v4f rr, jj;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int s = tb * 16 + 4 * (lane >> 4) + i;
-          const int idx = s * D + c_mf;
           const bool ok = s < Lv;
           const float p = Xc[s * LD + c_mf];
           float r = sigm(gv[i][0] + acc[0][i] + bhr);
@@ -490,7 +551,7 @@ __global__ void __launch_bounds__(PNR_BLOCK, (RES && TL > 64) ? 1 : 2)
           float n = tanh_(fmaf(r, ghn, gv[i][2]));
           float res = fmaf(z, p - n, n) - Xc[(s + 1) * LD + c_mf];
           res = ok ? res : 0.f;
-          R[idx] = res;
+          rr[i] = res;
           tmax = max(tmax, abs_bits(res));
           float pj = p;
           if (stale) {
@@ -503,8 +564,11 @@ __global__ void __launch_bounds__(PNR_BLOCK, (RES && TL > 64) ? 1 : 2)
           const float omz = 1.f - z, cn = omz * (1.f - n * n);
           float jd = z + (pj - n) * z * omz * udg[1] + cn * ghn * r * (1.f - r) * udg[0] + cn * r * udg[2];
           jd = a.jac_mode == PNR_JAC_ZERO ? 0.f : jd;
-          Jd[idx] = ok ? jd : 1.f;
+          jj[i] = ok ? jd : 1.f;
         }
+        const int o = c_mf * RLD + tb * 16 + 4 * (lane >> 4);
+        *reinterpret_cast<v4f*>(R + o) = rr;
+        *reinterpret_cast<v4f*>(Jd + o) = jj;
       };
       // Software pipeline over the blocks of 16 steps: block u's MFMAs are issued
       // before block u-1's elementwise work, which does not depend on them.  The gate
@@ -545,62 +609,28 @@ __global__ void __launch_bounds__(PNR_BLOCK, (RES && TL > 64) ? 1 : 2)
           __hip_atomic_store(a.partials + (size_t)km3 * grid + blockIdx.x, ((uint64_t)ep << 32) | m,
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        if (merger) {
-          uint32_t mm = 0;
-          int wst = 0;
-          for (int i = tid; i < grid; i += PNR_BLOCK) {
-            const uint64_t* pw = a.partials + (size_t)km3 * grid + i;
-            uint64_t x = 0;
-            const int w = wait_for([&]() {
-              x = __hip_atomic_load(pw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              return (uint32_t)(x >> 32) == ep;
-            }, ctrl);
-            if (w) wst = w;
-            mm = max(mm, (uint32_t)x);
-          }
-          mm = wave_max_u32(mm);
-          __syncthreads();
-          if (lane == 0) s_wmax[wid] = mm;
-          if (wst) atomicMax(&s_flag, wst);
-          __syncthreads();
-          if (s_flag) {
-            stop = s_flag;
-            break;
-          }
-          if (tid == 0) {
-            for (int w2 = 0; w2 < PNR_WAVES; ++w2) mm = max(mm, s_wmax[w2]);
-            finish_iteration(ctrl, a.rho_hist, bits_to_rho(mm), k, cur, a.max_iters, a.tol);
-            const int done = __hip_atomic_load(&ctrl->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            drain_memory_ops();   // rho, status and iters land before the decision word
-            __hip_atomic_store(&ctrl->dec, ((uint64_t)ep << 32) | (uint64_t)(done ? 1 : 0), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-            s_flag = done ? 1 : 0;
-          }
-          __syncthreads();
-          if (s_flag) {   // this block just decided to stop
-            stop = s_flag;
-            break;
-          }
-        }
       }
 
       uint64_t* myslot = a.slots + ((size_t)tile * 3 + km3) * SVP;
       float ta = 1.f, tbv = 0.f;
       if (!resid_only) {
         // ---- scan inside the tile: part aggregates, tile total, publication ----
+        float jv[LP], rv[LP];   // this (part, channel)'s J and r: all loads first
+        const int po = ci * RLD + pp_ * LP;   // its steps, contiguous
+#pragma unroll
+        for (int j = 0; j < LP; j += 4) {
+          const v4f jq = *reinterpret_cast<const v4f*>(Jd + po + j), rq = *reinterpret_cast<const v4f*>(R + po + j);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            jv[j + e] = jq[e];
+            rv[j + e] = rq[e];
+          }
+        }
         float ea = 1.f, eb = 0.f;
-        {
-          float jv[LP], rv[LP];   // all loads of the part first, then the serial composition
 #pragma unroll
-          for (int j = 0; j < LP; ++j) {
-            jv[j] = Jd[(pp_ * LP + j) * D + ci];
-            rv[j] = R[(pp_ * LP + j) * D + ci];
-          }
-#pragma unroll
-          for (int j = 0; j < LP; ++j) {
-            eb = fmaf(jv[j], eb, rv[j]);
-            ea *= jv[j];
-          }
+        for (int j = 0; j < LP; ++j) {
+          eb = fmaf(jv[j], eb, rv[j]);
+          ea *= jv[j];
         }
         Sa[pp_ * D + ci] = ea;
         Sb[pp_ * D + ci] = eb;
@@ -617,11 +647,36 @@ __global__ void __launch_bounds__(PNR_BLOCK, (RES && TL > 64) ? 1 : 2)
             slot_put(myslot + D + tid, ep, tbv);
           }
         }
+        // Before the increment entering the tile (d_in) is known, write every step's
+        // increment as d_s = L_s + M_s d_in: L and M are the chain d -> J d + r started
+        // from the parts before this one, applied to (d_in = 0) and to the unit map.
+        // They replace r and J in place (each element is this thread's own), so the
+        // fix-up after the look-back is one independent FMA per element.
+        {
+          float ma = 1.f, lb = 0.f;
+          for (int q = 0; q < pp_; ++q) {
+            lb = fmaf(Sa[q * D + ci], lb, Sb[q * D + ci]);
+            ma *= Sa[q * D + ci];
+          }
+#pragma unroll
+          for (int j = 0; j < LP; j += 4) {
+            v4f lq, mq;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              lb = fmaf(jv[j + e], lb, rv[j + e]);
+              ma *= jv[j + e];
+              lq[e] = lb;
+              mq[e] = ma;
+            }
+            *reinterpret_cast<v4f*>(R + po + j) = lq;
+            *reinterpret_cast<v4f*>(Jd + po + j) = mq;
+          }
+        }
         // ---- decoupled look-back over the predecessors, in registers ----
         if (seg > 0) {
           int w = 0;
-          const float dl = lookback_regs<D, mfd_lookback_per_thread(DM, RES)>(a.slots, tile, seg, km3, ep, Agg,
-                                                                               ctrl, w);
+          const float dl = lookback_regs<D, mfd_lookback_per_thread(DM), mfd_lookback_chunks(DM)>(
+              a.slots, tile, seg, km3, ep, Agg, ctrl, w);
           if (w) {
             stop = w;
             break;
@@ -638,6 +693,14 @@ __global__ void __launch_bounds__(PNR_BLOCK, (RES && TL > 64) ? 1 : 2)
       if (resid_only) continue;
 
       // ---- the decision on pass k-1 guards the first overwrite of iterate k-1 ----
+      if (!dec_seen && merger) {
+        const int w = merge(k - 1, prev);
+        if (w) {
+          stop = w;
+          break;
+        }
+        dec_seen = true;
+      }
       if (!dec_seen) {
         if (tid == 0) {
           uint64_t d = 0;
@@ -655,32 +718,43 @@ __global__ void __launch_bounds__(PNR_BLOCK, (RES && TL > 64) ? 1 : 2)
         dec_seen = true;
       }
       __syncthreads();
-      // ---- fix-up: each (part, channel) walks its steps from its incoming increment ----
+      // ---- fix-up: s <- s + L + M d_in, element by element ----
       {
-        float dl = Din[ci];
-        for (int q = 0; q < pp_; ++q) dl = fmaf(Sa[q * D + ci], dl, Sb[q * D + ci]);
+        const float din = Din[ci];
         if (tid < D) {   // the next iterate's halo
           const float h = seg == 0 ? (a.h0 ? a.h0[(size_t)b * D + tid] : 0.f) : Xc[tid] + Din[tid];
           if (RES) Xn[tid] = h;
           else hal[tid] = h;
         }
-        float jv[LP], rv[LP];
+        float xv[LP], lv[LP], mv[LP];
+        const int po = ci * RLD + pp_ * LP;
 #pragma unroll
-        for (int j = 0; j < LP; ++j) {
-          jv[j] = Jd[(pp_ * LP + j) * D + ci];
-          rv[j] = R[(pp_ * LP + j) * D + ci];
+        for (int j = 0; j < LP; j += 4) {
+          const v4f lq = *reinterpret_cast<const v4f*>(R + po + j), mq = *reinterpret_cast<const v4f*>(Jd + po + j);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            lv[j + e] = lq[e];
+            mv[j + e] = mq[e];
+          }
         }
 #pragma unroll
+        for (int j = 0; j < LP; ++j) xv[j] = Xc[(pp_ * LP + j + 1) * LD + ci];
+        // (rows past the end of the sequence are written too in LDS, where they are never
+        // read as states; only real steps go to the state buffer)
+        float* hn = Hnext + ((size_t)b * T + t0 + pp_ * LP) * D + ci;
+#pragma unroll
         for (int j = 0; j < LP; ++j) {
-          const int s = pp_ * LP + j;
-          dl = fmaf(jv[j], dl, rv[j]);
-          if (s >= Lv) continue;
-          const float v = Xc[(s + 1) * LD + ci] + dl;
-          if (RES) Xn[(s + 1) * LD + ci] = v;
-          else Hnext[((size_t)b * T + t0 + s) * D + ci] = v;
+          const float v = xv[j] + fmaf(mv[j], din, lv[j]);
+          if (RES) Xn[(pp_ * LP + j + 1) * LD + ci] = v;
+          else if (pp_ * LP + j < Lv) hn[(size_t)j * D] = v;
         }
       }
       __syncthreads();
+    }
+    if (stop == 0 && resid_only && merger) {
+      // the last pass (no fix-up, so no gate): the decisions on passes M-1 and M
+      if (!dec_seen) stop = merge(k - 1, prev);
+      if (!stop) stop = merge(k, cur);
     }
     if (stop == 0 && resid_only) {
       // the last pass: wait for its (stopping) decision
@@ -695,6 +769,7 @@ __global__ void __launch_bounds__(PNR_BLOCK, (RES && TL > 64) ? 1 : 2)
       finish(k);
       return;
     }
+    prev = cur;
     cur = next;
     if (RES) {
       float* t = Xc;

@@ -271,8 +271,8 @@ def test_mfma_dense_paths_match_newton_oracle(D, mode, every, resident, monkeypa
 
 @pytest.mark.parametrize("resident", ["64", "128", "0"])
 def test_mfma_dense_diag_long_row_chains_lookback_windows(resident, monkeypatch):
-    """One batch row much longer than the look-back window of the D = 64 kernel (32
-    tiles): tiles beyond the window resolve from a predecessor's published prefix."""
+    """One batch row many times longer than the look-back window of the D = 64 kernel
+    (8 tiles): tiles beyond the window resolve from a predecessor's published prefix."""
     monkeypatch.setenv("PNR_DENSE_RESIDENT", resident)
     D, T = 64, 64 * 128 + 300
     p = WL.random_problem(WL.CELL_GRU, 1, T, D, 8, seed=11, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32,
