@@ -6,8 +6,8 @@
 //   C[z][i][j] = sum_k A[z][i][k] * Bm[z][j][k] + bias[i or j]      (fp32 or fp64 out)
 //
 // Both operands are K-contiguous.  bf16 inputs run on MFMA (v_mfma_f32_32x32x16_bf16,
-// fp32 accumulate); fp32/fp64 inputs use an LDS-tiled VALU kernel (the dense-GRU
-// projections are a few GFLOP).
+// fp32 accumulate), fp32 inputs on fp32 MFMA; fp64 inputs use an LDS-tiled VALU kernel
+// (the fp64 projections are tiny).
 #include "common.h"
 #include "kernels.h"
 
@@ -119,6 +119,100 @@ __global__ void __launch_bounds__(256) gemm_bf16_mfma(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------------
+// fp32 MFMA GEMM (v_mfma_f32_16x16x4f32, fp32 products and sums).  Block tile 64 x 64, K
+// step 32, 4 waves in 2 x 2, each 32 x 32 = 2 x 2 MFMA tiles.  In MFMA step kk the lane
+// group q = lane / 16 contributes k = 8q + kk for both operands, so a lane's operands of
+// one K step are 8 consecutive floats of one LDS row (two 16-byte reads).
+constexpr int GF_M = 64, GF_N = 64, GF_K = 32, GF_LD = GF_K + 4;
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__global__ void __launch_bounds__(256) gemm_f32_mfma(GemmArgs g) {
+  __shared__ __align__(16) float As[GF_M * GF_LD];
+  __shared__ __align__(16) float Bs[GF_N * GF_LD];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1, q = lane >> 4, r16 = lane & 15;
+  const int z = blockIdx.z;
+  const int i0 = blockIdx.y * GF_M, j0 = blockIdx.x * GF_N;
+  const float* A = reinterpret_cast<const float*>(g.A) + (size_t)z * g.sA;
+  const float* Bm = reinterpret_cast<const float*>(g.Bm) + (size_t)z * g.sB;
+  float* C = reinterpret_cast<float*>(g.C) + (size_t)z * g.sC;
+  const bool vec = (g.lda % 4) == 0 && (g.ldb % 4) == 0 && (g.sA % 4) == 0 && (g.sB % 4) == 0 &&
+                   ((uintptr_t)g.A % 16) == 0 && ((uintptr_t)g.Bm % 16) == 0;
+
+  // one operand row segment of 4 k values, zero outside the matrix
+  auto load4 = [&](const float* P, int ld, int rows, int r, int k) -> f32x4_t {
+    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+    if (r >= rows) return v;
+    const float* p = P + (size_t)r * ld + k;
+    if (vec && k + 3 < g.K) return *reinterpret_cast<const f32x4_t*>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (k + e < g.K) ? p[e] : 0.f;
+    return v;
+  };
+
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int k0 = 0; k0 < g.K; k0 += GF_K) {
+    f32x4_t va[2], vb[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = tid + 256 * h, r = e >> 3, kq = (e & 7) * 4;
+      va[h] = load4(A, g.lda, g.M, i0 + r, k0 + kq);
+      vb[h] = load4(Bm, g.ldb, g.N, j0 + r, k0 + kq);
+    }
+    __syncthreads();   // the previous step's reads are done
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = tid + 256 * h, r = e >> 3, kq = (e & 7) * 4;
+      *reinterpret_cast<f32x4_t*>(&As[r * GF_LD + kq]) = va[h];
+      *reinterpret_cast<f32x4_t*>(&Bs[r * GF_LD + kq]) = vb[h];
+    }
+    __syncthreads();
+    f32x4_t fa[2][2], fb[2][2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+      const float* pa = &As[(wm * 32 + mi * 16 + r16) * GF_LD + 8 * q];
+      fa[mi][0] = *reinterpret_cast<const f32x4_t*>(pa);
+      fa[mi][1] = *reinterpret_cast<const f32x4_t*>(pa + 4);
+    }
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+      const float* pb = &Bs[(wn * 32 + ni * 16 + r16) * GF_LD + 8 * q];
+      fb[ni][0] = *reinterpret_cast<const f32x4_t*>(pb);
+      fb[ni][1] = *reinterpret_cast<const f32x4_t*>(pb + 4);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[mi][kk >> 2][kk & 3], fb[ni][kk >> 2][kk & 3],
+                                                             acc[mi][ni], 0, 0, 0);
+  }
+
+  // epilogue: lane holds rows 4q + e, column r16 of each 16 x 16 tile
+  const float* bias = reinterpret_cast<const float*>(g.bias);
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+      const int j = j0 + wn * 32 + ni * 16 + r16;
+      if (j >= g.N) continue;
+      const float bj = (bias && !g.bias_on_i) ? bias[j] : 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = i0 + wm * 32 + mi * 16 + 4 * q + e;
+        if (i < g.M) C[(size_t)i * g.ldc + j] = acc[mi][ni][e] + bj + ((bias && g.bias_on_i) ? bias[i] : 0.f);
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------------
 // Generic LDS-tiled GEMM: 64 x 64 block tile, K step 16, 256 threads with 4 x 4 outputs.
 template <typename Tin> __device__ __forceinline__ float to_acc(Tin v, float) { return (float)v; }
 template <typename Tin> __device__ __forceinline__ double to_acc(Tin v, double) { return (double)v; }
@@ -182,7 +276,7 @@ hipError_t launch_gemm(int in_dtype, int out_dtype, const GemmArgs& g, hipStream
   if (in_dtype == PNR_BF16 && out_dtype == PNR_F32)
     hipLaunchKernelGGL((gemm_generic<__bf16, float>), grid, dim3(256), 0, st, g);
   else if (in_dtype == PNR_F32 && out_dtype == PNR_F32)
-    hipLaunchKernelGGL((gemm_generic<float, float>), grid, dim3(256), 0, st, g);
+    hipLaunchKernelGGL(gemm_f32_mfma, grid, dim3(256), 0, st, g);
   else if (in_dtype == PNR_F64 && out_dtype == PNR_F64)
     hipLaunchKernelGGL((gemm_generic<double, double>), grid, dim3(256), 0, st, g);
   else
