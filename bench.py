@@ -53,6 +53,14 @@ def src_hash(path):
     return h.hexdigest()[:16]
 
 
+def projection_fused(w, mode):
+    """True when the loop kernel computes the input projection itself (fp32 dense GRU with a
+    diagonal Jacobian on the MFMA kernel)."""
+    from nonlinear_rnn_evaluation_amd import workloads as WL
+    return (w.cell == WL.CELL_GRU and w.x_dtype == WL.DT_F32 and w.state_dtype == WL.DT_F32
+            and mode != WL.JAC_FULL and w.D in (16, 32, 64))
+
+
 def iteration_bytes(w, k, iters_total, resid=False):
     """Algorithmic HBM bytes of one fused iteration kernel launch that did work.
 
@@ -127,6 +135,10 @@ def run_workload(name, steps, warmup, mode=None, with_cpu=True, cpu_budget=12.0,
     passes = profs[-1]["passes"]
     resid_last = profs[-1]["resid_only"]
     bytes_call = sum(iteration_bytes(w, k, iters, resid=(resid_last and k == passes - 1)) for k in range(passes))
+    fused = projection_fused(w, mode)
+    if fused:
+        # the loop kernel also computes the projection: read x, write gx
+        bytes_call += w.B * w.T * (w.D_in + w.G * w.D) * 4
     achieved = bytes_call / (newton_ms * 1e-3) / 1e9 if newton_ms > 0 else 0.0
     kname, ksrc = newton_kernel(w, mode)
     traffic = None
@@ -144,7 +156,9 @@ def run_workload(name, steps, warmup, mode=None, with_cpu=True, cpu_budget=12.0,
     phases = {k: round(sum(pp[k] for pp in profs) / steps, 4)
               for k in ("total_ms", "proj_ms", "newton_ms", "out_ms")}
     proj_flops = 2.0 * w.B * w.T * w.D_in * w.G * w.D
-    phases["proj_tflops"] = round(proj_flops / (phases["proj_ms"] * 1e-3) / 1e12, 2) if phases["proj_ms"] else None
+    phases["proj_tflops"] = (round(proj_flops / (phases["proj_ms"] * 1e-3) / 1e12, 2)
+                             if phases["proj_ms"] and not fused else None)
+    phases["projection"] = "inside the loop kernel" if fused else "GEMM kernel"
 
     rec = {"workload": name, "status": int(status), "iters": int(iters), "ms_per_step": round(ms, 4),
            "value": (w.B * w.T) / (ms * 1e-3) if status == 0 else None,

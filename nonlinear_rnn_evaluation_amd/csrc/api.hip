@@ -2,12 +2,12 @@
 //
 // pnr_eval validates its arguments without touching HIP, carves the caller's workspace,
 // then enqueues on the caller's stream:
-//   init -> input projection GEMM -> max_iters fused Newton iterations -> one
-//   residual-only pass -> output layout conversion -> one control read-back.
-// Every iteration kernel reads the device control block first and returns at once
-// when an earlier iteration has already decided, so the host never waits between
-// iterations (ParaRNN overview page, "Technical Implementation": Newton iterations
-// with a residual check; the check runs on the device).
+//   init -> input projection (a GEMM, or inside the loop kernel for the quasi-Newton
+//   dense GRU) -> one persistent launch running every Newton iteration -> output layout
+//   conversion (unless the loop kernel wrote h_out) -> one control read-back.
+// The loop decides on the device when to stop, so the host never waits between
+// iterations (ParaRNN overview page, "Technical Implementation": Newton iterations with
+// a residual check).
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -269,8 +269,12 @@ int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, cons
     // gx[(b,t)][m] = sum_k x[(b,t)][k] W[m][k] + b_x[m]
     g = GemmArgs{x, params->W, params->b_x, gx, B * T, G * D, Din, 0, 0, 0, Din, Din, G * D, 1, 0};
   }
+  // The quasi-Newton dense GRU kernel (fp32 inputs) computes its tiles' projection itself,
+  // saving a launch and a round trip of gx through the queue.
+  const bool fused_proj = kind == PNR_CELL_GRU && cell->x_dtype == PNR_F32 && cell->state_dtype == PNR_F32 &&
+                          !l.dense_full && dense_mfma_supported(D, 0, 0);
   Mark m_proj = mark_begin(st);
-  PNR_HIP(launch_gemm(cell->x_dtype, cell->state_dtype, g, st));
+  if (!fused_proj) PNR_HIP(launch_gemm(cell->x_dtype, cell->state_dtype, g, st));
   mark_end(m_proj, st);
 
   // ---- the Newton loop: one persistent launch; the device decides when to stop ----
@@ -314,6 +318,13 @@ int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, cons
     a.B = B; a.D = D; a.T = T; a.L = l.L;
     a.tiles_per_row = l.tiles_per_row; a.n_tiles = l.n_tiles;
     a.max_iters = max_iters; a.jac_every = cell->jac_every; a.jac_mode = jac_mode; a.tol = tol;
+    if (fused_proj) {
+      a.x = static_cast<const float*>(x);
+      a.W = static_cast<const float*>(params->W);
+      a.bx = static_cast<const float*>(params->b_x);
+      a.gx_out = static_cast<float*>(gx);
+      a.D_in = Din;
+    }
     // resident variant: the loop kernel writes the returned iterate to h_out itself.  Its
     // tiles are at least as long as the layout's, so the slot region suffices.
     const int rtl = dense_mfma_resident_tile(D, l.dense_full, B, T, cell->jac_every > 1, num_cu);
@@ -365,14 +376,23 @@ int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, cons
 
   // ---- the one device -> host crossing of the call ----
   // control block and residual history are adjacent in the workspace: one copy
-  static thread_local std::vector<char> rb;
+  // into a pinned, thread-local buffer (allocated once, grown rarely, kept for the life
+  // of the thread) so the copy is a plain DMA on the stream
+  static thread_local char* rb = nullptr;
+  static thread_local size_t rb_cap = 0;
   const size_t rb_bytes = (l.hist - l.ctrl) + sizeof(double) * (max_iters + 1);
-  if (rb.size() < rb_bytes) rb.resize(rb_bytes);
-  PNR_HIP(hipMemcpyAsync(rb.data(), ws + l.ctrl, rb_bytes, hipMemcpyDeviceToHost, st));
+  if (rb_cap < rb_bytes) {
+    if (rb) (void)hipHostFree(rb);
+    rb = nullptr;
+    rb_cap = 0;
+    PNR_HIP(hipHostMalloc(reinterpret_cast<void**>(&rb), rb_bytes, hipHostMallocDefault));
+    rb_cap = rb_bytes;
+  }
+  PNR_HIP(hipMemcpyAsync(rb, ws + l.ctrl, rb_bytes, hipMemcpyDeviceToHost, st));
   PNR_HIP(hipStreamSynchronize(st));
   Ctrl hc;
-  memcpy(&hc, rb.data(), sizeof(Ctrl));
-  const double* hh = reinterpret_cast<const double*>(rb.data() + (l.hist - l.ctrl));
+  memcpy(&hc, rb, sizeof(Ctrl));
+  const double* hh = reinterpret_cast<const double*>(rb + (l.hist - l.ctrl));
   if (hc.fault)
     return fail(PNR_E_HIP, "device loop gave up waiting (%s); results are not valid",
                 hc.fault == 1 ? "look-back" : "grid barrier");

@@ -737,13 +737,7 @@ size_t dense_lds_bytes(int D, int full, int is_f64, int reuse) {
 
 template <typename Tt, int DM, bool FULL, bool MF>
 static int dense_capacity_t(int num_cu, size_t lds) {
-  auto fn = dense_newton_kernel<Tt, DM, FULL, MF>;
-  if (lds > 65536) {
-    if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return 0;
-  }
-  int v = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, fn, PNR_BLOCK, lds) != hipSuccess) return 0;
+  const int v = cached_occupancy((const void*)dense_newton_kernel<Tt, DM, FULL, MF>, lds);
   long g = (long)v * num_cu;
   return (int)(g > kMaxGrid ? kMaxGrid : g);
 }

@@ -362,6 +362,79 @@ __device__ __forceinline__ float lookback_regs(const uint64_t* __restrict__ slot
   return din;
 }
 
+// Input projection of one tile inside the loop kernel (fp32 inputs):
+//   gx[b][t0 + s][m] = sum_k x[b][t0 + s][k] W[m][k] + b_x[m],   s < Lv, m < 3D.
+// The tile's inputs are staged in LDS in chunks of 64 k (zero-padded); wave w owns the
+// column blocks w, w+4, ... of 16 output columns and every row block of 16 steps, on
+// v_mfma_f32_16x16x4f32 with the k split of load_afrag (lane group q takes k = 16q + kk),
+// its W fragments read straight from global memory (W is small and stays in L2).  Each
+// tile's gate inputs are read later only by the block that owns the tile.
+template <int DM, int TL>
+__device__ __forceinline__ void project_tile(const DenseLoopArgs<float>& a, float* __restrict__ Xs, int b, int t0,
+                                             int Lv) {
+  constexpr int N = 3 * DM, NCB = N / 16, MCB = (NCB + PNR_WAVES - 1) / PNR_WAVES, RB = TL / 16, XLD = 68;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, q = lane >> 4, r16 = lane & 15;
+  const int K = a.D_in, T = a.T;
+  const bool wvec = (K % 4) == 0 && ((uintptr_t)a.W % 16) == 0;
+  v4f acc[MCB][RB];
+#pragma unroll
+  for (int c = 0; c < MCB; ++c)
+#pragma unroll
+    for (int r = 0; r < RB; ++r) acc[c][r] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int kc = 0; kc < K; kc += 64) {
+    __syncthreads();   // the previous chunk's reads are done
+    for (int e = tid; e < TL * 64; e += PNR_BLOCK) {
+      const int s = e >> 6, k = e & 63;
+      Xs[s * XLD + k] = (s < Lv && kc + k < K) ? a.x[((size_t)b * T + t0 + s) * K + kc + k] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < MCB; ++c) {
+      const int cbk = wid + c * PNR_WAVES;
+      if (cbk >= NCB) break;
+      // W fragment: column n, k = kc + 16q + kk
+      const int n = cbk * 16 + r16, k0 = kc + 16 * q;
+      float bf[16];
+      const float* wp = a.W + (size_t)n * K + k0;
+      if (wvec && k0 + 15 < K) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const v4f v = *reinterpret_cast<const v4f*>(wp + 4 * j);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bf[4 * j + e] = v[e];
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) bf[j] = k0 + j < K ? wp[j] : 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        v4f af[4];
+        const v4f* ap = reinterpret_cast<const v4f*>(Xs + (r * 16 + r16) * XLD + 16 * q);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) af[j] = ap[j];
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) acc[c][r] = mfma4(af[kk >> 2][kk & 3], bf[kk], acc[c][r]);
+      }
+    }
+  }
+  // lane holds rows 4q + e, column r16 of each 16 x 16 tile
+#pragma unroll
+  for (int c = 0; c < MCB; ++c) {
+    const int cbk = wid + c * PNR_WAVES;
+    if (cbk >= NCB) break;
+    const int m = cbk * 16 + r16;
+    const float bias = a.bx ? a.bx[m] : 0.f;
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s = r * 16 + 4 * q + e;
+        if (s < Lv) a.gx_out[((size_t)b * T + t0 + s) * N + m] = acc[c][r][e] + bias;
+      }
+  }
+}
+
 template <int DM, int TL, bool RES, bool REUSE>
 __global__ void __launch_bounds__(PNR_BLOCK, (RES && TL > 64) ? 1 : 2)
     dense_diag_mfma_kernel(DenseLoopArgs<float> a) {
@@ -387,6 +460,16 @@ __global__ void __launch_bounds__(PNR_BLOCK, (RES && TL > 64) ? 1 : 2)
   float* Agg = Sb + P * D;
   float* Din = Agg + 2 * P * D;
 
+  if (a.x) {
+    // the input projection of this block's tiles (see project_tile); every wave drains
+    // its stores before the barrier, so the loop below may read any of them
+    for (int item = blockIdx.x; item < a.n_tiles; item += gridDim.x) {
+      const int seg = item / a.B, b = item - seg * a.B;
+      project_tile<D, TL>(a, lds, b, seg * TL, min(TL, T - seg * TL));
+    }
+    drain_memory_ops();
+    __syncthreads();
+  }
   for (int i = tid; i < 3 * D; i += PNR_BLOCK) Bh[i] = a.bh ? a.bh[i] : 0.f;
   // this wave's U fragments (recurrent product) and the diagonal of each gate block
   const int cb = wid % NCB, tb0 = wid / NCB;
@@ -1114,13 +1197,7 @@ int dense_mfma_supported(int D, int full, int is_f64) {
 int dense_mfma_tile_len() { return kTL; }
 int dense_mfma_slot_words(int D, int full) { return full ? kFSlot : 10 * D; }
 
-static int block_occupancy(const void* fn, size_t lds) {
-  if (lds > 65536 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-    return 0;
-  int v = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, fn, PNR_BLOCK, lds) != hipSuccess) return 0;
-  return v;
-}
+static int block_occupancy(const void* fn, size_t lds) { return cached_occupancy(fn, lds); }
 
 // Cooperative launch of a persistent loop kernel: at most the co-resident grid, at most
 // one block per tile.
@@ -1173,6 +1250,7 @@ hipError_t launch_dense_mfma(const DenseLoopArgs<float>& a, int full, int num_cu
   if (!res && a.L != kTL) return hipErrorInvalidValue;
   const void* fn = diag_kernel_for(a.D, res ? a.L : 0, dreuse);
   const size_t lds = mfd_lds_floats(a.D, a.L, dreuse, res) * 4;
+  if (a.x && lds < (size_t)a.L * 68 * 4) return hipErrorInvalidValue;   // room to stage the projection
   // the resident variant needs one co-resident block per tile
   if (res && (long)block_occupancy(fn, lds) * num_cu < a.n_tiles) return hipErrorInvalidValue;
   return coop_launch(fn, a, lds, num_cu, st);

@@ -8,6 +8,11 @@ namespace pnr {
 // Upper bound on the grid of any persistent iteration kernel (sizes the partials array).
 constexpr int kMaxGrid = 16384;
 
+// Resident blocks of `fn` per CU with `lds` bytes of dynamic LDS (raising the kernel's
+// LDS limit first when needed), 0 when it cannot run.  Cached per (kernel, LDS size):
+// the runtime queries cost tens of microseconds per call.
+int cached_occupancy(const void* fn, size_t lds);
+
 // ---------------------------------------------------------------------------------
 // Decision taken by the block that merges the residual partials of iteration k (the
 // "final block" of the two-level reduction): record rho_k and stop when it is within
@@ -67,6 +72,13 @@ hipError_t launch_diag_newton(int cell, const DiagLoopArgs& a, int grid, hipStre
 template <typename Tt>
 struct DenseLoopArgs {
   const Tt* gx;        // [B][T][3D]
+  // When x is set, the loop kernel computes gx itself (writing gx_out == gx) from
+  // x [B][T][D_in], W [3D][D_in] and bx [3D] (or nullptr) before its first pass.
+  const Tt* x;
+  const Tt* W;
+  const Tt* bx;
+  Tt* gx_out;
+  int D_in;
   const Tt* U;         // [3D][D]
   const Tt* bh;        // [3D] or nullptr
   const Tt* h0;        // [B][D] or nullptr

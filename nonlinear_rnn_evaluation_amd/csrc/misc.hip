@@ -1,10 +1,29 @@
 // Small kernels around the Newton loop: per-call initialisation of the control block
 // and look-back slots, and the conversion of the returned iterate to the caller's
 // [B, T, S] layout.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace pnr {
+
+int cached_occupancy(const void* fn, size_t lds) {
+  struct Entry { const void* fn; size_t lds; int dev, v; };
+  static Entry cache[64];
+  static int n = 0;
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < n; ++i)
+    if (cache[i].fn == fn && cache[i].lds == lds && cache[i].dev == dev) return cache[i].v;
+  int v = 0;
+  if (lds <= 65536 || hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, fn, PNR_BLOCK, lds) != hipSuccess) v = 0;
+  if (n < 64) cache[n++] = Entry{fn, lds, dev, v};
+  return v;
+}
 
 __global__ void init_kernel(Ctrl* ctrl, uint64_t* slots, size_t n, uint64_t* partials, size_t np) {
   const size_t i0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
