@@ -303,7 +303,15 @@ int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, cons
     // grid; otherwise rows are cut into tiles linked by the decoupled look-back.
     a.walk = walk_mode(a.n_rows, cap);
     const int items = a.walk ? a.n_rows : a.n_tiles;
-    const int grid = items < cap ? items : cap;
+    int grid = items < cap ? items : cap;
+    // a walking grid takes the largest divisor of the row count above half the capacity,
+    // so that every block walks the same number of rows
+    if (a.walk && items > cap)
+      for (int g = cap; 2 * g > cap; --g)
+        if (items % g == 0) {
+          grid = g;
+          break;
+        }
     PNR_HIP(launch_diag_newton(kind, a, grid, st));
   } else if (cell->state_dtype == PNR_F32) {
     DenseLoopArgs<float> a{};

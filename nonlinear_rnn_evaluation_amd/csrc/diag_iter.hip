@@ -313,22 +313,29 @@ __device__ __forceinline__ typename DeltaOf<typename DiagCell<CELL>::E>::T diag_
     float h[N], pj[N];
     if (v.cur_zero) { for (int i = 0; i < N; ++i) h[i] = 0.f; }
     else load_n(v.Hcur + roff, tb, T, vec, N, h);
-    // the state before a tile's first step was written by the block owning the
-    // previous tile: read it coherently (everything else here is this block's own)
+    // The state before a thread's first step is the previous lane's last one (DPP);
+    // only lane 0 of each wave loads it.  Before a tile's first step it was written by
+    // the block owning the previous tile: read it coherently (everything else here is
+    // this block's own).
     const bool halo_other = tid == 0 && !walk;
-    float p0;
-    if (tb == 0) p0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
-    else if (v.cur_zero || tb > T) p0 = 0.f;
-    else p0 = halo_other ? coherent_load(v.Hcur + roff + tb - 1) : v.Hcur[roff + tb - 1];
+    float p0 = 0.f;
+    if (lane == 0) {
+      if (tb == 0) p0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
+      else if (v.cur_zero || tb > T) p0 = 0.f;
+      else p0 = halo_other ? coherent_load(v.Hcur + roff + tb - 1) : v.Hcur[roff + tb - 1];
+    }
+    p0 = wave_shr1(h[N - 1], p0);
     if (stale) {
-      float pj0;
-      if (tb == 0) pj0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
-      else if (v.jac_zero || tb > T) pj0 = 0.f;
-      else pj0 = halo_other ? coherent_load(v.Hjac + roff + tb - 1) : v.Hjac[roff + tb - 1];
       float hj[N];
       if (v.jac_zero) { for (int i = 0; i < N; ++i) hj[i] = 0.f; }
       else load_n(v.Hjac + roff, tb, T, vec, N, hj);
-      pj[0] = pj0;
+      float pj0 = 0.f;
+      if (lane == 0) {
+        if (tb == 0) pj0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
+        else if (v.jac_zero || tb > T) pj0 = 0.f;
+        else pj0 = halo_other ? coherent_load(v.Hjac + roff + tb - 1) : v.Hjac[roff + tb - 1];
+      }
+      pj[0] = wave_shr1(hj[N - 1], pj0);
       for (int i = 1; i < N; ++i) pj[i] = hj[i - 1];
     }
 #pragma unroll
@@ -349,31 +356,39 @@ __device__ __forceinline__ typename DeltaOf<typename DiagCell<CELL>::E>::T diag_
     if (v.cur_zero) { for (int i = 0; i < N; ++i) { c[i] = 0.f; h[i] = 0.f; } }
     else { load_n(v.Hcur + coff, tb, T, vec, N, c); load_n(v.Hcur + hoff, tb, T, vec, N, h); }
     const bool halo_other = tid == 0 && !walk;   // see the GRU branch
-    float cp0, hp0;
-    if (tb == 0) {
-      cp0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
-      hp0 = a.h0 ? a.h0[(size_t)b * S + D + d] : 0.f;
-    } else if (v.cur_zero || tb > T) {
-      cp0 = 0.f; hp0 = 0.f;
-    } else if (halo_other) {
-      cp0 = coherent_load(v.Hcur + coff + tb - 1); hp0 = coherent_load(v.Hcur + hoff + tb - 1);
-    } else {
-      cp0 = v.Hcur[coff + tb - 1]; hp0 = v.Hcur[hoff + tb - 1];
+    float cp0 = 0.f, hp0 = 0.f;
+    if (lane == 0) {
+      if (tb == 0) {
+        cp0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
+        hp0 = a.h0 ? a.h0[(size_t)b * S + D + d] : 0.f;
+      } else if (v.cur_zero || tb > T) {
+        cp0 = 0.f; hp0 = 0.f;
+      } else if (halo_other) {
+        cp0 = coherent_load(v.Hcur + coff + tb - 1); hp0 = coherent_load(v.Hcur + hoff + tb - 1);
+      } else {
+        cp0 = v.Hcur[coff + tb - 1]; hp0 = v.Hcur[hoff + tb - 1];
+      }
     }
+    cp0 = wave_shr1(c[N - 1], cp0);
+    hp0 = wave_shr1(h[N - 1], hp0);
     float cj[N], hj[N], cpj0 = 0.f, hpj0 = 0.f;
     if (stale) {
-      if (tb == 0) {
-        cpj0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
-        hpj0 = a.h0 ? a.h0[(size_t)b * S + D + d] : 0.f;
-      } else if (!(v.jac_zero || tb > T)) {
-        if (halo_other) {
-          cpj0 = coherent_load(v.Hjac + coff + tb - 1); hpj0 = coherent_load(v.Hjac + hoff + tb - 1);
-        } else {
-          cpj0 = v.Hjac[coff + tb - 1]; hpj0 = v.Hjac[hoff + tb - 1];
-        }
-      }
       if (v.jac_zero) { for (int i = 0; i < N; ++i) { cj[i] = 0.f; hj[i] = 0.f; } }
       else { load_n(v.Hjac + coff, tb, T, vec, N, cj); load_n(v.Hjac + hoff, tb, T, vec, N, hj); }
+      if (lane == 0) {
+        if (tb == 0) {
+          cpj0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
+          hpj0 = a.h0 ? a.h0[(size_t)b * S + D + d] : 0.f;
+        } else if (!(v.jac_zero || tb > T)) {
+          if (halo_other) {
+            cpj0 = coherent_load(v.Hjac + coff + tb - 1); hpj0 = coherent_load(v.Hjac + hoff + tb - 1);
+          } else {
+            cpj0 = v.Hjac[coff + tb - 1]; hpj0 = v.Hjac[hoff + tb - 1];
+          }
+        }
+      }
+      cpj0 = wave_shr1(cj[N - 1], cpj0);
+      hpj0 = wave_shr1(hj[N - 1], hpj0);
     }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
@@ -474,8 +489,10 @@ __device__ __forceinline__ int pick_next(int cur, int jac, int nbuf) {
 // The state buffers rotate exactly as the host would rotate them: the next iterate goes
 // to a buffer holding neither the current iterate nor the state the Jacobian is taken at.
 // Registers capped at 128 VGPRs (four waves per SIMD) to keep enough loads in flight.
+template <int CELL> constexpr int diag_min_waves() { return 4; }
+
 template <int CELL, int N>
-__global__ void __launch_bounds__(PNR_BLOCK, 4) diag_newton_kernel(DiagLoopArgs a) {
+__global__ void __launch_bounds__(PNR_BLOCK, diag_min_waves<CELL>()) diag_newton_kernel(DiagLoopArgs a) {
   using C = DiagCell<CELL>;
   using E = typename C::E;
   using Dl = typename DeltaOf<E>::T;
@@ -622,9 +639,11 @@ __global__ void __launch_bounds__(PNR_BLOCK) scan_kernel(ScanArgs a) {
   }
 }
 
-constexpr int kDiagN = 8;   // consecutive steps per thread (two float4 per state row)
+// consecutive steps per thread in the fused loop kernel (float4 loads per state row)
+template <int CELL> constexpr int diag_n() { return CELL == PNR_CELL_LSTM_DIAG ? 4 : 8; }
+constexpr int kScanN = 8;
 
-int scan_default_tile(int) { return PNR_BLOCK * kDiagN; }
+int scan_default_tile(int) { return PNR_BLOCK * kScanN; }
 int scan_slot_words(int kind) { return diag_slot_words(kind == 1 ? PNR_CELL_GRU_DIAG : PNR_CELL_LSTM_DIAG); }
 
 template <int KIND, int N>
@@ -659,7 +678,9 @@ hipError_t launch_scan(int kind, int R, int T, const float* A, const float* b, f
 }
 
 // ---------------------------------------------------------------------------------
-int diag_items_per_thread(int) { return kDiagN; }
+int diag_items_per_thread(int cell) {
+  return cell == PNR_CELL_LSTM_DIAG ? diag_n<PNR_CELL_LSTM_DIAG>() : diag_n<PNR_CELL_GRU_DIAG>();
+}
 int diag_slot_words(int cell) {
   return cell == PNR_CELL_LSTM_DIAG ? DiagCell<PNR_CELL_LSTM_DIAG>::AGG_WORDS + DiagCell<PNR_CELL_LSTM_DIAG>::PRE_WORDS
                                     : DiagCell<PNR_CELL_GRU_DIAG>::AGG_WORDS + DiagCell<PNR_CELL_GRU_DIAG>::PRE_WORDS;
@@ -670,7 +691,7 @@ static int diag_capacity(int num_cu) {
   static int per_cu = 0;
   if (per_cu == 0) {
     int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, diag_newton_kernel<CELL, kDiagN>, PNR_BLOCK, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, diag_newton_kernel<CELL, diag_n<CELL>()>, PNR_BLOCK, 0) !=
             hipSuccess || v < 1)
       v = 1;
     per_cu = v;
@@ -686,8 +707,8 @@ int diag_grid_capacity(int cell, int num_cu) {
 
 hipError_t launch_diag_newton(int cell, const DiagLoopArgs& a, int grid, hipStream_t st) {
   void* args[] = {const_cast<DiagLoopArgs*>(&a)};
-  const void* fn = cell == PNR_CELL_GRU_DIAG ? (const void*)diag_newton_kernel<PNR_CELL_GRU_DIAG, kDiagN>
-                                             : (const void*)diag_newton_kernel<PNR_CELL_LSTM_DIAG, kDiagN>;
+  const void* fn = cell == PNR_CELL_GRU_DIAG ? (const void*)diag_newton_kernel<PNR_CELL_GRU_DIAG, diag_n<PNR_CELL_GRU_DIAG>()>
+                                             : (const void*)diag_newton_kernel<PNR_CELL_LSTM_DIAG, diag_n<PNR_CELL_LSTM_DIAG>()>;
   return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(PNR_BLOCK), args, 0, st);
 }
 
