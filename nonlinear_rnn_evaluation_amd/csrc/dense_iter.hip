@@ -750,8 +750,7 @@ static hipError_t launch_t(const DenseLoopArgs<Tt>& a, int num_cu, hipStream_t s
   int grid = a.n_tiles < cap ? a.n_tiles : cap;
   if (grid < 1) grid = 1;
   void* args[] = {const_cast<DenseLoopArgs<Tt>*>(&a)};
-  return hipLaunchCooperativeKernel((const void*)dense_newton_kernel<Tt, DM, FULL, MF>, dim3(grid),
-                                    dim3(PNR_BLOCK), args, (unsigned)lds, st);
+  return launch_persistent((const void*)dense_newton_kernel<Tt, DM, FULL, MF>, grid, lds, args, st);
 }
 
 template <typename Tt>

@@ -367,46 +367,70 @@ __device__ __forceinline__ float lookback_regs(const uint64_t* __restrict__ slot
 // The tile's inputs are staged in LDS in chunks of 64 k (zero-padded); wave w owns the
 // column blocks w, w+4, ... of 16 output columns and every row block of 16 steps, on
 // v_mfma_f32_16x16x4f32 with the k split of load_afrag (lane group q takes k = 16q + kk),
-// its W fragments read straight from global memory (W is small and stays in L2).  Each
-// tile's gate inputs are read later only by the block that owns the tile.
+// its W fragments read straight from global memory (W is small and stays in L2).  All
+// loads of a chunk (the x rows as float4s, every W fragment of the wave) are issued
+// before the first one is used, so the chunk costs one memory round trip.  Each tile's
+// gate inputs are read later only by the block that owns the tile.
 template <int DM, int TL>
 __device__ __forceinline__ void project_tile(const DenseLoopArgs<float>& a, float* __restrict__ Xs, int b, int t0,
                                              int Lv) {
   constexpr int N = 3 * DM, NCB = N / 16, MCB = (NCB + PNR_WAVES - 1) / PNR_WAVES, RB = TL / 16, XLD = 68;
+  constexpr int XV = TL * 16 / PNR_BLOCK;   // float4s of x per thread and chunk
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, q = lane >> 4, r16 = lane & 15;
   const int K = a.D_in, T = a.T;
   const bool wvec = (K % 4) == 0 && ((uintptr_t)a.W % 16) == 0;
+  const bool xvec = (K % 4) == 0 && ((uintptr_t)a.x % 16) == 0;
   v4f acc[MCB][RB];
 #pragma unroll
   for (int c = 0; c < MCB; ++c)
 #pragma unroll
     for (int r = 0; r < RB; ++r) acc[c][r] = v4f{0.f, 0.f, 0.f, 0.f};
   for (int kc = 0; kc < K; kc += 64) {
-    __syncthreads();   // the previous chunk's reads are done
-    for (int e = tid; e < TL * 64; e += PNR_BLOCK) {
-      const int s = e >> 6, k = e & 63;
-      Xs[s * XLD + k] = (s < Lv && kc + k < K) ? a.x[((size_t)b * T + t0 + s) * K + kc + k] : 0.f;
+    // ---- issue every load of the chunk ----
+    v4f xv[XV];
+#pragma unroll
+    for (int j = 0; j < XV; ++j) {
+      const int e = tid + j * PNR_BLOCK, srow = e >> 4, k = kc + 4 * (e & 15);
+      const float* xp = a.x + ((size_t)b * T + t0 + srow) * K + k;
+      if (srow >= Lv) {
+        xv[j] = v4f{0.f, 0.f, 0.f, 0.f};
+      } else if (xvec && k + 3 < K) {
+        xv[j] = *reinterpret_cast<const v4f*>(xp);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xv[j][i] = k + i < K ? xp[i] : 0.f;
+      }
     }
-    __syncthreads();
+    float bf[MCB][16];
 #pragma unroll
     for (int c = 0; c < MCB; ++c) {
       const int cbk = wid + c * PNR_WAVES;
-      if (cbk >= NCB) break;
       // W fragment: column n, k = kc + 16q + kk
-      const int n = cbk * 16 + r16, k0 = kc + 16 * q;
-      float bf[16];
+      const int n = (cbk < NCB ? cbk : 0) * 16 + r16, k0 = kc + 16 * q;
       const float* wp = a.W + (size_t)n * K + k0;
       if (wvec && k0 + 15 < K) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const v4f v = *reinterpret_cast<const v4f*>(wp + 4 * j);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) bf[4 * j + e] = v[e];
+          for (int e = 0; e < 4; ++e) bf[c][4 * j + e] = v[e];
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) bf[j] = k0 + j < K ? wp[j] : 0.f;
+        for (int j = 0; j < 16; ++j) bf[c][j] = k0 + j < K ? wp[j] : 0.f;
       }
+    }
+    __syncthreads();   // the previous chunk's reads are done
+#pragma unroll
+    for (int j = 0; j < XV; ++j) {
+      const int e = tid + j * PNR_BLOCK;
+      *reinterpret_cast<v4f*>(Xs + (e >> 4) * XLD + 4 * (e & 15)) = xv[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < MCB; ++c) {
+      const int cbk = wid + c * PNR_WAVES;
+      if (cbk >= NCB) break;
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
         v4f af[4];
@@ -414,7 +438,7 @@ __device__ __forceinline__ void project_tile(const DenseLoopArgs<float>& a, floa
 #pragma unroll
         for (int j = 0; j < 4; ++j) af[j] = ap[j];
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) acc[c][r] = mfma4(af[kk >> 2][kk & 3], bf[kk], acc[c][r]);
+        for (int kk = 0; kk < 16; ++kk) acc[c][r] = mfma4(af[kk >> 2][kk & 3], bf[c][kk], acc[c][r]);
       }
     }
   }
@@ -1199,9 +1223,9 @@ int dense_mfma_slot_words(int D, int full) { return full ? kFSlot : 10 * D; }
 
 static int block_occupancy(const void* fn, size_t lds) { return cached_occupancy(fn, lds); }
 
-// Cooperative launch of a persistent loop kernel: at most the co-resident grid, at most
-// one block per tile.
-static hipError_t coop_launch(const void* fn, const DenseLoopArgs<float>& a, size_t lds, int num_cu, hipStream_t st) {
+// Launch of a persistent loop kernel: at most the co-resident grid, at most one block
+// per tile.
+static hipError_t persistent_launch(const void* fn, const DenseLoopArgs<float>& a, size_t lds, int num_cu, hipStream_t st) {
   const int v = block_occupancy(fn, lds);
   if (v < 1) return hipErrorInvalidConfiguration;
   long g = (long)v * num_cu;
@@ -1209,7 +1233,7 @@ static hipError_t coop_launch(const void* fn, const DenseLoopArgs<float>& a, siz
   if (g > a.n_tiles) g = a.n_tiles;
   if (g < 1) g = 1;
   void* args[] = {const_cast<DenseLoopArgs<float>*>(&a)};
-  return hipLaunchCooperativeKernel(fn, dim3((int)g), dim3(PNR_BLOCK), args, (unsigned)lds, st);
+  return launch_persistent(fn, (int)g, lds, args, st);
 }
 
 template <int DM>
@@ -1242,7 +1266,7 @@ int dense_mfma_resident_tile(int D, int full, int B, int T, int reuse, int num_c
 
 hipError_t launch_dense_mfma(const DenseLoopArgs<float>& a, int full, int num_cu, hipStream_t st) {
   const bool reuse = a.nbuf > 2;
-  if (full) return coop_launch((const void*)dense_full_mfma_kernel, a, mff_lds_floats(reuse) * 4, num_cu, st);
+  if (full) return persistent_launch((const void*)dense_full_mfma_kernel, a, mff_lds_floats(reuse) * 4, num_cu, st);
   const bool res = a.out != nullptr;
   const bool dreuse = a.jac_every > 1;
   if (a.nbuf != (dreuse ? 3 : 2)) return hipErrorInvalidValue;
@@ -1253,7 +1277,7 @@ hipError_t launch_dense_mfma(const DenseLoopArgs<float>& a, int full, int num_cu
   if (a.x && lds < (size_t)a.L * 68 * 4) return hipErrorInvalidValue;   // room to stage the projection
   // the resident variant needs one co-resident block per tile
   if (res && (long)block_occupancy(fn, lds) * num_cu < a.n_tiles) return hipErrorInvalidValue;
-  return coop_launch(fn, a, lds, num_cu, st);
+  return persistent_launch(fn, a, lds, num_cu, st);
 }
 
 }  // namespace pnr

@@ -709,7 +709,7 @@ hipError_t launch_diag_newton(int cell, const DiagLoopArgs& a, int grid, hipStre
   void* args[] = {const_cast<DiagLoopArgs*>(&a)};
   const void* fn = cell == PNR_CELL_GRU_DIAG ? (const void*)diag_newton_kernel<PNR_CELL_GRU_DIAG, diag_n<PNR_CELL_GRU_DIAG>()>
                                              : (const void*)diag_newton_kernel<PNR_CELL_LSTM_DIAG, diag_n<PNR_CELL_LSTM_DIAG>()>;
-  return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(PNR_BLOCK), args, 0, st);
+  return launch_persistent(fn, grid, 0, args, st);
 }
 
 }  // namespace pnr

@@ -12,6 +12,9 @@ constexpr int kMaxGrid = 16384;
 // LDS limit first when needed), 0 when it cannot run.  Cached per (kernel, LDS size):
 // the runtime queries cost tens of microseconds per call.
 int cached_occupancy(const void* fn, size_t lds);
+// launch of a grid sized to the resident capacity (ordinary, or cooperative when
+// PNR_COOPERATIVE=1)
+hipError_t launch_persistent(const void* fn, int grid, size_t lds, void** args, hipStream_t st);
 
 // ---------------------------------------------------------------------------------
 // Decision taken by the block that merges the residual partials of iteration k (the

@@ -1,6 +1,7 @@
 // Small kernels around the Newton loop: per-call initialisation of the control block
 // and look-back slots, and the conversion of the returned iterate to the caller's
 // [B, T, S] layout.
+#include <cstdlib>
 #include <mutex>
 
 #include "common.h"
@@ -23,6 +24,23 @@ int cached_occupancy(const void* fn, size_t lds) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, fn, PNR_BLOCK, lds) != hipSuccess) v = 0;
   if (n < 64) cache[n++] = Entry{fn, lds, dev, v};
   return v;
+}
+
+// Persistent launches.  Every persistent grid here is sized to the device's resident
+// capacity (cached_occupancy) and every wait inside it is bounded (a wait that runs out
+// records a fault, which the call reports as an error, never a hang).  Such a grid goes
+// out as an ordinary launch: on a device that runs nothing else at the same time all of
+// its workgroups are resident together, and the ordinary path costs ~15-20 us less per
+// call than the cooperative one.  PNR_COOPERATIVE=1 selects hipLaunchCooperativeKernel,
+// which also guarantees co-residency next to other work (several persistent calls
+// running at once on different streams, for instance).
+hipError_t launch_persistent(const void* fn, int grid, size_t lds, void** args, hipStream_t st) {
+  static const bool coop = [] {
+    const char* e = getenv("PNR_COOPERATIVE");
+    return e && e[0] == '1';
+  }();
+  if (coop) return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(PNR_BLOCK), args, (unsigned)lds, st);
+  return hipLaunchKernel(fn, dim3(grid), dim3(PNR_BLOCK), args, lds, st);
 }
 
 __global__ void init_kernel(Ctrl* ctrl, uint64_t* slots, size_t n, uint64_t* partials, size_t np) {
