@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 METRIC = "converged timesteps·batch/sec (B·T/s) per layer; Newton iters; scan HBM GB/s"
 UNIT = "timesteps*batch/s"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0, "f64": 78.6}   # dense, published
 PRIMARY = "gru_quasi"
 DEFAULT_OTHERS = "tiny_gru,gru_full,gru_diag_long,lstm_diag_long,lstm_diag_long_stiff"
 CSRC = "nonlinear_rnn_evaluation_amd/csrc/"
@@ -81,6 +82,34 @@ def iteration_bytes(w, k, iters_total, resid=False):
     jk = k - (k % w.jac_every)
     jac = h if (jk != k and jk > 0) else 0
     return gx + cur + h + jac
+
+
+def mfma_counters(name, mode, phases):
+    """MFMA utilisation of the workload's matrix-core kernels, from the committed rocprofv3
+    counter summary (profiles/mfma_<workload>_pmc.json): busy fraction of the matrix
+    cores (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs) and the counted MFMA
+    flops per launch, which over this run's live launch time give TFLOP/s.  Entries whose
+    kernel source changed since the counters were taken are left out."""
+    path = os.path.join(ROOT, "profiles", f"mfma_{name}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("jac_mode") != mode:
+        return None
+    out = []
+    for k in rec["kernels"]:
+        if k["kernel_src_sha"] != src_hash(k["kernel_src"]):
+            continue
+        live_ms = phases["proj_ms"] if "gemm" in k["kernel"] else phases["newton_ms"]
+        tf = k["mfma_flops_per_launch"] / (live_ms * 1e-3) / 1e12 if live_ms else None
+        pk = MFMA_PEAK_TFLOPS[k["dtype"]]
+        out.append({"kernel": k["kernel"].split("(")[0], "dtype": k["dtype"],
+                    "busy_util": round(k["mfma_busy_util"], 4),
+                    "counted_flops_per_launch": k["mfma_flops_per_launch"],
+                    "tflops": None if tf is None else round(tf, 2), "peak_tflops": pk,
+                    "frac": None if tf is None else round(tf / pk, 4)})
+    return out or None
 
 
 def run_workload(name, steps, warmup, mode=None, with_cpu=True, cpu_budget=12.0, parity=True):
@@ -148,11 +177,24 @@ def run_workload(name, steps, warmup, mode=None, with_cpu=True, cpu_budget=12.0,
             pmc = json.load(f)
         if pmc.get("kernel_src_sha") == src_hash(ksrc) and pmc.get("jac_mode") == mode:
             traffic = pmc.get("bytes_per_launch")
-    roof = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "avg_launch_us": round(newton_ms * 1e3, 3), "launches_per_step": 1, "passes_per_launch": passes,
-            "algorithmic_bytes_per_launch": bytes_call,
-            "us_per_pass": round(newton_ms * 1e3 / max(passes, 1), 3)}
+    common = {"kernel": kname, "avg_launch_us": round(newton_ms * 1e3, 3), "launches_per_step": 1,
+              "passes_per_launch": passes, "us_per_pass": round(newton_ms * 1e3 / max(passes, 1), 3)}
+    hbm = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+           "algorithmic_bytes_per_launch": bytes_call}
+    if fused:
+        # The quasi-Newton dense kernel keeps every iterate in LDS: its HBM traffic is the
+        # inputs, gx and the output only, so the bytes a streaming design would move do not
+        # bound it.  Its arithmetic is the fp32 recurrent product U h of every pass (one per
+        # iterate whose residual is checked) plus the input projection, all on MFMA.
+        flops = (iters + 1) * 2.0 * w.B * w.T * w.D * w.G * w.D + 2.0 * w.B * w.T * w.D_in * w.G * w.D
+        tf = flops / (newton_ms * 1e-3) / 1e12 if newton_ms > 0 else 0.0
+        pk = MFMA_PEAK_TFLOPS["f32"]
+        roof = dict(common, bound="mfma", achieved=round(tf, 2), peak=pk, unit="TFLOP/s",
+                    frac=round(tf / pk, 4), traffic=traffic, algorithmic_flops_per_launch=flops,
+                    streaming_model_hbm=hbm)
+    else:
+        roof = dict(common, **hbm)
     phases = {k: round(sum(pp[k] for pp in profs) / steps, 4)
               for k in ("total_ms", "proj_ms", "newton_ms", "out_ms")}
     proj_flops = 2.0 * w.B * w.T * w.D_in * w.G * w.D
@@ -163,6 +205,7 @@ def run_workload(name, steps, warmup, mode=None, with_cpu=True, cpu_budget=12.0,
     rec = {"workload": name, "status": int(status), "iters": int(iters), "ms_per_step": round(ms, 4),
            "value": (w.B * w.T) / (ms * 1e-3) if status == 0 else None,
            "wall_s": round(wall, 3), "gen_s": round(t_gen, 2), "roofline": roof, "phases_ms": phases,
+           "mfma": mfma_counters(name, mode, phases),
            "residual": last["residual"], "jac_mode": ["full", "diag", "zero"][mode],
            "config": w.describe()}
 
@@ -269,7 +312,7 @@ def main():
         "config": dict({"workload": prim["workload"]}, **{k: v for k, v in prim["config"].items() if k != "workload"}),
         "newton_iters": prim["iters"], "status": prim["status"],
         "roofline": prim["roofline"], "cpu_baseline": prim.get("cpu_baseline"), "parity": prim.get("parity"),
-        "phases_ms": prim["phases_ms"], "others": others,
+        "phases_ms": prim["phases_ms"], "mfma": prim["mfma"], "others": others,
     }
     print(json.dumps(line), flush=True)
 
