@@ -19,16 +19,24 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16_t;
 // ---------------------------------------------------------------------------------
 // bf16 MFMA GEMM.  Block tile 128 x 128, K step 32, 256 threads = 4 waves in 2 x 2,
 // each wave 64 x 64 = 2 x 2 MFMA tiles of 32 x 32.  LDS double buffered; rows padded
-// by 8 bf16 to spread ds_read_b128 over banks.
-constexpr int GB_M = 128, GB_N = 128, GB_K = 32, GB_LD = GB_K + 8;
+// by 8 bf16 to spread ds_read_b128 over banks.  Registers are held to 128 so that four
+// blocks share a CU (their waves hide each other's global-load latency; LDS 4 x 40 KB).
+// Block order: groups of GB_GM row tiles sweep the column tiles together, so each
+// column-operand tile is fetched by GB_GM blocks at about the same time (one trip from
+// HBM instead of one per row tile) while the group's row tiles stay cached.
+constexpr int GB_M = 128, GB_N = 128, GB_K = 32, GB_LD = GB_K + 8, GB_GM = 32;
 
-__global__ void __launch_bounds__(256) gemm_bf16_mfma(GemmArgs g) {
+__global__ void __launch_bounds__(256, 4) gemm_bf16_mfma(GemmArgs g) {
   __shared__ __align__(16) __bf16 As[2][GB_M * GB_LD];
   __shared__ __align__(16) __bf16 Bs[2][GB_N * GB_LD];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
   const int z = blockIdx.z;
-  const int i0 = blockIdx.y * GB_M, j0 = blockIdx.x * GB_N;
+  const int gx = (int)gridDim.x, gy = (int)gridDim.y;
+  const int lin = (int)blockIdx.y * gx + (int)blockIdx.x;
+  const int grp = lin / (GB_GM * gx), loc = lin - grp * GB_GM * gx;
+  const int gm = min(GB_GM, gy - grp * GB_GM);   // row tiles in this group
+  const int i0 = (grp * GB_GM + loc % gm) * GB_M, j0 = (loc / gm) * GB_N;
   const __bf16* A = reinterpret_cast<const __bf16*>(g.A) + (size_t)z * g.sA;
   const __bf16* Bm = reinterpret_cast<const __bf16*>(g.Bm) + (size_t)z * g.sB;
   float* C = reinterpret_cast<float*>(g.C) + (size_t)z * g.sC;
