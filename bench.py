@@ -281,7 +281,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=PRIMARY)
     ap.add_argument("--others", default=DEFAULT_OTHERS, help="comma list, or 'none'")
-    ap.add_argument("--other-steps", type=int, default=5)
+    ap.add_argument("--other-steps", type=int, default=10)
+    ap.add_argument("--other-warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     args = ap.parse_args()
@@ -303,7 +304,7 @@ def main():
             w = WL.get_workload(name)
             for mode in w.jac_modes:
                 print(f"# bench: {name} mode {mode}", file=sys.stderr, flush=True)
-                r = run_workload(name, args.other_steps, 1, mode=mode, with_cpu=False)
+                r = run_workload(name, args.other_steps, args.other_warmup, mode=mode, with_cpu=False)
                 others.append(r)
     line = {
         "metric": METRIC, "value": prim["value"], "unit": UNIT, "n_gpus": 1, "steps": args.steps,

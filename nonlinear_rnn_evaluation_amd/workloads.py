@@ -119,7 +119,8 @@ def named_workloads() -> dict:
         state_dtype=DT_F32, w_init="glorot", u_init="uniform1", forget_bias=1.0,
         jac_modes=(JAC_FULL,), jac_every=2, tol=1e-4, max_iters=64)
     w["lstm_diag_long_stiff"] = dataclasses.replace(
-        w["lstm_diag_long"], name="lstm_diag_long_stiff", u_scale=3.0, max_iters=256)
+        w["lstm_diag_long"], name="lstm_diag_long_stiff", u_scale=3.0, max_iters=256,
+        jac_modes=(JAC_FULL, JAC_DIAG))
     return w
 
 
