@@ -113,7 +113,8 @@ Layout make_layout(const pnr_cell* c, int jac_mode) {
     l.slot_words = (size_t)l.n_tiles * dense_slot_words(c->D, l.dense_full, c->state_dtype == PNR_F64);
   }
   l.slots = off; off = align_up(off + sizeof(uint64_t) * (l.slot_words ? l.slot_words : 1));
-  l.gx = off; off = align_up(off + es * B * T * (size_t)G * D);
+  // gx, plus kGxPadRows rows that the dense kernels may read (and mask) past the end
+  l.gx = off; off = align_up(off + es * (B * T + (size_t)kGxPadRows) * (size_t)G * D);
   for (int i = 0; i < l.nbuf; ++i) { l.h[i] = off; off = align_up(off + es * B * T * (size_t)S); }
   l.total = off;
   return l;

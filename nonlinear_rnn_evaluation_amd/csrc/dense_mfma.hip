@@ -511,15 +511,20 @@ __global__ void __launch_bounds__(PNR_BLOCK, (RES && TL > 64) ? 1 : 2)
   const int grid = (int)gridDim.x;
   const bool merger = blockIdx.x == 0;
 
-  // Gate inputs of step tb*16 + 4(lane/16) + i, channel c_mf, of a tile.
-  auto load_gx = [&](float (&v)[4][3], int b, int t0, int Lv, int tb) {
+  // Gate inputs of step tb*16 + 4(lane/16) + i, channel c_mf, of a tile.  The loads are
+  // unconditional and unmasked: the gx region is padded by kGxPadRows rows, so the rows
+  // of a tile past the end of the sequence are readable, and every value computed from
+  // such a row is replaced in cell_elem (residual 0, Jacobian 1) by a select.  With no
+  // branch and no select at the load, the loads stay in flight across the next block's
+  // MFMAs instead of each one being waited for.
+  auto load_gx = [&](float (&v)[4][3], int b, int t0, int tb) {
     const float* gxb = a.gx + (size_t)b * T * 3 * D;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int s = tb * 16 + 4 * (lane >> 4) + i;
       const float* g = gxb + (size_t)(t0 + s) * 3 * D;
 #pragma unroll
-      for (int q = 0; q < 3; ++q) v[i][q] = s < Lv ? g[q * D + c_mf] : 0.f;
+      for (int q = 0; q < 3; ++q) v[i][q] = g[q * D + c_mf];
     }
   };
 
@@ -679,29 +684,31 @@ __global__ void __launch_bounds__(PNR_BLOCK, (RES && TL > 64) ? 1 : 2)
       };
       // Software pipeline over the blocks of 16 steps: block u's MFMAs are issued
       // before block u-1's elementwise work, which does not depend on them.  The gate
-      // inputs are loaded a block ahead.
+      // inputs are loaded a block ahead.  Two blocks per trip in ping-pong registers:
+      // copying just-loaded gate inputs from one set to the other would make the
+      // compiler wait for those loads in the middle of the elementwise work.
       {
         v4f fa[D / 16];
         v4f accA[3], accB[3];
         float gvA[4][3], gvB[4][3];
         load_afrag<D>(Xc, LD, tb0, fa);
-        load_gx(gvA, b, t0, Lv, tb0);
+        load_gx(gvA, b, t0, tb0);
         gates_frag<D>(fa, uf, accA);
         if (NTB > 1) load_afrag<D>(Xc, LD, tb0 + TBS, fa);
-#pragma unroll 1
-        for (int u = 1; u < NTB; ++u) {
-          load_gx(gvB, b, t0, Lv, tb0 + u * TBS);
+#pragma unroll
+        for (int u = 1; u < NTB; u += 2) {
+          load_gx(gvB, b, t0, tb0 + u * TBS);
           gates_frag<D>(fa, uf, accB);
           if (u + 1 < NTB) load_afrag<D>(Xc, LD, tb0 + (u + 1) * TBS, fa);
           cell_elem(tb0 + (u - 1) * TBS, accA, gvA);
-#pragma unroll
-          for (int g = 0; g < 3; ++g) accA[g] = accB[g];
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int q = 0; q < 3; ++q) gvA[i][q] = gvB[i][q];
+          if (u + 1 < NTB) {
+            load_gx(gvA, b, t0, tb0 + (u + 1) * TBS);
+            gates_frag<D>(fa, uf, accA);
+            if (u + 2 < NTB) load_afrag<D>(Xc, LD, tb0 + (u + 2) * TBS, fa);
+          }
+          cell_elem(tb0 + u * TBS, accB, gvB);
         }
-        cell_elem(tb0 + (NTB - 1) * TBS, accA, gvA);
+        if (NTB & 1) cell_elem(tb0 + (NTB - 1) * TBS, accA, gvA);
       }
       blk_max = max(blk_max, tmax);
       __syncthreads();

@@ -7,6 +7,9 @@ namespace pnr {
 
 // Upper bound on the grid of any persistent iteration kernel (sizes the partials array).
 constexpr int kMaxGrid = 16384;
+// rows of padding after the gate-input region: the longest dense tile, so a tile's rows
+// past the end of the sequence can be read (and masked) without a bounds branch
+constexpr int kGxPadRows = 128;
 
 // Resident blocks of `fn` per CU with `lds` bytes of dynamic LDS (raising the kernel's
 // LDS limit first when needed), 0 when it cannot run.  Cached per (kernel, LDS size):
