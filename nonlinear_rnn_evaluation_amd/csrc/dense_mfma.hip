@@ -44,27 +44,27 @@ __device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Stage rows s = 0..TL of the tile: row s holds the state before step t0+s.  Row 0 is
-// the previous tile's last step (another block's): read coherently.  Batched loads.
+// Stage rows s = 0..TL of the tile: row s holds the state before step t0+s.  Rows 1..TL
+// are this block's own states of the pass before: plain loads, every load of a batch
+// issued before any is used (addresses clamped into the sequence, values past its end
+// replaced afterwards), so a batch costs one memory round trip.  Row 0 is the previous
+// tile's last step, written by another block: threads tid < D read it coherently.
 template <int TL = kTL>
 __device__ __forceinline__ void stage_rows(float* __restrict__ X, const float* __restrict__ H,
                                            const float* __restrict__ h0, int b, int t0, int T, int D,
                                            int LD) {
   const int tid = threadIdx.x;
   const int n = (TL + 1) * D;
-  for (int j0 = 0; j0 < n; j0 += kLoadBatch * PNR_BLOCK) {
+  for (int j0 = D; j0 < n; j0 += kLoadBatch * PNR_BLOCK) {
     float v[kLoadBatch];
 #pragma unroll
-    for (int j = 0; j < kLoadBatch; ++j) {
-      const int idx = j0 + tid + j * PNR_BLOCK;
-      v[j] = 0.f;
-      if (idx < n) {
-        const int s = idx / D, c = idx - s * D, t = t0 + s - 1;
-        if (t < 0) v[j] = h0 ? h0[(size_t)b * D + c] : 0.f;
-        else if (t < T && H) {
-          const float* p = H + ((size_t)b * T + t) * D + c;
-          v[j] = s == 0 ? coherent_load(p) : *p;
-        }
+    for (int j = 0; j < kLoadBatch; ++j) v[j] = 0.f;
+    if (H) {
+#pragma unroll
+      for (int j = 0; j < kLoadBatch; ++j) {
+        const int idx = min(j0 + tid + j * PNR_BLOCK, n - 1);
+        const int s = idx / D, c = idx - s * D, t = min(t0 + s - 1, T - 1);
+        v[j] = H[((size_t)b * T + t) * D + c];
       }
     }
 #pragma unroll
@@ -72,9 +72,14 @@ __device__ __forceinline__ void stage_rows(float* __restrict__ X, const float* _
       const int idx = j0 + tid + j * PNR_BLOCK;
       if (idx < n) {
         const int s = idx / D, c = idx - s * D;
-        X[s * LD + c] = v[j];
+        X[s * LD + c] = t0 + s - 1 < T ? v[j] : 0.f;
       }
     }
+  }
+  if (tid < D) {
+    const int t = t0 - 1;
+    X[tid] = t < 0 ? (h0 ? h0[(size_t)b * D + tid] : 0.f)
+                   : (H ? coherent_load(H + ((size_t)b * T + t) * D + tid) : 0.f);
   }
 }
 
@@ -163,26 +168,22 @@ __device__ __forceinline__ int window_read(const uint64_t* __restrict__ slots, i
   const int tid = threadIdx.x;
   if (tid < Wn) { s_ok[tid][0] = 1; s_ok[tid][1] = 1; }
   __syncthreads();
+  // every load of a batch first (indices clamped into the window), then the tag checks
   for (int j0 = 0; j0 < Wn * SV; j0 += kLoadBatch * PNR_BLOCK) {
-    float v[kLoadBatch];
-    bool ok[kLoadBatch];
+    uint64_t x[kLoadBatch];
 #pragma unroll
     for (int j = 0; j < kLoadBatch; ++j) {
-      const int idx = j0 + tid + j * PNR_BLOCK;
-      ok[j] = true;
-      v[j] = 0.f;
-      if (idx < Wn * SV) {
-        const int w = idx / SV, e = idx - w * SV;
-        ok[j] = slot_get(slots + (size_t)(tile - 1 - w) * SV + e, ep, v[j]);
-      }
+      const int idx = min(j0 + tid + j * PNR_BLOCK, Wn * SV - 1);
+      const int w = idx / SV, e = idx - w * SV;
+      x[j] = __hip_atomic_load(slots + (size_t)(tile - 1 - w) * SV + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 #pragma unroll
     for (int j = 0; j < kLoadBatch; ++j) {
       const int idx = j0 + tid + j * PNR_BLOCK;
       if (idx < Wn * SV) {
         const int w = idx / SV, e = idx - w * SV;
-        if (!ok[j]) s_ok[w][e < SA ? 0 : 1] = 0;
-        Win[w * SV + e] = v[j];
+        if ((uint32_t)(x[j] >> 32) != ep) s_ok[w][e < SA ? 0 : 1] = 0;
+        Win[w * SV + e] = __uint_as_float((uint32_t)x[j]);
       }
     }
   }
@@ -981,13 +982,15 @@ __global__ void __launch_bounds__(PNR_BLOCK) dense_full_mfma_kernel(DenseLoopArg
       uint32_t tmax = 0;
       {
         const int tb = wid;
+        // unconditional loads (the gx region is padded by kGxPadRows rows); steps past
+        // the end of the sequence never read their values
         float gxv[4][3];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int s = tb * 16 + 4 * q + i;
           const float* g = gxb + (size_t)(t0 + s) * 3 * D;
 #pragma unroll
-          for (int gg = 0; gg < 3; ++gg) gxv[i][gg] = s < Lv ? g[gg * D + m] : 0.f;
+          for (int gg = 0; gg < 3; ++gg) gxv[i][gg] = g[gg * D + m];
         }
         v4f acc[3], accj[3];
         gates_block<D>(X, LD, tb, uf, acc);
