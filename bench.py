@@ -277,12 +277,12 @@ def oracle_leg(w, p, out, with_cpu, budget):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default=PRIMARY)
     ap.add_argument("--others", default=DEFAULT_OTHERS, help="comma list, or 'none'")
     ap.add_argument("--other-steps", type=int, default=10)
-    ap.add_argument("--other-warmup", type=int, default=3)
+    ap.add_argument("--other-warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     args = ap.parse_args()
