@@ -23,6 +23,10 @@ What it computes (sources are the five pages on this method):
   "Builds on: parallel associative scan").
 * ``sequential(..., dtype=np.float32)`` -- the same loop in fp32: the conditioning
   floor, i.e. the best agreement any fp32 evaluation can reach on a workload.
+* ``lm_step_dense`` / ``lm_step_kalman`` -- the damped (Levenberg-Marquardt) step of
+  ELK / quasi-ELK, by its normal equations and as a Kalman filter and smoother
+  ("Towards Scalable and Stable Parallelization of Nonlinear RNNs", abstract and the
+  summary's "Approach"); ``newton_dense(..., damping=lam)`` iterates it.
 
 Cell equations are not printed on the pages; the readings used (linear-before-reset
 GRU with gates (r, z, n); LSTM with gates (i, f, o, g) and state (c, h); elementwise
@@ -34,6 +38,7 @@ from .cells import (CELL_GRU, CELL_GRU_DIAG, CELL_LSTM_DIAG, JAC_FULL, JAC_DIAG,
 from .sequential import project, sequential, restrict_channels
 from .newton import newton_dense, STATUS_OK, STATUS_NOT_CONVERGED, STATUS_NONFINITE, max_abs
 from .scan import scan_loop, scan_doubling, compose
+from .damped import lm_step_dense, lm_step_kalman, damped_step
 
 __all__ = [
     "CELL_GRU", "CELL_GRU_DIAG", "CELL_LSTM_DIAG", "JAC_FULL", "JAC_DIAG", "JAC_ZERO",
@@ -41,4 +46,5 @@ __all__ = [
     "project", "sequential", "restrict_channels",
     "newton_dense", "STATUS_OK", "STATUS_NOT_CONVERGED", "STATUS_NONFINITE", "max_abs",
     "scan_loop", "scan_doubling", "compose",
+    "lm_step_dense", "lm_step_kalman", "damped_step",
 ]

@@ -32,6 +32,7 @@ from __future__ import annotations
 import numpy as np
 
 from .cells import approx_jacobian, cell_jacobian, cell_step
+from .damped import damped_step
 from .scan import scan_loop
 from .sequential import project
 
@@ -56,12 +57,17 @@ def _previous_states(h0, H):
 
 
 def newton_dense(cell: int, W, U, b_x, b_h, x, h0, max_iters: int, tol: float,
-                 jac_mode: int, jac_every: int = 1, gx=None, solver: str = "dense"):
+                 jac_mode: int, jac_every: int = 1, gx=None, solver: str = "dense",
+                 damping: float = 0.0):
     """Returns dict(states [B,T,S], iters, status, rhos[list], jac_evals).
 
     solver="dense" assembles the block-bidiagonal matrix and calls LAPACK (only for
     T*S up to a few thousand); solver="loop" solves the same system by forward
     substitution (``scan_loop``), which the tests pin to the dense solve.
+
+    damping = lam > 0 takes the damped (Levenberg-Marquardt / ELK) step of
+    ``oracle.damped`` instead: solver="dense" solves its normal equations with LAPACK,
+    solver="loop" runs the Kalman filter and smoother.
     """
     if jac_every < 1:
         raise ValueError("jac_every must be >= 1")
@@ -95,6 +101,9 @@ def newton_dense(cell: int, W, U, b_x, b_h, x, h0, max_iters: int, tol: float,
             Jhat = approx_jacobian(J, jac_mode).reshape(B, T, S, S)
             jac_evals += 1
         for b in range(B):
+            if damping > 0:
+                H[b] = H[b] + damped_step(Jhat[b], r[b], damping, "dense" if solver == "dense" else "kalman")
+                continue
             if solver == "loop":
                 H[b] = H[b] + scan_loop(Jhat[b], r[b])
                 continue
