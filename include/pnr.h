@@ -147,6 +147,27 @@ int pnr_last_residual_history(double* out, int max_n);
 const char* pnr_last_error(void);
 
 /*
+ * Damped Newton evaluation: ELK / quasi-ELK ("Towards Scalable and Stable
+ * Parallelization of Nonlinear RNNs", abstract; summary page, "Approach": a
+ * Levenberg-Marquardt trust region whose linear-Gaussian MAP solve is a Kalman filter
+ * and smoother; with the diagonal Jacobian, quasi-ELK; "Limitations": the trust-region
+ * strength is a hyperparameter).  Same iteration, stopping test and results as
+ * pnr_eval, except that the update d minimises
+ *     sum_t |d_t - J_t d_{t-1} - r_t|^2 + damping * sum_t |d_t|^2      (d_0 = 0)
+ * instead of solving d_t = J_t d_{t-1} + r_t (damping -> 0 gives pnr_eval's step).  Per
+ * channel this is a scalar Kalman filter (forward scan) and RTS smoother (backward scan).
+ * The step is always taken (fixed damping, no adaptive trust region).
+ * Supported: PNR_CELL_GRU_DIAG (whose exact Jacobian is diagonal) with jac_mode
+ * PNR_JAC_FULL or PNR_JAC_DIAG, jac_every = 1, (x, state) as for pnr_eval; others
+ * return PNR_E_UNSUPPORTED.  damping must be finite and > 0 (else PNR_E_INVALID).
+ * Workspace: pnr_workspace_bytes_damped() bytes (the filter's per-step variance, mean,
+ * Jacobian and residual take 16 bytes per state element more than pnr_eval).
+ */
+size_t pnr_workspace_bytes_damped(const pnr_cell* cell, int jac_mode);
+int pnr_eval_damped(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0,
+                    void* h_out, int max_iters, double tol, int jac_mode, double damping);
+
+/*
  * Standalone linear solve used inside every Newton iteration, exposed for testing
  * the scan on its own: d_t = A_t d_{t-1} + b_t, d_0 = 0 along t, for R independent
  * rows (ParaRNN overview, "Newton's Iteration": forward substitution on the block

@@ -191,6 +191,49 @@ int device_info(int* num_cu) {
     if (e_ != hipSuccess) return fail(PNR_E_HIP, "%s failed: %s", #call, hipGetErrorString(e_)); \
   } while (0)
 
+// The one device -> host crossing of a call: the control block and the residual
+// history (adjacent in the workspace) in one copy into a pinned, thread-local buffer
+// (allocated once, grown rarely, kept for the life of the thread) so the copy is a
+// plain DMA on the stream; then the call's results and, in measurement mode, its
+// per-phase timing.  Returns the call's status.
+int finish_call(const Layout& l, char* ws, int max_iters, hipStream_t st, const Mark& m_first, const Mark& m_proj,
+                const Mark& m_newton, const Mark& m_out) {
+  static thread_local char* rb = nullptr;
+  static thread_local size_t rb_cap = 0;
+  const size_t rb_bytes = (l.hist - l.ctrl) + sizeof(double) * (max_iters + 1);
+  if (rb_cap < rb_bytes) {
+    if (rb) (void)hipHostFree(rb);
+    rb = nullptr;
+    rb_cap = 0;
+    PNR_HIP(hipHostMalloc(reinterpret_cast<void**>(&rb), rb_bytes, hipHostMallocDefault));
+    rb_cap = rb_bytes;
+  }
+  PNR_HIP(hipMemcpyAsync(rb, ws + l.ctrl, rb_bytes, hipMemcpyDeviceToHost, st));
+  PNR_HIP(hipStreamSynchronize(st));
+  Ctrl hc;
+  memcpy(&hc, rb, sizeof(Ctrl));
+  const double* hh = reinterpret_cast<const double*>(rb + (l.hist - l.ctrl));
+  if (hc.fault)
+    return fail(PNR_E_HIP, "device loop gave up waiting (%s); results are not valid",
+                hc.fault == 1 ? "look-back" : "grid barrier");
+  if (!hc.done || hc.iters < 0) return fail(PNR_E_HIP, "device loop did not record a decision");
+  g_last.iters = hc.iters;
+  g_last.residual = hc.rho;
+  g_last.hist.assign(hh, hh + hc.iters + 1);
+  if (g_prof.on) {
+    pnr_profile p{};
+    p.total_ms = mark_ms(m_first);
+    p.proj_ms = mark_ms(m_proj);
+    p.newton_ms = mark_ms(m_newton);
+    p.out_ms = mark_ms(m_out);
+    p.passes = hc.iters + 1;
+    p.resid_only = hc.iters == max_iters;
+    g_prof.last = p;
+    g_prof.valid = true;
+  }
+  return hc.status;
+}
+
 }  // namespace
 
 extern "C" {
@@ -383,44 +426,104 @@ int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, cons
   mark_end(m_out, st);
   mark_end(m_first, st);
 
-  // ---- the one device -> host crossing of the call ----
-  // control block and residual history are adjacent in the workspace: one copy
-  // into a pinned, thread-local buffer (allocated once, grown rarely, kept for the life
-  // of the thread) so the copy is a plain DMA on the stream
-  static thread_local char* rb = nullptr;
-  static thread_local size_t rb_cap = 0;
-  const size_t rb_bytes = (l.hist - l.ctrl) + sizeof(double) * (max_iters + 1);
-  if (rb_cap < rb_bytes) {
-    if (rb) (void)hipHostFree(rb);
-    rb = nullptr;
-    rb_cap = 0;
-    PNR_HIP(hipHostMalloc(reinterpret_cast<void**>(&rb), rb_bytes, hipHostMallocDefault));
-    rb_cap = rb_bytes;
+  return finish_call(l, ws, max_iters, st, m_first, m_proj, m_newton, m_out);
+}
+
+// ---- damped (quasi-ELK) evaluation ----
+namespace {
+int validate_damped(const pnr_cell* c, int jac_mode) {
+  int rc = validate(c, jac_mode);
+  if (rc) return rc;
+  if (c->kind != PNR_CELL_GRU_DIAG || jac_mode == PNR_JAC_ZERO)
+    return fail(PNR_E_UNSUPPORTED, "the damped step is implemented for GRU_DIAG with a full or diagonal Jacobian");
+  if (c->jac_every != 1) return fail(PNR_E_UNSUPPORTED, "the damped step needs jac_every = 1");
+  return 0;
+}
+// pnr_eval's layout, plus four per-step planes of the filter (P, m, J, r)
+size_t damped_planes_offset(const Layout& l) { return l.total; }
+size_t damped_total(const pnr_cell* c, const Layout& l) {
+  return align_up(l.total + 4 * sizeof(float) * (size_t)c->B * c->T * c->D);
+}
+}  // namespace
+
+size_t pnr_workspace_bytes_damped(const pnr_cell* cell, int jac_mode) {
+  if (validate_damped(cell, jac_mode) != 0) return 0;
+  return damped_total(cell, make_layout(cell, jac_mode));
+}
+
+int pnr_eval_damped(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, void* h_out,
+                    int max_iters, double tol, int jac_mode, double damping) {
+  g_last = LastCall();
+  g_prof.valid = false;
+  int rc = validate_damped(cell, jac_mode);
+  if (rc) return rc;
+  if (!params) return fail(PNR_E_INVALID, "params is NULL");
+  if (!x || !h_out || !params->W || !params->U) return fail(PNR_E_INVALID, "x, h_out, W and U must be non-NULL");
+  if (max_iters < 0 || max_iters >= PNR_MAX_ITERS)
+    return fail(PNR_E_INVALID, "max_iters must be in [0, %d)", PNR_MAX_ITERS);
+  if (isnan(tol)) return fail(PNR_E_INVALID, "tol is NaN");
+  if (!(damping > 0.0) || !(damping < 1e30)) return fail(PNR_E_INVALID, "damping must be finite and > 0");
+  const Layout l = make_layout(cell, jac_mode);
+  const size_t need = damped_total(cell, l);
+  if (!cell->workspace) return fail(PNR_E_WORKSPACE, "workspace is NULL (%zu bytes required)", need);
+  if ((uintptr_t)cell->workspace % 256) return fail(PNR_E_WORKSPACE, "workspace must be 256-byte aligned");
+  if (cell->workspace_bytes < need)
+    return fail(PNR_E_WORKSPACE, "workspace has %zu bytes, %zu required", cell->workspace_bytes, need);
+  if (cell->T == 0) {
+    g_last.iters = 0;
+    g_last.residual = 0.0;
+    g_last.hist.assign(1, 0.0);
+    return PNR_OK;
   }
-  PNR_HIP(hipMemcpyAsync(rb, ws + l.ctrl, rb_bytes, hipMemcpyDeviceToHost, st));
-  PNR_HIP(hipStreamSynchronize(st));
-  Ctrl hc;
-  memcpy(&hc, rb, sizeof(Ctrl));
-  const double* hh = reinterpret_cast<const double*>(rb + (l.hist - l.ctrl));
-  if (hc.fault)
-    return fail(PNR_E_HIP, "device loop gave up waiting (%s); results are not valid",
-                hc.fault == 1 ? "look-back" : "grid barrier");
-  if (!hc.done || hc.iters < 0) return fail(PNR_E_HIP, "device loop did not record a decision");
-  g_last.iters = hc.iters;
-  g_last.residual = hc.rho;
-  g_last.hist.assign(hh, hh + hc.iters + 1);
-  if (g_prof.on) {
-    pnr_profile p{};
-    p.total_ms = mark_ms(m_first);
-    p.proj_ms = mark_ms(m_proj);
-    p.newton_ms = mark_ms(m_newton);
-    p.out_ms = mark_ms(m_out);
-    p.passes = hc.iters + 1;
-    p.resid_only = hc.iters == max_iters;
-    g_prof.last = p;
-    g_prof.valid = true;
-  }
-  return hc.status;
+  int num_cu = 0;
+  if ((rc = device_info(&num_cu))) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(cell->stream);
+  char* ws = static_cast<char*>(cell->workspace);
+  Ctrl* ctrl = reinterpret_cast<Ctrl*>(ws + l.ctrl);
+  double* hist = reinterpret_cast<double*>(ws + l.hist);
+  const int D = cell->D, T = cell->T, B = cell->B, Din = cell->D_in;
+  const size_t plane = (size_t)B * T * D;
+  float* planes = reinterpret_cast<float*>(ws + damped_planes_offset(l));
+
+  Mark m_first = mark_begin(st);
+  PNR_HIP(launch_init(ctrl, reinterpret_cast<uint64_t*>(ws + l.slots), l.slot_words,
+                      reinterpret_cast<uint64_t*>(ws + l.partials), kPartialWords, st));
+  // gx[b][m][t] = sum_k W[m][k] x[b][t][k] + b_x[m]
+  GemmArgs g{params->W, x, params->b_x, ws + l.gx, 3 * D, T, Din, 0, (long long)T * Din, (long long)3 * D * T,
+             Din, Din, T, B, 1};
+  Mark m_proj = mark_begin(st);
+  PNR_HIP(launch_gemm(cell->x_dtype, cell->state_dtype, g, st));
+  mark_end(m_proj, st);
+
+  ElkArgs a{};
+  a.gx = reinterpret_cast<const float*>(ws + l.gx);
+  a.u = static_cast<const float*>(params->U);
+  a.bh = static_cast<const float*>(params->b_h);
+  a.h0 = static_cast<const float*>(h0);
+  a.H[0] = reinterpret_cast<float*>(ws + l.h[0]);
+  a.H[1] = reinterpret_cast<float*>(ws + l.h[1]);
+  a.Pf = planes;
+  a.Mf = planes + plane;
+  a.Jf = planes + 2 * plane;
+  a.Rf = planes + 3 * plane;
+  a.partials = reinterpret_cast<uint32_t*>(ws + l.partials);
+  a.ctrl = ctrl;
+  a.rho_hist = hist;
+  a.B = B; a.D = D; a.T = T;
+  a.tiles_per_row = (T + PNR_BLOCK * elk_items_per_thread() - 1) / (PNR_BLOCK * elk_items_per_thread());
+  a.n_rows = B * D;
+  a.max_iters = max_iters; a.jac_mode = jac_mode; a.tol = tol;
+  a.lam = (float)damping;
+  Mark m_newton = mark_begin(st);
+  PNR_HIP(launch_elk_gru_diag(a, num_cu, st));
+  mark_end(m_newton, st);
+
+  Mark m_out = mark_begin(st);
+  const float* bufs[3] = {a.H[0], a.H[1], nullptr};
+  PNR_HIP(launch_diag_output(bufs, ctrl, static_cast<float*>(h_out), B, D, T, st));
+  mark_end(m_out, st);
+  mark_end(m_first, st);
+  return finish_call(l, ws, max_iters, st, m_first, m_proj, m_newton, m_out);
 }
 
 size_t pnr_scan_workspace_bytes(int kind, int R, int T, int tile_len) {

@@ -712,4 +712,281 @@ hipError_t launch_diag_newton(int cell, const DiagLoopArgs& a, int grid, hipStre
   return launch_persistent(fn, grid, 0, args, st);
 }
 
+// ---------------------------------------------------------------------------------
+// Damped (Levenberg-Marquardt) Newton step -- quasi-ELK -- for the GRU with elementwise
+// recurrent weights ("Towards Scalable and Stable Parallelization of Nonlinear RNNs",
+// abstract and the summary's "Approach": a trust region whose linear-Gaussian MAP
+// solve is a Kalman filter and smoother; with the diagonal Jacobian, quasi-ELK).
+//
+// Per channel the step D minimises sum_t (D_t - J_t D_{t-1} - r_t)^2 + lam sum_t D_t^2
+// (D_0 = 0), the smoothed mean of the scalar state-space model D_t = J_t D_{t-1} + r_t +
+// w_t (unit noise), 0 = D_t + v_t (noise variance 1/lam):
+//   filter:   P- = J^2 P + 1,  m- = J m + r,  P = P- / (1 + lam P-),  m = m- / (1 + lam P-)
+//   smoother: G_t = P_t J_{t+1} / P-_{t+1},  D_t = m_t + G_t (D_{t+1} - m-_{t+1}),  D_T = m_T.
+// In homogeneous coordinates (u, v, n) with P = u / v and m = n / v one filter step is
+// linear: u' = J^2 u + v, v' = lam J^2 u + (1 + lam) v, n' = r v + J n.  So the filter is
+// one associative scan of 3x3 maps [[a b 0][c d 0][e f g]] (7 numbers), started from
+// (0, 1, 0); the smoother is a scan of affine maps d -> G d + c run backwards in time.
+//
+// One block walks a whole row (channel): a forward sweep over its tiles evaluates the
+// cell, residual and Jacobian and runs the filter, storing P, m, J, r per step; a
+// backward sweep runs the smoother and writes the next iterate.  Tiles, thread-serial /
+// DPP / LDS scans and the carry between tiles are those of diag_newton_kernel; the
+// backward sweep maps thread t to the (255 - t)-th run of steps so that lane order is
+// reverse time and the same forward scan machinery applies.
+struct Flt {
+  float a, b, c, d, e, f, g;
+};
+__device__ __forceinline__ Flt compose(const Flt& l, const Flt& x) {
+  Flt o;
+  o.a = fmaf(l.a, x.a, l.b * x.c);
+  o.b = fmaf(l.a, x.b, l.b * x.d);
+  o.c = fmaf(l.c, x.a, l.d * x.c);
+  o.d = fmaf(l.c, x.b, l.d * x.d);
+  o.e = fmaf(l.e, x.a, fmaf(l.f, x.c, l.g * x.e));
+  o.f = fmaf(l.e, x.b, fmaf(l.f, x.d, l.g * x.f));
+  o.g = l.g * x.g;
+  // a positive rescaling changes neither P = u / v nor m = n / v: keep the entries near 1
+  const float s = fast_rcp(fmaxf(fmaxf(fabsf(o.a), fabsf(o.b)), fmaxf(fabsf(o.c), fabsf(o.d))));
+  o.a *= s; o.b *= s; o.c *= s; o.d *= s; o.e *= s; o.f *= s; o.g *= s;
+  return o;
+}
+__device__ __forceinline__ Flt flt_identity() { return Flt{1.f, 0.f, 0.f, 1.f, 0.f, 0.f, 1.f}; }
+template <> __device__ __forceinline__ Flt identity_of<Flt>() { return flt_identity(); }
+__device__ __forceinline__ Flt shfl_row_shr_aff(const Flt& v, const Flt& id, int s) {
+  Flt o;
+#define PNR_DPP7(C)                                                                 \
+  o.a = dpp_f<C>(id.a, v.a); o.b = dpp_f<C>(id.b, v.b); o.c = dpp_f<C>(id.c, v.c); \
+  o.d = dpp_f<C>(id.d, v.d); o.e = dpp_f<C>(id.e, v.e); o.f = dpp_f<C>(id.f, v.f); \
+  o.g = dpp_f<C>(id.g, v.g);
+  switch (s) {
+    case 1: PNR_DPP7(0x111) break;
+    case 2: PNR_DPP7(0x112) break;
+    case 4: PNR_DPP7(0x114) break;
+    default: PNR_DPP7(0x118) break;
+  }
+#undef PNR_DPP7
+  return o;
+}
+__device__ __forceinline__ Flt readlane_aff(const Flt& v, int l) {
+  return Flt{readlane_f(v.a, l), readlane_f(v.b, l), readlane_f(v.c, l), readlane_f(v.d, l),
+             readlane_f(v.e, l), readlane_f(v.f, l), readlane_f(v.g, l)};
+}
+struct V3 {
+  float u, v, n;
+};
+__device__ __forceinline__ V3 apply(const Flt& F, const V3& x) {
+  return V3{fmaf(F.a, x.u, F.b * x.v), fmaf(F.c, x.u, F.d * x.v), fmaf(F.e, x.u, fmaf(F.f, x.v, F.g * x.n))};
+}
+__device__ __forceinline__ V3 normalized(const V3& x) {
+  const float s = fast_rcp(x.v);
+  return V3{x.u * s, 1.f, x.n * s};
+}
+__device__ __forceinline__ V3 wave_shr1(const V3& x, const V3& lane0) {
+  return V3{wave_shr1(x.u, lane0.u), wave_shr1(x.v, lane0.v), wave_shr1(x.n, lane0.n)};
+}
+
+struct ElkShared {
+  Flt ftot[PNR_WAVES];
+  Aff1 btot[PNR_WAVES];
+  V3 fcarry;
+  float bcarry, jnext, rnext;
+};
+
+// Forward sweep over one tile: cell, residual, Jacobian, filter; stores P, m, J, r.
+template <int N>
+__device__ __forceinline__ void elk_forward_tile(const ElkArgs& a, ElkShared& sh, int row, int seg, const float* Hcur,
+                                                 uint32_t& blk_max) {
+  using C = DiagCell<PNR_CELL_GRU_DIAG>;
+  constexpr int TILE = PNR_BLOCK * N;
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int D = a.D, T = a.T;
+  const bool vec = (T & 3) == 0;
+  const int b = row / D, d = row - b * D;
+  const int tb = seg * TILE + tid * N;
+  const size_t roff = (size_t)row * T;
+  const C::Par q = C::load_par(a.u, a.bh, D, d);
+  float g[3][N], h[N];
+#pragma unroll
+  for (int gg = 0; gg < 3; ++gg) load_n(a.gx + ((size_t)(b * 3 + gg) * D + d) * T, tb, T, vec, N, g[gg]);
+  if (!Hcur) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) h[i] = 0.f;
+  } else {
+    load_n(Hcur + roff, tb, T, vec, N, h);
+  }
+  // the state before the thread's first step: the previous lane's last one (DPP); lane 0
+  // of each wave loads it (this block wrote it, or it is h0 / the zero guess)
+  float p0 = 0.f;
+  if (lane == 0) {
+    if (tb == 0) p0 = a.h0 ? a.h0[(size_t)b * D + d] : 0.f;
+    else if (Hcur && tb <= T) p0 = Hcur[roff + tb - 1];
+  }
+  p0 = wave_shr1(h[N - 1], p0);
+  const float lam = a.lam;
+  float jv[N], rv[N];
+  Flt F[N];
+  uint32_t tmax = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float p = i == 0 ? p0 : h[i - 1];
+    float gi[3] = {g[0][i], g[1][i], g[2][i]};
+    float res, ja = 0.f;
+    C::eval(q, gi, p, h[i], a.jac_mode, true, res, ja);
+    const bool in = tb + i < T;
+    res = in ? res : 0.f;
+    tmax = max(tmax, abs_bits(res));
+    jv[i] = ja;
+    rv[i] = res;
+    const float j2 = ja * ja;
+    F[i] = in ? Flt{j2, 1.f, lam * j2, 1.f + lam, 0.f, res, ja} : flt_identity();
+  }
+  blk_max = max(blk_max, tmax);
+  // ---- filter scan: thread-serial, wave (DPP), block (LDS), carry ----
+  Flt agg = F[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) agg = compose(F[i], agg);
+  const Flt incl = wave_inclusive_scan(agg, flt_identity());
+  if (lane == 63) sh.ftot[wid] = incl;
+  __syncthreads();
+  V3 xw = sh.fcarry;   // vector entering this wave's first step
+  for (int w = 0; w < wid; ++w) xw = normalized(apply(sh.ftot[w], xw));
+  V3 x = wave_shr1(normalized(apply(incl, xw)), xw);   // entering this thread's first step
+  float Pv[N], mv[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    x = normalized(apply(F[i], x));
+    Pv[i] = x.u;
+    mv[i] = x.n;
+  }
+  store_n(a.Pf + roff, tb, T, vec, N, Pv);
+  store_n(a.Mf + roff, tb, T, vec, N, mv);
+  store_n(a.Jf + roff, tb, T, vec, N, jv);
+  store_n(a.Rf + roff, tb, T, vec, N, rv);
+  __syncthreads();   // everyone has read ftot and fcarry
+  if (tid == PNR_BLOCK - 1) sh.fcarry = x;   // the last thread's last step: the next tile's carry
+  __syncthreads();
+}
+
+// Backward sweep over one tile: smoother, next iterate.  Thread t takes the run of N
+// steps that starts at step (PNR_BLOCK - 1 - t) * N of the tile and walks it backwards.
+template <int N>
+__device__ __forceinline__ void elk_backward_tile(const ElkArgs& a, ElkShared& sh, int row, int seg, const float* Hcur,
+                                                  float* Hnext) {
+  constexpr int TILE = PNR_BLOCK * N;
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int T = a.T;
+  const bool vec = (T & 3) == 0;
+  const int tb = seg * TILE + (PNR_BLOCK - 1 - tid) * N;
+  const size_t roff = (size_t)row * T;
+  float Pv[N], mv[N], jv[N + 1], rv[N + 1], h[N];
+  load_n(a.Pf + roff, tb, T, vec, N, Pv);
+  load_n(a.Mf + roff, tb, T, vec, N, mv);
+  load_n(a.Jf + roff, tb, T, vec, N, jv);
+  load_n(a.Rf + roff, tb, T, vec, N, rv);
+  // J and r of the step after the run (the next run's first step; stored by the forward sweep)
+  jv[N] = tb + N < T ? a.Jf[roff + tb + N] : 0.f;
+  rv[N] = tb + N < T ? a.Rf[roff + tb + N] : 0.f;
+  if (!Hcur) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) h[i] = 0.f;
+  } else {
+    load_n(Hcur + roff, tb, T, vec, N, h);
+  }
+  // smoother maps, latest step first: D_t = G_t D_{t+1} + c_t
+  Aff1 e[N];
+#pragma unroll
+  for (int i = N - 1; i >= 0; --i) {
+    const int t = tb + i;
+    const float j1 = jv[i + 1], r1 = rv[i + 1];
+    const float Gv = t + 1 < T ? Pv[i] * j1 * fast_rcp(fmaf(j1 * j1, Pv[i], 1.f)) : 0.f;
+    const float cv = mv[i] - Gv * fmaf(j1, mv[i], r1);
+    e[N - 1 - i] = t < T ? Aff1{Gv, cv} : aff_identity1();
+  }
+  Aff1 agg = e[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) agg = compose(e[i], agg);
+  const Aff1 incl = wave_inclusive_scan(agg, aff_identity1());
+  if (lane == 63) sh.btot[wid] = incl;
+  __syncthreads();
+  float dw = sh.bcarry;   // smoothed increment of the step after this wave's run
+  for (int w = 0; w < wid; ++w) dw = apply(sh.btot[w], dw);
+  float dl = wave_shr1(apply(incl, dw), dw);
+  float out[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    dl = apply(e[i], dl);   // D at step tb + N - 1 - i
+    out[N - 1 - i] = h[N - 1 - i] + dl;
+  }
+  store_n(Hnext + roff, tb, T, vec, N, out);
+  __syncthreads();
+  if (tid == PNR_BLOCK - 1) sh.bcarry = dl;   // D at the tile's first step
+  __syncthreads();
+}
+
+template <int N>
+__global__ void __launch_bounds__(PNR_BLOCK, 2) elk_gru_diag_kernel(ElkArgs a) {
+  __shared__ ElkShared sh;
+  __shared__ uint32_t s_wmax[PNR_WAVES];
+  Ctrl* ctrl = a.ctrl;
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  int cur = -1;
+  for (int k = 0; k <= a.max_iters; ++k) {
+    const bool resid_only = k == a.max_iters;
+    const int next = resid_only ? cur : (cur == 0 ? 1 : 0);
+    const float* Hcur = cur >= 0 ? a.H[cur] : nullptr;
+    float* Hnext = a.H[next < 0 ? 0 : next];
+    uint32_t blk_max = 0;
+    for (int row = blockIdx.x; row < a.n_rows; row += gridDim.x) {
+      if (tid == 0) sh.fcarry = V3{0.f, 1.f, 0.f};
+      __syncthreads();
+      for (int seg = 0; seg < a.tiles_per_row; ++seg) elk_forward_tile<N>(a, sh, row, seg, Hcur, blk_max);
+      if (resid_only) continue;
+      if (tid == 0) sh.bcarry = 0.f;
+      __syncthreads();
+      for (int seg = a.tiles_per_row - 1; seg >= 0; --seg) elk_backward_tile<N>(a, sh, row, seg, Hcur, Hnext);
+      if (has_fault(ctrl)) break;
+    }
+    blk_max = wave_max_u32(blk_max);
+    if (lane == 0) s_wmax[wid] = blk_max;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t m = s_wmax[0];
+      for (int w = 1; w < PNR_WAVES; ++w) m = max(m, s_wmax[w]);
+      __hip_atomic_store(&a.partials[blockIdx.x], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    grid_barrier(ctrl, [&]() {
+      uint32_t m = 0;
+      for (int i = tid; i < (int)gridDim.x; i += PNR_BLOCK)
+        m = max(m, __hip_atomic_load(&a.partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      m = wave_max_u32(m);
+      __syncthreads();
+      if (lane == 0) s_wmax[wid] = m;
+      __syncthreads();
+      if (tid == 0) {
+        for (int w = 0; w < PNR_WAVES; ++w) m = max(m, s_wmax[w]);
+        finish_iteration(ctrl, a.rho_hist, bits_to_rho(m), k, cur, a.max_iters, a.tol);
+      }
+    });
+    if (__hip_atomic_load(&ctrl->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) || has_fault(ctrl)) break;
+    cur = next;
+  }
+}
+
+constexpr int kElkN = 4;   // steps per thread (float4 loads per plane)
+
+int elk_items_per_thread() { return kElkN; }
+
+hipError_t launch_elk_gru_diag(const ElkArgs& a, int num_cu, hipStream_t st) {
+  const void* fn = (const void*)elk_gru_diag_kernel<kElkN>;
+  const int per_cu = cached_occupancy(fn, 0);
+  if (per_cu < 1) return hipErrorInvalidConfiguration;
+  long g = (long)per_cu * num_cu;
+  if (g > kMaxGrid) g = kMaxGrid;
+  if (g > a.n_rows) g = a.n_rows;
+  if (g < 1) g = 1;
+  void* args[] = {const_cast<ElkArgs*>(&a)};
+  return launch_persistent(fn, (int)g, 0, args, st);
+}
+
 }  // namespace pnr

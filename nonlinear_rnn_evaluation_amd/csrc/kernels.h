@@ -69,6 +69,31 @@ struct DiagLoopArgs {
   double tol;
 };
 
+// Damped (quasi-ELK) Newton loop for GRU_DIAG: one block walks a whole row (channel)
+// per pass, a forward (filter) and a backward (smoother) sweep over its tiles.
+struct ElkArgs {
+  const float* gx;     // [B][3][D][T]
+  const float* u;      // [3][D]
+  const float* bh;     // [3*D] or nullptr
+  const float* h0;     // [B][D] or nullptr
+  float* H[2];         // state buffers [B][D][T]
+  float* Pf;           // filtered variance, per step [B][D][T]
+  float* Mf;           // filtered mean
+  float* Jf;           // Jacobian (diagonal)
+  float* Rf;           // residual
+  uint32_t* partials;  // per-block residual maxima
+  Ctrl* ctrl;
+  double* rho_hist;
+  int B, D, T;
+  int tiles_per_row;
+  int n_rows;          // B * D
+  int max_iters, jac_mode;
+  double tol;
+  float lam;           // damping (> 0)
+};
+int elk_items_per_thread();
+hipError_t launch_elk_gru_diag(const ElkArgs& a, int num_cu, hipStream_t st);
+
 int diag_items_per_thread(int cell);
 int diag_slot_words(int cell);
 int diag_grid_capacity(int cell, int num_cu);

@@ -96,3 +96,20 @@ def test_scan_argument_checks():
     assert pnr.pnr_scan(1, 4, 100, 1, 2, 3, 300, 256, 1 << 20, None) == pnr.E_INVALID
     assert pnr.pnr_scan(1, 4, 100, 1, 2, 3, 0, None, 0, None) == pnr.E_WORKSPACE
     assert pnr.pnr_scan(1, 0, 100, 1, 2, 3, 0, None, 0, None) == pnr.OK
+
+
+def test_damped_requests_are_validated_without_a_gpu():
+    params = pnr.PnrParams(1024, 2048, None, None)
+    ok = _cell()
+    assert pnr.pnr_workspace_bytes_damped(ok, pnr.JAC_FULL) > pnr.pnr_workspace_bytes(ok, pnr.JAC_FULL)
+    # damping must be finite and positive
+    for lam in (0.0, -1.0, float("nan"), float("inf")):
+        assert pnr.pnr_eval_damped(ok, params, 4096, None, 8192, 10, 1e-5, pnr.JAC_FULL, lam) == pnr.E_INVALID
+    # only the diagonal GRU, with an exact or diagonal Jacobian, refreshed every iteration
+    for bad in (dict(kind=pnr.CELL_LSTM_DIAG), dict(kind=pnr.CELL_GRU, D=16), dict(jac_every=2)):
+        cell = _cell(**bad)
+        assert pnr.pnr_workspace_bytes_damped(cell, pnr.JAC_FULL) == 0
+        assert pnr.pnr_eval_damped(cell, params, 4096, None, 8192, 10, 1e-5, pnr.JAC_FULL, 0.5) == pnr.E_UNSUPPORTED
+    assert pnr.pnr_eval_damped(ok, params, 4096, None, 8192, 10, 1e-5, pnr.JAC_ZERO, 0.5) == pnr.E_UNSUPPORTED
+    # workspace missing
+    assert pnr.pnr_eval_damped(ok, params, 4096, None, 8192, 10, 1e-5, pnr.JAC_FULL, 0.5) in (pnr.E_WORKSPACE,)

@@ -1,0 +1,98 @@
+"""GPU parity of the damped (quasi-ELK) evaluation against the CPU oracle.
+
+The oracle's damped step (oracle.damped: Kalman filter + RTS smoother, itself pinned
+against the normal equations of the Levenberg-Marquardt step) is iterated with the same
+stopping rule as the HIP path.  Bars as for the undamped path: fp32 state against the
+fp64 oracle at max-abs 1e-4, per iteration and at convergence.  Sizes span several
+1024-step tiles with a ragged tail (the kernel's tile is 256 threads x 4 steps).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from nonlinear_rnn_evaluation_amd import pnr
+from nonlinear_rnn_evaluation_amd import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+CELL = WL.CELL_GRU_DIAG
+
+
+def _np(t):
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def _run(p, max_iters, tol, mode, lam):
+    d = {k: (None if v is None else v.to(DEV)) for k, v in p.items()}
+    return pnr.evaluate(CELL, d["W"], d["U"], d["x"], b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"],
+                        max_iters=max_iters, tol=tol, jac_mode=mode, damping=lam)
+
+
+def _f64(p):
+    return {k: WL.as_f64(v) for k, v in p.items()}
+
+
+def _problem(T, D=5, B=2, seed=0, x_dtype=WL.DT_F32):
+    return WL.random_problem(CELL, B, T, D, 3, seed=seed, x_dtype=x_dtype, state_dtype=WL.DT_F32,
+                             bias_std=0.2, h0_std=0.3)
+
+
+@pytest.mark.parametrize("T", [37, 1024, 2 * 1024 + 300])
+@pytest.mark.parametrize("mode", [WL.JAC_FULL, WL.JAC_DIAG])
+@pytest.mark.parametrize("lam", [0.05, 1.0])
+def test_fixed_iterations_match_damped_oracle(T, mode, lam):
+    p = _problem(T, seed=T % 97)
+    q = _f64(p)
+    print(f"# damped fixed iterations T={T} mode={mode} lam={lam}", flush=True)
+    got = _run(p, 3, -1.0, mode, lam)
+    ref = O.newton_dense(CELL, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], 3, -1.0, mode,
+                         solver="loop", damping=lam)
+    assert got["status"] == pnr.NOT_CONVERGED and got["iters"] == 3
+    np.testing.assert_allclose(_np(got["h"]), ref["states"], rtol=0, atol=1e-4)
+    np.testing.assert_allclose(got["history"], ref["rhos"], rtol=1e-3, atol=1e-5)
+
+
+def test_converged_damped_equals_sequential():
+    p = _problem(3000, D=7, B=3, seed=4)
+    q = _f64(p)
+    got = _run(p, 200, 1e-6, WL.JAC_FULL, 0.3)
+    assert got["status"] == pnr.OK, (got["status"], got["history"][-3:])
+    ref = O.sequential(CELL, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"])
+    assert np.abs(_np(got["h"]) - ref).max() < 1e-4
+    # damping costs iterations against the undamped step on the same problem
+    d = {k: (None if v is None else v.to(DEV)) for k, v in p.items()}
+    und = pnr.evaluate(CELL, d["W"], d["U"], d["x"], b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"],
+                       max_iters=200, tol=1e-6, jac_mode=WL.JAC_FULL)
+    assert und["status"] == pnr.OK and und["iters"] < got["iters"]
+
+
+def test_vanishing_damping_gives_the_newton_iterates():
+    p = _problem(1500, seed=9)
+    d = {k: (None if v is None else v.to(DEV)) for k, v in p.items()}
+    und = pnr.evaluate(CELL, d["W"], d["U"], d["x"], b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"],
+                       max_iters=2, tol=-1.0, jac_mode=WL.JAC_FULL)
+    got = _run(p, 2, -1.0, WL.JAC_FULL, 1e-7)
+    np.testing.assert_allclose(_np(got["h"]), _np(und["h"]), rtol=0, atol=1e-4)
+
+
+def test_bf16_inputs_and_zero_iterations():
+    p = _problem(1300, seed=2, x_dtype=WL.DT_BF16)
+    q = _f64(p)
+    got = _run(p, 2, -1.0, WL.JAC_DIAG, 0.5)
+    ref = O.newton_dense(CELL, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], 2, -1.0, WL.JAC_DIAG,
+                         solver="loop", damping=0.5)
+    np.testing.assert_allclose(_np(got["h"]), ref["states"], rtol=0, atol=1e-4)
+    zero = _run(p, 0, 1e-5, WL.JAC_DIAG, 0.5)
+    assert zero["iters"] == 0 and np.abs(_np(zero["h"])).max() == 0.0
+
+
+def test_damped_nonfinite_input_reports_nonfinite():
+    p = _problem(700, seed=3)
+    p["x"][1, 123, 2] = float("nan")
+    got = _run(p, 10, 1e-6, WL.JAC_FULL, 0.5)
+    assert got["status"] == pnr.NONFINITE and got["iters"] == 0
+    assert math.isinf(got["residual"])
