@@ -27,13 +27,15 @@ UNIT = "timesteps*batch/s"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0, "f64": 78.6}   # dense, published
 PRIMARY = "gru_quasi"
-DEFAULT_OTHERS = "tiny_gru,gru_full,gru_diag_long,lstm_diag_long,lstm_diag_long_stiff"
+DEFAULT_OTHERS = "tiny_gru,gru_full,gru_diag_long,lstm_diag_long,lstm_diag_long_stiff,gru_diag_long_elk"
 CSRC = "nonlinear_rnn_evaluation_amd/csrc/"
 
 
 def newton_kernel(w, mode):
     """(kernel name as the profiler lists it, source file) of the Newton loop kernel."""
     from nonlinear_rnn_evaluation_amd import workloads as WL
+    if w.damping is not None:
+        return "pnr::elk_gru_diag_kernel", CSRC + "diag_iter.hip"
     if w.cell in (WL.CELL_GRU_DIAG, WL.CELL_LSTM_DIAG):
         return "pnr::diag_newton_kernel", CSRC + "diag_iter.hip"
     full = mode == WL.JAC_FULL
@@ -60,6 +62,18 @@ def projection_fused(w, mode):
     from nonlinear_rnn_evaluation_amd import workloads as WL
     return (w.cell == WL.CELL_GRU and w.x_dtype == WL.DT_F32 and w.state_dtype == WL.DT_F32
             and mode != WL.JAC_FULL and w.D in (16, 32, 64))
+
+
+def damped_iteration_bytes(w, k, resid=False):
+    """Algorithmic HBM bytes of one pass of the damped (quasi-ELK) loop, per state element:
+    the forward sweep reads Gx (12 B) and the current iterate (4 B; not at k=0) and writes
+    the filter's P, m, J, r (16 B); the backward sweep reads them back (16 B) with the
+    current iterate (4 B; not at k=0) and writes the next iterate (4 B).  The
+    residual-only pass runs the forward sweep only."""
+    n = w.B * w.T * w.D
+    cur = 4 if k > 0 else 0
+    fwd = 12 + cur + 16
+    return n * (fwd if resid else fwd + 16 + cur + 4)
 
 
 def iteration_bytes(w, k, iters_total, resid=False):
@@ -131,7 +145,7 @@ def run_workload(name, steps, warmup, mode=None, with_cpu=True, cpu_budget=12.0,
     def call(ws=None, out=None):
         return pnr.evaluate(w.cell, d["W"], d["U"], d["x"], b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"],
                             max_iters=w.max_iters, tol=w.tol, jac_mode=mode, jac_every=w.jac_every,
-                            workspace=ws, h_out=out)
+                            workspace=ws, h_out=out, damping=w.damping)
 
     first = call()
     ws, out = first["workspace"], first["h"]
@@ -163,7 +177,10 @@ def run_workload(name, steps, warmup, mode=None, with_cpu=True, cpu_budget=12.0,
     newton_ms = sum(pp["newton_ms"] for pp in profs) / steps
     passes = profs[-1]["passes"]
     resid_last = profs[-1]["resid_only"]
-    bytes_call = sum(iteration_bytes(w, k, iters, resid=(resid_last and k == passes - 1)) for k in range(passes))
+    if w.damping is not None:
+        bytes_call = sum(damped_iteration_bytes(w, k, resid=(resid_last and k == passes - 1)) for k in range(passes))
+    else:
+        bytes_call = sum(iteration_bytes(w, k, iters, resid=(resid_last and k == passes - 1)) for k in range(passes))
     fused = projection_fused(w, mode)
     if fused:
         # the loop kernel also computes the projection: read x, write gx

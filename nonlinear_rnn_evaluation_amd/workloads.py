@@ -78,6 +78,7 @@ class Workload:
     tol: float = 1e-5
     max_iters: int = 64
     seed: int = 0
+    damping: Optional[float] = None   # set: the damped (quasi-ELK) step with this strength
 
     @property
     def G(self) -> int:
@@ -95,6 +96,7 @@ class Workload:
             "state_dtype": ["f64", "f32", "bf16"][self.state_dtype],
             "jac_modes": [["full", "diag", "zero"][m] for m in self.jac_modes],
             "jac_every": self.jac_every, "tol": self.tol, "max_iters": self.max_iters,
+            **({"damping": self.damping} if self.damping is not None else {}),
         }
 
 
@@ -118,6 +120,9 @@ def named_workloads() -> dict:
         "lstm_diag_long", CELL_LSTM_DIAG, B=1, T=131072, D=4096, D_in=4096, x_dtype=DT_BF16,
         state_dtype=DT_F32, w_init="glorot", u_init="uniform1", forget_bias=1.0,
         jac_modes=(JAC_FULL,), jac_every=2, tol=1e-4, max_iters=64)
+    # the long diagonal GRU with the damped (quasi-ELK) step; the strength is a swept
+    # hyperparameter: 0.01 still converges in 6 iterations (4 undamped), 0.1 takes 31
+    w["gru_diag_long_elk"] = dataclasses.replace(w["gru_diag_long"], name="gru_diag_long_elk", damping=0.01)
     w["lstm_diag_long_stiff"] = dataclasses.replace(
         w["lstm_diag_long"], name="lstm_diag_long_stiff", u_scale=3.0, max_iters=256,
         jac_modes=(JAC_FULL, JAC_DIAG))

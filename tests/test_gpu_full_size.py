@@ -1,7 +1,8 @@
 """Full-size parity: every named workload at its full shape, through the same C ABI call
 and launch configuration the benchmark times, against the fp64 sequential oracle.
 
-Dense-GRU workloads are compared on every output.  For the diagonal-recurrence cells a
+Dense-GRU workloads are compared on every output.  The damped (quasi-ELK) variant of the
+long diagonal GRU is included: it converges to the same trajectory.  For the diagonal-recurrence cells a
 set of evenly spaced channels is compared: with elementwise recurrent weights a channel
 subset is an exact sub-problem of its own (oracle.restrict_channels), so the oracle
 computes those outputs one channel group at a time.  Bar: 1e-4 max-abs for fp32 state,
@@ -25,7 +26,8 @@ def _check(name, mode):
     d = {k: (None if v is None else v.to("cuda")) for k, v in p.items()}
     print(f"# full-size parity: {name} mode {mode}", flush=True)
     res = pnr.evaluate(w.cell, d["W"], d["U"], d["x"], b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"],
-                       max_iters=w.max_iters, tol=w.tol, jac_mode=mode, jac_every=w.jac_every)
+                       max_iters=w.max_iters, tol=w.tol, jac_mode=mode, jac_every=w.jac_every,
+                       damping=w.damping)
     assert res["status"] == pnr.OK, (name, res["status"], res["residual"])
     assert 0 < res["iters"] <= w.max_iters
     assert res["residual"] <= w.tol
@@ -50,7 +52,8 @@ def _check(name, mode):
     assert err <= bar, (name, mode, err)
 
 
-CASES = [(name, mode) for name in WL.WORKLOAD_ORDER for mode in WL.get_workload(name).jac_modes]
+CASES = [(name, mode) for name in WL.WORKLOAD_ORDER + ["gru_diag_long_elk"]
+         for mode in WL.get_workload(name).jac_modes]
 
 
 @pytest.mark.parametrize("name,mode", CASES, ids=[f"{n}-{['full', 'diag', 'zero'][m]}" for n, m in CASES])
