@@ -284,3 +284,52 @@ def test_mfma_dense_diag_long_row_chains_lookback_windows(resident, monkeypatch)
                              WL.JAC_DIAG, 1, solver="loop")
         np.testing.assert_allclose(_np(got["h"]), ref["states"], rtol=0, atol=1e-4)
         np.testing.assert_allclose(got["history"], ref["rhos"], rtol=1e-3, atol=1e-5)
+
+
+@pytest.mark.parametrize("resident", ["64", "0"])
+@pytest.mark.parametrize("D_in", [100, 130])
+def test_fused_projection_with_wide_and_ragged_inputs(D_in, resident, monkeypatch):
+    """The quasi-Newton kernel computes its tiles' input projection itself (fp32 inputs):
+    inputs wider than one 64-feature chunk, a multiple of 4 (float4 loads, partial last
+    chunk) or not (scalar loads), over several tiles and a ragged tail."""
+    monkeypatch.setenv("PNR_DENSE_RESIDENT", resident)
+    D, T = 64, 2 * 128 + 45
+    p = WL.random_problem(WL.CELL_GRU, 3, T, D, D_in, seed=D_in, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32,
+                          bias_std=0.2, h0_std=0.3, w_std=0.5 / math.sqrt(D))
+    q = _f64(p)
+    for k in (0, 2):
+        got = _run(WL.CELL_GRU, p, k, -1.0, WL.JAC_DIAG)
+        ref = O.newton_dense(WL.CELL_GRU, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], k, -1.0,
+                             WL.JAC_DIAG, 1, solver="loop")
+        np.testing.assert_allclose(_np(got["h"]), ref["states"], rtol=0, atol=1e-4)
+        np.testing.assert_allclose(got["history"], ref["rhos"], rtol=1e-3, atol=1e-5)
+
+
+def test_cooperative_launch_mode_gives_the_same_result():
+    """PNR_COOPERATIVE=1 (read once per process) launches the persistent loops with
+    hipLaunchCooperativeKernel; run it in a child process and compare to the oracle."""
+    import os
+    import subprocess
+    import sys
+    script = r'''
+import sys, numpy as np, torch
+sys.path.insert(0, sys.argv[1])
+import oracle as O
+from nonlinear_rnn_evaluation_amd import pnr, workloads as WL
+for cell, mode, D in ((WL.CELL_GRU, WL.JAC_DIAG, 64), (WL.CELL_GRU_DIAG, WL.JAC_FULL, 6), (WL.CELL_GRU, WL.JAC_FULL, 16)):
+    p = WL.random_problem(cell, 2, 700, D, 5, seed=3, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32, bias_std=0.2,
+                          h0_std=0.3)
+    d = {k: (None if v is None else v.cuda()) for k, v in p.items()}
+    got = pnr.evaluate(cell, d["W"], d["U"], d["x"], b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"], max_iters=3, tol=-1.0,
+                       jac_mode=mode)
+    q = {k: WL.as_f64(v) for k, v in p.items()}
+    ref = O.newton_dense(cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], 3, -1.0, mode, solver="loop")
+    err = np.abs(got["h"].double().cpu().numpy() - ref["states"]).max()
+    assert err < 1e-4, (cell, err)
+print("cooperative ok")
+'''
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, PNR_COOPERATIVE="1")
+    out = subprocess.run([sys.executable, "-c", script, root], env=env, capture_output=True, text=True, timeout=240)
+    assert out.returncode == 0, out.stderr[-2000:]
+    assert "cooperative ok" in out.stdout
