@@ -305,6 +305,24 @@ def test_fused_projection_with_wide_and_ragged_inputs(D_in, resident, monkeypatc
         np.testing.assert_allclose(got["history"], ref["rhos"], rtol=1e-3, atol=1e-5)
 
 
+@pytest.mark.parametrize("cell,D,D_in", [(WL.CELL_GRU_DIAG, 100, 72), (WL.CELL_LSTM_DIAG, 70, 40),
+                                         (WL.CELL_GRU_DIAG, 128, 256)])
+def test_bf16_projection_over_several_column_tiles(cell, D, D_in):
+    """bf16 inputs with K a multiple of 8 take the MFMA GEMM for the projection: gate widths
+    (3D or 4D) spanning two or more 128/256-column tiles with a ragged last one, and rows
+    (B*T) spanning several 128-row tiles with a ragged tail."""
+    B, T = 3, 2 * 128 + 77
+    p = WL.random_problem(cell, B, T, D, D_in, seed=D + D_in, x_dtype=WL.DT_BF16, state_dtype=WL.DT_F32,
+                          bias_std=0.2, h0_std=0.3, w_std=1.0 / math.sqrt(D_in))
+    q = _f64(p)
+    for k in (1, 3):
+        got = _run(cell, p, k, -1.0, WL.JAC_FULL)
+        ref = O.newton_dense(cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], k, -1.0, WL.JAC_FULL, 1,
+                             solver="loop")
+        np.testing.assert_allclose(_np(got["h"]), ref["states"], rtol=0, atol=1e-4)
+        np.testing.assert_allclose(got["history"], ref["rhos"], rtol=1e-3, atol=1e-5)
+
+
 def test_cooperative_launch_mode_gives_the_same_result():
     """PNR_COOPERATIVE=1 (read once per process) launches the persistent loops with
     hipLaunchCooperativeKernel; run it in a child process and compare to the oracle."""
