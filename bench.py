@@ -65,15 +65,16 @@ def projection_fused(w, mode):
 
 
 def damped_iteration_bytes(w, k, resid=False):
-    """Algorithmic HBM bytes of one pass of the damped (quasi-ELK) loop, per state element:
-    the forward sweep reads Gx (12 B) and the current iterate (4 B; not at k=0) and writes
-    the filter's P, m, J, r (16 B); the backward sweep reads them back (16 B) with the
-    current iterate (4 B; not at k=0) and writes the next iterate (4 B).  The
-    residual-only pass runs the forward sweep only."""
-    n = w.B * w.T * w.D
-    cur = 4 if k > 0 else 0
-    fwd = 12 + cur + 16
-    return n * (fwd if resid else fwd + 16 + cur + 4)
+    """Algorithmic HBM bytes of one pass of the damped (quasi-ELK) loop: the forward sweep
+    reads the gate pre-activations (G fp32 per channel and step) and the current iterate
+    (4 B per state element; not at k=0) and writes the smoother's gain and offset (8 B per
+    state element); the backward sweep reads them back (8 B) and writes the next iterate
+    (4 B).  The residual-only pass runs the forward sweep's reads only."""
+    n_bt = w.B * w.T
+    gx = n_bt * w.G * w.D * 4
+    h = n_bt * w.S * 4
+    cur = h if k > 0 else 0
+    return gx + cur if resid else gx + cur + 5 * h
 
 
 def iteration_bytes(w, k, iters_total, resid=False):

@@ -154,14 +154,18 @@ const char* pnr_last_error(void);
  * strength is a hyperparameter).  Same iteration, stopping test and results as
  * pnr_eval, except that the update d minimises
  *     sum_t |d_t - J_t d_{t-1} - r_t|^2 + damping * sum_t |d_t|^2      (d_0 = 0)
- * instead of solving d_t = J_t d_{t-1} + r_t (damping -> 0 gives pnr_eval's step).  Per
- * channel this is a scalar Kalman filter (forward scan) and RTS smoother (backward scan).
- * The step is always taken (fixed damping, no adaptive trust region).
- * Supported: PNR_CELL_GRU_DIAG (whose exact Jacobian is diagonal) with jac_mode
- * PNR_JAC_FULL or PNR_JAC_DIAG, jac_every = 1, (x, state) as for pnr_eval; others
- * return PNR_E_UNSUPPORTED.  damping must be finite and > 0 (else PNR_E_INVALID).
- * Workspace: pnr_workspace_bytes_damped() bytes (the filter's per-step variance, mean,
- * Jacobian and residual take 16 bytes per state element more than pnr_eval).
+ * instead of solving d_t = J_t d_{t-1} + r_t (damping -> 0 gives pnr_eval's step).  With
+ * a diagonal J_t this splits into one scalar problem per state component, solved by a
+ * Kalman filter (forward scan) and RTS smoother (backward scan).  The step is always
+ * taken (fixed damping, no adaptive trust region).
+ * Supported, with jac_every = 1 and (x, state) as for pnr_eval:
+ *   PNR_CELL_GRU_DIAG, jac_mode PNR_JAC_FULL or PNR_JAC_DIAG (its exact Jacobian is
+ *     diagonal, so both are ELK);
+ *   PNR_CELL_LSTM_DIAG, jac_mode PNR_JAC_DIAG (quasi-ELK: the diagonal of the 2x2 block,
+ *     dc'/dc and dh'/dh, per channel; h_out holds (c, h) as for pnr_eval).
+ * Others return PNR_E_UNSUPPORTED.  damping must be finite and > 0 (else PNR_E_INVALID).
+ * Workspace: pnr_workspace_bytes_damped() bytes (the smoother's per-step gain and
+ * offset take 8 bytes per state element more than pnr_eval).
  */
 size_t pnr_workspace_bytes_damped(const pnr_cell* cell, int jac_mode);
 int pnr_eval_damped(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0,

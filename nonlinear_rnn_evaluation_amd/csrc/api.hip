@@ -434,15 +434,18 @@ namespace {
 int validate_damped(const pnr_cell* c, int jac_mode) {
   int rc = validate(c, jac_mode);
   if (rc) return rc;
-  if (c->kind != PNR_CELL_GRU_DIAG || jac_mode == PNR_JAC_ZERO)
-    return fail(PNR_E_UNSUPPORTED, "the damped step is implemented for GRU_DIAG with a full or diagonal Jacobian");
+  if (!(c->kind == PNR_CELL_GRU_DIAG && (jac_mode == PNR_JAC_FULL || jac_mode == PNR_JAC_DIAG)) &&
+      !(c->kind == PNR_CELL_LSTM_DIAG && jac_mode == PNR_JAC_DIAG))
+    return fail(PNR_E_UNSUPPORTED,
+                "the damped step is implemented for GRU_DIAG (full or diagonal Jacobian) and LSTM_DIAG (diagonal "
+                "Jacobian)");
   if (c->jac_every != 1) return fail(PNR_E_UNSUPPORTED, "the damped step needs jac_every = 1");
   return 0;
 }
-// pnr_eval's layout, plus four per-step planes of the filter (P, m, J, r)
+// pnr_eval's layout, plus two per-step planes of the smoother (gain, offset) per state component
 size_t damped_planes_offset(const Layout& l) { return l.total; }
 size_t damped_total(const pnr_cell* c, const Layout& l) {
-  return align_up(l.total + 4 * sizeof(float) * (size_t)c->B * c->T * c->D);
+  return align_up(l.total + 2 * sizeof(float) * (size_t)c->B * c->T * states(c->kind, c->D));
 }
 }  // namespace
 
@@ -482,14 +485,15 @@ int pnr_eval_damped(const pnr_cell* cell, const pnr_params* params, const void* 
   Ctrl* ctrl = reinterpret_cast<Ctrl*>(ws + l.ctrl);
   double* hist = reinterpret_cast<double*>(ws + l.hist);
   const int D = cell->D, T = cell->T, B = cell->B, Din = cell->D_in;
-  const size_t plane = (size_t)B * T * D;
+  const int G = gates(cell->kind), S = states(cell->kind, D);
+  const size_t plane = (size_t)B * T * S;
   float* planes = reinterpret_cast<float*>(ws + damped_planes_offset(l));
 
   Mark m_first = mark_begin(st);
   PNR_HIP(launch_init(ctrl, reinterpret_cast<uint64_t*>(ws + l.slots), l.slot_words,
                       reinterpret_cast<uint64_t*>(ws + l.partials), kPartialWords, st));
   // gx[b][m][t] = sum_k W[m][k] x[b][t][k] + b_x[m]
-  GemmArgs g{params->W, x, params->b_x, ws + l.gx, 3 * D, T, Din, 0, (long long)T * Din, (long long)3 * D * T,
+  GemmArgs g{params->W, x, params->b_x, ws + l.gx, G * D, T, Din, 0, (long long)T * Din, (long long)G * D * T,
              Din, Din, T, B, 1};
   Mark m_proj = mark_begin(st);
   PNR_HIP(launch_gemm(cell->x_dtype, cell->state_dtype, g, st));
@@ -502,10 +506,8 @@ int pnr_eval_damped(const pnr_cell* cell, const pnr_params* params, const void* 
   a.h0 = static_cast<const float*>(h0);
   a.H[0] = reinterpret_cast<float*>(ws + l.h[0]);
   a.H[1] = reinterpret_cast<float*>(ws + l.h[1]);
-  a.Pf = planes;
-  a.Mf = planes + plane;
-  a.Jf = planes + 2 * plane;
-  a.Rf = planes + 3 * plane;
+  a.Gs = planes;
+  a.Es = planes + plane;
   a.partials = reinterpret_cast<uint32_t*>(ws + l.partials);
   a.ctrl = ctrl;
   a.rho_hist = hist;
@@ -515,12 +517,12 @@ int pnr_eval_damped(const pnr_cell* cell, const pnr_params* params, const void* 
   a.max_iters = max_iters; a.jac_mode = jac_mode; a.tol = tol;
   a.lam = (float)damping;
   Mark m_newton = mark_begin(st);
-  PNR_HIP(launch_elk_gru_diag(a, num_cu, st));
+  PNR_HIP(launch_elk_diag(cell->kind, a, num_cu, st));
   mark_end(m_newton, st);
 
   Mark m_out = mark_begin(st);
   const float* bufs[3] = {a.H[0], a.H[1], nullptr};
-  PNR_HIP(launch_diag_output(bufs, ctrl, static_cast<float*>(h_out), B, D, T, st));
+  PNR_HIP(launch_diag_output(bufs, ctrl, static_cast<float*>(h_out), B, S, T, st));
   mark_end(m_out, st);
   mark_end(m_first, st);
   return finish_call(l, ws, max_iters, st, m_first, m_proj, m_newton, m_out);

@@ -713,27 +713,33 @@ hipError_t launch_diag_newton(int cell, const DiagLoopArgs& a, int grid, hipStre
 }
 
 // ---------------------------------------------------------------------------------
-// Damped (Levenberg-Marquardt) Newton step -- quasi-ELK -- for the GRU with elementwise
+// Damped (Levenberg-Marquardt) Newton step -- quasi-ELK -- for the cells with elementwise
 // recurrent weights ("Towards Scalable and Stable Parallelization of Nonlinear RNNs",
-// abstract and the summary's "Approach": a trust region whose linear-Gaussian MAP
-// solve is a Kalman filter and smoother; with the diagonal Jacobian, quasi-ELK).
+// abstract and the summary's "Approach": a trust region whose linear-Gaussian MAP solve
+// is a Kalman filter and smoother; with the diagonal Jacobian, quasi-ELK).
 //
-// Per channel the step D minimises sum_t (D_t - J_t D_{t-1} - r_t)^2 + lam sum_t D_t^2
-// (D_0 = 0), the smoothed mean of the scalar state-space model D_t = J_t D_{t-1} + r_t +
-// w_t (unit noise), 0 = D_t + v_t (noise variance 1/lam):
+// Each state component (the GRU's h; the LSTM's c and h, each with its own diagonal
+// Jacobian entry) is its own scalar problem: the step D minimises
+// sum_t (D_t - J_t D_{t-1} - r_t)^2 + lam sum_t D_t^2 (D_0 = 0), the smoothed mean of the
+// state-space model D_t = J_t D_{t-1} + r_t + w_t (unit noise), 0 = D_t + v_t (noise
+// variance 1/lam):
 //   filter:   P- = J^2 P + 1,  m- = J m + r,  P = P- / (1 + lam P-),  m = m- / (1 + lam P-)
 //   smoother: G_t = P_t J_{t+1} / P-_{t+1},  D_t = m_t + G_t (D_{t+1} - m-_{t+1}),  D_T = m_T.
 // In homogeneous coordinates (u, v, n) with P = u / v and m = n / v one filter step is
 // linear: u' = J^2 u + v, v' = lam J^2 u + (1 + lam) v, n' = r v + J n.  So the filter is
 // one associative scan of 3x3 maps [[a b 0][c d 0][e f g]] (7 numbers), started from
-// (0, 1, 0); the smoother is a scan of affine maps d -> G d + c run backwards in time.
+// (0, 1, 0).  The new iterate h'_t = h_t + D_t obeys
+//   h'_t = G_t h'_{t+1} + e_t,   e_t = m_t + h_t - G_t (m-_{t+1} + h_{t+1})
+// (G = 0 and e = m + h at the last step), so the forward sweep -- which has P, m of each
+// step and J, r, h of the step after it -- stores only G and e, and the backward sweep is
+// one affine scan of them run backwards in time that writes h' directly: two planes
+// written and read per component, and the current iterate is not read again.
 //
 // One block walks a whole row (channel): a forward sweep over its tiles evaluates the
-// cell, residual and Jacobian and runs the filter, storing P, m, J, r per step; a
-// backward sweep runs the smoother and writes the next iterate.  Tiles, thread-serial /
-// DPP / LDS scans and the carry between tiles are those of diag_newton_kernel; the
-// backward sweep maps thread t to the (255 - t)-th run of steps so that lane order is
-// reverse time and the same forward scan machinery applies.
+// cell, residual and Jacobian and runs the filter; a backward sweep runs the smoother.
+// Tiles, thread-serial / DPP / LDS scans and the carry between tiles are those of
+// diag_newton_kernel; the backward sweep maps thread t to the (255 - t)-th run of steps
+// so that lane order is reverse time and the same forward scan machinery applies.
 struct Flt {
   float a, b, c, d, e, f, g;
 };
@@ -786,147 +792,216 @@ __device__ __forceinline__ V3 wave_shr1(const V3& x, const V3& lane0) {
   return V3{wave_shr1(x.u, lane0.u), wave_shr1(x.v, lane0.v), wave_shr1(x.n, lane0.n)};
 }
 
+template <int K>   // state components per channel
 struct ElkShared {
-  Flt ftot[PNR_WAVES];
-  Aff1 btot[PNR_WAVES];
-  V3 fcarry;
-  float bcarry, jnext, rnext;
+  Flt ftot[K][PNR_WAVES];
+  Aff1 btot[K][PNR_WAVES];
+  float nj[K][PNR_WAVES], nr[K][PNR_WAVES], nh[K][PNR_WAVES];   // each wave's first step: J, r, state
+  V3 fcarry[K];      // filter state (P, 1, m) after the previous tile's last step
+  float bcarry[K];   // new iterate at the step after the tile (backward sweep)
 };
 
-// Forward sweep over one tile: cell, residual, Jacobian, filter; stores P, m, J, r.
-template <int N>
-__device__ __forceinline__ void elk_forward_tile(const ElkArgs& a, ElkShared& sh, int row, int seg, const float* Hcur,
-                                                 uint32_t& blk_max) {
-  using C = DiagCell<PNR_CELL_GRU_DIAG>;
+// Smoother coefficients of one step from its filtered P, m and state h, and the next
+// step's Jacobian j1, residual r1 and state h1 (last: the row's last step).
+__device__ __forceinline__ void elk_coeffs(float P, float m, float h, float j1, float r1, float h1, bool last,
+                                           float& G, float& e) {
+  if (last) {
+    G = 0.f;
+    e = m + h;
+  } else {
+    G = P * j1 * fast_rcp(fmaf(j1 * j1, P, 1.f));
+    e = (m + h) - G * (fmaf(j1, m, r1) + h1);
+  }
+}
+
+// Forward sweep over one tile: cell, residual, Jacobian, filter; stores G and e.
+template <int CELL, int N>
+__device__ __forceinline__ void elk_forward_tile(const ElkArgs& a, ElkShared<DiagCell<CELL>::SP>& sh, int b, int d,
+                                                 int seg, const float* Hcur, bool resid_only, uint32_t& blk_max) {
+  using C = DiagCell<CELL>;
+  constexpr int K = C::SP, NG = C::G;
   constexpr int TILE = PNR_BLOCK * N;
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
-  const int D = a.D, T = a.T;
+  const int D = a.D, T = a.T, S = K * D;
   const bool vec = (T & 3) == 0;
-  const int b = row / D, d = row - b * D;
   const int tb = seg * TILE + tid * N;
-  const size_t roff = (size_t)row * T;
-  const C::Par q = C::load_par(a.u, a.bh, D, d);
-  float g[3][N], h[N];
+  const typename C::Par q = C::load_par(a.u, a.bh, D, d);
+  size_t off[K];
 #pragma unroll
-  for (int gg = 0; gg < 3; ++gg) load_n(a.gx + ((size_t)(b * 3 + gg) * D + d) * T, tb, T, vec, N, g[gg]);
-  if (!Hcur) {
+  for (int k = 0; k < K; ++k) off[k] = ((size_t)b * S + k * D + d) * T;
+  float g[NG][N], h[K][N], p0[K];
 #pragma unroll
-    for (int i = 0; i < N; ++i) h[i] = 0.f;
-  } else {
-    load_n(Hcur + roff, tb, T, vec, N, h);
+  for (int gg = 0; gg < NG; ++gg) load_n(a.gx + ((size_t)(b * NG + gg) * D + d) * T, tb, T, vec, N, g[gg]);
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    if (!Hcur) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) h[k][i] = 0.f;
+    } else {
+      load_n(Hcur + off[k], tb, T, vec, N, h[k]);
+    }
+    // the state before the thread's first step: the previous lane's last one (DPP); lane 0
+    // of each wave loads it (this block wrote it, or it is h0 / the zero guess)
+    float v = 0.f;
+    if (lane == 0) {
+      if (tb == 0) v = a.h0 ? a.h0[(size_t)b * S + k * D + d] : 0.f;
+      else if (Hcur && tb <= T) v = Hcur[off[k] + tb - 1];
+    }
+    p0[k] = wave_shr1(h[k][N - 1], v);
   }
-  // the state before the thread's first step: the previous lane's last one (DPP); lane 0
-  // of each wave loads it (this block wrote it, or it is h0 / the zero guess)
-  float p0 = 0.f;
-  if (lane == 0) {
-    if (tb == 0) p0 = a.h0 ? a.h0[(size_t)b * D + d] : 0.f;
-    else if (Hcur && tb <= T) p0 = Hcur[roff + tb - 1];
-  }
-  p0 = wave_shr1(h[N - 1], p0);
-  const float lam = a.lam;
-  float jv[N], rv[N];
-  Flt F[N];
+  float jv[K][N], rv[K][N];
   uint32_t tmax = 0;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const float p = i == 0 ? p0 : h[i - 1];
-    float gi[3] = {g[0][i], g[1][i], g[2][i]};
-    float res, ja = 0.f;
-    C::eval(q, gi, p, h[i], a.jac_mode, true, res, ja);
     const bool in = tb + i < T;
-    res = in ? res : 0.f;
-    tmax = max(tmax, abs_bits(res));
-    jv[i] = ja;
-    rv[i] = res;
-    const float j2 = ja * ja;
-    F[i] = in ? Flt{j2, 1.f, lam * j2, 1.f + lam, 0.f, res, ja} : flt_identity();
+    float gi[NG];
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) gi[gg] = g[gg][i];
+    if constexpr (CELL == PNR_CELL_GRU_DIAG) {
+      float res, ja = 0.f;
+      C::eval(q, gi, i == 0 ? p0[0] : h[0][i - 1], h[0][i], a.jac_mode, true, res, ja);
+      rv[0][i] = in ? res : 0.f;
+      jv[0][i] = ja;
+    } else {
+      float rc, rh;
+      Aff2 J = aff_identity2();
+      C::eval(q, gi, i == 0 ? p0[0] : h[0][i - 1], i == 0 ? p0[1] : h[1][i - 1], h[0][i], h[1][i], PNR_JAC_DIAG,
+              true, rc, rh, J);
+      rv[0][i] = in ? rc : 0.f;
+      rv[1][i] = in ? rh : 0.f;
+      jv[0][i] = J.a00;
+      jv[1][i] = J.a11;
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) tmax = max(tmax, abs_bits(rv[k][i]));
   }
   blk_max = max(blk_max, tmax);
+  if (resid_only) return;   // uniform over the block
   // ---- filter scan: thread-serial, wave (DPP), block (LDS), carry ----
-  Flt agg = F[0];
+  const float lam = a.lam;
+  Flt F[K][N], incl[K];
 #pragma unroll
-  for (int i = 1; i < N; ++i) agg = compose(F[i], agg);
-  const Flt incl = wave_inclusive_scan(agg, flt_identity());
-  if (lane == 63) sh.ftot[wid] = incl;
-  __syncthreads();
-  V3 xw = sh.fcarry;   // vector entering this wave's first step
-  for (int w = 0; w < wid; ++w) xw = normalized(apply(sh.ftot[w], xw));
-  V3 x = wave_shr1(normalized(apply(incl, xw)), xw);   // entering this thread's first step
-  float Pv[N], mv[N];
+  for (int k = 0; k < K; ++k) {
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    x = normalized(apply(F[i], x));
-    Pv[i] = x.u;
-    mv[i] = x.n;
+    for (int i = 0; i < N; ++i) {
+      const float j2 = jv[k][i] * jv[k][i];
+      F[k][i] = tb + i < T ? Flt{j2, 1.f, lam * j2, 1.f + lam, 0.f, rv[k][i], jv[k][i]} : flt_identity();
+    }
+    Flt agg = F[k][0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) agg = compose(F[k][i], agg);
+    incl[k] = wave_inclusive_scan(agg, flt_identity());
+    if (lane == 63) sh.ftot[k][wid] = incl[k];
+    if (lane == 0) {
+      sh.nj[k][wid] = jv[k][0];
+      sh.nr[k][wid] = rv[k][0];
+      sh.nh[k][wid] = h[k][0];
+    }
   }
-  store_n(a.Pf + roff, tb, T, vec, N, Pv);
-  store_n(a.Mf + roff, tb, T, vec, N, mv);
-  store_n(a.Jf + roff, tb, T, vec, N, jv);
-  store_n(a.Rf + roff, tb, T, vec, N, rv);
-  __syncthreads();   // everyone has read ftot and fcarry
-  if (tid == PNR_BLOCK - 1) sh.fcarry = x;   // the last thread's last step: the next tile's carry
+  __syncthreads();
+  // the block's last step takes its coefficients in the next tile (thread 0 there), unless
+  // it is the row's last step
+  const int lim = (tid == PNR_BLOCK - 1 && tb + N < T) ? tb + N - 1 : T;
+  V3 xlast[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    V3 xw = sh.fcarry[k];   // filter state entering this wave's first step
+    // the previous tile's last step: filtered (P, m) = the carry, state = p0
+    float dG = 0.f, dE = 0.f;
+    if (tid == 0 && seg > 0) elk_coeffs(xw.u, xw.n, p0[k], jv[k][0], rv[k][0], h[k][0], false, dG, dE);
+    for (int w = 0; w < wid; ++w) xw = normalized(apply(sh.ftot[k][w], xw));
+    V3 x = wave_shr1(normalized(apply(incl[k], xw)), xw);   // entering this thread's first step
+    float Pv[N], mv[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      x = normalized(apply(F[k][i], x));
+      Pv[i] = x.u;
+      mv[i] = x.n;
+    }
+    xlast[k] = x;
+    // the step after the thread's last one: the next lane's first; lane 63 takes the next
+    // wave's first from LDS
+    float j1 = shfl_down_f(jv[k][0], 1), r1 = shfl_down_f(rv[k][0], 1), h1 = shfl_down_f(h[k][0], 1);
+    if (lane == 63 && wid + 1 < PNR_WAVES) {
+      j1 = sh.nj[k][wid + 1];
+      r1 = sh.nr[k][wid + 1];
+      h1 = sh.nh[k][wid + 1];
+    }
+    float Gv[N], Ev[N];
+#pragma unroll
+    for (int i = 0; i < N - 1; ++i)
+      elk_coeffs(Pv[i], mv[i], h[k][i], jv[k][i + 1], rv[k][i + 1], h[k][i + 1], tb + i + 1 >= T, Gv[i], Ev[i]);
+    elk_coeffs(Pv[N - 1], mv[N - 1], h[k][N - 1], j1, r1, h1, tb + N >= T, Gv[N - 1], Ev[N - 1]);
+    store_n(a.Gs + off[k], tb, lim, vec, N, Gv);
+    store_n(a.Es + off[k], tb, lim, vec, N, Ev);
+    if (tid == 0 && seg > 0) {
+      a.Gs[off[k] + tb - 1] = dG;
+      a.Es[off[k] + tb - 1] = dE;
+    }
+  }
+  __syncthreads();   // everyone has read ftot, nj / nr / nh and fcarry
+  if (tid == PNR_BLOCK - 1) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) sh.fcarry[k] = xlast[k];   // the next tile's carry
+  }
   __syncthreads();
 }
 
 // Backward sweep over one tile: smoother, next iterate.  Thread t takes the run of N
 // steps that starts at step (PNR_BLOCK - 1 - t) * N of the tile and walks it backwards.
-template <int N>
-__device__ __forceinline__ void elk_backward_tile(const ElkArgs& a, ElkShared& sh, int row, int seg, const float* Hcur,
+template <int K, int N>
+__device__ __forceinline__ void elk_backward_tile(const ElkArgs& a, ElkShared<K>& sh, int b, int d, int seg,
                                                   float* Hnext) {
   constexpr int TILE = PNR_BLOCK * N;
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
-  const int T = a.T;
+  const int D = a.D, T = a.T, S = K * D;
   const bool vec = (T & 3) == 0;
   const int tb = seg * TILE + (PNR_BLOCK - 1 - tid) * N;
-  const size_t roff = (size_t)row * T;
-  float Pv[N], mv[N], jv[N + 1], rv[N + 1], h[N];
-  load_n(a.Pf + roff, tb, T, vec, N, Pv);
-  load_n(a.Mf + roff, tb, T, vec, N, mv);
-  load_n(a.Jf + roff, tb, T, vec, N, jv);
-  load_n(a.Rf + roff, tb, T, vec, N, rv);
-  // J and r of the step after the run (the next run's first step; stored by the forward sweep)
-  jv[N] = tb + N < T ? a.Jf[roff + tb + N] : 0.f;
-  rv[N] = tb + N < T ? a.Rf[roff + tb + N] : 0.f;
-  if (!Hcur) {
+  Aff1 e[K][N], incl[K];
 #pragma unroll
-    for (int i = 0; i < N; ++i) h[i] = 0.f;
-  } else {
-    load_n(Hcur + roff, tb, T, vec, N, h);
+  for (int k = 0; k < K; ++k) {
+    const size_t off = ((size_t)b * S + k * D + d) * T;
+    float Gv[N], Ev[N];
+    load_n(a.Gs + off, tb, T, vec, N, Gv);
+    load_n(a.Es + off, tb, T, vec, N, Ev);
+    // h'_t = G_t h'_{t+1} + e_t, latest step first
+#pragma unroll
+    for (int i = 0; i < N; ++i) e[k][N - 1 - i] = tb + i < T ? Aff1{Gv[i], Ev[i]} : aff_identity1();
+    Aff1 agg = e[k][0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) agg = compose(e[k][i], agg);
+    incl[k] = wave_inclusive_scan(agg, aff_identity1());
+    if (lane == 63) sh.btot[k][wid] = incl[k];
   }
-  // smoother maps, latest step first: D_t = G_t D_{t+1} + c_t
-  Aff1 e[N];
-#pragma unroll
-  for (int i = N - 1; i >= 0; --i) {
-    const int t = tb + i;
-    const float j1 = jv[i + 1], r1 = rv[i + 1];
-    const float Gv = t + 1 < T ? Pv[i] * j1 * fast_rcp(fmaf(j1 * j1, Pv[i], 1.f)) : 0.f;
-    const float cv = mv[i] - Gv * fmaf(j1, mv[i], r1);
-    e[N - 1 - i] = t < T ? Aff1{Gv, cv} : aff_identity1();
-  }
-  Aff1 agg = e[0];
-#pragma unroll
-  for (int i = 1; i < N; ++i) agg = compose(e[i], agg);
-  const Aff1 incl = wave_inclusive_scan(agg, aff_identity1());
-  if (lane == 63) sh.btot[wid] = incl;
   __syncthreads();
-  float dw = sh.bcarry;   // smoothed increment of the step after this wave's run
-  for (int w = 0; w < wid; ++w) dw = apply(sh.btot[w], dw);
-  float dl = wave_shr1(apply(incl, dw), dw);
-  float out[N];
+  float first[K];
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    dl = apply(e[i], dl);   // D at step tb + N - 1 - i
-    out[N - 1 - i] = h[N - 1 - i] + dl;
+  for (int k = 0; k < K; ++k) {
+    const size_t off = ((size_t)b * S + k * D + d) * T;
+    float hw = sh.bcarry[k];   // new iterate at the step after this wave's runs
+    for (int w = 0; w < wid; ++w) hw = apply(sh.btot[k][w], hw);
+    float hl = wave_shr1(apply(incl[k], hw), hw);
+    float out[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      hl = apply(e[k][i], hl);   // step tb + N - 1 - i
+      out[N - 1 - i] = hl;
+    }
+    store_n(Hnext + off, tb, T, vec, N, out);
+    first[k] = hl;
   }
-  store_n(Hnext + roff, tb, T, vec, N, out);
   __syncthreads();
-  if (tid == PNR_BLOCK - 1) sh.bcarry = dl;   // D at the tile's first step
+  if (tid == PNR_BLOCK - 1) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) sh.bcarry[k] = first[k];   // the tile's first step
+  }
   __syncthreads();
 }
 
-template <int N>
-__global__ void __launch_bounds__(PNR_BLOCK, 2) elk_gru_diag_kernel(ElkArgs a) {
-  __shared__ ElkShared sh;
+template <int CELL, int N>
+__global__ void __launch_bounds__(PNR_BLOCK, 2) elk_diag_kernel(ElkArgs a) {
+  constexpr int K = DiagCell<CELL>::SP;
+  __shared__ ElkShared<K> sh;
   __shared__ uint32_t s_wmax[PNR_WAVES];
   Ctrl* ctrl = a.ctrl;
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
@@ -938,14 +1013,22 @@ __global__ void __launch_bounds__(PNR_BLOCK, 2) elk_gru_diag_kernel(ElkArgs a) {
     float* Hnext = a.H[next < 0 ? 0 : next];
     uint32_t blk_max = 0;
     for (int row = blockIdx.x; row < a.n_rows; row += gridDim.x) {
-      if (tid == 0) sh.fcarry = V3{0.f, 1.f, 0.f};
+      const int b = row / a.D, d = row - b * a.D;
+      if (tid == 0) {
+#pragma unroll
+        for (int c = 0; c < K; ++c) sh.fcarry[c] = V3{0.f, 1.f, 0.f};
+      }
       __syncthreads();
-      for (int seg = 0; seg < a.tiles_per_row; ++seg) elk_forward_tile<N>(a, sh, row, seg, Hcur, blk_max);
+      for (int seg = 0; seg < a.tiles_per_row; ++seg)
+        elk_forward_tile<CELL, N>(a, sh, b, d, seg, Hcur, resid_only, blk_max);
       if (resid_only) continue;
-      if (tid == 0) sh.bcarry = 0.f;
+      if (tid == 0) {
+#pragma unroll
+        for (int c = 0; c < K; ++c) sh.bcarry[c] = 0.f;
+      }
       __syncthreads();
-      for (int seg = a.tiles_per_row - 1; seg >= 0; --seg) elk_backward_tile<N>(a, sh, row, seg, Hcur, Hnext);
-      if (has_fault(ctrl)) break;
+      for (int seg = a.tiles_per_row - 1; seg >= 0; --seg) elk_backward_tile<K, N>(a, sh, b, d, seg, Hnext);
+      if (__syncthreads_or(has_fault(ctrl))) break;   // the same decision in every wave
     }
     blk_max = wave_max_u32(blk_max);
     if (lane == 0) s_wmax[wid] = blk_max;
@@ -977,8 +1060,9 @@ constexpr int kElkN = 4;   // steps per thread (float4 loads per plane)
 
 int elk_items_per_thread() { return kElkN; }
 
-hipError_t launch_elk_gru_diag(const ElkArgs& a, int num_cu, hipStream_t st) {
-  const void* fn = (const void*)elk_gru_diag_kernel<kElkN>;
+hipError_t launch_elk_diag(int cell, const ElkArgs& a, int num_cu, hipStream_t st) {
+  const void* fn = cell == PNR_CELL_GRU_DIAG ? (const void*)elk_diag_kernel<PNR_CELL_GRU_DIAG, kElkN>
+                                             : (const void*)elk_diag_kernel<PNR_CELL_LSTM_DIAG, kElkN>;
   const int per_cu = cached_occupancy(fn, 0);
   if (per_cu < 1) return hipErrorInvalidConfiguration;
   long g = (long)per_cu * num_cu;

@@ -69,18 +69,17 @@ struct DiagLoopArgs {
   double tol;
 };
 
-// Damped (quasi-ELK) Newton loop for GRU_DIAG: one block walks a whole row (channel)
-// per pass, a forward (filter) and a backward (smoother) sweep over its tiles.
+// Damped (quasi-ELK) Newton loop for GRU_DIAG and LSTM_DIAG (G gates, S = D or 2D state
+// components per batch element): one block walks a whole row (channel) per pass, a
+// forward (filter) and a backward (smoother) sweep over its tiles.
 struct ElkArgs {
-  const float* gx;     // [B][3][D][T]
-  const float* u;      // [3][D]
-  const float* bh;     // [3*D] or nullptr
-  const float* h0;     // [B][D] or nullptr
-  float* H[2];         // state buffers [B][D][T]
-  float* Pf;           // filtered variance, per step [B][D][T]
-  float* Mf;           // filtered mean
-  float* Jf;           // Jacobian (diagonal)
-  float* Rf;           // residual
+  const float* gx;     // [B][G][D][T]
+  const float* u;      // [G][D]
+  const float* bh;     // [G*D] or nullptr
+  const float* h0;     // [B][S] or nullptr
+  float* H[2];         // state buffers [B][S][T]
+  float* Gs;           // smoother gain per step [B][S][T]
+  float* Es;           // smoother offset per step, in new-iterate space [B][S][T]
   uint32_t* partials;  // per-block residual maxima
   Ctrl* ctrl;
   double* rho_hist;
@@ -92,7 +91,7 @@ struct ElkArgs {
   float lam;           // damping (> 0)
 };
 int elk_items_per_thread();
-hipError_t launch_elk_gru_diag(const ElkArgs& a, int num_cu, hipStream_t st);
+hipError_t launch_elk_diag(int cell, const ElkArgs& a, int num_cu, hipStream_t st);
 
 int diag_items_per_thread(int cell);
 int diag_slot_words(int cell);

@@ -126,6 +126,11 @@ def named_workloads() -> dict:
     w["lstm_diag_long_stiff"] = dataclasses.replace(
         w["lstm_diag_long"], name="lstm_diag_long_stiff", u_scale=3.0, max_iters=256,
         jac_modes=(JAC_FULL, JAC_DIAG))
+    # the stiff LSTM with the damped step on the diagonal Jacobian (quasi-ELK), which
+    # converges where both undamped variants do not
+    w["lstm_diag_long_stiff_elk"] = dataclasses.replace(
+        w["lstm_diag_long_stiff"], name="lstm_diag_long_stiff_elk", jac_modes=(JAC_DIAG,), jac_every=1,
+        damping=0.01)
     return w
 
 

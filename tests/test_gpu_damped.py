@@ -4,7 +4,10 @@ The oracle's damped step (oracle.damped: Kalman filter + RTS smoother, itself pi
 against the normal equations of the Levenberg-Marquardt step) is iterated with the same
 stopping rule as the HIP path.  Bars as for the undamped path: fp32 state against the
 fp64 oracle at max-abs 1e-4, per iteration and at convergence.  Sizes span several
-1024-step tiles with a ragged tail (the kernel's tile is 256 threads x 4 steps).
+1024-step tiles with a ragged tail (the kernel's tile is 256 threads x 4 steps); a tile's
+last step takes its smoother coefficients from the next tile's first, so lengths one past
+a tile boundary are covered too.  The diagonal LSTM runs quasi-ELK (diagonal of its 2x2
+Jacobian): two scalar filters per channel, for c and for h.
 """
 import math
 
@@ -26,9 +29,9 @@ def _np(t):
     return t.detach().to("cpu").to(torch.float64).numpy()
 
 
-def _run(p, max_iters, tol, mode, lam):
+def _run(p, max_iters, tol, mode, lam, cell=CELL):
     d = {k: (None if v is None else v.to(DEV)) for k, v in p.items()}
-    return pnr.evaluate(CELL, d["W"], d["U"], d["x"], b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"],
+    return pnr.evaluate(cell, d["W"], d["U"], d["x"], b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"],
                         max_iters=max_iters, tol=tol, jac_mode=mode, damping=lam)
 
 
@@ -36,8 +39,8 @@ def _f64(p):
     return {k: WL.as_f64(v) for k, v in p.items()}
 
 
-def _problem(T, D=5, B=2, seed=0, x_dtype=WL.DT_F32):
-    return WL.random_problem(CELL, B, T, D, 3, seed=seed, x_dtype=x_dtype, state_dtype=WL.DT_F32,
+def _problem(T, D=5, B=2, seed=0, x_dtype=WL.DT_F32, cell=CELL):
+    return WL.random_problem(cell, B, T, D, 3, seed=seed, x_dtype=x_dtype, state_dtype=WL.DT_F32,
                              bias_std=0.2, h0_std=0.3)
 
 
@@ -96,3 +99,46 @@ def test_damped_nonfinite_input_reports_nonfinite():
     got = _run(p, 10, 1e-6, WL.JAC_FULL, 0.5)
     assert got["status"] == pnr.NONFINITE and got["iters"] == 0
     assert math.isinf(got["residual"])
+
+
+LSTM = WL.CELL_LSTM_DIAG
+
+
+@pytest.mark.parametrize("T", [1, 37, 1023, 1025, 2 * 1024 + 300])
+@pytest.mark.parametrize("lam", [0.05, 1.0])
+def test_lstm_fixed_iterations_match_damped_oracle(T, lam):
+    p = _problem(T, D=4, seed=T % 89, cell=LSTM)
+    q = _f64(p)
+    print(f"# damped LSTM fixed iterations T={T} lam={lam}", flush=True)
+    got = _run(p, 3, -1.0, WL.JAC_DIAG, lam, cell=LSTM)
+    ref = O.newton_dense(LSTM, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], 3, -1.0, WL.JAC_DIAG,
+                         solver="loop", damping=lam)
+    assert got["status"] == pnr.NOT_CONVERGED and got["iters"] == 3
+    np.testing.assert_allclose(_np(got["h"]), ref["states"], rtol=0, atol=1e-4)
+    np.testing.assert_allclose(got["history"], ref["rhos"], rtol=1e-3, atol=1e-5)
+
+
+def test_lstm_damped_step_matches_normal_equations():
+    """One damped step from the zero guess against the Levenberg-Marquardt normal equations
+    solved densely (a short sequence, so the dense solve stays small)."""
+    p = _problem(150, D=3, B=2, seed=21, cell=LSTM)
+    q = _f64(p)
+    got = _run(p, 1, -1.0, WL.JAC_DIAG, 0.3, cell=LSTM)
+    ref = O.newton_dense(LSTM, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], 1, -1.0, WL.JAC_DIAG,
+                         solver="dense", damping=0.3)
+    np.testing.assert_allclose(_np(got["h"]), ref["states"], rtol=0, atol=1e-4)
+
+
+def test_lstm_converged_damped_equals_sequential():
+    p = _problem(2500, D=6, B=3, seed=5, cell=LSTM)
+    q = _f64(p)
+    got = _run(p, 300, 1e-6, WL.JAC_DIAG, 0.2, cell=LSTM)
+    assert got["status"] == pnr.OK, (got["status"], got["history"][-3:])
+    ref = O.sequential(LSTM, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"])
+    assert np.abs(_np(got["h"]) - ref).max() < 1e-4
+
+
+def test_lstm_damped_rejects_the_full_jacobian():
+    p = _problem(64, D=2, cell=LSTM)
+    with pytest.raises(pnr.PnrError):
+        _run(p, 2, -1.0, WL.JAC_FULL, 0.5, cell=LSTM)
