@@ -12,6 +12,7 @@ quasi-Newton Jacobians, B=8, T=4096) it reports the other named workloads under
 "others", each with its own roofline and parity numbers.
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -27,7 +28,8 @@ UNIT = "timesteps*batch/s"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0, "f64": 78.6}   # dense, published
 PRIMARY = "gru_quasi"
-DEFAULT_OTHERS = "tiny_gru,gru_full,gru_diag_long,lstm_diag_long,lstm_diag_long_stiff,gru_diag_long_elk"
+DEFAULT_OTHERS = ("tiny_gru,gru_full,gru_diag_long,lstm_diag_long,lstm_diag_long_chunked,lstm_diag_long_stiff,"
+                  "gru_diag_long_elk")
 CSRC = "nonlinear_rnn_evaluation_amd/csrc/"
 
 
@@ -35,7 +37,7 @@ def newton_kernel(w, mode):
     """(kernel name as the profiler lists it, source file) of the Newton loop kernel."""
     from nonlinear_rnn_evaluation_amd import workloads as WL
     if w.damping is not None:
-        return "pnr::elk_gru_diag_kernel", CSRC + "diag_iter.hip"
+        return "pnr::elk_diag_kernel", CSRC + "diag_iter.hip"
     if w.cell in (WL.CELL_GRU_DIAG, WL.CELL_LSTM_DIAG):
         return "pnr::diag_newton_kernel", CSRC + "diag_iter.hip"
     full = mode == WL.JAC_FULL
@@ -75,6 +77,25 @@ def damped_iteration_bytes(w, k, resid=False):
     h = n_bt * w.S * 4
     cur = h if k > 0 else 0
     return gx + cur if resid else gx + cur + 5 * h
+
+
+def chunk_iterations(history, w, n_chunks):
+    """Iterations of each chunk of a chunked call, read off the concatenated residual
+    history: a chunk's history ends at the first residual within tol, at a non-finite one,
+    or after max_iters + 1 values."""
+    out, i = [], 0
+    for _ in range(n_chunks):
+        k = 0
+        while True:
+            v = history[i + k]
+            if not math.isfinite(v) or v <= w.tol or k == w.max_iters:
+                break
+            k += 1
+        out.append(k)
+        i += k + 1
+        if i >= len(history):
+            break
+    return out
 
 
 def iteration_bytes(w, k, iters_total, resid=False):
@@ -146,7 +167,7 @@ def run_workload(name, steps, warmup, mode=None, with_cpu=True, cpu_budget=12.0,
     def call(ws=None, out=None):
         return pnr.evaluate(w.cell, d["W"], d["U"], d["x"], b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"],
                             max_iters=w.max_iters, tol=w.tol, jac_mode=mode, jac_every=w.jac_every,
-                            workspace=ws, h_out=out, damping=w.damping)
+                            workspace=ws, h_out=out, damping=w.damping, chunk_len=w.chunk_len)
 
     first = call()
     ws, out = first["workspace"], first["h"]
@@ -178,7 +199,17 @@ def run_workload(name, steps, warmup, mode=None, with_cpu=True, cpu_budget=12.0,
     newton_ms = sum(pp["newton_ms"] for pp in profs) / steps
     passes = profs[-1]["passes"]
     resid_last = profs[-1]["resid_only"]
-    if w.damping is not None:
+    launches = 1
+    if w.chunk_len is not None:
+        # one launch per chunk; each chunk's passes from its part of the residual history
+        per_chunk = chunk_iterations(last["history"], w, len(range(0, w.T, w.chunk_len)))
+        launches = len(per_chunk)
+        bytes_call = 0
+        for t0, it in zip(range(0, w.T, w.chunk_len), per_chunk):
+            wc = dataclasses.replace(w, T=min(w.chunk_len, w.T - t0))
+            ro = it == w.max_iters
+            bytes_call += sum(iteration_bytes(wc, k, it, resid=(ro and k == it)) for k in range(it + 1))
+    elif w.damping is not None:
         bytes_call = sum(damped_iteration_bytes(w, k, resid=(resid_last and k == passes - 1)) for k in range(passes))
     else:
         bytes_call = sum(iteration_bytes(w, k, iters, resid=(resid_last and k == passes - 1)) for k in range(passes))
@@ -195,8 +226,9 @@ def run_workload(name, steps, warmup, mode=None, with_cpu=True, cpu_budget=12.0,
             pmc = json.load(f)
         if pmc.get("kernel_src_sha") == src_hash(ksrc) and pmc.get("jac_mode") == mode:
             traffic = pmc.get("bytes_per_launch")
-    common = {"kernel": kname, "avg_launch_us": round(newton_ms * 1e3, 3), "launches_per_step": 1,
-              "passes_per_launch": passes, "us_per_pass": round(newton_ms * 1e3 / max(passes, 1), 3)}
+    common = {"kernel": kname, "avg_launch_us": round(newton_ms * 1e3 / launches, 3), "launches_per_step": launches,
+              "passes_per_launch": round(passes / launches, 3),
+              "us_per_pass": round(newton_ms * 1e3 / max(passes, 1), 3)}
     hbm = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
            "algorithmic_bytes_per_launch": bytes_call}

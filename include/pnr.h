@@ -42,7 +42,8 @@
  * Jacobian recomputed only every few steps); the residual is always fresh.
  *
  * Memory and layout.  Every tensor argument is a DEVICE pointer, row-major, owned by
- * the caller and not retained after the call returns:
+ * the caller and not retained after the call returns (x and h_out may be NULL when
+ * T = 0):
  *   x      [B, T, D_in]            x_dtype
  *   h0     [B, S]                  state_dtype (may be NULL: zeros)
  *   h_out  [B, T, S]               state_dtype; h_out[b, t] = s_{t+1}; h0 excluded
@@ -170,6 +171,32 @@ const char* pnr_last_error(void);
 size_t pnr_workspace_bytes_damped(const pnr_cell* cell, int jac_mode);
 int pnr_eval_damped(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0,
                     void* h_out, int max_iters, double tol, int jac_mode, double damping);
+
+/*
+ * Chunked evaluation (ParaRNN overview page, "Experimental Results", on long sequences:
+ * the memory that stored hidden states take during the Newton iteration is kept in check
+ * by chunking, together with gradient checkpointing).  The sequence is cut into consecutive
+ * chunks of chunk_len steps (the last may be shorter).  Chunk c is evaluated exactly as
+ * pnr_eval (damping == 0) or pnr_eval_damped (damping > 0) evaluates a sequence of its
+ * length, with the same max_iters, tol and jac_mode per chunk, and with initial state
+ * h0 for the first chunk and, for the others, the returned state at the previous chunk's
+ * last step (h_out[b, t0 - 1]).  At convergence the result is the sequential one within
+ * the tolerance, as for pnr_eval; the workspace covers one chunk instead of the whole
+ * sequence (plus, for B > 1 with more than one chunk, contiguous staging of the chunk's
+ * x, boundary state and output, copied on the stream).
+ * Arguments and layouts as for pnr_eval / pnr_eval_damped; chunk_len >= 1; damping
+ * finite and >= 0.  Results: the worst status over chunks (NONFINITE > NOT_CONVERGED >
+ * OK; after a NONFINITE chunk the later chunks are not evaluated and their h_out
+ * entries are left as they were); pnr_iters_used() = the sum of the chunks' iterations;
+ * pnr_last_residual() = the largest final rho; pnr_last_residual_history() = the chunks'
+ * histories one after another; in measurement mode (pnr_profile_enable) the profile
+ * record holds sums over the chunks (resid_only: the number of chunks whose last pass
+ * only evaluated the residual).  Synchronises the stream before returning.
+ * pnr_workspace_bytes_chunked returns 0 for an invalid or unsupported request.
+ */
+size_t pnr_workspace_bytes_chunked(const pnr_cell* cell, int jac_mode, double damping, int chunk_len);
+int pnr_eval_chunked(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0,
+                     void* h_out, int max_iters, double tol, int jac_mode, double damping, int chunk_len);
 
 /*
  * Standalone linear solve used inside every Newton iteration, exposed for testing

@@ -271,7 +271,8 @@ int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, cons
   int rc = validate(cell, jac_mode);
   if (rc) return rc;
   if (!params) return fail(PNR_E_INVALID, "params is NULL");
-  if (!x || !h_out || !params->W || !params->U) return fail(PNR_E_INVALID, "x, h_out, W and U must be non-NULL");
+  if (!params->W || !params->U || (cell->T > 0 && (!x || !h_out)))
+    return fail(PNR_E_INVALID, "W, U and (for T > 0) x and h_out must be non-NULL");
   if (max_iters < 0 || max_iters >= PNR_MAX_ITERS)
     return fail(PNR_E_INVALID, "max_iters must be in [0, %d)", PNR_MAX_ITERS);
   if (isnan(tol)) return fail(PNR_E_INVALID, "tol is NaN");
@@ -458,10 +459,12 @@ int pnr_eval_damped(const pnr_cell* cell, const pnr_params* params, const void* 
                     int max_iters, double tol, int jac_mode, double damping) {
   g_last = LastCall();
   g_prof.valid = false;
+  g_prof.used = 0;
   int rc = validate_damped(cell, jac_mode);
   if (rc) return rc;
   if (!params) return fail(PNR_E_INVALID, "params is NULL");
-  if (!x || !h_out || !params->W || !params->U) return fail(PNR_E_INVALID, "x, h_out, W and U must be non-NULL");
+  if (!params->W || !params->U || (cell->T > 0 && (!x || !h_out)))
+    return fail(PNR_E_INVALID, "W, U and (for T > 0) x and h_out must be non-NULL");
   if (max_iters < 0 || max_iters >= PNR_MAX_ITERS)
     return fail(PNR_E_INVALID, "max_iters must be in [0, %d)", PNR_MAX_ITERS);
   if (isnan(tol)) return fail(PNR_E_INVALID, "tol is NaN");
@@ -526,6 +529,126 @@ int pnr_eval_damped(const pnr_cell* cell, const pnr_params* params, const void* 
   mark_end(m_out, st);
   mark_end(m_first, st);
   return finish_call(l, ws, max_iters, st, m_first, m_proj, m_newton, m_out);
+}
+
+// ---- chunked evaluation ----
+namespace {
+// The per-chunk problem, its workspace, and (for B > 1 with several chunks) contiguous
+// staging for the chunk's inputs, boundary state and output behind it.
+struct ChunkPlan {
+  int L = 0;              // chunk length (steps)
+  bool staged = false;
+  pnr_cell sub{};         // the problem of one chunk (T = L)
+  size_t sub_bytes = 0, x_off = 0, h0_off = 0, out_off = 0, total = 0;
+};
+int plan_chunks(const pnr_cell* c, int jac_mode, double damping, int chunk_len, ChunkPlan& p) {
+  if (!c) return fail(PNR_E_INVALID, "cell descriptor is NULL");
+  if (chunk_len < 1) return fail(PNR_E_INVALID, "chunk_len must be >= 1 (got %d)", chunk_len);
+  if (!(damping >= 0.0) || !(damping < 1e30)) return fail(PNR_E_INVALID, "damping must be finite and >= 0");
+  if (c->T < 0) return fail(PNR_E_INVALID, "T must be >= 0 (got %d)", c->T);
+  p.L = c->T < chunk_len ? c->T : chunk_len;
+  p.sub = *c;
+  p.sub.T = p.L;
+  const int rc = damping > 0 ? validate_damped(&p.sub, jac_mode) : validate(&p.sub, jac_mode);
+  if (rc) return rc;
+  const Layout l = make_layout(&p.sub, jac_mode);
+  p.sub_bytes = damping > 0 ? damped_total(&p.sub, l) : l.total;
+  p.staged = c->B > 1 && c->T > p.L;
+  size_t off = align_up(p.sub_bytes);
+  if (p.staged) {
+    const size_t B = c->B, L = p.L, S = states(c->kind, c->D);
+    p.x_off = off; off = align_up(off + B * L * c->D_in * dsize(c->x_dtype));
+    p.h0_off = off; off = align_up(off + B * S * dsize(c->state_dtype));
+    p.out_off = off; off = align_up(off + B * L * S * dsize(c->state_dtype));
+  }
+  p.total = off;
+  return 0;
+}
+int status_rank(int s) { return s == PNR_NONFINITE ? 2 : (s == PNR_NOT_CONVERGED ? 1 : 0); }
+}  // namespace
+
+size_t pnr_workspace_bytes_chunked(const pnr_cell* cell, int jac_mode, double damping, int chunk_len) {
+  ChunkPlan p;
+  if (plan_chunks(cell, jac_mode, damping, chunk_len, p) != 0) return 0;
+  return p.total;
+}
+
+int pnr_eval_chunked(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, void* h_out,
+                     int max_iters, double tol, int jac_mode, double damping, int chunk_len) {
+  g_last = LastCall();
+  g_prof.valid = false;
+  ChunkPlan p;
+  int rc = plan_chunks(cell, jac_mode, damping, chunk_len, p);
+  if (rc) return rc;
+  if (!params) return fail(PNR_E_INVALID, "params is NULL");
+  if (!params->W || !params->U || (cell->T > 0 && (!x || !h_out)))
+    return fail(PNR_E_INVALID, "W, U and (for T > 0) x and h_out must be non-NULL");
+  if (!cell->workspace) return fail(PNR_E_WORKSPACE, "workspace is NULL (%zu bytes required)", p.total);
+  if ((uintptr_t)cell->workspace % 256) return fail(PNR_E_WORKSPACE, "workspace must be 256-byte aligned");
+  if (cell->workspace_bytes < p.total)
+    return fail(PNR_E_WORKSPACE, "workspace has %zu bytes, %zu required", cell->workspace_bytes, p.total);
+  if (cell->T == 0) {
+    g_last.iters = 0;
+    g_last.residual = 0.0;
+    g_last.hist.assign(1, 0.0);
+    return PNR_OK;
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(cell->stream);
+  char* ws = static_cast<char*>(cell->workspace);
+  const size_t B = cell->B, T = cell->T, Din = cell->D_in, S = states(cell->kind, cell->D);
+  const size_t xes = dsize(cell->x_dtype), ses = dsize(cell->state_dtype);
+  const char* xb = static_cast<const char*>(x);
+  char* ob = static_cast<char*>(h_out);
+  int iters = 0, status = PNR_OK;
+  double residual = 0.0;
+  std::vector<double> hist;
+  pnr_profile acc{};
+  bool prof_ok = g_prof.on;
+  for (size_t t0 = 0; t0 < T; t0 += p.L) {
+    const size_t Lc = T - t0 < (size_t)p.L ? T - t0 : (size_t)p.L;
+    pnr_cell sub = p.sub;
+    sub.T = (int)Lc;
+    sub.workspace = ws;
+    sub.workspace_bytes = p.sub_bytes;
+    const void* xc = xb + t0 * Din * xes;
+    const void* h0c = t0 == 0 ? h0 : static_cast<const void*>(ob + (t0 - 1) * S * ses);   // the carried-in state
+    void* oc = ob + t0 * S * ses;
+    if (p.staged) {
+      PNR_HIP(hipMemcpy2DAsync(ws + p.x_off, Lc * Din * xes, xc, T * Din * xes, Lc * Din * xes, B,
+                               hipMemcpyDeviceToDevice, st));
+      if (t0 > 0) {
+        PNR_HIP(hipMemcpy2DAsync(ws + p.h0_off, S * ses, h0c, T * S * ses, S * ses, B, hipMemcpyDeviceToDevice, st));
+        h0c = ws + p.h0_off;
+      }
+      xc = ws + p.x_off;
+      oc = ws + p.out_off;
+    }
+    rc = damping > 0 ? pnr_eval_damped(&sub, params, xc, h0c, oc, max_iters, tol, jac_mode, damping)
+                     : pnr_eval(&sub, params, xc, h0c, oc, max_iters, tol, jac_mode);
+    if (rc < 0) return rc;   // g_last.err holds the chunk's error
+    if (p.staged)
+      PNR_HIP(hipMemcpy2DAsync(ob + t0 * S * ses, T * S * ses, oc, Lc * S * ses, Lc * S * ses, B,
+                               hipMemcpyDeviceToDevice, st));
+    if (prof_ok && g_prof.valid) {
+      const pnr_profile& c = g_prof.last;
+      acc.total_ms += c.total_ms; acc.proj_ms += c.proj_ms; acc.newton_ms += c.newton_ms; acc.out_ms += c.out_ms;
+      acc.passes += c.passes; acc.resid_only += c.resid_only;
+    } else {
+      prof_ok = false;
+    }
+    iters += g_last.iters;
+    if (!(g_last.residual <= residual)) residual = g_last.residual;   // max, NaN wins
+    hist.insert(hist.end(), g_last.hist.begin(), g_last.hist.end());
+    if (status_rank(rc) > status_rank(status)) status = rc;
+    if (rc == PNR_NONFINITE) break;   // later chunks would start from a non-finite state
+  }
+  PNR_HIP(hipStreamSynchronize(st));
+  g_last.iters = iters;
+  g_last.residual = residual;
+  g_last.hist = std::move(hist);
+  g_prof.valid = prof_ok;
+  if (prof_ok) g_prof.last = acc;
+  return status;
 }
 
 size_t pnr_scan_workspace_bytes(int kind, int R, int T, int tile_len) {

@@ -68,6 +68,11 @@ def load() -> ctypes.CDLL:
     lib.pnr_eval_damped.argtypes = [P(PnrCell), P(PnrParams), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_double]
     lib.pnr_eval_damped.restype = ctypes.c_int
+    lib.pnr_workspace_bytes_chunked.argtypes = [P(PnrCell), ctypes.c_int, ctypes.c_double, ctypes.c_int]
+    lib.pnr_workspace_bytes_chunked.restype = ctypes.c_size_t
+    lib.pnr_eval_chunked.argtypes = [P(PnrCell), P(PnrParams), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_double, ctypes.c_int]
+    lib.pnr_eval_chunked.restype = ctypes.c_int
     lib.pnr_iters_used.argtypes = []
     lib.pnr_iters_used.restype = ctypes.c_int
     lib.pnr_last_residual.argtypes = []
@@ -137,6 +142,16 @@ def pnr_eval_damped(cell: PnrCell, params: PnrParams, x: int, h0: Optional[int],
                                   damping)
 
 
+def pnr_workspace_bytes_chunked(cell: PnrCell, jac_mode: int, damping: float, chunk_len: int) -> int:
+    return load().pnr_workspace_bytes_chunked(ctypes.byref(cell), jac_mode, damping, chunk_len)
+
+
+def pnr_eval_chunked(cell: PnrCell, params: PnrParams, x: int, h0: Optional[int], h_out: int, max_iters: int,
+                     tol: float, jac_mode: int, damping: float, chunk_len: int) -> int:
+    return load().pnr_eval_chunked(ctypes.byref(cell), ctypes.byref(params), x, h0, h_out, max_iters, tol, jac_mode,
+                                   damping, chunk_len)
+
+
 def pnr_iters_used() -> int:
     return load().pnr_iters_used()
 
@@ -185,16 +200,22 @@ class PnrError(RuntimeError):
 def evaluate(kind: int, W: torch.Tensor, U: torch.Tensor, x: torch.Tensor, *, b_x=None, b_h=None,
              h0=None, max_iters: int = 64, tol: float = 1e-5, jac_mode: int = JAC_FULL,
              jac_every: int = 1, h_out: Optional[torch.Tensor] = None,
-             workspace: Optional[torch.Tensor] = None, damping: Optional[float] = None) -> dict:
-    """Run pnr_eval (or pnr_eval_damped when `damping` is given) on device tensors;
-    returns dict(h=[B,T,S], status, iters, residual, history)."""
+             workspace: Optional[torch.Tensor] = None, damping: Optional[float] = None,
+             chunk_len: Optional[int] = None) -> dict:
+    """Run pnr_eval (or pnr_eval_damped when `damping` is given, or pnr_eval_chunked when
+    `chunk_len` is given) on device tensors; returns dict(h=[B,T,S], status, iters,
+    residual, history)."""
     B, T, D_in = x.shape
     D = U.shape[1]
     S = 2 * D if kind == CELL_LSTM_DIAG else D
     xdt, sdt = _DT[x.dtype], _DT[U.dtype]
     cell = make_cell(kind, D, D_in, T, B, xdt, sdt, jac_every, _stream())
-    need = (pnr_workspace_bytes(cell, jac_mode) if damping is None
-            else pnr_workspace_bytes_damped(cell, jac_mode))
+    if chunk_len is not None:
+        need = pnr_workspace_bytes_chunked(cell, jac_mode, damping or 0.0, chunk_len)
+    elif damping is None:
+        need = pnr_workspace_bytes(cell, jac_mode)
+    else:
+        need = pnr_workspace_bytes_damped(cell, jac_mode)
     if need == 0:
         raise PnrError(pnr_last_error())
     if workspace is None or workspace.numel() < need:
@@ -204,7 +225,10 @@ def evaluate(kind: int, W: torch.Tensor, U: torch.Tensor, x: torch.Tensor, *, b_
     if h_out is None:
         h_out = torch.empty(B, T, S, dtype=U.dtype, device=x.device)
     params = PnrParams(_ptr(W), _ptr(U), _ptr(b_x), _ptr(b_h))
-    if damping is None:
+    if chunk_len is not None:
+        rc = pnr_eval_chunked(cell, params, _ptr(x), _ptr(h0), _ptr(h_out), max_iters, tol, jac_mode,
+                              damping or 0.0, chunk_len)
+    elif damping is None:
         rc = pnr_eval(cell, params, _ptr(x), _ptr(h0), _ptr(h_out), max_iters, tol, jac_mode)
     else:
         rc = pnr_eval_damped(cell, params, _ptr(x), _ptr(h0), _ptr(h_out), max_iters, tol, jac_mode, damping)

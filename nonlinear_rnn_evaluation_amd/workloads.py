@@ -79,6 +79,7 @@ class Workload:
     max_iters: int = 64
     seed: int = 0
     damping: Optional[float] = None   # set: the damped (quasi-ELK) step with this strength
+    chunk_len: Optional[int] = None   # set: evaluated in chunks of this many steps
 
     @property
     def G(self) -> int:
@@ -97,6 +98,7 @@ class Workload:
             "jac_modes": [["full", "diag", "zero"][m] for m in self.jac_modes],
             "jac_every": self.jac_every, "tol": self.tol, "max_iters": self.max_iters,
             **({"damping": self.damping} if self.damping is not None else {}),
+            **({"chunk_len": self.chunk_len} if self.chunk_len is not None else {}),
         }
 
 
@@ -126,6 +128,10 @@ def named_workloads() -> dict:
     w["lstm_diag_long_stiff"] = dataclasses.replace(
         w["lstm_diag_long"], name="lstm_diag_long_stiff", u_scale=3.0, max_iters=256,
         jac_modes=(JAC_FULL, JAC_DIAG))
+    # the long LSTM evaluated in chunks of 8192 steps, each from the previous chunk's last
+    # state: the workspace covers one chunk (16x less), and short chunks need fewer iterations
+    w["lstm_diag_long_chunked"] = dataclasses.replace(w["lstm_diag_long"], name="lstm_diag_long_chunked",
+                                                      chunk_len=8192)
     # the stiff LSTM with the damped step on the diagonal Jacobian (quasi-ELK), which
     # converges where both undamped variants do not
     w["lstm_diag_long_stiff_elk"] = dataclasses.replace(

@@ -27,6 +27,9 @@ What it computes (sources are the five pages on this method):
   ELK / quasi-ELK, by its normal equations and as a Kalman filter and smoother
   ("Towards Scalable and Stable Parallelization of Nonlinear RNNs", abstract and the
   summary's "Approach"); ``newton_dense(..., damping=lam)`` iterates it.
+* ``newton_chunked`` -- the sequence evaluated chunk by chunk, each chunk from the
+  previous chunk's last state (ParaRNN overview, "Experimental Results": chunking to
+  bound the memory of long sequences).
 
 Cell equations are not printed on the pages; the readings used (linear-before-reset
 GRU with gates (r, z, n); LSTM with gates (i, f, o, g) and state (c, h); elementwise
@@ -39,6 +42,7 @@ from .sequential import project, sequential, restrict_channels
 from .newton import newton_dense, STATUS_OK, STATUS_NOT_CONVERGED, STATUS_NONFINITE, max_abs
 from .scan import scan_loop, scan_doubling, compose
 from .damped import lm_step_dense, lm_step_kalman, damped_step
+from .chunked import newton_chunked
 
 __all__ = [
     "CELL_GRU", "CELL_GRU_DIAG", "CELL_LSTM_DIAG", "JAC_FULL", "JAC_DIAG", "JAC_ZERO",
@@ -47,4 +51,5 @@ __all__ = [
     "newton_dense", "STATUS_OK", "STATUS_NOT_CONVERGED", "STATUS_NONFINITE", "max_abs",
     "scan_loop", "scan_doubling", "compose",
     "lm_step_dense", "lm_step_kalman", "damped_step",
+    "newton_chunked",
 ]

@@ -121,3 +121,36 @@ def test_damped_requests_are_validated_without_a_gpu():
     assert pnr.pnr_eval_damped(ok, params, 4096, None, 8192, 10, 1e-5, pnr.JAC_ZERO, 0.5) == pnr.E_UNSUPPORTED
     # workspace missing
     assert pnr.pnr_eval_damped(ok, params, 4096, None, 8192, 10, 1e-5, pnr.JAC_FULL, 0.5) in (pnr.E_WORKSPACE,)
+
+
+def test_chunked_requests_are_validated_without_a_gpu():
+    params = pnr.PnrParams(1024, 2048, None, None)
+    lstm = _cell(kind=pnr.CELL_LSTM_DIAG, B=1, T=131072, D=64)
+    full = pnr.pnr_workspace_bytes(lstm, pnr.JAC_FULL)
+    ch = pnr.pnr_workspace_bytes_chunked(lstm, pnr.JAC_FULL, 0.0, 8192)
+    # the workspace covers one chunk: B = 1 needs no staging
+    one = pnr.pnr_workspace_bytes(_cell(kind=pnr.CELL_LSTM_DIAG, B=1, T=8192, D=64), pnr.JAC_FULL)
+    assert ch == one and ch < full / 8
+    # damped chunks: the damped workspace of one chunk
+    dm = pnr.pnr_workspace_bytes_chunked(lstm, pnr.JAC_DIAG, 0.5, 8192)
+    assert dm == pnr.pnr_workspace_bytes_damped(_cell(kind=pnr.CELL_LSTM_DIAG, B=1, T=8192, D=64), pnr.JAC_DIAG)
+    # B > 1 with several chunks stages x, the boundary state and the output of a chunk
+    gru = _cell(B=3, T=5000, D=16, D_in=8)
+    st = pnr.pnr_workspace_bytes_chunked(gru, pnr.JAC_FULL, 0.0, 1000)
+    base = pnr.pnr_workspace_bytes(_cell(B=3, T=1000, D=16, D_in=8), pnr.JAC_FULL)
+    assert base + 3 * 1000 * (8 + 16) * 4 + 3 * 16 * 4 <= st < base + 3 * 1000 * (8 + 16) * 4 + 3 * 16 * 4 + 4 * 256
+    # a chunk at least as long as the sequence is the unchunked problem
+    assert pnr.pnr_workspace_bytes_chunked(gru, pnr.JAC_FULL, 0.0, 5000) == pnr.pnr_workspace_bytes(gru, pnr.JAC_FULL)
+    for bad_len in (0, -3):
+        assert pnr.pnr_workspace_bytes_chunked(gru, pnr.JAC_FULL, 0.0, bad_len) == 0
+        assert pnr.pnr_eval_chunked(gru, params, 4096, None, 8192, 10, 1e-5, pnr.JAC_FULL, 0.0,
+                                    bad_len) == pnr.E_INVALID
+    for lam in (-1.0, float("nan"), float("inf")):
+        assert pnr.pnr_eval_chunked(gru, params, 4096, None, 8192, 10, 1e-5, pnr.JAC_FULL, lam,
+                                    100) == pnr.E_INVALID
+    # what the unchunked entry points reject, the chunked one rejects the same way
+    assert pnr.pnr_eval_chunked(_cell(kind=pnr.CELL_LSTM_DIAG), params, 4096, None, 8192, 10, 1e-5,
+                                pnr.JAC_FULL, 0.5, 100) == pnr.E_UNSUPPORTED
+    assert pnr.pnr_eval_chunked(_cell(kind=pnr.CELL_GRU, D=100), params, 4096, None, 8192, 10, 1e-5,
+                                pnr.JAC_DIAG, 0.0, 100) == pnr.E_UNSUPPORTED
+    assert pnr.pnr_eval_chunked(gru, params, 4096, None, 8192, 10, 1e-5, pnr.JAC_FULL, 0.0, 100) == pnr.E_WORKSPACE
