@@ -27,6 +27,10 @@ What it computes (sources are the five pages on this method):
   ELK / quasi-ELK, by its normal equations and as a Kalman filter and smoother
   ("Towards Scalable and Stable Parallelization of Nonlinear RNNs", abstract and the
   summary's "Approach"); ``newton_dense(..., damping=lam)`` iterates it.
+* ``bptt`` / ``cell_vjp`` -- gradients through the evaluated sequence: the adjoint run
+  backwards in time, step by step (ParaRNN overview, "Newton's Iteration": forward and
+  backward substitution; training through the parallel evaluation, "Parallelizing
+  non-linear sequential models over the sequence length", abstract).
 * ``newton_chunked`` -- the sequence evaluated chunk by chunk, each chunk from the
   previous chunk's last state (ParaRNN overview, "Experimental Results": chunking to
   bound the memory of long sequences).
@@ -43,6 +47,7 @@ from .newton import newton_dense, STATUS_OK, STATUS_NOT_CONVERGED, STATUS_NONFIN
 from .scan import scan_loop, scan_doubling, compose
 from .damped import lm_step_dense, lm_step_kalman, damped_step
 from .chunked import newton_chunked
+from .backward import bptt, cell_vjp
 
 __all__ = [
     "CELL_GRU", "CELL_GRU_DIAG", "CELL_LSTM_DIAG", "JAC_FULL", "JAC_DIAG", "JAC_ZERO",
@@ -51,5 +56,5 @@ __all__ = [
     "newton_dense", "STATUS_OK", "STATUS_NOT_CONVERGED", "STATUS_NONFINITE", "max_abs",
     "scan_loop", "scan_doubling", "compose",
     "lm_step_dense", "lm_step_kalman", "damped_step",
-    "newton_chunked",
+    "newton_chunked", "bptt", "cell_vjp",
 ]

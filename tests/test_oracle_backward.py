@@ -1,0 +1,72 @@
+"""Pins of the backpropagation-through-time oracle (CPU).
+
+The gradients of L = sum_t <g_t, s_t> are checked against central finite differences of
+L through the sequential recurrence (an independent route: only the forward definition
+is shared), for every argument and every cell; the adjoint's structure is checked by
+linearity in g and by its last step (lam_T = g_T).
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from nonlinear_rnn_evaluation_amd import workloads as WL
+
+
+def _problem(cell, D, B=2, T=6, Din=3, seed=1):
+    p = WL.random_problem(cell, B, T, D, Din, seed=seed, x_dtype=WL.DT_F64, state_dtype=WL.DT_F64,
+                          bias_std=0.3, h0_std=0.5)
+    q = {k: WL.as_f64(v) for k, v in p.items()}
+    if q["b_h"] is None:
+        q["b_h"] = np.random.default_rng(seed + 100).normal(size=q["b_x"].shape) * 0.3
+    return q
+
+
+@pytest.mark.parametrize("cell,D", [(WL.CELL_GRU, 3), (WL.CELL_GRU_DIAG, 3), (WL.CELL_LSTM_DIAG, 2)])
+def test_gradients_match_central_differences(cell, D):
+    q = _problem(cell, D)
+    S = q["h0"].shape[1]
+    g = np.random.default_rng(5).normal(size=(2, 6, S))
+
+    def loss(**kw):
+        a = dict(q)
+        a.update(kw)
+        return (O.sequential(cell, a["W"], a["U"], a["b_x"], a["b_h"], a["x"], a["h0"]) * g).sum()
+
+    H = O.sequential(cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"])
+    r = O.bptt(cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], H, g)
+    eps = 1e-6
+    for name, key in (("W", "dW"), ("U", "dU"), ("b_x", "db_x"), ("b_h", "db_h"), ("x", "dx"), ("h0", "dh0")):
+        base = q[name]
+        fd = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            bp, bm = base.copy(), base.copy()
+            bp[idx] += eps
+            bm[idx] -= eps
+            fd[idx] = (loss(**{name: bp}) - loss(**{name: bm})) / (2 * eps)
+        assert r[key].shape == base.shape
+        assert np.abs(fd - r[key]).max() < 1e-7 * max(1.0, np.abs(fd).max()), name
+
+
+@pytest.mark.parametrize("cell,D", [(WL.CELL_GRU, 4), (WL.CELL_LSTM_DIAG, 3)])
+def test_adjoint_is_linear_in_the_loss_gradient_and_starts_at_the_last_step(cell, D):
+    q = _problem(cell, D, T=9, seed=3)
+    S = q["h0"].shape[1]
+    rng = np.random.default_rng(7)
+    g1, g2 = rng.normal(size=(2, 9, S)), rng.normal(size=(2, 9, S))
+    H = O.sequential(cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"])
+    args = (cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], H)
+    a, b, c = O.bptt(*args, g1), O.bptt(*args, g2), O.bptt(*args, g1 - 2.5 * g2)
+    for k in ("dx", "dW", "dU", "db_x", "db_h", "dh0", "lam"):
+        assert np.allclose(c[k], a[k] - 2.5 * b[k], rtol=1e-12, atol=1e-12), k
+    assert np.array_equal(a["lam"][:, -1], g1[:, -1])
+    # a loss on the last state only: lam at earlier steps is J^T applied repeatedly
+    gl = np.zeros_like(g1)
+    gl[:, -1] = g1[:, -1]
+    r = O.bptt(*args, gl)
+    P = np.concatenate([q["h0"][:, None], H[:, :-1]], axis=1)
+    gx = O.project(q["W"], q["x"], q["b_x"])
+    lam = g1[:, -1]
+    for t in range(8, 0, -1):
+        J = O.cell_jacobian(cell, q["U"], q["b_h"], P[:, t], gx[:, t])
+        lam = np.einsum("bij,bi->bj", J, lam)
+        assert np.allclose(r["lam"][:, t - 1], lam, rtol=1e-12, atol=1e-13)
