@@ -199,6 +199,35 @@ int pnr_eval_chunked(const pnr_cell* cell, const pnr_params* params, const void*
                      void* h_out, int max_iters, double tol, int jac_mode, double damping, int chunk_len);
 
 /*
+ * Backward pass: gradients through an evaluated sequence, for training through the
+ * parallel evaluation ("Parallelizing non-linear sequential models over the sequence
+ * length", abstract; ParaRNN overview, "Newton's Iteration": the block lower-triangular
+ * system is solved by backward as well as forward substitution).  Given the states h
+ * (e.g. pnr_eval's h_out at convergence) and g = dL/dh, the explicit loss gradient at
+ * every state, it computes the gradients of L through the recurrence
+ * s_t = f(s_{t-1}, x_t), s_0 = h0, taking h as its solution:
+ *     lam_t = g_t + J_{t+1}^T lam_{t+1}   (lam_T = g_T; J exact, not approximated)
+ * is run backwards in time as a scan, and each step's lam_t is sent back through the
+ * cell's gates to the pre-activations, the recurrent weights and biases, the inputs
+ * (through W) and h0.
+ * Supported: PNR_CELL_GRU_DIAG and PNR_CELL_LSTM_DIAG, x in {f32, bf16}, state f32 (the
+ * cell's jac_every is ignored).  Device pointers, caller-owned; each gradient output
+ * may be NULL (not computed); all gradients are fp32 and overwritten (not accumulated):
+ *   h, grad_h  [B, T, S]   fp32, inputs (S = D, or 2D for the LSTM's (c, h))
+ *   grad_x     [B, T, D_in]     grad_W    [G*D, D_in]     grad_U   [G, D]
+ *   grad_b_x   [G*D]            grad_b_h  [G*D]           grad_h0  [B, S]
+ * x, h0, params as for pnr_eval (h0 may be NULL: zeros).  Workspace:
+ * pnr_workspace_bytes_backward() bytes (0 = invalid or unsupported request).  The work
+ * is enqueued on cell->stream and the call returns without waiting for it.  In
+ * measurement mode the profile record holds: proj_ms the recomputed input projection,
+ * newton_ms the adjoint scan kernel, out_ms the reductions and the two gradient GEMMs.
+ */
+size_t pnr_workspace_bytes_backward(const pnr_cell* cell);
+int pnr_backward(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0,
+                 const void* h, const void* grad_h, void* grad_x, void* grad_W, void* grad_U,
+                 void* grad_b_x, void* grad_b_h, void* grad_h0);
+
+/*
  * Standalone linear solve used inside every Newton iteration, exposed for testing
  * the scan on its own: d_t = A_t d_{t-1} + b_t, d_0 = 0 along t, for R independent
  * rows (ParaRNN overview, "Newton's Iteration": forward substitution on the block

@@ -651,6 +651,143 @@ int pnr_eval_chunked(const pnr_cell* cell, const pnr_params* params, const void*
   return status;
 }
 
+// ---- backward pass (diagonal-recurrence cells) ----
+namespace {
+struct BwdLayout {
+  size_t gx = 0, states = 0, dgx = 0, wt = 0, part = 0, total = 0;
+};
+int validate_backward(const pnr_cell* c) {
+  if (!c) return fail(PNR_E_INVALID, "cell descriptor is NULL");
+  pnr_cell v = *c;
+  v.jac_every = 1;
+  int rc = validate(&v, PNR_JAC_FULL);
+  if (rc) return rc;
+  if (c->kind != PNR_CELL_GRU_DIAG && c->kind != PNR_CELL_LSTM_DIAG)
+    return fail(PNR_E_UNSUPPORTED, "the backward pass is implemented for GRU_DIAG and LSTM_DIAG");
+  if ((double)c->B * c->T > 2.0e9 || (double)gates(c->kind) * c->D * c->D_in > 2.0e9)
+    return fail(PNR_E_INVALID, "problem too large for this library's index range");
+  return 0;
+}
+BwdLayout make_bwd_layout(const pnr_cell* c) {
+  BwdLayout l;
+  const size_t B = c->B, T = c->T, D = c->D, Din = c->D_in, G = gates(c->kind), S = states(c->kind, c->D);
+  const size_t gd = B * T * G * D * sizeof(float);
+  size_t off = 0;
+  l.gx = off; off = align_up(off + gd);                       // gx, then dL/dgx transposed
+  const size_t st = 2 * B * T * S, xt = B * T * Din;
+  l.states = off; off = align_up(off + sizeof(float) * (st > xt ? st : xt));   // h, dL/dh; then x transposed
+  l.dgx = off; off = align_up(off + gd);
+  l.wt = off; off = align_up(off + sizeof(float) * G * D * Din);
+  l.part = off; off = align_up(off + sizeof(float) * B * 3 * G * D);
+  l.total = off;
+  return l;
+}
+}  // namespace
+
+size_t pnr_workspace_bytes_backward(const pnr_cell* cell) {
+  if (validate_backward(cell) != 0) return 0;
+  return make_bwd_layout(cell).total;
+}
+
+int pnr_backward(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, const void* h,
+                 const void* grad_h, void* grad_x, void* grad_W, void* grad_U, void* grad_b_x, void* grad_b_h,
+                 void* grad_h0) {
+  g_last = LastCall();
+  g_prof.valid = false;
+  g_prof.used = 0;
+  int rc = validate_backward(cell);
+  if (rc) return rc;
+  if (!params) return fail(PNR_E_INVALID, "params is NULL");
+  if (!params->W || !params->U || (cell->T > 0 && (!x || !h || !grad_h)))
+    return fail(PNR_E_INVALID, "W, U and (for T > 0) x, h and grad_h must be non-NULL");
+  const BwdLayout l = make_bwd_layout(cell);
+  if (!cell->workspace) return fail(PNR_E_WORKSPACE, "workspace is NULL (%zu bytes required)", l.total);
+  if ((uintptr_t)cell->workspace % 256) return fail(PNR_E_WORKSPACE, "workspace must be 256-byte aligned");
+  if (cell->workspace_bytes < l.total)
+    return fail(PNR_E_WORKSPACE, "workspace has %zu bytes, %zu required", cell->workspace_bytes, l.total);
+  const int kind = cell->kind, D = cell->D, T = cell->T, B = cell->B, Din = cell->D_in;
+  const int G = gates(kind), S = states(kind, D);
+  hipStream_t st = reinterpret_cast<hipStream_t>(cell->stream);
+  if (T == 0) {   // no steps: every gradient but dL/dh0 (= 0) is an empty sum
+    PNR_HIP(launch_fill_zero(static_cast<float*>(grad_W), (size_t)G * D * Din, st));
+    PNR_HIP(launch_fill_zero(static_cast<float*>(grad_U), (size_t)G * D, st));
+    PNR_HIP(launch_fill_zero(static_cast<float*>(grad_b_x), (size_t)G * D, st));
+    PNR_HIP(launch_fill_zero(static_cast<float*>(grad_b_h), (size_t)G * D, st));
+    PNR_HIP(launch_fill_zero(static_cast<float*>(grad_h0), (size_t)B * S, st));
+    return PNR_OK;
+  }
+  int num_cu = 0;
+  if ((rc = device_info(&num_cu))) return rc;
+  char* ws = static_cast<char*>(cell->workspace);
+  float* gx = reinterpret_cast<float*>(ws + l.gx);
+  float* hT = reinterpret_cast<float*>(ws + l.states);
+  float* gT = hT + (size_t)B * T * S;
+  float* dgx = reinterpret_cast<float*>(ws + l.dgx);
+  float* part = reinterpret_cast<float*>(ws + l.part);
+  const size_t BT = (size_t)B * T;
+
+  Mark m_first = mark_begin(st);
+  // the forward's input projection, recomputed: gx[b][m][t] = sum_k W[m][k] x[b][t][k] + b_x[m]
+  GemmArgs g{params->W, x, params->b_x, gx, G * D, T, Din, 0, (long long)T * Din, (long long)G * D * T,
+             Din, Din, T, B, 1};
+  Mark m_proj = mark_begin(st);
+  PNR_HIP(launch_gemm(cell->x_dtype, PNR_F32, g, st));
+  mark_end(m_proj, st);
+  PNR_HIP(launch_transpose(h, PNR_F32, hT, B, T, S, st));
+  PNR_HIP(launch_transpose(grad_h, PNR_F32, gT, B, T, S, st));
+
+  BwdArgs a{};
+  a.gx = gx;
+  a.u = static_cast<const float*>(params->U);
+  a.bh = static_cast<const float*>(params->b_h);
+  a.h0 = static_cast<const float*>(h0);
+  a.hT = hT;
+  a.gT = gT;
+  a.dgx = dgx;
+  a.part = part;
+  a.dh0 = static_cast<float*>(grad_h0);
+  a.B = B; a.D = D; a.T = T;
+  a.tiles_per_row = (T + PNR_BLOCK * adjoint_items_per_thread() - 1) / (PNR_BLOCK * adjoint_items_per_thread());
+  a.n_rows = B * D;
+  Mark m_adj = mark_begin(st);
+  PNR_HIP(launch_adjoint_diag(kind, a, num_cu, st));
+  mark_end(m_adj, st);
+
+  Mark m_grads = mark_begin(st);
+  PNR_HIP(launch_sum_over_batch(part, B, G * D, static_cast<float*>(grad_U), static_cast<float*>(grad_b_h),
+                                static_cast<float*>(grad_b_x), st));
+  if (grad_W) {
+    // dW[m][k] = sum_{b,t} dgx[m][(b,t)] x[(b,t)][k]: x transposed to [k][(b,t)]
+    float* xT = hT;   // the transposed states are no longer needed
+    PNR_HIP(launch_transpose(x, cell->x_dtype, xT, 1, (int)BT, Din, st));
+    GemmArgs gw{dgx, xT, nullptr, grad_W, G * D, Din, (int)BT, 0, 0, 0, (int)BT, (int)BT, Din, 1, 0};
+    PNR_HIP(launch_gemm(PNR_F32, PNR_F32, gw, st));
+  }
+  if (grad_x) {
+    // dx[(b,t)][k] = sum_m dgx[m][(b,t)] W[m][k]: dgx transposed to [(b,t)][m], W to [k][m]
+    float* dgxT = gx;   // gx is no longer needed
+    float* WT = reinterpret_cast<float*>(ws + l.wt);
+    PNR_HIP(launch_transpose(dgx, PNR_F32, dgxT, 1, G * D, (int)BT, st));
+    PNR_HIP(launch_transpose(params->W, cell->x_dtype, WT, 1, G * D, Din, st));
+    GemmArgs gxg{dgxT, WT, nullptr, grad_x, (int)BT, Din, G * D, 0, 0, 0, G * D, G * D, Din, 1, 0};
+    PNR_HIP(launch_gemm(PNR_F32, PNR_F32, gxg, st));
+  }
+  mark_end(m_grads, st);
+  mark_end(m_first, st);
+  if (g_prof.on) {
+    PNR_HIP(hipStreamSynchronize(st));
+    pnr_profile p{};
+    p.total_ms = mark_ms(m_first);
+    p.proj_ms = mark_ms(m_proj);
+    p.newton_ms = mark_ms(m_adj);
+    p.out_ms = mark_ms(m_grads);
+    p.passes = 1;
+    g_prof.last = p;
+    g_prof.valid = true;
+  }
+  return PNR_OK;
+}
+
 size_t pnr_scan_workspace_bytes(int kind, int R, int T, int tile_len) {
   if ((kind != 1 && kind != 2) || R < 0 || T < 0) {
     fail(PNR_E_INVALID, "bad scan arguments");

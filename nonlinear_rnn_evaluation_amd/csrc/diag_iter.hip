@@ -1073,4 +1073,225 @@ hipError_t launch_elk_diag(int cell, const ElkArgs& a, int num_cu, hipStream_t s
   return launch_persistent(fn, (int)g, 0, args, st);
 }
 
+// ---------------------------------------------------------------------------------
+// Backward pass: gradients through the evaluated sequence, for the cells with
+// elementwise recurrent weights (ParaRNN overview, "Newton's Iteration": the block
+// lower-triangular system is solved by forward and by backward substitution; training
+// through the parallel evaluation: "Parallelizing non-linear sequential models over the
+// sequence length", abstract).
+//
+// With g_t = dL/ds_t and mu_t = J_t^T lam_t (what step t sends back to s_{t-1}), the
+// adjoint lam_t = g_t + mu_{t+1} (mu_T = 0) gives mu_t = J_t^T mu_{t+1} + J_t^T g_t: an
+// affine map built from step t's own state and input, so mu is one scan of such maps run
+// backwards in time (the damped smoother's mirrored thread mapping).  Each thread then
+// walks its steps from the last to the first, recomputes the gates, and sends lam_t back
+// through them: pre-activation gradients (kept for the projection's gradients), the
+// recurrent-weight and bias sums of the row, and mu_t.  mu at the row's first step is
+// dL/dh0.  One block walks a whole row (channel) from its last tile to its first.
+
+// GRU: h' = (1 - z) n + z p with gates r, z, n (pre-activations gx + u p + b).
+__device__ __forceinline__ void vjp_gru(const DiagCell<PNR_CELL_GRU_DIAG>::Par& q, const float* g, float p,
+                                        float lam, float* dgx, float* dgh, float& dprev) {
+  const float ghr = fmaf(q.ur, p, q.br), ghz = fmaf(q.uz, p, q.bz), ghn = fmaf(q.un, p, q.bn);
+  const float r = sigm(g[0] + ghr), z = sigm(g[1] + ghz);
+  const float n = tanh_(fmaf(r, ghn, g[2]));
+  const float dan = lam * (1.f - z) * (1.f - n * n);
+  const float daz = lam * (p - n) * z * (1.f - z);
+  const float dar = dan * ghn * r * (1.f - r);
+  dgx[0] = dar; dgx[1] = daz; dgx[2] = dan;
+  dgh[0] = dar; dgh[1] = daz; dgh[2] = dan * r;
+  dprev = fmaf(lam, z, fmaf(q.ur, dgh[0], fmaf(q.uz, dgh[1], q.un * dgh[2])));
+}
+
+// LSTM: c' = f c + i g, h' = o tanh(c') with gates i, f, o, g (pre-activations gx + u h + b).
+__device__ __forceinline__ void vjp_lstm(const DiagCell<PNR_CELL_LSTM_DIAG>::Par& q, const float* gx, float cp,
+                                         float hp, float lc, float lh, float* da, float2& dprev) {
+  const float i = sigm(gx[0] + fmaf(q.ui, hp, q.bi));
+  const float f = sigm(gx[1] + fmaf(q.uf, hp, q.bf));
+  const float o = sigm(gx[2] + fmaf(q.uo, hp, q.bo));
+  const float g = tanh_(gx[3] + fmaf(q.ug, hp, q.bg));
+  const float tau = tanh_(fmaf(f, cp, i * g));
+  const float dcn = fmaf(lh * o, 1.f - tau * tau, lc);   // c' is reached directly and through h'
+  da[0] = dcn * g * i * (1.f - i);
+  da[1] = dcn * cp * f * (1.f - f);
+  da[2] = lh * tau * o * (1.f - o);
+  da[3] = dcn * i * (1.f - g * g);
+  dprev = make_float2(dcn * f, fmaf(q.ui, da[0], fmaf(q.uf, da[1], fmaf(q.uo, da[2], q.ug * da[3]))));
+}
+
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+template <int CELL>
+struct BwdShared {
+  using E = typename DiagCell<CELL>::E;
+  E tot[PNR_WAVES];
+  typename DeltaOf<E>::T carry;   // mu at the step after the tile
+  float red[PNR_WAVES][3 * DiagCell<CELL>::G];
+};
+
+// One tile of the backward walk.  Thread t takes the run of N steps that starts at step
+// (PNR_BLOCK - 1 - t) * N of the tile.  acc: the thread's sums (dU, db_h, db_x per gate).
+// Returns mu at the thread's first step.
+template <int CELL, int N>
+__device__ __forceinline__ typename DeltaOf<typename DiagCell<CELL>::E>::T adjoint_tile(
+    const BwdArgs& a, BwdShared<CELL>& sh, int b, int d, int seg, float* acc) {
+  using C = DiagCell<CELL>;
+  using E = typename C::E;
+  using Dl = typename DeltaOf<E>::T;
+  constexpr int K = C::SP, NG = C::G;
+  constexpr int TILE = PNR_BLOCK * N;
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int D = a.D, T = a.T, S = K * D;
+  const bool vec = (T & 3) == 0;
+  const int tb = seg * TILE + (PNR_BLOCK - 1 - tid) * N;
+  const typename C::Par q = C::load_par(a.u, a.bh, D, d);
+  size_t off[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) off[k] = ((size_t)b * S + k * D + d) * T;
+  float gx[NG][N], hv[K][N], gv[K][N], p0[K];
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) load_n(a.gx + ((size_t)(b * NG + gg) * D + d) * T, tb, T, vec, N, gx[gg]);
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    load_n(a.hT + off[k], tb, T, vec, N, hv[k]);
+    load_n(a.gT + off[k], tb, T, vec, N, gv[k]);
+    p0[k] = tb == 0 ? (a.h0 ? a.h0[(size_t)b * S + k * D + d] : 0.f) : (tb <= T ? a.hT[off[k] + tb - 1] : 0.f);
+  }
+  // scan elements mu -> J^T mu + J^T g, latest step first
+  E e[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    float gi[NG];
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) gi[gg] = gx[gg][i];
+    const bool in = tb + i < T;
+    if constexpr (CELL == PNR_CELL_GRU_DIAG) {
+      float res, ja = 0.f;
+      C::eval(q, gi, i == 0 ? p0[0] : hv[0][i - 1], 0.f, PNR_JAC_FULL, true, res, ja);
+      e[N - 1 - i] = in ? Aff1{ja, ja * gv[0][i]} : aff_identity1();
+    } else {
+      float rc, rh;
+      Aff2 J = aff_identity2();
+      C::eval(q, gi, i == 0 ? p0[0] : hv[0][i - 1], i == 0 ? p0[1] : hv[1][i - 1], 0.f, 0.f, PNR_JAC_FULL, true, rc,
+              rh, J);
+      const float g0 = gv[0][i], g1 = gv[1][i];
+      e[N - 1 - i] = in ? Aff2{J.a00, J.a10, J.a01, J.a11, fmaf(J.a00, g0, J.a10 * g1), fmaf(J.a01, g0, J.a11 * g1)}
+                        : aff_identity2();
+    }
+  }
+  E agg = e[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) agg = compose(e[i], agg);
+  const E incl = wave_inclusive_scan(agg, identity_of<E>());
+  if (lane == 63) sh.tot[wid] = incl;
+  __syncthreads();
+  Dl mw = sh.carry;   // mu at the step after this wave's runs
+  for (int w = 0; w < wid; ++w) mw = apply(sh.tot[w], mw);
+  Dl mu = wave_shr1(apply(incl, mw), mw);   // mu at the step after this thread's run
+  float da[NG][N];
+#pragma unroll
+  for (int i = N - 1; i >= 0; --i) {
+    float gi[NG], dg[NG], dh[NG];
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) gi[gg] = gx[gg][i];
+    const bool in = tb + i < T;
+    if constexpr (CELL == PNR_CELL_GRU_DIAG) {
+      const float p = i == 0 ? p0[0] : hv[0][i - 1];
+      float dprev;
+      vjp_gru(q, gi, p, gv[0][i] + mu, dg, dh, dprev);
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) {
+        dg[gg] = in ? dg[gg] : 0.f;
+        dh[gg] = in ? dh[gg] : 0.f;
+        acc[gg] = fmaf(dh[gg], p, acc[gg]);
+        acc[NG + gg] += dh[gg];
+        acc[2 * NG + gg] += dg[gg];
+        da[gg][i] = dg[gg];
+      }
+      mu = in ? dprev : mu;
+    } else {
+      const float cp = i == 0 ? p0[0] : hv[0][i - 1];
+      const float hp = i == 0 ? p0[1] : hv[1][i - 1];
+      float2 dprev;
+      vjp_lstm(q, gi, cp, hp, gv[0][i] + mu.x, gv[1][i] + mu.y, dg, dprev);
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) {
+        dg[gg] = in ? dg[gg] : 0.f;
+        acc[gg] = fmaf(dg[gg], hp, acc[gg]);
+        acc[NG + gg] += dg[gg];
+        acc[2 * NG + gg] += dg[gg];
+        da[gg][i] = dg[gg];
+      }
+      mu = in ? dprev : mu;
+    }
+  }
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg)
+    store_n(a.dgx + (((size_t)gg * D + d) * a.B + b) * T, tb, T, vec, N, da[gg]);
+  __syncthreads();   // everyone has read tot and carry
+  if (tid == PNR_BLOCK - 1) sh.carry = mu;   // mu at the tile's first step
+  __syncthreads();
+  return mu;
+}
+
+template <int CELL, int N>
+__global__ void __launch_bounds__(PNR_BLOCK) adjoint_diag_kernel(BwdArgs a) {
+  using C = DiagCell<CELL>;
+  using Dl = typename DeltaOf<typename C::E>::T;
+  constexpr int NA = 3 * C::G;
+  __shared__ BwdShared<CELL> sh;
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  for (int row = blockIdx.x; row < a.n_rows; row += gridDim.x) {
+    const int b = row / a.D, d = row - b * a.D;
+    float acc[NA];
+#pragma unroll
+    for (int j = 0; j < NA; ++j) acc[j] = 0.f;
+    if (tid == 0) sh.carry = DeltaOf<typename C::E>::zero();
+    __syncthreads();
+    Dl mu = DeltaOf<typename C::E>::zero();
+    for (int seg = a.tiles_per_row - 1; seg >= 0; --seg) mu = adjoint_tile<CELL, N>(a, sh, b, d, seg, acc);
+    if (tid == PNR_BLOCK - 1 && a.dh0) {   // this thread's run starts at step 0: mu = dL/dh0
+      const int S = C::SP * a.D;
+      if constexpr (CELL == PNR_CELL_GRU_DIAG) {
+        a.dh0[(size_t)b * S + d] = mu;
+      } else {
+        a.dh0[(size_t)b * S + d] = mu.x;
+        a.dh0[(size_t)b * S + a.D + d] = mu.y;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      const float v = wave_sum_f(acc[j]);
+      if (lane == 0) sh.red[wid][j] = v;
+    }
+    __syncthreads();
+    if (tid < NA) {
+      float s = 0.f;
+      for (int w = 0; w < PNR_WAVES; ++w) s += sh.red[w][tid];
+      a.part[((size_t)b * NA + tid) * a.D + d] = s;   // [B][3][G][D]
+    }
+    __syncthreads();
+  }
+}
+
+constexpr int kAdjN = 4;   // steps per thread
+
+int adjoint_items_per_thread() { return kAdjN; }
+
+hipError_t launch_adjoint_diag(int cell, const BwdArgs& a, int num_cu, hipStream_t st) {
+  const void* fn = cell == PNR_CELL_GRU_DIAG ? (const void*)adjoint_diag_kernel<PNR_CELL_GRU_DIAG, kAdjN>
+                                             : (const void*)adjoint_diag_kernel<PNR_CELL_LSTM_DIAG, kAdjN>;
+  const int per_cu = cached_occupancy(fn, 0);
+  if (per_cu < 1) return hipErrorInvalidConfiguration;
+  long g = (long)per_cu * num_cu;
+  if (g > a.n_rows) g = a.n_rows;
+  if (g < 1) g = 1;
+  void* args[] = {const_cast<BwdArgs*>(&a)};
+  return hipLaunchKernel(fn, dim3((unsigned)g), dim3(PNR_BLOCK), args, 0, st);
+}
+
 }  // namespace pnr

@@ -93,6 +93,25 @@ struct ElkArgs {
 int elk_items_per_thread();
 hipError_t launch_elk_diag(int cell, const ElkArgs& a, int num_cu, hipStream_t st);
 
+// Backward pass of the diagonal-recurrence cells (GRU_DIAG, LSTM_DIAG): the adjoint
+// scan run backwards in time with the per-step gate gradients; one block walks a row.
+struct BwdArgs {
+  const float* gx;     // [B][G][D][T] pre-activations from the input projection
+  const float* u;      // [G][D]
+  const float* bh;     // [G*D] or nullptr
+  const float* h0;     // [B][S] or nullptr
+  const float* hT;     // states [B][S][T]
+  const float* gT;     // dL/ds [B][S][T]
+  float* dgx;          // out: dL/d(pre-activation) [G*D][B*T]
+  float* part;         // out: per batch element sums [B][3][G][D] (dU, db_h, db_x)
+  float* dh0;          // out: dL/dh0 [B][S] or nullptr
+  int B, D, T;
+  int tiles_per_row;
+  int n_rows;          // B * D
+};
+int adjoint_items_per_thread();
+hipError_t launch_adjoint_diag(int cell, const BwdArgs& a, int num_cu, hipStream_t st);
+
 int diag_items_per_thread(int cell);
 int diag_slot_words(int cell);
 int diag_grid_capacity(int cell, int num_cu);
@@ -164,6 +183,12 @@ hipError_t launch_gemm(int in_dtype, int out_dtype, const GemmArgs& g, hipStream
 // Per-block residual words: three per block (one per pass modulo 3) for the barrier-free
 // loops, which tag each word with its pass.
 constexpr size_t kPartialWords = 3 * (size_t)kMaxGrid;
+// [Z][R][C] (PNR_F32 or PNR_BF16) -> [Z][C][R] fp32.
+hipError_t launch_transpose(const void* in, int in_dtype, float* out, int Z, int R, int C, hipStream_t st);
+// p[0..n) = 0 (a kernel, so that the call can sit in a captured graph).
+hipError_t launch_fill_zero(float* p, size_t n, hipStream_t st);
+// out_q[j] = sum_b part[b][q][j], q = 0..2, j < n (null outputs are skipped).
+hipError_t launch_sum_over_batch(const float* part, int B, int n, float* o0, float* o1, float* o2, hipStream_t st);
 hipError_t launch_init(Ctrl* ctrl, uint64_t* slots, size_t slot_words, uint64_t* partials, size_t partial_words,
                        hipStream_t st);
 // diag layout [B][S][T] -> h_out [B][T][S] (or zeros when the result is the zero guess)

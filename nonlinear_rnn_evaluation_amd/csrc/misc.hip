@@ -127,4 +127,70 @@ hipError_t launch_dense_output(const Tt* const* bufs, const Ctrl* ctrl, Tt* h_ou
 template hipError_t launch_dense_output<float>(const float* const*, const Ctrl*, float*, size_t, hipStream_t);
 template hipError_t launch_dense_output<double>(const double* const*, const Ctrl*, double*, size_t, hipStream_t);
 
+// [Z][R][C] (fp32 or bf16) -> [Z][C][R] fp32 through a 32 x 33 LDS tile: reads run along
+// C and writes along R, both coalesced.
+template <typename Tin>
+__global__ void __launch_bounds__(256) transpose_kernel(const Tin* __restrict__ in, float* __restrict__ out, int R,
+                                                        int C) {
+  __shared__ float tile[32][33];
+  const size_t z = blockIdx.z;
+  const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8
+  const Tin* src = in + z * (size_t)R * C;
+  float* dst = out + z * (size_t)R * C;
+  for (int k = ty; k < 32; k += 8) {
+    const int r = r0 + k, c = c0 + tx;
+    tile[k][tx] = (r < R && c < C) ? (float)src[(size_t)r * C + c] : 0.f;
+  }
+  __syncthreads();
+  for (int k = ty; k < 32; k += 8) {
+    const int c = c0 + k, r = r0 + tx;
+    if (c < C && r < R) dst[(size_t)c * R + r] = tile[tx][k];
+  }
+}
+
+hipError_t launch_transpose(const void* in, int in_dtype, float* out, int Z, int R, int C, hipStream_t st) {
+  if (Z <= 0 || R <= 0 || C <= 0) return hipSuccess;
+  dim3 grid((C + 31) / 32, (R + 31) / 32, Z);
+  if (in_dtype == PNR_BF16)
+    hipLaunchKernelGGL(transpose_kernel<__bf16>, grid, dim3(256), 0, st, static_cast<const __bf16*>(in), out, R, C);
+  else if (in_dtype == PNR_F32)
+    hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(in), out, R, C);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// out_q[j] = sum_b part[b][q][j] for q = 0, 1, 2 (each output may be null); n values each.
+__global__ void __launch_bounds__(256) sum_over_batch_kernel(const float* __restrict__ part, int B, int n,
+                                                             float* o0, float* o1, float* o2) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  const int q = blockIdx.y;
+  float* o = q == 0 ? o0 : (q == 1 ? o1 : o2);
+  if (j >= n || !o) return;
+  float s = 0.f;
+  for (int b = 0; b < B; ++b) s += part[((size_t)b * 3 + q) * n + j];
+  o[j] = s;
+}
+
+hipError_t launch_sum_over_batch(const float* part, int B, int n, float* o0, float* o1, float* o2,
+                                 hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sum_over_batch_kernel, dim3((n + 255) / 256, 3), dim3(256), 0, st, part, B, n, o0, o1, o2);
+  return hipGetLastError();
+}
+
+__global__ void __launch_bounds__(256) fill_zero_kernel(float* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0.f;
+}
+
+hipError_t launch_fill_zero(float* p, size_t n, hipStream_t st) {
+  if (!p || n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
 }  // namespace pnr

@@ -73,6 +73,10 @@ def load() -> ctypes.CDLL:
     lib.pnr_eval_chunked.argtypes = [P(PnrCell), P(PnrParams), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_double, ctypes.c_int]
     lib.pnr_eval_chunked.restype = ctypes.c_int
+    lib.pnr_workspace_bytes_backward.argtypes = [P(PnrCell)]
+    lib.pnr_workspace_bytes_backward.restype = ctypes.c_size_t
+    lib.pnr_backward.argtypes = [P(PnrCell), P(PnrParams)] + [ctypes.c_void_p] * 10
+    lib.pnr_backward.restype = ctypes.c_int
     lib.pnr_iters_used.argtypes = []
     lib.pnr_iters_used.restype = ctypes.c_int
     lib.pnr_last_residual.argtypes = []
@@ -150,6 +154,17 @@ def pnr_eval_chunked(cell: PnrCell, params: PnrParams, x: int, h0: Optional[int]
                      tol: float, jac_mode: int, damping: float, chunk_len: int) -> int:
     return load().pnr_eval_chunked(ctypes.byref(cell), ctypes.byref(params), x, h0, h_out, max_iters, tol, jac_mode,
                                    damping, chunk_len)
+
+
+def pnr_workspace_bytes_backward(cell: PnrCell) -> int:
+    return load().pnr_workspace_bytes_backward(ctypes.byref(cell))
+
+
+def pnr_backward(cell: PnrCell, params: PnrParams, x: int, h0: Optional[int], h: int, grad_h: int,
+                 grad_x: Optional[int], grad_W: Optional[int], grad_U: Optional[int], grad_b_x: Optional[int],
+                 grad_b_h: Optional[int], grad_h0: Optional[int]) -> int:
+    return load().pnr_backward(ctypes.byref(cell), ctypes.byref(params), x, h0, h, grad_h, grad_x, grad_W, grad_U,
+                               grad_b_x, grad_b_h, grad_h0)
 
 
 def pnr_iters_used() -> int:
@@ -236,6 +251,35 @@ def evaluate(kind: int, W: torch.Tensor, U: torch.Tensor, x: torch.Tensor, *, b_
         raise PnrError(f"pnr_eval returned {rc}: {pnr_last_error()}")
     return {"h": h_out, "status": rc, "iters": pnr_iters_used(), "residual": pnr_last_residual(),
             "history": pnr_last_residual_history(), "workspace": workspace}
+
+
+def backward(kind: int, W: torch.Tensor, U: torch.Tensor, x: torch.Tensor, h: torch.Tensor, grad_h: torch.Tensor,
+             *, b_x=None, b_h=None, h0=None, want=("x", "W", "U", "b_x", "b_h", "h0"),
+             workspace: Optional[torch.Tensor] = None) -> dict:
+    """Run pnr_backward on device tensors: gradients of L through the recurrence whose
+    states are h, given grad_h = dL/dh.  Returns {name: fp32 tensor} for the names in
+    `want` (the others are not computed), plus "workspace"."""
+    B, T, D_in = x.shape
+    G, D = (U.shape[0] // U.shape[1], U.shape[1]) if kind == CELL_GRU else (U.shape[0], U.shape[1])
+    S = 2 * D if kind == CELL_LSTM_DIAG else D
+    cell = make_cell(kind, D, D_in, T, B, _DT[x.dtype], _DT[U.dtype], 1, _stream())
+    need = pnr_workspace_bytes_backward(cell)
+    if need == 0:
+        raise PnrError(pnr_last_error())
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    cell.workspace = workspace.data_ptr()
+    cell.workspace_bytes = workspace.numel()
+    f32 = dict(dtype=torch.float32, device=x.device)
+    shapes = {"x": (B, T, D_in), "W": (G * D, D_in), "U": (G, D), "b_x": (G * D,), "b_h": (G * D,), "h0": (B, S)}
+    out = {k: torch.empty(shapes[k], **f32) for k in want}
+    params = PnrParams(_ptr(W), _ptr(U), _ptr(b_x), _ptr(b_h))
+    rc = pnr_backward(cell, params, _ptr(x), _ptr(h0), _ptr(h), _ptr(grad_h), *(_ptr(out.get(k)) for k in
+                                                                              ("x", "W", "U", "b_x", "b_h", "h0")))
+    if rc < 0:
+        raise PnrError(f"pnr_backward returned {rc}: {pnr_last_error()}")
+    out["workspace"] = workspace
+    return out
 
 
 def scan(kind: int, A: torch.Tensor, b: torch.Tensor, tile_len: int = 0) -> torch.Tensor:

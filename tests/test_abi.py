@@ -154,3 +154,22 @@ def test_chunked_requests_are_validated_without_a_gpu():
     assert pnr.pnr_eval_chunked(_cell(kind=pnr.CELL_GRU, D=100), params, 4096, None, 8192, 10, 1e-5,
                                 pnr.JAC_DIAG, 0.0, 100) == pnr.E_UNSUPPORTED
     assert pnr.pnr_eval_chunked(gru, params, 4096, None, 8192, 10, 1e-5, pnr.JAC_FULL, 0.0, 100) == pnr.E_WORKSPACE
+
+
+def test_backward_requests_are_validated_without_a_gpu():
+    params = pnr.PnrParams(1024, 2048, None, None)
+    for kind in (pnr.CELL_GRU_DIAG, pnr.CELL_LSTM_DIAG):
+        c = _cell(kind=kind, B=2, T=1000, D=64, D_in=32)
+        G, S = (4, 128) if kind == pnr.CELL_LSTM_DIAG else (3, 64)
+        n = pnr.pnr_workspace_bytes_backward(c)
+        # gx and its gradient (2 x B*T*G*D), states and their gradient, W transposed, sums
+        low = 4 * (2 * 2 * 1000 * G * 64 + 2 * 2 * 1000 * S + G * 64 * 32 + 2 * 3 * G * 64)
+        assert low <= n < low + 8 * 256
+        args = (c, params, 4096, None, 8192, 8192, None, None, None, None, None, None)
+        assert pnr.pnr_backward(*args) == pnr.E_WORKSPACE
+        assert pnr.pnr_backward(c, params, 4096, None, None, 8192, *[None] * 6) == pnr.E_INVALID
+    dense = _cell(kind=pnr.CELL_GRU, D=16)
+    assert pnr.pnr_workspace_bytes_backward(dense) == 0
+    assert pnr.pnr_backward(dense, params, 4096, None, 8192, 8192, *[None] * 6) == pnr.E_UNSUPPORTED
+    # the cell's jac_every does not matter to the backward pass
+    assert pnr.pnr_workspace_bytes_backward(_cell(jac_every=3)) == pnr.pnr_workspace_bytes_backward(_cell())

@@ -1,0 +1,101 @@
+"""GPU parity of the backward pass (pnr_backward) against the backpropagation-through-time
+oracle (oracle.bptt, pinned by central differences on the CPU).
+
+The states passed in are the sequential fp64 states rounded to fp32 (the backward pass
+takes them as given), the loss gradient g is random; every gradient is compared element
+by element, relative to its largest entry: fp32 arithmetic over a few thousand steps
+stays near 1e-6 of that scale, so the bar is 1e-4 (a dropped term or a wrong sign is
+O(1)).  Lengths span several 1024-step tiles with a ragged tail, and the two cells, both
+input dtypes, B > 1, a given or zero h0 and partial output requests are covered.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from nonlinear_rnn_evaluation_amd import pnr
+from nonlinear_rnn_evaluation_amd import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+NAMES = {"x": "dx", "W": "dW", "U": "dU", "b_x": "db_x", "b_h": "db_h", "h0": "dh0"}
+
+
+def _case(cell, B, T, D, Din, xd=WL.DT_F32, seed=0, h0=True, bh=True):
+    p = WL.random_problem(cell, B, T, D, Din, seed=seed, x_dtype=xd, state_dtype=WL.DT_F32, bias_std=0.3,
+                          h0_std=0.4 if h0 else 0.0)
+    if bh and p["b_h"] is None:
+        p["b_h"] = (torch.randn(p["b_x"].shape, generator=torch.Generator().manual_seed(seed + 1)) * 0.3).float()
+    if not bh:
+        p["b_h"] = None
+    if not h0:
+        p["h0"] = None
+    q = {k: (None if v is None else WL.as_f64(v)) for k, v in p.items()}
+    S = 2 * D if cell == WL.CELL_LSTM_DIAG else D
+    h0q = q["h0"] if q["h0"] is not None else np.zeros((B, S))
+    H = O.sequential(cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], h0q)
+    H32 = H.astype(np.float32)
+    g = np.random.default_rng(seed + 2).normal(size=H.shape).astype(np.float32)
+    ref = O.bptt(cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], h0q, H32.astype(np.float64), g.astype(np.float64))
+    return p, H32, g, ref
+
+
+def _run(cell, p, H32, g, want=tuple(NAMES)):
+    d = {k: (None if v is None else v.to(DEV)) for k, v in p.items()}
+    return pnr.backward(cell, d["W"], d["U"], d["x"], torch.from_numpy(H32).to(DEV), torch.from_numpy(g).to(DEV),
+                        b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"], want=want)
+
+
+def _check(got, ref, names=tuple(NAMES), tol=1e-4):
+    for k in names:
+        a = got[k].double().cpu().numpy()
+        r = ref[NAMES[k]]
+        assert a.shape == r.shape, k
+        scale = max(np.abs(r).max(), 1e-30)
+        err = np.abs(a - r).max() / scale
+        assert err < tol, (k, err)
+
+
+@pytest.mark.parametrize("cell,D,Din", [(WL.CELL_GRU_DIAG, 6, 5), (WL.CELL_LSTM_DIAG, 4, 3)])
+@pytest.mark.parametrize("T", [1, 37, 1024, 1025, 2 * 1024 + 301])
+def test_gradients_match_the_oracle(cell, D, Din, T):
+    p, H32, g, ref = _case(cell, 2, T, D, Din, seed=T % 91)
+    print(f"# backward cell={cell} T={T}", flush=True)
+    got = _run(cell, p, H32, g)
+    _check(got, ref)
+
+
+@pytest.mark.parametrize("cell", [WL.CELL_GRU_DIAG, WL.CELL_LSTM_DIAG])
+def test_bf16_inputs_zero_h0_and_no_recurrent_bias(cell):
+    p, H32, g, ref = _case(cell, 3, 1500, 5, 8, xd=WL.DT_BF16, seed=4, h0=False, bh=False)
+    got = _run(cell, p, H32, g)
+    _check(got, ref)
+
+
+def test_partial_requests_and_wide_layers():
+    cell = WL.CELL_GRU_DIAG
+    p, H32, g, ref = _case(cell, 2, 700, 130, 72, seed=6)
+    got = _run(cell, p, H32, g, want=("W", "h0"))
+    assert set(got) == {"W", "h0", "workspace"}
+    _check(got, ref, names=("W", "h0"))
+    got = _run(cell, p, H32, g, want=("x", "U", "b_x"))
+    _check(got, ref, names=("x", "U", "b_x"))
+
+
+def test_many_rows_per_block():
+    """More channels than the grid holds blocks: blocks walk several rows."""
+    cell = WL.CELL_LSTM_DIAG
+    p, H32, g, ref = _case(cell, 2, 300, 700, 4, seed=8)
+    got = _run(cell, p, H32, g)
+    _check(got, ref)
+
+
+def test_empty_sequence():
+    cell = WL.CELL_GRU_DIAG
+    p = WL.random_problem(cell, 2, 0, 3, 2, seed=1, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32)
+    d = {k: (None if v is None else v.to(DEV)) for k, v in p.items()}
+    z = torch.empty(2, 0, 3, device=DEV)
+    got = pnr.backward(cell, d["W"], d["U"], d["x"], z, z, b_x=d["b_x"], h0=d["h0"])
+    for k in ("W", "U", "b_x", "b_h", "h0"):
+        assert torch.count_nonzero(got[k]) == 0
