@@ -29,7 +29,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0, "f64": 78.6}   # dense, published
 PRIMARY = "gru_quasi"
 DEFAULT_OTHERS = ("tiny_gru,gru_full,gru_diag_long,lstm_diag_long,lstm_diag_long_chunked,lstm_diag_long_stiff,"
-                  "gru_diag_long_elk")
+                  "gru_diag_long_elk,gru_diag_long_bwd,lstm_diag_long_bwd")
 CSRC = "nonlinear_rnn_evaluation_amd/csrc/"
 
 
@@ -267,6 +267,133 @@ def run_workload(name, steps, warmup, mode=None, with_cpu=True, cpu_budget=12.0,
     return rec
 
 
+def adjoint_bytes(w):
+    """Algorithmic HBM bytes of the backward pass's adjoint kernel: it reads the gate
+    pre-activations (G fp32 per channel and step), the states and dL/ds (4 B each per state
+    element), and writes the pre-activation gradients (G per channel and step, in the
+    input's type: bf16 for bf16 inputs)."""
+    from nonlinear_rnn_evaluation_amd import workloads as WL
+    ge = 2 if w.x_dtype == WL.DT_BF16 else 4
+    n_bt = w.B * w.T
+    return n_bt * (w.G * w.D * (4 + ge) + 2 * w.S * 4)
+
+
+def run_backward(name, steps, warmup, parity=True):
+    """The backward pass (pnr_backward, every gradient) at the states a forward call
+    converged to, for a seeded random dL/ds.  One step = one backward call."""
+    import numpy as np
+    import torch
+
+    from nonlinear_rnn_evaluation_amd import pnr
+    from nonlinear_rnn_evaluation_amd import workloads as WL
+
+    w = WL.get_workload(name)
+    t_gen = time.perf_counter()
+    p = WL.generate(w)
+    dev = torch.device("cuda:0")
+    d = {k: (None if v is None else v.to(dev)) for k, v in p.items()}
+    fwd = pnr.evaluate(w.cell, d["W"], d["U"], d["x"], b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"],
+                       max_iters=w.max_iters, tol=w.tol, jac_mode=w.jac_modes[0], jac_every=w.jac_every)
+    h = fwd["h"]
+    del fwd
+    torch.cuda.empty_cache()
+    g = torch.randn(h.shape, generator=torch.Generator().manual_seed(w.seed + 7)).to(dev)
+    t_gen = time.perf_counter() - t_gen
+    stream = torch.cuda.current_stream()
+
+    def call(ws=None):
+        return pnr.backward(w.cell, d["W"], d["U"], d["x"], h, g, b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"],
+                            workspace=ws)
+
+    first = call()
+    ws = first["workspace"]
+    for _ in range(max(0, warmup - 1)):
+        call(ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        grads = call(ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+
+    pnr.pnr_profile_enable(True)
+    profs = []
+    for _ in range(steps):
+        call(ws)
+        profs.append(pnr.pnr_last_profile())
+    pnr.pnr_profile_enable(False)
+    phases = {k: round(sum(pp[k] for pp in profs) / steps, 4) for k in ("total_ms", "proj_ms", "newton_ms", "out_ms")}
+    adj_ms = phases["newton_ms"]
+    bytes_call = adjoint_bytes(w)
+    achieved = bytes_call / (adj_ms * 1e-3) / 1e9 if adj_ms > 0 else 0.0
+    ksrc = CSRC + "diag_iter.hip"
+    traffic = None
+    pmc_path = os.path.join(ROOT, "profiles", f"newton_kernel_{name}_pmc.json")
+    if os.path.exists(pmc_path):
+        with open(pmc_path) as f:
+            pmc = json.load(f)
+        if pmc.get("kernel_src_sha") == src_hash(ksrc):
+            traffic = pmc.get("bytes_per_launch")
+    roof = {"kernel": "pnr::adjoint_diag_kernel", "avg_launch_us": round(adj_ms * 1e3, 3), "launches_per_step": 1,
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "algorithmic_bytes_per_launch": bytes_call}
+    gemm_flops = 2 * 2.0 * w.B * w.T * w.D_in * w.G * w.D
+    phases["projection"] = "GEMM kernel (recomputed)"
+    phases["proj_tflops"] = round(2.0 * w.B * w.T * w.D_in * w.G * w.D / (phases["proj_ms"] * 1e-3) / 1e12, 2)
+    phases["gradient_products_tflops"] = round(gemm_flops / (phases["out_ms"] * 1e-3) / 1e12, 2)
+    phases["gradient_products"] = ("dW and dx GEMMs in " + ("bf16" if w.x_dtype == WL.DT_BF16 else "fp32")
+                                   + ", with their operand transposes and the batch sums (out_ms)")
+    rec = {"workload": name, "status": 0, "iters": 0, "ms_per_step": round(ms, 4),
+           "value": (w.B * w.T) / (ms * 1e-3), "wall_s": round(wall, 3), "gen_s": round(t_gen, 2),
+           "roofline": roof, "phases_ms": phases, "mfma": None, "jac_mode": "exact (adjoint)",
+           "config": w.describe()}
+    if parity:
+        rec["parity"] = backward_parity(w, p, h, g, grads)
+    del ws, grads, first, d, h, g
+    torch.cuda.empty_cache()
+    return rec
+
+
+def backward_parity(w, p, h, g, grads):
+    """Gradients of a sample of channels against the BPTT oracle on the channel-restricted
+    sub-problem (channels are independent in the diagonal-recurrence cells, so the sample's
+    dW rows, dU, db_x, db_h and dh0 columns are exactly those of the sub-problem; dx mixes
+    all channels and is left to the tests).  Max error relative to each gradient's scale."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+    from oracle.sequential import output_channel_columns
+    from nonlinear_rnn_evaluation_amd import workloads as WL
+
+    n_ch = 8 if w.B * w.T > 100000 else 32
+    ch = np.linspace(0, w.D - 1, n_ch).round().astype(int)
+    W, U, bx, h0 = (WL.as_f64(p[k]) for k in ("W", "U", "b_x", "h0"))
+    bh = None if p["b_h"] is None else WL.as_f64(p["b_h"])
+    Wc, Uc, bxc, bhc, h0c, _ = O.restrict_channels(w.cell, w.D, W, U, bx, bh, h0, ch)
+    cols = torch.from_numpy(output_channel_columns(w.cell, w.D, ch)).to(h.device)
+    Hc = h[:, :, cols].double().cpu().numpy()
+    gc = g[:, :, cols].double().cpu().numpy()
+    xs = p["x"].float().numpy() if p["x"].dtype == torch.bfloat16 else p["x"].numpy()
+    t0 = time.perf_counter()
+    ref = O.bptt(w.cell, Wc, Uc, bxc, bhc, xs, h0c, Hc, gc)
+    el = time.perf_counter() - t0
+    rows = (np.arange(w.G)[:, None] * w.D + ch[None, :]).reshape(-1)
+    got = {"dW": grads["W"][torch.from_numpy(rows).to(h.device)], "dU": grads["U"][:, torch.from_numpy(ch).to(h.device)],
+           "db_x": grads["b_x"][torch.from_numpy(rows).to(h.device)],
+           "db_h": grads["b_h"][torch.from_numpy(rows).to(h.device)], "dh0": grads["h0"][:, cols]}
+    rel = {}
+    for k, v in got.items():
+        r = ref[k]
+        rel[k] = float(np.abs(v.double().cpu().numpy() - r).max() / max(np.abs(r).max(), 1e-30))
+    return {"max_rel": rel, "vs": "fp64 BPTT oracle", "oracle_s": round(el, 2),
+            "sample": f"{n_ch} of {w.D} channels (evenly spaced), all {w.B}x{w.T} steps"}
+
+
 def oracle_leg(w, p, out, with_cpu, budget):
     """Sequential fp64 oracle on the same inputs: timed (bounded sample) and compared."""
     import numpy as np
@@ -352,6 +479,10 @@ def main():
         for name in args.others.split(","):
             from nonlinear_rnn_evaluation_amd import workloads as WL
             w = WL.get_workload(name)
+            if w.backward:
+                print(f"# bench: {name} (backward)", file=sys.stderr, flush=True)
+                others.append(run_backward(name, args.other_steps, args.other_warmup))
+                continue
             for mode in w.jac_modes:
                 print(f"# bench: {name} mode {mode}", file=sys.stderr, flush=True)
                 r = run_workload(name, args.other_steps, args.other_warmup, mode=mode, with_cpu=False)

@@ -671,13 +671,13 @@ int validate_backward(const pnr_cell* c) {
 BwdLayout make_bwd_layout(const pnr_cell* c) {
   BwdLayout l;
   const size_t B = c->B, T = c->T, D = c->D, Din = c->D_in, G = gates(c->kind), S = states(c->kind, c->D);
-  const size_t gd = B * T * G * D * sizeof(float);
+  const size_t ge = dsize(c->x_dtype);   // the gradient GEMMs' operand type: that of x
   size_t off = 0;
-  l.gx = off; off = align_up(off + gd);                       // gx, then dL/dgx transposed
-  const size_t st = 2 * B * T * S, xt = B * T * Din;
-  l.states = off; off = align_up(off + sizeof(float) * (st > xt ? st : xt));   // h, dL/dh; then x transposed
-  l.dgx = off; off = align_up(off + gd);
-  l.wt = off; off = align_up(off + sizeof(float) * G * D * Din);
+  l.gx = off; off = align_up(off + B * T * G * D * sizeof(float));   // gx, then dL/dgx transposed
+  const size_t st = 2 * B * T * S * sizeof(float), xt = B * T * Din * ge;
+  l.states = off; off = align_up(off + (st > xt ? st : xt));          // h, dL/dh; then x transposed
+  l.dgx = off; off = align_up(off + B * T * G * D * ge);
+  l.wt = off; off = align_up(off + ge * G * D * Din);
   l.part = off; off = align_up(off + sizeof(float) * B * 3 * G * D);
   l.total = off;
   return l;
@@ -722,7 +722,8 @@ int pnr_backward(const pnr_cell* cell, const pnr_params* params, const void* x, 
   float* gx = reinterpret_cast<float*>(ws + l.gx);
   float* hT = reinterpret_cast<float*>(ws + l.states);
   float* gT = hT + (size_t)B * T * S;
-  float* dgx = reinterpret_cast<float*>(ws + l.dgx);
+  void* dgx = ws + l.dgx;
+  const int ge = cell->x_dtype;   // PNR_F32 or PNR_BF16: the gradient GEMMs run in the input's type
   float* part = reinterpret_cast<float*>(ws + l.part);
   const size_t BT = (size_t)B * T;
 
@@ -733,8 +734,8 @@ int pnr_backward(const pnr_cell* cell, const pnr_params* params, const void* x, 
   Mark m_proj = mark_begin(st);
   PNR_HIP(launch_gemm(cell->x_dtype, PNR_F32, g, st));
   mark_end(m_proj, st);
-  PNR_HIP(launch_transpose(h, PNR_F32, hT, B, T, S, st));
-  PNR_HIP(launch_transpose(grad_h, PNR_F32, gT, B, T, S, st));
+  PNR_HIP(launch_transpose(h, PNR_F32, hT, PNR_F32, B, T, S, st));
+  PNR_HIP(launch_transpose(grad_h, PNR_F32, gT, PNR_F32, B, T, S, st));
 
   BwdArgs a{};
   a.gx = gx;
@@ -749,6 +750,7 @@ int pnr_backward(const pnr_cell* cell, const pnr_params* params, const void* x, 
   a.B = B; a.D = D; a.T = T;
   a.tiles_per_row = (T + PNR_BLOCK * adjoint_items_per_thread() - 1) / (PNR_BLOCK * adjoint_items_per_thread());
   a.n_rows = B * D;
+  a.dgx_bf16 = ge == PNR_BF16;
   Mark m_adj = mark_begin(st);
   PNR_HIP(launch_adjoint_diag(kind, a, num_cu, st));
   mark_end(m_adj, st);
@@ -758,19 +760,19 @@ int pnr_backward(const pnr_cell* cell, const pnr_params* params, const void* x, 
                                 static_cast<float*>(grad_b_x), st));
   if (grad_W) {
     // dW[m][k] = sum_{b,t} dgx[m][(b,t)] x[(b,t)][k]: x transposed to [k][(b,t)]
-    float* xT = hT;   // the transposed states are no longer needed
-    PNR_HIP(launch_transpose(x, cell->x_dtype, xT, 1, (int)BT, Din, st));
+    void* xT = hT;   // the transposed states are no longer needed
+    PNR_HIP(launch_transpose(x, cell->x_dtype, xT, ge, 1, (int)BT, Din, st));
     GemmArgs gw{dgx, xT, nullptr, grad_W, G * D, Din, (int)BT, 0, 0, 0, (int)BT, (int)BT, Din, 1, 0};
-    PNR_HIP(launch_gemm(PNR_F32, PNR_F32, gw, st));
+    PNR_HIP(launch_gemm(ge, PNR_F32, gw, st));
   }
   if (grad_x) {
     // dx[(b,t)][k] = sum_m dgx[m][(b,t)] W[m][k]: dgx transposed to [(b,t)][m], W to [k][m]
-    float* dgxT = gx;   // gx is no longer needed
-    float* WT = reinterpret_cast<float*>(ws + l.wt);
-    PNR_HIP(launch_transpose(dgx, PNR_F32, dgxT, 1, G * D, (int)BT, st));
-    PNR_HIP(launch_transpose(params->W, cell->x_dtype, WT, 1, G * D, Din, st));
+    void* dgxT = gx;   // gx is no longer needed
+    void* WT = ws + l.wt;
+    PNR_HIP(launch_transpose(dgx, ge, dgxT, ge, 1, G * D, (int)BT, st));
+    PNR_HIP(launch_transpose(params->W, cell->x_dtype, WT, ge, 1, G * D, Din, st));
     GemmArgs gxg{dgxT, WT, nullptr, grad_x, (int)BT, Din, G * D, 0, 0, 0, G * D, G * D, Din, 1, 0};
-    PNR_HIP(launch_gemm(PNR_F32, PNR_F32, gxg, st));
+    PNR_HIP(launch_gemm(ge, PNR_F32, gxg, st));
   }
   mark_end(m_grads, st);
   mark_end(m_first, st);

@@ -1136,7 +1136,22 @@ struct BwdShared {
 // One tile of the backward walk.  Thread t takes the run of N steps that starts at step
 // (PNR_BLOCK - 1 - t) * N of the tile.  acc: the thread's sums (dU, db_h, db_x per gate).
 // Returns mu at the thread's first step.
-template <int CELL, int N>
+// N bf16 values at row[tb..tb+N) (8-byte stores when T is a multiple of 4), masked at T.
+__device__ __forceinline__ void store_n_bf16(__bf16* __restrict__ row, int tb, int T, bool vec, int N,
+                                             const float* in) {
+  if (vec && tb + N <= T) {
+    for (int v = 0; v < N / 4; ++v) {
+      typedef __bf16 bf4_t __attribute__((ext_vector_type(4)));
+      bf4_t x = {(__bf16)in[4 * v], (__bf16)in[4 * v + 1], (__bf16)in[4 * v + 2], (__bf16)in[4 * v + 3]};
+      *reinterpret_cast<bf4_t*>(row + tb + 4 * v) = x;
+    }
+  } else {
+    for (int i = 0; i < N; ++i)
+      if (tb + i < T) row[tb + i] = (__bf16)in[i];
+  }
+}
+
+template <int CELL, int N, bool BF16OUT>
 __device__ __forceinline__ typename DeltaOf<typename DiagCell<CELL>::E>::T adjoint_tile(
     const BwdArgs& a, BwdShared<CELL>& sh, int b, int d, int seg, float* acc) {
   using C = DiagCell<CELL>;
@@ -1230,15 +1245,18 @@ __device__ __forceinline__ typename DeltaOf<typename DiagCell<CELL>::E>::T adjoi
     }
   }
 #pragma unroll
-  for (int gg = 0; gg < NG; ++gg)
-    store_n(a.dgx + (((size_t)gg * D + d) * a.B + b) * T, tb, T, vec, N, da[gg]);
+  for (int gg = 0; gg < NG; ++gg) {
+    const size_t o = (((size_t)gg * D + d) * a.B + b) * T;
+    if constexpr (BF16OUT) store_n_bf16(static_cast<__bf16*>(a.dgx) + o, tb, T, vec, N, da[gg]);
+    else store_n(static_cast<float*>(a.dgx) + o, tb, T, vec, N, da[gg]);
+  }
   __syncthreads();   // everyone has read tot and carry
   if (tid == PNR_BLOCK - 1) sh.carry = mu;   // mu at the tile's first step
   __syncthreads();
   return mu;
 }
 
-template <int CELL, int N>
+template <int CELL, int N, bool BF16OUT>
 __global__ void __launch_bounds__(PNR_BLOCK) adjoint_diag_kernel(BwdArgs a) {
   using C = DiagCell<CELL>;
   using Dl = typename DeltaOf<typename C::E>::T;
@@ -1253,7 +1271,7 @@ __global__ void __launch_bounds__(PNR_BLOCK) adjoint_diag_kernel(BwdArgs a) {
     if (tid == 0) sh.carry = DeltaOf<typename C::E>::zero();
     __syncthreads();
     Dl mu = DeltaOf<typename C::E>::zero();
-    for (int seg = a.tiles_per_row - 1; seg >= 0; --seg) mu = adjoint_tile<CELL, N>(a, sh, b, d, seg, acc);
+    for (int seg = a.tiles_per_row - 1; seg >= 0; --seg) mu = adjoint_tile<CELL, N, BF16OUT>(a, sh, b, d, seg, acc);
     if (tid == PNR_BLOCK - 1 && a.dh0) {   // this thread's run starts at step 0: mu = dL/dh0
       const int S = C::SP * a.D;
       if constexpr (CELL == PNR_CELL_GRU_DIAG) {
@@ -1283,8 +1301,12 @@ constexpr int kAdjN = 4;   // steps per thread
 int adjoint_items_per_thread() { return kAdjN; }
 
 hipError_t launch_adjoint_diag(int cell, const BwdArgs& a, int num_cu, hipStream_t st) {
-  const void* fn = cell == PNR_CELL_GRU_DIAG ? (const void*)adjoint_diag_kernel<PNR_CELL_GRU_DIAG, kAdjN>
-                                             : (const void*)adjoint_diag_kernel<PNR_CELL_LSTM_DIAG, kAdjN>;
+  const void* fn =
+      cell == PNR_CELL_GRU_DIAG
+          ? (a.dgx_bf16 ? (const void*)adjoint_diag_kernel<PNR_CELL_GRU_DIAG, kAdjN, true>
+                        : (const void*)adjoint_diag_kernel<PNR_CELL_GRU_DIAG, kAdjN, false>)
+          : (a.dgx_bf16 ? (const void*)adjoint_diag_kernel<PNR_CELL_LSTM_DIAG, kAdjN, true>
+                        : (const void*)adjoint_diag_kernel<PNR_CELL_LSTM_DIAG, kAdjN, false>);
   const int per_cu = cached_occupancy(fn, 0);
   if (per_cu < 1) return hipErrorInvalidConfiguration;
   long g = (long)per_cu * num_cu;

@@ -102,12 +102,13 @@ struct BwdArgs {
   const float* h0;     // [B][S] or nullptr
   const float* hT;     // states [B][S][T]
   const float* gT;     // dL/ds [B][S][T]
-  float* dgx;          // out: dL/d(pre-activation) [G*D][B*T]
+  void* dgx;           // out: dL/d(pre-activation) [G*D][B*T], fp32 or (dgx_bf16) bf16
   float* part;         // out: per batch element sums [B][3][G][D] (dU, db_h, db_x)
   float* dh0;          // out: dL/dh0 [B][S] or nullptr
   int B, D, T;
   int tiles_per_row;
   int n_rows;          // B * D
+  int dgx_bf16;
 };
 int adjoint_items_per_thread();
 hipError_t launch_adjoint_diag(int cell, const BwdArgs& a, int num_cu, hipStream_t st);
@@ -183,8 +184,9 @@ hipError_t launch_gemm(int in_dtype, int out_dtype, const GemmArgs& g, hipStream
 // Per-block residual words: three per block (one per pass modulo 3) for the barrier-free
 // loops, which tag each word with its pass.
 constexpr size_t kPartialWords = 3 * (size_t)kMaxGrid;
-// [Z][R][C] (PNR_F32 or PNR_BF16) -> [Z][C][R] fp32.
-hipError_t launch_transpose(const void* in, int in_dtype, float* out, int Z, int R, int C, hipStream_t st);
+// [Z][R][C] -> [Z][C][R]; in and out each PNR_F32 or PNR_BF16 (round to nearest even).
+hipError_t launch_transpose(const void* in, int in_dtype, void* out, int out_dtype, int Z, int R, int C,
+                            hipStream_t st);
 // p[0..n) = 0 (a kernel, so that the call can sit in a captured graph).
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t st);
 // out_q[j] = sum_b part[b][q][j], q = 0..2, j < n (null outputs are skipped).

@@ -127,17 +127,17 @@ hipError_t launch_dense_output(const Tt* const* bufs, const Ctrl* ctrl, Tt* h_ou
 template hipError_t launch_dense_output<float>(const float* const*, const Ctrl*, float*, size_t, hipStream_t);
 template hipError_t launch_dense_output<double>(const double* const*, const Ctrl*, double*, size_t, hipStream_t);
 
-// [Z][R][C] (fp32 or bf16) -> [Z][C][R] fp32 through a 32 x 33 LDS tile: reads run along
-// C and writes along R, both coalesced.
-template <typename Tin>
-__global__ void __launch_bounds__(256) transpose_kernel(const Tin* __restrict__ in, float* __restrict__ out, int R,
+// [Z][R][C] -> [Z][C][R] (fp32 or bf16 in, fp32 or bf16 out) through a 32 x 33 LDS tile:
+// reads run along C and writes along R, both coalesced.
+template <typename Tin, typename Tout>
+__global__ void __launch_bounds__(256) transpose_kernel(const Tin* __restrict__ in, Tout* __restrict__ out, int R,
                                                         int C) {
   __shared__ float tile[32][33];
   const size_t z = blockIdx.z;
   const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8
   const Tin* src = in + z * (size_t)R * C;
-  float* dst = out + z * (size_t)R * C;
+  Tout* dst = out + z * (size_t)R * C;
   for (int k = ty; k < 32; k += 8) {
     const int r = r0 + k, c = c0 + tx;
     tile[k][tx] = (r < R && c < C) ? (float)src[(size_t)r * C + c] : 0.f;
@@ -145,19 +145,22 @@ __global__ void __launch_bounds__(256) transpose_kernel(const Tin* __restrict__ 
   __syncthreads();
   for (int k = ty; k < 32; k += 8) {
     const int c = c0 + k, r = r0 + tx;
-    if (c < C && r < R) dst[(size_t)c * R + r] = tile[tx][k];
+    if (c < C && r < R) dst[(size_t)c * R + r] = (Tout)tile[tx][k];
   }
 }
 
-hipError_t launch_transpose(const void* in, int in_dtype, float* out, int Z, int R, int C, hipStream_t st) {
+hipError_t launch_transpose(const void* in, int in_dtype, void* out, int out_dtype, int Z, int R, int C,
+                            hipStream_t st) {
   if (Z <= 0 || R <= 0 || C <= 0) return hipSuccess;
   dim3 grid((C + 31) / 32, (R + 31) / 32, Z);
-  if (in_dtype == PNR_BF16)
-    hipLaunchKernelGGL(transpose_kernel<__bf16>, grid, dim3(256), 0, st, static_cast<const __bf16*>(in), out, R, C);
-  else if (in_dtype == PNR_F32)
-    hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(in), out, R, C);
-  else
-    return hipErrorInvalidValue;
+#define PNR_TR(TI, TO) \
+  hipLaunchKernelGGL((transpose_kernel<TI, TO>), grid, dim3(256), 0, st, static_cast<const TI*>(in), static_cast<TO*>(out), R, C)
+  if (in_dtype == PNR_BF16 && out_dtype == PNR_F32) PNR_TR(__bf16, float);
+  else if (in_dtype == PNR_F32 && out_dtype == PNR_F32) PNR_TR(float, float);
+  else if (in_dtype == PNR_BF16 && out_dtype == PNR_BF16) PNR_TR(__bf16, __bf16);
+  else if (in_dtype == PNR_F32 && out_dtype == PNR_BF16) PNR_TR(float, __bf16);
+  else return hipErrorInvalidValue;
+#undef PNR_TR
   return hipGetLastError();
 }
 

@@ -80,6 +80,7 @@ class Workload:
     seed: int = 0
     damping: Optional[float] = None   # set: the damped (quasi-ELK) step with this strength
     chunk_len: Optional[int] = None   # set: evaluated in chunks of this many steps
+    backward: bool = False            # the measured step is the backward pass at the evaluated states
 
     @property
     def G(self) -> int:
@@ -99,6 +100,7 @@ class Workload:
             "jac_every": self.jac_every, "tol": self.tol, "max_iters": self.max_iters,
             **({"damping": self.damping} if self.damping is not None else {}),
             **({"chunk_len": self.chunk_len} if self.chunk_len is not None else {}),
+            **({"pass": "backward"} if self.backward else {}),
         }
 
 
@@ -132,6 +134,9 @@ def named_workloads() -> dict:
     # state: the workspace covers one chunk (16x less), and short chunks need fewer iterations
     w["lstm_diag_long_chunked"] = dataclasses.replace(w["lstm_diag_long"], name="lstm_diag_long_chunked",
                                                       chunk_len=8192)
+    # the backward pass (all gradients) at the converged states of the two long workloads
+    for base in ("gru_diag_long", "lstm_diag_long"):
+        w[base + "_bwd"] = dataclasses.replace(w[base], name=base + "_bwd", backward=True)
     # the stiff LSTM with the damped step on the diagonal Jacobian (quasi-ELK), which
     # converges where both undamped variants do not
     w["lstm_diag_long_stiff_elk"] = dataclasses.replace(

@@ -5,7 +5,8 @@ The states passed in are the sequential fp64 states rounded to fp32 (the backwar
 takes them as given), the loss gradient g is random; every gradient is compared element
 by element, relative to its largest entry: fp32 arithmetic over a few thousand steps
 stays near 1e-6 of that scale, so the bar is 1e-4 (a dropped term or a wrong sign is
-O(1)).  Lengths span several 1024-step tiles with a ragged tail, and the two cells, both
+O(1)).  With bf16 inputs the two gradient products (dW, dx) run in bf16 and are held
+to a bound derived from that rounding instead.  Lengths span several 1024-step tiles with a ragged tail, and the two cells, both
 input dtypes, B > 1, a given or zero h0 and partial output requests are covered.
 """
 import numpy as np
@@ -68,9 +69,24 @@ def test_gradients_match_the_oracle(cell, D, Din, T):
 
 @pytest.mark.parametrize("cell", [WL.CELL_GRU_DIAG, WL.CELL_LSTM_DIAG])
 def test_bf16_inputs_zero_h0_and_no_recurrent_bias(cell):
+    """With bf16 inputs the two gradient products run in bf16 like the forward projection:
+    the pre-activation gradients are rounded to bf16 (relative error <= 2^-9 each, x and W
+    are bf16 already) and summed in fp32.  So each entry of dW and dx is within
+    2^-9 * sum |dgx| |x| (resp. |dgx| |W|) of the exact value; the bar doubles that for the
+    fp32 sums.  The other gradients do not pass through those products."""
     p, H32, g, ref = _case(cell, 3, 1500, 5, 8, xd=WL.DT_BF16, seed=4, h0=False, bh=False)
     got = _run(cell, p, H32, g)
-    _check(got, ref)
+    _check(got, ref, names=("U", "b_x", "b_h", "h0"))
+    B, T = 3, 1500
+    dgx = np.abs(ref["dgx"].reshape(B * T, -1))
+    xa = np.abs(WL.as_f64(p["x"]).reshape(B * T, -1))
+    Wa = np.abs(WL.as_f64(p["W"]))
+    for k, bound in (("W", dgx.T @ xa), ("x", (dgx @ Wa).reshape(B, T, -1))):
+        r = ref[NAMES[k]]
+        err = np.abs(got[k].double().cpu().numpy() - r)
+        assert np.all(err <= 2.0 ** -8 * bound + 1e-5 * np.abs(r).max()), (k, (err / (bound + 1e-30)).max())
+        # and the rounding is really there: bf16 products, not an fp32 path
+        assert err.max() > 0
 
 
 def test_partial_requests_and_wide_layers():
