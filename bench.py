@@ -231,7 +231,7 @@ def run_workload(name, steps, warmup, mode=None, with_cpu=True, cpu_budget=12.0,
               "us_per_pass": round(newton_ms * 1e3 / max(passes, 1), 3)}
     hbm = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-           "algorithmic_bytes_per_launch": bytes_call}
+           "algorithmic_bytes_per_launch": round(bytes_call / launches)}
     if fused:
         # The quasi-Newton dense kernel keeps every iterate in LDS: its HBM traffic is the
         # inputs, gx and the output only, so the bytes a streaming design would move do not
@@ -472,8 +472,12 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
-    prim = run_workload(args.workload, args.steps, args.warmup, with_cpu=not args.no_cpu_baseline,
-                        cpu_budget=args.cpu_budget)
+    from nonlinear_rnn_evaluation_amd import workloads as WL
+    if WL.get_workload(args.workload).backward:
+        prim = run_backward(args.workload, args.steps, args.warmup)
+    else:
+        prim = run_workload(args.workload, args.steps, args.warmup, with_cpu=not args.no_cpu_baseline,
+                            cpu_budget=args.cpu_budget)
     others = []
     if args.others and args.others != "none":
         for name in args.others.split(","):
