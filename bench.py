@@ -120,12 +120,13 @@ def iteration_bytes(w, k, iters_total, resid=False):
     return gx + cur + h + jac
 
 
-def mfma_counters(name, mode, phases):
+def mfma_counters(name, mode, phases, launches=1):
     """MFMA utilisation of the workload's matrix-core kernels, from the committed rocprofv3
     counter summary (profiles/mfma_<workload>_pmc.json): busy fraction of the matrix
     cores (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs) and the counted MFMA
     flops per launch, which over this run's live launch time give TFLOP/s.  Entries whose
-    kernel source changed since the counters were taken are left out."""
+    kernel source changed since the counters were taken are left out.  `launches`: launches
+    of each kernel per step (chunked calls launch one of each per chunk)."""
     path = os.path.join(ROOT, "profiles", f"mfma_{name}_pmc.json")
     if not os.path.exists(path):
         return None
@@ -138,6 +139,7 @@ def mfma_counters(name, mode, phases):
         if k["kernel_src_sha"] != src_hash(k["kernel_src"]):
             continue
         live_ms = phases["proj_ms"] if "gemm" in k["kernel"] else phases["newton_ms"]
+        live_ms = live_ms / launches if live_ms else None
         tf = k["mfma_flops_per_launch"] / (live_ms * 1e-3) / 1e12 if live_ms else None
         pk = MFMA_PEAK_TFLOPS[k["dtype"]]
         out.append({"kernel": k["kernel"].split("(")[0], "dtype": k["dtype"],
@@ -255,7 +257,7 @@ def run_workload(name, steps, warmup, mode=None, with_cpu=True, cpu_budget=12.0,
     rec = {"workload": name, "status": int(status), "iters": int(iters), "ms_per_step": round(ms, 4),
            "value": (w.B * w.T) / (ms * 1e-3) if status == 0 else None,
            "wall_s": round(wall, 3), "gen_s": round(t_gen, 2), "roofline": roof, "phases_ms": phases,
-           "mfma": mfma_counters(name, mode, phases),
+           "mfma": mfma_counters(name, mode, phases, launches),
            "residual": last["residual"], "jac_mode": ["full", "diag", "zero"][mode],
            "config": w.describe()}
 
@@ -349,7 +351,10 @@ def run_backward(name, steps, warmup, parity=True):
                                    + ", with their operand transposes and the batch sums (out_ms)")
     rec = {"workload": name, "status": 0, "iters": 0, "ms_per_step": round(ms, 4),
            "value": (w.B * w.T) / (ms * 1e-3), "wall_s": round(wall, 3), "gen_s": round(t_gen, 2),
-           "roofline": roof, "phases_ms": phases, "mfma": None, "jac_mode": "exact (adjoint)",
+           "roofline": roof, "phases_ms": phases, "jac_mode": "exact (adjoint)",
+           # the three GEMMs of a backward call (projection, dW, dx) share one counter
+           # entry; their busy fraction is reported, not a per-launch rate
+           "mfma": mfma_counters(name, w.jac_modes[0], {"proj_ms": None, "newton_ms": None}),
            "config": w.describe()}
     if parity:
         rec["parity"] = backward_parity(w, p, h, g, grads)
