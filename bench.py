@@ -299,7 +299,7 @@ def run_backward(name, steps, warmup, parity=True):
     h = fwd["h"]
     del fwd
     torch.cuda.empty_cache()
-    g = torch.randn(h.shape, generator=torch.Generator().manual_seed(w.seed + 7)).to(dev)
+    g = torch.randn(h.shape, generator=torch.Generator().manual_seed(w.seed + 7), dtype=torch.float32).to(dev)
     t_gen = time.perf_counter() - t_gen
     stream = torch.cuda.current_stream()
 

@@ -116,6 +116,22 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return t.data_ptr()
 
 
+def _check(t: Optional[torch.Tensor], name: str, dtype: torch.dtype, shape: tuple) -> Optional[torch.Tensor]:
+    """The library reads raw memory, so a tensor of another dtype or shape would be
+    reinterpreted, not converted: refuse it."""
+    if t is None:
+        return None
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    return t
+
+
+def _arg(t: Optional[torch.Tensor], name: str, dtype: torch.dtype, shape: tuple) -> Optional[int]:
+    return _ptr(_check(t, name, dtype, shape))
+
+
 def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
@@ -223,7 +239,18 @@ def evaluate(kind: int, W: torch.Tensor, U: torch.Tensor, x: torch.Tensor, *, b_
     B, T, D_in = x.shape
     D = U.shape[1]
     S = 2 * D if kind == CELL_LSTM_DIAG else D
+    if x.dtype not in _DT or U.dtype not in _DT:
+        raise TypeError(f"unsupported dtypes x {x.dtype}, U {U.dtype}")
     xdt, sdt = _DT[x.dtype], _DT[U.dtype]
+    G = 4 if kind == CELL_LSTM_DIAG else 3
+    sd = U.dtype
+    args = dict(W=_check(W, "W", x.dtype, (G * D, D_in)),
+                U=_check(U, "U", sd, (G * D, D) if kind == CELL_GRU else (G, D)),
+                b_x=_check(b_x, "b_x", sd, (G * D,)), b_h=_check(b_h, "b_h", sd, (G * D,)),
+                h0=_check(h0, "h0", sd, (B, S)), x=x)
+    if h_out is not None:
+        _check(h_out, "h_out", sd, (B, T, S))
+    ptrs = {k: _ptr(v) for k, v in args.items()}
     cell = make_cell(kind, D, D_in, T, B, xdt, sdt, jac_every, _stream())
     if chunk_len is not None:
         need = pnr_workspace_bytes_chunked(cell, jac_mode, damping or 0.0, chunk_len)
@@ -239,14 +266,15 @@ def evaluate(kind: int, W: torch.Tensor, U: torch.Tensor, x: torch.Tensor, *, b_
     cell.workspace_bytes = workspace.numel()
     if h_out is None:
         h_out = torch.empty(B, T, S, dtype=U.dtype, device=x.device)
-    params = PnrParams(_ptr(W), _ptr(U), _ptr(b_x), _ptr(b_h))
+    out = _arg(h_out, "h_out", sd, (B, T, S))
+    params = PnrParams(ptrs["W"], ptrs["U"], ptrs["b_x"], ptrs["b_h"])
     if chunk_len is not None:
-        rc = pnr_eval_chunked(cell, params, _ptr(x), _ptr(h0), _ptr(h_out), max_iters, tol, jac_mode,
+        rc = pnr_eval_chunked(cell, params, ptrs["x"], ptrs["h0"], out, max_iters, tol, jac_mode,
                               damping or 0.0, chunk_len)
     elif damping is None:
-        rc = pnr_eval(cell, params, _ptr(x), _ptr(h0), _ptr(h_out), max_iters, tol, jac_mode)
+        rc = pnr_eval(cell, params, ptrs["x"], ptrs["h0"], out, max_iters, tol, jac_mode)
     else:
-        rc = pnr_eval_damped(cell, params, _ptr(x), _ptr(h0), _ptr(h_out), max_iters, tol, jac_mode, damping)
+        rc = pnr_eval_damped(cell, params, ptrs["x"], ptrs["h0"], out, max_iters, tol, jac_mode, damping)
     if rc < 0:
         raise PnrError(f"pnr_eval returned {rc}: {pnr_last_error()}")
     return {"h": h_out, "status": rc, "iters": pnr_iters_used(), "residual": pnr_last_residual(),
@@ -262,6 +290,13 @@ def backward(kind: int, W: torch.Tensor, U: torch.Tensor, x: torch.Tensor, h: to
     B, T, D_in = x.shape
     G, D = (U.shape[0] // U.shape[1], U.shape[1]) if kind == CELL_GRU else (U.shape[0], U.shape[1])
     S = 2 * D if kind == CELL_LSTM_DIAG else D
+    if x.dtype not in _DT or U.dtype not in _DT:
+        raise TypeError(f"unsupported dtypes x {x.dtype}, U {U.dtype}")
+    sd = U.dtype
+    args = dict(h=_check(h, "h", sd, (B, T, S)), grad_h=_check(grad_h, "grad_h", sd, (B, T, S)),
+                W=_check(W, "W", x.dtype, (G * D, D_in)), b_x=_check(b_x, "b_x", sd, (G * D,)),
+                b_h=_check(b_h, "b_h", sd, (G * D,)), h0=_check(h0, "h0", sd, (B, S)), U=U, x=x)
+    ptrs = {k: _ptr(v) for k, v in args.items()}
     cell = make_cell(kind, D, D_in, T, B, _DT[x.dtype], _DT[U.dtype], 1, _stream())
     need = pnr_workspace_bytes_backward(cell)
     if need == 0:
@@ -273,9 +308,9 @@ def backward(kind: int, W: torch.Tensor, U: torch.Tensor, x: torch.Tensor, h: to
     f32 = dict(dtype=torch.float32, device=x.device)
     shapes = {"x": (B, T, D_in), "W": (G * D, D_in), "U": (G, D), "b_x": (G * D,), "b_h": (G * D,), "h0": (B, S)}
     out = {k: torch.empty(shapes[k], **f32) for k in want}
-    params = PnrParams(_ptr(W), _ptr(U), _ptr(b_x), _ptr(b_h))
-    rc = pnr_backward(cell, params, _ptr(x), _ptr(h0), _ptr(h), _ptr(grad_h), *(_ptr(out.get(k)) for k in
-                                                                              ("x", "W", "U", "b_x", "b_h", "h0")))
+    params = PnrParams(ptrs["W"], ptrs["U"], ptrs["b_x"], ptrs["b_h"])
+    rc = pnr_backward(cell, params, ptrs["x"], ptrs["h0"], ptrs["h"], ptrs["grad_h"],
+                      *(_ptr(out.get(k)) for k in ("x", "W", "U", "b_x", "b_h", "h0")))
     if rc < 0:
         raise PnrError(f"pnr_backward returned {rc}: {pnr_last_error()}")
     out["workspace"] = workspace
@@ -285,6 +320,10 @@ def backward(kind: int, W: torch.Tensor, U: torch.Tensor, x: torch.Tensor, h: to
 def scan(kind: int, A: torch.Tensor, b: torch.Tensor, tile_len: int = 0) -> torch.Tensor:
     """Standalone linear scan d_t = A_t d_{t-1} + b_t (kind 1: [R,T]; kind 2: A [R,4,T], b [R,2,T])."""
     R, T = b.shape[0], b.shape[-1]
+    shapes = {1: ((R, T), (R, T)), 2: ((R, 4, T), (R, 2, T))}.get(kind)
+    if shapes is not None:
+        _check(A, "A", torch.float32, shapes[0])
+        _check(b, "b", torch.float32, shapes[1])
     d = torch.empty_like(b)
     need = pnr_scan_workspace_bytes(kind, R, T, tile_len)
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device=b.device)

@@ -173,3 +173,24 @@ def test_backward_requests_are_validated_without_a_gpu():
     assert pnr.pnr_backward(dense, params, 4096, None, 8192, 8192, *[None] * 6) == pnr.E_UNSUPPORTED
     # the cell's jac_every does not matter to the backward pass
     assert pnr.pnr_workspace_bytes_backward(_cell(jac_every=3)) == pnr.pnr_workspace_bytes_backward(_cell())
+
+
+def test_binding_rejects_tensors_of_the_wrong_dtype_or_shape():
+    """The library reads raw memory: the binding must refuse a tensor whose dtype or shape
+    differs from what the call describes instead of letting it be reinterpreted."""
+    import torch
+    B, T, D, Din = 2, 5, 3, 4
+    W = torch.zeros(3 * D, Din)
+    U = torch.zeros(3, D)
+    x = torch.zeros(B, T, Din)
+    h = torch.zeros(B, T, D)
+    with pytest.raises(TypeError):
+        pnr.backward(pnr.CELL_GRU_DIAG, W, U, x, h, h.double())
+    with pytest.raises(ValueError):
+        pnr.backward(pnr.CELL_GRU_DIAG, W, U, x, h, torch.zeros(B, T, D + 1))
+    with pytest.raises(TypeError):
+        pnr.evaluate(pnr.CELL_GRU_DIAG, W.double(), U, x)
+    with pytest.raises(TypeError):
+        pnr.evaluate(pnr.CELL_GRU_DIAG, W, U, x, h0=torch.zeros(B, D, dtype=torch.float64))
+    with pytest.raises(ValueError):
+        pnr.evaluate(pnr.CELL_GRU_DIAG, W, U, x, b_x=torch.zeros(3 * D + 1))

@@ -27,7 +27,8 @@ def _case(cell, B, T, D, Din, xd=WL.DT_F32, seed=0, h0=True, bh=True):
     p = WL.random_problem(cell, B, T, D, Din, seed=seed, x_dtype=xd, state_dtype=WL.DT_F32, bias_std=0.3,
                           h0_std=0.4 if h0 else 0.0)
     if bh and p["b_h"] is None:
-        p["b_h"] = (torch.randn(p["b_x"].shape, generator=torch.Generator().manual_seed(seed + 1)) * 0.3).float()
+        p["b_h"] = torch.randn(p["b_x"].shape, generator=torch.Generator().manual_seed(seed + 1),
+                               dtype=torch.float32) * 0.3
     if not bh:
         p["b_h"] = None
     if not h0:
@@ -111,7 +112,7 @@ def test_empty_sequence():
     cell = WL.CELL_GRU_DIAG
     p = WL.random_problem(cell, 2, 0, 3, 2, seed=1, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32)
     d = {k: (None if v is None else v.to(DEV)) for k, v in p.items()}
-    z = torch.empty(2, 0, 3, device=DEV)
+    z = torch.empty(2, 0, 3, device=DEV, dtype=torch.float32)
     got = pnr.backward(cell, d["W"], d["U"], d["x"], z, z, b_x=d["b_x"], h0=d["h0"])
     for k in ("W", "U", "b_x", "b_h", "h0"):
         assert torch.count_nonzero(got[k]) == 0

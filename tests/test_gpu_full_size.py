@@ -2,7 +2,9 @@
 and launch configuration the benchmark times, against the fp64 sequential oracle.
 
 Dense-GRU workloads are compared on every output.  The damped (quasi-ELK) variant of the
-long diagonal GRU is included: it converges to the same trajectory.  For the diagonal-recurrence cells a
+long diagonal GRU and the chunked long LSTM are included: they converge to the same
+trajectory.  The backward pass is checked at full size on sampled channels against the
+BPTT oracle (last test).  For the diagonal-recurrence cells a
 set of evenly spaced channels is compared: with elementwise recurrent weights a channel
 subset is an exact sub-problem of its own (oracle.restrict_channels), so the oracle
 computes those outputs one channel group at a time.  Bar: 1e-4 max-abs for fp32 state,
@@ -27,11 +29,18 @@ def _check(name, mode):
     print(f"# full-size parity: {name} mode {mode}", flush=True)
     res = pnr.evaluate(w.cell, d["W"], d["U"], d["x"], b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"],
                        max_iters=w.max_iters, tol=w.tol, jac_mode=mode, jac_every=w.jac_every,
-                       damping=w.damping)
+                       damping=w.damping, chunk_len=w.chunk_len)
     assert res["status"] == pnr.OK, (name, res["status"], res["residual"])
-    assert 0 < res["iters"] <= w.max_iters
     assert res["residual"] <= w.tol
-    assert res["history"][res["iters"]] == res["residual"]
+    if w.chunk_len is None:
+        assert 0 < res["iters"] <= w.max_iters
+        assert res["history"][res["iters"]] == res["residual"]
+    else:
+        # one history per chunk, each ending at its first residual within tol
+        n_chunks = -(-w.T // w.chunk_len)
+        ends = [i for i, v in enumerate(res["history"]) if v <= w.tol]
+        assert len(ends) == n_chunks and ends[-1] == len(res["history"]) - 1
+        assert res["iters"] == len(res["history"]) - n_chunks
     h = res["h"]
     assert h.shape == (w.B, w.T, WL.state_size(w.cell, w.D))
     W, U, bx, h0 = (WL.as_f64(p[k]) for k in ("W", "U", "b_x", "h0"))
@@ -52,7 +61,7 @@ def _check(name, mode):
     assert err <= bar, (name, mode, err)
 
 
-CASES = [(name, mode) for name in WL.WORKLOAD_ORDER + ["gru_diag_long_elk"]
+CASES = [(name, mode) for name in WL.WORKLOAD_ORDER + ["gru_diag_long_elk", "lstm_diag_long_chunked"]
          for mode in WL.get_workload(name).jac_modes]
 
 
@@ -60,5 +69,59 @@ CASES = [(name, mode) for name in WL.WORKLOAD_ORDER + ["gru_diag_long_elk"]
 def test_full_size_workload_matches_sequential_oracle(name, mode):
     try:
         _check(name, mode)
+    finally:
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["gru_diag_long_bwd", "lstm_diag_long_bwd"])
+def test_full_size_backward_matches_bptt_oracle_on_sampled_channels(name):
+    """The backward pass at the converged states of the long workloads, in bench's launch
+    configuration, against the BPTT oracle on 8 evenly spaced channels (an exact
+    sub-problem: those channels' dW rows, dU, db_x, db_h and dh0 columns).  dW goes
+    through the bf16 gradient product and is held to 2^-8 sum |dgx| |x| per entry (the
+    rounding of the pre-activation gradients to bf16); the others to 1e-4 of their scale."""
+    w = WL.get_workload(name)
+    p = WL.generate(w)
+    d = {k: (None if v is None else v.to("cuda")) for k, v in p.items()}
+    print(f"# full-size backward: {name}", flush=True)
+    try:
+        fwd = pnr.evaluate(w.cell, d["W"], d["U"], d["x"], b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"],
+                           max_iters=w.max_iters, tol=w.tol, jac_mode=w.jac_modes[0], jac_every=w.jac_every)
+        assert fwd["status"] == pnr.OK
+        h = fwd["h"]
+        del fwd
+        g = torch.randn(h.shape, generator=torch.Generator().manual_seed(w.seed + 7), dtype=torch.float32).to("cuda")
+        got = pnr.backward(w.cell, d["W"], d["U"], d["x"], h, g, b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"],
+                           want=("W", "U", "b_x", "b_h", "h0"))
+        ch = np.linspace(0, w.D - 1, 8).round().astype(int)
+        W, U, bx, h0 = (WL.as_f64(p[k]) for k in ("W", "U", "b_x", "h0"))
+        bh = None if p["b_h"] is None else WL.as_f64(p["b_h"])
+        Wc, Uc, bxc, bhc, h0c, _ = O.restrict_channels(w.cell, w.D, W, U, bx, bh, h0, ch)
+        cols = torch.from_numpy(output_channel_columns(w.cell, w.D, ch)).to("cuda")
+        x = p["x"].float().numpy() if p["x"].dtype == torch.bfloat16 else p["x"].numpy()
+        # the states the gradients are taken at are the converged trajectory
+        seq = O.sequential(w.cell, Wc, Uc, bxc, bhc, x, h0c)
+        hs = h[:, :, cols].double().cpu().numpy()
+        print(f"#   states: non-finite {int((~torch.isfinite(h)).sum())}, max-abs vs sequential "
+              f"{np.abs(hs - seq).max():.2e}", flush=True)
+        assert np.abs(hs - seq).max() < 1e-4
+        for k, v in got.items():
+            if k != "workspace":
+                assert bool(torch.isfinite(v).all()), k
+        ref = O.bptt(w.cell, Wc, Uc, bxc, bhc, x, h0c, hs, g[:, :, cols].double().cpu().numpy())
+        rows = torch.from_numpy((np.arange(w.G)[:, None] * w.D + ch[None, :]).reshape(-1)).to("cuda")
+        chd = torch.from_numpy(ch).to("cuda")
+        for k, v in (("dU", got["U"][:, chd]), ("db_x", got["b_x"][rows]), ("db_h", got["b_h"][rows]),
+                     ("dh0", got["h0"][:, cols])):
+            r = ref[k]
+            err = np.abs(v.double().cpu().numpy() - r).max() / np.abs(r).max()
+            print(f"#   {k} relative error {err:.2e}", flush=True)
+            assert err < 1e-4, (k, err)
+        dgx = np.abs(ref["dgx"].reshape(w.B * w.T, -1))
+        bound = dgx.T @ np.abs(x.reshape(w.B * w.T, -1))
+        r = ref["dW"]
+        err = np.abs(got["W"][rows].double().cpu().numpy() - r)
+        print(f"#   dW max error / bound {(err / (2.0 ** -8 * bound + 1e-30)).max():.3f}", flush=True)
+        assert np.all(err <= 2.0 ** -8 * bound + 1e-5 * np.abs(r).max())
     finally:
         torch.cuda.empty_cache()

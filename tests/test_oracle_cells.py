@@ -10,7 +10,7 @@ import torch
 
 import oracle as O
 
-torch.set_default_dtype(torch.float64)
+
 
 
 def _rand(rng, *shape, scale=1.0):
