@@ -210,17 +210,29 @@ int pnr_eval_chunked(const pnr_cell* cell, const pnr_params* params, const void*
  * is run backwards in time as a scan, and each step's lam_t is sent back through the
  * cell's gates to the pre-activations, the recurrent weights and biases, the inputs
  * (through W) and h0.
- * Supported: PNR_CELL_GRU_DIAG and PNR_CELL_LSTM_DIAG, x in {f32, bf16}, state f32 (the
- * cell's jac_every is ignored).  Device pointers, caller-owned; each gradient output
- * may be NULL (not computed); all gradients are fp32 and overwritten (not accumulated):
+ * Supported: PNR_CELL_GRU_DIAG and PNR_CELL_LSTM_DIAG (the adjoint is one scan: status
+ * PNR_OK, pnr_iters_used() = 0), and PNR_CELL_GRU with D <= 64, whose dense Jacobians
+ * couple the channels: there the adjoint system is solved by quasi-Newton refinement
+ * ("Towards Scalable and Stable Parallelization of Nonlinear RNNs", abstract: the
+ * diagonal approximation, here as the preconditioner of a diagonal scan, with the dense
+ * J^T lam of each residual on MFMA) from lam = 0 until max |residual| <= 2e-5 max |g|,
+ * checked after every group of 4 iterations, at most 256.  Status PNR_OK,
+ * PNR_NOT_CONVERGED (gradients of the last iterate) or PNR_NONFINITE;
+ * pnr_iters_used() = refinement updates applied (up to 3 past the passing check),
+ * pnr_last_residual_history() = the residuals up to the passing one.  x in {f32, bf16}, state f32; the
+ * cell's jac_every is ignored.  Device pointers, caller-owned; each gradient output may
+ * be NULL (not computed); all gradients are fp32 and overwritten (not accumulated):
  *   h, grad_h  [B, T, S]   fp32, inputs (S = D, or 2D for the LSTM's (c, h))
- *   grad_x     [B, T, D_in]     grad_W    [G*D, D_in]     grad_U   [G, D]
+ *   grad_x     [B, T, D_in]     grad_W    [G*D, D_in]     grad_U   as U ([3D, D] or [G, D])
  *   grad_b_x   [G*D]            grad_b_h  [G*D]           grad_h0  [B, S]
  * x, h0, params as for pnr_eval (h0 may be NULL: zeros).  Workspace:
- * pnr_workspace_bytes_backward() bytes (0 = invalid or unsupported request).  The work
- * is enqueued on cell->stream and the call returns without waiting for it.  In
- * measurement mode the profile record holds: proj_ms the recomputed input projection,
- * newton_ms the adjoint scan kernel, out_ms the reductions and the two gradient GEMMs.
+ * pnr_workspace_bytes_backward() bytes (0 = invalid or unsupported request).  For the
+ * diagonal cells the work is enqueued on cell->stream and the call returns without
+ * waiting for it; the dense GRU's refinement reads its residual back every iteration
+ * and the call returns with the work still enqueued for the final gradients.  In
+ * measurement mode the profile record holds: proj_ms the recomputed gate
+ * pre-activations, newton_ms the adjoint (scan kernel, or the refinement loop with its
+ * read-backs), out_ms the reductions and gradient GEMMs.
  */
 size_t pnr_workspace_bytes_backward(const pnr_cell* cell);
 int pnr_backward(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0,

@@ -660,16 +660,55 @@ int validate_backward(const pnr_cell* c) {
   if (!c) return fail(PNR_E_INVALID, "cell descriptor is NULL");
   pnr_cell v = *c;
   v.jac_every = 1;
-  int rc = validate(&v, PNR_JAC_FULL);
+  // the dense GRU's limits are those of its diagonal-Jacobian forward kernels
+  int rc = validate(&v, c->kind == PNR_CELL_GRU ? PNR_JAC_DIAG : PNR_JAC_FULL);
   if (rc) return rc;
-  if (c->kind != PNR_CELL_GRU_DIAG && c->kind != PNR_CELL_LSTM_DIAG)
-    return fail(PNR_E_UNSUPPORTED, "the backward pass is implemented for GRU_DIAG and LSTM_DIAG");
+  if (c->state_dtype != PNR_F32)
+    return fail(PNR_E_UNSUPPORTED, "the backward pass is implemented for fp32 state");
   if ((double)c->B * c->T > 2.0e9 || (double)gates(c->kind) * c->D * c->D_in > 2.0e9)
     return fail(PNR_E_INVALID, "problem too large for this library's index range");
   return 0;
 }
+constexpr int kBwdMaxIters = 256;      // refinement iterations of the dense adjoint
+constexpr int kBwdGroup = 4;           // iterations between read-backs of the residuals
+constexpr double kBwdTolRel = 2e-5;    // stop when max |R| <= kBwdTolRel * max |g|
+
+// Dense GRU: every array [B*T][.] row-major, fp32.
+struct DenseBwdLayout {
+  size_t gx = 0, gh = 0, hprev = 0, F = 0, lam = 0, dgh = 0, v = 0, scan3 = 0, ut = 0, xt = 0, wt = 0, scan_ws = 0,
+         rmax = 0, part = 0, total = 0;
+  int tile = 0;
+};
+DenseBwdLayout make_dense_bwd_layout(const pnr_cell* c) {
+  DenseBwdLayout l;
+  const size_t BT = (size_t)c->B * c->T, D = c->D, GD = 3 * D, Din = c->D_in, f = sizeof(float);
+  size_t off = 0;
+  l.gx = off; off = align_up(off + f * BT * GD);       // gx, then dL/dgx
+  l.gh = off; off = align_up(off + f * BT * GD);       // U h + b_h, then dL/dgh transposed
+  l.hprev = off; off = align_up(off + f * BT * D);
+  l.F = off; off = align_up(off + f * 6 * BT * D);
+  l.lam = off; off = align_up(off + f * BT * D);
+  l.dgh = off; off = align_up(off + f * BT * GD);
+  l.v = off; off = align_up(off + f * BT * D);         // U^T dgh, then h_prev transposed
+  l.scan3 = off; off = align_up(off + f * 3 * BT * D); // scan A, b, d; then dL/dgx transposed
+  l.ut = off; off = align_up(off + f * D * GD);
+  l.xt = off; off = align_up(off + f * BT * Din);
+  l.wt = off; off = align_up(off + f * Din * GD);
+  l.tile = scan_default_tile(1);
+  const size_t tiles = (size_t)c->B * D * ((c->T + l.tile - 1) / l.tile);
+  l.scan_ws = off; off = align_up(off + align_up(sizeof(Ctrl)) + align_up(sizeof(uint64_t) * (tiles * scan_slot_words(1) + 1)));
+  l.rmax = off; off = align_up(off + sizeof(uint32_t) * (kBwdMaxIters + 1));
+  l.part = off; off = align_up(off + f * kSplitKSlices * GD * (D > Din ? D : Din));   // split-K partials
+  l.total = off;
+  return l;
+}
+
 BwdLayout make_bwd_layout(const pnr_cell* c) {
   BwdLayout l;
+  if (c->kind == PNR_CELL_GRU) {
+    l.total = make_dense_bwd_layout(c).total;
+    return l;
+  }
   const size_t B = c->B, T = c->T, D = c->D, Din = c->D_in, G = gates(c->kind), S = states(c->kind, c->D);
   const size_t ge = dsize(c->x_dtype);   // the gradient GEMMs' operand type: that of x
   size_t off = 0;
@@ -681,6 +720,136 @@ BwdLayout make_bwd_layout(const pnr_cell* c) {
   l.part = off; off = align_up(off + sizeof(float) * B * 3 * G * D);
   l.total = off;
   return l;
+}
+}  // namespace
+
+namespace {
+int backward_dense(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, const void* h,
+                   const void* grad_h, void* grad_x, void* grad_W, void* grad_U, void* grad_b_x, void* grad_b_h,
+                   void* grad_h0) {
+  const DenseBwdLayout l = make_dense_bwd_layout(cell);
+  const int D = cell->D, T = cell->T, B = cell->B, Din = cell->D_in, GD = 3 * D;
+  const size_t BT = (size_t)B * T, n = BT * D;
+  hipStream_t st = reinterpret_cast<hipStream_t>(cell->stream);
+  int num_cu = 0, rc;
+  if ((rc = device_info(&num_cu))) return rc;
+  char* ws = static_cast<char*>(cell->workspace);
+  auto fp = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  float *gx = fp(l.gx), *gh = fp(l.gh), *hprev = fp(l.hprev), *F = fp(l.F), *lam = fp(l.lam), *dgh = fp(l.dgh),
+        *v = fp(l.v), *Ar = fp(l.scan3), *br = Ar + n, *dr = br + n, *UT = fp(l.ut);
+  uint32_t* rmax = reinterpret_cast<uint32_t*>(ws + l.rmax);
+  Ctrl* sctrl = reinterpret_cast<Ctrl*>(ws + l.scan_ws);
+  uint64_t* slots = reinterpret_cast<uint64_t*>(ws + l.scan_ws + align_up(sizeof(Ctrl)));
+  const size_t slot_words = (size_t)B * D * ((T + l.tile - 1) / l.tile) * scan_slot_words(1);
+  const float* U = static_cast<const float*>(params->U);
+  static thread_local uint32_t* host_words = nullptr;
+  if (!host_words)
+    PNR_HIP(hipHostMalloc(reinterpret_cast<void**>(&host_words), sizeof(uint32_t) * (kBwdMaxIters + 1),
+                          hipHostMallocDefault));
+
+  Mark m_first = mark_begin(st);
+  Mark m_proj = mark_begin(st);
+  // the forward's gate pre-activations: gx = x W^T + b_x, gh = h_{t-1} U^T + b_h
+  GemmArgs gp{x, params->W, params->b_x, gx, (int)BT, GD, Din, 0, 0, 0, Din, Din, GD, 1, 0};
+  PNR_HIP(launch_gemm(cell->x_dtype, PNR_F32, gp, st));
+  PNR_HIP(launch_gru_shift_states(static_cast<const float*>(h), static_cast<const float*>(h0), hprev, B, T, D, st));
+  GemmArgs gq{hprev, U, params->b_h, gh, (int)BT, GD, D, 0, 0, 0, D, D, GD, 1, 0};
+  PNR_HIP(launch_gemm(PNR_F32, PNR_F32, gq, st));
+  PNR_HIP(launch_gru_bwd_factors(gx, gh, hprev, U, F, n, D, st));
+  PNR_HIP(launch_transpose(U, PNR_F32, UT, PNR_F32, 1, GD, D, st));
+  mark_end(m_proj, st);
+
+  // ---- adjoint: quasi-Newton refinement from lam = 0 ----
+  // Residuals are read back after every group of kBwdGroup iterations; the refinement
+  // stops after the group whose check passed, so the returned adjoint may have had a few
+  // more (contracting) updates than the residual history shows checks before the pass.
+  Mark m_adj = mark_begin(st);
+  PNR_HIP(launch_fill_zero(lam, n, st));
+  PNR_HIP(launch_fill_zero(dgh, BT * GD, st));
+  PNR_HIP(launch_fill_zero(reinterpret_cast<float*>(rmax), kBwdMaxIters + 1, st));
+  int status = PNR_NOT_CONVERGED, k = 0, updates = 0;
+  double rho0 = 0.0, rho = 0.0;
+  std::vector<double> hist;
+  const GemmArgs gv{dgh, UT, nullptr, v, (int)BT, D, GD, 0, 0, 0, GD, GD, D, 1, 0};
+  bool done = false;
+  while (!done) {
+    const int k1 = std::min(k + kBwdGroup - 1, kBwdMaxIters);
+    for (int j = k; j <= k1; ++j) {
+      PNR_HIP(launch_gemm(PNR_F32, PNR_F32, gv, st));
+      PNR_HIP(launch_gru_bwd_resid(F, lam, v, static_cast<const float*>(grad_h), Ar, br, rmax + j, B, T, D, st));
+      if (j == kBwdMaxIters) break;
+      PNR_HIP(launch_init(sctrl, slots, slot_words, nullptr, 0, st));
+      PNR_HIP(launch_scan(1, B * D, T, Ar, br, dr, l.tile, slots, sctrl, num_cu, st));
+      PNR_HIP(launch_gru_bwd_update(dr, lam, F, dgh, B, T, D, st));
+      ++updates;
+    }
+    PNR_HIP(hipMemcpyAsync(host_words + k, rmax + k, sizeof(uint32_t) * (k1 - k + 1), hipMemcpyDeviceToHost, st));
+    PNR_HIP(hipStreamSynchronize(st));
+    for (int j = k; j <= k1; ++j) {
+      const uint32_t bits = host_words[j];
+      float rf;
+      memcpy(&rf, &bits, sizeof(rf));
+      rho = bits >= 0x7f800000u ? INFINITY : (double)rf;   // NaN counts as +inf
+      hist.push_back(rho);
+      if (j == 0) rho0 = rho;
+      if (!std::isfinite(rho)) { status = PNR_NONFINITE; done = true; break; }
+      if (rho <= kBwdTolRel * rho0) { status = PNR_OK; done = true; break; }
+    }
+    k = k1 + 1;
+    if (k > kBwdMaxIters) done = true;
+  }
+  mark_end(m_adj, st);
+
+  // ---- gradients from the adjoint ----
+  Mark m_grads = mark_begin(st);
+  float* dgx = gx;   // gx is no longer needed
+  PNR_HIP(launch_gru_bwd_gates(F, lam, dgh, dgx, n, D, st));
+  if (grad_h0) {
+    PNR_HIP(launch_gemm(PNR_F32, PNR_F32, gv, st));
+    PNR_HIP(launch_gru_bwd_dh0(F, lam, v, static_cast<float*>(grad_h0), B, T, D, st));
+  }
+  float* dghT = gh;   // [3D][B*T]
+  float* dgxT = Ar;   // [3D][B*T]
+  if (grad_U || grad_b_h) PNR_HIP(launch_transpose(dgh, PNR_F32, dghT, PNR_F32, 1, (int)BT, GD, st));
+  if (grad_W || grad_b_x) PNR_HIP(launch_transpose(dgx, PNR_F32, dgxT, PNR_F32, 1, (int)BT, GD, st));
+  PNR_HIP(launch_row_sum(dghT, grad_b_h ? GD : 0, BT, static_cast<float*>(grad_b_h), st));
+  PNR_HIP(launch_row_sum(dgxT, grad_b_x ? GD : 0, BT, static_cast<float*>(grad_b_x), st));
+  if (grad_U) {
+    // dU[m][j] = sum_{b,t} dgh[(b,t)][m] h_{t-1}[(b,t)][j]
+    float* hprevT = v;
+    PNR_HIP(launch_transpose(hprev, PNR_F32, hprevT, PNR_F32, 1, (int)BT, D, st));
+    PNR_HIP(launch_gemm_split_k(dghT, (int)BT, hprevT, (int)BT, static_cast<float*>(grad_U), GD, D, (int)BT,
+                                fp(l.part), kSplitKSlices, st));
+  }
+  if (grad_W) {
+    float* xT = fp(l.xt);
+    PNR_HIP(launch_transpose(x, cell->x_dtype, xT, PNR_F32, 1, (int)BT, Din, st));
+    PNR_HIP(launch_gemm_split_k(dgxT, (int)BT, xT, (int)BT, static_cast<float*>(grad_W), GD, Din, (int)BT,
+                                fp(l.part), kSplitKSlices, st));
+  }
+  if (grad_x) {
+    float* WT = fp(l.wt);
+    PNR_HIP(launch_transpose(params->W, cell->x_dtype, WT, PNR_F32, 1, GD, Din, st));
+    GemmArgs gxg{dgx, WT, nullptr, grad_x, (int)BT, Din, GD, 0, 0, 0, GD, GD, Din, 1, 0};
+    PNR_HIP(launch_gemm(PNR_F32, PNR_F32, gxg, st));
+  }
+  mark_end(m_grads, st);
+  mark_end(m_first, st);
+  g_last.iters = updates;
+  g_last.residual = rho;
+  g_last.hist = std::move(hist);
+  if (g_prof.on) {
+    PNR_HIP(hipStreamSynchronize(st));
+    pnr_profile p{};
+    p.total_ms = mark_ms(m_first);
+    p.proj_ms = mark_ms(m_proj);
+    p.newton_ms = mark_ms(m_adj);
+    p.out_ms = mark_ms(m_grads);
+    p.passes = updates + 1;
+    g_prof.last = p;
+    g_prof.valid = true;
+  }
+  return status;
 }
 }  // namespace
 
@@ -710,12 +879,17 @@ int pnr_backward(const pnr_cell* cell, const pnr_params* params, const void* x, 
   hipStream_t st = reinterpret_cast<hipStream_t>(cell->stream);
   if (T == 0) {   // no steps: every gradient but dL/dh0 (= 0) is an empty sum
     PNR_HIP(launch_fill_zero(static_cast<float*>(grad_W), (size_t)G * D * Din, st));
-    PNR_HIP(launch_fill_zero(static_cast<float*>(grad_U), (size_t)G * D, st));
+    PNR_HIP(launch_fill_zero(static_cast<float*>(grad_U), (size_t)G * D * (kind == PNR_CELL_GRU ? D : 1), st));
     PNR_HIP(launch_fill_zero(static_cast<float*>(grad_b_x), (size_t)G * D, st));
     PNR_HIP(launch_fill_zero(static_cast<float*>(grad_b_h), (size_t)G * D, st));
     PNR_HIP(launch_fill_zero(static_cast<float*>(grad_h0), (size_t)B * S, st));
+    g_last.iters = 0;
+    g_last.residual = 0.0;
+    g_last.hist.assign(1, 0.0);
     return PNR_OK;
   }
+  if (kind == PNR_CELL_GRU)
+    return backward_dense(cell, params, x, h0, h, grad_h, grad_x, grad_W, grad_U, grad_b_x, grad_b_h, grad_h0);
   int num_cu = 0;
   if ((rc = device_info(&num_cu))) return rc;
   char* ws = static_cast<char*>(cell->workspace);
@@ -776,6 +950,9 @@ int pnr_backward(const pnr_cell* cell, const pnr_params* params, const void* x, 
   }
   mark_end(m_grads, st);
   mark_end(m_first, st);
+  g_last.iters = 0;   // the adjoint is one scan
+  g_last.residual = 0.0;
+  g_last.hist.assign(1, 0.0);
   if (g_prof.on) {
     PNR_HIP(hipStreamSynchronize(st));
     pnr_profile p{};

@@ -113,6 +113,29 @@ struct BwdArgs {
 int adjoint_items_per_thread();
 hipError_t launch_adjoint_diag(int cell, const BwdArgs& a, int num_cu, hipStream_t st);
 
+// Backward pass of the dense GRU (dense_bwd.hip): the adjoint solved by quasi-Newton
+// refinement (diagonal scan + one GEMM per iteration).  Layouts [B][T][D] / [B][T][3D].
+hipError_t launch_gru_shift_states(const float* h, const float* h0, float* hprev, int B, int T, int D,
+                                   hipStream_t st);
+// F: six [B*T][D] planes (z, diag J, f_z, f_n, r, f_r)
+hipError_t launch_gru_bwd_factors(const float* gx, const float* gh, const float* hprev, const float* U, float* F,
+                                  size_t n, int D, hipStream_t st);
+hipError_t launch_gru_bwd_gates(const float* F, const float* lam, float* dgh, float* dgx, size_t n, int D,
+                                hipStream_t st);
+hipError_t launch_gru_bwd_resid(const float* F, const float* lam, const float* v, const float* g, float* Ar,
+                                float* br, uint32_t* rmax, int B, int T, int D, hipStream_t st);
+hipError_t launch_gru_bwd_update(const float* dr, float* lam, const float* F, float* dgh, int B, int T, int D,
+                                 hipStream_t st);
+hipError_t launch_gru_bwd_dh0(const float* F, const float* lam, const float* v, float* dh0, int B, int T, int D,
+                              hipStream_t st);
+// C [M][N] = A [M][K] B[N][K]^T (fp32) for a long K and small M x N: K cut into at most
+// max_slices slices summed from `part` (max_slices * M * N floats).
+constexpr int kSplitKSlices = 64;
+hipError_t launch_gemm_split_k(const float* A, int lda, const float* Bm, int ldb, float* C, int M, int N, int K,
+                               float* part, int max_slices, hipStream_t st);
+// out[r] = sum over the cols of row r of M [rows][cols]
+hipError_t launch_row_sum(const float* M, int rows, size_t cols, float* out, hipStream_t st);
+
 int diag_items_per_thread(int cell);
 int diag_slot_words(int cell);
 int diag_grid_capacity(int cell, int num_cu);

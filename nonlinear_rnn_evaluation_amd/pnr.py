@@ -286,7 +286,9 @@ def backward(kind: int, W: torch.Tensor, U: torch.Tensor, x: torch.Tensor, h: to
              workspace: Optional[torch.Tensor] = None) -> dict:
     """Run pnr_backward on device tensors: gradients of L through the recurrence whose
     states are h, given grad_h = dL/dh.  Returns {name: fp32 tensor} for the names in
-    `want` (the others are not computed), plus "workspace"."""
+    `want` (the others are not computed), plus "workspace" and the adjoint solve's
+    "status", "iters", "residual" and "history" (dense GRU: refinement iterations;
+    diagonal cells: one scan, iters 0)."""
     B, T, D_in = x.shape
     G, D = (U.shape[0] // U.shape[1], U.shape[1]) if kind == CELL_GRU else (U.shape[0], U.shape[1])
     S = 2 * D if kind == CELL_LSTM_DIAG else D
@@ -306,14 +308,16 @@ def backward(kind: int, W: torch.Tensor, U: torch.Tensor, x: torch.Tensor, h: to
     cell.workspace = workspace.data_ptr()
     cell.workspace_bytes = workspace.numel()
     f32 = dict(dtype=torch.float32, device=x.device)
-    shapes = {"x": (B, T, D_in), "W": (G * D, D_in), "U": (G, D), "b_x": (G * D,), "b_h": (G * D,), "h0": (B, S)}
+    shapes = {"x": (B, T, D_in), "W": (G * D, D_in), "U": tuple(U.shape), "b_x": (G * D,), "b_h": (G * D,),
+              "h0": (B, S)}
     out = {k: torch.empty(shapes[k], **f32) for k in want}
     params = PnrParams(ptrs["W"], ptrs["U"], ptrs["b_x"], ptrs["b_h"])
     rc = pnr_backward(cell, params, ptrs["x"], ptrs["h0"], ptrs["h"], ptrs["grad_h"],
                       *(_ptr(out.get(k)) for k in ("x", "W", "U", "b_x", "b_h", "h0")))
     if rc < 0:
         raise PnrError(f"pnr_backward returned {rc}: {pnr_last_error()}")
-    out["workspace"] = workspace
+    out.update(workspace=workspace, status=rc, iters=pnr_iters_used(), residual=pnr_last_residual(),
+               history=pnr_last_residual_history())
     return out
 
 

@@ -135,7 +135,7 @@ def named_workloads() -> dict:
     w["lstm_diag_long_chunked"] = dataclasses.replace(w["lstm_diag_long"], name="lstm_diag_long_chunked",
                                                       chunk_len=8192)
     # the backward pass (all gradients) at the converged states of the two long workloads
-    for base in ("gru_diag_long", "lstm_diag_long"):
+    for base in ("gru_quasi", "gru_diag_long", "lstm_diag_long"):
         w[base + "_bwd"] = dataclasses.replace(w[base], name=base + "_bwd", backward=True)
     # the stiff LSTM with the damped step on the diagonal Jacobian (quasi-ELK), which
     # converges where both undamped variants do not

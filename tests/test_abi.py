@@ -168,9 +168,13 @@ def test_backward_requests_are_validated_without_a_gpu():
         args = (c, params, 4096, None, 8192, 8192, None, None, None, None, None, None)
         assert pnr.pnr_backward(*args) == pnr.E_WORKSPACE
         assert pnr.pnr_backward(c, params, 4096, None, None, 8192, *[None] * 6) == pnr.E_INVALID
-    dense = _cell(kind=pnr.CELL_GRU, D=16)
-    assert pnr.pnr_workspace_bytes_backward(dense) == 0
-    assert pnr.pnr_backward(dense, params, 4096, None, 8192, 8192, *[None] * 6) == pnr.E_UNSUPPORTED
+    dense = _cell(kind=pnr.CELL_GRU, D=64)
+    assert pnr.pnr_workspace_bytes_backward(dense) > 0
+    assert pnr.pnr_backward(dense, params, 4096, None, 8192, 8192, *[None] * 6) == pnr.E_WORKSPACE
+    for bad in (dict(kind=pnr.CELL_GRU, D=65), dict(kind=pnr.CELL_GRU, D=16, x_dtype=pnr.F64, state_dtype=pnr.F64)):
+        c = _cell(**bad)
+        assert pnr.pnr_workspace_bytes_backward(c) == 0
+        assert pnr.pnr_backward(c, params, 4096, None, 8192, 8192, *[None] * 6) == pnr.E_UNSUPPORTED
     # the cell's jac_every does not matter to the backward pass
     assert pnr.pnr_workspace_bytes_backward(_cell(jac_every=3)) == pnr.pnr_workspace_bytes_backward(_cell())
 
