@@ -675,9 +675,8 @@ constexpr double kBwdTolRel = 2e-5;    // stop when max |R| <= kBwdTolRel * max 
 
 // Dense GRU: every array [B*T][.] row-major, fp32.
 struct DenseBwdLayout {
-  size_t gx = 0, gh = 0, hprev = 0, F = 0, lam = 0, dgh = 0, v = 0, scan3 = 0, ut = 0, xt = 0, wt = 0, scan_ws = 0,
-         rmax = 0, part = 0, total = 0;
-  int tile = 0;
+  size_t gx = 0, gh = 0, hprev = 0, F = 0, lam = 0, dgh = 0, v = 0, scan3 = 0, ut = 0, xt = 0, wt = 0, rmax = 0,
+         part = 0, total = 0;
 };
 DenseBwdLayout make_dense_bwd_layout(const pnr_cell* c) {
   DenseBwdLayout l;
@@ -690,13 +689,13 @@ DenseBwdLayout make_dense_bwd_layout(const pnr_cell* c) {
   l.lam = off; off = align_up(off + f * BT * D);
   l.dgh = off; off = align_up(off + f * BT * GD);
   l.v = off; off = align_up(off + f * BT * D);         // U^T dgh, then h_prev transposed
-  l.scan3 = off; off = align_up(off + f * 3 * BT * D); // scan A, b, d; then dL/dgx transposed
+  // the second adjoint buffer and the chunk scan's aggregates and carries; afterwards
+  // dL/dgx transposed (3 B*T*D floats)
+  const size_t chunks = (size_t)c->B * gru_bwd_chunks(c->T) * D;
+  l.scan3 = off; off = align_up(off + f * std::max(3 * BT * D, BT * D + 3 * chunks + 1));
   l.ut = off; off = align_up(off + f * D * GD);
   l.xt = off; off = align_up(off + f * BT * Din);
   l.wt = off; off = align_up(off + f * Din * GD);
-  l.tile = scan_default_tile(1);
-  const size_t tiles = (size_t)c->B * D * ((c->T + l.tile - 1) / l.tile);
-  l.scan_ws = off; off = align_up(off + align_up(sizeof(Ctrl)) + align_up(sizeof(uint64_t) * (tiles * scan_slot_words(1) + 1)));
   l.rmax = off; off = align_up(off + sizeof(uint32_t) * (kBwdMaxIters + 1));
   l.part = off; off = align_up(off + f * kSplitKSlices * GD * (D > Din ? D : Din));   // split-K partials
   l.total = off;
@@ -736,11 +735,12 @@ int backward_dense(const pnr_cell* cell, const pnr_params* params, const void* x
   char* ws = static_cast<char*>(cell->workspace);
   auto fp = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
   float *gx = fp(l.gx), *gh = fp(l.gh), *hprev = fp(l.hprev), *F = fp(l.F), *lam = fp(l.lam), *dgh = fp(l.dgh),
-        *v = fp(l.v), *Ar = fp(l.scan3), *br = Ar + n, *dr = br + n, *UT = fp(l.ut);
+        *v = fp(l.v), *UT = fp(l.ut);
+  float* lam2 = fp(l.scan3);   // the other adjoint buffer
+  const size_t chunks = (size_t)B * gru_bwd_chunks(T) * D;
+  float2* agg = reinterpret_cast<float2*>(lam2 + ((n + 1) & ~(size_t)1));
+  float* carry = reinterpret_cast<float*>(agg + chunks);
   uint32_t* rmax = reinterpret_cast<uint32_t*>(ws + l.rmax);
-  Ctrl* sctrl = reinterpret_cast<Ctrl*>(ws + l.scan_ws);
-  uint64_t* slots = reinterpret_cast<uint64_t*>(ws + l.scan_ws + align_up(sizeof(Ctrl)));
-  const size_t slot_words = (size_t)B * D * ((T + l.tile - 1) / l.tile) * scan_slot_words(1);
   const float* U = static_cast<const float*>(params->U);
   static thread_local uint32_t* host_words = nullptr;
   if (!host_words)
@@ -775,12 +775,11 @@ int backward_dense(const pnr_cell* cell, const pnr_params* params, const void* x
   while (!done) {
     const int k1 = std::min(k + kBwdGroup - 1, kBwdMaxIters);
     for (int j = k; j <= k1; ++j) {
+      // residual of lam (max into rmax[j]), then lam2 = lam + delta and its gate gradients
       PNR_HIP(launch_gemm(PNR_F32, PNR_F32, gv, st));
-      PNR_HIP(launch_gru_bwd_resid(F, lam, v, static_cast<const float*>(grad_h), Ar, br, rmax + j, B, T, D, st));
-      if (j == kBwdMaxIters) break;
-      PNR_HIP(launch_init(sctrl, slots, slot_words, nullptr, 0, st));
-      PNR_HIP(launch_scan(1, B * D, T, Ar, br, dr, l.tile, slots, sctrl, num_cu, st));
-      PNR_HIP(launch_gru_bwd_update(dr, lam, F, dgh, B, T, D, st));
+      PNR_HIP(launch_gru_bwd_refine(F, lam, v, static_cast<const float*>(grad_h), lam2, dgh, agg, carry, rmax + j,
+                                    B, T, D, st));
+      std::swap(lam, lam2);
       ++updates;
     }
     PNR_HIP(hipMemcpyAsync(host_words + k, rmax + k, sizeof(uint32_t) * (k1 - k + 1), hipMemcpyDeviceToHost, st));
@@ -808,12 +807,12 @@ int backward_dense(const pnr_cell* cell, const pnr_params* params, const void* x
     PNR_HIP(launch_gemm(PNR_F32, PNR_F32, gv, st));
     PNR_HIP(launch_gru_bwd_dh0(F, lam, v, static_cast<float*>(grad_h0), B, T, D, st));
   }
-  float* dghT = gh;   // [3D][B*T]
-  float* dgxT = Ar;   // [3D][B*T]
+  float* dghT = gh;           // [3D][B*T]
+  float* dgxT = fp(l.scan3);  // [3D][B*T]; the adjoint (possibly here) is not read after dh0
   if (grad_U || grad_b_h) PNR_HIP(launch_transpose(dgh, PNR_F32, dghT, PNR_F32, 1, (int)BT, GD, st));
   if (grad_W || grad_b_x) PNR_HIP(launch_transpose(dgx, PNR_F32, dgxT, PNR_F32, 1, (int)BT, GD, st));
-  PNR_HIP(launch_row_sum(dghT, grad_b_h ? GD : 0, BT, static_cast<float*>(grad_b_h), st));
-  PNR_HIP(launch_row_sum(dgxT, grad_b_x ? GD : 0, BT, static_cast<float*>(grad_b_x), st));
+  PNR_HIP(launch_row_sum(dghT, grad_b_h ? GD : 0, BT, static_cast<float*>(grad_b_h), fp(l.part), st));
+  PNR_HIP(launch_row_sum(dgxT, grad_b_x ? GD : 0, BT, static_cast<float*>(grad_b_x), fp(l.part), st));
   if (grad_U) {
     // dU[m][j] = sum_{b,t} dgh[(b,t)][m] h_{t-1}[(b,t)][j]
     float* hprevT = v;

@@ -91,79 +91,114 @@ __global__ void __launch_bounds__(256) gru_bwd_gates_kernel(const float* __restr
   }
 }
 
-// Residual of the adjoint system and the reversed, transposed inputs of the diagonal
-// scan, through a 32 (t) x 32 (channel) LDS tile of batch element b:
-//   R_t = g_t + z_{t+1} lam_{t+1} + v_{t+1} - lam_t,   a_t = d_{t+1}   (0 past the end)
-//   Ar[b*D + i][T-1-t] = a_t,  br[b*D + i][T-1-t] = R_t;  rmax = max |R| (as bits).
-__global__ void __launch_bounds__(256) gru_bwd_resid_kernel(const float* __restrict__ F, const float* __restrict__ lam,
-                                                            const float* __restrict__ v, const float* __restrict__ g,
-                                                            float* __restrict__ Ar, float* __restrict__ br,
-                                                            uint32_t* __restrict__ rmax, int T, int D) {
-  __shared__ float sR[32][33], sA[32][33];
+// ---- refinement step as a chunked scan in the [B][T][D] layout ----
+// delta_t = a_t delta_{t+1} + R_t run backwards in time, with
+//   R_t = g_t + z_{t+1} lam_{t+1} + v_{t+1} - lam_t,  a_t = d_{t+1}   (t+1 terms 0 at T-1),
+// over chunks of kChunk steps: one wave per chunk, one lane per channel (D <= 64).
+// Pass 1 composes each chunk's map delta_{end} -> delta_{start} (and max |R|); pass 2
+// walks the chunks of each channel; pass 3 re-walks each chunk from its carry, writes
+// lam + delta into the other adjoint buffer and the recurrent-gate gradients of it.
+constexpr int kChunk = 32;
+constexpr int kBatch = 8;   // steps whose loads are issued together
+
+struct StepIn {   // per-step inputs of one lane
+  float g, lam, z, v, d;
+};
+__device__ __forceinline__ StepIn load_step(const float* g, const float* lam, const float* F, const float* v,
+                                            size_t n, size_t e) {
+  return StepIn{g[e], lam[e], F[e], v[e], F[n + e]};
+}
+
+template <bool APPLY>
+__global__ void __launch_bounds__(256) gru_bwd_chunk_kernel(const float* __restrict__ F,
+                                                            const float* __restrict__ lam,
+                                                            const float* __restrict__ v,
+                                                            const float* __restrict__ g, float2* __restrict__ agg,
+                                                            const float* __restrict__ carry,
+                                                            float* __restrict__ lam_new, float* __restrict__ dgh,
+                                                            uint32_t* __restrict__ rmax, int T, int D, int nch) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int b = blockIdx.y, c = blockIdx.x * 4 + w;
+  const size_t n = (size_t)gridDim.y * T * D;
   __shared__ uint32_t swmax[4];
-  const size_t n = (size_t)gridDim.z * T * D;
-  const int b = blockIdx.z, t0 = blockIdx.x * 32, i0 = blockIdx.y * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8
   uint32_t m = 0;
-  for (int k = ty; k < 32; k += 8) {
-    const int t = t0 + k, i = i0 + tx;
-    float R = 0.f, a = 0.f;
-    if (t < T && i < D) {
-      const size_t e = ((size_t)b * T + t) * D + i;
-      R = g[e] - lam[e];
-      if (t + 1 < T) {
-        const size_t e1 = e + D;
-        R += fmaf(F[e1], lam[e1], v[e1]);
-        a = F[n + e1];
+  if (c < nch && lane < D) {
+    const int t0 = c * kChunk, t1 = min(T, t0 + kChunk);
+    const size_t base = (size_t)b * T * D + lane;
+    // the step after the chunk (t1): its lam, z, v, d enter R and a of step t1 - 1
+    StepIn nx{0.f, 0.f, 0.f, 0.f, 0.f};
+    if (t1 < T) nx = load_step(g, lam, F, v, n, base + (size_t)t1 * D);
+    float P = 1.f, Q = 0.f;                          // pass 1: delta_t = P delta_{t1} + Q
+    float dl = APPLY ? carry[((size_t)b * nch + c) * D + lane] : 0.f;   // pass 3: delta at t1
+    for (int tb = t1 - 1; tb >= t0; tb -= kBatch) {
+      // loads of kBatch steps first (indices clamped into the chunk, results masked)
+      StepIn in[kBatch];
+      float fg[kBatch][4];   // pass 3: the gate factors f_r, f_z, f_n, r
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const size_t e = base + (size_t)max(tb - u, t0) * D;
+        in[u] = load_step(g, lam, F, v, n, e);
+        if constexpr (APPLY) {
+          fg[u][0] = F[5 * n + e];
+          fg[u][1] = F[2 * n + e];
+          fg[u][2] = F[3 * n + e];
+          fg[u][3] = F[4 * n + e];
+        }
       }
-      m = max(m, __float_as_uint(fabsf(R)));
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int t = tb - u;
+        if (t < t0) break;
+        const StepIn& cu = in[u];
+        const float R = cu.g + fmaf(nx.z, nx.lam, nx.v) - cu.lam;
+        const float a = nx.d;
+        m = max(m, __float_as_uint(fabsf(R)));
+        if constexpr (APPLY) {
+          const size_t e = base + (size_t)t * D;
+          dl = fmaf(a, dl, R);
+          const float l = cu.lam + dl;
+          lam_new[e] = l;
+          const size_t bt = (size_t)b * T + t;
+          float* o = dgh + bt * 3 * D;
+          o[lane] = fg[u][0] * l;
+          o[D + lane] = fg[u][1] * l;
+          o[2 * D + lane] = fg[u][2] * l * fg[u][3];
+        } else {
+          P *= a;
+          Q = fmaf(a, Q, R);
+        }
+        nx = cu;
+      }
     }
-    sR[k][tx] = R;
-    sA[k][tx] = a;
+    if constexpr (!APPLY) agg[((size_t)b * nch + c) * D + lane] = make_float2(P, Q);
   }
-  __syncthreads();
-  for (int k = ty; k < 32; k += 8) {
-    const int i = i0 + k, t = t0 + tx;
-    if (t < T && i < D) {
-      const size_t o = ((size_t)b * D + i) * T + (T - 1 - t);
-      Ar[o] = sA[tx][k];
-      br[o] = sR[tx][k];
-    }
-  }
-  // block max of |R|, then one atomic per block
-  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-  if ((threadIdx.x & 63) == 0) swmax[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    m = max(max(swmax[0], swmax[1]), max(swmax[2], swmax[3]));
-    atomicMax(rmax, m);
+  if constexpr (!APPLY) {
+    for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+    if (lane == 0) swmax[w] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) atomicMax(rmax, max(max(swmax[0], swmax[1]), max(swmax[2], swmax[3])));
   }
 }
 
-// lam[b][t][i] += dr[b*D + i][T-1-t], and the recurrent-gate gradients of the new lam
-// (dgh as in gru_bwd_gates_kernel) for the next residual
-__global__ void __launch_bounds__(256) gru_bwd_update_kernel(const float* __restrict__ dr, float* __restrict__ lam,
-                                                             const float* __restrict__ F, float* __restrict__ dgh,
-                                                             int T, int D) {
-  __shared__ float s[32][33];
-  const size_t n = (size_t)gridDim.z * T * D;
-  const int b = blockIdx.z, t0 = blockIdx.x * 32, i0 = blockIdx.y * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  for (int k = ty; k < 32; k += 8) {
-    const int i = i0 + k, t = t0 + tx;
-    s[k][tx] = (t < T && i < D) ? dr[((size_t)b * D + i) * T + (T - 1 - t)] : 0.f;
-  }
-  __syncthreads();
-  for (int k = ty; k < 32; k += 8) {
-    const int t = t0 + k, i = i0 + tx;
-    if (t < T && i < D) {
-      const size_t bt = (size_t)b * T + t, e = bt * D + i;
-      const float l = lam[e] + s[tx][k];
-      lam[e] = l;
-      float* o = dgh + bt * 3 * D;
-      o[i] = F[5 * n + e] * l;
-      o[D + i] = F[2 * n + e] * l;
-      o[2 * D + i] = F[3 * n + e] * l * F[4 * n + e];
+// carry[b][c][i] = delta at the first step after chunk c (0 after the last chunk); the
+// aggregates are loaded kBatch * 2 at a time ahead of the dependent chain
+__global__ void __launch_bounds__(64) gru_bwd_chunk_carry_kernel(const float2* __restrict__ agg,
+                                                                 float* __restrict__ carry, int D, int nch) {
+  constexpr int NB = 2 * kBatch;
+  const int b = blockIdx.x, i = threadIdx.x;
+  if (i >= D) return;
+  const size_t row = (size_t)b * nch;
+  float dl = 0.f;
+  for (int cb = nch - 1; cb >= 0; cb -= NB) {
+    float2 pq[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) pq[u] = agg[(row + max(cb - u, 0)) * D + i];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int c = cb - u;
+      if (c < 0) break;
+      carry[(row + c) * D + i] = dl;
+      dl = fmaf(pq[u].x, dl, pq[u].y);
     }
   }
 }
@@ -179,16 +214,19 @@ __global__ void __launch_bounds__(256) gru_bwd_dh0_kernel(const float* __restric
   dh0[e] = fmaf(F[s], lam[s], v[s]);
 }
 
-// out[r] = sum_c M[r][c]: one block per row
-__global__ void __launch_bounds__(256) row_sum_kernel(const float* __restrict__ M, size_t cols, float* __restrict__ out) {
+// part[s][r] = sum of row r of M over column segment s (segments of ceil(cols / S))
+__global__ void __launch_bounds__(256) row_sum_kernel(const float* __restrict__ M, size_t cols, size_t seg,
+                                                      float* __restrict__ part) {
   __shared__ float sw[4];
-  const float* row = M + (size_t)blockIdx.x * cols;
-  float s = 0.f;
-  for (size_t c = threadIdx.x; c < cols; c += blockDim.x) s += row[c];
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
-  if ((threadIdx.x & 63) == 0) sw[threadIdx.x >> 6] = s;
+  const size_t r = blockIdx.x, s = blockIdx.y;
+  const float* row = M + r * cols;
+  const size_t c0 = s * seg, c1 = c0 + seg < cols ? c0 + seg : cols;
+  float acc = 0.f;
+  for (size_t c = c0 + threadIdx.x; c < c1; c += blockDim.x) acc += row[c];
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if ((threadIdx.x & 63) == 0) sw[threadIdx.x >> 6] = acc;
   __syncthreads();
-  if (threadIdx.x == 0) out[blockIdx.x] = (sw[0] + sw[1]) + (sw[2] + sw[3]);
+  if (threadIdx.x == 0) part[s * gridDim.x + r] = (sw[0] + sw[1]) + (sw[2] + sw[3]);
 }
 
 // out[j] = sum_s part[s][j]
@@ -229,19 +267,21 @@ hipError_t launch_gru_bwd_gates(const float* F, const float* lam, float* dgh, fl
   return hipGetLastError();
 }
 
-hipError_t launch_gru_bwd_resid(const float* F, const float* lam, const float* v, const float* g, float* Ar,
-                                float* br, uint32_t* rmax, int B, int T, int D, hipStream_t st) {
-  dim3 grid((T + 31) / 32, (D + 31) / 32, B);
-  hipLaunchKernelGGL(gru_bwd_resid_kernel, grid, dim3(256), 0, st, F, lam, v, g, Ar, br, rmax, T, D);
+hipError_t launch_gru_bwd_refine(const float* F, const float* lam, const float* v, const float* g, float* lam_new,
+                                 float* dgh, float2* agg, float* carry, uint32_t* rmax, int B, int T, int D,
+                                 hipStream_t st) {
+  if (D > 64) return hipErrorInvalidValue;
+  const int nch = (T + kChunk - 1) / kChunk;
+  dim3 grid((nch + 3) / 4, B);
+  hipLaunchKernelGGL(gru_bwd_chunk_kernel<false>, grid, dim3(256), 0, st, F, lam, v, g, agg, nullptr, nullptr,
+                     nullptr, rmax, T, D, nch);
+  hipLaunchKernelGGL(gru_bwd_chunk_carry_kernel, dim3(B), dim3(64), 0, st, agg, carry, D, nch);
+  hipLaunchKernelGGL(gru_bwd_chunk_kernel<true>, grid, dim3(256), 0, st, F, lam, v, g, agg, carry, lam_new, dgh,
+                     nullptr, T, D, nch);
   return hipGetLastError();
 }
 
-hipError_t launch_gru_bwd_update(const float* dr, float* lam, const float* F, float* dgh, int B, int T, int D,
-                                 hipStream_t st) {
-  dim3 grid((T + 31) / 32, (D + 31) / 32, B);
-  hipLaunchKernelGGL(gru_bwd_update_kernel, grid, dim3(256), 0, st, dr, lam, F, dgh, T, D);
-  return hipGetLastError();
-}
+int gru_bwd_chunks(int T) { return (T + kChunk - 1) / kChunk; }
 
 hipError_t launch_gru_bwd_dh0(const float* F, const float* lam, const float* v, float* dh0, int B, int T, int D,
                               hipStream_t st) {
@@ -277,10 +317,12 @@ hipError_t launch_gemm_split_k(const float* A, int lda, const float* Bm, int ldb
   return launch_sum_slices(part, full + (rest > 0), mn, C, st);
 }
 
-hipError_t launch_row_sum(const float* M, int rows, size_t cols, float* out, hipStream_t st) {
+hipError_t launch_row_sum(const float* M, int rows, size_t cols, float* out, float* part, hipStream_t st) {
   if (rows <= 0 || !out) return hipSuccess;
-  hipLaunchKernelGGL(row_sum_kernel, dim3(rows), dim3(256), 0, st, M, cols, out);
-  return hipGetLastError();
+  constexpr int S = 32;   // column segments per row
+  const size_t seg = (cols + S - 1) / S;
+  hipLaunchKernelGGL(row_sum_kernel, dim3(rows, S), dim3(256), 0, st, M, cols, seg, part);
+  return launch_sum_slices(part, S, rows, out, st);
 }
 
 }  // namespace pnr

@@ -122,10 +122,13 @@ hipError_t launch_gru_bwd_factors(const float* gx, const float* gh, const float*
                                   size_t n, int D, hipStream_t st);
 hipError_t launch_gru_bwd_gates(const float* F, const float* lam, float* dgh, float* dgx, size_t n, int D,
                                 hipStream_t st);
-hipError_t launch_gru_bwd_resid(const float* F, const float* lam, const float* v, const float* g, float* Ar,
-                                float* br, uint32_t* rmax, int B, int T, int D, hipStream_t st);
-hipError_t launch_gru_bwd_update(const float* dr, float* lam, const float* F, float* dgh, int B, int T, int D,
+// One refinement step of the dense adjoint in the [B][T][D] layout (D <= 64): residual
+// (max |R| into rmax), the diagonal scan over chunks of 64 steps, lam_new = lam + delta,
+// and dgh of lam_new.  agg: B * chunks * D float2, carry: B * chunks * D floats.
+hipError_t launch_gru_bwd_refine(const float* F, const float* lam, const float* v, const float* g, float* lam_new,
+                                 float* dgh, float2* agg, float* carry, uint32_t* rmax, int B, int T, int D,
                                  hipStream_t st);
+int gru_bwd_chunks(int T);
 hipError_t launch_gru_bwd_dh0(const float* F, const float* lam, const float* v, float* dh0, int B, int T, int D,
                               hipStream_t st);
 // C [M][N] = A [M][K] B[N][K]^T (fp32) for a long K and small M x N: K cut into at most
@@ -133,8 +136,9 @@ hipError_t launch_gru_bwd_dh0(const float* F, const float* lam, const float* v, 
 constexpr int kSplitKSlices = 64;
 hipError_t launch_gemm_split_k(const float* A, int lda, const float* Bm, int ldb, float* C, int M, int N, int K,
                                float* part, int max_slices, hipStream_t st);
-// out[r] = sum over the cols of row r of M [rows][cols]
-hipError_t launch_row_sum(const float* M, int rows, size_t cols, float* out, hipStream_t st);
+// out[r] = sum over the cols of row r of M [rows][cols], in 32 column segments per row
+// (partials in `part`: 32 * rows floats) summed in a fixed order
+hipError_t launch_row_sum(const float* M, int rows, size_t cols, float* out, float* part, hipStream_t st);
 
 int diag_items_per_thread(int cell);
 int diag_slot_words(int cell);
