@@ -29,13 +29,16 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0, "f64": 78.6}   # dense, published
 PRIMARY = "gru_quasi"
 DEFAULT_OTHERS = ("tiny_gru,gru_full,gru_diag_long,lstm_diag_long,lstm_diag_long_chunked,lstm_diag_long_stiff,"
-                  "gru_diag_long_elk,gru_quasi_bwd,gru_diag_long_bwd,lstm_diag_long_bwd")
+                  "gru_diag_long_elk,gru_quasi_elk,gru_quasi_bwd,gru_diag_long_bwd,lstm_diag_long_bwd")
 CSRC = "nonlinear_rnn_evaluation_amd/csrc/"
 
 
 def newton_kernel(w, mode):
     """(kernel name as the profiler lists it, source file) of the Newton loop kernel."""
     from nonlinear_rnn_evaluation_amd import workloads as WL
+    if w.damping is not None and w.cell == WL.CELL_GRU:
+        return ("quasi-ELK loop (recurrent GEMM, cell, filter and smoother scans; one read-back per iteration)",
+                CSRC + "dense_elk.hip")
     if w.damping is not None:
         return "pnr::elk_diag_kernel", CSRC + "diag_iter.hip"
     if w.cell in (WL.CELL_GRU_DIAG, WL.CELL_LSTM_DIAG):
@@ -63,7 +66,17 @@ def projection_fused(w, mode):
     diagonal Jacobian on the MFMA kernel)."""
     from nonlinear_rnn_evaluation_amd import workloads as WL
     return (w.cell == WL.CELL_GRU and w.x_dtype == WL.DT_F32 and w.state_dtype == WL.DT_F32
-            and mode != WL.JAC_FULL and w.D in (16, 32, 64))
+            and mode != WL.JAC_FULL and w.D in (16, 32, 64) and w.damping is None)
+
+
+def dense_damped_iteration_bytes(w, k, resid=False):
+    """Algorithmic HBM bytes of one iteration of the dense GRU's damped (quasi-ELK) loop,
+    per (b, t, channel): shift the iterate (8 B), the recurrent GEMM (read 4, write 12 B),
+    the cell (read Gx 12, Gh 12, h_{t-1} 4, h 4; write r and J 8 B), the filter (read J, r
+    8 B; then J, r, h 12 B and write G, e 8 B) and the smoother (read G, e 8 B; then 8 B
+    and write the next iterate 4 B): 112 B; the residual-only pass stops after the cell
+    (64 B)."""
+    return w.B * w.T * w.D * (64 if resid else 112)
 
 
 def damped_iteration_bytes(w, k, resid=False):
@@ -212,7 +225,8 @@ def run_workload(name, steps, warmup, mode=None, with_cpu=True, cpu_budget=12.0,
             ro = it == w.max_iters
             bytes_call += sum(iteration_bytes(wc, k, it, resid=(ro and k == it)) for k in range(it + 1))
     elif w.damping is not None:
-        bytes_call = sum(damped_iteration_bytes(w, k, resid=(resid_last and k == passes - 1)) for k in range(passes))
+        fn = dense_damped_iteration_bytes if w.cell == WL.CELL_GRU else damped_iteration_bytes
+        bytes_call = sum(fn(w, k, resid=(resid_last and k == passes - 1)) for k in range(passes))
     else:
         bytes_call = sum(iteration_bytes(w, k, iters, resid=(resid_last and k == passes - 1)) for k in range(passes))
     fused = projection_fused(w, mode)

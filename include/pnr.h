@@ -163,7 +163,11 @@ const char* pnr_last_error(void);
  *   PNR_CELL_GRU_DIAG, jac_mode PNR_JAC_FULL or PNR_JAC_DIAG (its exact Jacobian is
  *     diagonal, so both are ELK);
  *   PNR_CELL_LSTM_DIAG, jac_mode PNR_JAC_DIAG (quasi-ELK: the diagonal of the 2x2 block,
- *     dc'/dc and dh'/dh, per channel; h_out holds (c, h) as for pnr_eval).
+ *     dc'/dc and dh'/dh, per channel; h_out holds (c, h) as for pnr_eval);
+ *   PNR_CELL_GRU (dense U), fp32 state, D <= 64, jac_mode PNR_JAC_DIAG (quasi-ELK: the
+ *     diagonal of the dense Jacobian).  Each iteration is a host-driven sequence of
+ *     launches (the recurrent GEMM, the cell, one 4-byte read-back of max |r|, the filter
+ *     and smoother scans).
  * Others return PNR_E_UNSUPPORTED.  damping must be finite and > 0 (else PNR_E_INVALID).
  * Workspace: pnr_workspace_bytes_damped() bytes (the smoother's per-step gain and
  * offset take 8 bytes per state element more than pnr_eval).

@@ -436,12 +436,39 @@ int validate_damped(const pnr_cell* c, int jac_mode) {
   int rc = validate(c, jac_mode);
   if (rc) return rc;
   if (!(c->kind == PNR_CELL_GRU_DIAG && (jac_mode == PNR_JAC_FULL || jac_mode == PNR_JAC_DIAG)) &&
-      !(c->kind == PNR_CELL_LSTM_DIAG && jac_mode == PNR_JAC_DIAG))
+      !(c->kind == PNR_CELL_LSTM_DIAG && jac_mode == PNR_JAC_DIAG) &&
+      !(c->kind == PNR_CELL_GRU && jac_mode == PNR_JAC_DIAG && c->state_dtype == PNR_F32))
     return fail(PNR_E_UNSUPPORTED,
-                "the damped step is implemented for GRU_DIAG (full or diagonal Jacobian) and LSTM_DIAG (diagonal "
-                "Jacobian)");
+                "the damped step is implemented for GRU_DIAG (full or diagonal Jacobian), LSTM_DIAG and the fp32 "
+                "GRU (diagonal Jacobian)");
   if (c->jac_every != 1) return fail(PNR_E_UNSUPPORTED, "the damped step needs jac_every = 1");
   return 0;
+}
+// The dense GRU's damped loop (host-driven, [B][T][D] / [B][T][3D] fp32 arrays).
+struct DenseElkLayout {
+  size_t gx = 0, gh = 0, hprev = 0, h[2] = {0, 0}, R = 0, J = 0, G = 0, E = 0, agg = 0, carry = 0, agg2 = 0,
+         carry2 = 0, rmax = 0, total = 0;
+};
+DenseElkLayout make_dense_elk_layout(const pnr_cell* c) {
+  DenseElkLayout l;
+  const size_t BT = (size_t)c->B * c->T, D = c->D, f = sizeof(float);
+  const size_t ch = (size_t)c->B * elk_dense_chunks(c->T) * D;
+  size_t off = 0;
+  l.gx = off; off = align_up(off + f * BT * 3 * D);
+  l.gh = off; off = align_up(off + f * BT * 3 * D);
+  l.hprev = off; off = align_up(off + f * BT * D);
+  for (int i = 0; i < 2; ++i) { l.h[i] = off; off = align_up(off + f * BT * D); }
+  l.R = off; off = align_up(off + f * BT * D);
+  l.J = off; off = align_up(off + f * BT * D);
+  l.G = off; off = align_up(off + f * BT * D);
+  l.E = off; off = align_up(off + f * BT * D);
+  l.agg = off; off = align_up(off + f * 7 * ch);
+  l.carry = off; off = align_up(off + f * 2 * ch);
+  l.agg2 = off; off = align_up(off + f * 2 * ch);
+  l.carry2 = off; off = align_up(off + f * ch);
+  l.rmax = off; off = align_up(off + sizeof(uint32_t) * (PNR_MAX_ITERS + 1));
+  l.total = off;
+  return l;
 }
 // pnr_eval's layout, plus two per-step planes of the smoother (gain, offset) per state component
 size_t damped_planes_offset(const Layout& l) { return l.total; }
@@ -452,8 +479,81 @@ size_t damped_total(const pnr_cell* c, const Layout& l) {
 
 size_t pnr_workspace_bytes_damped(const pnr_cell* cell, int jac_mode) {
   if (validate_damped(cell, jac_mode) != 0) return 0;
+  if (cell->kind == PNR_CELL_GRU) return make_dense_elk_layout(cell).total;
   return damped_total(cell, make_layout(cell, jac_mode));
 }
+
+namespace {
+// quasi-ELK for the dense GRU: per iteration the recurrent GEMM, the cell, one read-back of
+// max |R| (the returned iterate is the one whose residual was checked), then the filter and
+// smoother scans.
+int eval_damped_dense(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, void* h_out,
+                      int max_iters, double tol, float lam) {
+  const DenseElkLayout l = make_dense_elk_layout(cell);
+  const int D = cell->D, T = cell->T, B = cell->B, Din = cell->D_in, GD = 3 * D;
+  const size_t BT = (size_t)B * T, n = BT * D;
+  hipStream_t st = reinterpret_cast<hipStream_t>(cell->stream);
+  char* ws = static_cast<char*>(cell->workspace);
+  auto fp = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  float *gx = fp(l.gx), *gh = fp(l.gh), *hprev = fp(l.hprev), *R = fp(l.R), *J = fp(l.J);
+  float* H[2] = {fp(l.h[0]), fp(l.h[1])};
+  uint32_t* rmax = reinterpret_cast<uint32_t*>(ws + l.rmax);
+  const float* U = static_cast<const float*>(params->U);
+  static thread_local uint32_t* host_word = nullptr;
+  if (!host_word) PNR_HIP(hipHostMalloc(reinterpret_cast<void**>(&host_word), 256, hipHostMallocDefault));
+
+  Mark m_first = mark_begin(st);
+  Mark m_proj = mark_begin(st);
+  GemmArgs gp{x, params->W, params->b_x, gx, (int)BT, GD, Din, 0, 0, 0, Din, Din, GD, 1, 0};
+  PNR_HIP(launch_gemm(cell->x_dtype, PNR_F32, gp, st));
+  mark_end(m_proj, st);
+  Mark m_loop = mark_begin(st);
+  PNR_HIP(launch_fill_zero(reinterpret_cast<float*>(rmax), max_iters + 1, st));
+  PNR_HIP(launch_fill_zero(H[0], n, st));   // the zero guess, stored
+  const GemmArgs gq{hprev, U, params->b_h, gh, (int)BT, GD, D, 0, 0, 0, D, D, GD, 1, 0};
+  int cur = 0, k = 0, status = PNR_NOT_CONVERGED;
+  double rho = 0.0;
+  std::vector<double> hist;
+  for (;; ++k) {
+    PNR_HIP(launch_gru_shift_states(H[cur], static_cast<const float*>(h0), hprev, B, T, D, st));
+    PNR_HIP(launch_gemm(PNR_F32, PNR_F32, gq, st));
+    PNR_HIP(launch_gru_elk_cell(gx, gh, hprev, H[cur], U, R, J, rmax + k, n, D, st));
+    PNR_HIP(hipMemcpyAsync(host_word, rmax + k, sizeof(uint32_t), hipMemcpyDeviceToHost, st));
+    PNR_HIP(hipStreamSynchronize(st));
+    float rf;
+    memcpy(&rf, host_word, sizeof(rf));
+    rho = *host_word >= 0x7f800000u ? INFINITY : (double)rf;   // NaN counts as +inf
+    hist.push_back(rho);
+    if (!std::isfinite(rho)) { status = PNR_NONFINITE; break; }
+    if (rho <= tol) { status = PNR_OK; break; }
+    if (k == max_iters) break;
+    PNR_HIP(launch_gru_elk_step(J, R, H[cur], lam, fp(l.agg), fp(l.carry), fp(l.G), fp(l.E), fp(l.agg2),
+                                fp(l.carry2), H[cur ^ 1], B, T, D, st));
+    cur ^= 1;
+  }
+  mark_end(m_loop, st);
+  Mark m_out = mark_begin(st);
+  PNR_HIP(hipMemcpyAsync(h_out, H[cur], sizeof(float) * n, hipMemcpyDeviceToDevice, st));
+  mark_end(m_out, st);
+  mark_end(m_first, st);
+  PNR_HIP(hipStreamSynchronize(st));
+  g_last.iters = k;
+  g_last.residual = rho;
+  g_last.hist = std::move(hist);
+  if (g_prof.on) {
+    pnr_profile p{};
+    p.total_ms = mark_ms(m_first);
+    p.proj_ms = mark_ms(m_proj);
+    p.newton_ms = mark_ms(m_loop);
+    p.out_ms = mark_ms(m_out);
+    p.passes = k + 1;
+    p.resid_only = k == max_iters;
+    g_prof.last = p;
+    g_prof.valid = true;
+  }
+  return status;
+}
+}  // namespace
 
 int pnr_eval_damped(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, void* h_out,
                     int max_iters, double tol, int jac_mode, double damping) {
@@ -470,7 +570,7 @@ int pnr_eval_damped(const pnr_cell* cell, const pnr_params* params, const void* 
   if (isnan(tol)) return fail(PNR_E_INVALID, "tol is NaN");
   if (!(damping > 0.0) || !(damping < 1e30)) return fail(PNR_E_INVALID, "damping must be finite and > 0");
   const Layout l = make_layout(cell, jac_mode);
-  const size_t need = damped_total(cell, l);
+  const size_t need = cell->kind == PNR_CELL_GRU ? make_dense_elk_layout(cell).total : damped_total(cell, l);
   if (!cell->workspace) return fail(PNR_E_WORKSPACE, "workspace is NULL (%zu bytes required)", need);
   if ((uintptr_t)cell->workspace % 256) return fail(PNR_E_WORKSPACE, "workspace must be 256-byte aligned");
   if (cell->workspace_bytes < need)
@@ -481,6 +581,7 @@ int pnr_eval_damped(const pnr_cell* cell, const pnr_params* params, const void* 
     g_last.hist.assign(1, 0.0);
     return PNR_OK;
   }
+  if (cell->kind == PNR_CELL_GRU) return eval_damped_dense(cell, params, x, h0, h_out, max_iters, tol, (float)damping);
   int num_cu = 0;
   if ((rc = device_info(&num_cu))) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(cell->stream);
@@ -552,7 +653,8 @@ int plan_chunks(const pnr_cell* c, int jac_mode, double damping, int chunk_len, 
   const int rc = damping > 0 ? validate_damped(&p.sub, jac_mode) : validate(&p.sub, jac_mode);
   if (rc) return rc;
   const Layout l = make_layout(&p.sub, jac_mode);
-  p.sub_bytes = damping > 0 ? damped_total(&p.sub, l) : l.total;
+  p.sub_bytes = damping <= 0 ? l.total
+                : (p.sub.kind == PNR_CELL_GRU ? make_dense_elk_layout(&p.sub).total : damped_total(&p.sub, l));
   p.staged = c->B > 1 && c->T > p.L;
   size_t off = align_up(p.sub_bytes);
   if (p.staged) {

@@ -219,6 +219,38 @@ __device__ __forceinline__ Aff2 compose(const Aff2& l, const Aff2& e) {
 }
 __device__ __forceinline__ Aff2 aff_identity2() { return Aff2{1.f, 0.f, 0.f, 1.f, 0.f, 0.f}; }
 
+// The damped step's Kalman filter in homogeneous coordinates (u, v, n), P = u / v and
+// m = n / v: one step is the linear map [[a b 0][c d 0][e f g]] (7 numbers).
+// compose(later, earlier) = later o earlier, rescaled by the largest 2x2 entry (a
+// positive factor changes neither P nor m).
+struct Flt {
+  float a, b, c, d, e, f, g;
+};
+__device__ __forceinline__ Flt compose(const Flt& l, const Flt& x) {
+  Flt o;
+  o.a = fmaf(l.a, x.a, l.b * x.c);
+  o.b = fmaf(l.a, x.b, l.b * x.d);
+  o.c = fmaf(l.c, x.a, l.d * x.c);
+  o.d = fmaf(l.c, x.b, l.d * x.d);
+  o.e = fmaf(l.e, x.a, fmaf(l.f, x.c, l.g * x.e));
+  o.f = fmaf(l.e, x.b, fmaf(l.f, x.d, l.g * x.f));
+  o.g = l.g * x.g;
+  // a positive rescaling changes neither P = u / v nor m = n / v: keep the entries near 1
+  const float s = fast_rcp(fmaxf(fmaxf(fabsf(o.a), fabsf(o.b)), fmaxf(fabsf(o.c), fabsf(o.d))));
+  o.a *= s; o.b *= s; o.c *= s; o.d *= s; o.e *= s; o.f *= s; o.g *= s;
+  return o;
+}
+__device__ __forceinline__ Flt flt_identity() { return Flt{1.f, 0.f, 0.f, 1.f, 0.f, 0.f, 1.f}; }
+struct V3 {
+  float u, v, n;
+};
+__device__ __forceinline__ V3 apply(const Flt& F, const V3& x) {
+  return V3{fmaf(F.a, x.u, F.b * x.v), fmaf(F.c, x.u, F.d * x.v), fmaf(F.e, x.u, fmaf(F.f, x.v, F.g * x.n))};
+}
+__device__ __forceinline__ V3 normalized(const V3& x) {
+  const float s = fast_rcp(x.v);
+  return V3{x.u * s, 1.f, x.n * s};
+}
 // Inclusive scan over the 64 lanes of a wave, in lane order (lane 0 earliest):
 // after it, lane l holds e_l o e_{l-1} o ... o e_0.  Within each 16-lane row a
 // Hillis-Steele pass with DPP row_shr:1,2,4,8; across rows the row totals are

@@ -740,24 +740,6 @@ hipError_t launch_diag_newton(int cell, const DiagLoopArgs& a, int grid, hipStre
 // Tiles, thread-serial / DPP / LDS scans and the carry between tiles are those of
 // diag_newton_kernel; the backward sweep maps thread t to the (255 - t)-th run of steps
 // so that lane order is reverse time and the same forward scan machinery applies.
-struct Flt {
-  float a, b, c, d, e, f, g;
-};
-__device__ __forceinline__ Flt compose(const Flt& l, const Flt& x) {
-  Flt o;
-  o.a = fmaf(l.a, x.a, l.b * x.c);
-  o.b = fmaf(l.a, x.b, l.b * x.d);
-  o.c = fmaf(l.c, x.a, l.d * x.c);
-  o.d = fmaf(l.c, x.b, l.d * x.d);
-  o.e = fmaf(l.e, x.a, fmaf(l.f, x.c, l.g * x.e));
-  o.f = fmaf(l.e, x.b, fmaf(l.f, x.d, l.g * x.f));
-  o.g = l.g * x.g;
-  // a positive rescaling changes neither P = u / v nor m = n / v: keep the entries near 1
-  const float s = fast_rcp(fmaxf(fmaxf(fabsf(o.a), fabsf(o.b)), fmaxf(fabsf(o.c), fabsf(o.d))));
-  o.a *= s; o.b *= s; o.c *= s; o.d *= s; o.e *= s; o.f *= s; o.g *= s;
-  return o;
-}
-__device__ __forceinline__ Flt flt_identity() { return Flt{1.f, 0.f, 0.f, 1.f, 0.f, 0.f, 1.f}; }
 template <> __device__ __forceinline__ Flt identity_of<Flt>() { return flt_identity(); }
 __device__ __forceinline__ Flt shfl_row_shr_aff(const Flt& v, const Flt& id, int s) {
   Flt o;
@@ -777,16 +759,6 @@ __device__ __forceinline__ Flt shfl_row_shr_aff(const Flt& v, const Flt& id, int
 __device__ __forceinline__ Flt readlane_aff(const Flt& v, int l) {
   return Flt{readlane_f(v.a, l), readlane_f(v.b, l), readlane_f(v.c, l), readlane_f(v.d, l),
              readlane_f(v.e, l), readlane_f(v.f, l), readlane_f(v.g, l)};
-}
-struct V3 {
-  float u, v, n;
-};
-__device__ __forceinline__ V3 apply(const Flt& F, const V3& x) {
-  return V3{fmaf(F.a, x.u, F.b * x.v), fmaf(F.c, x.u, F.d * x.v), fmaf(F.e, x.u, fmaf(F.f, x.v, F.g * x.n))};
-}
-__device__ __forceinline__ V3 normalized(const V3& x) {
-  const float s = fast_rcp(x.v);
-  return V3{x.u * s, 1.f, x.n * s};
 }
 __device__ __forceinline__ V3 wave_shr1(const V3& x, const V3& lane0) {
   return V3{wave_shr1(x.u, lane0.u), wave_shr1(x.v, lane0.v), wave_shr1(x.n, lane0.n)};

@@ -140,6 +140,16 @@ hipError_t launch_gemm_split_k(const float* A, int lda, const float* Bm, int ldb
 // (partials in `part`: 32 * rows floats) summed in a fixed order
 hipError_t launch_row_sum(const float* M, int rows, size_t cols, float* out, float* part, hipStream_t st);
 
+// Damped (quasi-ELK) step of the dense GRU (dense_elk.hip), [B][T][D] layout, D <= 64.
+int elk_dense_chunks(int T);
+hipError_t launch_gru_elk_cell(const float* gx, const float* gh, const float* hprev, const float* H, const float* U,
+                               float* R, float* J, uint32_t* rmax, size_t n, int D, hipStream_t st);
+// filter + smoother: agg [B*chunks][7][D], carry [B*chunks][2][D], agg2 [B*chunks][2][D],
+// carry2 [B*chunks][D]; G, E, Hn [B][T][D]
+hipError_t launch_gru_elk_step(const float* J, const float* R, const float* H, float lam, float* agg, float* carry,
+                               float* Gc, float* Ec, float* agg2, float* carry2, float* Hn, int B, int T, int D,
+                               hipStream_t st);
+
 int diag_items_per_thread(int cell);
 int diag_slot_words(int cell);
 int diag_grid_capacity(int cell, int num_cu);

@@ -127,6 +127,8 @@ def named_workloads() -> dict:
     # the long diagonal GRU with the damped (quasi-ELK) step; the strength is a swept
     # hyperparameter: 0.01 still converges in 6 iterations (4 undamped), 0.1 takes 31
     w["gru_diag_long_elk"] = dataclasses.replace(w["gru_diag_long"], name="gru_diag_long_elk", damping=0.01)
+    # the dense GRU of the quasi workload with the damped step on its diagonal Jacobian
+    w["gru_quasi_elk"] = dataclasses.replace(w["gru_quasi"], name="gru_quasi_elk", damping=0.01)
     w["lstm_diag_long_stiff"] = dataclasses.replace(
         w["lstm_diag_long"], name="lstm_diag_long_stiff", u_scale=3.0, max_iters=256,
         jac_modes=(JAC_FULL, JAC_DIAG))

@@ -142,3 +142,50 @@ def test_lstm_damped_rejects_the_full_jacobian():
     p = _problem(64, D=2, cell=LSTM)
     with pytest.raises(pnr.PnrError):
         _run(p, 2, -1.0, WL.JAC_FULL, 0.5, cell=LSTM)
+
+
+# Dense GRU (quasi-ELK): the iteration against the oracle's Kalman-smoother step with the
+# diagonal of the dense Jacobian; chunks of 32 steps in the filter and smoother scans, so
+# lengths span many chunks and a ragged last one.
+GRU = WL.CELL_GRU
+
+
+@pytest.mark.parametrize("D,T", [(16, 37), (16, 1000), (64, 333), (40, 1500)])
+@pytest.mark.parametrize("lam", [0.05, 1.0])
+def test_dense_gru_fixed_iterations_match_damped_oracle(D, T, lam):
+    p = WL.random_problem(GRU, 2, T, D, 5, seed=D + T, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32, bias_std=0.2,
+                          h0_std=0.3, w_std=0.7 / math.sqrt(D))
+    q = _f64(p)
+    print(f"# damped dense GRU D={D} T={T} lam={lam}", flush=True)
+    got = _run(p, 3, -1.0, WL.JAC_DIAG, lam, cell=GRU)
+    ref = O.newton_dense(GRU, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], 3, -1.0, WL.JAC_DIAG,
+                         solver="loop", damping=lam)
+    assert got["status"] == pnr.NOT_CONVERGED and got["iters"] == 3
+    np.testing.assert_allclose(_np(got["h"]), ref["states"], rtol=0, atol=1e-4)
+    np.testing.assert_allclose(got["history"], ref["rhos"], rtol=1e-3, atol=1e-5)
+
+
+def test_dense_gru_damped_converges_to_the_sequential_states():
+    p = WL.random_problem(GRU, 3, 2000, 64, 8, seed=3, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32, bias_std=0.2,
+                          h0_std=0.3, w_std=0.7 / math.sqrt(64))
+    q = _f64(p)
+    got = _run(p, 200, 1e-6, WL.JAC_DIAG, 0.1, cell=GRU)
+    assert got["status"] == pnr.OK, (got["status"], got["history"][-3:])
+    ref = O.sequential(GRU, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"])
+    assert np.abs(_np(got["h"]) - ref).max() < 1e-4
+    # damped chunks of the same problem
+    d = {k: (None if v is None else v.to(DEV)) for k, v in p.items()}
+    ch = pnr.evaluate(GRU, d["W"], d["U"], d["x"], b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"], max_iters=200, tol=1e-6,
+                      jac_mode=WL.JAC_DIAG, damping=0.1, chunk_len=700)
+    assert ch["status"] == pnr.OK and np.abs(_np(ch["h"]) - ref).max() < 1e-4
+
+
+def test_dense_gru_damped_edge_cases():
+    p = WL.random_problem(GRU, 1, 300, 16, 3, seed=9, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32, bias_std=0.2)
+    zero = _run(p, 0, 1e-5, WL.JAC_DIAG, 0.5, cell=GRU)
+    assert zero["iters"] == 0 and np.abs(_np(zero["h"])).max() == 0.0
+    p["x"][0, 77, 1] = float("nan")
+    bad = _run(p, 10, 1e-6, WL.JAC_DIAG, 0.5, cell=GRU)
+    assert bad["status"] == pnr.NONFINITE and bad["iters"] == 0
+    with pytest.raises(pnr.PnrError):
+        _run(p, 2, -1.0, WL.JAC_FULL, 0.5, cell=GRU)
