@@ -180,26 +180,39 @@ __global__ void __launch_bounds__(256) gru_bwd_chunk_kernel(const float* __restr
   }
 }
 
-// carry[b][c][i] = delta at the first step after chunk c (0 after the last chunk); the
-// aggregates are loaded kBatch * 2 at a time ahead of the dependent chain
+// carry[b][c][i] = delta at the first step after chunk c (0 after the last chunk).  One
+// 64-thread block per (channel, b); lane l takes chunk nch - 1 - (g0 + l), so lane order is
+// reverse time, and an inclusive Hillis-Steele scan of the chunk maps through LDS gives
+// each lane's carry from the group's.
 __global__ void __launch_bounds__(64) gru_bwd_chunk_carry_kernel(const float2* __restrict__ agg,
                                                                  float* __restrict__ carry, int D, int nch) {
-  constexpr int NB = 2 * kBatch;
-  const int b = blockIdx.x, i = threadIdx.x;
-  if (i >= D) return;
-  const size_t row = (size_t)b * nch;
-  float dl = 0.f;
-  for (int cb = nch - 1; cb >= 0; cb -= NB) {
-    float2 pq[NB];
-#pragma unroll
-    for (int u = 0; u < NB; ++u) pq[u] = agg[(row + max(cb - u, 0)) * D + i];
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const int c = cb - u;
-      if (c < 0) break;
-      carry[(row + c) * D + i] = dl;
-      dl = fmaf(pq[u].x, dl, pq[u].y);
+  __shared__ float sp[64], sq[64];
+  const int i = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  float x = 0.f;
+  for (int g0 = 0; g0 < nch; g0 += 64) {
+    const int c = nch - 1 - (g0 + lane);
+    float P = 1.f, Q = 0.f;
+    if (c >= 0) {
+      const float2 pq = agg[((size_t)b * nch + c) * D + i];
+      P = pq.x;
+      Q = pq.y;
     }
+    for (int off = 1; off < 64; off <<= 1) {
+      sp[lane] = P;
+      sq[lane] = Q;
+      __syncthreads();
+      const float pp = lane >= off ? sp[lane - off] : 1.f, pq = lane >= off ? sq[lane - off] : 0.f;
+      __syncthreads();
+      Q = fmaf(P, pq, Q);
+      P *= pp;
+    }
+    sp[lane] = P;
+    sq[lane] = Q;
+    __syncthreads();
+    const float xin = lane == 0 ? x : fmaf(sp[lane - 1], x, sq[lane - 1]);
+    if (c >= 0) carry[((size_t)b * nch + c) * D + i] = xin;
+    x = fmaf(sp[63], x, sq[63]);
+    __syncthreads();
   }
 }
 
@@ -275,7 +288,7 @@ hipError_t launch_gru_bwd_refine(const float* F, const float* lam, const float* 
   dim3 grid((nch + 3) / 4, B);
   hipLaunchKernelGGL(gru_bwd_chunk_kernel<false>, grid, dim3(256), 0, st, F, lam, v, g, agg, nullptr, nullptr,
                      nullptr, rmax, T, D, nch);
-  hipLaunchKernelGGL(gru_bwd_chunk_carry_kernel, dim3(B), dim3(64), 0, st, agg, carry, D, nch);
+  hipLaunchKernelGGL(gru_bwd_chunk_carry_kernel, dim3(D, B), dim3(64), 0, st, agg, carry, D, nch);
   hipLaunchKernelGGL(gru_bwd_chunk_kernel<true>, grid, dim3(256), 0, st, F, lam, v, g, agg, carry, lam_new, dgh,
                      nullptr, T, D, nch);
   return hipGetLastError();

@@ -26,17 +26,19 @@ constexpr int kEBatch = 8;   // steps whose loads are issued together
 
 int elk_dense_chunks(int T) { return (T + kEChunk - 1) / kEChunk; }
 
-// Residual and quasi Jacobian at the iterate (H == nullptr: the zero guess).
+// Residual and quasi Jacobian at the iterate (H == nullptr: the zero guess).  A block
+// covers 4 steps (rows of B*T) x 64 channels (D <= 64).
 __global__ void __launch_bounds__(256) gru_elk_cell_kernel(const float* __restrict__ gx, const float* __restrict__ gh,
                                                            const float* __restrict__ hprev,
                                                            const float* __restrict__ H, const float* __restrict__ U,
                                                            float* __restrict__ R, float* __restrict__ J,
-                                                           uint32_t* __restrict__ rmax, size_t n, int D) {
+                                                           uint32_t* __restrict__ rmax, size_t rows, int D) {
   __shared__ uint32_t swmax[4];
+  const int i = threadIdx.x & 63, w = threadIdx.x >> 6;
   uint32_t m = 0;
-  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
-    const size_t bt = e / D;
-    const int i = (int)(e - bt * D);
+  // rows walked grid-stride, so that one atomic per block stays cheap
+  for (size_t bt = (size_t)blockIdx.x * 4 + w; bt < rows && i < D; bt += (size_t)gridDim.x * 4) {
+    const size_t e = bt * D + i;
     const float* gxr = gx + bt * 3 * D;
     const float* ghr = gh + bt * 3 * D;
     const float r = sigm(gxr[i] + ghr[i]);
@@ -53,7 +55,7 @@ __global__ void __launch_bounds__(256) gru_elk_cell_kernel(const float* __restri
     m = max(m, __float_as_uint(fabsf(res)));
   }
   for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-  if ((threadIdx.x & 63) == 0) swmax[threadIdx.x >> 6] = m;
+  if (i == 0) swmax[w] = m;
   __syncthreads();
   if (threadIdx.x == 0) atomicMax(rmax, max(max(swmax[0], swmax[1]), max(swmax[2], swmax[3])));
 }
@@ -129,19 +131,39 @@ __global__ void __launch_bounds__(256) gru_elk_filter_kernel(const float* __rest
   }
 }
 
-// Filter carry along the chunks of each channel: state (u, 1, n) entering chunk c.
+// Filter carry along the chunks of one channel (one 64-thread block per (channel, b)):
+// the state (u, 1, n) entering each chunk.  Lanes take 64 chunks at a time; an inclusive
+// Hillis-Steele scan of their maps through LDS (lane order = time) gives each lane's
+// entering state from the group's.
 __global__ void __launch_bounds__(64) gru_elk_filter_carry_kernel(const float* __restrict__ agg,
                                                                   float* __restrict__ carry, int D, int nch) {
-  const int b = blockIdx.x, i = threadIdx.x;
-  if (i >= D) return;
-  V3 x{0.f, 1.f, 0.f};
-  for (int c = 0; c < nch; ++c) {
-    const size_t cb = (size_t)b * nch + c;
-    carry[cb * 2 * D + i] = x.u;
-    carry[cb * 2 * D + D + i] = x.n;
-    const float* a = agg + cb * 7 * D + i;
-    const Flt F{a[0], a[D], a[2 * D], a[3 * D], a[4 * D], a[5 * D], a[6 * D]};
-    x = normalized(apply(F, x));
+  __shared__ Flt sm[64];
+  const int i = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  V3 x{0.f, 1.f, 0.f};   // entering the group
+  for (int g0 = 0; g0 < nch; g0 += 64) {
+    const int c = g0 + lane;
+    Flt F = flt_identity();
+    if (c < nch) {
+      const float* a = agg + ((size_t)b * nch + c) * 7 * D + i;
+      F = Flt{a[0], a[D], a[2 * D], a[3 * D], a[4 * D], a[5 * D], a[6 * D]};
+    }
+    for (int off = 1; off < 64; off <<= 1) {
+      sm[lane] = F;
+      __syncthreads();
+      const Flt prev = lane >= off ? sm[lane - off] : flt_identity();
+      __syncthreads();
+      F = compose(F, prev);
+    }
+    sm[lane] = F;
+    __syncthreads();
+    const V3 xin = lane == 0 ? x : normalized(apply(sm[lane - 1], x));
+    if (c < nch) {
+      const size_t cb = (size_t)b * nch + c;
+      carry[cb * 2 * D + i] = xin.u;
+      carry[cb * 2 * D + D + i] = xin.n;
+    }
+    x = normalized(apply(sm[63], x));
+    __syncthreads();
   }
 }
 
@@ -185,24 +207,48 @@ __global__ void __launch_bounds__(256) gru_elk_smooth_kernel(const float* __rest
   }
 }
 
+// Smoother carry along the chunks of one channel, backwards in time: lane l takes chunk
+// nch - 1 - (g0 + l), so lane order is reverse time and the same lane scan applies.
 __global__ void __launch_bounds__(64) gru_elk_smooth_carry_kernel(const float* __restrict__ agg2,
                                                                   float* __restrict__ carry2, int D, int nch) {
-  const int b = blockIdx.x, i = threadIdx.x;
-  if (i >= D) return;
-  float x = 0.f;
-  for (int c = nch - 1; c >= 0; --c) {
-    const size_t cb = (size_t)b * nch + c;
-    carry2[cb * D + i] = x;
-    x = fmaf(agg2[cb * 2 * D + i], x, agg2[cb * 2 * D + D + i]);
+  __shared__ float sp[64], sq[64];
+  const int i = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  float x = 0.f;   // h' at the step after the group (none after the last chunk)
+  for (int g0 = 0; g0 < nch; g0 += 64) {
+    const int c = nch - 1 - (g0 + lane);
+    float P = 1.f, Q = 0.f;
+    if (c >= 0) {
+      const size_t cb = (size_t)b * nch + c;
+      P = agg2[cb * 2 * D + i];
+      Q = agg2[cb * 2 * D + D + i];
+    }
+    for (int off = 1; off < 64; off <<= 1) {
+      sp[lane] = P;
+      sq[lane] = Q;
+      __syncthreads();
+      const float pp = lane >= off ? sp[lane - off] : 1.f, pq = lane >= off ? sq[lane - off] : 0.f;
+      __syncthreads();
+      Q = fmaf(P, pq, Q);   // (P, Q) o (pp, pq)
+      P *= pp;
+    }
+    sp[lane] = P;
+    sq[lane] = Q;
+    __syncthreads();
+    const float xin = lane == 0 ? x : fmaf(sp[lane - 1], x, sq[lane - 1]);
+    if (c >= 0) carry2[((size_t)b * nch + c) * D + i] = xin;
+    x = fmaf(sp[63], x, sq[63]);
+    __syncthreads();
   }
 }
 
 hipError_t launch_gru_elk_cell(const float* gx, const float* gh, const float* hprev, const float* H, const float* U,
                                float* R, float* J, uint32_t* rmax, size_t n, int D, hipStream_t st) {
-  size_t blocks = (n + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
+  if (D > 64) return hipErrorInvalidValue;
+  const size_t rows = n / D;
+  size_t blocks = (rows + 3) / 4;
+  if (blocks > 1024) blocks = 1024;
   hipLaunchKernelGGL(gru_elk_cell_kernel, dim3((unsigned)blocks), dim3(256), 0, st, gx, gh, hprev, H, U, R, J, rmax,
-                     n, D);
+                     rows, D);
   return hipGetLastError();
 }
 
@@ -214,11 +260,11 @@ hipError_t launch_gru_elk_step(const float* J, const float* R, const float* H, f
   dim3 grid((nch + 3) / 4, B);
   hipLaunchKernelGGL(gru_elk_filter_kernel<false>, grid, dim3(256), 0, st, J, R, H, lam, agg, nullptr, nullptr,
                      nullptr, T, D, nch);
-  hipLaunchKernelGGL(gru_elk_filter_carry_kernel, dim3(B), dim3(64), 0, st, agg, carry, D, nch);
+  hipLaunchKernelGGL(gru_elk_filter_carry_kernel, dim3(D, B), dim3(64), 0, st, agg, carry, D, nch);
   hipLaunchKernelGGL(gru_elk_filter_kernel<true>, grid, dim3(256), 0, st, J, R, H, lam, agg, carry, Gc, Ec, T, D,
                      nch);
   hipLaunchKernelGGL(gru_elk_smooth_kernel<false>, grid, dim3(256), 0, st, Gc, Ec, agg2, nullptr, nullptr, T, D, nch);
-  hipLaunchKernelGGL(gru_elk_smooth_carry_kernel, dim3(B), dim3(64), 0, st, agg2, carry2, D, nch);
+  hipLaunchKernelGGL(gru_elk_smooth_carry_kernel, dim3(D, B), dim3(64), 0, st, agg2, carry2, D, nch);
   hipLaunchKernelGGL(gru_elk_smooth_kernel<true>, grid, dim3(256), 0, st, Gc, Ec, agg2, carry2, Hn, T, D, nch);
   return hipGetLastError();
 }
