@@ -29,7 +29,8 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0, "f64": 78.6}   # dense, published
 PRIMARY = "gru_quasi"
 DEFAULT_OTHERS = ("tiny_gru,gru_full,gru_diag_long,lstm_diag_long,lstm_diag_long_chunked,lstm_diag_long_stiff,"
-                  "gru_diag_long_elk,gru_quasi_elk,gru_quasi_bwd,gru_diag_long_bwd,lstm_diag_long_bwd")
+                  "gru_diag_long_elk,gru_quasi_elk,gru_quasi_bwd,gru_diag_long_bwd,lstm_diag_long_bwd,"
+                  "lstm_diag_long_chunked_bwd")
 CSRC = "nonlinear_rnn_evaluation_amd/csrc/"
 
 
@@ -330,9 +331,12 @@ def run_backward(name, steps, warmup, parity=True):
     t_gen = time.perf_counter() - t_gen
     stream = torch.cuda.current_stream()
 
+    chunk_len = w.chunk_len or 0
+    launches = -(-w.T // chunk_len) if chunk_len else 1
+
     def call(ws=None):
         return pnr.backward(w.cell, d["W"], d["U"], d["x"], h, g, b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"],
-                            workspace=ws)
+                            workspace=ws, chunk_len=chunk_len)
 
     first = call()
     ws = first["workspace"]
@@ -370,9 +374,10 @@ def run_backward(name, steps, warmup, parity=True):
             traffic = pmc.get("bytes_per_launch")
     kname = ("adjoint refinement loop (MFMA GEMM, residual, scan and update kernels; one read-back per 4 "
              "iterations)" if dense else "pnr::adjoint_diag_kernel")
-    roof = {"kernel": kname, "avg_launch_us": round(adj_ms * 1e3, 3), "launches_per_step": 1,
+    roof = {"kernel": kname, "avg_launch_us": round(adj_ms * 1e3 / launches, 3), "launches_per_step": launches,
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "algorithmic_bytes_per_launch": bytes_call}
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "algorithmic_bytes_per_launch": bytes_call // launches}
     gemm_flops = 2 * 2.0 * w.B * w.T * w.D_in * w.G * w.D
     phases["projection"] = "GEMM kernel (recomputed)"
     phases["proj_tflops"] = round(2.0 * w.B * w.T * w.D_in * w.G * w.D / (phases["proj_ms"] * 1e-3) / 1e12, 2)

@@ -244,6 +244,34 @@ int pnr_backward(const pnr_cell* cell, const pnr_params* params, const void* x, 
                  void* grad_b_x, void* grad_b_h, void* grad_h0);
 
 /*
+ * Backward pass over chunks, the gradient-checkpointing half of chunked evaluation
+ * (ParaRNN overview page, "Experimental Results": chunking together with gradient
+ * checkpointing keeps the memory of long sequences in check).  The sequence is cut into
+ * consecutive chunks of chunk_len steps (the last may be shorter), as pnr_eval_chunked
+ * cuts it, and the chunks are processed last to first, each by pnr_backward on the
+ * chunk's steps, with initial state h0 for the first chunk and h[b, t0 - 1] for the
+ * others.  The adjoint crossing a boundary, J^T lam of the later chunk's first step
+ * (that chunk's grad_h0), is added to grad_h at the earlier chunk's last step, so that
+ * the result is pnr_backward's on the whole sequence up to rounding (and, for the dense
+ * GRU, up to each chunk's refinement tolerance).  Weight and bias gradients are summed
+ * over chunks; grad_x and the first chunk's grad_h0 are written per chunk.  Arguments,
+ * layouts and NULL outputs as for pnr_backward; chunk_len >= 1.  Workspace:
+ * pnr_workspace_bytes_backward_chunked() bytes (0 = invalid or unsupported request): one
+ * chunk's pnr_backward workspace, the chunk's grad_h, two B x S boundary adjoints, one
+ * set of weight-gradient partials and, for B > 1 with more than one chunk, contiguous
+ * staging of the chunk's x, h and grad_x.  Results: the worst status over chunks
+ * (NONFINITE > NOT_CONVERGED > OK; every chunk is processed); pnr_iters_used() = the
+ * sum of the chunks' refinement iterations; pnr_last_residual() = the largest;
+ * pnr_last_residual_history() = the chunks' histories, last chunk first; the profile
+ * record holds sums over chunks.  Synchronises the stream before returning.
+ */
+size_t pnr_workspace_bytes_backward_chunked(const pnr_cell* cell, int chunk_len);
+int pnr_backward_chunked(const pnr_cell* cell, const pnr_params* params, const void* x,
+                         const void* h0, const void* h, const void* grad_h, void* grad_x,
+                         void* grad_W, void* grad_U, void* grad_b_x, void* grad_b_h,
+                         void* grad_h0, int chunk_len);
+
+/*
  * Standalone linear solve used inside every Newton iteration, exposed for testing
  * the scan on its own: d_t = A_t d_{t-1} + b_t, d_0 = 0 along t, for R independent
  * rows (ParaRNN overview, "Newton's Iteration": forward substitution on the block

@@ -1068,6 +1068,179 @@ int pnr_backward(const pnr_cell* cell, const pnr_params* params, const void* x, 
   return PNR_OK;
 }
 
+// ---- backward pass over chunks (gradient checkpointing) ----
+namespace {
+__global__ void __launch_bounds__(256) axpy_kernel(float* __restrict__ y, const float* __restrict__ x, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    y[i] += x[i];
+}
+// g[b][L-1][s] += mu[b][s]: the adjoint arriving from the later chunk joins the loss
+// gradient of the chunk's last step
+__global__ void __launch_bounds__(256) add_last_row_kernel(float* __restrict__ g, const float* __restrict__ mu, int B,
+                                                           int L, int S) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= B * S) return;
+  const int b = e / S, c = e - b * S;
+  g[((size_t)b * L + (L - 1)) * S + c] += mu[e];
+}
+hipError_t launch_axpy(float* y, const float* x, size_t n, hipStream_t st) {
+  if (!y || n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(axpy_kernel, dim3((unsigned)blocks), dim3(256), 0, st, y, x, n);
+  return hipGetLastError();
+}
+
+struct BwdChunkPlan {
+  int L = 0;
+  bool staged = false;   // B > 1 with several chunks: x, h, dx of a chunk go through staging
+  pnr_cell sub{};
+  size_t sub_bytes = 0, x_off = 0, h_off = 0, g_off = 0, dx_off = 0, h0_off = 0, gw_off = 0, gu_off = 0,
+         gbx_off = 0, gbh_off = 0, mu_off[2] = {0, 0}, total = 0;
+};
+int plan_bwd_chunks(const pnr_cell* c, int chunk_len, BwdChunkPlan& p) {
+  if (!c) return fail(PNR_E_INVALID, "cell descriptor is NULL");
+  if (chunk_len < 1) return fail(PNR_E_INVALID, "chunk_len must be >= 1 (got %d)", chunk_len);
+  if (c->T < 0) return fail(PNR_E_INVALID, "T must be >= 0 (got %d)", c->T);
+  p.L = c->T < chunk_len ? c->T : chunk_len;
+  p.sub = *c;
+  p.sub.T = p.L;
+  const int rc = validate_backward(&p.sub);
+  if (rc) return rc;
+  p.sub_bytes = make_bwd_layout(&p.sub).total;
+  p.staged = c->B > 1 && c->T > p.L;
+  const size_t B = c->B, L = p.L, D = c->D, Din = c->D_in, G = gates(c->kind), S = states(c->kind, c->D);
+  const size_t f = sizeof(float), u_elems = c->kind == PNR_CELL_GRU ? G * D * D : G * D;
+  size_t off = align_up(p.sub_bytes);
+  p.g_off = off; off = align_up(off + f * B * L * S);
+  if (p.staged) {
+    p.x_off = off; off = align_up(off + dsize(c->x_dtype) * B * L * Din);
+    p.h_off = off; off = align_up(off + f * B * L * S);
+    p.dx_off = off; off = align_up(off + f * B * L * Din);
+  }
+  p.h0_off = off; off = align_up(off + f * B * S);
+  p.gw_off = off; off = align_up(off + f * G * D * Din);
+  p.gu_off = off; off = align_up(off + f * u_elems);
+  p.gbx_off = off; off = align_up(off + f * G * D);
+  p.gbh_off = off; off = align_up(off + f * G * D);
+  for (int i = 0; i < 2; ++i) { p.mu_off[i] = off; off = align_up(off + f * B * S); }
+  p.total = off;
+  return 0;
+}
+}  // namespace
+
+size_t pnr_workspace_bytes_backward_chunked(const pnr_cell* cell, int chunk_len) {
+  BwdChunkPlan p;
+  if (plan_bwd_chunks(cell, chunk_len, p) != 0) return 0;
+  return p.total;
+}
+
+int pnr_backward_chunked(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, const void* h,
+                         const void* grad_h, void* grad_x, void* grad_W, void* grad_U, void* grad_b_x,
+                         void* grad_b_h, void* grad_h0, int chunk_len) {
+  g_last = LastCall();
+  g_prof.valid = false;
+  BwdChunkPlan p;
+  int rc = plan_bwd_chunks(cell, chunk_len, p);
+  if (rc) return rc;
+  if (!params) return fail(PNR_E_INVALID, "params is NULL");
+  if (!params->W || !params->U || (cell->T > 0 && (!x || !h || !grad_h)))
+    return fail(PNR_E_INVALID, "W, U and (for T > 0) x, h and grad_h must be non-NULL");
+  if (!cell->workspace) return fail(PNR_E_WORKSPACE, "workspace is NULL (%zu bytes required)", p.total);
+  if ((uintptr_t)cell->workspace % 256) return fail(PNR_E_WORKSPACE, "workspace must be 256-byte aligned");
+  if (cell->workspace_bytes < p.total)
+    return fail(PNR_E_WORKSPACE, "workspace has %zu bytes, %zu required", cell->workspace_bytes, p.total);
+  if (cell->T == 0) {
+    pnr_cell sub = p.sub;
+    sub.workspace_bytes = p.sub_bytes;
+    return pnr_backward(&sub, params, x, h0, h, grad_h, grad_x, grad_W, grad_U, grad_b_x, grad_b_h, grad_h0);
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(cell->stream);
+  char* ws = static_cast<char*>(cell->workspace);
+  auto fp = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  const size_t B = cell->B, T = cell->T, D = cell->D, Din = cell->D_in, G = gates(cell->kind);
+  const size_t S = states(cell->kind, cell->D), xes = dsize(cell->x_dtype), f = sizeof(float);
+  const size_t u_elems = cell->kind == PNR_CELL_GRU ? G * D * D : G * D;
+  const char* xb = static_cast<const char*>(x);
+  const char* hb = static_cast<const char*>(h);
+  const char* gb = static_cast<const char*>(grad_h);
+  const int nck = (int)((T + p.L - 1) / p.L);
+  int status = PNR_OK, iters = 0, mu = 0;
+  double residual = 0.0;
+  std::vector<double> hist;
+  pnr_profile acc{};
+  bool prof_ok = g_prof.on;
+  for (int c = nck - 1; c >= 0; --c) {
+    const size_t t0 = (size_t)c * p.L, Lc = std::min((size_t)p.L, T - t0);
+    pnr_cell sub = p.sub;
+    sub.T = (int)Lc;
+    sub.workspace = ws;
+    sub.workspace_bytes = p.sub_bytes;
+    // the chunk's loss gradient, with the adjoint from the later chunk at its last step
+    float* gc = fp(p.g_off);
+    PNR_HIP(hipMemcpy2DAsync(gc, Lc * S * f, gb + t0 * S * f, T * S * f, Lc * S * f, B, hipMemcpyDeviceToDevice, st));
+    if (c < nck - 1)
+      hipLaunchKernelGGL(add_last_row_kernel, dim3((unsigned)((B * S + 255) / 256)), dim3(256), 0, st, gc,
+                         fp(p.mu_off[mu ^ 1]), (int)B, (int)Lc, (int)S);
+    const void* xc = xb + t0 * Din * xes;
+    const void* hc = hb + t0 * S * f;
+    void* dxc = grad_x ? static_cast<char*>(grad_x) + t0 * Din * f : nullptr;
+    if (p.staged) {
+      PNR_HIP(hipMemcpy2DAsync(ws + p.x_off, Lc * Din * xes, xc, T * Din * xes, Lc * Din * xes, B,
+                               hipMemcpyDeviceToDevice, st));
+      PNR_HIP(hipMemcpy2DAsync(ws + p.h_off, Lc * S * f, hc, T * S * f, Lc * S * f, B, hipMemcpyDeviceToDevice, st));
+      xc = ws + p.x_off;
+      hc = ws + p.h_off;
+      if (dxc) dxc = ws + p.dx_off;
+    }
+    // the state before the chunk: h0, or the last state of the earlier chunk
+    const void* h0c = h0;
+    if (t0 > 0) {
+      PNR_HIP(hipMemcpy2DAsync(ws + p.h0_off, S * f, hb + (t0 - 1) * S * f, T * S * f, S * f, B,
+                               hipMemcpyDeviceToDevice, st));
+      h0c = ws + p.h0_off;
+    }
+    // the first chunk processed writes the weight gradients, the others are added to them
+    const bool first = c == nck - 1;
+    float* gW = grad_W ? (first ? static_cast<float*>(grad_W) : fp(p.gw_off)) : nullptr;
+    float* gU = grad_U ? (first ? static_cast<float*>(grad_U) : fp(p.gu_off)) : nullptr;
+    float* gbx = grad_b_x ? (first ? static_cast<float*>(grad_b_x) : fp(p.gbx_off)) : nullptr;
+    float* gbh = grad_b_h ? (first ? static_cast<float*>(grad_b_h) : fp(p.gbh_off)) : nullptr;
+    // dL/d(state before the chunk): the next chunk's carry, or dL/dh0 for the first chunk
+    float* dmu = c > 0 ? fp(p.mu_off[mu]) : static_cast<float*>(grad_h0);
+    rc = pnr_backward(&sub, params, xc, h0c, hc, gc, dxc, gW, gU, gbx, gbh, dmu);
+    if (rc < 0) return rc;   // g_last.err holds the chunk's error
+    if (status_rank(rc) > status_rank(status)) status = rc;
+    if (prof_ok && g_prof.valid) {
+      const pnr_profile& q = g_prof.last;
+      acc.total_ms += q.total_ms; acc.proj_ms += q.proj_ms; acc.newton_ms += q.newton_ms; acc.out_ms += q.out_ms;
+      acc.passes += q.passes;
+    } else {
+      prof_ok = false;
+    }
+    iters += g_last.iters;
+    if (!(g_last.residual <= residual)) residual = g_last.residual;
+    hist.insert(hist.end(), g_last.hist.begin(), g_last.hist.end());
+    if (p.staged && grad_x)
+      PNR_HIP(hipMemcpy2DAsync(static_cast<char*>(grad_x) + t0 * Din * f, T * Din * f, dxc, Lc * Din * f,
+                               Lc * Din * f, B, hipMemcpyDeviceToDevice, st));
+    if (!first) {
+      PNR_HIP(launch_axpy(static_cast<float*>(grad_W), gW, G * D * Din, st));
+      PNR_HIP(launch_axpy(static_cast<float*>(grad_U), gU, u_elems, st));
+      PNR_HIP(launch_axpy(static_cast<float*>(grad_b_x), gbx, G * D, st));
+      PNR_HIP(launch_axpy(static_cast<float*>(grad_b_h), gbh, G * D, st));
+    }
+    mu ^= 1;
+  }
+  PNR_HIP(hipStreamSynchronize(st));
+  g_last.iters = iters;
+  g_last.residual = residual;
+  g_last.hist = std::move(hist);
+  g_prof.valid = prof_ok;
+  if (prof_ok) g_prof.last = acc;
+  return status;
+}
+
 size_t pnr_scan_workspace_bytes(int kind, int R, int T, int tile_len) {
   if ((kind != 1 && kind != 2) || R < 0 || T < 0) {
     fail(PNR_E_INVALID, "bad scan arguments");

@@ -77,6 +77,10 @@ def load() -> ctypes.CDLL:
     lib.pnr_workspace_bytes_backward.restype = ctypes.c_size_t
     lib.pnr_backward.argtypes = [P(PnrCell), P(PnrParams)] + [ctypes.c_void_p] * 10
     lib.pnr_backward.restype = ctypes.c_int
+    lib.pnr_workspace_bytes_backward_chunked.argtypes = [P(PnrCell), ctypes.c_int]
+    lib.pnr_workspace_bytes_backward_chunked.restype = ctypes.c_size_t
+    lib.pnr_backward_chunked.argtypes = [P(PnrCell), P(PnrParams)] + [ctypes.c_void_p] * 10 + [ctypes.c_int]
+    lib.pnr_backward_chunked.restype = ctypes.c_int
     lib.pnr_iters_used.argtypes = []
     lib.pnr_iters_used.restype = ctypes.c_int
     lib.pnr_last_residual.argtypes = []
@@ -183,6 +187,18 @@ def pnr_backward(cell: PnrCell, params: PnrParams, x: int, h0: Optional[int], h:
                                grad_b_x, grad_b_h, grad_h0)
 
 
+def pnr_workspace_bytes_backward_chunked(cell: PnrCell, chunk_len: int) -> int:
+    return load().pnr_workspace_bytes_backward_chunked(ctypes.byref(cell), chunk_len)
+
+
+def pnr_backward_chunked(cell: PnrCell, params: PnrParams, x: int, h0: Optional[int], h: int, grad_h: int,
+                         grad_x: Optional[int], grad_W: Optional[int], grad_U: Optional[int],
+                         grad_b_x: Optional[int], grad_b_h: Optional[int], grad_h0: Optional[int],
+                         chunk_len: int) -> int:
+    return load().pnr_backward_chunked(ctypes.byref(cell), ctypes.byref(params), x, h0, h, grad_h, grad_x, grad_W,
+                                       grad_U, grad_b_x, grad_b_h, grad_h0, chunk_len)
+
+
 def pnr_iters_used() -> int:
     return load().pnr_iters_used()
 
@@ -283,12 +299,14 @@ def evaluate(kind: int, W: torch.Tensor, U: torch.Tensor, x: torch.Tensor, *, b_
 
 def backward(kind: int, W: torch.Tensor, U: torch.Tensor, x: torch.Tensor, h: torch.Tensor, grad_h: torch.Tensor,
              *, b_x=None, b_h=None, h0=None, want=("x", "W", "U", "b_x", "b_h", "h0"),
-             workspace: Optional[torch.Tensor] = None) -> dict:
+             workspace: Optional[torch.Tensor] = None, chunk_len: int = 0) -> dict:
     """Run pnr_backward on device tensors: gradients of L through the recurrence whose
     states are h, given grad_h = dL/dh.  Returns {name: fp32 tensor} for the names in
     `want` (the others are not computed), plus "workspace" and the adjoint solve's
     "status", "iters", "residual" and "history" (dense GRU: refinement iterations;
-    diagonal cells: one scan, iters 0)."""
+    diagonal cells: one scan, iters 0).  chunk_len > 0 runs pnr_backward_chunked: the
+    sequence is processed in chunks of that many steps, last chunk first, with a
+    workspace sized for one chunk."""
     B, T, D_in = x.shape
     G, D = (U.shape[0] // U.shape[1], U.shape[1]) if kind == CELL_GRU else (U.shape[0], U.shape[1])
     S = 2 * D if kind == CELL_LSTM_DIAG else D
@@ -300,7 +318,9 @@ def backward(kind: int, W: torch.Tensor, U: torch.Tensor, x: torch.Tensor, h: to
                 b_h=_check(b_h, "b_h", sd, (G * D,)), h0=_check(h0, "h0", sd, (B, S)), U=U, x=x)
     ptrs = {k: _ptr(v) for k, v in args.items()}
     cell = make_cell(kind, D, D_in, T, B, _DT[x.dtype], _DT[U.dtype], 1, _stream())
-    need = pnr_workspace_bytes_backward(cell)
+    if chunk_len < 0:
+        raise ValueError(f"chunk_len must be >= 0 (got {chunk_len})")
+    need = pnr_workspace_bytes_backward_chunked(cell, chunk_len) if chunk_len else pnr_workspace_bytes_backward(cell)
     if need == 0:
         raise PnrError(pnr_last_error())
     if workspace is None or workspace.numel() < need:
@@ -312,10 +332,13 @@ def backward(kind: int, W: torch.Tensor, U: torch.Tensor, x: torch.Tensor, h: to
               "h0": (B, S)}
     out = {k: torch.empty(shapes[k], **f32) for k in want}
     params = PnrParams(ptrs["W"], ptrs["U"], ptrs["b_x"], ptrs["b_h"])
-    rc = pnr_backward(cell, params, ptrs["x"], ptrs["h0"], ptrs["h"], ptrs["grad_h"],
-                      *(_ptr(out.get(k)) for k in ("x", "W", "U", "b_x", "b_h", "h0")))
+    grads = [_ptr(out.get(k)) for k in ("x", "W", "U", "b_x", "b_h", "h0")]
+    if chunk_len:
+        rc = pnr_backward_chunked(cell, params, ptrs["x"], ptrs["h0"], ptrs["h"], ptrs["grad_h"], *grads, chunk_len)
+    else:
+        rc = pnr_backward(cell, params, ptrs["x"], ptrs["h0"], ptrs["h"], ptrs["grad_h"], *grads)
     if rc < 0:
-        raise PnrError(f"pnr_backward returned {rc}: {pnr_last_error()}")
+        raise PnrError(f"pnr_backward{'_chunked' if chunk_len else ''} returned {rc}: {pnr_last_error()}")
     out.update(workspace=workspace, status=rc, iters=pnr_iters_used(), residual=pnr_last_residual(),
                history=pnr_last_residual_history())
     return out

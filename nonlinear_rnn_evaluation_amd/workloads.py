@@ -139,6 +139,10 @@ def named_workloads() -> dict:
     # the backward pass (all gradients) at the converged states of the two long workloads
     for base in ("gru_quasi", "gru_diag_long", "lstm_diag_long"):
         w[base + "_bwd"] = dataclasses.replace(w[base], name=base + "_bwd", backward=True)
+    # ... and the long LSTM's backward pass over chunks of 8192 steps (gradient
+    # checkpointing: the workspace covers one chunk)
+    w["lstm_diag_long_chunked_bwd"] = dataclasses.replace(w["lstm_diag_long_chunked"],
+                                                          name="lstm_diag_long_chunked_bwd", backward=True)
     # the stiff LSTM with the damped step on the diagonal Jacobian (quasi-ELK), which
     # converges where both undamped variants do not
     w["lstm_diag_long_stiff_elk"] = dataclasses.replace(

@@ -179,6 +179,36 @@ def test_backward_requests_are_validated_without_a_gpu():
     assert pnr.pnr_workspace_bytes_backward(_cell(jac_every=3)) == pnr.pnr_workspace_bytes_backward(_cell())
 
 
+def test_chunked_backward_requests_are_validated_without_a_gpu():
+    params = pnr.PnrParams(1024, 2048, None, None)
+    for kind in (pnr.CELL_GRU_DIAG, pnr.CELL_LSTM_DIAG, pnr.CELL_GRU):
+        c = _cell(kind=kind, B=2, T=1000, D=64, D_in=32)
+        one = _cell(kind=kind, B=2, T=250, D=64, D_in=32)
+        G, S = {pnr.CELL_GRU_DIAG: (3, 64), pnr.CELL_LSTM_DIAG: (4, 128), pnr.CELL_GRU: (3, 64)}[kind]
+        Uel = 3 * 64 * 64 if kind == pnr.CELL_GRU else G * 64
+        n = pnr.pnr_workspace_bytes_backward_chunked(c, 250)
+        # one chunk's workspace, its grad_h, staging of x, h and grad_x (B > 1), the
+        # boundary state, the weight-gradient partials and two boundary adjoints
+        low = (pnr.pnr_workspace_bytes_backward(one)
+               + 4 * (2 * 250 * S * 2 + 2 * 250 * 32 * 2 + 2 * S * 3 + G * 64 * 32 + Uel + 2 * G * 64))
+        assert low <= n < low + 16 * 256
+        # the chunk's workspace is what bounds memory: a quarter of the unchunked one, roughly
+        assert n < 0.5 * pnr.pnr_workspace_bytes_backward(c)
+        # a chunk at least as long as the sequence needs no staging
+        whole = pnr.pnr_workspace_bytes_backward_chunked(c, 1000)
+        assert pnr.pnr_workspace_bytes_backward(c) < whole == pnr.pnr_workspace_bytes_backward_chunked(c, 5000)
+        for bad_len in (0, -3):
+            assert pnr.pnr_workspace_bytes_backward_chunked(c, bad_len) == 0
+            assert pnr.pnr_backward_chunked(c, params, 4096, None, 8192, 8192, *[None] * 6, bad_len) == pnr.E_INVALID
+        assert pnr.pnr_backward_chunked(c, params, 4096, None, 8192, 8192, *[None] * 6, 250) == pnr.E_WORKSPACE
+        assert pnr.pnr_backward_chunked(c, params, 4096, None, None, 8192, *[None] * 6, 250) == pnr.E_INVALID
+    # what pnr_backward rejects, the chunked call rejects the same way
+    for bad in (dict(kind=pnr.CELL_GRU, D=65), dict(kind=pnr.CELL_GRU, D=16, x_dtype=pnr.F64, state_dtype=pnr.F64)):
+        c = _cell(**bad)
+        assert pnr.pnr_workspace_bytes_backward_chunked(c, 100) == 0
+        assert pnr.pnr_backward_chunked(c, params, 4096, None, 8192, 8192, *[None] * 6, 100) == pnr.E_UNSUPPORTED
+
+
 def test_binding_rejects_tensors_of_the_wrong_dtype_or_shape():
     """The library reads raw memory: the binding must refuse a tensor whose dtype or shape
     differs from what the call describes instead of letting it be reinterpreted."""

@@ -43,10 +43,10 @@ def _case(cell, B, T, D, Din, xd=WL.DT_F32, seed=0, h0=True, bh=True):
     return p, H32, g, ref
 
 
-def _run(cell, p, H32, g, want=tuple(NAMES)):
+def _run(cell, p, H32, g, want=tuple(NAMES), chunk_len=0):
     d = {k: (None if v is None else v.to(DEV)) for k, v in p.items()}
     return pnr.backward(cell, d["W"], d["U"], d["x"], torch.from_numpy(H32).to(DEV), torch.from_numpy(g).to(DEV),
-                        b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"], want=want)
+                        b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"], want=want, chunk_len=chunk_len)
 
 
 def _check(got, ref, names=tuple(NAMES), tol=1e-4):
@@ -156,3 +156,75 @@ def test_dense_gru_bf16_inputs_and_empty_sequence():
     z = torch.empty(2, 0, 16, device=DEV, dtype=torch.float32)
     r = pnr.backward(cell, d["W"], d["U"], d["x"], z, z, b_x=d["b_x"], h0=d["h0"])
     assert r["U"].shape == (48, 16) and torch.count_nonzero(r["U"]) == 0 and torch.count_nonzero(r["h0"]) == 0
+
+
+# ---------------------------------------------------------------------------------
+# Chunked backward (pnr_backward_chunked): chunks processed last to first, the adjoint
+# carried across each boundary.  Held to the oracle's bar, and to the unchunked call on
+# the same inputs, which differs from it only in the order of fp32 sums (adjoint across
+# a boundary, weight gradients summed per chunk), so far more tightly.
+def _close(a, b, names, tol):
+    for k in names:
+        x, y = a[k].double().cpu(), b[k].double().cpu()
+        scale = max(float(y.abs().max()), 1e-30)
+        err = float((x - y).abs().max()) / scale
+        assert err < tol, (k, err)
+
+
+@pytest.mark.parametrize("cell,D,Din", [(WL.CELL_GRU_DIAG, 6, 5), (WL.CELL_LSTM_DIAG, 4, 3)])
+@pytest.mark.parametrize("B,T,L", [(2, 37, 1), (2, 1025, 100), (1, 1025, 100), (2, 2 * 1024 + 301, 1024),
+                                   (3, 700, 700), (2, 300, 5000)])
+def test_chunked_gradients_match_the_oracle(cell, D, Din, B, T, L):
+    p, H32, g, ref = _case(cell, B, T, D, Din, seed=(T + L) % 97)
+    print(f"# chunked backward cell={cell} B={B} T={T} chunk={L}", flush=True)
+    got = _run(cell, p, H32, g, chunk_len=L)
+    assert got["status"] == pnr.OK
+    _check(got, ref)
+    _close(got, _run(cell, p, H32, g), NAMES, 2e-5)
+
+
+@pytest.mark.parametrize("D,T,L", [(16, 1025, 300), (64, 2100, 512), (40, 777, 1)])
+def test_chunked_dense_gru_gradients_match_the_oracle(D, T, L):
+    """Each chunk's refinement stops at 2e-5 of that chunk's max |g| (the carried adjoint
+    included), so the bar is the unchunked dense one: 2e-4 of each gradient's scale."""
+    cell = WL.CELL_GRU
+    T = 60 if L == 1 else T   # one refinement per step: keep the one-step chunks few
+    p = WL.random_problem(cell, 2, T, D, 9, seed=D + T + L, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32,
+                          bias_std=0.2, h0_std=0.3, w_std=0.7 / np.sqrt(D))
+    q = {k: (None if v is None else WL.as_f64(v)) for k, v in p.items()}
+    H = O.sequential(cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"])
+    H32 = H.astype(np.float32)
+    g = np.random.default_rng(D * T + L).normal(size=H.shape).astype(np.float32)
+    ref = O.bptt(cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], H32.astype(np.float64),
+                 g.astype(np.float64))
+    print(f"# chunked dense backward D={D} T={T} chunk={L}", flush=True)
+    got = _run(cell, p, H32, g, chunk_len=L)
+    assert got["status"] == pnr.OK and got["iters"] > 0
+    _check(got, ref, tol=2e-4)
+
+
+def test_chunked_bf16_inputs_partial_requests_and_empty_sequence():
+    cell = WL.CELL_LSTM_DIAG
+    p, H32, g, ref = _case(cell, 3, 1500, 5, 8, xd=WL.DT_BF16, seed=4, h0=False, bh=False)
+    got = _run(cell, p, H32, g, chunk_len=333)
+    _check(got, ref, names=("U", "b_x", "b_h", "h0"))
+    B, T = 3, 1500
+    dgx = np.abs(ref["dgx"].reshape(B * T, -1))
+    xa = np.abs(WL.as_f64(p["x"]).reshape(B * T, -1))
+    Wa = np.abs(WL.as_f64(p["W"]))
+    for k, bound in (("W", dgx.T @ xa), ("x", (dgx @ Wa).reshape(B, T, -1))):
+        r = ref[NAMES[k]]
+        err = np.abs(got[k].double().cpu().numpy() - r)
+        assert np.all(err <= 2.0 ** -8 * bound + 1e-5 * np.abs(r).max()), (k, (err / (bound + 1e-30)).max())
+    p, H32, g, ref = _case(WL.CELL_GRU_DIAG, 2, 900, 7, 6, seed=9)
+    got = _run(WL.CELL_GRU_DIAG, p, H32, g, want=("W", "h0"), chunk_len=200)
+    assert set(got) & set(NAMES) == {"W", "h0"}
+    _check(got, ref, names=("W", "h0"))
+    got = _run(WL.CELL_GRU_DIAG, p, H32, g, want=("x", "b_h"), chunk_len=256)
+    _check(got, ref, names=("x", "b_h"))
+    e = WL.random_problem(cell, 2, 0, 3, 2, seed=1, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32)
+    d = {k: (None if v is None else v.to(DEV)) for k, v in e.items()}
+    z = torch.empty(2, 0, 6, device=DEV, dtype=torch.float32)
+    r = pnr.backward(cell, d["W"], d["U"], d["x"], z, z, b_x=d["b_x"], h0=d["h0"], chunk_len=16)
+    for k in ("W", "U", "b_x", "b_h", "h0"):
+        assert torch.count_nonzero(r[k]) == 0
