@@ -127,6 +127,179 @@ __global__ void __launch_bounds__(256, 4) gemm_bf16_mfma(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------------
+// bf16 MFMA GEMM with direct global -> LDS loads (global_load_lds_dwordx4), for K a
+// multiple of 32.  Waves and MFMA tiles as in gemm_bf16_mfma (each wave 64 x 64 of C), in
+// WM x 2 waves: block tile (64 WM) x 128 -- 256 x 128 for long M, which cuts the operand
+// bytes each CU pulls from L2 per MFMA by a quarter against 128 x 128.
+//  * Each lane's 16 B go straight from global memory into LDS (lane l of a load writes
+//    bytes 16l..16l+15 of a 1 KB run), so no registers stage the tiles and no LDS store
+//    instructions are issued.
+//  * Three LDS stages: loads run two K steps ahead of the MFMAs, with one barrier per K
+//    step.  Each stage is its own LDS array, so that the compiler can tell the stage being
+//    read from the stages being loaded and waits only for the loads it needs.
+//  * A tile row is 64 B (32 bf16) with its four 16-B chunks permuted by row bits 2-3.
+//    ds_read_b128 serves 16 lanes per cycle from 64 four-byte banks (measured with the
+//    bank-conflict counter); a fragment read's 16 lanes take 16 consecutive rows at one
+//    chunk, and the permutation puts them on 16 distinct 16-B bank groups.
+//  * Rows past M (or N) read the last row instead (their results are not stored), so
+//    every load is issued unconditionally and the wait counts stay exact.
+constexpr int GD_K = 32, GD_ROW = GD_K * 2;   // bytes of one tile row
+
+__device__ __forceinline__ int gd_swz(int row) { return (row >> 2) & 3; }
+
+template <int WM, int WN>
+struct GdCfg {
+  static constexpr int BM = 64 * WM, BN = 64 * WN, THREADS = 64 * WM * WN;
+  static constexpr int A_RUNS = BM / 16 / (WM * WN);   // 1 KB runs per wave and stage
+  static constexpr int B_RUNS = BN / 16 / (WM * WN);
+  static constexpr int LOADS = A_RUNS + B_RUNS;        // vmcnt of one stage
+};
+
+template <int WM, int WN>
+struct GdLoad {
+  const __bf16* pa[GdCfg<WM, WN>::A_RUNS];   // this lane's source rows
+  const __bf16* pb[GdCfg<WM, WN>::B_RUNS];
+  int ka[GdCfg<WM, WN>::A_RUNS], kb[GdCfg<WM, WN>::B_RUNS];   // element offset of its 16-B chunk
+};
+
+template <int WAIT>
+__device__ __forceinline__ void gd_wait_barrier() {
+  // vmcnt <= WAIT (expcnt and lgkmcnt left at their maxima), then the barrier
+  __builtin_amdgcn_s_waitcnt(0x0F70 | WAIT);
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <int WM, int WN>
+__device__ __forceinline__ void gd_issue(const GdLoad<WM, WN>& L, int k0, char* sa, char* sb, int wid) {
+  using C = GdCfg<WM, WN>;
+#pragma unroll
+  for (int h = 0; h < C::A_RUNS; ++h)
+    __builtin_amdgcn_global_load_lds(L.pa[h] + k0 + L.ka[h], sa + (C::A_RUNS * wid + h) * 1024, 16, 0, 0);
+#pragma unroll
+  for (int h = 0; h < C::B_RUNS; ++h)
+    __builtin_amdgcn_global_load_lds(L.pb[h] + k0 + L.kb[h], sb + (C::B_RUNS * wid + h) * 1024, 16, 0, 0);
+}
+
+__device__ __forceinline__ void gd_compute(const char* sa, const char* sb, int wm, int wn, int lane,
+                                           floatx16_t (&acc)[2][2]) {
+#pragma unroll
+  for (int ks = 0; ks < GD_K / 16; ++ks) {
+    const int kc = ks * 2 + (lane >> 5);
+    bf16x8_t fa[2], fb[2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+      const int r = wm * 64 + mi * 32 + (lane & 31);
+      fa[mi] = *reinterpret_cast<const bf16x8_t*>(sa + r * GD_ROW + 16 * (kc ^ gd_swz(r)));
+    }
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+      const int r = wn * 64 + ni * 32 + (lane & 31);
+      fb[ni] = *reinterpret_cast<const bf16x8_t*>(sb + r * GD_ROW + 16 * (kc ^ gd_swz(r)));
+    }
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+  }
+}
+
+// Four waves per SIMD: registers held to 128.
+template <int WM, int WN>
+__global__ void __launch_bounds__((GdCfg<WM, WN>::THREADS), 4) gemm_bf16_dma(GemmArgs g) {
+  using Cf = GdCfg<WM, WN>;
+  constexpr int SA = Cf::BM * GD_ROW, SB = Cf::BN * GD_ROW;
+  __shared__ __align__(1024) char sa0[SA], sa1[SA], sa2[SA];
+  __shared__ __align__(1024) char sb0[SB], sb1[SB], sb2[SB];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid / WN, wn = wid % WN;
+  const int z = blockIdx.z;
+  const int gx = (int)gridDim.x, gy = (int)gridDim.y;
+  const int lin = (int)blockIdx.y * gx + (int)blockIdx.x;
+  const int grp = lin / (GB_GM * gx), loc = lin - grp * GB_GM * gx;
+  const int gm = min(GB_GM, gy - grp * GB_GM);
+  const int i0 = (grp * GB_GM + loc % gm) * Cf::BM, j0 = (loc / gm) * Cf::BN;
+  const __bf16* A = reinterpret_cast<const __bf16*>(g.A) + (size_t)z * g.sA;
+  const __bf16* Bm = reinterpret_cast<const __bf16*>(g.Bm) + (size_t)z * g.sB;
+  float* C = reinterpret_cast<float*>(g.C) + (size_t)z * g.sC;
+
+  // lane l of a 1 KB run holds tile row 16 run + l/4, physical chunk l%4
+  GdLoad<WM, WN> L;
+#pragma unroll
+  for (int h = 0; h < Cf::A_RUNS; ++h) {
+    const int row = (Cf::A_RUNS * wid + h) * 16 + (lane >> 2);
+    L.ka[h] = 8 * ((lane & 3) ^ gd_swz(row));
+    L.pa[h] = A + (size_t)min(i0 + row, g.M - 1) * g.lda;
+  }
+#pragma unroll
+  for (int h = 0; h < Cf::B_RUNS; ++h) {
+    const int row = (Cf::B_RUNS * wid + h) * 16 + (lane >> 2);
+    L.kb[h] = 8 * ((lane & 3) ^ gd_swz(row));
+    L.pb[h] = Bm + (size_t)min(j0 + row, g.N - 1) * g.ldb;
+  }
+
+  floatx16_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+  // K step t: wait for its own loads (those of step t+1 stay in flight), barrier (every
+  // wave's loads of step t have landed and every wave is done reading step t-1), load
+  // step t+2 into step t-1's stage, multiply step t.  Every step issues its loads, past
+  // the last K step too (they reload the last one, unused), so that each wait is the
+  // same on every path; the rotation is unrolled by three with no exit inside the loop
+  // body, so that the loop head is reached with one order of pending loads.
+  constexpr int W = Cf::LOADS;
+  const int nk = g.K / GD_K, kmax = (nk - 1) * GD_K;
+  gd_issue<WM, WN>(L, 0, sa0, sb0, wid);
+  gd_issue<WM, WN>(L, min(GD_K, kmax), sa1, sb1, wid);
+  int t = 0;
+  for (; t + 3 <= nk; t += 3) {
+    gd_wait_barrier<W>();
+    gd_issue<WM, WN>(L, min((t + 2) * GD_K, kmax), sa2, sb2, wid);
+    gd_compute(sa0, sb0, wm, wn, lane, acc);
+    gd_wait_barrier<W>();
+    gd_issue<WM, WN>(L, min((t + 3) * GD_K, kmax), sa0, sb0, wid);
+    gd_compute(sa1, sb1, wm, wn, lane, acc);
+    gd_wait_barrier<W>();
+    gd_issue<WM, WN>(L, min((t + 4) * GD_K, kmax), sa1, sb1, wid);
+    gd_compute(sa2, sb2, wm, wn, lane, acc);
+  }
+  if (t < nk) {   // one or two K steps left: stages 0 and 1
+    gd_wait_barrier<W>();
+    gd_compute(sa0, sb0, wm, wn, lane, acc);
+    if (t + 1 < nk) {
+      gd_wait_barrier<0>();
+      gd_compute(sa1, sb1, wm, wn, lane, acc);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // no load into LDS outlives the block
+
+  const float* bias = reinterpret_cast<const float*>(g.bias);
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+      const int j = j0 + wn * 64 + ni * 32 + (lane & 31);
+      if (j >= g.N) continue;
+      const float bj = (bias && !g.bias_on_i) ? bias[j] : 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = i0 + wm * 64 + mi * 32 + 8 * q + 4 * (lane >> 5) + e;
+          if (i < g.M) {
+            const float bi = (bias && g.bias_on_i) ? bias[i] : 0.f;
+            __builtin_nontemporal_store(acc[mi][ni][4 * q + e] + bi + bj, &C[(size_t)i * g.ldc + j]);
+          }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------
 // fp32 MFMA GEMM (v_mfma_f32_16x16x4f32, fp32 products and sums).  Block tile 64 x 64, K
 // step 32, 4 waves in 2 x 2, each 32 x 32 = 2 x 2 MFMA tiles.  In MFMA step kk the lane
 // group q = lane / 16 contributes k = 8q + kk for both operands, so a lane's operands of
@@ -276,6 +449,20 @@ hipError_t launch_gemm(int in_dtype, int out_dtype, const GemmArgs& g, hipStream
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
   if (in_dtype == PNR_BF16 && out_dtype == PNR_F32 && (g.K % 8) == 0 && (g.lda % 8) == 0 &&
       (g.ldb % 8) == 0 && (g.sA % 8) == 0 && (g.sB % 8) == 0) {
+    const bool aligned = ((uintptr_t)g.A % 16) == 0 && ((uintptr_t)g.Bm % 16) == 0;
+    if ((g.K % GD_K) == 0 && aligned) {
+      if (g.M >= 1024 && g.N >= 1024) {   // 256 x 256 tiles once both sides fill several
+        dim3 grid((g.N + 255) / 256, (g.M + 255) / 256, g.batch);
+        hipLaunchKernelGGL((gemm_bf16_dma<4, 4>), grid, dim3(GdCfg<4, 4>::THREADS), 0, st, g);
+      } else if (g.M >= 1024) {
+        dim3 grid((g.N + 127) / 128, (g.M + 255) / 256, g.batch);
+        hipLaunchKernelGGL((gemm_bf16_dma<4, 2>), grid, dim3(GdCfg<4, 2>::THREADS), 0, st, g);
+      } else {
+        dim3 grid((g.N + 127) / 128, (g.M + 127) / 128, g.batch);
+        hipLaunchKernelGGL((gemm_bf16_dma<2, 2>), grid, dim3(GdCfg<2, 2>::THREADS), 0, st, g);
+      }
+      return hipGetLastError();
+    }
     dim3 grid((g.N + GB_N - 1) / GB_N, (g.M + GB_M - 1) / GB_M, g.batch);
     hipLaunchKernelGGL(gemm_bf16_mfma, grid, dim3(256), 0, st, g);
     return hipGetLastError();

@@ -68,17 +68,19 @@ def test_gradients_match_the_oracle(cell, D, Din, T):
     _check(got, ref)
 
 
-@pytest.mark.parametrize("cell", [WL.CELL_GRU_DIAG, WL.CELL_LSTM_DIAG])
-def test_bf16_inputs_zero_h0_and_no_recurrent_bias(cell):
+@pytest.mark.parametrize("cell,B,T,D,Din", [(WL.CELL_GRU_DIAG, 3, 1500, 5, 8), (WL.CELL_LSTM_DIAG, 3, 1500, 5, 8),
+                                            (WL.CELL_LSTM_DIAG, 2, 1024, 8, 64), (WL.CELL_GRU_DIAG, 1, 4096, 32, 96)])
+def test_bf16_inputs_zero_h0_and_no_recurrent_bias(cell, B, T, D, Din):
     """With bf16 inputs the two gradient products run in bf16 like the forward projection:
     the pre-activation gradients are rounded to bf16 (relative error <= 2^-9 each, x and W
     are bf16 already) and summed in fp32.  So each entry of dW and dx is within
     2^-9 * sum |dgx| |x| (resp. |dgx| |W|) of the exact value; the bar doubles that for the
-    fp32 sums.  The other gradients do not pass through those products."""
-    p, H32, g, ref = _case(cell, 3, 1500, 5, 8, xd=WL.DT_BF16, seed=4, h0=False, bh=False)
+    fp32 sums.  The other gradients do not pass through those products.  The last two
+    cases have every GEMM dimension K (D_in, B*T, G*D) a multiple of 32, so the projection
+    and both gradient products take the direct-to-LDS GEMM kernel."""
+    p, H32, g, ref = _case(cell, B, T, D, Din, xd=WL.DT_BF16, seed=4, h0=False, bh=False)
     got = _run(cell, p, H32, g)
     _check(got, ref, names=("U", "b_x", "b_h", "h0"))
-    B, T = 3, 1500
     dgx = np.abs(ref["dgx"].reshape(B * T, -1))
     xa = np.abs(WL.as_f64(p["x"]).reshape(B * T, -1))
     Wa = np.abs(WL.as_f64(p["W"]))

@@ -306,11 +306,18 @@ def test_fused_projection_with_wide_and_ragged_inputs(D_in, resident, monkeypatc
 
 
 @pytest.mark.parametrize("cell,D,D_in", [(WL.CELL_GRU_DIAG, 100, 72), (WL.CELL_LSTM_DIAG, 70, 40),
-                                         (WL.CELL_GRU_DIAG, 128, 256)])
+                                         (WL.CELL_GRU_DIAG, 128, 256), (WL.CELL_GRU_DIAG, 100, 32),
+                                         (WL.CELL_LSTM_DIAG, 70, 96), (WL.CELL_GRU_DIAG, 45, 128),
+                                         (WL.CELL_LSTM_DIAG, 33, 160), (WL.CELL_LSTM_DIAG, 300, 64),
+                                         (WL.CELL_GRU_DIAG, 350, 96)])
 def test_bf16_projection_over_several_column_tiles(cell, D, D_in):
-    """bf16 inputs with K a multiple of 8 take the MFMA GEMM for the projection: gate widths
-    (3D or 4D) spanning two or more 128/256-column tiles with a ragged last one, and rows
-    (B*T) spanning several 128-row tiles with a ragged tail."""
+    """bf16 inputs with K a multiple of 8 take an MFMA GEMM for the projection: gate widths
+    (3D or 4D) spanning two or more 128-row tiles with a ragged last one, and steps
+    spanning several 128-column tiles with a ragged tail, for three batch elements.  K a
+    multiple of 32 takes the kernel with direct-to-LDS loads and a three-stage ring: 1, 3,
+    4, 5 and 8 K steps cover a tail of one or two steps after the unrolled loop, no tail,
+    and no loop at all, and gate widths of 1050 and 1200 rows take its 256-row tiles; the
+    other K take the register-staged kernel."""
     B, T = 3, 2 * 128 + 77
     p = WL.random_problem(cell, B, T, D, D_in, seed=D + D_in, x_dtype=WL.DT_BF16, state_dtype=WL.DT_F32,
                           bias_std=0.2, h0_std=0.3, w_std=1.0 / math.sqrt(D_in))
@@ -321,6 +328,21 @@ def test_bf16_projection_over_several_column_tiles(cell, D, D_in):
                              solver="loop")
         np.testing.assert_allclose(_np(got["h"]), ref["states"], rtol=0, atol=1e-4)
         np.testing.assert_allclose(got["history"], ref["rhos"], rtol=1e-3, atol=1e-5)
+
+
+@pytest.mark.parametrize("cell,D,D_in,B,T", [(WL.CELL_LSTM_DIAG, 300, 64, 1, 1100),
+                                              (WL.CELL_GRU_DIAG, 512, 32, 2, 1030)])
+def test_bf16_projection_with_large_tiles(cell, D, D_in, B, T):
+    """Gate widths (1200, 1536 rows) and step counts (1100, 1030 columns) both past 1024
+    take the direct-to-LDS GEMM's 256 x 256 tiles, ragged on both sides."""
+    p = WL.random_problem(cell, B, T, D, D_in, seed=D + T, x_dtype=WL.DT_BF16, state_dtype=WL.DT_F32,
+                          bias_std=0.2, h0_std=0.3, w_std=1.0 / math.sqrt(D_in))
+    q = _f64(p)
+    got = _run(cell, p, 2, -1.0, WL.JAC_FULL)
+    ref = O.newton_dense(cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], 2, -1.0, WL.JAC_FULL, 1,
+                         solver="loop")
+    np.testing.assert_allclose(_np(got["h"]), ref["states"], rtol=0, atol=1e-4)
+    np.testing.assert_allclose(got["history"], ref["rhos"], rtol=1e-3, atol=1e-5)
 
 
 def test_cooperative_launch_mode_gives_the_same_result():
