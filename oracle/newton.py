@@ -21,6 +21,14 @@ Options:
 * jac_every: the Jacobian is recomputed only when k % jac_every == 0 and reused
   otherwise (ParaRNN overview, "Newton's Iteration": recomputing the Jacobian only
   every few steps).  The residual is always fresh.
+* refresh_ratio = theta >= 0 (adaptive refresh, one of the approximate-Newton variants
+  the ParaRNN overview names beside the fixed schedule, "Newton's Iteration"; no rule is
+  given there): the Jacobian is also recomputed at iteration k >= 2 when the update
+  before last contracted the residual by less than theta, rho_{k-1} > theta rho_{k-2};
+  jac_every is then the largest age (k - last refresh) a Jacobian may reach.  The rule
+  looks one update back because a fused pass must take its Jacobian before it learns
+  its own residual.  theta = inf gives the fixed schedule, theta = 0 refreshes at every
+  k >= 2.
 
 Readings where the pages are silent: initial guess H = 0; stop when the max-abs
 residual (NaN counted as +inf) is <= tol, testing *before* each update so the
@@ -58,8 +66,9 @@ def _previous_states(h0, H):
 
 def newton_dense(cell: int, W, U, b_x, b_h, x, h0, max_iters: int, tol: float,
                  jac_mode: int, jac_every: int = 1, gx=None, solver: str = "dense",
-                 damping: float = 0.0):
-    """Returns dict(states [B,T,S], iters, status, rhos[list], jac_evals).
+                 damping: float = 0.0, refresh_ratio=None):
+    """Returns dict(states [B,T,S], iters, status, rhos[list], jac_evals, refreshes[list
+    of the iterations that recomputed the Jacobian]).
 
     solver="dense" assembles the block-bidiagonal matrix and calls LAPACK (only for
     T*S up to a few thousand); solver="loop" solves the same system by forward
@@ -71,6 +80,8 @@ def newton_dense(cell: int, W, U, b_x, b_h, x, h0, max_iters: int, tol: float,
     """
     if jac_every < 1:
         raise ValueError("jac_every must be >= 1")
+    if refresh_ratio is not None and not refresh_ratio >= 0:
+        raise ValueError("refresh_ratio must be >= 0 (or None)")
     U = np.asarray(U, dtype=np.float64)
     b_h = None if b_h is None else np.asarray(b_h, dtype=np.float64)
     h0 = np.asarray(h0, dtype=np.float64)
@@ -82,6 +93,7 @@ def newton_dense(cell: int, W, U, b_x, b_h, x, h0, max_iters: int, tol: float,
     rhos = []
     Jhat = None
     jac_evals = 0
+    refreshes = []
     k = 0
     while True:
         P = _previous_states(h0, H)
@@ -90,13 +102,18 @@ def newton_dense(cell: int, W, U, b_x, b_h, x, h0, max_iters: int, tol: float,
         rho = max_abs(r)
         rhos.append(rho)
         if not np.isfinite(rho):
-            return dict(states=H, iters=k, status=STATUS_NONFINITE, rhos=rhos, jac_evals=jac_evals)
+            return dict(states=H, iters=k, status=STATUS_NONFINITE, rhos=rhos, jac_evals=jac_evals,
+                        refreshes=refreshes)
         if rho <= tol:
-            return dict(states=H, iters=k, status=STATUS_OK, rhos=rhos, jac_evals=jac_evals)
+            return dict(states=H, iters=k, status=STATUS_OK, rhos=rhos, jac_evals=jac_evals,
+                        refreshes=refreshes)
         if k == max_iters:
             return dict(states=H, iters=k, status=STATUS_NOT_CONVERGED, rhos=rhos,
-                        jac_evals=jac_evals)
-        if k % jac_every == 0:
+                        jac_evals=jac_evals, refreshes=refreshes)
+        aged = not refreshes or k - refreshes[-1] >= jac_every
+        slow = refresh_ratio is not None and k >= 2 and rhos[k - 1] > refresh_ratio * rhos[k - 2]
+        if aged or slow:
+            refreshes.append(k)
             J = cell_jacobian(cell, U, b_h, P.reshape(B * T, S), gx.reshape(B * T, GD))
             Jhat = approx_jacobian(J, jac_mode).reshape(B, T, S, S)
             jac_evals += 1

@@ -284,3 +284,65 @@ def test_loop_solver_matches_dense_solver(cell):
                            solver="loop")
         np.testing.assert_allclose(b["states"], a["states"], rtol=0, atol=1e-13)
         np.testing.assert_allclose(b["rhos"], a["rhos"], rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------------
+# Adaptive Jacobian refresh (refresh_ratio): pinned by its two limits, which reduce to
+# schedules pinned above, by a step-by-step construction from the cell, its Jacobian and
+# the scan loop, and by convergence to the sequential trajectory.
+@pytest.mark.parametrize("cell", CELLS)
+def test_adaptive_refresh_limits(cell):
+    p = _problem(cell, T=11)
+    args = (cell, p["W"], p["U"], p["b_x"], p["b_h"], p["x"], p["h0"])
+    fixed = O.newton_dense(*args, 6, -1.0, O.JAC_FULL, 3, solver="loop")
+    never = O.newton_dense(*args, 6, -1.0, O.JAC_FULL, 3, solver="loop", refresh_ratio=float("inf"))
+    np.testing.assert_array_equal(never["states"], fixed["states"])
+    assert never["refreshes"] == fixed["refreshes"] == [0, 3]
+    # theta = 0: every iteration from k = 2 on refreshes (each residual is positive), and
+    # with jac_every = 1 nothing changes from plain Newton
+    always = O.newton_dense(*args, 6, -1.0, O.JAC_FULL, 50, solver="loop", refresh_ratio=0.0)
+    assert always["refreshes"] == [0, 2, 3, 4, 5]
+    newton = O.newton_dense(*args, 6, -1.0, O.JAC_FULL, 1, solver="loop")
+    same = O.newton_dense(*args, 6, -1.0, O.JAC_FULL, 1, solver="loop", refresh_ratio=0.7)
+    np.testing.assert_array_equal(same["states"], newton["states"])
+    with pytest.raises(ValueError):
+        O.newton_dense(*args, 2, -1.0, O.JAC_FULL, 2, refresh_ratio=-0.5)
+
+
+@pytest.mark.parametrize("cell", [O.CELL_GRU_DIAG, O.CELL_LSTM_DIAG])
+def test_adaptive_refresh_step_by_step(cell):
+    """Four updates built by hand from cell_step, cell_jacobian and scan_loop, refreshing
+    the Jacobian at k = 0 and wherever the update before last shrank the residual by less
+    than theta (jac_every large enough never to force one)."""
+    p = _problem(cell, B=1, T=9, u_scale=1.5)
+    S = p["h0"].shape[1]
+    gx = O.project(p["W"], p["x"], p["b_x"])[0]
+    h0 = p["h0"][0]
+    H = np.zeros((9, S))
+    rhos, J, refreshed = [], None, []
+    # theta between the first two contraction ratios, so that exactly one of them refreshes
+    probe = O.newton_dense(cell, p["W"], p["U"], p["b_x"], p["b_h"], p["x"], p["h0"], 4, -1.0, O.JAC_FULL, 100,
+                           solver="loop", refresh_ratio=float("inf"))
+    q = [probe["rhos"][i + 1] / probe["rhos"][i] for i in range(2)]
+    theta = 0.5 * (q[0] + q[1])
+    for k in range(4):
+        P = np.concatenate([h0[None], H[:-1]], 0)
+        F = O.cell_step(cell, p["U"], p["b_h"], P, gx)
+        rhos.append(np.abs(F - H).max())
+        if k == 0 or (k >= 2 and rhos[k - 1] > theta * rhos[k - 2]):
+            J = O.cell_jacobian(cell, p["U"], p["b_h"], P, gx)
+            refreshed.append(k)
+        H = H + O.scan_loop(J, F - H)
+    got = O.newton_dense(cell, p["W"], p["U"], p["b_x"], p["b_h"], p["x"], p["h0"], 4, -1.0, O.JAC_FULL, 100,
+                         solver="loop", refresh_ratio=theta)
+    assert got["refreshes"] == refreshed and len(refreshed) == 2
+    np.testing.assert_allclose(got["states"][0], H, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("cell", CELLS)
+def test_adaptive_refresh_converges_to_the_sequential_states(cell):
+    p = _problem(cell, T=14)
+    res = O.newton_dense(cell, p["W"], p["U"], p["b_x"], p["b_h"], p["x"], p["h0"], 64, 1e-12, O.JAC_FULL, 4,
+                         solver="loop", refresh_ratio=0.5)
+    assert res["status"] == O.STATUS_OK
+    np.testing.assert_allclose(res["states"], _seq(cell, p), rtol=0, atol=1e-11)
