@@ -30,7 +30,7 @@ MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0, "f64": 78.6}   # dense, publis
 PRIMARY = "gru_quasi"
 DEFAULT_OTHERS = ("tiny_gru,gru_full,gru_diag_long,lstm_diag_long,lstm_diag_long_chunked,lstm_diag_long_stiff,"
                   "gru_diag_long_elk,gru_quasi_elk,gru_quasi_bwd,gru_diag_long_bwd,lstm_diag_long_bwd,"
-                  "lstm_diag_long_chunked_bwd")
+                  "lstm_diag_long_chunked_bwd,lstm_diag_long_adaptive")
 CSRC = "nonlinear_rnn_evaluation_amd/csrc/"
 
 
@@ -112,13 +112,27 @@ def chunk_iterations(history, w, n_chunks):
     return out
 
 
-def iteration_bytes(w, k, iters_total, resid=False):
+def refresh_points(w, rhos, passes):
+    """Iterations (< passes) that took a new Jacobian: the fixed schedule k % jac_every,
+    or for the adaptive refresh the same rule the device applies, replayed on the residual
+    history the call returned (the device decided on exactly these values)."""
+    out = []
+    for k in range(passes):
+        aged = not out or k - out[-1] >= w.jac_every
+        slow = w.refresh_ratio is not None and k >= 2 and rhos[k - 1] > w.refresh_ratio * rhos[k - 2]
+        if aged or slow:
+            out.append(k)
+    return out
+
+
+def iteration_bytes(w, k, iters_total, resid=False, refreshes=None):
     """Algorithmic HBM bytes of one fused iteration kernel launch that did work.
 
     Per element the kernel must read the gate pre-activations and the current iterate
     (not at k=0: the zero guess is never stored), write the next iterate, and -- when
     the Jacobian is reused -- read the state it was taken at (unless that is the zero
-    guess).  The residual-only pass reads and does not write.
+    guess).  The residual-only pass reads and does not write.  `refreshes`: the
+    iterations that took a new Jacobian (default: the fixed schedule).
     """
     from nonlinear_rnn_evaluation_amd import workloads as WL
     es = 8 if w.state_dtype == WL.DT_F64 else 4
@@ -129,7 +143,7 @@ def iteration_bytes(w, k, iters_total, resid=False):
     cur = h if k > 0 else 0
     if resid:
         return gx + cur
-    jk = k - (k % w.jac_every)
+    jk = k - (k % w.jac_every) if refreshes is None else max(r for r in refreshes if r <= k)
     jac = h if (jk != k and jk > 0) else 0
     return gx + cur + h + jac
 
@@ -183,7 +197,8 @@ def run_workload(name, steps, warmup, mode=None, with_cpu=True, cpu_budget=12.0,
     def call(ws=None, out=None):
         return pnr.evaluate(w.cell, d["W"], d["U"], d["x"], b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"],
                             max_iters=w.max_iters, tol=w.tol, jac_mode=mode, jac_every=w.jac_every,
-                            workspace=ws, h_out=out, damping=w.damping, chunk_len=w.chunk_len)
+                            workspace=ws, h_out=out, damping=w.damping, chunk_len=w.chunk_len,
+                            refresh_ratio=w.refresh_ratio)
 
     first = call()
     ws, out = first["workspace"], first["h"]
@@ -229,7 +244,9 @@ def run_workload(name, steps, warmup, mode=None, with_cpu=True, cpu_budget=12.0,
         fn = dense_damped_iteration_bytes if w.cell == WL.CELL_GRU else damped_iteration_bytes
         bytes_call = sum(fn(w, k, resid=(resid_last and k == passes - 1)) for k in range(passes))
     else:
-        bytes_call = sum(iteration_bytes(w, k, iters, resid=(resid_last and k == passes - 1)) for k in range(passes))
+        refr = refresh_points(w, last["history"], passes)
+        bytes_call = sum(iteration_bytes(w, k, iters, resid=(resid_last and k == passes - 1), refreshes=refr)
+                         for k in range(passes))
     fused = projection_fused(w, mode)
     if fused:
         # the loop kernel also computes the projection: read x, write gx

@@ -132,6 +132,24 @@ size_t pnr_workspace_bytes(const pnr_cell* cell, int jac_mode);
 int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0,
              void* h_out, int max_iters, double tol, int jac_mode);
 
+/*
+ * pnr_eval with an adaptive Jacobian refresh, for the diagonal-recurrence cells
+ * (PNR_CELL_GRU_DIAG, PNR_CELL_LSTM_DIAG).  The ParaRNN overview ("Newton's Iteration")
+ * names Jacobian reuse schedules other than a fixed period among the approximate-Newton
+ * variants, without giving one; this is the plainest: iteration k takes a new Jacobian
+ * (at its current iterate) when
+ *     k == 0,  or  k - (last refresh) >= cell->jac_every,
+ *     or  k >= 2 and rho_{k-1} > refresh_ratio * rho_{k-2},
+ * i.e. also when the update before last shrank the max-norm residual by less than the
+ * ratio.  The rule looks one update back because the fused pass that evaluates the
+ * residual rho_k also takes the Jacobian, before rho_k is known.  refresh_ratio = +inf
+ * is pnr_eval's fixed schedule; refresh_ratio = 0 refreshes at every k >= 2.  Arguments,
+ * workspace (pnr_workspace_bytes) and results as pnr_eval.  refresh_ratio must be >= 0
+ * (PNR_E_INVALID otherwise, NaN included); the dense-U GRU returns PNR_E_UNSUPPORTED.
+ */
+int pnr_eval_adaptive(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0,
+                      void* h_out, int max_iters, double tol, int jac_mode, double refresh_ratio);
+
 /* Newton updates applied by the calling thread's last pnr_eval (-1 if it failed before). */
 int pnr_iters_used(void);
 

@@ -263,8 +263,9 @@ int pnr_last_residual_history(double* out, int max_n) {
   return n;
 }
 
-int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, void* h_out,
-             int max_iters, double tol, int jac_mode) {
+namespace {
+int eval_impl(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, void* h_out,
+              int max_iters, double tol, int jac_mode, double refresh_ratio) {
   g_last = LastCall();
   g_prof.valid = false;
   g_prof.used = 0;
@@ -343,6 +344,7 @@ int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, cons
     a.n_rows = B * D;
     a.max_iters = max_iters; a.jac_every = cell->jac_every; a.jac_mode = jac_mode;
     a.tol = tol;
+    a.refresh_ratio = refresh_ratio;
     const int cap = diag_grid_capacity(kind, num_cu);
     // A block walks whole rows (no look-back) when there are enough rows to fill the
     // grid; otherwise rows are cut into tiles linked by the decoupled look-back.
@@ -428,6 +430,22 @@ int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, cons
   mark_end(m_first, st);
 
   return finish_call(l, ws, max_iters, st, m_first, m_proj, m_newton, m_out);
+}
+}  // namespace
+
+int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, void* h_out,
+             int max_iters, double tol, int jac_mode) {
+  return eval_impl(cell, params, x, h0, h_out, max_iters, tol, jac_mode, -1.0);
+}
+
+int pnr_eval_adaptive(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, void* h_out,
+                      int max_iters, double tol, int jac_mode, double refresh_ratio) {
+  g_last = LastCall();
+  g_prof.valid = false;
+  if (!(refresh_ratio >= 0.0)) return fail(PNR_E_INVALID, "refresh_ratio must be >= 0 (got %g)", refresh_ratio);
+  if (cell && cell->kind == PNR_CELL_GRU)
+    return fail(PNR_E_UNSUPPORTED, "the adaptive Jacobian refresh is implemented for the diagonal-recurrence cells");
+  return eval_impl(cell, params, x, h0, h_out, max_iters, tol, jac_mode, refresh_ratio);
 }
 
 // ---- damped (quasi-ELK) evaluation ----

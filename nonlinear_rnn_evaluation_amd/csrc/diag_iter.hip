@@ -501,10 +501,19 @@ __global__ void __launch_bounds__(PNR_BLOCK, diag_min_waves<CELL>()) diag_newton
   Ctrl* ctrl = a.ctrl;
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int n_items = a.walk ? a.n_rows : a.n_tiles;
-  int cur = -1, jac = -1;
+  int cur = -1, jac = -1, k_jac = 0;
   for (int k = 0; k <= a.max_iters; ++k) {
     const bool resid_only = k == a.max_iters;
-    if (!resid_only && k % a.jac_every == 0) jac = cur;
+    // a new Jacobian at k = 0, when the current one reaches jac_every updates of age, and
+    // (adaptive refresh) when the finisher of pass k-1 found that update k-2 contracted
+    // the residual too little; every block takes the same decision
+    bool refresh = k == 0 || k - k_jac >= a.jac_every;
+    if (!refresh && a.refresh_ratio >= 0.0 && k >= 2)
+      refresh = __hip_atomic_load(&ctrl->refresh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+    if (!resid_only && refresh) {
+      jac = cur;
+      k_jac = k;
+    }
     const int next = resid_only ? cur : pick_next(cur, jac, a.nbuf);
     IterView v;
     v.Hcur = cur >= 0 ? a.H[cur] : nullptr;
@@ -554,7 +563,7 @@ __global__ void __launch_bounds__(PNR_BLOCK, diag_min_waves<CELL>()) diag_newton
       __syncthreads();
       if (tid == 0) {
         for (int w = 0; w < PNR_WAVES; ++w) m = max(m, s_wmax[w]);
-        finish_iteration(ctrl, a.rho_hist, bits_to_rho(m), k, cur, a.max_iters, a.tol);
+        finish_iteration(ctrl, a.rho_hist, bits_to_rho(m), k, cur, a.max_iters, a.tol, a.refresh_ratio);
       }
     });
     if (__hip_atomic_load(&ctrl->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) || has_fault(ctrl)) break;

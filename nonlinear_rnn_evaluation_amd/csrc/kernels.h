@@ -27,9 +27,17 @@ hipError_t launch_persistent(const void* fn, int grid, size_t lds, void** args, 
 // Every field of the control block is written with agent-scope (coherent) stores: the
 // merging block differs from pass to pass and may sit on another XCD, and plain stores
 // of one address from several XCDs' L2 caches reach memory in no defined order.
+// refresh_ratio >= 0: also decide the adaptive Jacobian refresh of the next pass, which
+// takes a new Jacobian when this update contracted the residual by less than the ratio
+// (rho_k > ratio * rho_{k-1}, k >= 1; c->rho still holds rho_{k-1} here).
 __device__ inline void finish_iteration(Ctrl* c, double* hist, double rho, int k, int cur_buf,
-                                        int max_iters, double tol) {
+                                        int max_iters, double tol, double refresh_ratio = -1.0) {
   hist[k] = rho;
+  if (refresh_ratio >= 0.0) {
+    const double prev = __hip_atomic_load(&c->rho, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&c->refresh, (k >= 1 && rho > refresh_ratio * prev) ? 1 : 0, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
   __hip_atomic_store(&c->rho, rho, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   int done = 0, status = PNR_NOT_CONVERGED;
   if (!(rho < __builtin_inf())) {
@@ -67,6 +75,7 @@ struct DiagLoopArgs {
   int walk;            // 1: one block walks a whole row with a carry; 0: tiles + look-back
   int max_iters, jac_every, jac_mode;
   double tol;
+  double refresh_ratio;   // >= 0: adaptive Jacobian refresh (jac_every = largest age); < 0: fixed schedule
 };
 
 // Damped (quasi-ELK) Newton loop for GRU_DIAG and LSTM_DIAG (G gates, S = D or 2D state

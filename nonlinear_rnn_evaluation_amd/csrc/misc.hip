@@ -55,6 +55,7 @@ __global__ void init_kernel(Ctrl* ctrl, uint64_t* slots, size_t n, uint64_t* par
     ctrl->bar_top = 0;
     ctrl->bar_gen = 0;
     ctrl->fault = 0;
+    ctrl->refresh = 0;
     for (int g = 0; g < kBarGroups; ++g) ctrl->bar_group[g].count = 0;
     ctrl->dec = 0;
   }

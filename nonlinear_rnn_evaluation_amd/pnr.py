@@ -77,6 +77,9 @@ def load() -> ctypes.CDLL:
     lib.pnr_workspace_bytes_backward.restype = ctypes.c_size_t
     lib.pnr_backward.argtypes = [P(PnrCell), P(PnrParams)] + [ctypes.c_void_p] * 10
     lib.pnr_backward.restype = ctypes.c_int
+    lib.pnr_eval_adaptive.argtypes = [P(PnrCell), P(PnrParams), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_double]
+    lib.pnr_eval_adaptive.restype = ctypes.c_int
     lib.pnr_workspace_bytes_backward_chunked.argtypes = [P(PnrCell), ctypes.c_int]
     lib.pnr_workspace_bytes_backward_chunked.restype = ctypes.c_size_t
     lib.pnr_backward_chunked.argtypes = [P(PnrCell), P(PnrParams)] + [ctypes.c_void_p] * 10 + [ctypes.c_int]
@@ -154,6 +157,12 @@ def pnr_workspace_bytes(cell: PnrCell, jac_mode: int) -> int:
 def pnr_eval(cell: PnrCell, params: PnrParams, x: int, h0: Optional[int], h_out: int, max_iters: int,
              tol: float, jac_mode: int) -> int:
     return load().pnr_eval(ctypes.byref(cell), ctypes.byref(params), x, h0, h_out, max_iters, tol, jac_mode)
+
+
+def pnr_eval_adaptive(cell: PnrCell, params: PnrParams, x: int, h0: Optional[int], h_out: int, max_iters: int,
+                      tol: float, jac_mode: int, refresh_ratio: float) -> int:
+    return load().pnr_eval_adaptive(ctypes.byref(cell), ctypes.byref(params), x, h0, h_out, max_iters, tol,
+                                    jac_mode, refresh_ratio)
 
 
 def pnr_workspace_bytes_damped(cell: PnrCell, jac_mode: int) -> int:
@@ -248,10 +257,12 @@ def evaluate(kind: int, W: torch.Tensor, U: torch.Tensor, x: torch.Tensor, *, b_
              h0=None, max_iters: int = 64, tol: float = 1e-5, jac_mode: int = JAC_FULL,
              jac_every: int = 1, h_out: Optional[torch.Tensor] = None,
              workspace: Optional[torch.Tensor] = None, damping: Optional[float] = None,
-             chunk_len: Optional[int] = None) -> dict:
-    """Run pnr_eval (or pnr_eval_damped when `damping` is given, or pnr_eval_chunked when
-    `chunk_len` is given) on device tensors; returns dict(h=[B,T,S], status, iters,
-    residual, history)."""
+             chunk_len: Optional[int] = None, refresh_ratio: Optional[float] = None) -> dict:
+    """Run pnr_eval (or pnr_eval_damped when `damping` is given, pnr_eval_chunked when
+    `chunk_len` is given, pnr_eval_adaptive when `refresh_ratio` is given) on device
+    tensors; returns dict(h=[B,T,S], status, iters, residual, history)."""
+    if refresh_ratio is not None and (damping is not None or chunk_len is not None):
+        raise ValueError("refresh_ratio combines with neither damping nor chunk_len")
     B, T, D_in = x.shape
     D = U.shape[1]
     S = 2 * D if kind == CELL_LSTM_DIAG else D
@@ -287,6 +298,8 @@ def evaluate(kind: int, W: torch.Tensor, U: torch.Tensor, x: torch.Tensor, *, b_
     if chunk_len is not None:
         rc = pnr_eval_chunked(cell, params, ptrs["x"], ptrs["h0"], out, max_iters, tol, jac_mode,
                               damping or 0.0, chunk_len)
+    elif refresh_ratio is not None:
+        rc = pnr_eval_adaptive(cell, params, ptrs["x"], ptrs["h0"], out, max_iters, tol, jac_mode, refresh_ratio)
     elif damping is None:
         rc = pnr_eval(cell, params, ptrs["x"], ptrs["h0"], out, max_iters, tol, jac_mode)
     else:

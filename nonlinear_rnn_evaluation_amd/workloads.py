@@ -81,6 +81,7 @@ class Workload:
     damping: Optional[float] = None   # set: the damped (quasi-ELK) step with this strength
     chunk_len: Optional[int] = None   # set: evaluated in chunks of this many steps
     backward: bool = False            # the measured step is the backward pass at the evaluated states
+    refresh_ratio: Optional[float] = None   # set: adaptive Jacobian refresh with this ratio
 
     @property
     def G(self) -> int:
@@ -101,6 +102,7 @@ class Workload:
             **({"damping": self.damping} if self.damping is not None else {}),
             **({"chunk_len": self.chunk_len} if self.chunk_len is not None else {}),
             **({"pass": "backward"} if self.backward else {}),
+            **({"refresh_ratio": self.refresh_ratio} if self.refresh_ratio is not None else {}),
         }
 
 
@@ -143,6 +145,10 @@ def named_workloads() -> dict:
     # checkpointing: the workspace covers one chunk)
     w["lstm_diag_long_chunked_bwd"] = dataclasses.replace(w["lstm_diag_long_chunked"],
                                                           name="lstm_diag_long_chunked_bwd", backward=True)
+    # the long LSTM with the adaptive Jacobian refresh: a new Jacobian when the update
+    # before last shrank the residual by less than 0.3, at most every 4 updates
+    w["lstm_diag_long_adaptive"] = dataclasses.replace(w["lstm_diag_long"], name="lstm_diag_long_adaptive",
+                                                       jac_every=4, refresh_ratio=0.3)
     # the stiff LSTM with the damped step on the diagonal Jacobian (quasi-ELK), which
     # converges where both undamped variants do not
     w["lstm_diag_long_stiff_elk"] = dataclasses.replace(

@@ -179,6 +179,19 @@ def test_backward_requests_are_validated_without_a_gpu():
     assert pnr.pnr_workspace_bytes_backward(_cell(jac_every=3)) == pnr.pnr_workspace_bytes_backward(_cell())
 
 
+def test_adaptive_requests_are_validated_without_a_gpu():
+    params = pnr.PnrParams(1024, 2048, None, None)
+    c = _cell(jac_every=3)
+    for bad in (-0.5, float("nan")):
+        assert pnr.pnr_eval_adaptive(c, params, 4096, None, 8192, 10, 1e-5, pnr.JAC_FULL, bad) == pnr.E_INVALID
+    assert pnr.pnr_eval_adaptive(_cell(kind=pnr.CELL_GRU), params, 4096, None, 8192, 10, 1e-5, pnr.JAC_DIAG,
+                                 0.5) == pnr.E_UNSUPPORTED
+    assert pnr.pnr_eval_adaptive(_cell(kind=7), params, 4096, None, 8192, 10, 1e-5, pnr.JAC_FULL,
+                                 0.5) == pnr.E_INVALID
+    # no workspace: rejected before any HIP call, as pnr_eval does
+    assert pnr.pnr_eval_adaptive(c, params, 4096, None, 8192, 10, 1e-5, pnr.JAC_FULL, 0.5) == pnr.E_WORKSPACE
+
+
 def test_chunked_backward_requests_are_validated_without_a_gpu():
     params = pnr.PnrParams(1024, 2048, None, None)
     for kind in (pnr.CELL_GRU_DIAG, pnr.CELL_LSTM_DIAG, pnr.CELL_GRU):
