@@ -25,7 +25,8 @@ struct Ctrl {
   uint32_t ticket;     // dynamic tile counter (standalone scan)
   int32_t fault;       // a bounded device wait ran out (1 = look-back, 2 = barrier)
   int32_t refresh;     // adaptive Jacobian refresh: 1 if the next pass takes a new Jacobian
-  uint32_t pad0[23];
+  int32_t jac_pass;    // adaptive Jacobian refresh: the last pass that took one
+  uint32_t pad0[22];
   // Grid barrier.  Every counter sits on a 256-byte line of its own: blocks arrive on
   // one of kBarGroups group counters, the last of each group on the top counter, and
   // all blocks poll the generation word.

@@ -501,19 +501,16 @@ __global__ void __launch_bounds__(PNR_BLOCK, diag_min_waves<CELL>()) diag_newton
   Ctrl* ctrl = a.ctrl;
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int n_items = a.walk ? a.n_rows : a.n_tiles;
-  int cur = -1, jac = -1, k_jac = 0;
+  int cur = -1, jac = -1;
   for (int k = 0; k <= a.max_iters; ++k) {
     const bool resid_only = k == a.max_iters;
-    // a new Jacobian at k = 0, when the current one reaches jac_every updates of age, and
-    // (adaptive refresh) when the finisher of pass k-1 found that update k-2 contracted
-    // the residual too little; every block takes the same decision
-    bool refresh = k == 0 || k - k_jac >= a.jac_every;
-    if (!refresh && a.refresh_ratio >= 0.0 && k >= 2)
-      refresh = __hip_atomic_load(&ctrl->refresh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
-    if (!resid_only && refresh) {
-      jac = cur;
-      k_jac = k;
-    }
+    // a new Jacobian every jac_every updates, or (adaptive refresh) when the finisher of
+    // pass k-1 decided so; every block takes the same decision
+    const bool refresh = a.refresh_ratio < 0.0
+                             ? k % a.jac_every == 0
+                             : (k == 0 || __hip_atomic_load(&ctrl->refresh, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT) != 0);
+    if (!resid_only && refresh) jac = cur;
     const int next = resid_only ? cur : pick_next(cur, jac, a.nbuf);
     IterView v;
     v.Hcur = cur >= 0 ? a.H[cur] : nullptr;
@@ -563,7 +560,8 @@ __global__ void __launch_bounds__(PNR_BLOCK, diag_min_waves<CELL>()) diag_newton
       __syncthreads();
       if (tid == 0) {
         for (int w = 0; w < PNR_WAVES; ++w) m = max(m, s_wmax[w]);
-        finish_iteration(ctrl, a.rho_hist, bits_to_rho(m), k, cur, a.max_iters, a.tol, a.refresh_ratio);
+        finish_iteration(ctrl, a.rho_hist, bits_to_rho(m), k, cur, a.max_iters, a.tol, a.refresh_ratio,
+                         a.jac_every);
       }
     });
     if (__hip_atomic_load(&ctrl->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) || has_fault(ctrl)) break;

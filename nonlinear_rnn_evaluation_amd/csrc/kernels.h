@@ -27,16 +27,21 @@ hipError_t launch_persistent(const void* fn, int grid, size_t lds, void** args, 
 // Every field of the control block is written with agent-scope (coherent) stores: the
 // merging block differs from pass to pass and may sit on another XCD, and plain stores
 // of one address from several XCDs' L2 caches reach memory in no defined order.
-// refresh_ratio >= 0: also decide the adaptive Jacobian refresh of the next pass, which
-// takes a new Jacobian when this update contracted the residual by less than the ratio
-// (rho_k > ratio * rho_{k-1}, k >= 1; c->rho still holds rho_{k-1} here).
+// refresh_ratio >= 0: also decide the adaptive Jacobian refresh of pass k+1, which takes
+// a new Jacobian when the current one has jac_every updates of age or when this update
+// contracted the residual by less than the ratio (rho_k > ratio * rho_{k-1}, k >= 1;
+// c->rho still holds rho_{k-1} here).  Pass 0 always takes one; c->jac_pass records the
+// last pass that did.
 __device__ inline void finish_iteration(Ctrl* c, double* hist, double rho, int k, int cur_buf,
-                                        int max_iters, double tol, double refresh_ratio = -1.0) {
+                                        int max_iters, double tol, double refresh_ratio = -1.0,
+                                        int jac_every = 1) {
   hist[k] = rho;
   if (refresh_ratio >= 0.0) {
     const double prev = __hip_atomic_load(&c->rho, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&c->refresh, (k >= 1 && rho > refresh_ratio * prev) ? 1 : 0, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+    const int last = __hip_atomic_load(&c->jac_pass, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool next = (k + 1 - last >= jac_every) || (k >= 1 && rho > refresh_ratio * prev);
+    __hip_atomic_store(&c->refresh, next ? 1 : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (next) __hip_atomic_store(&c->jac_pass, k + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __hip_atomic_store(&c->rho, rho, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   int done = 0, status = PNR_NOT_CONVERGED;

@@ -56,6 +56,7 @@ __global__ void init_kernel(Ctrl* ctrl, uint64_t* slots, size_t n, uint64_t* par
     ctrl->bar_gen = 0;
     ctrl->fault = 0;
     ctrl->refresh = 0;
+    ctrl->jac_pass = 0;
     for (int g = 0; g < kBarGroups; ++g) ctrl->bar_group[g].count = 0;
     ctrl->dec = 0;
   }
