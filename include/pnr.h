@@ -135,9 +135,9 @@ int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, cons
 /*
  * pnr_eval with an adaptive Jacobian refresh, for the diagonal-recurrence cells
  * (PNR_CELL_GRU_DIAG, PNR_CELL_LSTM_DIAG).  The ParaRNN overview ("Newton's Iteration")
- * names Jacobian reuse schedules other than a fixed period among the approximate-Newton
- * variants, without giving one; this is the plainest: iteration k takes a new Jacobian
- * (at its current iterate) when
+ * names recomputing the Jacobian only every few steps among its approximate-Newton
+ * strategies; here the residual decides when, by a rule of this library's own: iteration
+ * k takes a new Jacobian (at its current iterate) when
  *     k == 0,  or  k - (last refresh) >= cell->jac_every,
  *     or  k >= 2 and rho_{k-1} > refresh_ratio * rho_{k-2},
  * i.e. also when the update before last shrank the max-norm residual by less than the

@@ -21,10 +21,11 @@ Options:
 * jac_every: the Jacobian is recomputed only when k % jac_every == 0 and reused
   otherwise (ParaRNN overview, "Newton's Iteration": recomputing the Jacobian only
   every few steps).  The residual is always fresh.
-* refresh_ratio = theta >= 0 (adaptive refresh, one of the approximate-Newton variants
-  the ParaRNN overview names beside the fixed schedule, "Newton's Iteration"; no rule is
-  given there): the Jacobian is also recomputed at iteration k >= 2 when the update
-  before last contracted the residual by less than theta, rho_{k-1} > theta rho_{k-2};
+* refresh_ratio = theta >= 0 (adaptive refresh: the ParaRNN overview, "Newton's
+  Iteration", names recomputing the Jacobian only every few steps; choosing when by the
+  residual is this reading's own rule, not the page's): the Jacobian is also recomputed
+  at iteration k >= 2 when the update before last contracted the residual by less than
+  theta, rho_{k-1} > theta rho_{k-2};
   jac_every is then the largest age (k - last refresh) a Jacobian may reach.  The rule
   looks one update back because a fused pass must take its Jacobian before it learns
   its own residual.  theta = inf gives the fixed schedule, theta = 0 refreshes at every
