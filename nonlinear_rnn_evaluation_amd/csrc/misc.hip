@@ -151,9 +151,59 @@ __global__ void __launch_bounds__(256) transpose_kernel(const Tin* __restrict__ 
   }
 }
 
+// The same for R and C multiples of 4 (and 4-element-aligned rows): a 64 x 64 tile, each
+// thread moving 4 consecutive elements per access, so that a wave reads and writes whole
+// 128-256 B row segments instead of 2-4 B per lane.  A 4-element group is entirely inside
+// or entirely outside the matrix, so each group needs one bounds test.
+template <typename T, int N> struct alignas(sizeof(T) * N) VecOf { T v[N]; };
+template <typename Tin, typename Tout>
+__global__ void __launch_bounds__(256) transpose4_kernel(const Tin* __restrict__ in, Tout* __restrict__ out, int R,
+                                                         int C) {
+  __shared__ float tile[64][65];
+  const size_t z = blockIdx.z;
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  const int g = threadIdx.x & 15, q = threadIdx.x >> 4;   // 16 groups of 4 along a row, 16 rows
+  const Tin* src = in + z * (size_t)R * C;
+  Tout* dst = out + z * (size_t)R * C;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rr = q + 16 * i, r = r0 + rr, c = c0 + 4 * g;
+    VecOf<Tin, 4> v;
+    if (r < R && c < C) v = *reinterpret_cast<const VecOf<Tin, 4>*>(src + (size_t)r * C + c);
+    else v = VecOf<Tin, 4>{};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tile[rr][4 * g + j] = (float)v.v[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int cc = q + 16 * i, c = c0 + cc, r = r0 + 4 * g;
+    if (c < C && r < R) {
+      VecOf<Tout, 4> v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v.v[j] = (Tout)tile[4 * g + j][cc];
+      *reinterpret_cast<VecOf<Tout, 4>*>(dst + (size_t)c * R + r) = v;
+    }
+  }
+}
+
 hipError_t launch_transpose(const void* in, int in_dtype, void* out, int out_dtype, int Z, int R, int C,
                             hipStream_t st) {
   if (Z <= 0 || R <= 0 || C <= 0) return hipSuccess;
+  const size_t ein = in_dtype == PNR_BF16 ? 2 : 4, eout = out_dtype == PNR_BF16 ? 2 : 4;
+  const bool vec = R % 4 == 0 && C % 4 == 0 && (uintptr_t)in % (4 * ein) == 0 && (uintptr_t)out % (4 * eout) == 0;
+  if (vec) {
+    dim3 grid4((C + 63) / 64, (R + 63) / 64, Z);
+#define PNR_TR4(TI, TO) \
+  hipLaunchKernelGGL((transpose4_kernel<TI, TO>), grid4, dim3(256), 0, st, static_cast<const TI*>(in), static_cast<TO*>(out), R, C)
+    if (in_dtype == PNR_BF16 && out_dtype == PNR_F32) PNR_TR4(__bf16, float);
+    else if (in_dtype == PNR_F32 && out_dtype == PNR_F32) PNR_TR4(float, float);
+    else if (in_dtype == PNR_BF16 && out_dtype == PNR_BF16) PNR_TR4(__bf16, __bf16);
+    else if (in_dtype == PNR_F32 && out_dtype == PNR_BF16) PNR_TR4(float, __bf16);
+    else return hipErrorInvalidValue;
+#undef PNR_TR4
+    return hipGetLastError();
+  }
   dim3 grid((C + 31) / 32, (R + 31) / 32, Z);
 #define PNR_TR(TI, TO) \
   hipLaunchKernelGGL((transpose_kernel<TI, TO>), grid, dim3(256), 0, st, static_cast<const TI*>(in), static_cast<TO*>(out), R, C)
