@@ -29,7 +29,7 @@ def _check(name, mode):
     print(f"# full-size parity: {name} mode {mode}", flush=True)
     res = pnr.evaluate(w.cell, d["W"], d["U"], d["x"], b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"],
                        max_iters=w.max_iters, tol=w.tol, jac_mode=mode, jac_every=w.jac_every,
-                       damping=w.damping, chunk_len=w.chunk_len)
+                       damping=w.damping, chunk_len=w.chunk_len, refresh_ratio=w.refresh_ratio)
     assert res["status"] == pnr.OK, (name, res["status"], res["residual"])
     assert res["residual"] <= w.tol
     if w.chunk_len is None:
@@ -61,7 +61,8 @@ def _check(name, mode):
     assert err <= bar, (name, mode, err)
 
 
-CASES = [(name, mode) for name in WL.WORKLOAD_ORDER + ["gru_diag_long_elk", "lstm_diag_long_chunked"]
+CASES = [(name, mode) for name in WL.WORKLOAD_ORDER + ["gru_diag_long_elk", "lstm_diag_long_chunked",
+                                                       "lstm_diag_long_adaptive"]
          for mode in WL.get_workload(name).jac_modes]
 
 
@@ -73,10 +74,11 @@ def test_full_size_workload_matches_sequential_oracle(name, mode):
         torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("name", ["gru_diag_long_bwd", "lstm_diag_long_bwd"])
+@pytest.mark.parametrize("name", ["gru_diag_long_bwd", "lstm_diag_long_bwd", "lstm_diag_long_chunked_bwd"])
 def test_full_size_backward_matches_bptt_oracle_on_sampled_channels(name):
     """The backward pass at the converged states of the long workloads, in bench's launch
-    configuration, against the BPTT oracle on 8 evenly spaced channels (an exact
+    configuration (the chunked one: 16 chunks of 8192 steps, last first), against the BPTT
+    oracle on 8 evenly spaced channels (an exact
     sub-problem: those channels' dW rows, dU, db_x, db_h and dh0 columns).  dW goes
     through the bf16 gradient product and is held to 2^-8 sum |dgx| |x| per entry (the
     rounding of the pre-activation gradients to bf16); the others to 1e-4 of their scale."""
@@ -92,7 +94,7 @@ def test_full_size_backward_matches_bptt_oracle_on_sampled_channels(name):
         del fwd
         g = torch.randn(h.shape, generator=torch.Generator().manual_seed(w.seed + 7), dtype=torch.float32).to("cuda")
         got = pnr.backward(w.cell, d["W"], d["U"], d["x"], h, g, b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"],
-                           want=("W", "U", "b_x", "b_h", "h0"))
+                           want=("W", "U", "b_x", "b_h", "h0"), chunk_len=w.chunk_len or 0)
         ch = np.linspace(0, w.D - 1, 8).round().astype(int)
         W, U, bx, h0 = (WL.as_f64(p[k]) for k in ("W", "U", "b_x", "h0"))
         bh = None if p["b_h"] is None else WL.as_f64(p["b_h"])
