@@ -126,9 +126,13 @@ def named_workloads() -> dict:
         "lstm_diag_long", CELL_LSTM_DIAG, B=1, T=131072, D=4096, D_in=4096, x_dtype=DT_BF16,
         state_dtype=DT_F32, w_init="glorot", u_init="uniform1", forget_bias=1.0,
         jac_modes=(JAC_FULL,), jac_every=2, tol=1e-4, max_iters=64)
-    # the long diagonal GRU with the damped (quasi-ELK) step; the strength is a swept
-    # hyperparameter: 0.01 still converges in 6 iterations (4 undamped), 0.1 takes 31
-    w["gru_diag_long_elk"] = dataclasses.replace(w["gru_diag_long"], name="gru_diag_long_elk", damping=0.01)
+    # the long diagonal GRU with the damped (ELK) step; the strength is a swept
+    # hyperparameter: 0.01 still converges in 6 iterations to 1e-4 (4 undamped), 0.1 takes
+    # 31.  The damped iteration contracts linearly, so a residual just under tol leaves a
+    # state error of about tol / (1 - contraction): its tolerance is 10x tighter than the
+    # undamped workload's, which keeps the states within 1e-4 of the sequential ones.
+    w["gru_diag_long_elk"] = dataclasses.replace(w["gru_diag_long"], name="gru_diag_long_elk", damping=0.01,
+                                                 tol=1e-5)
     # the dense GRU of the quasi workload with the damped step on its diagonal Jacobian
     w["gru_quasi_elk"] = dataclasses.replace(w["gru_quasi"], name="gru_quasi_elk", damping=0.01)
     w["lstm_diag_long_stiff"] = dataclasses.replace(
