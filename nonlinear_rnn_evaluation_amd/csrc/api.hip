@@ -24,22 +24,59 @@ using namespace pnr;
 
 namespace {
 
+// Residual history of the calling thread's last call.  A single solve (max_iters <
+// PNR_MAX_ITERS) fits the fixed part, so recording it touches no heap; only the chunked
+// calls, which concatenate one history per chunk, may spill into the heap-backed tail.
+class History {
+ public:
+  void clear() {
+    n_ = 0;
+    tail_.clear();
+  }
+  size_t size() const { return n_ + tail_.size(); }
+  double operator[](size_t i) const { return i < n_ ? head_[i] : tail_[i - n_]; }
+  void push_back(double v) {
+    if (n_ < kHead && tail_.empty())
+      head_[n_++] = v;
+    else
+      tail_.push_back(v);
+  }
+  void assign(const double* b, const double* e) {
+    clear();
+    for (; b != e; ++b) push_back(*b);
+  }
+  void assign(size_t n, double v) {
+    clear();
+    for (size_t i = 0; i < n; ++i) push_back(v);
+  }
+
+ private:
+  static constexpr size_t kHead = PNR_MAX_ITERS + 1;
+  double head_[kHead];
+  size_t n_ = 0;
+  std::vector<double> tail_;
+};
+
 struct LastCall {
   int iters = -1;
   double residual = NAN;
-  std::vector<double> hist;
-  std::string err;
+  History hist;
+  char err[512] = {0};
+  void reset() {
+    iters = -1;
+    residual = NAN;
+    hist.clear();
+    err[0] = 0;
+  }
 };
 thread_local LastCall g_last;
 
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int code, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
+  vsnprintf(g_last.err, sizeof g_last.err, fmt, ap);
   va_end(ap);
-  g_last.err = buf;
   return code;
 }
 
@@ -192,22 +229,17 @@ int device_info(int* num_cu) {
   } while (0)
 
 // The one device -> host crossing of a call: the control block and the residual
-// history (adjacent in the workspace) in one copy into a pinned, thread-local buffer
-// (allocated once, grown rarely, kept for the life of the thread) so the copy is a
-// plain DMA on the stream; then the call's results and, in measurement mode, its
-// per-phase timing.  Returns the call's status.
+// history (adjacent in the workspace) in one copy into thread-local host storage (plain
+// pageable memory of fixed size: the library holds no pinned host allocation, so nothing
+// is left to release at exit), one stream synchronisation; then the call's results and,
+// in measurement mode, its per-phase timing.  Returns the call's status.
+constexpr size_t kReadBackMax = 4096 + sizeof(double) * (PNR_MAX_ITERS + 1);
 int finish_call(const Layout& l, char* ws, int max_iters, hipStream_t st, const Mark& m_first, const Mark& m_proj,
                 const Mark& m_newton, const Mark& m_out) {
-  static thread_local char* rb = nullptr;
-  static thread_local size_t rb_cap = 0;
+  alignas(64) static thread_local char rb[kReadBackMax];
   const size_t rb_bytes = (l.hist - l.ctrl) + sizeof(double) * (max_iters + 1);
-  if (rb_cap < rb_bytes) {
-    if (rb) (void)hipHostFree(rb);
-    rb = nullptr;
-    rb_cap = 0;
-    PNR_HIP(hipHostMalloc(reinterpret_cast<void**>(&rb), rb_bytes, hipHostMallocDefault));
-    rb_cap = rb_bytes;
-  }
+  if (rb_bytes > kReadBackMax) return fail(PNR_E_INVALID, "control read-back of %zu bytes exceeds %zu", rb_bytes,
+                                           kReadBackMax);
   PNR_HIP(hipMemcpyAsync(rb, ws + l.ctrl, rb_bytes, hipMemcpyDeviceToHost, st));
   PNR_HIP(hipStreamSynchronize(st));
   Ctrl hc;
@@ -243,7 +275,7 @@ size_t pnr_workspace_bytes(const pnr_cell* cell, int jac_mode) {
   return make_layout(cell, jac_mode).total;
 }
 
-const char* pnr_last_error(void) { return g_last.err.c_str(); }
+const char* pnr_last_error(void) { return g_last.err; }
 
 int pnr_profile_enable(int on) {
   g_prof.on = on != 0;
@@ -264,11 +296,9 @@ int pnr_last_residual_history(double* out, int max_n) {
 }
 
 namespace {
-int eval_impl(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, void* h_out,
-              int max_iters, double tol, int jac_mode, double refresh_ratio) {
-  g_last = LastCall();
-  g_prof.valid = false;
-  g_prof.used = 0;
+// Argument checks shared by pnr_eval and pnr_eval_adaptive (no HIP call).
+int check_eval_args(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h_out,
+                    int max_iters, double tol, int jac_mode) {
   int rc = validate(cell, jac_mode);
   if (rc) return rc;
   if (!params) return fail(PNR_E_INVALID, "params is NULL");
@@ -277,11 +307,15 @@ int eval_impl(const pnr_cell* cell, const pnr_params* params, const void* x, con
   if (max_iters < 0 || max_iters >= PNR_MAX_ITERS)
     return fail(PNR_E_INVALID, "max_iters must be in [0, %d)", PNR_MAX_ITERS);
   if (isnan(tol)) return fail(PNR_E_INVALID, "tol is NaN");
+  return 0;
+}
+
+// The evaluation proper, on the scratch memory `ws` (at least make_layout(...).total bytes,
+// 256-byte aligned; checked by the callers).
+int eval_impl(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, void* h_out,
+              int max_iters, double tol, int jac_mode, double refresh_ratio, char* ws) {
+  int rc = 0;
   const Layout l = make_layout(cell, jac_mode);
-  if (!cell->workspace) return fail(PNR_E_WORKSPACE, "workspace is NULL (%zu bytes required)", l.total);
-  if ((uintptr_t)cell->workspace % 256) return fail(PNR_E_WORKSPACE, "workspace must be 256-byte aligned");
-  if (cell->workspace_bytes < l.total)
-    return fail(PNR_E_WORKSPACE, "workspace has %zu bytes, %zu required", cell->workspace_bytes, l.total);
   if (cell->T == 0) {
     g_last.iters = 0;
     g_last.residual = 0.0;
@@ -292,7 +326,6 @@ int eval_impl(const pnr_cell* cell, const pnr_params* params, const void* x, con
   int num_cu = 0;
   if ((rc = device_info(&num_cu))) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(cell->stream);
-  char* ws = static_cast<char*>(cell->workspace);
   Ctrl* ctrl = reinterpret_cast<Ctrl*>(ws + l.ctrl);
   double* hist = reinterpret_cast<double*>(ws + l.hist);
   uint64_t* slots = reinterpret_cast<uint64_t*>(ws + l.slots);
@@ -433,19 +466,39 @@ int eval_impl(const pnr_cell* cell, const pnr_params* params, const void* x, con
 }
 }  // namespace
 
+namespace {
+// pnr_eval / pnr_eval_adaptive on the caller's workspace.
+int eval_workspace(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, void* h_out,
+                   int max_iters, double tol, int jac_mode, double refresh_ratio) {
+  int rc = check_eval_args(cell, params, x, h_out, max_iters, tol, jac_mode);
+  if (rc) return rc;
+  const size_t need = make_layout(cell, jac_mode).total;
+  if (!cell->workspace) return fail(PNR_E_WORKSPACE, "workspace is NULL (%zu bytes required)", need);
+  if ((uintptr_t)cell->workspace % 256) return fail(PNR_E_WORKSPACE, "workspace must be 256-byte aligned");
+  if (cell->workspace_bytes < need)
+    return fail(PNR_E_WORKSPACE, "workspace has %zu bytes, %zu required", cell->workspace_bytes, need);
+  return eval_impl(cell, params, x, h0, h_out, max_iters, tol, jac_mode, refresh_ratio,
+                   static_cast<char*>(cell->workspace));
+}
+}  // namespace
+
 int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, void* h_out,
              int max_iters, double tol, int jac_mode) {
-  return eval_impl(cell, params, x, h0, h_out, max_iters, tol, jac_mode, -1.0);
+  g_last.reset();
+  g_prof.valid = false;
+  g_prof.used = 0;
+  return eval_workspace(cell, params, x, h0, h_out, max_iters, tol, jac_mode, -1.0);
 }
 
 int pnr_eval_adaptive(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, void* h_out,
                       int max_iters, double tol, int jac_mode, double refresh_ratio) {
-  g_last = LastCall();
+  g_last.reset();
   g_prof.valid = false;
+  g_prof.used = 0;
   if (!(refresh_ratio >= 0.0)) return fail(PNR_E_INVALID, "refresh_ratio must be >= 0 (got %g)", refresh_ratio);
   if (cell && cell->kind == PNR_CELL_GRU)
     return fail(PNR_E_UNSUPPORTED, "the adaptive Jacobian refresh is implemented for the diagonal-recurrence cells");
-  return eval_impl(cell, params, x, h0, h_out, max_iters, tol, jac_mode, refresh_ratio);
+  return eval_workspace(cell, params, x, h0, h_out, max_iters, tol, jac_mode, refresh_ratio);
 }
 
 // ---- damped (quasi-ELK) evaluation ----
@@ -557,7 +610,7 @@ int eval_damped_dense(const pnr_cell* cell, const pnr_params* params, const void
   PNR_HIP(hipStreamSynchronize(st));
   g_last.iters = k;
   g_last.residual = rho;
-  g_last.hist = std::move(hist);
+  g_last.hist.assign(hist.data(), hist.data() + hist.size());
   if (g_prof.on) {
     pnr_profile p{};
     p.total_ms = mark_ms(m_first);
@@ -575,7 +628,7 @@ int eval_damped_dense(const pnr_cell* cell, const pnr_params* params, const void
 
 int pnr_eval_damped(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, void* h_out,
                     int max_iters, double tol, int jac_mode, double damping) {
-  g_last = LastCall();
+  g_last.reset();
   g_prof.valid = false;
   g_prof.used = 0;
   int rc = validate_damped(cell, jac_mode);
@@ -695,7 +748,7 @@ size_t pnr_workspace_bytes_chunked(const pnr_cell* cell, int jac_mode, double da
 
 int pnr_eval_chunked(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, void* h_out,
                      int max_iters, double tol, int jac_mode, double damping, int chunk_len) {
-  g_last = LastCall();
+  g_last.reset();
   g_prof.valid = false;
   ChunkPlan p;
   int rc = plan_chunks(cell, jac_mode, damping, chunk_len, p);
@@ -758,14 +811,14 @@ int pnr_eval_chunked(const pnr_cell* cell, const pnr_params* params, const void*
     }
     iters += g_last.iters;
     if (!(g_last.residual <= residual)) residual = g_last.residual;   // max, NaN wins
-    hist.insert(hist.end(), g_last.hist.begin(), g_last.hist.end());
+    for (size_t i = 0; i < g_last.hist.size(); ++i) hist.push_back(g_last.hist[i]);
     if (status_rank(rc) > status_rank(status)) status = rc;
     if (rc == PNR_NONFINITE) break;   // later chunks would start from a non-finite state
   }
   PNR_HIP(hipStreamSynchronize(st));
   g_last.iters = iters;
   g_last.residual = residual;
-  g_last.hist = std::move(hist);
+  g_last.hist.assign(hist.data(), hist.data() + hist.size());
   g_prof.valid = prof_ok;
   if (prof_ok) g_prof.last = acc;
   return status;
@@ -956,7 +1009,7 @@ int backward_dense(const pnr_cell* cell, const pnr_params* params, const void* x
   mark_end(m_first, st);
   g_last.iters = updates;
   g_last.residual = rho;
-  g_last.hist = std::move(hist);
+  g_last.hist.assign(hist.data(), hist.data() + hist.size());
   if (g_prof.on) {
     PNR_HIP(hipStreamSynchronize(st));
     pnr_profile p{};
@@ -980,7 +1033,7 @@ size_t pnr_workspace_bytes_backward(const pnr_cell* cell) {
 int pnr_backward(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, const void* h,
                  const void* grad_h, void* grad_x, void* grad_W, void* grad_U, void* grad_b_x, void* grad_b_h,
                  void* grad_h0) {
-  g_last = LastCall();
+  g_last.reset();
   g_prof.valid = false;
   g_prof.used = 0;
   int rc = validate_backward(cell);
@@ -1156,7 +1209,7 @@ size_t pnr_workspace_bytes_backward_chunked(const pnr_cell* cell, int chunk_len)
 int pnr_backward_chunked(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, const void* h,
                          const void* grad_h, void* grad_x, void* grad_W, void* grad_U, void* grad_b_x,
                          void* grad_b_h, void* grad_h0, int chunk_len) {
-  g_last = LastCall();
+  g_last.reset();
   g_prof.valid = false;
   BwdChunkPlan p;
   int rc = plan_bwd_chunks(cell, chunk_len, p);
@@ -1238,7 +1291,7 @@ int pnr_backward_chunked(const pnr_cell* cell, const pnr_params* params, const v
     }
     iters += g_last.iters;
     if (!(g_last.residual <= residual)) residual = g_last.residual;
-    hist.insert(hist.end(), g_last.hist.begin(), g_last.hist.end());
+    for (size_t i = 0; i < g_last.hist.size(); ++i) hist.push_back(g_last.hist[i]);
     if (p.staged && grad_x)
       PNR_HIP(hipMemcpy2DAsync(static_cast<char*>(grad_x) + t0 * Din * f, T * Din * f, dxc, Lc * Din * f,
                                Lc * Din * f, B, hipMemcpyDeviceToDevice, st));
@@ -1253,7 +1306,7 @@ int pnr_backward_chunked(const pnr_cell* cell, const pnr_params* params, const v
   PNR_HIP(hipStreamSynchronize(st));
   g_last.iters = iters;
   g_last.residual = residual;
-  g_last.hist = std::move(hist);
+  g_last.hist.assign(hist.data(), hist.data() + hist.size());
   g_prof.valid = prof_ok;
   if (prof_ok) g_prof.last = acc;
   return status;
@@ -1271,7 +1324,7 @@ size_t pnr_scan_workspace_bytes(int kind, int R, int T, int tile_len) {
 
 int pnr_scan(int kind, int R, int T, const float* A, const float* b, float* d, int tile_len, void* workspace,
              size_t workspace_bytes, void* stream) {
-  g_last = LastCall();
+  g_last.reset();
   if (kind != 1 && kind != 2) return fail(PNR_E_INVALID, "scan kind must be 1 (diagonal) or 2 (2x2)");
   if (R < 0 || T < 0) return fail(PNR_E_INVALID, "R and T must be >= 0");
   if (tile_len == 0) tile_len = scan_default_tile(kind);
