@@ -150,6 +150,25 @@ int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, cons
 int pnr_eval_adaptive(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0,
                       void* h_out, int max_iters, double tol, int jac_mode, double refresh_ratio);
 
+/*
+ * pnr_eval without allocation, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, iteration, results and errors as pnr_eval, except that pnr_cell.workspace
+ * and workspace_bytes are ignored: the scratch (control words, residual partials,
+ * look-back slots, gate pre-activations and iterates) lives in a static device array of
+ * PNR_STATIC_SCRATCH_BYTES, one per device, held from the library's first use on that
+ * device until the process ends.  A problem whose pnr_workspace_bytes() exceeds that
+ * size returns PNR_E_WORKSPACE before any device work (e.g. B=8, T=4096, D=64 fits; the
+ * long diagonal workloads do not).  The call makes no hipMalloc/hipFree and no other
+ * allocating call; it clears what must start at zero with a kernel on the caller's
+ * stream.  Every call on one device shares that device's array: calls that overlap on
+ * one device (other threads, other streams) race and must be serialised by the caller.
+ * Measurement mode (pnr_profile_enable) does not apply to this entry point.
+ */
+#define PNR_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int pnr_eval_static(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0,
+                    void* h_out, int max_iters, double tol, int jac_mode);
+
 /* Newton updates applied by the calling thread's last pnr_eval (-1 if it failed before). */
 int pnr_iters_used(void);
 

@@ -14,6 +14,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -296,7 +297,7 @@ int pnr_last_residual_history(double* out, int max_n) {
 }
 
 namespace {
-// Argument checks shared by pnr_eval and pnr_eval_adaptive (no HIP call).
+// Argument checks shared by pnr_eval, pnr_eval_adaptive and pnr_eval_static (no HIP call).
 int check_eval_args(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h_out,
                     int max_iters, double tol, int jac_mode) {
   int rc = validate(cell, jac_mode);
@@ -499,6 +500,60 @@ int pnr_eval_adaptive(const pnr_cell* cell, const pnr_params* params, const void
   if (cell && cell->kind == PNR_CELL_GRU)
     return fail(PNR_E_UNSUPPORTED, "the adaptive Jacobian refresh is implemented for the diagonal-recurrence cells");
   return eval_workspace(cell, params, x, h0, h_out, max_iters, tol, jac_mode, refresh_ratio);
+}
+
+// ---- evaluation without allocation: pnr_eval on a static device scratch ----
+// Callers that cannot allocate (code under graph capture, tight serving loops) use this
+// array instead of a workspace.  Each device the library runs on holds its own copy for
+// the life of the process.  Host code never passes the array's name to a kernel: its
+// device address is looked up once per device with hipGetSymbolAddress and kept below.
+static __device__ __align__(256) unsigned char scratch[PNR_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxScratchDevices];   // per device; guarded by g_scratch_mu
+
+// Device address of `scratch` on the current device (looked up on the first call there).
+int static_scratch(char** out) {
+  int dev = 0;
+  PNR_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(PNR_E_UNSUPPORTED, "device %d is beyond the %d devices pnr_eval_static tracks", dev,
+                kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    PNR_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p || (uintptr_t)p % 256) return fail(PNR_E_HIP, "hipGetSymbolAddress gave an unusable scratch address");
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return 0;
+}
+}  // namespace
+
+int pnr_eval_static(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, void* h_out,
+                    int max_iters, double tol, int jac_mode) {
+  g_last.reset();
+  g_prof.valid = false;
+  g_prof.used = 0;
+  int rc = check_eval_args(cell, params, x, h_out, max_iters, tol, jac_mode);
+  if (rc) return rc;
+  const size_t need = make_layout(cell, jac_mode).total;
+  if (need > PNR_STATIC_SCRATCH_BYTES)
+    return fail(PNR_E_WORKSPACE,
+                "this problem needs %zu bytes of scratch; pnr_eval_static's static scratch holds %zu "
+                "(use pnr_eval with a workspace)",
+                need, (size_t)PNR_STATIC_SCRATCH_BYTES);
+  char* ws = nullptr;
+  if (cell->T > 0 && (rc = static_scratch(&ws))) return rc;
+  // measurement mode would create HIP events: it does not apply to this entry point
+  const bool prof = g_prof.on;
+  g_prof.on = false;
+  rc = eval_impl(cell, params, x, h0, h_out, max_iters, tol, jac_mode, -1.0, ws);
+  g_prof.on = prof;
+  return rc;
 }
 
 // ---- damped (quasi-ELK) evaluation ----

@@ -23,6 +23,7 @@ JAC_FULL, JAC_DIAG, JAC_ZERO = 0, 1, 2
 F64, F32, BF16 = 0, 1, 2
 OK, NOT_CONVERGED, NONFINITE = 0, 1, 2
 E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP = -1, -2, -3, -4
+STATIC_SCRATCH_BYTES = 64 << 20   # PNR_STATIC_SCRATCH_BYTES of include/pnr.h
 
 _DT = {torch.float64: F64, torch.float32: F32, torch.bfloat16: BF16}
 
@@ -77,6 +78,9 @@ def load() -> ctypes.CDLL:
     lib.pnr_workspace_bytes_backward.restype = ctypes.c_size_t
     lib.pnr_backward.argtypes = [P(PnrCell), P(PnrParams)] + [ctypes.c_void_p] * 10
     lib.pnr_backward.restype = ctypes.c_int
+    lib.pnr_eval_static.argtypes = [P(PnrCell), P(PnrParams), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_int, ctypes.c_double, ctypes.c_int]
+    lib.pnr_eval_static.restype = ctypes.c_int
     lib.pnr_eval_adaptive.argtypes = [P(PnrCell), P(PnrParams), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_double]
     lib.pnr_eval_adaptive.restype = ctypes.c_int
@@ -157,6 +161,11 @@ def pnr_workspace_bytes(cell: PnrCell, jac_mode: int) -> int:
 def pnr_eval(cell: PnrCell, params: PnrParams, x: int, h0: Optional[int], h_out: int, max_iters: int,
              tol: float, jac_mode: int) -> int:
     return load().pnr_eval(ctypes.byref(cell), ctypes.byref(params), x, h0, h_out, max_iters, tol, jac_mode)
+
+
+def pnr_eval_static(cell: PnrCell, params: PnrParams, x: int, h0: Optional[int], h_out: int, max_iters: int,
+                    tol: float, jac_mode: int) -> int:
+    return load().pnr_eval_static(ctypes.byref(cell), ctypes.byref(params), x, h0, h_out, max_iters, tol, jac_mode)
 
 
 def pnr_eval_adaptive(cell: PnrCell, params: PnrParams, x: int, h0: Optional[int], h_out: int, max_iters: int,
@@ -257,12 +266,17 @@ def evaluate(kind: int, W: torch.Tensor, U: torch.Tensor, x: torch.Tensor, *, b_
              h0=None, max_iters: int = 64, tol: float = 1e-5, jac_mode: int = JAC_FULL,
              jac_every: int = 1, h_out: Optional[torch.Tensor] = None,
              workspace: Optional[torch.Tensor] = None, damping: Optional[float] = None,
-             chunk_len: Optional[int] = None, refresh_ratio: Optional[float] = None) -> dict:
+             chunk_len: Optional[int] = None, refresh_ratio: Optional[float] = None,
+             static_scratch: bool = False) -> dict:
     """Run pnr_eval (or pnr_eval_damped when `damping` is given, pnr_eval_chunked when
-    `chunk_len` is given, pnr_eval_adaptive when `refresh_ratio` is given) on device
-    tensors; returns dict(h=[B,T,S], status, iters, residual, history)."""
+    `chunk_len` is given, pnr_eval_adaptive when `refresh_ratio` is given, pnr_eval_static
+    -- no workspace; the library's static device scratch -- when `static_scratch`) on
+    device tensors; returns dict(h=[B,T,S], status, iters, residual, history)."""
     if refresh_ratio is not None and (damping is not None or chunk_len is not None):
         raise ValueError("refresh_ratio combines with neither damping nor chunk_len")
+    if static_scratch and (refresh_ratio is not None or damping is not None or chunk_len is not None
+                           or workspace is not None):
+        raise ValueError("static_scratch is pnr_eval's variant: no damping, chunking, refresh ratio or workspace")
     B, T, D_in = x.shape
     D = U.shape[1]
     S = 2 * D if kind == CELL_LSTM_DIAG else D
@@ -279,23 +293,28 @@ def evaluate(kind: int, W: torch.Tensor, U: torch.Tensor, x: torch.Tensor, *, b_
         _check(h_out, "h_out", sd, (B, T, S))
     ptrs = {k: _ptr(v) for k, v in args.items()}
     cell = make_cell(kind, D, D_in, T, B, xdt, sdt, jac_every, _stream())
-    if chunk_len is not None:
+    if static_scratch:
+        need = 0
+    elif chunk_len is not None:
         need = pnr_workspace_bytes_chunked(cell, jac_mode, damping or 0.0, chunk_len)
     elif damping is None:
         need = pnr_workspace_bytes(cell, jac_mode)
     else:
         need = pnr_workspace_bytes_damped(cell, jac_mode)
-    if need == 0:
+    if need == 0 and not static_scratch:
         raise PnrError(pnr_last_error())
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    cell.workspace = workspace.data_ptr()
-    cell.workspace_bytes = workspace.numel()
+    if not static_scratch:
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        cell.workspace = workspace.data_ptr()
+        cell.workspace_bytes = workspace.numel()
     if h_out is None:
         h_out = torch.empty(B, T, S, dtype=U.dtype, device=x.device)
     out = _arg(h_out, "h_out", sd, (B, T, S))
     params = PnrParams(ptrs["W"], ptrs["U"], ptrs["b_x"], ptrs["b_h"])
-    if chunk_len is not None:
+    if static_scratch:
+        rc = pnr_eval_static(cell, params, ptrs["x"], ptrs["h0"], out, max_iters, tol, jac_mode)
+    elif chunk_len is not None:
         rc = pnr_eval_chunked(cell, params, ptrs["x"], ptrs["h0"], out, max_iters, tol, jac_mode,
                               damping or 0.0, chunk_len)
     elif refresh_ratio is not None:
