@@ -62,6 +62,15 @@
  *   GRU_DIAG,
  *   LSTM_DIAG:  (x, state) in {(f32, f32), (bf16, f32)}
  *
+ * Launches.  Each Newton loop is one persistent kernel whose workgroups wait on one
+ * another, sized to the device's resident capacity and launched with
+ * hipLaunchCooperativeKernel, which guarantees that they are all resident at once, also
+ * next to other work on the device; calls with distinct workspaces may therefore run on
+ * different streams at the same time.  Every device-side wait is bounded: one that runs
+ * out is reported as PNR_E_HIP, never a hang.  Setting PNR_COOPERATIVE=0 in the
+ * environment (read once per process) selects ordinary launches, slightly cheaper, for
+ * callers that run nothing else on the device while a call is in flight.
+ *
  * Errors.  Functions never abort and never print.  Negative return codes mean no
  * result was produced; the text of the last error of the calling thread is
  * available from pnr_last_error().  Argument validation happens before any HIP call.

@@ -695,14 +695,9 @@ int diag_slot_words(int cell) {
 
 template <int CELL>
 static int diag_capacity(int num_cu) {
-  static int per_cu = 0;
-  if (per_cu == 0) {
-    int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, diag_newton_kernel<CELL, diag_n<CELL>()>, PNR_BLOCK, 0) !=
-            hipSuccess || v < 1)
-      v = 1;
-    per_cu = v;
-  }
+  // per device and thread-safe (cached_occupancy)
+  int per_cu = cached_occupancy((const void*)diag_newton_kernel<CELL, diag_n<CELL>()>, 0);
+  if (per_cu < 1) per_cu = 1;
   long g = (long)per_cu * num_cu;
   return (int)(g > kMaxGrid ? kMaxGrid : g);
 }

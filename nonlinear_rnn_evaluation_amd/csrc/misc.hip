@@ -27,17 +27,18 @@ int cached_occupancy(const void* fn, size_t lds) {
 }
 
 // Persistent launches.  Every persistent grid here is sized to the device's resident
-// capacity (cached_occupancy) and every wait inside it is bounded (a wait that runs out
-// records a fault, which the call reports as an error, never a hang).  Such a grid goes
-// out as an ordinary launch: on a device that runs nothing else at the same time all of
-// its workgroups are resident together, and the ordinary path costs ~15-20 us less per
-// call than the cooperative one.  PNR_COOPERATIVE=1 selects hipLaunchCooperativeKernel,
-// which also guarantees co-residency next to other work (several persistent calls
-// running at once on different streams, for instance).
+// capacity (cached_occupancy), and the loop inside needs all of its workgroups resident
+// at once (look-back and grid-barrier waits on other workgroups).  By default the grid
+// goes out through hipLaunchCooperativeKernel, which guarantees that co-residency even
+// next to other work on the device (other streams, other persistent calls).  Every wait
+// is also bounded: a wait that runs out records a fault, which the call reports as an
+// error, never a hang.  PNR_COOPERATIVE=0 (read once per process) selects the ordinary
+// launch, about 15-20 us cheaper per call, for callers that run nothing else on the
+// device at the same time.
 hipError_t launch_persistent(const void* fn, int grid, size_t lds, void** args, hipStream_t st) {
   static const bool coop = [] {
     const char* e = getenv("PNR_COOPERATIVE");
-    return e && e[0] == '1';
+    return !(e && e[0] == '0');
   }();
   if (coop) return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(PNR_BLOCK), args, (unsigned)lds, st);
   return hipLaunchKernel(fn, dim3(grid), dim3(PNR_BLOCK), args, lds, st);
