@@ -31,6 +31,10 @@ What it computes (sources are the five pages on this method):
   backwards in time, step by step (ParaRNN overview, "Newton's Iteration": forward and
   backward substitution; training through the parallel evaluation, "Parallelizing
   non-linear sequential models over the sequence length", abstract).
+* ``newton_dense(..., bounded=True)`` -- each Newton iterate projected onto the box every
+  reachable state lies in (``state_bounds``): a safeguard of this oracle's readings against
+  the divergence of undamped Newton ("Towards Scalable and Stable Parallelization of
+  Nonlinear RNNs", summary page, "Problem").
 * ``newton_chunked`` -- the sequence evaluated chunk by chunk, each chunk from the
   previous chunk's last state (ParaRNN overview, "Experimental Results": chunking to
   bound the memory of long sequences).
@@ -43,7 +47,8 @@ recurrent weights for the diagonal-recurrence variants) are pinned by the tests 
 from .cells import (CELL_GRU, CELL_GRU_DIAG, CELL_LSTM_DIAG, JAC_FULL, JAC_DIAG, JAC_ZERO,
                     cell_step, cell_jacobian, approx_jacobian, gates_of, state_size)
 from .sequential import project, sequential, restrict_channels
-from .newton import newton_dense, STATUS_OK, STATUS_NOT_CONVERGED, STATUS_NONFINITE, max_abs
+from .newton import (newton_dense, STATUS_OK, STATUS_NOT_CONVERGED, STATUS_NONFINITE, max_abs,
+                     state_bounds, project_states)
 from .scan import scan_loop, scan_doubling, compose
 from .damped import lm_step_dense, lm_step_kalman, damped_step
 from .chunked import newton_chunked
@@ -54,6 +59,7 @@ __all__ = [
     "cell_step", "cell_jacobian", "approx_jacobian", "gates_of", "state_size",
     "project", "sequential", "restrict_channels",
     "newton_dense", "STATUS_OK", "STATUS_NOT_CONVERGED", "STATUS_NONFINITE", "max_abs",
+    "state_bounds", "project_states",
     "scan_loop", "scan_doubling", "compose",
     "lm_step_dense", "lm_step_kalman", "damped_step",
     "newton_chunked", "bptt", "cell_vjp",

@@ -31,6 +31,14 @@ Options:
   its own residual.  theta = inf gives the fixed schedule, theta = 0 refreshes at every
   k >= 2.
 
+* bounded = True (a safeguard of this reading's own, not the pages': "Towards Scalable and
+  Stable Parallelization of Nonlinear RNNs", abstract and summary "Problem", says
+  undamped Newton can be numerically unstable and diverge): after each update the new
+  iterate is projected onto the box that every state of the recurrence lies in
+  (``state_bounds``), and a component the step made NaN keeps its previous value.  The
+  true states lie inside the box, so the projection never moves them: the exact-prefix
+  property below still holds, and so does the fixed point.
+
 Readings where the pages are silent: initial guess H = 0; stop when the max-abs
 residual (NaN counted as +inf) is <= tol, testing *before* each update so the
 returned iterate is the one whose residual was checked; one shared loop for all
@@ -40,7 +48,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .cells import approx_jacobian, cell_jacobian, cell_step
+from .cells import CELL_LSTM_DIAG, approx_jacobian, cell_jacobian, cell_step
 from .damped import damped_step
 from .scan import scan_loop
 from .sequential import project
@@ -60,6 +68,34 @@ def max_abs(r) -> float:
     return float(a.max())
 
 
+def state_bounds(cell: int, h0, T: int):
+    """Bounds [B, T, S] with |s_t| <= bound for every state s_1..s_T the recurrence can reach
+    from h0, per component.
+
+    GRU cells: h' = (1 - z) n + z h is a convex combination of n (|n| < 1, a tanh) and h, so
+    |h'_i| <= max(1, |h_i|) <= max(1, |h0_i|).  LSTM: h' = o tanh(c') with 0 < o < 1, so
+    |h'| < 1; c' = f c + i g with 0 < f, i < 1 and |g| < 1, so |c'| < |c| + 1 and
+    |c_t| < |c0| + t.
+    """
+    h0 = np.asarray(h0, dtype=np.float64)
+    B, S = h0.shape
+    if cell == CELL_LSTM_DIAG:
+        D = S // 2
+        t = np.arange(1, T + 1, dtype=np.float64)[None, :, None]
+        c = np.abs(h0[:, None, :D]) + t
+        h = np.ones((B, T, D))
+        return np.concatenate([c, h], axis=2)
+    return np.broadcast_to(np.maximum(1.0, np.abs(h0))[:, None, :], (B, T, S)).copy()
+
+
+def project_states(cell: int, h0, H_new, H_old):
+    """The projected update: NaN components keep their previous value, then every component
+    is clipped to its state bound."""
+    H = np.where(np.isnan(H_new), H_old, H_new)
+    bound = state_bounds(cell, h0, H.shape[1])
+    return np.clip(H, -bound, bound)
+
+
 def _previous_states(h0, H):
     """P_t = H_{t-1} (with H_0 = h0) for every step: [B, T, S]."""
     return np.concatenate([h0[:, None, :], H[:, :-1, :]], axis=1)
@@ -67,7 +103,7 @@ def _previous_states(h0, H):
 
 def newton_dense(cell: int, W, U, b_x, b_h, x, h0, max_iters: int, tol: float,
                  jac_mode: int, jac_every: int = 1, gx=None, solver: str = "dense",
-                 damping: float = 0.0, refresh_ratio=None):
+                 damping: float = 0.0, refresh_ratio=None, bounded: bool = False):
     """Returns dict(states [B,T,S], iters, status, rhos[list], jac_evals, refreshes[list
     of the iterations that recomputed the Jacobian]).
 
@@ -118,16 +154,19 @@ def newton_dense(cell: int, W, U, b_x, b_h, x, h0, max_iters: int, tol: float,
             J = cell_jacobian(cell, U, b_h, P.reshape(B * T, S), gx.reshape(B * T, GD))
             Jhat = approx_jacobian(J, jac_mode).reshape(B, T, S, S)
             jac_evals += 1
-        for b in range(B):
-            if damping > 0:
-                H[b] = H[b] + damped_step(Jhat[b], r[b], damping, "dense" if solver == "dense" else "kalman")
-                continue
-            if solver == "loop":
-                H[b] = H[b] + scan_loop(Jhat[b], r[b])
-                continue
-            A = np.eye(T * S)
-            for t in range(1, T):
-                A[t * S:(t + 1) * S, (t - 1) * S:t * S] = -Jhat[b, t]
-            delta = np.linalg.solve(A, r[b].reshape(T * S))
-            H[b] = H[b] + delta.reshape(T, S)
+        Hn = np.empty_like(H)
+        with np.errstate(over="ignore", invalid="ignore"):
+            for b in range(B):
+                if damping > 0:
+                    Hn[b] = H[b] + damped_step(Jhat[b], r[b], damping, "dense" if solver == "dense" else "kalman")
+                    continue
+                if solver == "loop":
+                    Hn[b] = H[b] + scan_loop(Jhat[b], r[b])
+                    continue
+                A = np.eye(T * S)
+                for t in range(1, T):
+                    A[t * S:(t + 1) * S, (t - 1) * S:t * S] = -Jhat[b, t]
+                delta = np.linalg.solve(A, r[b].reshape(T * S))
+                Hn[b] = H[b] + delta.reshape(T, S)
+        H = project_states(cell, h0, Hn, H) if bounded else Hn
         k += 1
