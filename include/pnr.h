@@ -178,6 +178,25 @@ int pnr_eval_adaptive(const pnr_cell* cell, const pnr_params* params, const void
 int pnr_eval_static(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0,
                     void* h_out, int max_iters, double tol, int jac_mode);
 
+/*
+ * pnr_eval with a bounded iteration, for the diagonal-recurrence cells (PNR_CELL_GRU_DIAG,
+ * PNR_CELL_LSTM_DIAG).  Undamped Newton can diverge ("Towards Scalable and Stable
+ * Parallelization of Nonlinear RNNs", summary page, "Problem"): from the zero guess the
+ * linearised recurrence of a stiff cell can be so expansive that the step overflows.
+ * Here each new iterate is projected onto the box every reachable state lies in -- a
+ * safeguard of this library's own, not the pages' damping -- and a component the step
+ * made NaN keeps its current value:
+ *     GRU_DIAG:   |h_t| <= max(1, |h0|)      (h' is a convex combination of tanh(.) and h)
+ *     LSTM_DIAG:  |h_t| <= 1,  |c_t| <= |c0| + t      (t = 1..T)
+ * The true states lie inside the box, so the projection never moves them: every property
+ * of pnr_eval's iteration that rests on them holds (after k updates the first k states
+ * are exact; the fixed point is the sequential trajectory), and iterates that stay inside
+ * are pnr_eval's, bit for bit.  Arguments, workspace (pnr_workspace_bytes), jac_mode,
+ * jac_every and results as pnr_eval; the dense-U GRU returns PNR_E_UNSUPPORTED.
+ */
+int pnr_eval_bounded(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0,
+                     void* h_out, int max_iters, double tol, int jac_mode);
+
 /* Newton updates applied by the calling thread's last pnr_eval (-1 if it failed before). */
 int pnr_iters_used(void);
 

@@ -297,7 +297,7 @@ int pnr_last_residual_history(double* out, int max_n) {
 }
 
 namespace {
-// Argument checks shared by pnr_eval, pnr_eval_adaptive and pnr_eval_static (no HIP call).
+// Argument checks shared by pnr_eval and its variants (no HIP call).
 int check_eval_args(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h_out,
                     int max_iters, double tol, int jac_mode) {
   int rc = validate(cell, jac_mode);
@@ -314,7 +314,7 @@ int check_eval_args(const pnr_cell* cell, const pnr_params* params, const void* 
 // The evaluation proper, on the scratch memory `ws` (at least make_layout(...).total bytes,
 // 256-byte aligned; checked by the callers).
 int eval_impl(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, void* h_out,
-              int max_iters, double tol, int jac_mode, double refresh_ratio, char* ws) {
+              int max_iters, double tol, int jac_mode, double refresh_ratio, int bounded, char* ws) {
   int rc = 0;
   const Layout l = make_layout(cell, jac_mode);
   if (cell->T == 0) {
@@ -379,6 +379,7 @@ int eval_impl(const pnr_cell* cell, const pnr_params* params, const void* x, con
     a.max_iters = max_iters; a.jac_every = cell->jac_every; a.jac_mode = jac_mode;
     a.tol = tol;
     a.refresh_ratio = refresh_ratio;
+    a.bounded = bounded;
     const int cap = diag_grid_capacity(kind, num_cu);
     // A block walks whole rows (no look-back) when there are enough rows to fill the
     // grid; otherwise rows are cut into tiles linked by the decoupled look-back.
@@ -470,7 +471,7 @@ int eval_impl(const pnr_cell* cell, const pnr_params* params, const void* x, con
 namespace {
 // pnr_eval / pnr_eval_adaptive on the caller's workspace.
 int eval_workspace(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, void* h_out,
-                   int max_iters, double tol, int jac_mode, double refresh_ratio) {
+                   int max_iters, double tol, int jac_mode, double refresh_ratio, int bounded) {
   int rc = check_eval_args(cell, params, x, h_out, max_iters, tol, jac_mode);
   if (rc) return rc;
   const size_t need = make_layout(cell, jac_mode).total;
@@ -478,7 +479,7 @@ int eval_workspace(const pnr_cell* cell, const pnr_params* params, const void* x
   if ((uintptr_t)cell->workspace % 256) return fail(PNR_E_WORKSPACE, "workspace must be 256-byte aligned");
   if (cell->workspace_bytes < need)
     return fail(PNR_E_WORKSPACE, "workspace has %zu bytes, %zu required", cell->workspace_bytes, need);
-  return eval_impl(cell, params, x, h0, h_out, max_iters, tol, jac_mode, refresh_ratio,
+  return eval_impl(cell, params, x, h0, h_out, max_iters, tol, jac_mode, refresh_ratio, bounded,
                    static_cast<char*>(cell->workspace));
 }
 }  // namespace
@@ -488,7 +489,17 @@ int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, cons
   g_last.reset();
   g_prof.valid = false;
   g_prof.used = 0;
-  return eval_workspace(cell, params, x, h0, h_out, max_iters, tol, jac_mode, -1.0);
+  return eval_workspace(cell, params, x, h0, h_out, max_iters, tol, jac_mode, -1.0, 0);
+}
+
+int pnr_eval_bounded(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, void* h_out,
+                     int max_iters, double tol, int jac_mode) {
+  g_last.reset();
+  g_prof.valid = false;
+  g_prof.used = 0;
+  if (cell && cell->kind == PNR_CELL_GRU)
+    return fail(PNR_E_UNSUPPORTED, "the bounded iteration is implemented for the diagonal-recurrence cells");
+  return eval_workspace(cell, params, x, h0, h_out, max_iters, tol, jac_mode, -1.0, 1);
 }
 
 int pnr_eval_adaptive(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, void* h_out,
@@ -499,7 +510,7 @@ int pnr_eval_adaptive(const pnr_cell* cell, const pnr_params* params, const void
   if (!(refresh_ratio >= 0.0)) return fail(PNR_E_INVALID, "refresh_ratio must be >= 0 (got %g)", refresh_ratio);
   if (cell && cell->kind == PNR_CELL_GRU)
     return fail(PNR_E_UNSUPPORTED, "the adaptive Jacobian refresh is implemented for the diagonal-recurrence cells");
-  return eval_workspace(cell, params, x, h0, h_out, max_iters, tol, jac_mode, refresh_ratio);
+  return eval_workspace(cell, params, x, h0, h_out, max_iters, tol, jac_mode, refresh_ratio, 0);
 }
 
 // ---- evaluation without allocation: pnr_eval on a static device scratch ----
@@ -551,7 +562,7 @@ int pnr_eval_static(const pnr_cell* cell, const pnr_params* params, const void* 
   // measurement mode would create HIP events: it does not apply to this entry point
   const bool prof = g_prof.on;
   g_prof.on = false;
-  rc = eval_impl(cell, params, x, h0, h_out, max_iters, tol, jac_mode, -1.0, ws);
+  rc = eval_impl(cell, params, x, h0, h_out, max_iters, tol, jac_mode, -1.0, 0, ws);
   g_prof.on = prof;
   return rc;
 }

@@ -290,10 +290,32 @@ __device__ __forceinline__ Aff2 readlane_aff(const Aff2& v, int l) {
               readlane_f(v.a11, l), readlane_f(v.b0, l), readlane_f(v.b1, l)};
 }
 
+// Lanes with no source lane in their row keep their value (a select, not a composition
+// with the identity: with an infinite entry, inf * 0 in that product would make a NaN
+// that the plain sequence of compositions never forms).
+template <class E>
+__device__ __forceinline__ E select_aff(bool take, const E& a, const E& b);
+template <>
+__device__ __forceinline__ Aff1 select_aff(bool take, const Aff1& a, const Aff1& b) {
+  return Aff1{take ? a.a : b.a, take ? a.b : b.b};
+}
+template <>
+__device__ __forceinline__ Aff2 select_aff(bool take, const Aff2& a, const Aff2& b) {
+  return Aff2{take ? a.a00 : b.a00, take ? a.a01 : b.a01, take ? a.a10 : b.a10,
+              take ? a.a11 : b.a11, take ? a.b0 : b.b0,   take ? a.b1 : b.b1};
+}
+
+template <>
+__device__ __forceinline__ Flt select_aff(bool take, const Flt& a, const Flt& b) {
+  return Flt{take ? a.a : b.a, take ? a.b : b.b, take ? a.c : b.c, take ? a.d : b.d,
+             take ? a.e : b.e, take ? a.f : b.f, take ? a.g : b.g};
+}
+
 template <class E>
 __device__ __forceinline__ E wave_inclusive_scan(E v, const E& id) {
+  const int rl = (int)(lane_id() & 15);
 #pragma unroll
-  for (int s = 1; s <= 8; s <<= 1) v = compose(v, shfl_row_shr_aff(v, id, s));
+  for (int s = 1; s <= 8; s <<= 1) v = select_aff(rl >= s, compose(v, shfl_row_shr_aff(v, id, s)), v);
   const int row = (int)(lane_id() >> 4);
   E r0 = readlane_aff(v, 15), r1 = readlane_aff(v, 31), r2 = readlane_aff(v, 47);
   E p1 = r0;

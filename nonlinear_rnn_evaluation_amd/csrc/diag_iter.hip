@@ -137,6 +137,12 @@ __device__ __forceinline__ void store_n(float* __restrict__ row, int tb, int T, 
   }
 }
 
+// The bounded iteration's projection of one new state component: NaN keeps the current
+// value, anything else is clipped to [-lim, lim] (infinities included).
+__device__ __forceinline__ float project_state(float v, float cur, float lim) {
+  return v != v ? cur : fminf(fmaxf(v, -lim), lim);
+}
+
 // Apply an affine map to a state increment.
 __device__ __forceinline__ float apply(const Aff1& e, float d) { return fmaf(e.a, d, e.b); }
 __device__ __forceinline__ float2 apply(const Aff2& e, float2 d) {
@@ -243,12 +249,13 @@ __device__ typename DeltaOf<typename CellT::E>::T lookback_window(uint64_t* slot
       const int p = __ffsll((long long)pm) - 1;
       const uint64_t before = p == 0 ? 0ull : ((1ull << p) - 1ull);
       if ((bad & before) == 0) {
+        // lane 0 ends with e_0 o ... o e_{p-1}; lanes at or past p hold nothing and are never
+        // composed in (no identity products: see select_aff)
         E x = lane < p ? e : idn;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
           E o = shfl_down_e(x, off);
-          if (lane + off >= 64) o = idn;
-          x = compose(x, o);
+          if (lane + off < p) x = compose(x, o);
         }
         const E x0 = readlane_aff(x, 0);
         const Dl din = apply(x0, readlane_d(pre, p));
@@ -440,24 +447,36 @@ __device__ __forceinline__ typename DeltaOf<typename DiagCell<CELL>::E>::T diag_
     Dl dl = wave_shr1(dout, dw);   // increment entering this thread's first step
 
     // ---- fix-up: d_t = J_t d_{t-1} + r_t along the thread's steps, s <- s + d ----
+    // Bounded iteration: the new iterate is projected onto the box every reachable state
+    // lies in (a component the step made NaN keeps its current value).  GRU: h' is a
+    // convex combination of tanh(.) and h, so |h_t| <= max(1, |h0|).  LSTM: |h_t| < 1 and
+    // |c_t| < |c0| + t (c' = f c + i g, 0 < f, i < 1, |g| < 1).
+    const bool bounded = a.bounded != 0;
     if constexpr (CELL == PNR_CELL_GRU_DIAG) {
+      const float hb = bounded ? fmaxf(1.f, a.h0 ? fabsf(a.h0[(size_t)b * S + d]) : 0.f) : 0.f;
       float out[N];
 #pragma unroll
       for (int i = 0; i < N; ++i) {
         dl = apply(e[i], dl);
         out[i] = hc[0][i] + dl;
+        if (bounded) out[i] = project_state(out[i], hc[0][i], hb);
       }
       float* orow = v.Hnext + ((size_t)b * S + d) * T;
       store_n(orow, tb, T, vec, N, out);
       // the tile's last state is the next tile's halo, read by another block next pass
       if (!walk && tid == PNR_BLOCK - 1 && tb + N <= T) coherent_store(orow + tb + N - 1, out[N - 1]);
     } else {
+      const float c0b = bounded && a.h0 ? fabsf(a.h0[(size_t)b * S + d]) : 0.f;
       float oc[N], oh[N];
 #pragma unroll
       for (int i = 0; i < N; ++i) {
         dl = apply(e[i], dl);
         oc[i] = hc[0][i] + dl.x;
         oh[i] = hc[1][i] + dl.y;
+        if (bounded) {
+          oc[i] = project_state(oc[i], hc[0][i], c0b + (float)(tb + i + 1));
+          oh[i] = project_state(oh[i], hc[1][i], 1.f);
+        }
       }
       float* crow = v.Hnext + ((size_t)b * S + d) * T;
       float* hrow = v.Hnext + ((size_t)b * S + D + d) * T;

@@ -81,6 +81,7 @@ struct DiagLoopArgs {
   int max_iters, jac_every, jac_mode;
   double tol;
   double refresh_ratio;   // >= 0: adaptive Jacobian refresh (jac_every = largest age); < 0: fixed schedule
+  int bounded;            // 1: each new iterate projected onto the reachable-state box
 };
 
 // Damped (quasi-ELK) Newton loop for GRU_DIAG and LSTM_DIAG (G gates, S = D or 2D state

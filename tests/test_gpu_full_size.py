@@ -30,7 +30,8 @@ def _check(name, mode):
     print(f"# full-size parity: {name} mode {mode}", flush=True)
     res = pnr.evaluate(w.cell, d["W"], d["U"], d["x"], b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"],
                        max_iters=w.max_iters, tol=w.tol, jac_mode=mode, jac_every=w.jac_every,
-                       damping=w.damping, chunk_len=w.chunk_len, refresh_ratio=w.refresh_ratio)
+                       damping=w.damping, chunk_len=w.chunk_len, refresh_ratio=w.refresh_ratio,
+                       bounded=w.bounded)
     assert res["status"] == pnr.OK, (name, res["status"], res["residual"])
     assert res["residual"] <= w.tol
     if w.chunk_len is None:
@@ -56,14 +57,19 @@ def _check(name, mode):
     else:
         ref = O.sequential(w.cell, W, U, bx, bh, x, h0)
         got = h.double().cpu().numpy()
-    bar = 1e-9 if w.state_dtype == WL.DT_F64 else 1e-4
+    # the stiff variant is held to the 1e-2 ceiling of the bf16-input configurations: its
+    # fp32 conditioning floor (fp32 sequential evaluation against fp64) is ~4e-4
+    bar = 1e-9 if w.state_dtype == WL.DT_F64 else (1e-2 if w.u_scale != 1.0 else 1e-4)
     err = np.abs(got - ref).max()
     print(f"#   iters {res['iters']} residual {res['residual']:.3e} max-abs {err:.3e}", flush=True)
+    if w.u_scale != 1.0:
+        ref32 = O.sequential(w.cell, Wc, Uc, bxc, bhc, x, h0c, dtype=np.float32)
+        print(f"#   fp32 sequential floor {np.abs(ref32.astype(np.float64) - ref).max():.3e}", flush=True)
     assert err <= bar, (name, mode, err)
 
 
 CASES = [(name, mode) for name in WL.WORKLOAD_ORDER + ["gru_diag_long_elk", "lstm_diag_long_chunked",
-                                                       "lstm_diag_long_adaptive"]
+                                                       "lstm_diag_long_adaptive", "lstm_diag_long_stiff_bounded"]
          for mode in WL.get_workload(name).jac_modes]
 
 
