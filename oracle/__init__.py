@@ -35,6 +35,9 @@ What it computes (sources are the five pages on this method):
   reachable state lies in (``state_bounds``): a safeguard of this oracle's readings against
   the divergence of undamped Newton ("Towards Scalable and Stable Parallelization of
   Nonlinear RNNs", summary page, "Problem").
+* ``newton_dense(..., jac_rank=r)`` -- the dense GRU with a low-rank approximation of its
+  Jacobian (ParaRNN overview, "Newton's Iteration": low-rank approximations among the
+  approximate-Newton strategies; ``oracle.lowrank``).
 * ``newton_chunked`` -- the sequence evaluated chunk by chunk, each chunk from the
   previous chunk's last state (ParaRNN overview, "Experimental Results": chunking to
   bound the memory of long sequences).
@@ -52,6 +55,7 @@ from .newton import (newton_dense, STATUS_OK, STATUS_NOT_CONVERGED, STATUS_NONFI
 from .scan import scan_loop, scan_doubling, compose
 from .damped import lm_step_dense, lm_step_kalman, damped_step
 from .chunked import newton_chunked
+from .lowrank import lowrank_matrix, truncated
 from .backward import bptt, cell_vjp
 
 __all__ = [
@@ -62,5 +66,5 @@ __all__ = [
     "state_bounds", "project_states",
     "scan_loop", "scan_doubling", "compose",
     "lm_step_dense", "lm_step_kalman", "damped_step",
-    "newton_chunked", "bptt", "cell_vjp",
+    "newton_chunked", "bptt", "cell_vjp", "lowrank_matrix", "truncated",
 ]

@@ -101,8 +101,12 @@ def cell_step(cell: int, U, b_h, s, gx):
     raise ValueError(f"unknown cell {cell}")
 
 
-def cell_jacobian(cell: int, U, b_h, s, gx):
-    """Exact Jacobian d f(s, gx) / d s as dense [N, S, S] (row = output component)."""
+def cell_jacobian(cell: int, U, b_h, s, gx, U_jac=None):
+    """Exact Jacobian d f(s, gx) / d s as dense [N, S, S] (row = output component).
+
+    U_jac (dense GRU only): take the Jacobian's matrix factors from U_jac instead of U,
+    with the gates still computed from U -- the low-rank approximation of
+    ``oracle.lowrank``; U_jac = U is the exact Jacobian."""
     N, S = s.shape
     one = s.dtype.type(1)
     if cell in (CELL_GRU, CELL_GRU_DIAG):
@@ -114,7 +118,8 @@ def cell_jacobian(cell: int, U, b_h, s, gx):
         cz = (s - n) * z * (one - z)
         cn = (one - z) * (one - n * n)
         if cell == CELL_GRU:
-            Ur, Uz, Un = U[0:D], U[D:2 * D], U[2 * D:3 * D]
+            Um = U if U_jac is None else np.asarray(U_jac, dtype=s.dtype)
+            Ur, Uz, Un = Um[0:D], Um[D:2 * D], Um[2 * D:3 * D]
         else:
             Ur, Uz, Un = np.diag(U[0]), np.diag(U[1]), np.diag(U[2])
         J = (cz[:, :, None] * Uz[None]

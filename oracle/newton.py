@@ -39,6 +39,10 @@ Options:
   true states lie inside the box, so the projection never moves them: the exact-prefix
   property below still holds, and so does the fixed point.
 
+* jac_rank = r (dense GRU): the Jacobian's recurrent-matrix factors are the rank-r
+  truncations of ``oracle.lowrank`` (with jac_mode FULL; r = D is Newton, r = 0 the
+  diagonal approximation).
+
 Readings where the pages are silent: initial guess H = 0; stop when the max-abs
 residual (NaN counted as +inf) is <= tol, testing *before* each update so the
 returned iterate is the one whose residual was checked; one shared loop for all
@@ -50,6 +54,7 @@ import numpy as np
 
 from .cells import CELL_LSTM_DIAG, approx_jacobian, cell_jacobian, cell_step
 from .damped import damped_step
+from .lowrank import lowrank_matrix
 from .scan import scan_loop
 from .sequential import project
 
@@ -103,7 +108,7 @@ def _previous_states(h0, H):
 
 def newton_dense(cell: int, W, U, b_x, b_h, x, h0, max_iters: int, tol: float,
                  jac_mode: int, jac_every: int = 1, gx=None, solver: str = "dense",
-                 damping: float = 0.0, refresh_ratio=None, bounded: bool = False):
+                 damping: float = 0.0, refresh_ratio=None, bounded: bool = False, jac_rank=None):
     """Returns dict(states [B,T,S], iters, status, rhos[list], jac_evals, refreshes[list
     of the iterations that recomputed the Jacobian]).
 
@@ -126,6 +131,7 @@ def newton_dense(cell: int, W, U, b_x, b_h, x, h0, max_iters: int, tol: float,
         gx = project(W, x, b_x)
     B, T, GD = gx.shape
     S = h0.shape[1]
+    U_jac = None if jac_rank is None else lowrank_matrix(cell, U, jac_rank)
     H = np.zeros((B, T, S))
     rhos = []
     Jhat = None
@@ -151,7 +157,7 @@ def newton_dense(cell: int, W, U, b_x, b_h, x, h0, max_iters: int, tol: float,
         slow = refresh_ratio is not None and k >= 2 and rhos[k - 1] > refresh_ratio * rhos[k - 2]
         if aged or slow:
             refreshes.append(k)
-            J = cell_jacobian(cell, U, b_h, P.reshape(B * T, S), gx.reshape(B * T, GD))
+            J = cell_jacobian(cell, U, b_h, P.reshape(B * T, S), gx.reshape(B * T, GD), U_jac=U_jac)
             Jhat = approx_jacobian(J, jac_mode).reshape(B, T, S, S)
             jac_evals += 1
         Hn = np.empty_like(H)
