@@ -33,7 +33,7 @@ UNIT = "timesteps*batch/s"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0, "f64": 78.6}   # dense, published
 PRIMARY = "lstm_diag_long"
-DEFAULT_OTHERS = ("tiny_gru,gru_quasi,gru_full,gru_diag_long,lstm_diag_long_chunked,lstm_diag_long_stiff,"
+DEFAULT_OTHERS = ("tiny_gru,gru_quasi,gru_full,gru_full_rank4,gru_full_rank8,gru_diag_long,lstm_diag_long_chunked,lstm_diag_long_stiff,"
                   "lstm_diag_long_stiff_bounded,"
                   "gru_diag_long_elk,gru_quasi_elk,gru_quasi_bwd,gru_diag_long_bwd,lstm_diag_long_bwd,"
                   "lstm_diag_long_chunked_bwd,lstm_diag_long_adaptive")
@@ -204,7 +204,7 @@ def run_workload(name, steps, warmup, mode=None, with_cpu=True, cpu_budget=12.0,
         return pnr.evaluate(w.cell, d["W"], d["U"], d["x"], b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"],
                             max_iters=w.max_iters, tol=w.tol, jac_mode=mode, jac_every=w.jac_every,
                             workspace=ws, h_out=out, damping=w.damping, chunk_len=w.chunk_len,
-                            refresh_ratio=w.refresh_ratio, bounded=w.bounded)
+                            refresh_ratio=w.refresh_ratio, bounded=w.bounded, jac_rank=w.jac_rank)
 
     first = call()
     ws, out = first["workspace"], first["h"]

@@ -197,6 +197,27 @@ int pnr_eval_static(const pnr_cell* cell, const pnr_params* params, const void* 
 int pnr_eval_bounded(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0,
                      void* h_out, int max_iters, double tol, int jac_mode);
 
+/*
+ * pnr_eval with a low-rank approximation of the Jacobian, for the GRU with a dense
+ * recurrent matrix (PNR_CELL_GRU; D <= 32, the sizes its dense Jacobian supports).  The
+ * ParaRNN overview page ("Technical Implementation / Newton's Iteration") names low-rank
+ * approximations among the approximate-Newton strategies, with no form; this library's
+ * reading keeps the exact Jacobian's structure
+ *     J_t = diag(z) + diag(al) U_z + diag(be) U_r + diag(ga) U_n
+ * and replaces, in the Jacobian only, each gate block U_g by its best rank-`rank`
+ * approximation (truncated singular value decomposition; computed on the device, once
+ * per call, from the Gram matrix U_g^T U_g by the cyclic Jacobi eigenvalue method), with
+ * U_g's own diagonal restored so that the Jacobian's diagonal stays exact.  The gates and
+ * residuals still use U.  rank = D is pnr_eval's dense Jacobian (Newton); rank = 0 its
+ * diagonal (quasi-Newton).  rank must be in [0, D] (PNR_E_INVALID).  Other arguments and
+ * results as pnr_eval with jac_mode = PNR_JAC_FULL (cell->jac_every honoured).
+ * Workspace: pnr_workspace_bytes_lowrank() bytes (pnr_workspace_bytes(cell, FULL) plus the
+ * approximated factors, 3 D^2 state elements); 0 = invalid or unsupported request.
+ */
+size_t pnr_workspace_bytes_lowrank(const pnr_cell* cell, int rank);
+int pnr_eval_lowrank(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0,
+                     void* h_out, int max_iters, double tol, int rank);
+
 /* Newton updates applied by the calling thread's last pnr_eval (-1 if it failed before). */
 int pnr_iters_used(void);
 

@@ -314,9 +314,11 @@ int check_eval_args(const pnr_cell* cell, const pnr_params* params, const void* 
 // The evaluation proper, on the scratch memory `ws` (at least make_layout(...).total bytes,
 // 256-byte aligned; checked by the callers).
 int eval_impl(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, void* h_out,
-              int max_iters, double tol, int jac_mode, double refresh_ratio, int bounded, char* ws) {
+              int max_iters, double tol, int jac_mode, double refresh_ratio, int bounded, int jac_rank, char* ws) {
   int rc = 0;
   const Layout l = make_layout(cell, jac_mode);
+  // low-rank Jacobian (dense GRU): its matrix factors follow the layout
+  void* Uh = jac_rank >= 0 ? ws + l.total : nullptr;
   if (cell->T == 0) {
     g_last.iters = 0;
     g_last.residual = 0.0;
@@ -399,6 +401,10 @@ int eval_impl(const pnr_cell* cell, const pnr_params* params, const void* x, con
     DenseLoopArgs<float> a{};
     a.gx = static_cast<const float*>(gx);
     a.U = static_cast<const float*>(params->U);
+    if (Uh) {
+      PNR_HIP(launch_lowrank_matrix<float>(a.U, static_cast<float*>(Uh), D, jac_rank, st));
+      a.Uj = static_cast<const float*>(Uh);
+    }
     a.bh = static_cast<const float*>(params->b_h);
     a.h0 = static_cast<const float*>(h0);
     for (int i = 0; i < 4; ++i) a.H[i] = static_cast<float*>(H[i]);
@@ -430,6 +436,10 @@ int eval_impl(const pnr_cell* cell, const pnr_params* params, const void* x, con
     DenseLoopArgs<double> a{};
     a.gx = static_cast<const double*>(gx);
     a.U = static_cast<const double*>(params->U);
+    if (Uh) {
+      PNR_HIP(launch_lowrank_matrix<double>(a.U, static_cast<double*>(Uh), D, jac_rank, st));
+      a.Uj = static_cast<const double*>(Uh);
+    }
     a.bh = static_cast<const double*>(params->b_h);
     a.h0 = static_cast<const double*>(h0);
     for (int i = 0; i < 4; ++i) a.H[i] = static_cast<double*>(H[i]);
@@ -479,7 +489,7 @@ int eval_workspace(const pnr_cell* cell, const pnr_params* params, const void* x
   if ((uintptr_t)cell->workspace % 256) return fail(PNR_E_WORKSPACE, "workspace must be 256-byte aligned");
   if (cell->workspace_bytes < need)
     return fail(PNR_E_WORKSPACE, "workspace has %zu bytes, %zu required", cell->workspace_bytes, need);
-  return eval_impl(cell, params, x, h0, h_out, max_iters, tol, jac_mode, refresh_ratio, bounded,
+  return eval_impl(cell, params, x, h0, h_out, max_iters, tol, jac_mode, refresh_ratio, bounded, -1,
                    static_cast<char*>(cell->workspace));
 }
 }  // namespace
@@ -490,6 +500,42 @@ int pnr_eval(const pnr_cell* cell, const pnr_params* params, const void* x, cons
   g_prof.valid = false;
   g_prof.used = 0;
   return eval_workspace(cell, params, x, h0, h_out, max_iters, tol, jac_mode, -1.0, 0);
+}
+
+namespace {
+int validate_lowrank(const pnr_cell* c, int rank) {
+  int rc = validate(c, PNR_JAC_FULL);
+  if (rc) return rc;
+  if (c->kind != PNR_CELL_GRU)
+    return fail(PNR_E_UNSUPPORTED, "the low-rank Jacobian is defined for the GRU with a dense recurrent matrix");
+  if (rank < 0 || rank > c->D) return fail(PNR_E_INVALID, "rank must be in [0, D] (got %d, D = %d)", rank, c->D);
+  return 0;
+}
+size_t lowrank_total(const pnr_cell* c) {
+  return make_layout(c, PNR_JAC_FULL).total + align_up((size_t)3 * c->D * c->D * dsize(c->state_dtype));
+}
+}  // namespace
+
+size_t pnr_workspace_bytes_lowrank(const pnr_cell* cell, int rank) {
+  if (validate_lowrank(cell, rank) != 0) return 0;
+  return lowrank_total(cell);
+}
+
+int pnr_eval_lowrank(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, void* h_out,
+                     int max_iters, double tol, int rank) {
+  g_last.reset();
+  g_prof.valid = false;
+  g_prof.used = 0;
+  int rc = validate_lowrank(cell, rank);
+  if (rc) return rc;
+  if ((rc = check_eval_args(cell, params, x, h_out, max_iters, tol, PNR_JAC_FULL))) return rc;
+  const size_t need = lowrank_total(cell);
+  if (!cell->workspace) return fail(PNR_E_WORKSPACE, "workspace is NULL (%zu bytes required)", need);
+  if ((uintptr_t)cell->workspace % 256) return fail(PNR_E_WORKSPACE, "workspace must be 256-byte aligned");
+  if (cell->workspace_bytes < need)
+    return fail(PNR_E_WORKSPACE, "workspace has %zu bytes, %zu required", cell->workspace_bytes, need);
+  return eval_impl(cell, params, x, h0, h_out, max_iters, tol, PNR_JAC_FULL, -1.0, 0, rank,
+                   static_cast<char*>(cell->workspace));
 }
 
 int pnr_eval_bounded(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, void* h_out,
@@ -562,7 +608,7 @@ int pnr_eval_static(const pnr_cell* cell, const pnr_params* params, const void* 
   // measurement mode would create HIP events: it does not apply to this entry point
   const bool prof = g_prof.on;
   g_prof.on = false;
-  rc = eval_impl(cell, params, x, h0, h_out, max_iters, tol, jac_mode, -1.0, 0, ws);
+  rc = eval_impl(cell, params, x, h0, h_out, max_iters, tol, jac_mode, -1.0, 0, -1, ws);
   g_prof.on = prof;
   return rc;
 }

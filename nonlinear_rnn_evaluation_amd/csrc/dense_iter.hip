@@ -105,8 +105,10 @@ __device__ __forceinline__ double mul_add(double a, double b, double c) { return
 //   Fx   [2][parts][D] FULL: fix-up double buffer (also look-back scratch)
 //   Win  [WMAX][slot values]  look-back window
 //   Din  [D]         increment entering the tile
+//   UsJ  [D][3D]     FULL with a low-rank Jacobian: its matrix factors, transposed (the
+//                    Jacobian products read these, the gates still read Us)
 struct DenseLds {
-  int D, L, full, reuse, parts, wmax, ld, has_u;
+  int D, L, full, reuse, parts, wmax, ld, has_u, has_uj;
   __host__ __device__ size_t count() const {
     size_t n = (has_u ? (size_t)3 * D * D : 0) + 3 * D + (size_t)(L + 1) * ld * (reuse ? 2 : 1) + (size_t)L * D;
     if (full) {
@@ -116,6 +118,7 @@ struct DenseLds {
       n += (size_t)L * D + (size_t)2 * parts * D;
     }
     n += (size_t)wmax * dense_slot_values(D, full) + D;
+    if (has_uj) n += (size_t)3 * D * D;   // the Jacobian's own matrix (low-rank), transposed
     return n;
   }
 };
@@ -209,11 +212,14 @@ __global__ void __launch_bounds__(PNR_BLOCK) dense_newton_kernel(DenseLoopArgs<T
   Tt* Fx = Pin + (FULL ? (parts + 1) * D : 0);
   Tt* Win = Fx + (FULL ? 2 * parts * D : 0);
   Tt* Din = Win + WMAX * SV;
+  const bool own_uj = FULL && a.Uj != nullptr;
+  Tt* UsJ = own_uj ? Din + D : Us;
 
   if constexpr (HAS_U) {
     for (int idx = tid; idx < 3 * D * D; idx += PNR_BLOCK) {
       const int row = idx / D, k = idx - row * D;     // U[row][k] -> Ut[k][row]
       Us[(size_t)k * 3 * D + row] = a.U[idx];
+      if (own_uj) UsJ[(size_t)k * 3 * D + row] = a.Uj[idx];
     }
   }
   for (int idx = tid; idx < 3 * D; idx += PNR_BLOCK) Bh[idx] = a.bh ? a.bh[idx] : Tt(0);
@@ -462,7 +468,7 @@ __global__ void __launch_bounds__(PNR_BLOCK) dense_newton_kernel(DenseLoopArgs<T
 #pragma unroll
                 for (int kk = 0; kk < DM; ++kk) {
                   if (kk < D) {
-                    const Tt* u = Us + (size_t)kk * 3 * D;
+                    const Tt* u = UsJ + (size_t)kk * 3 * D;
                     ur = mul_add(u[m], col[kk], ur);
                     uz = mul_add(u[D + m], col[kk], uz);
                     un = mul_add(u[2 * D + m], col[kk], un);
@@ -655,7 +661,7 @@ __global__ void __launch_bounds__(PNR_BLOCK) dense_newton_kernel(DenseLoopArgs<T
             const Tt* dv = cb + part * D;
             Tt ur = 0, uz = 0, un = 0;
             for (int kk = 0; kk < D; ++kk) {
-              const Tt* u = Us + (size_t)kk * 3 * D;
+              const Tt* u = UsJ + (size_t)kk * 3 * D;
               ur = mul_add(u[jl], dv[kk], ur);
               uz = mul_add(u[D + jl], dv[kk], uz);
               un = mul_add(u[2 * D + jl], dv[kk], un);
@@ -728,10 +734,10 @@ int dense_slot_words(int D, int full, int is_f64) {
   return dense_slot_values(D, full) * (is_f64 ? 2 : 1);
 }
 
-size_t dense_lds_bytes(int D, int full, int is_f64, int reuse) {
+size_t dense_lds_bytes(int D, int full, int is_f64, int reuse, int lowrank) {
   const int es = is_f64 ? 8 : 4;
   DenseLds l{D, full ? dense_full_parts(D) * 8 : 64, full, reuse, dense_parts(D, full),
-             dense_window(D, full != 0, es), D, 1};
+             dense_window(D, full != 0, es), D, 1, full && lowrank};
   return l.count() * es;
 }
 
@@ -744,7 +750,7 @@ static int dense_capacity_t(int num_cu, size_t lds) {
 
 template <typename Tt, int DM, bool FULL, bool MF>
 static hipError_t launch_t(const DenseLoopArgs<Tt>& a, int num_cu, hipStream_t st) {
-  const size_t lds = dense_lds_bytes(a.D, FULL, sizeof(Tt) == 8, a.nbuf > 2);
+  const size_t lds = dense_lds_bytes(a.D, FULL, sizeof(Tt) == 8, a.nbuf > 2, a.Uj != nullptr);
   const int cap = dense_capacity_t<Tt, DM, FULL, MF>(num_cu, lds);
   if (cap < 1) return hipErrorInvalidConfiguration;
   int grid = a.n_tiles < cap ? a.n_tiles : cap;

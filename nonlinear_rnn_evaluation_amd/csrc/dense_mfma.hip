@@ -940,15 +940,17 @@ __global__ void __launch_bounds__(PNR_BLOCK) dense_full_mfma_kernel(DenseLoopArg
   for (int i = tid; i < 3 * D; i += PNR_BLOCK) Bh[i] = a.bh ? a.bh[i] : 0.f;
   // U in registers: MFMA B fragments for the recurrent product, and the entries each
   // lane needs to form J^T (aggregate pass) and J (fix-up pass) operands
+  // (the Jacobian's entries come from a.Uj when a low-rank approximation is in use)
   float uf[3][D / 4], ubT[3][4], ubN[3][4];
+  const float* Ujm = a.Uj ? a.Uj : a.U;
 #pragma unroll
   for (int g = 0; g < 3; ++g) {
 #pragma unroll
     for (int kk = 0; kk < D / 4; ++kk) uf[g][kk] = a.U[(size_t)(g * D + m) * D + 4 * kk + q];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ubT[g][i] = a.U[(size_t)(g * D + 4 * q + i) * D + m];   // U_g[4q+i][m]
-      ubN[g][i] = a.U[(size_t)(g * D + m) * D + 4 * q + i];   // U_g[m][4q+i]
+      ubT[g][i] = Ujm[(size_t)(g * D + 4 * q + i) * D + m];   // U_g[4q+i][m]
+      ubN[g][i] = Ujm[(size_t)(g * D + m) * D + 4 * q + i];   // U_g[m][4q+i]
     }
   }
   __syncthreads();

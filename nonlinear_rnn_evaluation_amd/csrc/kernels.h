@@ -182,6 +182,7 @@ struct DenseLoopArgs {
   Tt* gx_out;
   int D_in;
   const Tt* U;         // [3D][D]
+  const Tt* Uj;        // the Jacobian's matrix factors [3D][D] (low-rank approximation); nullptr: U
   const Tt* bh;        // [3D] or nullptr
   const Tt* h0;        // [B][D] or nullptr
   Tt* H[4];            // state buffers [B][T][D] (dense_state_buffers of them)
@@ -199,12 +200,17 @@ struct DenseLoopArgs {
   double tol;
 };
 
+// U^ [3D][D] of the low-rank Jacobian: every gate block of U truncated to rank r (its r
+// leading singular directions), its diagonal reset to U's own (D <= 32; r >= D copies U).
+template <typename Tt>
+hipError_t launch_lowrank_matrix(const Tt* U, Tt* Uh, int D, int rank, hipStream_t st);
+
 // Tile length, look-back slot words per tile and number of [B][T][D] state buffers for
 // the dense GRU path.
 int dense_state_buffers(int D, int full, int is_f64, int reuse);
 int dense_tile_len(int D, int full, int is_f64);
 int dense_slot_words(int D, int full, int is_f64);
-size_t dense_lds_bytes(int D, int full, int is_f64, int reuse);
+size_t dense_lds_bytes(int D, int full, int is_f64, int reuse, int lowrank = 0);
 int dense_supported(int D, int full, int is_f64);
 hipError_t launch_dense_newton_f32(const DenseLoopArgs<float>& a, int full, int num_cu, hipStream_t st);
 // MFMA kernels (fp32; diagonal Jacobian with D in {16, 32, 64}, dense Jacobian with D = 16)

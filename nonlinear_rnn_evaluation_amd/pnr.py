@@ -78,6 +78,11 @@ def load() -> ctypes.CDLL:
     lib.pnr_workspace_bytes_backward.restype = ctypes.c_size_t
     lib.pnr_backward.argtypes = [P(PnrCell), P(PnrParams)] + [ctypes.c_void_p] * 10
     lib.pnr_backward.restype = ctypes.c_int
+    lib.pnr_workspace_bytes_lowrank.argtypes = [P(PnrCell), ctypes.c_int]
+    lib.pnr_workspace_bytes_lowrank.restype = ctypes.c_size_t
+    lib.pnr_eval_lowrank.argtypes = [P(PnrCell), P(PnrParams), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_int, ctypes.c_double, ctypes.c_int]
+    lib.pnr_eval_lowrank.restype = ctypes.c_int
     lib.pnr_eval_bounded.argtypes = [P(PnrCell), P(PnrParams), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_int, ctypes.c_double, ctypes.c_int]
     lib.pnr_eval_bounded.restype = ctypes.c_int
@@ -164,6 +169,15 @@ def pnr_workspace_bytes(cell: PnrCell, jac_mode: int) -> int:
 def pnr_eval(cell: PnrCell, params: PnrParams, x: int, h0: Optional[int], h_out: int, max_iters: int,
              tol: float, jac_mode: int) -> int:
     return load().pnr_eval(ctypes.byref(cell), ctypes.byref(params), x, h0, h_out, max_iters, tol, jac_mode)
+
+
+def pnr_workspace_bytes_lowrank(cell: PnrCell, rank: int) -> int:
+    return load().pnr_workspace_bytes_lowrank(ctypes.byref(cell), rank)
+
+
+def pnr_eval_lowrank(cell: PnrCell, params: PnrParams, x: int, h0: Optional[int], h_out: int, max_iters: int,
+                     tol: float, rank: int) -> int:
+    return load().pnr_eval_lowrank(ctypes.byref(cell), ctypes.byref(params), x, h0, h_out, max_iters, tol, rank)
 
 
 def pnr_eval_bounded(cell: PnrCell, params: PnrParams, x: int, h0: Optional[int], h_out: int, max_iters: int,
@@ -275,17 +289,21 @@ def evaluate(kind: int, W: torch.Tensor, U: torch.Tensor, x: torch.Tensor, *, b_
              jac_every: int = 1, h_out: Optional[torch.Tensor] = None,
              workspace: Optional[torch.Tensor] = None, damping: Optional[float] = None,
              chunk_len: Optional[int] = None, refresh_ratio: Optional[float] = None,
-             static_scratch: bool = False, bounded: bool = False) -> dict:
+             static_scratch: bool = False, bounded: bool = False, jac_rank: Optional[int] = None) -> dict:
     """Run pnr_eval (or pnr_eval_damped when `damping` is given, pnr_eval_chunked when
     `chunk_len` is given, pnr_eval_adaptive when `refresh_ratio` is given, pnr_eval_static
     -- no workspace; the library's static device scratch -- when `static_scratch`,
-    pnr_eval_bounded when `bounded`) on device tensors; returns dict(h=[B,T,S], status,
+    pnr_eval_bounded when `bounded`, pnr_eval_lowrank when `jac_rank` is given -- the
+    jac_mode argument is then FULL) on device tensors; returns dict(h=[B,T,S], status,
     iters, residual, history)."""
     if refresh_ratio is not None and (damping is not None or chunk_len is not None):
         raise ValueError("refresh_ratio combines with neither damping nor chunk_len")
     if static_scratch and (refresh_ratio is not None or damping is not None or chunk_len is not None
                            or workspace is not None):
         raise ValueError("static_scratch is pnr_eval's variant: no damping, chunking, refresh ratio or workspace")
+    if jac_rank is not None and (refresh_ratio is not None or damping is not None or chunk_len is not None
+                                 or static_scratch or bounded):
+        raise ValueError("jac_rank is pnr_eval's variant: no damping, chunking, refresh ratio, bounds or static scratch")
     if bounded and (refresh_ratio is not None or damping is not None or chunk_len is not None or static_scratch):
         raise ValueError("bounded is pnr_eval's variant: no damping, chunking, refresh ratio or static scratch")
     B, T, D_in = x.shape
@@ -306,6 +324,8 @@ def evaluate(kind: int, W: torch.Tensor, U: torch.Tensor, x: torch.Tensor, *, b_
     cell = make_cell(kind, D, D_in, T, B, xdt, sdt, jac_every, _stream())
     if static_scratch:
         need = 0
+    elif jac_rank is not None:
+        need = pnr_workspace_bytes_lowrank(cell, jac_rank)
     elif chunk_len is not None:
         need = pnr_workspace_bytes_chunked(cell, jac_mode, damping or 0.0, chunk_len)
     elif damping is None:
@@ -323,7 +343,9 @@ def evaluate(kind: int, W: torch.Tensor, U: torch.Tensor, x: torch.Tensor, *, b_
         h_out = torch.empty(B, T, S, dtype=U.dtype, device=x.device)
     out = _arg(h_out, "h_out", sd, (B, T, S))
     params = PnrParams(ptrs["W"], ptrs["U"], ptrs["b_x"], ptrs["b_h"])
-    if bounded:
+    if jac_rank is not None:
+        rc = pnr_eval_lowrank(cell, params, ptrs["x"], ptrs["h0"], out, max_iters, tol, jac_rank)
+    elif bounded:
         rc = pnr_eval_bounded(cell, params, ptrs["x"], ptrs["h0"], out, max_iters, tol, jac_mode)
     elif static_scratch:
         rc = pnr_eval_static(cell, params, ptrs["x"], ptrs["h0"], out, max_iters, tol, jac_mode)

@@ -83,6 +83,7 @@ class Workload:
     backward: bool = False            # the measured step is the backward pass at the evaluated states
     refresh_ratio: Optional[float] = None   # set: adaptive Jacobian refresh with this ratio
     bounded: bool = False             # iterates projected onto the reachable-state box
+    jac_rank: Optional[int] = None    # set (dense GRU): low-rank approximation of the Jacobian
 
     @property
     def G(self) -> int:
@@ -105,6 +106,7 @@ class Workload:
             **({"pass": "backward"} if self.backward else {}),
             **({"refresh_ratio": self.refresh_ratio} if self.refresh_ratio is not None else {}),
             **({"bounded": True} if self.bounded else {}),
+            **({"jac_rank": self.jac_rank} if self.jac_rank is not None else {}),
             **({"u_scale": self.u_scale} if self.u_scale != 1.0 else {}),
         }
 
@@ -156,6 +158,9 @@ def named_workloads() -> dict:
     # before last shrank the residual by less than 0.3, at most every 4 updates
     w["lstm_diag_long_adaptive"] = dataclasses.replace(w["lstm_diag_long"], name="lstm_diag_long_adaptive",
                                                        jac_every=4, refresh_ratio=0.3)
+    # the dense-Jacobian GRU with a low-rank approximation of its Jacobian (rank 4 and 8 of 16)
+    for r in (4, 8):
+        w[f"gru_full_rank{r}"] = dataclasses.replace(w["gru_full"], name=f"gru_full_rank{r}", jac_rank=r)
     # the stiff LSTM with the bounded iteration: the exact 2x2 Jacobian taken at every
     # iteration (with reuse every 2, 17 of 64 sampled channels were not converged after 400
     # iterations in a CPU study), each iterate projected onto the reachable-state box.  In
