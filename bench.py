@@ -35,7 +35,7 @@ MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0, "f64": 78.6}   # dense, publis
 PRIMARY = "lstm_diag_long"
 DEFAULT_OTHERS = ("tiny_gru,gru_quasi,gru_full,gru_full_rank4,gru_full_rank8,gru_diag_long,lstm_diag_long_chunked,lstm_diag_long_stiff,"
                   "lstm_diag_long_stiff_bounded,"
-                  "gru_diag_long_elk,gru_quasi_elk,gru_quasi_bwd,gru_diag_long_bwd,lstm_diag_long_bwd,"
+                  "gru_diag_long_elk,lstm_diag_long_elk,gru_quasi_elk,gru_quasi_bwd,gru_diag_long_bwd,lstm_diag_long_bwd,"
                   "lstm_diag_long_chunked_bwd,lstm_diag_long_adaptive")
 CSRC = "nonlinear_rnn_evaluation_amd/csrc/"
 
@@ -46,6 +46,8 @@ def newton_kernel(w, mode):
     if w.damping is not None and w.cell == WL.CELL_GRU:
         return ("quasi-ELK loop (recurrent GEMM, cell, filter and smoother scans; one read-back per iteration)",
                 CSRC + "dense_elk.hip")
+    if w.damping is not None and w.cell == WL.CELL_LSTM_DIAG and mode == WL.JAC_FULL:
+        return "pnr::elk2_lstm_kernel", CSRC + "elk2.hip"
     if w.damping is not None:
         return "pnr::elk_diag_kernel", CSRC + "diag_iter.hip"
     if w.cell in (WL.CELL_GRU_DIAG, WL.CELL_LSTM_DIAG):
@@ -86,17 +88,20 @@ def dense_damped_iteration_bytes(w, k, resid=False):
     return w.B * w.T * w.D * (64 if resid else 112)
 
 
-def damped_iteration_bytes(w, k, resid=False):
-    """Algorithmic HBM bytes of one pass of the damped (quasi-ELK) loop: the forward sweep
-    reads the gate pre-activations (G fp32 per channel and step) and the current iterate
-    (4 B per state element; not at k=0) and writes the smoother's gain and offset (8 B per
-    state element); the backward sweep reads them back (8 B) and writes the next iterate
+def damped_iteration_bytes(w, k, resid=False, mode=None):
+    """Algorithmic HBM bytes of one pass of the damped (ELK / quasi-ELK) loop: the forward
+    sweep reads the gate pre-activations (G fp32 per channel and step) and the current
+    iterate (4 B per state element; not at k=0) and writes the smoother's gain and offset
+    (8 B per state element; 12 B for the LSTM's full 2x2 block: a 2x2 gain and a 2-vector
+    offset per channel); the backward sweep reads them back and writes the next iterate
     (4 B).  The residual-only pass runs the forward sweep's reads only."""
+    from nonlinear_rnn_evaluation_amd import workloads as WL
     n_bt = w.B * w.T
     gx = n_bt * w.G * w.D * 4
     h = n_bt * w.S * 4
     cur = h if k > 0 else 0
-    return gx + cur if resid else gx + cur + 5 * h
+    planes = 3 if (w.cell == WL.CELL_LSTM_DIAG and mode == WL.JAC_FULL) else 2
+    return gx + cur if resid else gx + cur + (2 * planes + 1) * h
 
 
 def chunk_iterations(history, w, n_chunks):
@@ -247,8 +252,12 @@ def run_workload(name, steps, warmup, mode=None, with_cpu=True, cpu_budget=12.0,
             ro = it == w.max_iters
             bytes_call += sum(iteration_bytes(wc, k, it, resid=(ro and k == it)) for k in range(it + 1))
     elif w.damping is not None:
-        fn = dense_damped_iteration_bytes if w.cell == WL.CELL_GRU else damped_iteration_bytes
-        bytes_call = sum(fn(w, k, resid=(resid_last and k == passes - 1)) for k in range(passes))
+        if w.cell == WL.CELL_GRU:
+            bytes_call = sum(dense_damped_iteration_bytes(w, k, resid=(resid_last and k == passes - 1))
+                             for k in range(passes))
+        else:
+            bytes_call = sum(damped_iteration_bytes(w, k, resid=(resid_last and k == passes - 1), mode=mode)
+                             for k in range(passes))
     else:
         refr = refresh_points(w, last["history"], passes)
         bytes_call = sum(iteration_bytes(w, k, iters, resid=(resid_last and k == passes - 1), refreshes=refr)

@@ -619,10 +619,10 @@ int validate_damped(const pnr_cell* c, int jac_mode) {
   int rc = validate(c, jac_mode);
   if (rc) return rc;
   if (!(c->kind == PNR_CELL_GRU_DIAG && (jac_mode == PNR_JAC_FULL || jac_mode == PNR_JAC_DIAG)) &&
-      !(c->kind == PNR_CELL_LSTM_DIAG && jac_mode == PNR_JAC_DIAG) &&
+      !(c->kind == PNR_CELL_LSTM_DIAG && (jac_mode == PNR_JAC_FULL || jac_mode == PNR_JAC_DIAG)) &&
       !(c->kind == PNR_CELL_GRU && jac_mode == PNR_JAC_DIAG && c->state_dtype == PNR_F32))
     return fail(PNR_E_UNSUPPORTED,
-                "the damped step is implemented for GRU_DIAG (full or diagonal Jacobian), LSTM_DIAG and the fp32 "
+                "the damped step is implemented for GRU_DIAG and LSTM_DIAG (full or diagonal Jacobian) and the fp32 "
                 "GRU (diagonal Jacobian)");
   if (c->jac_every != 1) return fail(PNR_E_UNSUPPORTED, "the damped step needs jac_every = 1");
   return 0;
@@ -655,15 +655,18 @@ DenseElkLayout make_dense_elk_layout(const pnr_cell* c) {
 }
 // pnr_eval's layout, plus two per-step planes of the smoother (gain, offset) per state component
 size_t damped_planes_offset(const Layout& l) { return l.total; }
-size_t damped_total(const pnr_cell* c, const Layout& l) {
-  return align_up(l.total + 2 * sizeof(float) * (size_t)c->B * c->T * states(c->kind, c->D));
+// the smoother's per-step gain and offset: one plane each per state component, or for the
+// LSTM's full 2x2 block (ELK proper) four gain planes and two offset planes per channel
+size_t damped_total(const pnr_cell* c, const Layout& l, int jac_mode) {
+  const size_t per = c->kind == PNR_CELL_LSTM_DIAG && jac_mode == PNR_JAC_FULL ? 3 : 2;
+  return align_up(l.total + per * sizeof(float) * (size_t)c->B * c->T * states(c->kind, c->D));
 }
 }  // namespace
 
 size_t pnr_workspace_bytes_damped(const pnr_cell* cell, int jac_mode) {
   if (validate_damped(cell, jac_mode) != 0) return 0;
   if (cell->kind == PNR_CELL_GRU) return make_dense_elk_layout(cell).total;
-  return damped_total(cell, make_layout(cell, jac_mode));
+  return damped_total(cell, make_layout(cell, jac_mode), jac_mode);
 }
 
 namespace {
@@ -753,7 +756,7 @@ int pnr_eval_damped(const pnr_cell* cell, const pnr_params* params, const void* 
   if (isnan(tol)) return fail(PNR_E_INVALID, "tol is NaN");
   if (!(damping > 0.0) || !(damping < 1e30)) return fail(PNR_E_INVALID, "damping must be finite and > 0");
   const Layout l = make_layout(cell, jac_mode);
-  const size_t need = cell->kind == PNR_CELL_GRU ? make_dense_elk_layout(cell).total : damped_total(cell, l);
+  const size_t need = cell->kind == PNR_CELL_GRU ? make_dense_elk_layout(cell).total : damped_total(cell, l, jac_mode);
   if (!cell->workspace) return fail(PNR_E_WORKSPACE, "workspace is NULL (%zu bytes required)", need);
   if ((uintptr_t)cell->workspace % 256) return fail(PNR_E_WORKSPACE, "workspace must be 256-byte aligned");
   if (cell->workspace_bytes < need)
@@ -793,8 +796,9 @@ int pnr_eval_damped(const pnr_cell* cell, const pnr_params* params, const void* 
   a.h0 = static_cast<const float*>(h0);
   a.H[0] = reinterpret_cast<float*>(ws + l.h[0]);
   a.H[1] = reinterpret_cast<float*>(ws + l.h[1]);
+  const bool elk2 = cell->kind == PNR_CELL_LSTM_DIAG && jac_mode == PNR_JAC_FULL;
   a.Gs = planes;
-  a.Es = planes + plane;
+  a.Es = planes + (elk2 ? 2 : 1) * plane;
   a.partials = reinterpret_cast<uint32_t*>(ws + l.partials);
   a.ctrl = ctrl;
   a.rho_hist = hist;
@@ -804,7 +808,10 @@ int pnr_eval_damped(const pnr_cell* cell, const pnr_params* params, const void* 
   a.max_iters = max_iters; a.jac_mode = jac_mode; a.tol = tol;
   a.lam = (float)damping;
   Mark m_newton = mark_begin(st);
-  PNR_HIP(launch_elk_diag(cell->kind, a, num_cu, st));
+  if (elk2)
+    PNR_HIP(launch_elk2_lstm(a, num_cu, st));
+  else
+    PNR_HIP(launch_elk_diag(cell->kind, a, num_cu, st));
   mark_end(m_newton, st);
 
   Mark m_out = mark_begin(st);
@@ -837,7 +844,8 @@ int plan_chunks(const pnr_cell* c, int jac_mode, double damping, int chunk_len, 
   if (rc) return rc;
   const Layout l = make_layout(&p.sub, jac_mode);
   p.sub_bytes = damping <= 0 ? l.total
-                : (p.sub.kind == PNR_CELL_GRU ? make_dense_elk_layout(&p.sub).total : damped_total(&p.sub, l));
+                : (p.sub.kind == PNR_CELL_GRU ? make_dense_elk_layout(&p.sub).total
+                                                : damped_total(&p.sub, l, jac_mode));
   p.staged = c->B > 1 && c->T > p.L;
   size_t off = align_up(p.sub_bytes);
   if (p.staged) {

@@ -107,6 +107,9 @@ struct ElkArgs {
 };
 int elk_items_per_thread();
 hipError_t launch_elk_diag(int cell, const ElkArgs& a, int num_cu, hipStream_t st);
+// ELK proper for LSTM_DIAG: the exact 2x2 Jacobian block per channel; Gs holds the 2x2
+// smoother gain as [B][4][D][T] and Es the offset as [B][2][D][T]
+hipError_t launch_elk2_lstm(const ElkArgs& a, int num_cu, hipStream_t st);
 
 // Backward pass of the diagonal-recurrence cells (GRU_DIAG, LSTM_DIAG): the adjoint
 // scan run backwards in time with the per-step gate gradients; one block walks a row.

@@ -138,6 +138,12 @@ def named_workloads() -> dict:
     # undamped workload's, which keeps the states within 1e-4 of the sequential ones.
     w["gru_diag_long_elk"] = dataclasses.replace(w["gru_diag_long"], name="gru_diag_long_elk", damping=0.01,
                                                  tol=1e-5)
+    # the long LSTM with ELK proper: the damped step with the exact 2x2 Jacobian block of
+    # every channel, taken at every iteration; tolerance 10x tighter as for the damped GRU.
+    # The strength is swept: to 1e-5, 1e-4 takes 10 iterations, 1e-3 41, 1e-2 over 200
+    # (undamped Newton: 7)
+    w["lstm_diag_long_elk"] = dataclasses.replace(w["lstm_diag_long"], name="lstm_diag_long_elk", jac_every=1,
+                                                  damping=1e-4, tol=1e-5)
     # the dense GRU of the quasi workload with the damped step on its diagonal Jacobian
     w["gru_quasi_elk"] = dataclasses.replace(w["gru_quasi"], name="gru_quasi_elk", damping=0.01)
     w["lstm_diag_long_stiff"] = dataclasses.replace(

@@ -105,19 +105,21 @@ def test_damped_requests_are_validated_without_a_gpu():
     # damping must be finite and positive
     for lam in (0.0, -1.0, float("nan"), float("inf")):
         assert pnr.pnr_eval_damped(ok, params, 4096, None, 8192, 10, 1e-5, pnr.JAC_FULL, lam) == pnr.E_INVALID
-    # the diagonal GRU with an exact or diagonal Jacobian, the diagonal LSTM with a diagonal
-    # one (quasi-ELK), refreshed every iteration
-    for bad in (dict(kind=pnr.CELL_LSTM_DIAG), dict(kind=pnr.CELL_GRU, D=16), dict(jac_every=2)):
+    # the diagonal GRU and LSTM with an exact (ELK) or diagonal (quasi-ELK) Jacobian, the dense
+    # GRU with a diagonal one, refreshed every iteration
+    for bad in (dict(kind=pnr.CELL_GRU, D=16), dict(jac_every=2)):
         cell = _cell(**bad)
         assert pnr.pnr_workspace_bytes_damped(cell, pnr.JAC_FULL) == 0
         assert pnr.pnr_eval_damped(cell, params, 4096, None, 8192, 10, 1e-5, pnr.JAC_FULL, 0.5) == pnr.E_UNSUPPORTED
     lstm = _cell(kind=pnr.CELL_LSTM_DIAG)
     assert pnr.pnr_workspace_bytes_damped(lstm, pnr.JAC_DIAG) > pnr.pnr_workspace_bytes(lstm, pnr.JAC_DIAG)
     assert pnr.pnr_workspace_bytes_damped(_cell(kind=pnr.CELL_LSTM_DIAG, jac_every=2), pnr.JAC_DIAG) == 0
-    # two per-step planes per state component: 8 bytes per state element
-    for c, mode, S in ((ok, pnr.JAC_FULL, ok.D), (lstm, pnr.JAC_DIAG, 2 * lstm.D)):
+    # two per-step planes per state component: 8 bytes per state element; the LSTM's full
+    # 2x2 block keeps a 2x2 gain and a 2-vector offset per channel: 12 bytes per state element
+    for c, mode, S, per in ((ok, pnr.JAC_FULL, ok.D, 8), (lstm, pnr.JAC_DIAG, 2 * lstm.D, 8),
+                            (lstm, pnr.JAC_FULL, 2 * lstm.D, 12)):
         extra = pnr.pnr_workspace_bytes_damped(c, mode) - pnr.pnr_workspace_bytes(c, mode)
-        assert 8 * c.B * c.T * S <= extra < 8 * c.B * c.T * S + 4096
+        assert per * c.B * c.T * S <= extra < per * c.B * c.T * S + 4096
     assert pnr.pnr_eval_damped(ok, params, 4096, None, 8192, 10, 1e-5, pnr.JAC_ZERO, 0.5) == pnr.E_UNSUPPORTED
     # workspace missing
     assert pnr.pnr_eval_damped(ok, params, 4096, None, 8192, 10, 1e-5, pnr.JAC_FULL, 0.5) in (pnr.E_WORKSPACE,)
@@ -149,7 +151,7 @@ def test_chunked_requests_are_validated_without_a_gpu():
         assert pnr.pnr_eval_chunked(gru, params, 4096, None, 8192, 10, 1e-5, pnr.JAC_FULL, lam,
                                     100) == pnr.E_INVALID
     # what the unchunked entry points reject, the chunked one rejects the same way
-    assert pnr.pnr_eval_chunked(_cell(kind=pnr.CELL_LSTM_DIAG), params, 4096, None, 8192, 10, 1e-5,
+    assert pnr.pnr_eval_chunked(_cell(kind=pnr.CELL_LSTM_DIAG, jac_every=2), params, 4096, None, 8192, 10, 1e-5,
                                 pnr.JAC_FULL, 0.5, 100) == pnr.E_UNSUPPORTED
     assert pnr.pnr_eval_chunked(_cell(kind=pnr.CELL_GRU, D=100), params, 4096, None, 8192, 10, 1e-5,
                                 pnr.JAC_DIAG, 0.0, 100) == pnr.E_UNSUPPORTED

@@ -7,7 +7,8 @@ fp64 oracle at max-abs 1e-4, per iteration and at convergence.  Sizes span sever
 1024-step tiles with a ragged tail (the kernel's tile is 256 threads x 4 steps); a tile's
 last step takes its smoother coefficients from the next tile's first, so lengths one past
 a tile boundary are covered too.  The diagonal LSTM runs quasi-ELK (diagonal of its 2x2
-Jacobian): two scalar filters per channel, for c and for h.
+Jacobian: two scalar filters per channel, for c and for h) and ELK proper (the exact 2x2
+block: one 2-state filter per channel).
 """
 import math
 
@@ -138,10 +139,49 @@ def test_lstm_converged_damped_equals_sequential():
     assert np.abs(_np(got["h"]) - ref).max() < 1e-4
 
 
-def test_lstm_damped_rejects_the_full_jacobian():
-    p = _problem(64, D=2, cell=LSTM)
-    with pytest.raises(pnr.PnrError):
-        _run(p, 2, -1.0, WL.JAC_FULL, 0.5, cell=LSTM)
+@pytest.mark.parametrize("T", [1, 37, 1023, 1025, 2 * 1024 + 300])
+@pytest.mark.parametrize("lam", [0.05, 1.0])
+def test_lstm_elk_fixed_iterations_match_damped_oracle(T, lam):
+    """ELK proper: the exact 2x2 Jacobian block per channel (the oracle's Kalman filter and
+    smoother run on the dense block-diagonal Jacobian)."""
+    p = _problem(T, D=4, seed=T % 83, cell=LSTM)
+    q = _f64(p)
+    print(f"# ELK LSTM fixed iterations T={T} lam={lam}", flush=True)
+    got = _run(p, 3, -1.0, WL.JAC_FULL, lam, cell=LSTM)
+    ref = O.newton_dense(LSTM, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], 3, -1.0, WL.JAC_FULL,
+                         solver="loop", damping=lam)
+    assert got["status"] == pnr.NOT_CONVERGED and got["iters"] == 3
+    np.testing.assert_allclose(_np(got["h"]), ref["states"], rtol=0, atol=1e-4)
+    np.testing.assert_allclose(got["history"], ref["rhos"], rtol=1e-3, atol=1e-5)
+
+
+def test_lstm_elk_step_matches_normal_equations():
+    """One ELK step from the zero guess against the Levenberg-Marquardt normal equations of
+    the dense block-bidiagonal system, solved by LAPACK."""
+    p = _problem(150, D=3, B=2, seed=22, cell=LSTM)
+    q = _f64(p)
+    got = _run(p, 1, -1.0, WL.JAC_FULL, 0.3, cell=LSTM)
+    ref = O.newton_dense(LSTM, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], 1, -1.0, WL.JAC_FULL,
+                         solver="dense", damping=0.3)
+    np.testing.assert_allclose(_np(got["h"]), ref["states"], rtol=0, atol=1e-4)
+
+
+def test_lstm_elk_vanishing_damping_gives_the_newton_iterates():
+    p = _problem(1500, D=3, B=2, seed=23, cell=LSTM)
+    d = {k: (None if v is None else v.to(DEV)) for k, v in p.items()}
+    newton = pnr.evaluate(LSTM, d["W"], d["U"], d["x"], b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"],
+                          max_iters=2, tol=-1.0, jac_mode=WL.JAC_FULL)
+    got = _run(p, 2, -1.0, WL.JAC_FULL, 1e-7, cell=LSTM)
+    np.testing.assert_allclose(_np(got["h"]), _np(newton["h"]), rtol=0, atol=1e-4)
+
+
+def test_lstm_elk_converged_equals_sequential():
+    p = _problem(2500, D=6, B=3, seed=6, cell=LSTM)
+    q = _f64(p)
+    got = _run(p, 300, 1e-6, WL.JAC_FULL, 0.2, cell=LSTM)
+    assert got["status"] == pnr.OK, (got["status"], got["history"][-3:])
+    ref = O.sequential(LSTM, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"])
+    assert np.abs(_np(got["h"]) - ref).max() < 1e-4
 
 
 # Dense GRU (quasi-ELK): the iteration against the oracle's Kalman-smoother step with the

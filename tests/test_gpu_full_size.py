@@ -69,7 +69,8 @@ def _check(name, mode):
 
 
 CASES = [(name, mode) for name in WL.WORKLOAD_ORDER + ["gru_diag_long_elk", "lstm_diag_long_chunked",
-                                                       "lstm_diag_long_adaptive", "lstm_diag_long_stiff_bounded"]
+                                                       "lstm_diag_long_adaptive", "lstm_diag_long_stiff_bounded",
+                                                       "lstm_diag_long_elk"]
          for mode in WL.get_workload(name).jac_modes]
 
 

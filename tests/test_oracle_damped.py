@@ -76,7 +76,7 @@ def test_large_damping_is_a_scaled_gradient_step():
 
 
 @pytest.mark.parametrize("cell,mode", [(O.CELL_GRU_DIAG, O.JAC_FULL), (O.CELL_LSTM_DIAG, O.JAC_DIAG),
-                                       (O.CELL_GRU, O.JAC_DIAG)])
+                                       (O.CELL_LSTM_DIAG, O.JAC_FULL), (O.CELL_GRU, O.JAC_DIAG)])
 def test_damped_iteration_converges_to_the_sequential_trajectory(cell, mode):
     p = {k: WL.as_f64(v) for k, v in WL.random_problem(cell, 2, 40, 3, 2, seed=5, bias_std=0.3,
                                                         h0_std=0.5).items()}
