@@ -25,7 +25,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .cells import CELL_GRU, CELL_GRU_DIAG, CELL_LSTM_DIAG, _recurrent, _sigmoid
+from .cells import CELL_GRU, CELL_GRU_DIAG, CELL_LSTM_DIAG, JAC_DIAG, JAC_FULL, _recurrent, _sigmoid, cell_jacobian
 from .sequential import project
 
 
@@ -70,10 +70,17 @@ def cell_vjp(cell: int, U, b_h, s, gx, lam):
     raise ValueError(f"unknown cell {cell}")
 
 
-def bptt(cell: int, W, U, b_x, b_h, x, h0, states, g):
+def bptt(cell: int, W, U, b_x, b_h, x, h0, states, g, jac_mode: int = JAC_FULL):
     """Gradients of L = sum_{b,t} <g[b,t], states[b,t]> where states solve the recurrence
     from h0 (the states are taken as given: the converged evaluation).  Returns dict(dx,
-    dW, dU, db_x, db_h, dh0, dgx [B, T, G*D], lam [B, T, S])."""
+    dW, dU, db_x, db_h, dh0, dgx [B, T, G*D], lam [B, T, S]).
+
+    jac_mode = JAC_DIAG is the diagonal approximation in the backward pass ("Towards
+    Scalable and Stable Parallelization of Nonlinear RNNs", summary page, "Measured
+    effects": diagonal Jacobians "including in the backward pass"): the adjoint recursion
+    carries diag(J_{t+1}) * lam_{t+1} instead of J_{t+1}^T lam_{t+1} (dh0 likewise), while
+    every step still sends its lam_t back through the cell's gates exactly.  With a
+    diagonal Jacobian (GRU_DIAG) it is the exact gradient."""
     W = np.asarray(W, dtype=np.float64)
     U = np.asarray(U, dtype=np.float64)
     x = np.asarray(x, dtype=np.float64)
@@ -102,7 +109,11 @@ def bptt(cell: int, W, U, b_x, b_h, x, h0, states, g):
         else:
             D = S // 2
             dU += (dgh.reshape(B, 4, D) * prev[:, None, D:]).sum(axis=0)
-        carry = dprev
+        if jac_mode == JAC_DIAG:
+            J = cell_jacobian(cell, U, b_h, prev, gx[:, t])
+            carry = np.einsum("nii->ni", J) * lam
+        else:
+            carry = dprev
     flat = dgx.reshape(B * T, GD)
     return dict(dx=(flat @ W).reshape(B, T, -1), dW=flat.T @ x.reshape(B * T, -1), dU=dU,
                 db_x=flat.sum(axis=0), db_h=db_h, dh0=carry, dgx=dgx, lam=lam_all)

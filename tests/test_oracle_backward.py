@@ -70,3 +70,58 @@ def test_adjoint_is_linear_in_the_loss_gradient_and_starts_at_the_last_step(cell
         J = O.cell_jacobian(cell, q["U"], q["b_h"], P[:, t], gx[:, t])
         lam = np.einsum("bij,bi->bj", J, lam)
         assert np.allclose(r["lam"][:, t - 1], lam, rtol=1e-12, atol=1e-13)
+
+
+# ---- the diagonal approximation in the backward pass -----------------------------------
+def _bwd_problem(cell, B=2, T=25, D=3, seed=11, diag_u=False):
+    p = WL.random_problem(cell, B, T, D, 4, seed=seed, bias_std=0.3, h0_std=0.4)
+    q = {k: (None if v is None else WL.as_f64(v)) for k, v in p.items()}
+    if diag_u:   # every gate block of the dense U diagonal: the Jacobian is diagonal
+        for gblk in range(3):
+            blk = q["U"][gblk * D:(gblk + 1) * D]
+            q["U"][gblk * D:(gblk + 1) * D] = np.diag(np.diag(blk))
+    H = O.sequential(cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"])
+    g = np.random.default_rng(seed + 1).normal(size=H.shape)
+    return q, H, g
+
+
+@pytest.mark.parametrize("cell,diag_u", [(O.CELL_GRU_DIAG, False), (O.CELL_GRU, True)])
+def test_diagonal_backward_is_exact_when_the_jacobian_is_diagonal(cell, diag_u):
+    q, H, g = _bwd_problem(cell, diag_u=diag_u)
+    a = O.bptt(cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], H, g)
+    b = O.bptt(cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], H, g, jac_mode=O.JAC_DIAG)
+    for k in ("dx", "dW", "dU", "db_x", "db_h", "dh0", "lam"):
+        assert np.abs(a[k] - b[k]).max() <= 1e-13 * max(1.0, np.abs(a[k]).max()), k
+
+
+@pytest.mark.parametrize("cell", [O.CELL_LSTM_DIAG, O.CELL_GRU])
+def test_diagonal_backward_adjoint_solves_the_transposed_diagonal_system(cell):
+    """lam of the diagonal approximation is the solution of (I - sub(diag J))^T lam = g,
+    the adjoint system of the block-bidiagonal Newton matrix with the Jacobians replaced by
+    their diagonals, solved densely by LAPACK; dh0 = diag(J_1) lam_1."""
+    q, H, g = _bwd_problem(cell, B=1, T=12)
+    r = O.bptt(cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], H, g, jac_mode=O.JAC_DIAG)
+    T, S = H.shape[1], H.shape[2]
+    gx = O.project(q["W"], q["x"], q["b_x"])[0]
+    P = np.concatenate([q["h0"], H[0, :-1]], axis=0)
+    J = O.cell_jacobian(cell, q["U"], q["b_h"], P, gx)
+    d = np.einsum("nii->ni", J)
+    A = np.eye(T * S)
+    for t in range(1, T):
+        A[t * S:(t + 1) * S, (t - 1) * S:t * S] = -np.diag(d[t])
+    lam = np.linalg.solve(A.T, g[0].reshape(-1)).reshape(T, S)
+    assert np.abs(r["lam"][0] - lam).max() < 1e-12
+    assert np.abs(r["dh0"][0] - d[0] * lam[0]).max() < 1e-12
+    # it is an approximation: the exact adjoint differs where the Jacobian couples channels
+    e = O.bptt(cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], H, g)
+    assert np.abs(e["lam"] - r["lam"]).max() > 1e-6
+
+
+def test_diagonal_backward_is_linear_in_the_loss_gradient():
+    q, H, g = _bwd_problem(O.CELL_LSTM_DIAG)
+    g2 = np.random.default_rng(5).normal(size=H.shape)
+    f = lambda gg: O.bptt(O.CELL_LSTM_DIAG, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], H, gg,
+                          jac_mode=O.JAC_DIAG)
+    a, b, c = f(g), f(g2), f(2.0 * g - 3.0 * g2)
+    for k in ("dx", "dW", "dU", "db_x", "dh0"):
+        assert np.abs(c[k] - (2.0 * a[k] - 3.0 * b[k])).max() < 1e-10 * max(1.0, np.abs(c[k]).max()), k
