@@ -330,6 +330,23 @@ int pnr_backward(const pnr_cell* cell, const pnr_params* params, const void* x, 
                  void* grad_b_x, void* grad_b_h, void* grad_h0);
 
 /*
+ * pnr_backward with a choice of Jacobian in the adjoint recursion.  jac_mode PNR_JAC_FULL is
+ * pnr_backward (the exact gradients).  PNR_JAC_DIAG is the diagonal approximation in the
+ * backward pass ("Towards Scalable and Stable Parallelization of Nonlinear RNNs", summary
+ * page, "Measured effects": diagonal Jacobian approximations "including in the backward
+ * pass"): the adjoint carries diag(J_{t+1}) lam_{t+1} instead of J_{t+1}^T lam_{t+1}
+ * (grad_h0 = diag(J_1) lam_1 likewise), while every step still sends its lam_t back
+ * through the cell's gates exactly; the gradients are those approximate adjoints' (exact
+ * for PNR_CELL_GRU_DIAG, whose Jacobian is diagonal).  For the dense GRU it is one
+ * diagonal scan instead of the refinement: pnr_iters_used() = 1, pnr_last_residual() = 0.
+ * Other jac_mode values return PNR_E_INVALID.  Arguments, workspace
+ * (pnr_workspace_bytes_backward) and results otherwise as pnr_backward.
+ */
+int pnr_backward_approx(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0,
+                        const void* h, const void* grad_h, void* grad_x, void* grad_W, void* grad_U,
+                        void* grad_b_x, void* grad_b_h, void* grad_h0, int jac_mode);
+
+/*
  * Backward pass over chunks, the gradient-checkpointing half of chunked evaluation
  * (ParaRNN overview page, "Experimental Results": chunking together with gradient
  * checkpointing keeps the memory of long sequences in check).  The sequence is cut into

@@ -1018,7 +1018,7 @@ BwdLayout make_bwd_layout(const pnr_cell* c) {
 namespace {
 int backward_dense(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, const void* h,
                    const void* grad_h, void* grad_x, void* grad_W, void* grad_U, void* grad_b_x, void* grad_b_h,
-                   void* grad_h0) {
+                   void* grad_h0, bool jdiag) {
   const DenseBwdLayout l = make_dense_bwd_layout(cell);
   const int D = cell->D, T = cell->T, B = cell->B, Din = cell->D_in, GD = 3 * D;
   const size_t BT = (size_t)B * T, n = BT * D;
@@ -1065,6 +1065,18 @@ int backward_dense(const pnr_cell* cell, const pnr_params* params, const void* x
   std::vector<double> hist;
   const GemmArgs gv{dgh, UT, nullptr, v, (int)BT, D, GD, 0, 0, 0, GD, GD, D, 1, 0};
   bool done = false;
+  if (jdiag) {
+    // the diagonal approximation: the first update from lam = 0 is the diagonal system's
+    // exact solution (R(0) = g, one diagonal scan); nothing to refine or read back
+    PNR_HIP(launch_gemm(PNR_F32, PNR_F32, gv, st));
+    PNR_HIP(launch_gru_bwd_refine(F, lam, v, static_cast<const float*>(grad_h), lam2, dgh, agg, carry, rmax, B, T, D,
+                                  st));
+    std::swap(lam, lam2);
+    updates = 1;
+    status = PNR_OK;
+    hist.push_back(0.0);
+    done = true;
+  }
   while (!done) {
     const int k1 = std::min(k + kBwdGroup - 1, kBwdMaxIters);
     for (int j = k; j <= k1; ++j) {
@@ -1098,7 +1110,9 @@ int backward_dense(const pnr_cell* cell, const pnr_params* params, const void* x
   PNR_HIP(launch_gru_bwd_gates(F, lam, dgh, dgx, n, D, st));
   if (grad_h0) {
     PNR_HIP(launch_gemm(PNR_F32, PNR_F32, gv, st));
-    PNR_HIP(launch_gru_bwd_dh0(F, lam, v, static_cast<float*>(grad_h0), B, T, D, st));
+    // exact: dh0 = J_1^T lam_1 = z lam + U^T dgh; diagonal approximation: diag(J_1) lam_1
+    PNR_HIP(launch_gru_bwd_dh0(jdiag ? F + n : F, lam, jdiag ? nullptr : v, static_cast<float*>(grad_h0), B, T, D,
+                               st));
   }
   float* dghT = gh;           // [3D][B*T]
   float* dgxT = fp(l.scan3);  // [3D][B*T]; the adjoint (possibly here) is not read after dh0
@@ -1150,9 +1164,10 @@ size_t pnr_workspace_bytes_backward(const pnr_cell* cell) {
   return make_bwd_layout(cell).total;
 }
 
-int pnr_backward(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, const void* h,
-                 const void* grad_h, void* grad_x, void* grad_W, void* grad_U, void* grad_b_x, void* grad_b_h,
-                 void* grad_h0) {
+namespace {
+int backward_impl(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, const void* h,
+                  const void* grad_h, void* grad_x, void* grad_W, void* grad_U, void* grad_b_x, void* grad_b_h,
+                  void* grad_h0, bool jdiag) {
   g_last.reset();
   g_prof.valid = false;
   g_prof.used = 0;
@@ -1181,7 +1196,7 @@ int pnr_backward(const pnr_cell* cell, const pnr_params* params, const void* x, 
     return PNR_OK;
   }
   if (kind == PNR_CELL_GRU)
-    return backward_dense(cell, params, x, h0, h, grad_h, grad_x, grad_W, grad_U, grad_b_x, grad_b_h, grad_h0);
+    return backward_dense(cell, params, x, h0, h, grad_h, grad_x, grad_W, grad_U, grad_b_x, grad_b_h, grad_h0, jdiag);
   int num_cu = 0;
   if ((rc = device_info(&num_cu))) return rc;
   char* ws = static_cast<char*>(cell->workspace);
@@ -1204,6 +1219,7 @@ int pnr_backward(const pnr_cell* cell, const pnr_params* params, const void* x, 
   PNR_HIP(launch_transpose(grad_h, PNR_F32, gT, PNR_F32, B, T, S, st));
 
   BwdArgs a{};
+  a.jdiag = jdiag ? 1 : 0;
   a.gx = gx;
   a.u = static_cast<const float*>(params->U);
   a.bh = static_cast<const float*>(params->b_h);
@@ -1257,6 +1273,25 @@ int pnr_backward(const pnr_cell* cell, const pnr_params* params, const void* x, 
     g_prof.valid = true;
   }
   return PNR_OK;
+}
+}  // namespace
+
+int pnr_backward(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, const void* h,
+                 const void* grad_h, void* grad_x, void* grad_W, void* grad_U, void* grad_b_x, void* grad_b_h,
+                 void* grad_h0) {
+  return backward_impl(cell, params, x, h0, h, grad_h, grad_x, grad_W, grad_U, grad_b_x, grad_b_h, grad_h0, false);
+}
+
+int pnr_backward_approx(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, const void* h,
+                        const void* grad_h, void* grad_x, void* grad_W, void* grad_U, void* grad_b_x, void* grad_b_h,
+                        void* grad_h0, int jac_mode) {
+  if (jac_mode != PNR_JAC_FULL && jac_mode != PNR_JAC_DIAG) {
+    g_last.reset();
+    g_prof.valid = false;
+    return fail(PNR_E_INVALID, "jac_mode must be PNR_JAC_FULL (exact) or PNR_JAC_DIAG (got %d)", jac_mode);
+  }
+  return backward_impl(cell, params, x, h0, h, grad_h, grad_x, grad_W, grad_U, grad_b_x, grad_b_h, grad_h0,
+                       jac_mode == PNR_JAC_DIAG);
 }
 
 // ---- backward pass over chunks (gradient checkpointing) ----

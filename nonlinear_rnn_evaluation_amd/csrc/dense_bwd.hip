@@ -224,7 +224,7 @@ __global__ void __launch_bounds__(256) gru_bwd_dh0_kernel(const float* __restric
   if (e >= B * D) return;
   const int b = e / D, i = e - b * D;
   const size_t s = (size_t)b * T * D + i;
-  dh0[e] = fmaf(F[s], lam[s], v[s]);
+  dh0[e] = v ? fmaf(F[s], lam[s], v[s]) : F[s] * lam[s];
 }
 
 // part[s][r] = sum of row r of M over column segment s (segments of ceil(cols / S))

@@ -1038,6 +1038,7 @@ __device__ __forceinline__ typename DeltaOf<typename DiagCell<CELL>::E>::T adjoi
       C::eval(q, gi, i == 0 ? p0[0] : hv[0][i - 1], i == 0 ? p0[1] : hv[1][i - 1], 0.f, 0.f, PNR_JAC_FULL, true, rc,
               rh, J);
       const float g0 = gv[0][i], g1 = gv[1][i];
+      if (a.jdiag) { J.a01 = 0.f; J.a10 = 0.f; }   // the diagonal approximation
       e[N - 1 - i] = in ? Aff2{J.a00, J.a10, J.a01, J.a11, fmaf(J.a00, g0, J.a10 * g1), fmaf(J.a01, g0, J.a11 * g1)}
                         : aff_identity2();
     }
@@ -1077,6 +1078,11 @@ __device__ __forceinline__ typename DeltaOf<typename DiagCell<CELL>::E>::T adjoi
       const float hp = i == 0 ? p0[1] : hv[1][i - 1];
       float2 dprev;
       vjp_lstm(q, gi, cp, hp, gv[0][i] + mu.x, gv[1][i] + mu.y, dg, dprev);
+      if (a.jdiag) {
+        // the diagonal approximation: mu_{t-1} = diag(J_t) lam_t, the step's own scan element
+        const Aff2& el = e[N - 1 - i];
+        dprev = make_float2(el.a00 * (gv[0][i] + mu.x), el.a11 * (gv[1][i] + mu.y));
+      }
 #pragma unroll
       for (int gg = 0; gg < NG; ++gg) {
         dg[gg] = in ? dg[gg] : 0.f;

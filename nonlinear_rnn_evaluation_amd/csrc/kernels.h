@@ -127,6 +127,7 @@ struct BwdArgs {
   int tiles_per_row;
   int n_rows;          // B * D
   int dgx_bf16;
+  int jdiag;           // 1: the adjoint carries diag(J) mu (the diagonal approximation), not J^T mu
 };
 int adjoint_items_per_thread();
 hipError_t launch_adjoint_diag(int cell, const BwdArgs& a, int num_cu, hipStream_t st);

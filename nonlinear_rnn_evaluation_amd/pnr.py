@@ -89,6 +89,8 @@ def load() -> ctypes.CDLL:
     lib.pnr_eval_static.argtypes = [P(PnrCell), P(PnrParams), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_int, ctypes.c_double, ctypes.c_int]
     lib.pnr_eval_static.restype = ctypes.c_int
+    lib.pnr_backward_approx.argtypes = [P(PnrCell), P(PnrParams)] + [ctypes.c_void_p] * 10 + [ctypes.c_int]
+    lib.pnr_backward_approx.restype = ctypes.c_int
     lib.pnr_eval_adaptive.argtypes = [P(PnrCell), P(PnrParams), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_double]
     lib.pnr_eval_adaptive.restype = ctypes.c_int
@@ -225,6 +227,14 @@ def pnr_backward(cell: PnrCell, params: PnrParams, x: int, h0: Optional[int], h:
                  grad_b_h: Optional[int], grad_h0: Optional[int]) -> int:
     return load().pnr_backward(ctypes.byref(cell), ctypes.byref(params), x, h0, h, grad_h, grad_x, grad_W, grad_U,
                                grad_b_x, grad_b_h, grad_h0)
+
+
+def pnr_backward_approx(cell: PnrCell, params: PnrParams, x: int, h0: Optional[int], h: int, grad_h: int,
+                        grad_x: Optional[int], grad_W: Optional[int], grad_U: Optional[int],
+                        grad_b_x: Optional[int], grad_b_h: Optional[int], grad_h0: Optional[int],
+                        jac_mode: int) -> int:
+    return load().pnr_backward_approx(ctypes.byref(cell), ctypes.byref(params), x, h0, h, grad_h, grad_x, grad_W,
+                                      grad_U, grad_b_x, grad_b_h, grad_h0, jac_mode)
 
 
 def pnr_workspace_bytes_backward_chunked(cell: PnrCell, chunk_len: int) -> int:
@@ -366,14 +376,18 @@ def evaluate(kind: int, W: torch.Tensor, U: torch.Tensor, x: torch.Tensor, *, b_
 
 def backward(kind: int, W: torch.Tensor, U: torch.Tensor, x: torch.Tensor, h: torch.Tensor, grad_h: torch.Tensor,
              *, b_x=None, b_h=None, h0=None, want=("x", "W", "U", "b_x", "b_h", "h0"),
-             workspace: Optional[torch.Tensor] = None, chunk_len: int = 0) -> dict:
+             workspace: Optional[torch.Tensor] = None, chunk_len: int = 0,
+             jac_mode: Optional[int] = None) -> dict:
     """Run pnr_backward on device tensors: gradients of L through the recurrence whose
     states are h, given grad_h = dL/dh.  Returns {name: fp32 tensor} for the names in
     `want` (the others are not computed), plus "workspace" and the adjoint solve's
     "status", "iters", "residual" and "history" (dense GRU: refinement iterations;
     diagonal cells: one scan, iters 0).  chunk_len > 0 runs pnr_backward_chunked: the
     sequence is processed in chunks of that many steps, last chunk first, with a
-    workspace sized for one chunk."""
+    workspace sized for one chunk.  jac_mode runs pnr_backward_approx: JAC_FULL exact,
+    JAC_DIAG the diagonal approximation in the adjoint recursion."""
+    if jac_mode is not None and chunk_len:
+        raise ValueError("jac_mode applies to the unchunked backward pass")
     B, T, D_in = x.shape
     G, D = (U.shape[0] // U.shape[1], U.shape[1]) if kind == CELL_GRU else (U.shape[0], U.shape[1])
     S = 2 * D if kind == CELL_LSTM_DIAG else D
@@ -402,6 +416,8 @@ def backward(kind: int, W: torch.Tensor, U: torch.Tensor, x: torch.Tensor, h: to
     grads = [_ptr(out.get(k)) for k in ("x", "W", "U", "b_x", "b_h", "h0")]
     if chunk_len:
         rc = pnr_backward_chunked(cell, params, ptrs["x"], ptrs["h0"], ptrs["h"], ptrs["grad_h"], *grads, chunk_len)
+    elif jac_mode is not None:
+        rc = pnr_backward_approx(cell, params, ptrs["x"], ptrs["h0"], ptrs["h"], ptrs["grad_h"], *grads, jac_mode)
     else:
         rc = pnr_backward(cell, params, ptrs["x"], ptrs["h0"], ptrs["h"], ptrs["grad_h"], *grads)
     if rc < 0:

@@ -230,3 +230,53 @@ def test_chunked_bf16_inputs_partial_requests_and_empty_sequence():
     r = pnr.backward(cell, d["W"], d["U"], d["x"], z, z, b_x=d["b_x"], h0=d["h0"], chunk_len=16)
     for k in ("W", "U", "b_x", "b_h", "h0"):
         assert torch.count_nonzero(r[k]) == 0
+
+
+# ---------------------------------------------------------------------------------
+# The diagonal approximation in the backward pass (pnr_backward_approx, JAC_DIAG): the
+# adjoint carries diag(J) lam; against oracle.bptt(..., jac_mode=JAC_DIAG), whose adjoint is
+# pinned to a LAPACK solve of the transposed diagonal system.  For GRU_DIAG (a diagonal
+# Jacobian) it must equal the exact gradients.
+@pytest.mark.parametrize("cell,D,Din", [(WL.CELL_GRU_DIAG, 6, 5), (WL.CELL_LSTM_DIAG, 4, 3)])
+@pytest.mark.parametrize("T", [1, 37, 1025, 2 * 1024 + 301])
+def test_diagonal_backward_matches_the_oracle(cell, D, Din, T):
+    p, H32, g, ref_exact = _case(cell, 2, T, D, Din, seed=T % 89 + 3)
+    q = {k: (None if v is None else WL.as_f64(v)) for k, v in p.items()}
+    S = 2 * D if cell == WL.CELL_LSTM_DIAG else D
+    h0q = q["h0"] if q["h0"] is not None else np.zeros((2, S))
+    ref = O.bptt(cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], h0q, H32.astype(np.float64), g.astype(np.float64),
+                 jac_mode=WL.JAC_DIAG)
+    d = {k: (None if v is None else v.to(DEV)) for k, v in p.items()}
+    print(f"# diagonal backward cell={cell} T={T}", flush=True)
+    got = pnr.backward(cell, d["W"], d["U"], d["x"], torch.from_numpy(H32).to(DEV), torch.from_numpy(g).to(DEV),
+                       b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"], jac_mode=WL.JAC_DIAG)
+    _check(got, ref)
+    if cell == WL.CELL_GRU_DIAG:
+        _check(got, ref_exact)
+
+
+@pytest.mark.parametrize("D,T", [(16, 37), (64, 2100), (40, 777)])
+def test_dense_gru_diagonal_backward_matches_the_oracle(D, T):
+    cell = WL.CELL_GRU
+    p = WL.random_problem(cell, 2, T, D, 9, seed=D + T + 1, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32, bias_std=0.2,
+                          h0_std=0.3, w_std=0.7 / np.sqrt(D))
+    q = {k: (None if v is None else WL.as_f64(v)) for k, v in p.items()}
+    H = O.sequential(cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"])
+    H32 = H.astype(np.float32)
+    g = np.random.default_rng(D * T + 1).normal(size=H.shape).astype(np.float32)
+    ref = O.bptt(cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], H32.astype(np.float64),
+                 g.astype(np.float64), jac_mode=WL.JAC_DIAG)
+    d = {k: (None if v is None else v.to(DEV)) for k, v in p.items()}
+    print(f"# dense diagonal backward D={D} T={T}", flush=True)
+    got = pnr.backward(cell, d["W"], d["U"], d["x"], torch.from_numpy(H32).to(DEV), torch.from_numpy(g).to(DEV),
+                       b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"], jac_mode=WL.JAC_DIAG)
+    assert got["status"] == pnr.OK and got["iters"] == 1
+    _check(got, ref)
+
+
+def test_backward_approx_rejects_other_modes():
+    p, H32, g, _ = _case(WL.CELL_GRU_DIAG, 1, 10, 3, 2)
+    d = {k: (None if v is None else v.to(DEV)) for k, v in p.items()}
+    with pytest.raises(pnr.PnrError, match="jac_mode"):
+        pnr.backward(WL.CELL_GRU_DIAG, d["W"], d["U"], d["x"], torch.from_numpy(H32).to(DEV),
+                     torch.from_numpy(g).to(DEV), b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"], jac_mode=WL.JAC_ZERO)
