@@ -35,14 +35,25 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found; libpnr needs the ROCm toolchain to build")
 
 
-def build_library(verbose: bool = False, jobs: int = 8) -> str:
+# host-code sanitizers for the checking build (device code is compiled as usual)
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+LIB_SANITIZED = os.path.join(HERE, "libpnr_san.so")
+
+
+def build_library(verbose: bool = False, jobs: int = 8, sanitize: bool = False) -> str:
+    """Compile every HIP source and link libpnr.so; with sanitize, the host code is built
+    with AddressSanitizer and UndefinedBehaviorSanitizer into libpnr_san.so instead (a
+    checking build of the argument validation and workspace arithmetic, run on the CPU)."""
     hipcc = _hipcc()
+    flags = COMMON_FLAGS + (SANITIZE_FLAGS if sanitize else [])
+    lib = LIB_SANITIZED if sanitize else LIB
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     tmp = tempfile.mkdtemp(prefix="pnr_build_")
     try:
         def compile_one(src):
             obj = os.path.join(tmp, os.path.basename(src) + ".o")
-            cmd = [hipcc, *COMMON_FLAGS, "-c", src, "-o", obj]
+            cmd = [hipcc, *flags, "-c", src, "-o", obj]
             r = subprocess.run(cmd, capture_output=True, text=True)
             if r.returncode != 0:
                 raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -51,15 +62,15 @@ def build_library(verbose: bool = False, jobs: int = 8) -> str:
             return obj
         with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
             objs = list(ex.map(compile_one, srcs))
-        out_tmp = LIB + ".tmp"
-        cmd = [hipcc, *COMMON_FLAGS, "-shared", *objs, "-o", out_tmp]
+        out_tmp = lib + ".tmp"
+        cmd = [hipcc, *flags, "-shared", *objs, "-o", out_tmp]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-        os.replace(out_tmp, LIB)
+        os.replace(out_tmp, lib)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
-    return LIB
+    return lib
 
 
 if __name__ == "__main__":
