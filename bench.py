@@ -62,9 +62,10 @@ def newton_kernel(w, mode):
 
 
 def src_hash(path):
-    """Hash of a kernel's source file and the two headers every kernel includes."""
+    """Hash of a kernel's source file and of every header in csrc/ (any of them may be included)."""
     h = hashlib.sha256()
-    for p in (path, CSRC + "common.h", CSRC + "kernels.h"):
+    headers = sorted(f for f in os.listdir(os.path.join(ROOT, CSRC)) if f.endswith(".h"))
+    for p in [path] + [CSRC + f for f in headers]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
