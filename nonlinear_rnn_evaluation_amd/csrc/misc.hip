@@ -100,9 +100,43 @@ __global__ void __launch_bounds__(256) diag_output_kernel(Bufs3f bufs, const Ctr
   }
 }
 
+// The same conversion 4 elements (16 B) per lane through a 64 x 65 tile, for S and T
+// multiples of 4: 256 B runs on both sides, about copy speed.
+__global__ void __launch_bounds__(256) diag_output4_kernel(Bufs3f bufs, const Ctrl* ctrl, float* out, int S,
+                                                           int T) {
+  __shared__ float tile[64][65];
+  const int rb = ctrl->result_buf;
+  const float* src = rb >= 0 ? bufs.p[rb] : nullptr;
+  const size_t b = blockIdx.z;
+  const int t0 = blockIdx.x * 64, s0 = blockIdx.y * 64;
+  const int g = threadIdx.x & 15, q = threadIdx.x >> 4;   // 16 groups of 4 along a row, 16 rows
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ss = q + 16 * i, s = s0 + ss, t = t0 + 4 * g;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (src && s < S && t < T) v = *reinterpret_cast<const float4*>(src + (b * S + s) * T + t);
+    tile[ss][4 * g] = v.x; tile[ss][4 * g + 1] = v.y; tile[ss][4 * g + 2] = v.z; tile[ss][4 * g + 3] = v.w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tt = q + 16 * i, t = t0 + tt, s = s0 + 4 * g;
+    if (t < T && s < S)
+      *reinterpret_cast<float4*>(out + (b * T + t) * S + s) =
+          make_float4(tile[4 * g][tt], tile[4 * g + 1][tt], tile[4 * g + 2][tt], tile[4 * g + 3][tt]);
+  }
+}
+
 hipError_t launch_diag_output(const float* const* bufs, const Ctrl* ctrl, float* h_out, int B, int S, int T,
                               hipStream_t st) {
   Bufs3f bb{{bufs[0], bufs[1], bufs[2]}};
+  bool vec = S % 4 == 0 && T % 4 == 0 && (uintptr_t)h_out % 16 == 0;
+  for (int i = 0; i < 3; ++i) vec = vec && (uintptr_t)bufs[i] % 16 == 0;
+  if (vec) {
+    dim3 grid4((T + 63) / 64, (S + 63) / 64, B);
+    hipLaunchKernelGGL(diag_output4_kernel, grid4, dim3(256), 0, st, bb, ctrl, h_out, S, T);
+    return hipGetLastError();
+  }
   dim3 grid((T + 31) / 32, (S + 31) / 32, B);
   hipLaunchKernelGGL(diag_output_kernel, grid, dim3(256), 0, st, bb, ctrl, h_out, S, T);
   return hipGetLastError();

@@ -374,3 +374,20 @@ print("ordinary launch ok")
     out = subprocess.run([sys.executable, "-c", script, root], env=env, capture_output=True, text=True, timeout=240)
     assert out.returncode == 0, out.stderr[-2000:]
     assert "ordinary launch ok" in out.stdout
+
+
+@pytest.mark.parametrize("cell,B,D,T", [(WL.CELL_LSTM_DIAG, 2, 6, 68), (WL.CELL_GRU_DIAG, 3, 20, 132),
+                                         (WL.CELL_GRU_DIAG, 2, 20, 130), (WL.CELL_LSTM_DIAG, 1, 34, 200),
+                                         (WL.CELL_GRU_DIAG, 1, 3, 64)])
+def test_output_layout_conversion_partial_tiles(cell, B, D, T):
+    """The [B][S][T] -> [B][T][S] conversion of the result: S and T multiples of 4 take the
+    16-byte-per-lane kernel (partial 64 x 64 tiles on both sides here), the others the
+    scalar one; after 0 updates (the never-stored zero guess) and after 2."""
+    p = WL.random_problem(cell, B, T, D, 5, seed=D * T, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32,
+                          bias_std=0.2, h0_std=0.3)
+    q = _f64(p)
+    for k in (0, 2):
+        got = _run(cell, p, k, -1.0, WL.JAC_FULL)
+        ref = O.newton_dense(cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], k, -1.0, WL.JAC_FULL, 1,
+                             solver="loop")
+        np.testing.assert_allclose(_np(got["h"]), ref["states"], rtol=0, atol=1e-4)
