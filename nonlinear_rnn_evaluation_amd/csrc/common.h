@@ -57,6 +57,12 @@ __device__ __forceinline__ void backoff(uint32_t spins) {
 __device__ __forceinline__ void record_fault(Ctrl* c, int code) {
   __hip_atomic_store(&c->fault, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// One 16-byte global -> LDS load per lane (global_load_lds_dwordx4): lane l writes bytes
+// 16l..16l+15 after the wave-uniform LDS address `dst`.  Counted by vmcnt.
+__device__ __forceinline__ void lds_load16(const float* src, float* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
 __device__ __forceinline__ bool has_fault(const Ctrl* c) {
   return __hip_atomic_load(&c->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
 }

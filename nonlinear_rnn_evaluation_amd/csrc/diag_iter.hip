@@ -140,14 +140,154 @@ struct IterView {
   uint32_t ep;
 };
 
+// What the tiles of a row share: the cell's per-channel parameters, and the bounded
+// iteration's state limit (GRU: max(1, |h0|); LSTM: |c0|, grown by one per step).
+template <int CELL>
+struct RowPar {
+  typename DiagCell<CELL>::Par q;
+  float lim;
+};
+
+template <int CELL>
+__device__ __forceinline__ RowPar<CELL> load_row(const DiagLoopArgs& a, int row) {
+  using C = DiagCell<CELL>;
+  const int D = a.D, S = D * C::SP;
+  const int b = row / D, d = row - b * D;
+  RowPar<CELL> r;
+  r.q = C::load_par(a.u, a.bh, D, d);
+  const float h0 = a.bounded && a.h0 ? fabsf(a.h0[(size_t)b * S + d]) : 0.f;
+  r.lim = CELL == PNR_CELL_GRU_DIAG ? fmaxf(1.f, h0) : h0;
+  return r;
+}
+
+// Everything a tile reads from HBM, gathered before any of it is used.
+template <int CELL, int N>
+struct TileIn {
+  float g[DiagCell<CELL>::G][N];     // gate pre-activations
+  float s[DiagCell<CELL>::SP][N];    // current iterate (LSTM: c, then h)
+  float sj[DiagCell<CELL>::SP][N];   // state the Jacobian is taken at (reuse passes)
+  float p[DiagCell<CELL>::SP];       // lane 0: the state before the wave's first step
+  float pj[DiagCell<CELL>::SP];
+};
+
+template <int CELL, int N>
+__device__ __forceinline__ void load_tile(const DiagLoopArgs& a, int row, int seg, bool walk, bool stale,
+                                          const IterView& v, TileIn<CELL, N>& in) {
+  using C = DiagCell<CELL>;
+  constexpr int G = C::G, SP = C::SP;
+  constexpr int TILE = PNR_BLOCK * N;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int D = a.D, T = a.T;
+  const int S = D * SP;
+  const bool vec = (T & 3) == 0;
+  const int b = row / D, d = row - b * D;
+  const int tb = seg * TILE + tid * N;
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) load_n(a.gx + ((size_t)(b * G + gg) * D + d) * T, tb, T, vec, N, in.g[gg]);
+  // The state before a thread's first step is the previous lane's last one (DPP); only
+  // lane 0 of each wave loads it.  Before a tile's first step it was written by the block
+  // owning the previous tile: read it coherently (everything else here is this block's own).
+  const bool halo_other = tid == 0 && !walk;
+#pragma unroll
+  for (int k = 0; k < SP; ++k) {
+    const size_t off = ((size_t)b * S + (size_t)k * D + d) * T;
+    if (v.cur_zero) { for (int i = 0; i < N; ++i) in.s[k][i] = 0.f; }
+    else load_n(v.Hcur + off, tb, T, vec, N, in.s[k]);
+    float p = 0.f;
+    if (lane == 0) {
+      if (tb == 0) p = a.h0 ? a.h0[(size_t)b * S + (size_t)k * D + d] : 0.f;
+      else if (v.cur_zero || tb > T) p = 0.f;
+      else p = halo_other ? coherent_load(v.Hcur + off + tb - 1) : v.Hcur[off + tb - 1];
+    }
+    in.p[k] = p;
+    if (stale) {
+      if (v.jac_zero) { for (int i = 0; i < N; ++i) in.sj[k][i] = 0.f; }
+      else load_n(v.Hjac + off, tb, T, vec, N, in.sj[k]);
+      float pj = 0.f;
+      if (lane == 0) {
+        if (tb == 0) pj = a.h0 ? a.h0[(size_t)b * S + (size_t)k * D + d] : 0.f;
+        else if (v.jac_zero || tb > T) pj = 0.f;
+        else pj = halo_other ? coherent_load(v.Hjac + off + tb - 1) : v.Hjac[off + tb - 1];
+      }
+      in.pj[k] = pj;
+    }
+  }
+}
+
+// LDS of the staged row walk: one staged tile, and what the waves of a tile pass on.
+template <int CELL, int N>
+struct WalkStage {
+  static constexpr int PLANES = DiagCell<CELL>::G + 2 * DiagCell<CELL>::SP;
+  float pl[PLANES][PNR_BLOCK * N];                   // staged planes, in step order
+  float edge[2][PNR_WAVES][2 * DiagCell<CELL>::SP];  // each wave's last current / Jacobian state, by tile parity
+  RowPar<CELL> rp;                                   // the row's parameters
+  int fault;                                         // the block's fault decision
+};
+
+// Direct-to-LDS staging of one full tile for the row walk (global_load_lds_dwordx4: lane
+// l of a wave's load writes bytes 16l..16l+15 of a 1 KB run, so plane p of the tile lands
+// in step order as pl[p][0 .. TILE)).  Planes: the gates, the current iterate, and on
+// reuse passes the state the Jacobian is taken at.  No register holds a staged tile, so
+// the next tile's loads can be in flight through the whole of the current tile.
+template <int CELL, int N>
+__device__ __forceinline__ void stage_issue(const DiagLoopArgs& a, const IterView& v, bool stale, int row, int seg,
+                                            WalkStage<CELL, N>& st) {
+  using C = DiagCell<CELL>;
+  constexpr int G = C::G, SP = C::SP, TILE = PNR_BLOCK * N;
+  static_assert(N == 4, "one 16-byte load per lane and plane");
+  const int tid = threadIdx.x;
+  const int D = a.D, T = a.T, S = D * SP;
+  const int b = row / D, d = row - b * D;
+  const size_t tb = (size_t)seg * TILE + tid * N;
+  const int w0 = (tid >> 6) * 64 * N;   // the wave's run in each plane
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg)
+    lds_load16(a.gx + ((size_t)(b * G + gg) * D + d) * T + tb, &st.pl[gg][w0]);
+  if (!v.cur_zero) {
+#pragma unroll
+    for (int k = 0; k < SP; ++k)
+      lds_load16(v.Hcur + ((size_t)b * S + (size_t)k * D + d) * T + tb, &st.pl[G + k][w0]);
+  }
+  if (stale && !v.jac_zero) {
+#pragma unroll
+    for (int k = 0; k < SP; ++k)
+      lds_load16(v.Hjac + ((size_t)b * S + (size_t)k * D + d) * T + tb, &st.pl[G + SP + k][w0]);
+  }
+}
+
+// A wave's part of a staged tile into registers: only what its own loads brought in, so
+// that the wait before these reads (the compiler's) is a wait for this wave's loads alone.
+// The steps before the wave's first (in.p, in.pj) are filled in by the caller.
+template <int CELL, int N>
+__device__ __forceinline__ void stage_read(const IterView& v, bool stale, const WalkStage<CELL, N>& st,
+                                           TileIn<CELL, N>& in) {
+  using C = DiagCell<CELL>;
+  constexpr int G = C::G, SP = C::SP;
+  const int tid = threadIdx.x;
+  auto rd = [&](const float* p, float* o) {
+    const float4 x = *reinterpret_cast<const float4*>(p);
+    o[0] = x.x; o[1] = x.y; o[2] = x.z; o[3] = x.w;
+  };
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) rd(&st.pl[gg][tid * N], in.g[gg]);
+#pragma unroll
+  for (int k = 0; k < SP; ++k) {
+    if (v.cur_zero) { for (int i = 0; i < N; ++i) in.s[k][i] = 0.f; }
+    else rd(&st.pl[G + k][tid * N], in.s[k]);
+    if (stale) {
+      if (v.jac_zero) { for (int i = 0; i < N; ++i) in.sj[k][i] = 0.f; }
+      else rd(&st.pl[G + SP + k][tid * N], in.sj[k]);
+    }
+  }
+}
+
 template <int CELL, int N, bool RESID_ONLY>
 __device__ __forceinline__ typename DeltaOf<typename DiagCell<CELL>::E>::T diag_tile(
-    const DiagLoopArgs& a, TileShared<CELL>& sh, int row, int seg, int tile, bool walk,
-    typename DeltaOf<typename DiagCell<CELL>::E>::T carry, const IterView& v, uint32_t& blk_max) {
+    const DiagLoopArgs& a, TileShared<CELL>& sh, const TileIn<CELL, N>& in, const RowPar<CELL>& rp, int row, int seg,
+    int tile, bool walk, typename DeltaOf<typename DiagCell<CELL>::E>::T carry, const IterView& v, uint32_t& blk_max) {
   using C = DiagCell<CELL>;
   using E = typename C::E;
   using Dl = typename DeltaOf<E>::T;
-  constexpr int G = C::G;
   constexpr int TILE = PNR_BLOCK * N;
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int D = a.D, T = a.T;
@@ -158,116 +298,57 @@ __device__ __forceinline__ typename DeltaOf<typename DiagCell<CELL>::E>::T diag_
   const bool stale = v.stale && !RESID_ONLY;
   const int jac_mode = a.jac_mode;
 
-  const typename C::Par q = C::load_par(a.u, a.bh, D, d);
-  float g[G][N];
-#pragma unroll
-  for (int gg = 0; gg < G; ++gg) load_n(a.gx + ((size_t)(b * G + gg) * D + d) * T, tb, T, vec, N, g[gg]);
-
+  const typename C::Par q = rp.q;
   uint32_t tmax = 0;
   E e[N];
   float hc[C::SP][N];
   if constexpr (CELL == PNR_CELL_GRU_DIAG) {
-    const size_t roff = ((size_t)b * S + d) * T;
-    float h[N], pj[N];
-    if (v.cur_zero) { for (int i = 0; i < N; ++i) h[i] = 0.f; }
-    else load_n(v.Hcur + roff, tb, T, vec, N, h);
-    // The state before a thread's first step is the previous lane's last one (DPP);
-    // only lane 0 of each wave loads it.  Before a tile's first step it was written by
-    // the block owning the previous tile: read it coherently (everything else here is
-    // this block's own).
-    const bool halo_other = tid == 0 && !walk;
-    float p0 = 0.f;
-    if (lane == 0) {
-      if (tb == 0) p0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
-      else if (v.cur_zero || tb > T) p0 = 0.f;
-      else p0 = halo_other ? coherent_load(v.Hcur + roff + tb - 1) : v.Hcur[roff + tb - 1];
-    }
-    p0 = wave_shr1(h[N - 1], p0);
+    const float p0 = wave_shr1(in.s[0][N - 1], in.p[0]);
+    float pj[N];
     if (stale) {
-      float hj[N];
-      if (v.jac_zero) { for (int i = 0; i < N; ++i) hj[i] = 0.f; }
-      else load_n(v.Hjac + roff, tb, T, vec, N, hj);
-      float pj0 = 0.f;
-      if (lane == 0) {
-        if (tb == 0) pj0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
-        else if (v.jac_zero || tb > T) pj0 = 0.f;
-        else pj0 = halo_other ? coherent_load(v.Hjac + roff + tb - 1) : v.Hjac[roff + tb - 1];
-      }
-      pj[0] = wave_shr1(hj[N - 1], pj0);
-      for (int i = 1; i < N; ++i) pj[i] = hj[i - 1];
+      pj[0] = wave_shr1(in.sj[0][N - 1], in.pj[0]);
+      for (int i = 1; i < N; ++i) pj[i] = in.sj[0][i - 1];
     }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const float p = i == 0 ? p0 : h[i - 1];
-      float gi[3] = {g[0][i], g[1][i], g[2][i]};
+      const float p = i == 0 ? p0 : in.s[0][i - 1];
+      float gi[3] = {in.g[0][i], in.g[1][i], in.g[2][i]};
       float res, ja = 0.f;
-      C::eval(q, gi, p, h[i], jac_mode, !stale && !RESID_ONLY, res, ja);
+      C::eval(q, gi, p, in.s[0][i], jac_mode, !stale && !RESID_ONLY, res, ja);
       if (stale) ja = C::jac_only(q, gi, pj[i], jac_mode);
       if (tb + i >= T) { res = 0.f; ja = 1.f; }
       tmax = max(tmax, abs_bits(res));
       e[i] = Aff1{ja, res};
-      hc[0][i] = h[i];
+      hc[0][i] = in.s[0][i];
     }
   } else {
-    const size_t coff = ((size_t)b * S + d) * T, hoff = ((size_t)b * S + D + d) * T;
-    float c[N], h[N];
-    if (v.cur_zero) { for (int i = 0; i < N; ++i) { c[i] = 0.f; h[i] = 0.f; } }
-    else { load_n(v.Hcur + coff, tb, T, vec, N, c); load_n(v.Hcur + hoff, tb, T, vec, N, h); }
-    const bool halo_other = tid == 0 && !walk;   // see the GRU branch
-    float cp0 = 0.f, hp0 = 0.f;
-    if (lane == 0) {
-      if (tb == 0) {
-        cp0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
-        hp0 = a.h0 ? a.h0[(size_t)b * S + D + d] : 0.f;
-      } else if (v.cur_zero || tb > T) {
-        cp0 = 0.f; hp0 = 0.f;
-      } else if (halo_other) {
-        cp0 = coherent_load(v.Hcur + coff + tb - 1); hp0 = coherent_load(v.Hcur + hoff + tb - 1);
-      } else {
-        cp0 = v.Hcur[coff + tb - 1]; hp0 = v.Hcur[hoff + tb - 1];
-      }
-    }
-    cp0 = wave_shr1(c[N - 1], cp0);
-    hp0 = wave_shr1(h[N - 1], hp0);
-    float cj[N], hj[N], cpj0 = 0.f, hpj0 = 0.f;
+    const float cp0 = wave_shr1(in.s[0][N - 1], in.p[0]);
+    const float hp0 = wave_shr1(in.s[1][N - 1], in.p[1]);
+    float cpj0 = 0.f, hpj0 = 0.f;
     if (stale) {
-      if (v.jac_zero) { for (int i = 0; i < N; ++i) { cj[i] = 0.f; hj[i] = 0.f; } }
-      else { load_n(v.Hjac + coff, tb, T, vec, N, cj); load_n(v.Hjac + hoff, tb, T, vec, N, hj); }
-      if (lane == 0) {
-        if (tb == 0) {
-          cpj0 = a.h0 ? a.h0[(size_t)b * S + d] : 0.f;
-          hpj0 = a.h0 ? a.h0[(size_t)b * S + D + d] : 0.f;
-        } else if (!(v.jac_zero || tb > T)) {
-          if (halo_other) {
-            cpj0 = coherent_load(v.Hjac + coff + tb - 1); hpj0 = coherent_load(v.Hjac + hoff + tb - 1);
-          } else {
-            cpj0 = v.Hjac[coff + tb - 1]; hpj0 = v.Hjac[hoff + tb - 1];
-          }
-        }
-      }
-      cpj0 = wave_shr1(cj[N - 1], cpj0);
-      hpj0 = wave_shr1(hj[N - 1], hpj0);
+      cpj0 = wave_shr1(in.sj[0][N - 1], in.pj[0]);
+      hpj0 = wave_shr1(in.sj[1][N - 1], in.pj[1]);
     }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const float cp = i == 0 ? cp0 : c[i - 1];
-      const float hp = i == 0 ? hp0 : h[i - 1];
-      float gi[4] = {g[0][i], g[1][i], g[2][i], g[3][i]};
+      const float cp = i == 0 ? cp0 : in.s[0][i - 1];
+      const float hp = i == 0 ? hp0 : in.s[1][i - 1];
+      float gi[4] = {in.g[0][i], in.g[1][i], in.g[2][i], in.g[3][i]};
       float rc, rh;
       Aff2 J = aff_identity2();
-      C::eval(q, gi, cp, hp, c[i], h[i], jac_mode, !stale && !RESID_ONLY, rc, rh, J);
+      C::eval(q, gi, cp, hp, in.s[0][i], in.s[1][i], jac_mode, !stale && !RESID_ONLY, rc, rh, J);
       if (stale) {
         float dc, dh;
-        const float cpj = i == 0 ? cpj0 : cj[i - 1];
-        const float hpj = i == 0 ? hpj0 : hj[i - 1];
+        const float cpj = i == 0 ? cpj0 : in.sj[0][i - 1];
+        const float hpj = i == 0 ? hpj0 : in.sj[1][i - 1];
         C::eval(q, gi, cpj, hpj, 0.f, 0.f, jac_mode, true, dc, dh, J);
       }
       if (tb + i >= T) { rc = 0.f; rh = 0.f; J = aff_identity2(); }
       tmax = max(tmax, max(abs_bits(rc), abs_bits(rh)));
       J.b0 = rc; J.b1 = rh;
       e[i] = J;
-      hc[0][i] = c[i];
-      hc[1][i] = h[i];
+      hc[0][i] = in.s[0][i];
+      hc[1][i] = in.s[1][i];
     }
   }
   blk_max = max(blk_max, tmax);
@@ -304,7 +385,7 @@ __device__ __forceinline__ typename DeltaOf<typename DiagCell<CELL>::E>::T diag_
     // |c_t| < |c0| + t (c' = f c + i g, 0 < f, i < 1, |g| < 1).
     const bool bounded = a.bounded != 0;
     if constexpr (CELL == PNR_CELL_GRU_DIAG) {
-      const float hb = bounded ? fmaxf(1.f, a.h0 ? fabsf(a.h0[(size_t)b * S + d]) : 0.f) : 0.f;
+      const float hb = rp.lim;
       float out[N];
 #pragma unroll
       for (int i = 0; i < N; ++i) {
@@ -317,7 +398,7 @@ __device__ __forceinline__ typename DeltaOf<typename DiagCell<CELL>::E>::T diag_
       // the tile's last state is the next tile's halo, read by another block next pass
       if (!walk && tid == PNR_BLOCK - 1 && tb + N <= T) coherent_store(orow + tb + N - 1, out[N - 1]);
     } else {
-      const float c0b = bounded && a.h0 ? fabsf(a.h0[(size_t)b * S + d]) : 0.f;
+      const float c0b = rp.lim;
       float oc[N], oh[N];
 #pragma unroll
       for (int i = 0; i < N; ++i) {
@@ -345,6 +426,82 @@ __device__ __forceinline__ typename DeltaOf<typename DiagCell<CELL>::E>::T diag_
   }
 }
 
+// The row walk with the next tile staged in LDS while the current one is computed (full
+// tiles only: T a multiple of the tile).  Per tile: publish each wave's last step (the
+// next wave's predecessor) in LDS, barrier, issue the next tile's loads into the stage,
+// then the tile's arithmetic, scans and stores, and last wait for this wave's staged
+// loads and read its part of the next tile.  No wave reads another wave's staged loads,
+// so each wave waits for its own only; the wait is explicit (vmcnt), since the compiler
+// does not order LDS reads after direct-to-LDS loads by itself.  RESID_ONLY is a template
+// argument so that each loop has one pattern of memory operations; its tiles have no
+// barriers of their own, so it closes each tile with one (the LDS slots below are reused
+// every two tiles).
+template <int CELL, int N, bool RESID_ONLY>
+__device__ __forceinline__ void walk_staged(const DiagLoopArgs& a, TileShared<CELL>& sh, WalkStage<CELL, N>& st,
+                                            const IterView& v, bool stale, int n_items, uint32_t& blk_max) {
+  using C = DiagCell<CELL>;
+  using E = typename C::E;
+  using Dl = typename DeltaOf<E>::T;
+  constexpr int SP = C::SP;
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int D = a.D, S = D * SP;
+  const int tpr = a.tiles_per_row;
+  const int my_rows = (int)blockIdx.x < n_items ? (n_items - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+  const int n_steps = my_rows * tpr;
+  if (n_steps == 0) return;
+  stage_issue<CELL, N>(a, v, stale, blockIdx.x, 0, st);
+  TileIn<CELL, N> in;
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the first tile's staged loads
+  stage_read<CELL, N>(v, stale, st, in);
+  int row = blockIdx.x, seg = 0;
+  Dl carry = DeltaOf<E>::zero();
+  for (int j = 0; j < n_steps; ++j) {
+    const int par = j & 1;
+    if (lane == 63) {
+#pragma unroll
+      for (int k = 0; k < SP; ++k) {
+        st.edge[par][wid][k] = in.s[k][N - 1];
+        if (stale) st.edge[par][wid][SP + k] = in.sj[k][N - 1];
+      }
+    }
+    // a row's parameters and the fault flag, once per row
+    if (seg == 0 && tid == 0) {
+      st.fault = has_fault(a.ctrl);
+      st.rp = load_row<CELL>(a, row);
+    }
+    __syncthreads();
+    if (st.fault) break;   // the same decision in every wave
+    const RowPar<CELL> rp = st.rp;
+    // the step before the wave's first: h0 at a row's start, else the previous wave's last
+    // step (for wave 0, the previous tile's last wave's)
+    if (lane == 0) {
+      const int b = row / D, d = row - b * D;
+      const bool first = seg == 0 && wid == 0;
+      const float* e = wid > 0 ? st.edge[par][wid - 1] : st.edge[par ^ 1][PNR_WAVES - 1];
+#pragma unroll
+      for (int k = 0; k < SP; ++k) {
+        const float init = a.h0 ? a.h0[(size_t)b * S + (size_t)k * D + d] : 0.f;
+        in.p[k] = first ? init : (v.cur_zero ? 0.f : e[k]);
+        if (stale) in.pj[k] = first ? init : (v.jac_zero ? 0.f : e[SP + k]);
+      }
+    }
+    const int nrow = seg + 1 < tpr ? row : row + (int)gridDim.x;
+    const int nseg = seg + 1 < tpr ? seg + 1 : 0;
+    const bool more = j + 1 < n_steps;
+    if (more) stage_issue<CELL, N>(a, v, stale, nrow, nseg, st);
+    carry = diag_tile<CELL, N, RESID_ONLY>(a, sh, in, rp, row, seg, 0, true, carry, v, blk_max);
+    if (nseg == 0) carry = DeltaOf<E>::zero();
+    row = nrow;
+    seg = nseg;
+    if (more) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's staged loads have landed
+      stage_read<CELL, N>(v, stale, st, in);
+    }
+    if constexpr (RESID_ONLY) __syncthreads();
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // no staged load outlives the walk
+}
+
 __device__ __forceinline__ int pick_next(int cur, int jac, int nbuf) {
   for (int i = 0; i < nbuf; ++i)
     if (i != cur && i != jac) return i;
@@ -361,7 +518,7 @@ __device__ __forceinline__ int pick_next(int cur, int jac, int nbuf) {
 // Registers capped at 128 VGPRs (four waves per SIMD) to keep enough loads in flight.
 template <int CELL> constexpr int diag_min_waves() { return 4; }
 
-template <int CELL, int N>
+template <int CELL, int N, bool STAGED>
 __global__ void __launch_bounds__(PNR_BLOCK, diag_min_waves<CELL>()) diag_newton_kernel(DiagLoopArgs a) {
   using C = DiagCell<CELL>;
   using E = typename C::E;
@@ -393,23 +550,37 @@ __global__ void __launch_bounds__(PNR_BLOCK, diag_min_waves<CELL>()) diag_newton
     uint32_t blk_max = 0;
     // Static assignment, items in increasing order per block: with a co-resident grid
     // the lowest unfinished tile never waits on anything, so the look-back always ends.
+    if constexpr (STAGED) {
+      __shared__ __align__(16) WalkStage<CELL, N> st;
+      if (resid_only)
+        walk_staged<CELL, N, true>(a, sh, st, v, false, n_items, blk_max);
+      else
+        walk_staged<CELL, N, false>(a, sh, st, v, v.stale, n_items, blk_max);
+    } else {
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
       if (a.walk) {
         Dl carry = DeltaOf<E>::zero();
         for (int seg = 0; seg < a.tiles_per_row; ++seg) {
+          const RowPar<CELL> rp = load_row<CELL>(a, item);
+          TileIn<CELL, N> in;
+          load_tile<CELL, N>(a, item, seg, true, v.stale && !resid_only, v, in);
           if (resid_only)
-            diag_tile<CELL, N, true>(a, sh, item, seg, 0, true, carry, v, blk_max);
+            diag_tile<CELL, N, true>(a, sh, in, rp, item, seg, 0, true, carry, v, blk_max);
           else
-            carry = diag_tile<CELL, N, false>(a, sh, item, seg, 0, true, carry, v, blk_max);
+            carry = diag_tile<CELL, N, false>(a, sh, in, rp, item, seg, 0, true, carry, v, blk_max);
         }
       } else {
         const int row = item / a.tiles_per_row, seg = item - row * a.tiles_per_row;
+        const RowPar<CELL> rp = load_row<CELL>(a, row);
+        TileIn<CELL, N> in;
+        load_tile<CELL, N>(a, row, seg, false, v.stale && !resid_only, v, in);
         if (resid_only)
-          diag_tile<CELL, N, true>(a, sh, row, seg, item, false, DeltaOf<E>::zero(), v, blk_max);
+          diag_tile<CELL, N, true>(a, sh, in, rp, row, seg, item, false, DeltaOf<E>::zero(), v, blk_max);
         else
-          diag_tile<CELL, N, false>(a, sh, row, seg, item, false, DeltaOf<E>::zero(), v, blk_max);
+          diag_tile<CELL, N, false>(a, sh, in, rp, row, seg, item, false, DeltaOf<E>::zero(), v, blk_max);
       }
       if (has_fault(ctrl)) break;
+    }
     }
     // ---- two-level residual max: block partial -> global; the barrier's last block merges ----
     blk_max = wave_max_u32(blk_max);
@@ -563,10 +734,20 @@ int diag_slot_words(int cell) {
                                     : DiagCell<PNR_CELL_GRU_DIAG>::AGG_WORDS + DiagCell<PNR_CELL_GRU_DIAG>::PRE_WORDS;
 }
 
+// The row walk with LDS staging: the LSTM with full tiles.
+bool diag_staged(int cell, int walk, int T) {
+  return cell == PNR_CELL_LSTM_DIAG && walk && T % (PNR_BLOCK * diag_n<PNR_CELL_LSTM_DIAG>()) == 0;
+}
+
 template <int CELL>
 static int diag_capacity(int num_cu) {
-  // per device and thread-safe (cached_occupancy)
-  int per_cu = cached_occupancy((const void*)diag_newton_kernel<CELL, diag_n<CELL>()>, 0);
+  // per device and thread-safe (cached_occupancy); the smaller of the two variants, so that
+  // the grid fits whichever is launched
+  int per_cu = cached_occupancy((const void*)diag_newton_kernel<CELL, diag_n<CELL>(), false>, 0);
+  if constexpr (CELL == PNR_CELL_LSTM_DIAG) {
+    const int staged = cached_occupancy((const void*)diag_newton_kernel<CELL, diag_n<CELL>(), true>, 0);
+    if (staged < per_cu) per_cu = staged;
+  }
   if (per_cu < 1) per_cu = 1;
   long g = (long)per_cu * num_cu;
   return (int)(g > kMaxGrid ? kMaxGrid : g);
@@ -579,8 +760,11 @@ int diag_grid_capacity(int cell, int num_cu) {
 
 hipError_t launch_diag_newton(int cell, const DiagLoopArgs& a, int grid, hipStream_t st) {
   void* args[] = {const_cast<DiagLoopArgs*>(&a)};
-  const void* fn = cell == PNR_CELL_GRU_DIAG ? (const void*)diag_newton_kernel<PNR_CELL_GRU_DIAG, diag_n<PNR_CELL_GRU_DIAG>()>
-                                             : (const void*)diag_newton_kernel<PNR_CELL_LSTM_DIAG, diag_n<PNR_CELL_LSTM_DIAG>()>;
+  const void* fn =
+      cell == PNR_CELL_GRU_DIAG ? (const void*)diag_newton_kernel<PNR_CELL_GRU_DIAG, diag_n<PNR_CELL_GRU_DIAG>(), false>
+      : diag_staged(cell, a.walk, a.T)
+          ? (const void*)diag_newton_kernel<PNR_CELL_LSTM_DIAG, diag_n<PNR_CELL_LSTM_DIAG>(), true>
+          : (const void*)diag_newton_kernel<PNR_CELL_LSTM_DIAG, diag_n<PNR_CELL_LSTM_DIAG>(), false>;
   return launch_persistent(fn, grid, 0, args, st);
 }
 
