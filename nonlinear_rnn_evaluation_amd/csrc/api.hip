@@ -184,13 +184,13 @@ Mark mark_begin(hipStream_t st) {
   Mark m;
   if (!g_prof.on) return m;
   m.a = g_prof.next();
-  if (m.a) hipEventRecord(m.a, st);
+  if (m.a) (void)hipEventRecord(m.a, st);
   return m;
 }
 void mark_end(Mark& m, hipStream_t st) {
   if (!g_prof.on || !m.a) return;
   m.b = g_prof.next();
-  if (m.b) hipEventRecord(m.b, st);
+  if (m.b) (void)hipEventRecord(m.b, st);
 }
 double mark_ms(const Mark& m) {
   float ms = 0.f;
