@@ -321,13 +321,12 @@ def run_workload(name, steps, warmup, mode=None, with_cpu=True, cpu_budget=12.0,
 
 
 def dense_adjoint_bytes(w, updates):
-    """Algorithmic HBM bytes of the dense GRU's adjoint refinement, per (b, t, channel): the
-    U^T product reads the recurrent-gate gradients and writes its result (16 B); the
-    residual reads g, the adjoint, two gate factors and that result and writes the scan's
-    two inputs (28 B); the scan reads them and writes the step (12 B); the update reads the
-    step, the adjoint and four gate factors and writes the adjoint and the next gradients
-    (40 B): 96 B per iteration, plus 16 B to clear the adjoint and gradients first."""
-    return w.B * w.T * w.D * (96 * updates + 16)
+    """Algorithmic HBM bytes of the dense GRU's adjoint refinement loop (one persistent
+    kernel), per (b, t, channel): each of the updates + 1 residual passes reads g, the
+    adjoint, v = U^T dgh and two gate factors (20 B); each of the updates then re-reads
+    those and four more gate factors and writes the next adjoint and its v (44 B; the
+    recurrent-gate gradients stay in LDS).  Plus 8 B to clear the adjoint and v first."""
+    return w.B * w.T * w.D * (20 * (updates + 1) + 44 * updates + 8)
 
 
 def adjoint_bytes(w):
@@ -405,8 +404,8 @@ def run_backward(name, steps, warmup, parity=True):
             pmc = json.load(f)
         if pmc.get("kernel_src_sha") == src_hash(ksrc):
             traffic = pmc.get("bytes_per_launch")
-    kname = ("adjoint refinement loop (MFMA GEMM, residual, scan and update kernels; one read-back per 4 "
-             "iterations)" if dense else "pnr::adjoint_diag_kernel")
+    kname = ("pnr::gru_bwd_loop_kernel (persistent refinement loop, one read-back per call)" if dense
+             else "pnr::adjoint_diag_kernel")
     roof = {"kernel": kname, "avg_launch_us": round(adj_ms * 1e3 / launches, 3), "launches_per_step": launches,
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,

@@ -963,13 +963,12 @@ int validate_backward(const pnr_cell* c) {
   return 0;
 }
 constexpr int kBwdMaxIters = 256;      // refinement iterations of the dense adjoint
-constexpr int kBwdGroup = 4;           // iterations between read-backs of the residuals
 constexpr double kBwdTolRel = 2e-5;    // stop when max |R| <= kBwdTolRel * max |g|
 
 // Dense GRU: every array [B*T][.] row-major, fp32.
 struct DenseBwdLayout {
   size_t gx = 0, gh = 0, hprev = 0, F = 0, lam = 0, dgh = 0, v = 0, scan3 = 0, ut = 0, xt = 0, wt = 0, rmax = 0,
-         part = 0, total = 0;
+         part = 0, v2 = 0, bnd = 0, ctrl = 0, hist = 0, partials = 0, total = 0;
 };
 DenseBwdLayout make_dense_bwd_layout(const pnr_cell* c) {
   DenseBwdLayout l;
@@ -991,6 +990,14 @@ DenseBwdLayout make_dense_bwd_layout(const pnr_cell* c) {
   l.wt = off; off = align_up(off + f * Din * GD);
   l.rmax = off; off = align_up(off + sizeof(uint32_t) * (kBwdMaxIters + 1));
   l.part = off; off = align_up(off + f * kSplitKSlices * GD * (D > Din ? D : Din));   // split-K partials
+  // the on-device refinement loop: the second v buffer, each chunk's boundary (lam, v),
+  // the control block with the residual history right after it (one read-back), and
+  // the per-block residual maxima
+  l.v2 = off; off = align_up(off + f * BT * D);
+  l.bnd = off; off = align_up(off + 2 * f * chunks);
+  l.ctrl = off; off = align_up(off + sizeof(Ctrl));
+  l.hist = off; off = align_up(off + sizeof(double) * (kBwdMaxIters + 1));
+  l.partials = off; off = align_up(off + sizeof(uint32_t) * kMaxGrid);
   l.total = off;
   return l;
 }
@@ -1035,10 +1042,6 @@ int backward_dense(const pnr_cell* cell, const pnr_params* params, const void* x
   float* carry = reinterpret_cast<float*>(agg + chunks);
   uint32_t* rmax = reinterpret_cast<uint32_t*>(ws + l.rmax);
   const float* U = static_cast<const float*>(params->U);
-  static thread_local uint32_t* host_words = nullptr;
-  if (!host_words)
-    PNR_HIP(hipHostMalloc(reinterpret_cast<void**>(&host_words), sizeof(uint32_t) * (kBwdMaxIters + 1),
-                          hipHostMallocDefault));
 
   Mark m_first = mark_begin(st);
   Mark m_proj = mark_begin(st);
@@ -1053,21 +1056,17 @@ int backward_dense(const pnr_cell* cell, const pnr_params* params, const void* x
   mark_end(m_proj, st);
 
   // ---- adjoint: quasi-Newton refinement from lam = 0 ----
-  // Residuals are read back after every group of kBwdGroup iterations; the refinement
-  // stops after the group whose check passed, so the returned adjoint may have had a few
-  // more (contracting) updates than the residual history shows checks before the pass.
   Mark m_adj = mark_begin(st);
   PNR_HIP(launch_fill_zero(lam, n, st));
-  PNR_HIP(launch_fill_zero(dgh, BT * GD, st));
-  PNR_HIP(launch_fill_zero(reinterpret_cast<float*>(rmax), kBwdMaxIters + 1, st));
-  int status = PNR_NOT_CONVERGED, k = 0, updates = 0;
-  double rho0 = 0.0, rho = 0.0;
+  int status = PNR_NOT_CONVERGED, updates = 0;
+  double rho = 0.0;
   std::vector<double> hist;
   const GemmArgs gv{dgh, UT, nullptr, v, (int)BT, D, GD, 0, 0, 0, GD, GD, D, 1, 0};
-  bool done = false;
   if (jdiag) {
     // the diagonal approximation: the first update from lam = 0 is the diagonal system's
     // exact solution (R(0) = g, one diagonal scan); nothing to refine or read back
+    PNR_HIP(launch_fill_zero(reinterpret_cast<float*>(rmax), 1, st));
+    PNR_HIP(launch_fill_zero(dgh, BT * GD, st));   // dgh(0): v = U^T dgh = 0
     PNR_HIP(launch_gemm(PNR_F32, PNR_F32, gv, st));
     PNR_HIP(launch_gru_bwd_refine(F, lam, v, static_cast<const float*>(grad_h), lam2, dgh, agg, carry, rmax, B, T, D,
                                   st));
@@ -1075,32 +1074,47 @@ int backward_dense(const pnr_cell* cell, const pnr_params* params, const void* x
     updates = 1;
     status = PNR_OK;
     hist.push_back(0.0);
-    done = true;
-  }
-  while (!done) {
-    const int k1 = std::min(k + kBwdGroup - 1, kBwdMaxIters);
-    for (int j = k; j <= k1; ++j) {
-      // residual of lam (max into rmax[j]), then lam2 = lam + delta and its gate gradients
-      PNR_HIP(launch_gemm(PNR_F32, PNR_F32, gv, st));
-      PNR_HIP(launch_gru_bwd_refine(F, lam, v, static_cast<const float*>(grad_h), lam2, dgh, agg, carry, rmax + j,
-                                    B, T, D, st));
-      std::swap(lam, lam2);
-      ++updates;
-    }
-    PNR_HIP(hipMemcpyAsync(host_words + k, rmax + k, sizeof(uint32_t) * (k1 - k + 1), hipMemcpyDeviceToHost, st));
+  } else {
+    // the whole refinement on the device: one persistent loop decides when to stop (the
+    // adjoint returned is the one whose residual passed) and is read back once
+    PNR_HIP(launch_fill_zero(v, n, st));   // v_0 = U^T dgh(0) = 0
+    PNR_HIP(launch_fill_zero(fp(l.bnd), 2 * chunks, st));
+    Ctrl* ctrl = reinterpret_cast<Ctrl*>(ws + l.ctrl);
+    PNR_HIP(launch_init(ctrl, nullptr, 0, nullptr, 0, st));
+    BwdLoopArgs la{};
+    la.F = F;
+    la.g = static_cast<const float*>(grad_h);
+    la.U = U;
+    la.lam[0] = lam; la.lam[1] = lam2;
+    la.v[0] = v; la.v[1] = fp(l.v2);
+    la.agg = agg;
+    la.carry = carry;
+    la.bnd = reinterpret_cast<float2*>(ws + l.bnd);
+    la.partials = reinterpret_cast<uint32_t*>(ws + l.partials);
+    la.ctrl = ctrl;
+    la.hist = reinterpret_cast<double*>(ws + l.hist);
+    la.B = B; la.T = T; la.D = D; la.nch = gru_bwd_chunks(T);
+    la.max_iters = kBwdMaxIters;
+    la.tol_rel = kBwdTolRel;
+    PNR_HIP(launch_gru_bwd_loop(la, num_cu, st));
+    constexpr size_t kRb = sizeof(double) * (kBwdMaxIters + 1);
+    alignas(64) static thread_local char rb[sizeof(Ctrl) + 256 + kRb];
+    const size_t rb_bytes = (l.hist - l.ctrl) + kRb;
+    if (rb_bytes > sizeof(rb)) return fail(PNR_E_INVALID, "control read-back of %zu bytes exceeds %zu", rb_bytes,
+                                           sizeof(rb));
+    PNR_HIP(hipMemcpyAsync(rb, ws + l.ctrl, rb_bytes, hipMemcpyDeviceToHost, st));
     PNR_HIP(hipStreamSynchronize(st));
-    for (int j = k; j <= k1; ++j) {
-      const uint32_t bits = host_words[j];
-      float rf;
-      memcpy(&rf, &bits, sizeof(rf));
-      rho = bits >= 0x7f800000u ? INFINITY : (double)rf;   // NaN counts as +inf
-      hist.push_back(rho);
-      if (j == 0) rho0 = rho;
-      if (!std::isfinite(rho)) { status = PNR_NONFINITE; done = true; break; }
-      if (rho <= kBwdTolRel * rho0) { status = PNR_OK; done = true; break; }
-    }
-    k = k1 + 1;
-    if (k > kBwdMaxIters) done = true;
+    Ctrl hc;
+    memcpy(&hc, rb, sizeof(Ctrl));
+    if (hc.fault)
+      return fail(PNR_E_HIP, "device loop gave up waiting (grid barrier); results are not valid");
+    if (!hc.done || hc.iters < 0) return fail(PNR_E_HIP, "device loop did not record a decision");
+    const double* hh = reinterpret_cast<const double*>(rb + (l.hist - l.ctrl));
+    hist.assign(hh, hh + hc.iters + 1);
+    status = hc.status;
+    updates = hc.iters;
+    rho = hc.rho;
+    if (hc.result_buf == 1) std::swap(lam, lam2);   // `lam` is the returned adjoint
   }
   mark_end(m_adj, st);
 

@@ -98,7 +98,7 @@ __global__ void __launch_bounds__(256) gru_bwd_gates_kernel(const float* __restr
 // Pass 1 composes each chunk's map delta_{end} -> delta_{start} (and max |R|); pass 2
 // walks the chunks of each channel; pass 3 re-walks each chunk from its carry, writes
 // lam + delta into the other adjoint buffer and the recurrent-gate gradients of it.
-constexpr int kChunk = 32;
+constexpr int kChunk = 16;
 constexpr int kBatch = 8;   // steps whose loads are issued together
 
 struct StepIn {   // per-step inputs of one lane
@@ -336,6 +336,286 @@ hipError_t launch_row_sum(const float* M, int rows, size_t cols, float* out, flo
   const size_t seg = (cols + S - 1) / S;
   hipLaunchKernelGGL(row_sum_kernel, dim3(rows, S), dim3(256), 0, st, M, cols, seg, part);
   return launch_sum_slices(part, S, rows, out, st);
+}
+
+
+// ---- the whole refinement loop in one persistent, co-resident grid ----
+// Iteration k on the adjoint lam_k (with v_k = U^T dgh(lam_k)):
+//   A. each wave, for its fixed chunks: R and the chunk's map delta_{end} -> delta_{start}
+//      (as pass 1 above), and max |R|;
+//   grid barrier: the final block merges the maxima, records rho_k and decides (stop when
+//      rho_k <= tol_rel rho_0, on a non-finite rho, or after max_iters updates), so the
+//      adjoint returned is exactly the one whose residual passed;
+//   B. one wave per (b, channel) walks the chunk maps into each chunk's carry (as the
+//      carry kernel, with lane shuffles);
+//   grid barrier;
+//   C. each wave, for its chunks: lam_{k+1} = lam_k + delta from the carry (as pass 3),
+//      and v_{k+1} = U^T dgh(lam_{k+1}) for the chunk's steps and for the step after it.
+//      Keeping that boundary step's lam and v with the chunk means pass A of the next
+//      iteration reads nothing another wave wrote, so no third barrier is needed.
+// Chunk maps and carries cross blocks: written and read with agent-scope atomics (the
+// grid barrier orders only those).  Everything else a wave reads it wrote itself.
+// v: the chunk's 16 dgh rows (staged by each wave in LDS) times [U_r; U_z; U_n] on fp32
+// MFMA (16x16x4; four 16-channel column tiles, 48 k-steps over the 3 x 64 padded rows),
+// the operands of U kept in LDS in fragment order; the boundary row on VALU.
+constexpr int kLoopWaves = 8;
+constexpr int kDgLd = 3 * 64 + 4;   // staged row stride: 16 rows x 4 k of an A fragment hit 64 banks
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+
+__global__ void __launch_bounds__(64 * kLoopWaves, 1) gru_bwd_loop_kernel(BwdLoopArgs a) {
+  static_assert(kChunk == 16, "a chunk is one 16-row MFMA tile");
+  __shared__ __align__(16) float dg[kLoopWaves][kChunk + 1][kDgLd];
+  // usf[kk][nt][l] = U_g[j][16 nt + l % 16] with g * 64 + j = 4 kk + l / 16 (zero past D):
+  // the B operand of k-step kk, column tile nt, for lane l -- one contiguous 256-B read
+  __shared__ float usf[48][4][64];
+  __shared__ uint32_t s_wmax[kLoopWaves];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, tid = threadIdx.x;
+  const int D = a.D, T = a.T, nch = a.nch;
+  const size_t n = (size_t)a.B * T * D;
+  const bool act = lane < D;
+  Ctrl* ctrl = a.ctrl;
+  for (int idx = tid; idx < 48 * 4 * 64; idx += 64 * kLoopWaves) {
+    const int kk = idx >> 8, nt = (idx >> 6) & 3, l = idx & 63;
+    const int K = 4 * kk + (l >> 4), g = K >> 6, j = K & 63, ch = 16 * nt + (l & 15);
+    usf[kk][nt][l] = (j < D && ch < D) ? a.U[(size_t)(g * D + j) * D + ch] : 0.f;
+  }
+  __syncthreads();
+  const int gw = blockIdx.x * kLoopWaves + wid, nw = gridDim.x * kLoopWaves;
+  const int ntask = a.B * nch, nrow = a.B * D;
+  float(*dgw)[kDgLd] = dg[wid];
+  int cur = 0;
+  for (int k = 0; k <= a.max_iters; ++k) {
+    const float* lam = a.lam[cur];
+    const float* vv = a.v[cur];
+    // ---- A: residual and chunk maps ----
+    uint32_t m = 0;
+    for (int task = gw; task < ntask; task += nw) {
+      const int b = task / nch, c = task - b * nch;
+      const int t0 = c * kChunk, t1 = min(T, t0 + kChunk);
+      const size_t base = (size_t)b * T * D + lane;
+      if (!act) continue;
+      // every load of the chunk first (indices clamped into it), then the recurrence
+      StepIn in[kChunk];
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) in[u] = load_step(a.g, lam, a.F, vv, n, base + (size_t)min(t0 + u, t1 - 1) * D);
+      float nlam = 0.f, nv = 0.f, nz = 0.f, nd = 0.f;   // the step after the current one
+      if (t1 < T) {
+        const float2 bv = a.bnd[(size_t)task * D + lane];
+        nlam = bv.x;
+        nv = bv.y;
+        nz = a.F[base + (size_t)t1 * D];
+        nd = a.F[n + base + (size_t)t1 * D];
+      }
+      float P = 1.f, Q = 0.f;
+#pragma unroll
+      for (int u = kChunk - 1; u >= 0; --u) {
+        if (t0 + u < t1) {
+          const float R = in[u].g + fmaf(nz, nlam, nv) - in[u].lam;
+          m = max(m, abs_bits(R));
+          P *= nd;
+          Q = fmaf(nd, Q, R);
+          nlam = in[u].lam; nv = in[u].v; nz = in[u].z; nd = in[u].d;
+        }
+      }
+      float* ag = reinterpret_cast<float*>(a.agg + (size_t)task * D + lane);
+      coherent_store(ag, P);
+      coherent_store(ag + 1, Q);
+    }
+    m = wave_max_u32(m);
+    if (lane == 0) s_wmax[wid] = m;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t bm = s_wmax[0];
+      for (int w = 1; w < kLoopWaves; ++w) bm = max(bm, s_wmax[w]);
+      __hip_atomic_store(&a.partials[blockIdx.x], bm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    grid_barrier(ctrl, [&]() {
+      uint32_t mm = 0;
+      for (int i = tid; i < (int)gridDim.x; i += 64 * kLoopWaves)
+        mm = max(mm, __hip_atomic_load(&a.partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      mm = wave_max_u32(mm);
+      __syncthreads();
+      if (lane == 0) s_wmax[wid] = mm;
+      __syncthreads();
+      if (tid == 0) {
+        for (int w = 0; w < kLoopWaves; ++w) mm = max(mm, s_wmax[w]);
+        const double rho = bits_to_rho(mm);
+        const double rho0 = k == 0 ? rho : coherent_load(&a.hist[0]);
+        finish_iteration(ctrl, a.hist, rho, k, cur, a.max_iters, a.tol_rel * rho0);
+        if (k == 0) coherent_store(&a.hist[0], rho);
+      }
+    });
+    if (__hip_atomic_load(&ctrl->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) || has_fault(ctrl)) break;
+
+    // ---- B: carries (delta at the first step after each chunk), lane order = reverse time ----
+    // The chunk maps of up to kCarryGroups groups of 64 are loaded together (one round trip)
+    // and scanned group by group in registers.
+    constexpr int kCarryGroups = 4;
+    for (int task = gw; task < nrow; task += nw) {
+      const int b = task / D, i = task - b * D;
+      float x = 0.f;
+      for (int h0 = 0; h0 < nch; h0 += 64 * kCarryGroups) {
+        float P[kCarryGroups], Q[kCarryGroups];
+#pragma unroll
+        for (int h = 0; h < kCarryGroups; ++h) {
+          const int c = nch - 1 - (h0 + 64 * h + lane);
+          P[h] = 1.f;
+          Q[h] = 0.f;
+          if (c >= 0) {
+            const float* ag = reinterpret_cast<const float*>(a.agg + ((size_t)b * nch + c) * D + i);
+            P[h] = coherent_load(ag);
+            Q[h] = coherent_load(ag + 1);
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < kCarryGroups; ++h) {
+          const int c = nch - 1 - (h0 + 64 * h + lane);
+          float p_ = P[h], q_ = Q[h];
+#pragma unroll
+          for (int off = 1; off < 64; off <<= 1) {
+            const float pp = __shfl_up(p_, off, 64), pq = __shfl_up(q_, off, 64);
+            if (lane >= off) {
+              q_ = fmaf(p_, pq, q_);
+              p_ *= pp;
+            }
+          }
+          const float pp = __shfl_up(p_, 1, 64), pq = __shfl_up(q_, 1, 64);
+          const float xin = lane == 0 ? x : fmaf(pp, x, pq);
+          if (c >= 0) coherent_store(a.carry + ((size_t)b * nch + c) * D + i, xin);
+          x = fmaf(__shfl(p_, 63, 64), x, __shfl(q_, 63, 64));
+        }
+      }
+    }
+    grid_barrier(ctrl, [] {});
+    if (has_fault(ctrl)) break;
+
+    // ---- C: the update and the next v ----
+    float* lam_n = a.lam[cur ^ 1];
+    float* v_n = a.v[cur ^ 1];
+    for (int task = gw; task < ntask; task += nw) {
+      const int b = task / nch, c = task - b * nch;
+      const int t0 = c * kChunk, t1 = min(T, t0 + kChunk);
+      const size_t base = (size_t)b * T * D + lane;
+      const bool tail = t1 < T;   // the step after the chunk exists
+      // The chunk in two batches of kBatch steps, latest first.  The first batch's loads
+      // are issued before the carry and the boundary step's, so that they share one round
+      // trip; the boundary row is staged once both have landed.
+      float dl = 0.f, nlam = 0.f, nv = 0.f, nz = 0.f, nd = 0.f, lb = 0.f;
+      for (int h = kChunk / kBatch - 1; h >= 0; --h) {
+        const int u0 = h * kBatch;
+        StepIn in[kBatch];
+        float fg[kBatch][4];   // the gate factors f_r, f_z, f_n, r
+        if (act) {
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {
+            const size_t e = base + (size_t)min(t0 + u0 + u, t1 - 1) * D;
+            in[u] = load_step(a.g, lam, a.F, vv, n, e);
+            fg[u][0] = a.F[5 * n + e];
+            fg[u][1] = a.F[2 * n + e];
+            fg[u][2] = a.F[3 * n + e];
+            fg[u][3] = a.F[4 * n + e];
+          }
+        }
+        if (h == kChunk / kBatch - 1) {
+          float ft[4] = {0.f, 0.f, 0.f, 0.f};
+          if (act) {
+            dl = coherent_load(a.carry + (size_t)task * D + lane);   // delta at t1
+            if (tail) {
+              const float2 bv = a.bnd[(size_t)task * D + lane];
+              const size_t e = base + (size_t)t1 * D;
+              nlam = bv.x;
+              nv = bv.y;
+              nz = a.F[e];
+              nd = a.F[n + e];
+              ft[0] = a.F[5 * n + e];
+              ft[1] = a.F[2 * n + e];
+              ft[2] = a.F[3 * n + e];
+              ft[3] = a.F[4 * n + e];
+            }
+          }
+          lb = nlam + dl;   // lam_{k+1} at t1
+          if (tail) {
+            dgw[kChunk][lane] = ft[0] * lb;
+            dgw[kChunk][64 + lane] = ft[1] * lb;
+            dgw[kChunk][128 + lane] = ft[2] * lb * ft[3];
+          }
+        }
+#pragma unroll
+        for (int u = kBatch - 1; u >= 0; --u) {
+          const int t = t0 + u0 + u;
+          if (t < t1) {
+            float l = 0.f;
+            if (act) {
+              const float R = in[u].g + fmaf(nz, nlam, nv) - in[u].lam;
+              dl = fmaf(nd, dl, R);
+              l = in[u].lam + dl;
+              lam_n[base + (size_t)t * D] = l;
+              nlam = in[u].lam; nv = in[u].v; nz = in[u].z; nd = in[u].d;
+            }
+            dgw[u0 + u][lane] = act ? fg[u][0] * l : 0.f;
+            dgw[u0 + u][64 + lane] = act ? fg[u][1] * l : 0.f;
+            dgw[u0 + u][128 + lane] = act ? fg[u][2] * l * fg[u][3] : 0.f;
+          }
+        }
+      }
+      // the rows just written are read back by every lane of this wave
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
+      // rows 0..15 on MFMA: lane l ends with V[4 (l / 16) + i][16 nt + l % 16]
+      const int m16 = lane & 15, q4 = lane >> 4;
+      v4f_t acc4[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc4[nt] = v4f_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int kk = 0; kk < 48; ++kk) {
+        const float av = dgw[m16][4 * kk + q4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          acc4[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, usf[kk][nt][lane], acc4[nt], 0, 0, 0);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int ch = 16 * nt + m16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 4 * q4 + i;
+          if (row < t1 - t0 && ch < D) v_n[((size_t)b * T + t0 + row) * D + ch] = acc4[nt][i];
+        }
+      }
+      // the boundary row on VALU: lane = channel, U_g[j][lane] read back from usf
+      if (tail) {
+        float accb = 0.f;
+#pragma unroll 4
+        for (int kk = 0; kk < 48; ++kk) {
+          const float4 d4 = *reinterpret_cast<const float4*>(&dgw[kChunk][4 * kk]);
+          const float* uq = usf[kk][lane >> 4];
+          accb = fmaf(uq[lane & 15], d4.x, accb);
+          accb = fmaf(uq[16 + (lane & 15)], d4.y, accb);
+          accb = fmaf(uq[32 + (lane & 15)], d4.z, accb);
+          accb = fmaf(uq[48 + (lane & 15)], d4.w, accb);
+        }
+        if (act) a.bnd[(size_t)task * D + lane] = make_float2(lb, accb);
+      }
+      // the staging rows are rewritten by this wave's next chunk only after these reads
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_wave_barrier();
+    }
+    cur ^= 1;
+  }
+}
+
+hipError_t launch_gru_bwd_loop(const BwdLoopArgs& a, int num_cu, hipStream_t st) {
+  if (a.D > 64) return hipErrorInvalidValue;
+  constexpr int threads = 64 * kLoopWaves;
+  int per_cu = cached_occupancy((const void*)gru_bwd_loop_kernel, 0, threads);
+  if (per_cu < 1) return hipErrorInvalidConfiguration;
+  long g = (long)per_cu * num_cu;
+  if (g > kMaxGrid) g = kMaxGrid;
+  const long work = (long)a.B * a.nch;
+  if (g > work) g = work;
+  if (g < 1) g = 1;
+  void* args[] = {const_cast<BwdLoopArgs*>(&a)};
+  return launch_persistent((const void*)gru_bwd_loop_kernel, (int)g, 0, args, st, threads);
 }
 
 }  // namespace pnr

@@ -14,10 +14,12 @@ constexpr int kGxPadRows = 128;
 // Resident blocks of `fn` per CU with `lds` bytes of dynamic LDS (raising the kernel's
 // LDS limit first when needed), 0 when it cannot run.  Cached per (kernel, LDS size):
 // the runtime queries cost tens of microseconds per call.
-int cached_occupancy(const void* fn, size_t lds);
+// `threads`: the kernel's block size (most persistent kernels use PNR_BLOCK).
+int cached_occupancy(const void* fn, size_t lds, int threads = PNR_BLOCK);
 // launch of a grid sized to the resident capacity (cooperative, or ordinary when
-// PNR_COOPERATIVE=0)
-hipError_t launch_persistent(const void* fn, int grid, size_t lds, void** args, hipStream_t st);
+// PNR_COOPERATIVE=0), with blocks of `threads` threads
+hipError_t launch_persistent(const void* fn, int grid, size_t lds, void** args, hipStream_t st,
+                             int threads = PNR_BLOCK);
 
 // ---------------------------------------------------------------------------------
 // Decision taken by the block that merges the residual partials of iteration k (the
@@ -148,6 +150,25 @@ hipError_t launch_gru_bwd_refine(const float* F, const float* lam, const float* 
                                  float* dgh, float2* agg, float* carry, uint32_t* rmax, int B, int T, int D,
                                  hipStream_t st);
 int gru_bwd_chunks(int T);
+// The dense GRU's adjoint refinement as one persistent loop (D <= 64): lam[0], v[0] and
+// bnd start at zero; on return ctrl and hist hold the decision as for the Newton loops,
+// and lam[ctrl->result_buf] is the adjoint whose residual passed.
+struct BwdLoopArgs {
+  const float* F;      // gate factors [6][B*T*D]: z, d, f_z, f_n, r, f_r
+  const float* g;      // dL/dh [B][T][D]
+  const float* U;      // [3D][D]
+  float* lam[2];       // adjoint iterates [B][T][D]
+  float* v[2];         // U^T dgh(lam) [B][T][D]
+  float2* agg;         // chunk maps [B][nch][D]
+  float* carry;        // delta at the first step after each chunk [B][nch][D]
+  float2* bnd;         // per chunk, (lam, v) of the iterate at the step after it [B][nch][D]
+  uint32_t* partials;  // per-block residual maxima
+  Ctrl* ctrl;
+  double* hist;        // [max_iters + 1]
+  int B, T, D, nch, max_iters;
+  double tol_rel;      // stop when rho_k <= tol_rel * rho_0
+};
+hipError_t launch_gru_bwd_loop(const BwdLoopArgs& a, int num_cu, hipStream_t st);
 hipError_t launch_gru_bwd_dh0(const float* F, const float* lam, const float* v, float* dh0, int B, int T, int D,
                               hipStream_t st);
 // C [M][N] = A [M][K] B[N][K]^T (fp32) for a long K and small M x N: K cut into at most

@@ -9,8 +9,8 @@
 
 namespace pnr {
 
-int cached_occupancy(const void* fn, size_t lds) {
-  struct Entry { const void* fn; size_t lds; int dev, v; };
+int cached_occupancy(const void* fn, size_t lds, int threads) {
+  struct Entry { const void* fn; size_t lds; int threads, dev, v; };
   static Entry cache[64];
   static int n = 0;
   static std::mutex mu;
@@ -18,11 +18,12 @@ int cached_occupancy(const void* fn, size_t lds) {
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   std::lock_guard<std::mutex> lock(mu);
   for (int i = 0; i < n; ++i)
-    if (cache[i].fn == fn && cache[i].lds == lds && cache[i].dev == dev) return cache[i].v;
+    if (cache[i].fn == fn && cache[i].lds == lds && cache[i].threads == threads && cache[i].dev == dev)
+      return cache[i].v;
   int v = 0;
   if (lds <= 65536 || hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess)
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, fn, PNR_BLOCK, lds) != hipSuccess) v = 0;
-  if (n < 64) cache[n++] = Entry{fn, lds, dev, v};
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, fn, threads, lds) != hipSuccess) v = 0;
+  if (n < 64) cache[n++] = Entry{fn, lds, threads, dev, v};
   return v;
 }
 
@@ -35,13 +36,13 @@ int cached_occupancy(const void* fn, size_t lds) {
 // error, never a hang.  PNR_COOPERATIVE=0 (read once per process) selects the ordinary
 // launch, about 15-20 us cheaper per call, for callers that run nothing else on the
 // device at the same time.
-hipError_t launch_persistent(const void* fn, int grid, size_t lds, void** args, hipStream_t st) {
+hipError_t launch_persistent(const void* fn, int grid, size_t lds, void** args, hipStream_t st, int threads) {
   static const bool coop = [] {
     const char* e = getenv("PNR_COOPERATIVE");
     return !(e && e[0] == '0');
   }();
-  if (coop) return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(PNR_BLOCK), args, (unsigned)lds, st);
-  return hipLaunchKernel(fn, dim3(grid), dim3(PNR_BLOCK), args, lds, st);
+  if (coop) return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(threads), args, (unsigned)lds, st);
+  return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, lds, st);
 }
 
 __global__ void init_kernel(Ctrl* ctrl, uint64_t* slots, size_t n, uint64_t* partials, size_t np) {
