@@ -44,8 +44,7 @@ def newton_kernel(w, mode):
     """(kernel name as the profiler lists it, source file) of the Newton loop kernel."""
     from nonlinear_rnn_evaluation_amd import workloads as WL
     if w.damping is not None and w.cell == WL.CELL_GRU:
-        return ("quasi-ELK loop (recurrent GEMM, cell, filter and smoother scans; one read-back per iteration)",
-                CSRC + "dense_elk.hip")
+        return "pnr::gru_elk_loop_kernel", CSRC + "dense_elk.hip"
     if w.damping is not None and w.cell == WL.CELL_LSTM_DIAG and mode == WL.JAC_FULL:
         return "pnr::elk2_lstm_kernel", CSRC + "elk2.hip"
     if w.damping is not None:
@@ -80,13 +79,14 @@ def projection_fused(w, mode):
 
 
 def dense_damped_iteration_bytes(w, k, resid=False):
-    """Algorithmic HBM bytes of one iteration of the dense GRU's damped (quasi-ELK) loop,
-    per (b, t, channel): shift the iterate (8 B), the recurrent GEMM (read 4, write 12 B),
-    the cell (read Gx 12, Gh 12, h_{t-1} 4, h 4; write r and J 8 B), the filter (read J, r
-    8 B; then J, r, h 12 B and write G, e 8 B) and the smoother (read G, e 8 B; then 8 B
-    and write the next iterate 4 B): 112 B; the residual-only pass stops after the cell
-    (64 B)."""
-    return w.B * w.T * w.D * (64 if resid else 112)
+    """Algorithmic HBM bytes of one iteration of the dense GRU's damped (quasi-ELK) loop
+    kernel, per (b, t, channel): the cell pass reads the gate inputs (12 B) and the iterate
+    (4 B) and writes r and J (8 B); the filter pass reads J, r and the iterate (12 B) and
+    writes the smoother's gain and offset (8 B); the smoother pass reads them (8 B) and
+    writes the next iterate (4 B): 56 B.  The pass whose residual ends the loop stops after
+    the cell pass (24 B).  Chunk maps, carries and boundary values (about 1/16 of the
+    per-step planes) are not counted."""
+    return w.B * w.T * w.D * (24 if resid else 56)
 
 
 def damped_iteration_bytes(w, k, resid=False, mode=None):
@@ -254,8 +254,8 @@ def run_workload(name, steps, warmup, mode=None, with_cpu=True, cpu_budget=12.0,
             bytes_call += sum(iteration_bytes(wc, k, it, resid=(ro and k == it)) for k in range(it + 1))
     elif w.damping is not None:
         if w.cell == WL.CELL_GRU:
-            bytes_call = sum(dense_damped_iteration_bytes(w, k, resid=(resid_last and k == passes - 1))
-                             for k in range(passes))
+            # the loop stops after the cell pass of its last iteration, converged or not
+            bytes_call = sum(dense_damped_iteration_bytes(w, k, resid=(k == passes - 1)) for k in range(passes))
         else:
             bytes_call = sum(damped_iteration_bytes(w, k, resid=(resid_last and k == passes - 1), mode=mode)
                              for k in range(passes))

@@ -234,18 +234,19 @@ int device_info(int* num_cu) {
 // pageable memory of fixed size: the library holds no pinned host allocation, so nothing
 // is left to release at exit), one stream synchronisation; then the call's results and,
 // in measurement mode, its per-phase timing.  Returns the call's status.
-constexpr size_t kReadBackMax = 4096 + sizeof(double) * (PNR_MAX_ITERS + 1);
-int finish_call(const Layout& l, char* ws, int max_iters, hipStream_t st, const Mark& m_first, const Mark& m_proj,
-                const Mark& m_newton, const Mark& m_out) {
+// The history follows the control block after at most 255 bytes of alignment.
+constexpr size_t kReadBackMax = sizeof(Ctrl) + 256 + sizeof(double) * (PNR_MAX_ITERS + 1);
+int finish_call(size_t ctrl_off, size_t hist_off, char* ws, int max_iters, hipStream_t st, const Mark& m_first,
+                const Mark& m_proj, const Mark& m_newton, const Mark& m_out) {
   alignas(64) static thread_local char rb[kReadBackMax];
-  const size_t rb_bytes = (l.hist - l.ctrl) + sizeof(double) * (max_iters + 1);
+  const size_t rb_bytes = (hist_off - ctrl_off) + sizeof(double) * (max_iters + 1);
   if (rb_bytes > kReadBackMax) return fail(PNR_E_INVALID, "control read-back of %zu bytes exceeds %zu", rb_bytes,
                                            kReadBackMax);
-  PNR_HIP(hipMemcpyAsync(rb, ws + l.ctrl, rb_bytes, hipMemcpyDeviceToHost, st));
+  PNR_HIP(hipMemcpyAsync(rb, ws + ctrl_off, rb_bytes, hipMemcpyDeviceToHost, st));
   PNR_HIP(hipStreamSynchronize(st));
   Ctrl hc;
   memcpy(&hc, rb, sizeof(Ctrl));
-  const double* hh = reinterpret_cast<const double*>(rb + (l.hist - l.ctrl));
+  const double* hh = reinterpret_cast<const double*>(rb + (hist_off - ctrl_off));
   if (hc.fault)
     return fail(PNR_E_HIP, "device loop gave up waiting (%s); results are not valid",
                 hc.fault == 1 ? "look-back" : "grid barrier");
@@ -474,7 +475,7 @@ int eval_impl(const pnr_cell* cell, const pnr_params* params, const void* x, con
   mark_end(m_out, st);
   mark_end(m_first, st);
 
-  return finish_call(l, ws, max_iters, st, m_first, m_proj, m_newton, m_out);
+  return finish_call(l.ctrl, l.hist, ws, max_iters, st, m_first, m_proj, m_newton, m_out);
 }
 }  // namespace
 
@@ -629,8 +630,8 @@ int validate_damped(const pnr_cell* c, int jac_mode) {
 }
 // The dense GRU's damped loop (host-driven, [B][T][D] / [B][T][3D] fp32 arrays).
 struct DenseElkLayout {
-  size_t gx = 0, gh = 0, hprev = 0, h[2] = {0, 0}, R = 0, J = 0, G = 0, E = 0, agg = 0, carry = 0, agg2 = 0,
-         carry2 = 0, rmax = 0, total = 0;
+  size_t gx = 0, h[2] = {0, 0}, R = 0, J = 0, G = 0, E = 0, agg = 0, carry = 0, agg2 = 0, carry2 = 0, head = 0,
+         tailge = 0, hb = 0, partials = 0, ctrl = 0, hist = 0, total = 0;
 };
 DenseElkLayout make_dense_elk_layout(const pnr_cell* c) {
   DenseElkLayout l;
@@ -638,18 +639,22 @@ DenseElkLayout make_dense_elk_layout(const pnr_cell* c) {
   const size_t ch = (size_t)c->B * elk_dense_chunks(c->T) * D;
   size_t off = 0;
   l.gx = off; off = align_up(off + f * BT * 3 * D);
-  l.gh = off; off = align_up(off + f * BT * 3 * D);
-  l.hprev = off; off = align_up(off + f * BT * D);
   for (int i = 0; i < 2; ++i) { l.h[i] = off; off = align_up(off + f * BT * D); }
   l.R = off; off = align_up(off + f * BT * D);
   l.J = off; off = align_up(off + f * BT * D);
   l.G = off; off = align_up(off + f * BT * D);
   l.E = off; off = align_up(off + f * BT * D);
-  l.agg = off; off = align_up(off + f * 7 * ch);
+  l.agg = off; off = align_up(off + f * 8 * ch);
   l.carry = off; off = align_up(off + f * 2 * ch);
   l.agg2 = off; off = align_up(off + f * 2 * ch);
   l.carry2 = off; off = align_up(off + f * ch);
-  l.rmax = off; off = align_up(off + sizeof(uint32_t) * (PNR_MAX_ITERS + 1));
+  l.head = off; off = align_up(off + f * 3 * ch);
+  l.tailge = off; off = align_up(off + f * 2 * ch);
+  l.hb = off; off = align_up(off + f * ch);
+  l.partials = off; off = align_up(off + sizeof(uint32_t) * kMaxGrid);
+  // the control block and the residual history, adjacent: one read-back
+  l.ctrl = off; off = align_up(off + sizeof(Ctrl));
+  l.hist = off; off = align_up(off + sizeof(double) * (PNR_MAX_ITERS + 1));
   l.total = off;
   return l;
 }
@@ -670,74 +675,53 @@ size_t pnr_workspace_bytes_damped(const pnr_cell* cell, int jac_mode) {
 }
 
 namespace {
-// quasi-ELK for the dense GRU: per iteration the recurrent GEMM, the cell, one read-back of
-// max |R| (the returned iterate is the one whose residual was checked), then the filter and
-// smoother scans.
+// quasi-ELK for the dense GRU: the input projection, then the whole loop in one persistent
+// launch (the returned iterate is the one whose residual was checked), the returned
+// iterate copied out on the device, and one read-back of the decision and the history.
 int eval_damped_dense(const pnr_cell* cell, const pnr_params* params, const void* x, const void* h0, void* h_out,
                       int max_iters, double tol, float lam) {
   const DenseElkLayout l = make_dense_elk_layout(cell);
   const int D = cell->D, T = cell->T, B = cell->B, Din = cell->D_in, GD = 3 * D;
   const size_t BT = (size_t)B * T, n = BT * D;
+  const int nch = elk_dense_chunks(T);
+  int num_cu = 0, rc = 0;
+  if ((rc = device_info(&num_cu))) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(cell->stream);
   char* ws = static_cast<char*>(cell->workspace);
   auto fp = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
-  float *gx = fp(l.gx), *gh = fp(l.gh), *hprev = fp(l.hprev), *R = fp(l.R), *J = fp(l.J);
-  float* H[2] = {fp(l.h[0]), fp(l.h[1])};
-  uint32_t* rmax = reinterpret_cast<uint32_t*>(ws + l.rmax);
-  const float* U = static_cast<const float*>(params->U);
-  static thread_local uint32_t* host_word = nullptr;
-  if (!host_word) PNR_HIP(hipHostMalloc(reinterpret_cast<void**>(&host_word), 256, hipHostMallocDefault));
-
   Mark m_first = mark_begin(st);
   Mark m_proj = mark_begin(st);
-  GemmArgs gp{x, params->W, params->b_x, gx, (int)BT, GD, Din, 0, 0, 0, Din, Din, GD, 1, 0};
+  GemmArgs gp{x, params->W, params->b_x, fp(l.gx), (int)BT, GD, Din, 0, 0, 0, Din, Din, GD, 1, 0};
   PNR_HIP(launch_gemm(cell->x_dtype, PNR_F32, gp, st));
   mark_end(m_proj, st);
   Mark m_loop = mark_begin(st);
-  PNR_HIP(launch_fill_zero(reinterpret_cast<float*>(rmax), max_iters + 1, st));
-  PNR_HIP(launch_fill_zero(H[0], n, st));   // the zero guess, stored
-  const GemmArgs gq{hprev, U, params->b_h, gh, (int)BT, GD, D, 0, 0, 0, D, D, GD, 1, 0};
-  int cur = 0, k = 0, status = PNR_NOT_CONVERGED;
-  double rho = 0.0;
-  std::vector<double> hist;
-  for (;; ++k) {
-    PNR_HIP(launch_gru_shift_states(H[cur], static_cast<const float*>(h0), hprev, B, T, D, st));
-    PNR_HIP(launch_gemm(PNR_F32, PNR_F32, gq, st));
-    PNR_HIP(launch_gru_elk_cell(gx, gh, hprev, H[cur], U, R, J, rmax + k, n, D, st));
-    PNR_HIP(hipMemcpyAsync(host_word, rmax + k, sizeof(uint32_t), hipMemcpyDeviceToHost, st));
-    PNR_HIP(hipStreamSynchronize(st));
-    float rf;
-    memcpy(&rf, host_word, sizeof(rf));
-    rho = *host_word >= 0x7f800000u ? INFINITY : (double)rf;   // NaN counts as +inf
-    hist.push_back(rho);
-    if (!std::isfinite(rho)) { status = PNR_NONFINITE; break; }
-    if (rho <= tol) { status = PNR_OK; break; }
-    if (k == max_iters) break;
-    PNR_HIP(launch_gru_elk_step(J, R, H[cur], lam, fp(l.agg), fp(l.carry), fp(l.G), fp(l.E), fp(l.agg2),
-                                fp(l.carry2), H[cur ^ 1], B, T, D, st));
-    cur ^= 1;
-  }
+  PNR_HIP(launch_fill_zero(fp(l.h[0]), n, st));                     // the zero guess, stored
+  PNR_HIP(launch_fill_zero(fp(l.hb), (size_t)B * nch * D, st));     // ... and its chunk halos
+  Ctrl* ctrl = reinterpret_cast<Ctrl*>(ws + l.ctrl);
+  PNR_HIP(launch_init(ctrl, nullptr, 0, nullptr, 0, st));
+  ElkLoopArgs a{};
+  a.gx = fp(l.gx);
+  a.U = static_cast<const float*>(params->U);
+  a.bh = static_cast<const float*>(params->b_h);
+  a.h0 = static_cast<const float*>(h0);
+  a.H[0] = fp(l.h[0]);
+  a.H[1] = fp(l.h[1]);
+  a.R = fp(l.R); a.J = fp(l.J); a.G = fp(l.G); a.E = fp(l.E);
+  a.agg = fp(l.agg); a.carry = fp(l.carry); a.agg2 = fp(l.agg2); a.carry2 = fp(l.carry2);
+  a.head = fp(l.head); a.tailge = fp(l.tailge); a.hb = fp(l.hb);
+  a.partials = reinterpret_cast<uint32_t*>(ws + l.partials);
+  a.ctrl = ctrl;
+  a.hist = reinterpret_cast<double*>(ws + l.hist);
+  a.B = B; a.T = T; a.D = D; a.nch = nch; a.max_iters = max_iters;
+  a.lam = lam;
+  a.tol = tol;
+  PNR_HIP(launch_gru_elk_loop(a, num_cu, st));
   mark_end(m_loop, st);
   Mark m_out = mark_begin(st);
-  PNR_HIP(hipMemcpyAsync(h_out, H[cur], sizeof(float) * n, hipMemcpyDeviceToDevice, st));
+  PNR_HIP(launch_elk_dense_output(a.H[0], a.H[1], ctrl, static_cast<float*>(h_out), n, st));
   mark_end(m_out, st);
   mark_end(m_first, st);
-  PNR_HIP(hipStreamSynchronize(st));
-  g_last.iters = k;
-  g_last.residual = rho;
-  g_last.hist.assign(hist.data(), hist.data() + hist.size());
-  if (g_prof.on) {
-    pnr_profile p{};
-    p.total_ms = mark_ms(m_first);
-    p.proj_ms = mark_ms(m_proj);
-    p.newton_ms = mark_ms(m_loop);
-    p.out_ms = mark_ms(m_out);
-    p.passes = k + 1;
-    p.resid_only = k == max_iters;
-    g_prof.last = p;
-    g_prof.valid = true;
-  }
-  return status;
+  return finish_call(l.ctrl, l.hist, ws, max_iters, st, m_first, m_proj, m_loop, m_out);
 }
 }  // namespace
 
@@ -819,7 +803,7 @@ int pnr_eval_damped(const pnr_cell* cell, const pnr_params* params, const void* 
   PNR_HIP(launch_diag_output(bufs, ctrl, static_cast<float*>(h_out), B, S, T, st));
   mark_end(m_out, st);
   mark_end(m_first, st);
-  return finish_call(l, ws, max_iters, st, m_first, m_proj, m_newton, m_out);
+  return finish_call(l.ctrl, l.hist, ws, max_iters, st, m_first, m_proj, m_newton, m_out);
 }
 
 // ---- chunked evaluation ----

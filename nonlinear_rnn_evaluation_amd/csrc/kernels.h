@@ -180,15 +180,37 @@ hipError_t launch_gemm_split_k(const float* A, int lda, const float* Bm, int ldb
 // (partials in `part`: 32 * rows floats) summed in a fixed order
 hipError_t launch_row_sum(const float* M, int rows, size_t cols, float* out, float* part, hipStream_t st);
 
-// Damped (quasi-ELK) step of the dense GRU (dense_elk.hip), [B][T][D] layout, D <= 64.
+// Damped (quasi-ELK) loop of the dense GRU (dense_elk.hip), [B][T][D] layout, D <= 64: one
+// persistent, co-resident grid runs every iteration and records the decision in ctrl.
 int elk_dense_chunks(int T);
-hipError_t launch_gru_elk_cell(const float* gx, const float* gh, const float* hprev, const float* H, const float* U,
-                               float* R, float* J, uint32_t* rmax, size_t n, int D, hipStream_t st);
-// filter + smoother: agg [B*chunks][7][D], carry [B*chunks][2][D], agg2 [B*chunks][2][D],
-// carry2 [B*chunks][D]; G, E, Hn [B][T][D]
-hipError_t launch_gru_elk_step(const float* J, const float* R, const float* H, float lam, float* agg, float* carry,
-                               float* Gc, float* Ec, float* agg2, float* carry2, float* Hn, int B, int T, int D,
-                               hipStream_t st);
+struct ElkLoopArgs {
+  const float* gx;     // x W^T + b_x [B][T][3D]
+  const float* U;      // [3D][D]
+  const float* bh;     // [3D] or nullptr
+  const float* h0;     // [B][D] or nullptr
+  float* H[2];         // iterates [B][T][D]; H[0] holds the zero guess at launch
+  float* R;            // residual of the iterate [B][T][D]
+  float* J;            // quasi Jacobian of the iterate [B][T][D]
+  float* G;            // smoother gain [B][T][D]
+  float* E;            // smoother offset [B][T][D]
+  float* agg;          // filter chunk maps [B][D][nch][8]
+  float* carry;        // filter state (u, n) entering each chunk [B][nch][2][D]
+  float* agg2;         // smoother chunk maps (P, Q) [B][D][nch][2]
+  float* carry2;       // smoothed state at the step after each chunk [B][nch][D]
+  float* head;         // (J, R, h) at each chunk's first step [B][nch][3][D]
+  float* tailge;       // (G, e) at each chunk's last step [B][nch][2][D]
+  float* hb;           // state before each chunk's first step [B][nch][D]; zero at launch
+  uint32_t* partials;  // per-block residual maxima
+  Ctrl* ctrl;
+  double* hist;        // [max_iters + 1]
+  int B, T, D, nch, max_iters;
+  float lam;           // damping
+  double tol;          // stop when rho_k <= tol
+};
+hipError_t launch_gru_elk_loop(const ElkLoopArgs& a, int num_cu, hipStream_t st);
+// out [n] = H[ctrl->result_buf] (the loop's decision, read on the device)
+hipError_t launch_elk_dense_output(const float* H0, const float* H1, const Ctrl* ctrl, float* out, size_t n,
+                                   hipStream_t st);
 
 int diag_items_per_thread(int cell);
 int diag_slot_words(int cell);

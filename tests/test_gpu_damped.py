@@ -185,18 +185,22 @@ def test_lstm_elk_converged_equals_sequential():
 
 
 # Dense GRU (quasi-ELK): the iteration against the oracle's Kalman-smoother step with the
-# diagonal of the dense Jacobian; chunks of 32 steps in the filter and smoother scans, so
-# lengths span many chunks and a ragged last one.
+# diagonal of the dense Jacobian.  The device loop cuts the sequence into chunks of 16
+# steps (one MFMA row tile) that cross waves only through their boundary values, so the
+# lengths span one partial chunk, exactly one, many with a ragged last one, and (B = 3,
+# T = 11000: 2064 chunks) more chunks than a full grid has waves; D = 1, 7 and 40 leave
+# most of the 64 padded channels of the recurrent product empty.
 GRU = WL.CELL_GRU
 
 
-@pytest.mark.parametrize("D,T", [(16, 37), (16, 1000), (64, 333), (40, 1500)])
+@pytest.mark.parametrize("B,D,T", [(2, 16, 37), (2, 16, 1000), (2, 64, 333), (2, 40, 1500), (2, 1, 17),
+                                   (2, 7, 5), (1, 64, 16), (3, 8, 11000)])
 @pytest.mark.parametrize("lam", [0.05, 1.0])
-def test_dense_gru_fixed_iterations_match_damped_oracle(D, T, lam):
-    p = WL.random_problem(GRU, 2, T, D, 5, seed=D + T, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32, bias_std=0.2,
+def test_dense_gru_fixed_iterations_match_damped_oracle(B, D, T, lam):
+    p = WL.random_problem(GRU, B, T, D, 5, seed=D + T, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32, bias_std=0.2,
                           h0_std=0.3, w_std=0.7 / math.sqrt(D))
     q = _f64(p)
-    print(f"# damped dense GRU D={D} T={T} lam={lam}", flush=True)
+    print(f"# damped dense GRU B={B} D={D} T={T} lam={lam}", flush=True)
     got = _run(p, 3, -1.0, WL.JAC_DIAG, lam, cell=GRU)
     ref = O.newton_dense(GRU, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], 3, -1.0, WL.JAC_DIAG,
                          solver="loop", damping=lam)

@@ -1,8 +1,8 @@
 """Full-size parity: every named workload at its full shape, through the same C ABI call
 and launch configuration the benchmark times, against the fp64 sequential oracle.
 
-Dense-GRU workloads are compared on every output.  The damped (quasi-ELK) variant of the
-long diagonal GRU and the chunked long LSTM are included: they converge to the same
+Dense-GRU workloads are compared on every output.  The damped (quasi-ELK) variants of the
+dense GRU and of the long diagonal GRU, and the chunked long LSTM, are included: they converge to the same
 trajectory.  The backward pass is checked at full size on sampled channels against the
 BPTT oracle (last test).  For the diagonal-recurrence cells a
 set of 256 evenly spaced channels is compared over every step (the benchmark compares
@@ -68,7 +68,7 @@ def _check(name, mode):
     assert err <= bar, (name, mode, err)
 
 
-CASES = [(name, mode) for name in WL.WORKLOAD_ORDER + ["gru_diag_long_elk", "lstm_diag_long_chunked",
+CASES = [(name, mode) for name in WL.WORKLOAD_ORDER + ["gru_diag_long_elk", "gru_quasi_elk", "lstm_diag_long_chunked",
                                                        "lstm_diag_long_adaptive", "lstm_diag_long_stiff_bounded",
                                                        "lstm_diag_long_elk"]
          for mode in WL.get_workload(name).jac_modes]
