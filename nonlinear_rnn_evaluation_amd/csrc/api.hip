@@ -631,7 +631,7 @@ int validate_damped(const pnr_cell* c, int jac_mode) {
 // The dense GRU's damped loop (host-driven, [B][T][D] / [B][T][3D] fp32 arrays).
 struct DenseElkLayout {
   size_t gx = 0, h[2] = {0, 0}, R = 0, J = 0, G = 0, E = 0, agg = 0, carry = 0, agg2 = 0, carry2 = 0, head = 0,
-         tailge = 0, hb = 0, partials = 0, ctrl = 0, hist = 0, total = 0;
+         tailge = 0, hb = 0, rmax = 0, ctrl = 0, hist = 0, total = 0;
 };
 DenseElkLayout make_dense_elk_layout(const pnr_cell* c) {
   DenseElkLayout l;
@@ -651,7 +651,7 @@ DenseElkLayout make_dense_elk_layout(const pnr_cell* c) {
   l.head = off; off = align_up(off + f * 3 * ch);
   l.tailge = off; off = align_up(off + f * 2 * ch);
   l.hb = off; off = align_up(off + f * ch);
-  l.partials = off; off = align_up(off + sizeof(uint32_t) * kMaxGrid);
+  l.rmax = off; off = align_up(off + sizeof(uint32_t) * (PNR_MAX_ITERS + 1));
   // the control block and the residual history, adjacent: one read-back
   l.ctrl = off; off = align_up(off + sizeof(Ctrl));
   l.hist = off; off = align_up(off + sizeof(double) * (PNR_MAX_ITERS + 1));
@@ -697,6 +697,7 @@ int eval_damped_dense(const pnr_cell* cell, const pnr_params* params, const void
   Mark m_loop = mark_begin(st);
   PNR_HIP(launch_fill_zero(fp(l.h[0]), n, st));                     // the zero guess, stored
   PNR_HIP(launch_fill_zero(fp(l.hb), (size_t)B * nch * D, st));     // ... and its chunk halos
+  PNR_HIP(launch_fill_zero(fp(l.rmax), (size_t)max_iters + 1, st));
   Ctrl* ctrl = reinterpret_cast<Ctrl*>(ws + l.ctrl);
   PNR_HIP(launch_init(ctrl, nullptr, 0, nullptr, 0, st));
   ElkLoopArgs a{};
@@ -709,7 +710,7 @@ int eval_damped_dense(const pnr_cell* cell, const pnr_params* params, const void
   a.R = fp(l.R); a.J = fp(l.J); a.G = fp(l.G); a.E = fp(l.E);
   a.agg = fp(l.agg); a.carry = fp(l.carry); a.agg2 = fp(l.agg2); a.carry2 = fp(l.carry2);
   a.head = fp(l.head); a.tailge = fp(l.tailge); a.hb = fp(l.hb);
-  a.partials = reinterpret_cast<uint32_t*>(ws + l.partials);
+  a.rmax = reinterpret_cast<uint32_t*>(ws + l.rmax);
   a.ctrl = ctrl;
   a.hist = reinterpret_cast<double*>(ws + l.hist);
   a.B = B; a.T = T; a.D = D; a.nch = nch; a.max_iters = max_iters;

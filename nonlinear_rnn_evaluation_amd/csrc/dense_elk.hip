@@ -46,8 +46,8 @@ namespace pnr {
 constexpr int kEChunk = 16;                 // steps per chunk: one 16-row MFMA tile
 constexpr int kElkWaves = 8;
 constexpr int kStLd = 64 + 4;               // staged h_{t-1} rows: 16 rows x 4 k of an A fragment hit 64 banks
-constexpr int kGhLd = 3 * 64 + 4;           // transposed gh rows
-constexpr int kCarryGroups = 4;             // chunk maps loaded together per carry round trip
+constexpr int kWaveLds = 3 * 64 * kEChunk;  // per wave: the staged rows, then gh transposed
+static_assert(kEChunk * kStLd <= kWaveLds, "staged rows fit the per-wave buffer");
 typedef float v4f_t __attribute__((ext_vector_type(4)));
 
 int elk_dense_chunks(int T) { return (T + kEChunk - 1) / kEChunk; }
@@ -70,236 +70,290 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// Grid-wide barrier for this loop.  Two-level arrival on agent-scope counters as in the
+// library's grid barrier, but the counters only ever grow: barrier n (counted from 0 in
+// this launch; the control block is zero at launch and every block passes the same
+// barriers in order) is complete at a group counter of members * (n + 1) and a top
+// counter of groups * (n + 1), so nothing is reset and no store needs draining on the way.
+// Each arrival is issued after the block's own stores have completed, and the value an
+// atomic returns shows every earlier arrival performed, so the block that completes the
+// top counter knows every block's data is visible before it publishes generation n + 1.
+// Returns false when this block's wait ran out (the fault is recorded); such a block
+// leaves the loop and the others give up at the next barrier, so every wave ends.
+__device__ __forceinline__ bool elk_grid_sync(Ctrl* c, uint32_t& gen) {
+  __shared__ int s_ok;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    drain_memory_ops();
+    const uint32_t g = blockIdx.x % kBarGroups;
+    const uint32_t members = (gridDim.x - g + kBarGroups - 1) / kBarGroups;
+    const uint32_t groups = gridDim.x < (unsigned)kBarGroups ? gridDim.x : (unsigned)kBarGroups;
+    bool released = false;
+    if (atomicAdd(&c->bar_group[g].count, 1u) == members * (gen + 1u) - 1u) {
+      if (atomicAdd(&c->bar_top, 1u) == groups * (gen + 1u) - 1u) {
+        __hip_atomic_store(&c->bar_gen, gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        released = true;
+      }
+    }
+    int ok = 1;
+    if (!released) {
+      uint32_t spins = 0;
+      while (__hip_atomic_load(&c->bar_gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
+        backoff(spins);
+        if (++spins > kSpinLimit) {
+          record_fault(c, 2);
+          ok = 0;
+          break;
+        }
+      }
+    }
+    s_ok = ok;
+  }
+  ++gen;
+  __syncthreads();
+  return s_ok != 0;
+}
+
+// A chunk's per-step values in one wave's registers (lane = channel).
+struct ChunkRegs {
+  float xg[kEChunk][3];   // gate inputs x W^T + b_x
+  float hv[kEChunk];      // the iterate
+  float hp;               // the state before the chunk's first step
+  float jv[kEChunk];      // quasi Jacobian (cell -> filter)
+  float rv[kEChunk];      // residual (cell -> filter)
+  float gv[kEChunk];      // smoother gain (filter -> smoother)
+  float ev[kEChunk];      // smoother offset (filter -> smoother)
+};
+
+// RES: every chunk has a wave of its own (B * nch <= waves of the grid), and the chunk's
+// per-step values stay in that wave's registers for the whole launch; the iterate is still
+// written out every iteration (the last one written is the result).  Otherwise a wave
+// loops over its chunks and keeps those values in the workspace planes.
+// Every array of a ChunkRegs is assigned in full by the phase that produces it (rows past
+// a ragged chunk's end and lanes past D compute on clamped, finite inputs, and only their
+// side effects are masked), so each value is live only from its producer to its consumer.
+template <bool RES>
 __global__ void __launch_bounds__(64 * kElkWaves, 1) gru_elk_loop_kernel(ElkLoopArgs a) {
-  // per wave: the staged h_{t-1} rows [16][kStLd] (MFMA A operand), then, over them, gh
-  // transposed [16][kGhLd]
-  __shared__ __align__(16) float wbuf[kElkWaves][kEChunk * kGhLd];
-  // uf[kk][nt][l] = U_g[c][j], g = nt / 4, c = 16 (nt % 4) + l % 16, j = 4 kk + l / 16
-  // (zero past D): the B operand of k-step kk, column tile nt, for lane l
-  __shared__ float uf[16][12][64];
+  // One pool, the operand table first (so that every read of it is a base register plus an
+  // immediate offset below 64 KiB):
+  //  ufv[kk][l][nt] = U_g[c][j], g = nt / 4, c = 16 (nt % 4) + l % 16, j = 16 (l / 16) + kk
+  //    (zero past D): the B operands of k-step kk for lane l, 12 column tiles, read as three
+  //    16-byte vectors (a lane stride of 48 bytes: 16 lanes cover the 64 banks once);
+  //  then per wave the staged h_{t-1} rows [16][kStLd] (MFMA A operand), and over them gh
+  //    transposed [3][64][16].
+  // The k index is split across lane groups (k = 16 (l / 16) + kk in k-step kk), so a lane's
+  // A operands for all 16 k-steps are 16 consecutive floats of its row.
+  __shared__ __align__(16) float pool[16 * 64 * 12 + kElkWaves * kWaveLds];
+  float* const ufv = pool;
   __shared__ uint32_t s_wmax[kElkWaves];
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, tid = threadIdx.x;
+  __shared__ uint32_t s_rbits;
+  __shared__ Flt s_tot[kElkWaves];       // carry scans: each wave's group total
+  __shared__ float2 s_tot2[kElkWaves];
+  // the wave index is uniform across the wave: saying so keeps every chunk index and base
+  // address derived from it in scalar registers
+  const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), tid = threadIdx.x;
   const int D = a.D, T = a.T, nch = a.nch;
+  // carry scans: groups of 64 chunks per row, waves per row (a power of two up to 8), rows per block
+  const int ngr = (nch + 63) / 64;
+  const int wpr = ngr >= 8 ? 8 : ngr > 2 ? 4 : ngr;
+  const int rpb = kElkWaves / wpr;
   const bool act = lane < D;
+  const int ln = act ? lane : 0;   // the channel whose addresses a lane uses
   const float lam = a.lam;
   Ctrl* ctrl = a.ctrl;
-  for (int idx = tid; idx < 16 * 12 * 64; idx += 64 * kElkWaves) {
-    const int kk = idx / (12 * 64), nt = (idx >> 6) % 12, l = idx & 63;
-    const int g = nt >> 2, c = 16 * (nt & 3) + (l & 15), j = 4 * kk + (l >> 4);
-    uf[kk][nt][l] = (c < D && j < D) ? a.U[(size_t)(g * D + c) * D + j] : 0.f;
+  for (int idx = tid; idx < 16 * 64 * 12; idx += 64 * kElkWaves) {
+    const int kk = idx / (64 * 12), l = (idx / 12) & 63, nt = idx % 12;
+    const int g = nt >> 2, c = 16 * (nt & 3) + (l & 15), j = 16 * (l >> 4) + kk;
+    ufv[idx] = (c < D && j < D) ? a.U[(size_t)(g * D + c) * D + j] : 0.f;
   }
   // per lane (channel): the diagonals U_r[i][i], U_z[i][i], U_n[i][i] and b_h
-  float ud[3] = {0.f, 0.f, 0.f}, bhv[3] = {0.f, 0.f, 0.f};
-  if (act) {
+  float ud[3], bhv[3];
 #pragma unroll
-    for (int g = 0; g < 3; ++g) {
-      ud[g] = a.U[(size_t)(g * D + lane) * D + lane];
-      bhv[g] = a.bh ? a.bh[g * D + lane] : 0.f;
-    }
+  for (int g = 0; g < 3; ++g) {
+    ud[g] = a.U[(size_t)(g * D + ln) * D + ln];
+    bhv[g] = a.bh ? a.bh[g * D + ln] : 0.f;
   }
   __syncthreads();
   const int gw = blockIdx.x * kElkWaves + wid, nw = gridDim.x * kElkWaves;
   const int ntask = a.B * nch, nrow = a.B * D;
-  float* st = wbuf[wid];
+  float* st = pool + 16 * 64 * 12 + wid * kWaveLds;
   const int m16 = lane & 15, q4 = lane >> 4;
-  int cur = 0;
-  for (int k = 0; k <= a.max_iters; ++k) {
-    const float* Hc = a.H[cur];
-    // ---- A: recurrent product, cell, filter chunk maps ----
-    uint32_t m = 0;
-    for (int task = gw; task < ntask; task += nw) {
-      const int b = task / nch, c = task - b * nch;
-      const int t0 = c * kEChunk, len = min(kEChunk, T - t0);
-      const size_t base = (size_t)b * T * D + lane;
-      const float* gxb = a.gx + (size_t)b * T * 3 * D + lane;
-      // every load of the chunk first (rows clamped into it)
-      float hv[kEChunk], xg[kEChunk][3];
-      float hp = 0.f;
-      if (act) {
+
+  // per-step gate inputs, iterate (from Hc) and the state before the chunk
+  auto load_inputs = [&](ChunkRegs& r, int task, const float* Hc) {
+    const int b = task / nch, c = task - b * nch;
+    const int t0 = c * kEChunk, len = min(kEChunk, T - t0);
+    const size_t base = (size_t)b * T * D + ln;
+    const float* gxb = a.gx + (size_t)b * T * 3 * D + ln;
 #pragma unroll
-        for (int u = 0; u < kEChunk; ++u) {
-          const int t = t0 + min(u, len - 1);
-          hv[u] = Hc[base + (size_t)t * D];
+    for (int u = 0; u < kEChunk; ++u) {
+      const int t = t0 + min(u, len - 1);
+      r.hv[u] = Hc ? Hc[base + (size_t)t * D] : 0.f;
 #pragma unroll
-          for (int g = 0; g < 3; ++g) xg[u][g] = gxb[(size_t)t * 3 * D + g * D];
-        }
-        hp = t0 == 0 ? (a.h0 ? a.h0[(size_t)b * D + lane] : 0.f) : a.hb[(size_t)task * D + lane];
-      } else {
+      for (int g = 0; g < 3; ++g) r.xg[u][g] = gxb[(size_t)t * 3 * D + g * D];
+    }
+    const float h0v = a.h0 ? a.h0[(size_t)b * D + ln] : 0.f;
+    r.hp = t0 == 0 ? h0v : (Hc ? a.hb[(size_t)task * D + ln] : 0.f);
+  };
+
+  // A: recurrent product, cell, the chunk's filter map; max |R| into m
+  auto phase_a = [&](ChunkRegs& r, int task, bool valid, uint32_t& m) {
+    const int b = task / nch, c = task - b * nch;
+    const int t0 = c * kEChunk, len = min(kEChunk, T - t0);
+    const size_t base = (size_t)b * T * D + ln;
+    // row u of the A operand: h_{t0+u-1} over the 64 (padded) channels
 #pragma unroll
-        for (int u = 0; u < kEChunk; ++u) {
-          hv[u] = 0.f;
-          xg[u][0] = xg[u][1] = xg[u][2] = 0.f;
-        }
+    for (int u = 0; u < kEChunk; ++u) st[u * kStLd + lane] = act ? (u == 0 ? r.hp : r.hv[u - 1]) : 0.f;
+    wave_lds_sync();
+    // lane l ends with gh[row 4 (l / 16) + i][column 16 nt + l % 16], column = 64 g + c
+    v4f_t acc[12];
+#pragma unroll
+    for (int nt = 0; nt < 12; ++nt) acc[nt] = v4f_t{0.f, 0.f, 0.f, 0.f};
+    float4 av[4];
+    const float4* arow = reinterpret_cast<const float4*>(st + m16 * kStLd + 16 * q4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) av[j] = arow[j];
+    const float4* ub = reinterpret_cast<const float4*>(ufv) + lane * 3;
+    float4 bcur[3], bnxt[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) bcur[j] = ub[j];
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      if (kk + 1 < 16) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) bnxt[j] = ub[(kk + 1) * 192 + j];
       }
-      // row u of the A operand: h_{t0+u-1} over the 64 (padded) channels
-#pragma unroll
-      for (int u = 0; u < kEChunk; ++u) st[u * kStLd + lane] = u == 0 ? hp : hv[u - 1];
-      wave_lds_sync();
-      // lane l ends with gh[row 4 (l / 16) + i][column 16 nt + l % 16], column = 64 g + c
-      v4f_t acc[12];
-#pragma unroll
-      for (int nt = 0; nt < 12; ++nt) acc[nt] = v4f_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-      for (int kk = 0; kk < 16; ++kk) {
-        const float av = st[m16 * kStLd + 4 * kk + q4];
-#pragma unroll
-        for (int nt = 0; nt < 12; ++nt)
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, uf[kk][nt][lane], acc[nt], 0, 0, 0);
-      }
-      wave_lds_sync();   // every read of the staged rows before they are overwritten
+      const float4 a4 = av[kk >> 2];
+      const float aval = (kk & 3) == 0 ? a4.x : (kk & 3) == 1 ? a4.y : (kk & 3) == 2 ? a4.z : a4.w;
+      const float bvals[12] = {bcur[0].x, bcur[0].y, bcur[0].z, bcur[0].w, bcur[1].x, bcur[1].y,
+                               bcur[1].z, bcur[1].w, bcur[2].x, bcur[2].y, bcur[2].z, bcur[2].w};
 #pragma unroll
       for (int nt = 0; nt < 12; ++nt)
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aval, bvals[nt], acc[nt], 0, 0, 0);
+      if (kk + 1 < 16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st[(4 * q4 + i) * kGhLd + 16 * nt + m16] = acc[nt][i];
-      wave_lds_sync();
-      // the cell and the filter map, lane = channel
-      Flt F = flt_identity();
-      if (act) {
+        for (int j = 0; j < 3; ++j) bcur[j] = bnxt[j];
+      }
+    }
+    wave_lds_sync();   // every read of the staged rows before they are overwritten
+    // gh transposed to [gate][channel][16 steps] (4-step groups XOR-swizzled by bits 2..3
+    // of the channel: the 16-byte writes below and the reads after them are conflict-free)
+    float4* gt = reinterpret_cast<float4*>(st);
+#pragma unroll
+    for (int nt = 0; nt < 12; ++nt)
+      gt[((nt >> 2) * 64 + 16 * (nt & 3) + m16) * 4 + (q4 ^ (m16 >> 2))] =
+          make_float4(acc[nt][0], acc[nt][1], acc[nt][2], acc[nt][3]);
+    wave_lds_sync();
+    const int sw = (lane >> 2) & 3;
+    // this lane's channel: gh of the three gates for steps 4j..4j+3, the next group's
+    // loads issued before the current group is used
+    float4 gcur[3], gnxt[3];
+#pragma unroll
+    for (int g = 0; g < 3; ++g) gcur[g] = gt[(g * 64 + lane) * 4 + sw];
+    // the cell and the filter map, lane = channel; every step is computed (rows past a
+    // ragged end on clamped inputs) and only steps < len enter the map and the maximum
+    const bool live = valid && act;
+    Flt F = flt_identity();
+    uint32_t mloc = 0;
+#pragma unroll
+    for (int u = 0; u < kEChunk; ++u) {
+      if ((u & 3) == 0 && u + 4 < kEChunk) {
+#pragma unroll
+        for (int g = 0; g < 3; ++g) gnxt[g] = gt[(g * 64 + lane) * 4 + (((u >> 2) + 1) ^ sw)];
+      }
+      const float4 g0 = gcur[0], g1 = gcur[1], g2 = gcur[2];
+      const int i = u & 3;
+      const float ghr = (i == 0 ? g0.x : i == 1 ? g0.y : i == 2 ? g0.z : g0.w) + bhv[0];
+      const float ghz = (i == 0 ? g1.x : i == 1 ? g1.y : i == 2 ? g1.z : g1.w) + bhv[1];
+      const float ghn = (i == 0 ? g2.x : i == 1 ? g2.y : i == 2 ? g2.z : g2.w) + bhv[2];
+      const float rr = sigm(r.xg[u][0] + ghr);
+      const float z = sigm(r.xg[u][1] + ghz);
+      const float nn = tanh_(fmaf(rr, ghn, r.xg[u][2]));
+      const float p = u == 0 ? r.hp : r.hv[u - 1];
+      const float res = fmaf(z, p - nn, nn) - r.hv[u];
+      const float fz = (p - nn) * z * (1.f - z);
+      const float fn = (1.f - z) * (1.f - nn * nn);
+      const float jj = z + fz * ud[1] + fn * rr * ud[2] + fn * ghn * rr * (1.f - rr) * ud[0];
+      r.jv[u] = jj;
+      r.rv[u] = res;
+      const bool in = u < len;
+      const Flt Fn = compose(filter_step(jj, res, lam), F);
+      F = Flt{in ? Fn.a : F.a, in ? Fn.b : F.b, in ? Fn.c : F.c, in ? Fn.d : F.d,
+              in ? Fn.e : F.e, in ? Fn.f : F.f, in ? Fn.g : F.g};
+      mloc = in ? max(mloc, abs_bits(res)) : mloc;
+      if ((u & 3) == 3 && u + 1 < kEChunk) {
+#pragma unroll
+        for (int g = 0; g < 3; ++g) gcur[g] = gnxt[g];
+      }
+    }
+    if (live) {
+      m = max(m, mloc);
+      if constexpr (!RES) {
 #pragma unroll
         for (int u = 0; u < kEChunk; ++u) {
           if (u < len) {
-            const float ghr = st[u * kGhLd + lane] + bhv[0];
-            const float ghz = st[u * kGhLd + 64 + lane] + bhv[1];
-            const float ghn = st[u * kGhLd + 128 + lane] + bhv[2];
-            const float r = sigm(xg[u][0] + ghr);
-            const float z = sigm(xg[u][1] + ghz);
-            const float nn = tanh_(fmaf(r, ghn, xg[u][2]));
-            const float p = u == 0 ? hp : hv[u - 1];
-            const float res = fmaf(z, p - nn, nn) - hv[u];
-            const float fz = (p - nn) * z * (1.f - z);
-            const float fn = (1.f - z) * (1.f - nn * nn);
-            const float jj = z + fz * ud[1] + fn * r * ud[2] + fn * ghn * r * (1.f - r) * ud[0];
             const size_t e = base + (size_t)(t0 + u) * D;
-            a.R[e] = res;
-            a.J[e] = jj;
-            m = max(m, abs_bits(res));
-            F = compose(filter_step(jj, res, lam), F);
-            if (u == 0) {
-              float* hd = a.head + (size_t)task * 3 * D + lane;
-              coherent_store(hd, jj);
-              coherent_store(hd + D, res);
-              coherent_store(hd + 2 * D, hv[0]);
-            }
+            a.R[e] = r.rv[u];
+            a.J[e] = r.jv[u];
           }
         }
-        float* ag = a.agg + (((size_t)b * D + lane) * nch + c) * 8;
-        coherent_store(ag, F.a);
-        coherent_store(ag + 1, F.b);
-        coherent_store(ag + 2, F.c);
-        coherent_store(ag + 3, F.d);
-        coherent_store(ag + 4, F.e);
-        coherent_store(ag + 5, F.f);
-        coherent_store(ag + 6, F.g);
       }
-      wave_lds_sync();   // the transposed rows are read before the next chunk stages its own
+      float* hd = a.head + (size_t)task * 3 * D + lane;
+      coherent_store(hd, r.jv[0]);
+      coherent_store(hd + D, r.rv[0]);
+      coherent_store(hd + 2 * D, r.hv[0]);
+      float* ag = a.agg + (((size_t)b * D + lane) * nch + c) * 8;
+      coherent_store(ag, F.a);
+      coherent_store(ag + 1, F.b);
+      coherent_store(ag + 2, F.c);
+      coherent_store(ag + 3, F.d);
+      coherent_store(ag + 4, F.e);
+      coherent_store(ag + 5, F.f);
+      coherent_store(ag + 6, F.g);
     }
-    m = wave_max_u32(m);
-    if (lane == 0) s_wmax[wid] = m;
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t bm = s_wmax[0];
-      for (int w = 1; w < kElkWaves; ++w) bm = max(bm, s_wmax[w]);
-      __hip_atomic_store(&a.partials[blockIdx.x], bm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    grid_barrier(ctrl, [&]() {
-      uint32_t mm = 0;
-      for (int i = tid; i < (int)gridDim.x; i += 64 * kElkWaves)
-        mm = max(mm, __hip_atomic_load(&a.partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      mm = wave_max_u32(mm);
-      __syncthreads();
-      if (lane == 0) s_wmax[wid] = mm;
-      __syncthreads();
-      if (tid == 0) {
-        for (int w = 0; w < kElkWaves; ++w) mm = max(mm, s_wmax[w]);
-        finish_iteration(ctrl, a.hist, bits_to_rho(mm), k, cur, a.max_iters, a.tol);
-      }
-    });
-    if (__hip_atomic_load(&ctrl->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) || has_fault(ctrl)) break;
+    wave_lds_sync();   // the transposed rows are read before the next chunk stages its own
+  };
 
-    // ---- B: filter state (u, 1, n) entering each chunk; lane order = time ----
-    for (int task = gw; task < nrow; task += nw) {
-      const int b = task / D, i = task - b * D;
-      const float* ag = a.agg + ((size_t)b * D + i) * nch * 8;
-      V3 x{0.f, 1.f, 0.f};   // entering the first chunk: P = 0, m = 0
-      for (int h0 = 0; h0 < nch; h0 += 64 * kCarryGroups) {
-        Flt F[kCarryGroups];
-#pragma unroll
-        for (int h = 0; h < kCarryGroups; ++h) {
-          const int c = h0 + 64 * h + lane;
-          F[h] = flt_identity();
-          if (c < nch) {
-            const float* p = ag + (size_t)c * 8;
-            F[h] = Flt{coherent_load(p), coherent_load(p + 1), coherent_load(p + 2), coherent_load(p + 3),
-                       coherent_load(p + 4), coherent_load(p + 5), coherent_load(p + 6)};
-          }
-        }
-#pragma unroll
-        for (int h = 0; h < kCarryGroups; ++h) {
-          const int c = h0 + 64 * h + lane;
-          Flt f = F[h];
-#pragma unroll
-          for (int off = 1; off < 64; off <<= 1) {
-            const Flt prev = flt_shfl_up(f, off);
-            if (lane >= off) f = compose(f, prev);
-          }
-          const Flt before = flt_shfl_up(f, 1);
-          const V3 xin = lane == 0 ? x : normalized(apply(before, x));
-          if (c < nch) {
-            float* cp = a.carry + ((size_t)b * nch + c) * 2 * D + i;
-            coherent_store(cp, xin.u);
-            coherent_store(cp + D, xin.n);
-          }
-          x = normalized(apply(flt_shfl(f, 63), x));
-        }
-      }
+  // C: filter walk from the chunk's entering state, smoother gain and offset, the chunk's
+  // smoother map
+  auto phase_c = [&](ChunkRegs& r, int task, bool valid) {
+    const int b = task / nch, c = task - b * nch;
+    const int t0 = c * kEChunk, len = min(kEChunk, T - t0);
+    const size_t base = (size_t)b * T * D + ln;
+    const bool live = valid && act;
+    const float* cp = a.carry + (size_t)task * 2 * D + ln;
+    V3 x{coherent_load(cp), 1.f, coherent_load(cp + D)};
+    const bool tail = t0 + len < T;   // the next chunk exists
+    float jt = 0.f, rt = 0.f, ht = 0.f;
+    if (tail) {
+      const float* hd = a.head + (size_t)(task + 1) * 3 * D + ln;
+      jt = coherent_load(hd);
+      rt = coherent_load(hd + D);
+      ht = coherent_load(hd + 2 * D);
     }
-    grid_barrier(ctrl, [] {});
-    if (has_fault(ctrl)) break;
-
-    // ---- C: filter walk, smoother gain and offset, smoother chunk maps ----
-    for (int task = gw; task < ntask; task += nw) {
-      if (!act) continue;
-      const int b = task / nch, c = task - b * nch;
-      const int t0 = c * kEChunk, len = min(kEChunk, T - t0);
-      const size_t base = (size_t)b * T * D + lane;
-      float jv[kEChunk], rv[kEChunk], hv[kEChunk];
+    float SP = 1.f, SQ = 0.f;   // the chunk's smoother map h'_{t1} -> h'_{t0}, composed forwards
 #pragma unroll
-      for (int u = 0; u < kEChunk; ++u) {
-        const size_t e = base + (size_t)(t0 + min(u, len - 1)) * D;
-        jv[u] = a.J[e];
-        rv[u] = a.R[e];
-        hv[u] = Hc[e];
-      }
-      const float* cp = a.carry + (size_t)task * 2 * D + lane;
-      V3 x{coherent_load(cp), 1.f, coherent_load(cp + D)};
-      const bool tail = t0 + len < T;   // the next chunk exists
-      float jt = 0.f, rt = 0.f, ht = 0.f;
-      if (tail) {
-        const float* hd = a.head + (size_t)(task + 1) * 3 * D + lane;
-        jt = coherent_load(hd);
-        rt = coherent_load(hd + D);
-        ht = coherent_load(hd + 2 * D);
-      }
-      float SP = 1.f, SQ = 0.f;   // the chunk's smoother map h'_{t1} -> h'_{t0}, composed forwards
-#pragma unroll
-      for (int u = 0; u < kEChunk; ++u) {
-        if (u < len) {
-          x = normalized(apply(filter_step(jv[u], rv[u], lam), x));
-          const float P = x.u, mm = x.n;
-          const bool last = u == len - 1;
-          float G = 0.f, e = mm + hv[u];
-          if (!last || tail) {
-            const float jn = last ? jt : jv[min(u + 1, kEChunk - 1)];
-            const float rn = last ? rt : rv[min(u + 1, kEChunk - 1)];
-            const float hn = last ? ht : hv[min(u + 1, kEChunk - 1)];
-            G = P * jn * fast_rcp(fmaf(jn * jn, P, 1.f));
-            e = (mm + hv[u]) - G * (fmaf(jn, mm, rn) + hn);
+    for (int u = 0; u < kEChunk; ++u) {
+      x = normalized(apply(filter_step(r.jv[u], r.rv[u], lam), x));
+      const float P = x.u, mm = x.n;
+      const bool last = u == len - 1;
+      const bool has_next = !last || tail;
+      const float jn = last ? jt : r.jv[min(u + 1, kEChunk - 1)];
+      const float rn = last ? rt : r.rv[min(u + 1, kEChunk - 1)];
+      const float hn = last ? ht : r.hv[min(u + 1, kEChunk - 1)];
+      const float G = has_next ? P * jn * fast_rcp(fmaf(jn * jn, P, 1.f)) : 0.f;
+      const float e = has_next ? (mm + r.hv[u]) - G * (fmaf(jn, mm, rn) + hn) : mm + r.hv[u];
+      r.gv[u] = G;
+      r.ev[u] = e;
+      if (u < len) {
+        SQ = fmaf(SP, e, SQ);
+        SP *= G;
+        if (live) {
+          if constexpr (!RES) {
+            const size_t o = base + (size_t)(t0 + u) * D;
+            a.G[o] = G;
+            a.E[o] = e;
           }
-          const size_t o = base + (size_t)(t0 + u) * D;
-          a.G[o] = G;
-          a.E[o] = e;
-          SQ = fmaf(SP, e, SQ);
-          SP *= G;
           if (last) {
             float* tg = a.tailge + (size_t)task * 2 * D + lane;
             coherent_store(tg, G);
@@ -307,81 +361,209 @@ __global__ void __launch_bounds__(64 * kElkWaves, 1) gru_elk_loop_kernel(ElkLoop
           }
         }
       }
+    }
+    if (live) {
       float* ag2 = a.agg2 + (((size_t)b * D + lane) * nch + c) * 2;
       coherent_store(ag2, SP);
       coherent_store(ag2 + 1, SQ);
     }
-    grid_barrier(ctrl, [] {});
-    if (has_fault(ctrl)) break;
+  };
 
-    // ---- D: smoothed state at the step after each chunk; lane order = reverse time ----
-    for (int task = gw; task < nrow; task += nw) {
-      const int b = task / D, i = task - b * D;
-      const float* ag2 = a.agg2 + ((size_t)b * D + i) * nch * 2;
-      float x = 0.f;   // after the last chunk: unused (the last step's gain is 0)
-      for (int h0 = 0; h0 < nch; h0 += 64 * kCarryGroups) {
-        float P[kCarryGroups], Q[kCarryGroups];
+  // E: smoother walk from the smoothed state after the chunk: the next iterate, and the
+  // state before the chunk from the predecessor's last gain and offset
+  auto phase_e = [&](ChunkRegs& r, int task, bool valid, float* Hn) {
+    const int b = task / nch, c = task - b * nch;
+    const int t0 = c * kEChunk, len = min(kEChunk, T - t0);
+    const size_t base = (size_t)b * T * D + ln;
+    const bool live = valid && act;
+    float x = coherent_load(a.carry2 + (size_t)task * D + ln);
+    float gl = 0.f, el = 0.f;
+    if (c > 0) {
+      const float* tg = a.tailge + (size_t)(task - 1) * 2 * D + ln;
+      gl = coherent_load(tg);
+      el = coherent_load(tg + D);
+    }
 #pragma unroll
-        for (int h = 0; h < kCarryGroups; ++h) {
-          const int c = nch - 1 - (h0 + 64 * h + lane);
-          P[h] = 1.f;
-          Q[h] = 0.f;
-          if (c >= 0) {
-            P[h] = coherent_load(ag2 + (size_t)c * 2);
-            Q[h] = coherent_load(ag2 + (size_t)c * 2 + 1);
-          }
-        }
+    for (int u = kEChunk - 1; u >= 0; --u) {
+      if (u < len) {
+        x = fmaf(r.gv[u], x, r.ev[u]);
+        if (live) Hn[base + (size_t)(t0 + u) * D] = x;
+      }
+      r.hv[u] = x;
+    }
+    const float hb = c > 0 ? fmaf(gl, x, el) : r.hp;
+    if constexpr (RES) r.hp = hb;
+    else if (live && c > 0) a.hb[(size_t)task * D + lane] = hb;
+  };
+
+  // the per-step planes of a chunk, for the looping variant
+  auto load_planes_c = [&](ChunkRegs& r, int task, const float* Hc) {
+    const int b = task / nch, c = task - b * nch;
+    const int t0 = c * kEChunk, len = min(kEChunk, T - t0);
+    const size_t base = (size_t)b * T * D + ln;
 #pragma unroll
-        for (int h = 0; h < kCarryGroups; ++h) {
-          const int c = nch - 1 - (h0 + 64 * h + lane);
-          float p_ = P[h], q_ = Q[h];
+    for (int u = 0; u < kEChunk; ++u) {
+      const size_t e = base + (size_t)(t0 + min(u, len - 1)) * D;
+      r.jv[u] = a.J[e];
+      r.rv[u] = a.R[e];
+      r.hv[u] = Hc[e];
+    }
+  };
+  auto load_planes_e = [&](ChunkRegs& r, int task) {
+    const int b = task / nch, c = task - b * nch;
+    const int t0 = c * kEChunk, len = min(kEChunk, T - t0);
+    const size_t base = (size_t)b * T * D + ln;
 #pragma unroll
-          for (int off = 1; off < 64; off <<= 1) {
-            const float pp = __shfl_up(p_, off, 64), pq = __shfl_up(q_, off, 64);
-            if (lane >= off) {
-              q_ = fmaf(p_, pq, q_);
-              p_ *= pp;
-            }
-          }
-          const float pp = __shfl_up(p_, 1, 64), pq = __shfl_up(q_, 1, 64);
-          const float xin = lane == 0 ? x : fmaf(pp, x, pq);
-          if (c >= 0) coherent_store(a.carry2 + ((size_t)b * nch + c) * D + i, xin);
-          x = fmaf(__shfl(p_, 63, 64), x, __shfl(q_, 63, 64));
-        }
+    for (int u = 0; u < kEChunk; ++u) {
+      const size_t e = base + (size_t)(t0 + min(u, len - 1)) * D;
+      r.gv[u] = a.G[e];
+      r.ev[u] = a.E[e];
+    }
+    r.hp = 0.f;
+  };
+
+  // RES: the wave's one chunk (a wave past the last chunk repeats it with its effects masked)
+  const int rtask = min(gw, ntask - 1);
+  const bool rvalid = gw < ntask;
+  ChunkRegs rr;
+  if constexpr (RES) load_inputs(rr, rtask, nullptr);   // the zero guess
+
+  int cur = 0;
+  uint32_t gen = 0;   // generation of the next grid barrier
+  for (int k = 0; k <= a.max_iters; ++k) {
+    const float* Hc = a.H[cur];
+    // ---- A ----
+    uint32_t m = 0;
+    if constexpr (RES) {
+      phase_a(rr, rtask, rvalid, m);
+    } else {
+      for (int task = gw; task < ntask; task += nw) {
+        ChunkRegs r;
+        load_inputs(r, task, Hc);
+        phase_a(r, task, true, m);
       }
     }
-    grid_barrier(ctrl, [] {});
-    if (has_fault(ctrl)) break;
+    // max |R| of the block into this iteration's word; after the barrier every block reads
+    // it and takes the same decision (stop when rho_k <= tol, on a non-finite rho, or
+    // after max_iters updates), which block 0 records
+    m = wave_max_u32(m);
+    if (lane == 0) s_wmax[wid] = m;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t bm = s_wmax[0];
+      for (int w = 1; w < kElkWaves; ++w) bm = max(bm, s_wmax[w]);
+      if (bm) __hip_atomic_fetch_max(&a.rmax[k], bm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (!elk_grid_sync(ctrl, gen)) break;
+    // the word is read here and the decision taken after B, so that its round trip overlaps
+    // B (whose writes are harmless when the loop stops)
+    uint32_t rbits = 0;
+    if (tid == 0) rbits = __hip_atomic_load(&a.rmax[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-    // ---- E: smoother walk, the next iterate, and the state before the chunk ----
-    float* Hn = a.H[cur ^ 1];
-    for (int task = gw; task < ntask; task += nw) {
-      if (!act) continue;
-      const int b = task / nch, c = task - b * nch;
-      const int t0 = c * kEChunk, len = min(kEChunk, T - t0);
-      const size_t base = (size_t)b * T * D + lane;
-      float gv[kEChunk], ev[kEChunk];
-#pragma unroll
-      for (int u = 0; u < kEChunk; ++u) {
-        const size_t e = base + (size_t)(t0 + min(u, len - 1)) * D;
-        gv[u] = a.G[e];
-        ev[u] = a.E[e];
-      }
-      float x = coherent_load(a.carry2 + (size_t)task * D + lane);
-      float gl = 0.f, el = 0.f;
-      if (c > 0) {
-        const float* tg = a.tailge + (size_t)(task - 1) * 2 * D + lane;
-        gl = coherent_load(tg);
-        el = coherent_load(tg + D);
-      }
-#pragma unroll
-      for (int u = kEChunk - 1; u >= 0; --u) {
-        if (u < len) {
-          x = fmaf(gv[u], x, ev[u]);
-          Hn[base + (size_t)(t0 + u) * D] = x;
+    // ---- B: filter state (u, 1, n) entering each chunk; lane order = time ----
+    // A row (b, channel) has ngr groups of 64 chunks; wpr waves of a block take wpr
+    // consecutive groups at once, scan them in registers, and exchange the group totals
+    // through LDS (every wave forms the same entering state from them).
+    for (int r0 = blockIdx.x * rpb; r0 < nrow; r0 += gridDim.x * rpb) {
+      const int row = r0 + wid / wpr, sub = wid % wpr;
+      const bool live = row < nrow;
+      const int b = live ? row / D : 0, i = live ? row - b * D : 0;
+      const float* ag = a.agg + ((size_t)b * D + i) * nch * 8;
+      V3 x{0.f, 1.f, 0.f};   // entering the row's first chunk: P = 0, m = 0
+      for (int g0 = 0; g0 < ngr; g0 += wpr) {
+        const int c = (g0 + sub) * 64 + lane;
+        Flt f = flt_identity();
+        if (live && c < nch) {
+          const float* p = ag + (size_t)c * 8;
+          f = Flt{coherent_load(p), coherent_load(p + 1), coherent_load(p + 2), coherent_load(p + 3),
+                  coherent_load(p + 4), coherent_load(p + 5), coherent_load(p + 6)};
         }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const Flt prev = flt_shfl_up(f, off);
+          if (lane >= off) f = compose(f, prev);
+        }
+        if (lane == 63) s_tot[wid] = f;
+        __syncthreads();
+        V3 xg = x;   // entering this wave's group
+        for (int s2 = wid - sub; s2 < wid; ++s2) xg = normalized(apply(s_tot[s2], xg));
+        const Flt before = flt_shfl_up(f, 1);
+        const V3 xin = lane == 0 ? xg : normalized(apply(before, xg));
+        if (live && c < nch) {
+          float* cp = a.carry + ((size_t)b * nch + c) * 2 * D + i;
+          coherent_store(cp, xin.u);
+          coherent_store(cp + D, xin.n);
+        }
+        for (int s2 = wid - sub; s2 < wid - sub + wpr; ++s2) x = normalized(apply(s_tot[s2], x));
+        __syncthreads();   // the totals are read before the next round writes them
       }
-      if (c > 0) a.hb[(size_t)task * D + lane] = fmaf(gl, x, el);
+    }
+    if (tid == 0) s_rbits = rbits;
+    if (!elk_grid_sync(ctrl, gen)) break;   // (its closing block-wide sync publishes s_rbits)
+    {
+      const double rho = bits_to_rho(s_rbits);
+      if (blockIdx.x == 0 && tid == 0) finish_iteration(ctrl, a.hist, rho, k, cur, a.max_iters, a.tol);
+      if (!(rho < __builtin_inf()) || rho <= a.tol || k >= a.max_iters) break;
+    }
+
+    // ---- C ----
+    if constexpr (RES) {
+      phase_c(rr, rtask, rvalid);
+    } else {
+      for (int task = gw; task < ntask; task += nw) {
+        ChunkRegs r;
+        load_planes_c(r, task, Hc);
+        phase_c(r, task, true);
+      }
+    }
+    if (!elk_grid_sync(ctrl, gen)) break;
+
+    // ---- D: smoothed state at the step after each chunk; lane order = reverse time ----
+    // (the same split of a row over wpr waves as in B)
+    for (int r0 = blockIdx.x * rpb; r0 < nrow; r0 += gridDim.x * rpb) {
+      const int row = r0 + wid / wpr, sub = wid % wpr;
+      const bool live = row < nrow;
+      const int b = live ? row / D : 0, i = live ? row - b * D : 0;
+      const float* ag2 = a.agg2 + ((size_t)b * D + i) * nch * 2;
+      float x = 0.f;   // after the row's last chunk: unused (the last step's gain is 0)
+      for (int g0 = 0; g0 < ngr; g0 += wpr) {
+        const int c = nch - 1 - ((g0 + sub) * 64 + lane);
+        float p_ = 1.f, q_ = 0.f;
+        if (live && c >= 0) {
+          p_ = coherent_load(ag2 + (size_t)c * 2);
+          q_ = coherent_load(ag2 + (size_t)c * 2 + 1);
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const float pp = __shfl_up(p_, off, 64), pq = __shfl_up(q_, off, 64);
+          if (lane >= off) {
+            q_ = fmaf(p_, pq, q_);
+            p_ *= pp;
+          }
+        }
+        if (lane == 63) s_tot2[wid] = make_float2(p_, q_);
+        __syncthreads();
+        float xg = x;   // after this wave's group
+        for (int s2 = wid - sub; s2 < wid; ++s2) xg = fmaf(s_tot2[s2].x, xg, s_tot2[s2].y);
+        const float pp = __shfl_up(p_, 1, 64), pq = __shfl_up(q_, 1, 64);
+        const float xin = lane == 0 ? xg : fmaf(pp, xg, pq);
+        if (live && c >= 0) coherent_store(a.carry2 + ((size_t)b * nch + c) * D + i, xin);
+        for (int s2 = wid - sub; s2 < wid - sub + wpr; ++s2) x = fmaf(s_tot2[s2].x, x, s_tot2[s2].y);
+        __syncthreads();
+      }
+    }
+    if (!elk_grid_sync(ctrl, gen)) break;
+
+    // ---- E ----
+    float* Hn = a.H[cur ^ 1];
+    if constexpr (RES) {
+      phase_e(rr, rtask, rvalid, Hn);
+    } else {
+      for (int task = gw; task < ntask; task += nw) {
+        ChunkRegs r;
+        load_planes_e(r, task);
+        phase_e(r, task, true, Hn);
+      }
     }
     cur ^= 1;
   }
@@ -417,15 +599,19 @@ hipError_t launch_elk_dense_output(const float* H0, const float* H1, const Ctrl*
 hipError_t launch_gru_elk_loop(const ElkLoopArgs& a, int num_cu, hipStream_t st) {
   if (a.D > 64 || a.D < 1) return hipErrorInvalidValue;
   constexpr int threads = 64 * kElkWaves;
-  const int per_cu = cached_occupancy((const void*)gru_elk_loop_kernel, 0, threads);
+  const int per_cu = min(cached_occupancy((const void*)gru_elk_loop_kernel<true>, 0, threads),
+                         cached_occupancy((const void*)gru_elk_loop_kernel<false>, 0, threads));
   if (per_cu < 1) return hipErrorInvalidConfiguration;
   long g = (long)per_cu * num_cu;
   if (g > kMaxGrid) g = kMaxGrid;
-  const long work = ((long)a.B * a.nch + kElkWaves - 1) / kElkWaves;
+  const long ntask = (long)a.B * a.nch;
+  const long work = (ntask + kElkWaves - 1) / kElkWaves;
+  const bool res = work <= g;   // a wave per chunk
   if (g > work) g = work;
   if (g < 1) g = 1;
   void* args[] = {const_cast<ElkLoopArgs*>(&a)};
-  return launch_persistent((const void*)gru_elk_loop_kernel, (int)g, 0, args, st, threads);
+  const void* fn = res ? (const void*)gru_elk_loop_kernel<true> : (const void*)gru_elk_loop_kernel<false>;
+  return launch_persistent(fn, (int)g, 0, args, st, threads);
 }
 
 }  // namespace pnr

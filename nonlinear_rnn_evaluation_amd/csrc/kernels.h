@@ -200,8 +200,8 @@ struct ElkLoopArgs {
   float* head;         // (J, R, h) at each chunk's first step [B][nch][3][D]
   float* tailge;       // (G, e) at each chunk's last step [B][nch][2][D]
   float* hb;           // state before each chunk's first step [B][nch][D]; zero at launch
-  uint32_t* partials;  // per-block residual maxima
-  Ctrl* ctrl;
+  uint32_t* rmax;      // max |R| of each iteration as ordered bits [max_iters + 1]; zero at launch
+  Ctrl* ctrl;          // zero at launch
   double* hist;        // [max_iters + 1]
   int B, T, D, nch, max_iters;
   float lam;           // damping
