@@ -975,14 +975,14 @@ DenseBwdLayout make_dense_bwd_layout(const pnr_cell* c) {
   l.wt = off; off = align_up(off + f * Din * GD);
   l.rmax = off; off = align_up(off + sizeof(uint32_t) * (kBwdMaxIters + 1));
   l.part = off; off = align_up(off + f * kSplitKSlices * GD * (D > Din ? D : Din));   // split-K partials
-  // the on-device refinement loop: the second v buffer, each chunk's boundary (lam, v),
-  // the control block with the residual history right after it (one read-back), and
-  // the per-block residual maxima
+  // the on-device refinement loop: the second v buffer, each chunk's boundary lam, the
+  // control block with the residual history right after it (one read-back), and the
+  // per-iteration residual maxima
   l.v2 = off; off = align_up(off + f * BT * D);
-  l.bnd = off; off = align_up(off + 2 * f * chunks);
+  l.bnd = off; off = align_up(off + f * chunks);
   l.ctrl = off; off = align_up(off + sizeof(Ctrl));
   l.hist = off; off = align_up(off + sizeof(double) * (kBwdMaxIters + 1));
-  l.partials = off; off = align_up(off + sizeof(uint32_t) * kMaxGrid);
+  l.partials = off; off = align_up(off + sizeof(uint32_t) * (kBwdMaxIters + 1));
   l.total = off;
   return l;
 }
@@ -1063,7 +1063,8 @@ int backward_dense(const pnr_cell* cell, const pnr_params* params, const void* x
     // the whole refinement on the device: one persistent loop decides when to stop (the
     // adjoint returned is the one whose residual passed) and is read back once
     PNR_HIP(launch_fill_zero(v, n, st));   // v_0 = U^T dgh(0) = 0
-    PNR_HIP(launch_fill_zero(fp(l.bnd), 2 * chunks, st));
+    PNR_HIP(launch_fill_zero(fp(l.bnd), chunks, st));
+    PNR_HIP(launch_fill_zero(fp(l.partials), kBwdMaxIters + 1, st));
     Ctrl* ctrl = reinterpret_cast<Ctrl*>(ws + l.ctrl);
     PNR_HIP(launch_init(ctrl, nullptr, 0, nullptr, 0, st));
     BwdLoopArgs la{};
@@ -1072,10 +1073,10 @@ int backward_dense(const pnr_cell* cell, const pnr_params* params, const void* x
     la.U = U;
     la.lam[0] = lam; la.lam[1] = lam2;
     la.v[0] = v; la.v[1] = fp(l.v2);
-    la.agg = agg;
+    la.agg = reinterpret_cast<float*>(agg);   // the same chunks x 2 floats, in the loop's [B][D][nch] order
     la.carry = carry;
-    la.bnd = reinterpret_cast<float2*>(ws + l.bnd);
-    la.partials = reinterpret_cast<uint32_t*>(ws + l.partials);
+    la.bnd = fp(l.bnd);
+    la.rmax = reinterpret_cast<uint32_t*>(ws + l.partials);
     la.ctrl = ctrl;
     la.hist = reinterpret_cast<double*>(ws + l.hist);
     la.B = B; la.T = T; la.D = D; la.nch = gru_bwd_chunks(T);

@@ -128,6 +128,51 @@ __device__ __forceinline__ void grid_barrier(Ctrl* c, Merge merge) {
   __syncthreads();
 }
 
+// Lean grid-wide barrier for loops that take their decisions without a merging block.
+// Two-level arrival on agent-scope counters as in grid_barrier, but the counters only
+// ever grow: barrier n (counted from 0 in this launch; the control block is zero at
+// launch and every block passes the same barriers in order) is complete at a group
+// counter of members * (n + 1) and a top counter of groups * (n + 1), so nothing is reset
+// and no store needs draining on the way.  `gen` is the caller's count of barriers passed.
+// Each arrival is issued after the block's own stores have completed, and the value an
+// atomic returns shows every earlier arrival performed, so the block that completes the
+// top counter knows every block's data is visible before it publishes generation n + 1.
+// Returns false when this block's wait ran out (the fault is recorded); such a block
+// leaves the loop and the others give up at the next barrier, so every wave ends.
+__device__ __forceinline__ bool grid_sync(Ctrl* c, uint32_t& gen) {
+  __shared__ int s_ok;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    drain_memory_ops();
+    const uint32_t g = blockIdx.x % kBarGroups;
+    const uint32_t members = (gridDim.x - g + kBarGroups - 1) / kBarGroups;
+    const uint32_t groups = gridDim.x < (unsigned)kBarGroups ? gridDim.x : (unsigned)kBarGroups;
+    bool released = false;
+    if (atomicAdd(&c->bar_group[g].count, 1u) == members * (gen + 1u) - 1u) {
+      if (atomicAdd(&c->bar_top, 1u) == groups * (gen + 1u) - 1u) {
+        __hip_atomic_store(&c->bar_gen, gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        released = true;
+      }
+    }
+    int ok = 1;
+    if (!released) {
+      uint32_t spins = 0;
+      while (__hip_atomic_load(&c->bar_gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
+        backoff(spins);
+        if (++spins > kSpinLimit) {
+          record_fault(c, 2);
+          ok = 0;
+          break;
+        }
+      }
+    }
+    s_ok = ok;
+  }
+  ++gen;
+  __syncthreads();
+  return s_ok != 0;
+}
+
 // Coherent (agent-scope) scalar load of data another block may have written during this
 // kernel, e.g. the last state of the preceding tile.
 __device__ __forceinline__ float coherent_load(const float* p) {

@@ -342,48 +342,63 @@ hipError_t launch_row_sum(const float* M, int rows, size_t cols, float* out, flo
 // ---- the whole refinement loop in one persistent, co-resident grid ----
 // Iteration k on the adjoint lam_k (with v_k = U^T dgh(lam_k)):
 //   A. each wave, for its fixed chunks: R and the chunk's map delta_{end} -> delta_{start}
-//      (as pass 1 above), and max |R|;
-//   grid barrier: the final block merges the maxima, records rho_k and decides (stop when
-//      rho_k <= tol_rel rho_0, on a non-finite rho, or after max_iters updates), so the
-//      adjoint returned is exactly the one whose residual passed;
-//   B. one wave per (b, channel) walks the chunk maps into each chunk's carry (as the
-//      carry kernel, with lane shuffles);
+//      (as pass 1 above), and max |R| into this iteration's word;
 //   grid barrier;
+//   B. the waves of a block take one (b, channel) row's chunk maps in groups of 64 (lanes
+//      = chunks, reverse time), scan them with lane shuffles and exchange the group totals
+//      through LDS: each chunk's carry.  Meanwhile thread 0 reads the residual word;
+//   grid barrier; every block then takes the same decision (stop when rho_k <= tol_rel
+//      rho_0, on a non-finite rho, or after max_iters updates) and block 0 records it, so
+//      the adjoint returned is exactly the one whose residual passed;
 //   C. each wave, for its chunks: lam_{k+1} = lam_k + delta from the carry (as pass 3),
-//      and v_{k+1} = U^T dgh(lam_{k+1}) for the chunk's steps and for the step after it.
-//      Keeping that boundary step's lam and v with the chunk means pass A of the next
-//      iteration reads nothing another wave wrote, so no third barrier is needed.
+//      and v_{k+1} = U^T dgh(lam_{k+1}) for steps t0+1 .. t1 of the chunk [t0, t1) -- the
+//      steps whose v the chunk's residuals read, t1 (the first step of the next chunk)
+//      included.  The chunk keeps lam_{k+1} at t1 too, so pass A of the next iteration
+//      reads nothing another wave wrote and no third barrier is needed.
 // Chunk maps and carries cross blocks: written and read with agent-scope atomics (the
 // grid barrier orders only those).  Everything else a wave reads it wrote itself.
-// v: the chunk's 16 dgh rows (staged by each wave in LDS) times [U_r; U_z; U_n] on fp32
-// MFMA (16x16x4; four 16-channel column tiles, 48 k-steps over the 3 x 64 padded rows),
-// the operands of U kept in LDS in fragment order; the boundary row on VALU.
+// v: the 16 staged dgh rows times [U_r; U_z; U_n] on fp32 MFMA (16x16x4, four 16-channel
+// column tiles, 48 k-steps over the 3 x 64 padded rows), the k index split across lane
+// groups (k = 48 (l / 16) + kk in k-step kk), so a lane's A operands are 48 consecutive
+// floats of its row and its B operands for one k-step one 16-byte vector.
 constexpr int kLoopWaves = 8;
-constexpr int kDgLd = 3 * 64 + 4;   // staged row stride: 16 rows x 4 k of an A fragment hit 64 banks
+constexpr int kDgLd = 3 * 64 + 4;   // staged row stride: 16 rows of 16-byte reads hit 64 banks
 typedef float v4f_t __attribute__((ext_vector_type(4)));
 
 __global__ void __launch_bounds__(64 * kLoopWaves, 1) gru_bwd_loop_kernel(BwdLoopArgs a) {
   static_assert(kChunk == 16, "a chunk is one 16-row MFMA tile");
-  __shared__ __align__(16) float dg[kLoopWaves][kChunk + 1][kDgLd];
-  // usf[kk][nt][l] = U_g[j][16 nt + l % 16] with g * 64 + j = 4 kk + l / 16 (zero past D):
-  // the B operand of k-step kk, column tile nt, for lane l -- one contiguous 256-B read
-  __shared__ float usf[48][4][64];
+  // One pool, the operand table first (every read of it a base register plus an immediate
+  // offset below 64 KiB):
+  //  ufb[kk][l][nt] = U_g[j][16 nt + l % 16], g * 64 + j = 48 (l / 16) + kk (zero past D);
+  //  then per wave the staged dgh rows [16][kDgLd].
+  __shared__ __align__(16) float pool[48 * 64 * 4 + kLoopWaves * kChunk * kDgLd];
   __shared__ uint32_t s_wmax[kLoopWaves];
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, tid = threadIdx.x;
+  __shared__ float2 s_tot[kLoopWaves];
+  __shared__ uint32_t s_rb[2];
+  float* const ufb = pool;
+  // the wave index is uniform across the wave: saying so keeps every chunk index and base
+  // address derived from it in scalar registers
+  const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), tid = threadIdx.x;
   const int D = a.D, T = a.T, nch = a.nch;
   const size_t n = (size_t)a.B * T * D;
   const bool act = lane < D;
   Ctrl* ctrl = a.ctrl;
-  for (int idx = tid; idx < 48 * 4 * 64; idx += 64 * kLoopWaves) {
-    const int kk = idx >> 8, nt = (idx >> 6) & 3, l = idx & 63;
-    const int K = 4 * kk + (l >> 4), g = K >> 6, j = K & 63, ch = 16 * nt + (l & 15);
-    usf[kk][nt][l] = (j < D && ch < D) ? a.U[(size_t)(g * D + j) * D + ch] : 0.f;
+  for (int idx = tid; idx < 48 * 64 * 4; idx += 64 * kLoopWaves) {
+    const int kk = idx >> 8, l = (idx >> 2) & 63, nt = idx & 3;
+    const int K = 48 * (l >> 4) + kk, g = K >> 6, j = K & 63, ch = 16 * nt + (l & 15);
+    ufb[idx] = (j < D && ch < D) ? a.U[(size_t)(g * D + j) * D + ch] : 0.f;
   }
   __syncthreads();
   const int gw = blockIdx.x * kLoopWaves + wid, nw = gridDim.x * kLoopWaves;
   const int ntask = a.B * nch, nrow = a.B * D;
-  float(*dgw)[kDgLd] = dg[wid];
+  // carry scans: groups of 64 chunks per row, waves per row (a power of two up to 8)
+  const int ngr = (nch + 63) / 64;
+  const int wpr = ngr >= 8 ? 8 : ngr > 2 ? 4 : ngr;
+  const int rpb = kLoopWaves / wpr;
+  float* const dgw = pool + 48 * 64 * 4 + wid * (kChunk * kDgLd);
+  const int m16 = lane & 15, q4 = lane >> 4;
   int cur = 0;
+  uint32_t gen = 0;   // generation of the next grid barrier
   for (int k = 0; k <= a.max_iters; ++k) {
     const float* lam = a.lam[cur];
     const float* vv = a.v[cur];
@@ -400,11 +415,11 @@ __global__ void __launch_bounds__(64 * kLoopWaves, 1) gru_bwd_loop_kernel(BwdLoo
       for (int u = 0; u < kChunk; ++u) in[u] = load_step(a.g, lam, a.F, vv, n, base + (size_t)min(t0 + u, t1 - 1) * D);
       float nlam = 0.f, nv = 0.f, nz = 0.f, nd = 0.f;   // the step after the current one
       if (t1 < T) {
-        const float2 bv = a.bnd[(size_t)task * D + lane];
-        nlam = bv.x;
-        nv = bv.y;
-        nz = a.F[base + (size_t)t1 * D];
-        nd = a.F[n + base + (size_t)t1 * D];
+        const size_t e = base + (size_t)t1 * D;
+        nlam = a.bnd[(size_t)task * D + lane];
+        nv = vv[e];
+        nz = a.F[e];
+        nd = a.F[n + e];
       }
       float P = 1.f, Q = 0.f;
 #pragma unroll
@@ -417,7 +432,7 @@ __global__ void __launch_bounds__(64 * kLoopWaves, 1) gru_bwd_loop_kernel(BwdLoo
           nlam = in[u].lam; nv = in[u].v; nz = in[u].z; nd = in[u].d;
         }
       }
-      float* ag = reinterpret_cast<float*>(a.agg + (size_t)task * D + lane);
+      float* ag = a.agg + (((size_t)b * D + lane) * nch + c) * 2;
       coherent_store(ag, P);
       coherent_store(ag + 1, Q);
     }
@@ -427,79 +442,85 @@ __global__ void __launch_bounds__(64 * kLoopWaves, 1) gru_bwd_loop_kernel(BwdLoo
     if (tid == 0) {
       uint32_t bm = s_wmax[0];
       for (int w = 1; w < kLoopWaves; ++w) bm = max(bm, s_wmax[w]);
-      __hip_atomic_store(&a.partials[blockIdx.x], bm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (bm) __hip_atomic_fetch_max(&a.rmax[k], bm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    grid_barrier(ctrl, [&]() {
-      uint32_t mm = 0;
-      for (int i = tid; i < (int)gridDim.x; i += 64 * kLoopWaves)
-        mm = max(mm, __hip_atomic_load(&a.partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      mm = wave_max_u32(mm);
-      __syncthreads();
-      if (lane == 0) s_wmax[wid] = mm;
-      __syncthreads();
-      if (tid == 0) {
-        for (int w = 0; w < kLoopWaves; ++w) mm = max(mm, s_wmax[w]);
-        const double rho = bits_to_rho(mm);
-        const double rho0 = k == 0 ? rho : coherent_load(&a.hist[0]);
-        finish_iteration(ctrl, a.hist, rho, k, cur, a.max_iters, a.tol_rel * rho0);
-        if (k == 0) coherent_store(&a.hist[0], rho);
-      }
-    });
-    if (__hip_atomic_load(&ctrl->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) || has_fault(ctrl)) break;
+    if (!grid_sync(ctrl, gen)) break;
+    // the residual words are read here and the decision taken after B, so that their round
+    // trip overlaps B (whose writes are harmless when the loop stops)
+    uint32_t rb0 = 0, rbk = 0;
+    if (tid == 0) {
+      rb0 = __hip_atomic_load(&a.rmax[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      rbk = __hip_atomic_load(&a.rmax[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 
     // ---- B: carries (delta at the first step after each chunk), lane order = reverse time ----
-    // The chunk maps of up to kCarryGroups groups of 64 are loaded together (one round trip)
-    // and scanned group by group in registers.
-    constexpr int kCarryGroups = 4;
-    for (int task = gw; task < nrow; task += nw) {
-      const int b = task / D, i = task - b * D;
-      float x = 0.f;
-      for (int h0 = 0; h0 < nch; h0 += 64 * kCarryGroups) {
-        float P[kCarryGroups], Q[kCarryGroups];
-#pragma unroll
-        for (int h = 0; h < kCarryGroups; ++h) {
-          const int c = nch - 1 - (h0 + 64 * h + lane);
-          P[h] = 1.f;
-          Q[h] = 0.f;
-          if (c >= 0) {
-            const float* ag = reinterpret_cast<const float*>(a.agg + ((size_t)b * nch + c) * D + i);
-            P[h] = coherent_load(ag);
-            Q[h] = coherent_load(ag + 1);
-          }
+    for (int r0 = blockIdx.x * rpb; r0 < nrow; r0 += gridDim.x * rpb) {
+      const int row = r0 + wid / wpr, sub = wid % wpr;
+      const bool live = row < nrow;
+      const int b = live ? row / D : 0, i = live ? row - b * D : 0;
+      const float* ag = a.agg + ((size_t)b * D + i) * nch * 2;
+      float x = 0.f;   // delta after the row's last chunk
+      for (int g0 = 0; g0 < ngr; g0 += wpr) {
+        const int c = nch - 1 - ((g0 + sub) * 64 + lane);
+        float p_ = 1.f, q_ = 0.f;
+        if (live && c >= 0) {
+          p_ = coherent_load(ag + (size_t)c * 2);
+          q_ = coherent_load(ag + (size_t)c * 2 + 1);
         }
 #pragma unroll
-        for (int h = 0; h < kCarryGroups; ++h) {
-          const int c = nch - 1 - (h0 + 64 * h + lane);
-          float p_ = P[h], q_ = Q[h];
-#pragma unroll
-          for (int off = 1; off < 64; off <<= 1) {
-            const float pp = __shfl_up(p_, off, 64), pq = __shfl_up(q_, off, 64);
-            if (lane >= off) {
-              q_ = fmaf(p_, pq, q_);
-              p_ *= pp;
-            }
+        for (int off = 1; off < 64; off <<= 1) {
+          const float pp = __shfl_up(p_, off, 64), pq = __shfl_up(q_, off, 64);
+          if (lane >= off) {
+            q_ = fmaf(p_, pq, q_);
+            p_ *= pp;
           }
-          const float pp = __shfl_up(p_, 1, 64), pq = __shfl_up(q_, 1, 64);
-          const float xin = lane == 0 ? x : fmaf(pp, x, pq);
-          if (c >= 0) coherent_store(a.carry + ((size_t)b * nch + c) * D + i, xin);
-          x = fmaf(__shfl(p_, 63, 64), x, __shfl(q_, 63, 64));
         }
+        if (lane == 63) s_tot[wid] = make_float2(p_, q_);
+        __syncthreads();
+        float xg = x;   // after this wave's group
+        for (int s2 = wid - sub; s2 < wid; ++s2) xg = fmaf(s_tot[s2].x, xg, s_tot[s2].y);
+        const float pp = __shfl_up(p_, 1, 64), pq = __shfl_up(q_, 1, 64);
+        const float xin = lane == 0 ? xg : fmaf(pp, xg, pq);
+        if (live && c >= 0) coherent_store(a.carry + ((size_t)b * nch + c) * D + i, xin);
+        for (int s2 = wid - sub; s2 < wid - sub + wpr; ++s2) x = fmaf(s_tot[s2].x, x, s_tot[s2].y);
+        __syncthreads();   // the totals are read before the next round writes them
       }
     }
-    grid_barrier(ctrl, [] {});
-    if (has_fault(ctrl)) break;
+    if (tid == 0) {
+      s_rb[0] = rb0;
+      s_rb[1] = rbk;
+    }
+    if (!grid_sync(ctrl, gen)) break;   // (its closing block-wide sync publishes s_rb)
+    {
+      const double rho = bits_to_rho(s_rb[1]), rho0 = bits_to_rho(s_rb[0]);
+      const double tol = a.tol_rel * rho0;
+      if (blockIdx.x == 0 && tid == 0) finish_iteration(ctrl, a.hist, rho, k, cur, a.max_iters, tol);
+      if (!(rho < __builtin_inf()) || rho <= tol || k >= a.max_iters) break;
+    }
 
     // ---- C: the update and the next v ----
     float* lam_n = a.lam[cur ^ 1];
     float* v_n = a.v[cur ^ 1];
     for (int task = gw; task < ntask; task += nw) {
       const int b = task / nch, c = task - b * nch;
-      const int t0 = c * kChunk, t1 = min(T, t0 + kChunk);
+      const int t0 = c * kChunk, t1 = min(T, t0 + kChunk), len = t1 - t0;
       const size_t base = (size_t)b * T * D + lane;
       const bool tail = t1 < T;   // the step after the chunk exists
+      // Staged row r holds dgh at step t0 + 1 + r: rows 0 .. len - 2 from the walk, row 15
+      // the step after the chunk (zero without one), and in a short last chunk the rows
+      // between are zero.
+      if (len < kChunk) {
+#pragma unroll
+        for (int r = 0; r < kChunk; ++r)
+          if (r >= len - 1) {
+            dgw[r * kDgLd + lane] = 0.f;
+            dgw[r * kDgLd + 64 + lane] = 0.f;
+            dgw[r * kDgLd + 128 + lane] = 0.f;
+          }
+      }
       // The chunk in two batches of kBatch steps, latest first.  The first batch's loads
       // are issued before the carry and the boundary step's, so that they share one round
-      // trip; the boundary row is staged once both have landed.
+      // trip.
       float dl = 0.f, nlam = 0.f, nv = 0.f, nz = 0.f, nd = 0.f, lb = 0.f;
       for (int h = kChunk / kBatch - 1; h >= 0; --h) {
         const int u0 = h * kBatch;
@@ -521,10 +542,9 @@ __global__ void __launch_bounds__(64 * kLoopWaves, 1) gru_bwd_loop_kernel(BwdLoo
           if (act) {
             dl = coherent_load(a.carry + (size_t)task * D + lane);   // delta at t1
             if (tail) {
-              const float2 bv = a.bnd[(size_t)task * D + lane];
               const size_t e = base + (size_t)t1 * D;
-              nlam = bv.x;
-              nv = bv.y;
+              nlam = a.bnd[(size_t)task * D + lane];
+              nv = vv[e];
               nz = a.F[e];
               nd = a.F[n + e];
               ft[0] = a.F[5 * n + e];
@@ -535,9 +555,9 @@ __global__ void __launch_bounds__(64 * kLoopWaves, 1) gru_bwd_loop_kernel(BwdLoo
           }
           lb = nlam + dl;   // lam_{k+1} at t1
           if (tail) {
-            dgw[kChunk][lane] = ft[0] * lb;
-            dgw[kChunk][64 + lane] = ft[1] * lb;
-            dgw[kChunk][128 + lane] = ft[2] * lb * ft[3];
+            dgw[15 * kDgLd + lane] = act ? ft[0] * lb : 0.f;
+            dgw[15 * kDgLd + 64 + lane] = act ? ft[1] * lb : 0.f;
+            dgw[15 * kDgLd + 128 + lane] = act ? ft[2] * lb * ft[3] : 0.f;
           }
         }
 #pragma unroll
@@ -552,49 +572,49 @@ __global__ void __launch_bounds__(64 * kLoopWaves, 1) gru_bwd_loop_kernel(BwdLoo
               lam_n[base + (size_t)t * D] = l;
               nlam = in[u].lam; nv = in[u].v; nz = in[u].z; nd = in[u].d;
             }
-            dgw[u0 + u][lane] = act ? fg[u][0] * l : 0.f;
-            dgw[u0 + u][64 + lane] = act ? fg[u][1] * l : 0.f;
-            dgw[u0 + u][128 + lane] = act ? fg[u][2] * l * fg[u][3] : 0.f;
+            const int r = u0 + u - 1;   // the staged row of step t
+            if (r >= 0) {
+              dgw[r * kDgLd + lane] = act ? fg[u][0] * l : 0.f;
+              dgw[r * kDgLd + 64 + lane] = act ? fg[u][1] * l : 0.f;
+              dgw[r * kDgLd + 128 + lane] = act ? fg[u][2] * l * fg[u][3] : 0.f;
+            }
           }
         }
       }
+      if (act && tail) a.bnd[(size_t)task * D + lane] = lb;
       // the rows just written are read back by every lane of this wave
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
       __builtin_amdgcn_wave_barrier();
-      // rows 0..15 on MFMA: lane l ends with V[4 (l / 16) + i][16 nt + l % 16]
-      const int m16 = lane & 15, q4 = lane >> 4;
-      v4f_t acc4[4];
+      // lane l ends with V[row 4 (l / 16) + i][channel 16 nt + l % 16]
+      v4f_t acc[4];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc4[nt] = v4f_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
+      for (int nt = 0; nt < 4; ++nt) acc[nt] = v4f_t{0.f, 0.f, 0.f, 0.f};
+      float4 av[12];
+      const float4* arow = reinterpret_cast<const float4*>(dgw + m16 * kDgLd + 48 * q4);
+#pragma unroll
+      for (int j = 0; j < 12; ++j) av[j] = arow[j];
+      const float4* ub = reinterpret_cast<const float4*>(ufb) + lane;
+      float4 bcur = ub[0], bnxt = bcur;
+#pragma unroll
       for (int kk = 0; kk < 48; ++kk) {
-        const float av = dgw[m16][4 * kk + q4];
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          acc4[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, usf[kk][nt][lane], acc4[nt], 0, 0, 0);
+        if (kk + 1 < 48) bnxt = ub[(kk + 1) * 64];
+        const float4 a4 = av[kk >> 2];
+        const float aval = (kk & 3) == 0 ? a4.x : (kk & 3) == 1 ? a4.y : (kk & 3) == 2 ? a4.z : a4.w;
+        acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(aval, bcur.x, acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(aval, bcur.y, acc[1], 0, 0, 0);
+        acc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(aval, bcur.z, acc[2], 0, 0, 0);
+        acc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(aval, bcur.w, acc[3], 0, 0, 0);
+        bcur = bnxt;
       }
+      // row r is step t0 + 1 + r: rows 0 .. len - 2 inside the chunk, row 15 the step after it
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const int ch = 16 * nt + m16;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int row = 4 * q4 + i;
-          if (row < t1 - t0 && ch < D) v_n[((size_t)b * T + t0 + row) * D + ch] = acc4[nt][i];
+          const int r = 4 * q4 + i;
+          if (ch < D && (r < len - 1 || (r == 15 && tail))) v_n[((size_t)b * T + t0 + 1 + r) * D + ch] = acc[nt][i];
         }
-      }
-      // the boundary row on VALU: lane = channel, U_g[j][lane] read back from usf
-      if (tail) {
-        float accb = 0.f;
-#pragma unroll 4
-        for (int kk = 0; kk < 48; ++kk) {
-          const float4 d4 = *reinterpret_cast<const float4*>(&dgw[kChunk][4 * kk]);
-          const float* uq = usf[kk][lane >> 4];
-          accb = fmaf(uq[lane & 15], d4.x, accb);
-          accb = fmaf(uq[16 + (lane & 15)], d4.y, accb);
-          accb = fmaf(uq[32 + (lane & 15)], d4.z, accb);
-          accb = fmaf(uq[48 + (lane & 15)], d4.w, accb);
-        }
-        if (act) a.bnd[(size_t)task * D + lane] = make_float2(lb, accb);
       }
       // the staging rows are rewritten by this wave's next chunk only after these reads
       __builtin_amdgcn_s_waitcnt(0xC07F);

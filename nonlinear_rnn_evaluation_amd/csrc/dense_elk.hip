@@ -70,50 +70,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-// Grid-wide barrier for this loop.  Two-level arrival on agent-scope counters as in the
-// library's grid barrier, but the counters only ever grow: barrier n (counted from 0 in
-// this launch; the control block is zero at launch and every block passes the same
-// barriers in order) is complete at a group counter of members * (n + 1) and a top
-// counter of groups * (n + 1), so nothing is reset and no store needs draining on the way.
-// Each arrival is issued after the block's own stores have completed, and the value an
-// atomic returns shows every earlier arrival performed, so the block that completes the
-// top counter knows every block's data is visible before it publishes generation n + 1.
-// Returns false when this block's wait ran out (the fault is recorded); such a block
-// leaves the loop and the others give up at the next barrier, so every wave ends.
-__device__ __forceinline__ bool elk_grid_sync(Ctrl* c, uint32_t& gen) {
-  __shared__ int s_ok;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    drain_memory_ops();
-    const uint32_t g = blockIdx.x % kBarGroups;
-    const uint32_t members = (gridDim.x - g + kBarGroups - 1) / kBarGroups;
-    const uint32_t groups = gridDim.x < (unsigned)kBarGroups ? gridDim.x : (unsigned)kBarGroups;
-    bool released = false;
-    if (atomicAdd(&c->bar_group[g].count, 1u) == members * (gen + 1u) - 1u) {
-      if (atomicAdd(&c->bar_top, 1u) == groups * (gen + 1u) - 1u) {
-        __hip_atomic_store(&c->bar_gen, gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        released = true;
-      }
-    }
-    int ok = 1;
-    if (!released) {
-      uint32_t spins = 0;
-      while (__hip_atomic_load(&c->bar_gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
-        backoff(spins);
-        if (++spins > kSpinLimit) {
-          record_fault(c, 2);
-          ok = 0;
-          break;
-        }
-      }
-    }
-    s_ok = ok;
-  }
-  ++gen;
-  __syncthreads();
-  return s_ok != 0;
-}
-
 // A chunk's per-step values in one wave's registers (lane = channel).
 struct ChunkRegs {
   float xg[kEChunk][3];   // gate inputs x W^T + b_x
@@ -454,7 +410,7 @@ __global__ void __launch_bounds__(64 * kElkWaves, 1) gru_elk_loop_kernel(ElkLoop
       for (int w = 1; w < kElkWaves; ++w) bm = max(bm, s_wmax[w]);
       if (bm) __hip_atomic_fetch_max(&a.rmax[k], bm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (!elk_grid_sync(ctrl, gen)) break;
+    if (!grid_sync(ctrl, gen)) break;
     // the word is read here and the decision taken after B, so that its round trip overlaps
     // B (whose writes are harmless when the loop stops)
     uint32_t rbits = 0;
@@ -499,7 +455,7 @@ __global__ void __launch_bounds__(64 * kElkWaves, 1) gru_elk_loop_kernel(ElkLoop
       }
     }
     if (tid == 0) s_rbits = rbits;
-    if (!elk_grid_sync(ctrl, gen)) break;   // (its closing block-wide sync publishes s_rbits)
+    if (!grid_sync(ctrl, gen)) break;   // (its closing block-wide sync publishes s_rbits)
     {
       const double rho = bits_to_rho(s_rbits);
       if (blockIdx.x == 0 && tid == 0) finish_iteration(ctrl, a.hist, rho, k, cur, a.max_iters, a.tol);
@@ -516,7 +472,7 @@ __global__ void __launch_bounds__(64 * kElkWaves, 1) gru_elk_loop_kernel(ElkLoop
         phase_c(r, task, true);
       }
     }
-    if (!elk_grid_sync(ctrl, gen)) break;
+    if (!grid_sync(ctrl, gen)) break;
 
     // ---- D: smoothed state at the step after each chunk; lane order = reverse time ----
     // (the same split of a row over wpr waves as in B)
@@ -552,7 +508,7 @@ __global__ void __launch_bounds__(64 * kElkWaves, 1) gru_elk_loop_kernel(ElkLoop
         __syncthreads();
       }
     }
-    if (!elk_grid_sync(ctrl, gen)) break;
+    if (!grid_sync(ctrl, gen)) break;
 
     // ---- E ----
     float* Hn = a.H[cur ^ 1];

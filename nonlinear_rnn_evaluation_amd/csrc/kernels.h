@@ -157,13 +157,13 @@ struct BwdLoopArgs {
   const float* F;      // gate factors [6][B*T*D]: z, d, f_z, f_n, r, f_r
   const float* g;      // dL/dh [B][T][D]
   const float* U;      // [3D][D]
-  float* lam[2];       // adjoint iterates [B][T][D]
-  float* v[2];         // U^T dgh(lam) [B][T][D]
-  float2* agg;         // chunk maps [B][nch][D]
+  float* lam[2];       // adjoint iterates [B][T][D]; lam[0] zero at launch
+  float* v[2];         // U^T dgh(lam) [B][T][D]; v[0] zero at launch
+  float* agg;          // chunk maps (P, Q) [B][D][nch][2]
   float* carry;        // delta at the first step after each chunk [B][nch][D]
-  float2* bnd;         // per chunk, (lam, v) of the iterate at the step after it [B][nch][D]
-  uint32_t* partials;  // per-block residual maxima
-  Ctrl* ctrl;
+  float* bnd;          // per chunk, lam of the iterate at the step after it [B][nch][D]; zero at launch
+  uint32_t* rmax;      // max |R| of each iteration as ordered bits [max_iters + 1]; zero at launch
+  Ctrl* ctrl;          // zero at launch
   double* hist;        // [max_iters + 1]
   int B, T, D, nch, max_iters;
   double tol_rel;      // stop when rho_k <= tol_rel * rho_0

@@ -124,10 +124,15 @@ def test_empty_sequence():
 # Dense GRU: the adjoint is solved by quasi-Newton refinement (diagonal scan + the dense
 # product on MFMA) until its residual is 2e-5 of max |g|; every gradient is held to
 # 2e-4 of its scale (the refinement's stopping point, not fp32 rounding, sets the bar).
-@pytest.mark.parametrize("D,T", [(16, 37), (16, 1025), (64, 300), (64, 2100), (40, 777)])
-def test_dense_gru_gradients_match_the_oracle(D, T):
+# The device loop's chunks are 16 steps (one MFMA row tile covering steps t0+1 .. t0+16),
+# so the lengths span a partial chunk, exactly one, one past it, many with a ragged end
+# and (B = 3, T = 11000: 2064 chunks) more chunks than a full grid has waves; D = 1, 7 and
+# 40 leave most of the 64 padded channels empty.
+@pytest.mark.parametrize("B,D,T", [(2, 16, 37), (2, 16, 1025), (2, 64, 300), (2, 64, 2100), (2, 40, 777),
+                                   (2, 1, 17), (2, 7, 5), (1, 64, 16), (3, 8, 11000)])
+def test_dense_gru_gradients_match_the_oracle(B, D, T):
     cell = WL.CELL_GRU
-    p = WL.random_problem(cell, 2, T, D, 9, seed=D + T, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32, bias_std=0.2,
+    p = WL.random_problem(cell, B, T, D, 9, seed=D + T, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32, bias_std=0.2,
                           h0_std=0.3, w_std=0.7 / np.sqrt(D))
     p["b_h"] = torch.randn(p["b_x"].shape, generator=torch.Generator().manual_seed(T), dtype=torch.float32) * 0.2
     q = {k: (None if v is None else WL.as_f64(v)) for k, v in p.items()}
@@ -136,7 +141,7 @@ def test_dense_gru_gradients_match_the_oracle(D, T):
     g = np.random.default_rng(D * T).normal(size=H.shape).astype(np.float32)
     ref = O.bptt(cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], H32.astype(np.float64),
                  g.astype(np.float64))
-    print(f"# dense backward D={D} T={T}", flush=True)
+    print(f"# dense backward B={B} D={D} T={T}", flush=True)
     got = _run(cell, p, H32, g)
     assert got["status"] == pnr.OK and 0 < got["iters"] <= 256
     assert got["history"][-1] <= 2e-5 * got["history"][0]
