@@ -365,6 +365,13 @@ constexpr int kLoopWaves = 8;
 constexpr int kDgLd = 3 * 64 + 4;   // staged row stride: 16 rows of 16-byte reads hit 64 banks
 typedef float v4f_t __attribute__((ext_vector_type(4)));
 
+// RES: every chunk has a wave of its own (B * nch <= waves of the grid).  The chunk's
+// per-step constants (g, z, d, f_r, f_z, f_n r), the adjoint and v then stay in the wave's
+// registers for the whole launch (v comes back from the MFMA layout through the staging
+// rows), and each iteration only stores the new adjoint; every register array is assigned
+// in full (rows past a ragged end on clamped, finite inputs, only their effects masked).
+// Otherwise a wave loops over its chunks and reads them from the workspace planes.
+template <bool RES>
 __global__ void __launch_bounds__(64 * kLoopWaves, 1) gru_bwd_loop_kernel(BwdLoopArgs a) {
   static_assert(kChunk == 16, "a chunk is one 16-row MFMA tile");
   // One pool, the operand table first (every read of it a base register plus an immediate
@@ -397,6 +404,39 @@ __global__ void __launch_bounds__(64 * kLoopWaves, 1) gru_bwd_loop_kernel(BwdLoo
   const int rpb = kLoopWaves / wpr;
   float* const dgw = pool + 48 * 64 * 4 + wid * (kChunk * kDgLd);
   const int m16 = lane & 15, q4 = lane >> 4;
+  // RES: the wave's chunk (a wave past the last chunk repeats it with its effects masked)
+  const int rtask = min(gw, ntask - 1);
+  const bool rlive = gw < ntask && act;
+  const int ln = act ? lane : 0;   // the channel whose addresses a lane uses
+  const int rb_ = rtask / nch, rc_ = rtask - rb_ * nch;
+  const int rt0 = rc_ * kChunk, rt1 = min(T, rt0 + kChunk), rlen = rt1 - rt0;
+  const bool rtail = rt1 < T;
+  const size_t rbase = (size_t)rb_ * T * D + ln;
+  float cg[kChunk], cz[kChunk], cd[kChunk], cfr[kChunk], cfz[kChunk], cfnr[kChunk], lv[kChunk], vr[kChunk];
+  float bz = 0.f, bd = 0.f, bfr = 0.f, bfz = 0.f, bfnr = 0.f;   // constants at the step after the chunk
+  float blam = 0.f, bv = 0.f;                                   // lam_k and v_k there
+  if constexpr (RES) {
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const size_t e = rbase + (size_t)min(rt0 + u, rt1 - 1) * D;
+      cg[u] = a.g[e];
+      cz[u] = a.F[e];
+      cd[u] = a.F[n + e];
+      cfz[u] = a.F[2 * n + e];
+      cfnr[u] = a.F[3 * n + e] * a.F[4 * n + e];
+      cfr[u] = a.F[5 * n + e];
+      lv[u] = 0.f;   // lam_0 = 0, v_0 = U^T dgh(0) = 0
+      vr[u] = 0.f;
+    }
+    if (rtail) {
+      const size_t e = rbase + (size_t)rt1 * D;
+      bz = a.F[e];
+      bd = a.F[n + e];
+      bfz = a.F[2 * n + e];
+      bfnr = a.F[3 * n + e] * a.F[4 * n + e];
+      bfr = a.F[5 * n + e];
+    }
+  }
   int cur = 0;
   uint32_t gen = 0;   // generation of the next grid barrier
   for (int k = 0; k <= a.max_iters; ++k) {
@@ -404,7 +444,31 @@ __global__ void __launch_bounds__(64 * kLoopWaves, 1) gru_bwd_loop_kernel(BwdLoo
     const float* vv = a.v[cur];
     // ---- A: residual and chunk maps ----
     uint32_t m = 0;
-    for (int task = gw; task < ntask; task += nw) {
+    if constexpr (RES) {
+      float nlam = blam, nv = bv, nz = bz, nd = bd;   // the step after the current one
+      float P = 1.f, Q = 0.f;
+      uint32_t mloc = 0;
+#pragma unroll
+      for (int u = kChunk - 1; u >= 0; --u) {
+        const bool in = u < rlen;
+        const float R = cg[u] + fmaf(nz, nlam, nv) - lv[u];
+        mloc = in ? max(mloc, abs_bits(R)) : mloc;
+        const float Pn = P * nd, Qn = fmaf(nd, Q, R);
+        P = in ? Pn : P;
+        Q = in ? Qn : Q;
+        nlam = in ? lv[u] : nlam;
+        nv = in ? vr[u] : nv;
+        nz = in ? cz[u] : nz;
+        nd = in ? cd[u] : nd;
+      }
+      if (rlive) {
+        m = mloc;
+        float* ag = a.agg + (((size_t)rb_ * D + lane) * nch + rc_) * 2;
+        coherent_store(ag, P);
+        coherent_store(ag + 1, Q);
+      }
+    }
+    for (int task = RES ? ntask : gw; task < ntask; task += nw) {   // (none with RES)
       const int b = task / nch, c = task - b * nch;
       const int t0 = c * kChunk, t1 = min(T, t0 + kChunk);
       const size_t base = (size_t)b * T * D + lane;
@@ -501,7 +565,76 @@ __global__ void __launch_bounds__(64 * kLoopWaves, 1) gru_bwd_loop_kernel(BwdLoo
     // ---- C: the update and the next v ----
     float* lam_n = a.lam[cur ^ 1];
     float* v_n = a.v[cur ^ 1];
-    for (int task = gw; task < ntask; task += nw) {
+    if constexpr (RES) {
+      const float dl0 = coherent_load(a.carry + (size_t)rtask * D + ln);   // delta at t1
+      const float lb = blam + dl0;                                         // lam_{k+1} at t1
+      // staged row r is dgh at step t0 + 1 + r; row 15 the step after the chunk
+      dgw[15 * kDgLd + lane] = act && rtail ? bfr * lb : 0.f;
+      dgw[15 * kDgLd + 64 + lane] = act && rtail ? bfz * lb : 0.f;
+      dgw[15 * kDgLd + 128 + lane] = act && rtail ? bfnr * lb : 0.f;
+      float dl = dl0, nlam = blam, nv = bv, nz = bz, nd = bd;
+#pragma unroll
+      for (int u = kChunk - 1; u >= 0; --u) {
+        const bool in = u < rlen;
+        const float R = cg[u] + fmaf(nz, nlam, nv) - lv[u];
+        const float dn = fmaf(nd, dl, R);
+        dl = in ? dn : dl;
+        const float l = lv[u] + dl;
+        nlam = in ? lv[u] : nlam;
+        nv = in ? vr[u] : nv;
+        nz = in ? cz[u] : nz;
+        nd = in ? cd[u] : nd;
+        lv[u] = l;
+        if (u >= 1) {
+          const bool st = act && in;
+          dgw[(u - 1) * kDgLd + lane] = st ? cfr[u] * l : 0.f;
+          dgw[(u - 1) * kDgLd + 64 + lane] = st ? cfz[u] * l : 0.f;
+          dgw[(u - 1) * kDgLd + 128 + lane] = st ? cfnr[u] * l : 0.f;
+        }
+      }
+      if (rlive) {
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u)
+          if (u < rlen) lam_n[rbase + (size_t)(rt0 + u) * D] = lv[u];
+      }
+      blam = lb;
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the rows are read by every lane
+      __builtin_amdgcn_wave_barrier();
+      v4f_t acc[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc[nt] = v4f_t{0.f, 0.f, 0.f, 0.f};
+      const float4* arow = reinterpret_cast<const float4*>(dgw + m16 * kDgLd + 48 * q4);
+      const float4* ub = reinterpret_cast<const float4*>(ufb) + lane;
+      float4 bcur = ub[0], bnxt = bcur, acur = arow[0], anxt = acur;
+#pragma unroll
+      for (int kk = 0; kk < 48; ++kk) {
+        if (kk + 1 < 48) bnxt = ub[(kk + 1) * 64];
+        if ((kk & 3) == 0 && kk + 4 < 48) anxt = arow[(kk >> 2) + 1];
+        const float aval = (kk & 3) == 0 ? acur.x : (kk & 3) == 1 ? acur.y : (kk & 3) == 2 ? acur.z : acur.w;
+        acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(aval, bcur.x, acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(aval, bcur.y, acc[1], 0, 0, 0);
+        acc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(aval, bcur.z, acc[2], 0, 0, 0);
+        acc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(aval, bcur.w, acc[3], 0, 0, 0);
+        bcur = bnxt;
+        if ((kk & 3) == 3) acur = anxt;
+      }
+      // V back to lane = channel through the staging rows: row r (step t0 + 1 + r) of
+      // channel 16 nt + l % 16 sits in lane l's acc[nt][r - 4 (l / 16)]
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // the MFMA operands are read before the rows are reused
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dgw[(4 * q4 + i) * kDgLd + 16 * nt + m16] = acc[nt][i];
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int u = 1; u < kChunk; ++u) vr[u] = dgw[(u - 1) * kDgLd + lane];
+      bv = rtail ? dgw[15 * kDgLd + lane] : 0.f;
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // read before the next iteration stages its rows
+      __builtin_amdgcn_wave_barrier();
+    }
+    for (int task = RES ? ntask : gw; task < ntask; task += nw) {   // (none with RES)
       const int b = task / nch, c = task - b * nch;
       const int t0 = c * kChunk, t1 = min(T, t0 + kChunk), len = t1 - t0;
       const size_t base = (size_t)b * T * D + lane;
@@ -627,15 +760,18 @@ __global__ void __launch_bounds__(64 * kLoopWaves, 1) gru_bwd_loop_kernel(BwdLoo
 hipError_t launch_gru_bwd_loop(const BwdLoopArgs& a, int num_cu, hipStream_t st) {
   if (a.D > 64) return hipErrorInvalidValue;
   constexpr int threads = 64 * kLoopWaves;
-  int per_cu = cached_occupancy((const void*)gru_bwd_loop_kernel, 0, threads);
+  const int per_cu = min(cached_occupancy((const void*)gru_bwd_loop_kernel<true>, 0, threads),
+                         cached_occupancy((const void*)gru_bwd_loop_kernel<false>, 0, threads));
   if (per_cu < 1) return hipErrorInvalidConfiguration;
   long g = (long)per_cu * num_cu;
   if (g > kMaxGrid) g = kMaxGrid;
-  const long work = (long)a.B * a.nch;
+  const long work = ((long)a.B * a.nch + kLoopWaves - 1) / kLoopWaves;
+  const bool res = work <= g;   // a wave per chunk
   if (g > work) g = work;
   if (g < 1) g = 1;
   void* args[] = {const_cast<BwdLoopArgs*>(&a)};
-  return launch_persistent((const void*)gru_bwd_loop_kernel, (int)g, 0, args, st, threads);
+  const void* fn = res ? (const void*)gru_bwd_loop_kernel<true> : (const void*)gru_bwd_loop_kernel<false>;
+  return launch_persistent(fn, (int)g, 0, args, st, threads);
 }
 
 }  // namespace pnr

@@ -134,3 +134,34 @@ def test_full_size_backward_matches_bptt_oracle_on_sampled_channels(name):
         assert np.all(err <= 2.0 ** -8 * bound + 1e-5 * np.abs(r).max())
     finally:
         torch.cuda.empty_cache()
+
+
+def test_full_size_dense_backward_matches_bptt_oracle():
+    """The dense GRU's backward pass (the adjoint refined on the device until its residual
+    is 2e-5 of its first) at the converged states of the quasi workload, at full size and
+    in bench's launch configuration, against the BPTT oracle on every output: each
+    gradient within 2e-4 of its scale, as for the small dense cases (the refinement's
+    stopping point sets the bar)."""
+    w = WL.get_workload("gru_quasi_bwd")
+    p = WL.generate(w)
+    d = {k: (None if v is None else v.to("cuda")) for k, v in p.items()}
+    print("# full-size backward: gru_quasi_bwd", flush=True)
+    try:
+        fwd = pnr.evaluate(w.cell, d["W"], d["U"], d["x"], b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"],
+                           max_iters=w.max_iters, tol=w.tol, jac_mode=w.jac_modes[0])
+        assert fwd["status"] == pnr.OK
+        h = fwd["h"]
+        g = torch.randn(h.shape, generator=torch.Generator().manual_seed(w.seed + 7), dtype=torch.float32).to("cuda")
+        got = pnr.backward(w.cell, d["W"], d["U"], d["x"], h, g, b_x=d["b_x"], b_h=d["b_h"], h0=d["h0"])
+        assert got["status"] == pnr.OK and got["history"][-1] <= 2e-5 * got["history"][0]
+        q = {k: (None if v is None else WL.as_f64(v)) for k, v in p.items()}
+        ref = O.bptt(w.cell, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], h.double().cpu().numpy(),
+                     g.double().cpu().numpy())
+        for k, rk in (("x", "dx"), ("W", "dW"), ("U", "dU"), ("b_x", "db_x"), ("b_h", "db_h"), ("h0", "dh0")):
+            a = got[k].double().cpu().numpy()
+            r = ref[rk]
+            err = np.abs(a - r).max() / max(np.abs(r).max(), 1e-30)
+            print(f"#   {rk} relative error {err:.2e} (iters {got['iters']})", flush=True)
+            assert err < 2e-4, (rk, err)
+    finally:
+        torch.cuda.empty_cache()
