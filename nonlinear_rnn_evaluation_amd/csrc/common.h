@@ -362,6 +362,35 @@ __device__ __forceinline__ Flt select_aff(bool take, const Flt& a, const Flt& b)
              take ? a.e : b.e, take ? a.f : b.f, take ? a.g : b.g};
 }
 
+__device__ __forceinline__ Flt shfl_row_shr_aff(const Flt& v, const Flt& id, int s) {
+  Flt o;
+#define PNR_DPP7(C)                                                                 \
+  o.a = dpp_f<C>(id.a, v.a); o.b = dpp_f<C>(id.b, v.b); o.c = dpp_f<C>(id.c, v.c); \
+  o.d = dpp_f<C>(id.d, v.d); o.e = dpp_f<C>(id.e, v.e); o.f = dpp_f<C>(id.f, v.f); \
+  o.g = dpp_f<C>(id.g, v.g);
+  switch (s) {
+    case 1: PNR_DPP7(0x111) break;
+    case 2: PNR_DPP7(0x112) break;
+    case 4: PNR_DPP7(0x114) break;
+    default: PNR_DPP7(0x118) break;
+  }
+#undef PNR_DPP7
+  return o;
+}
+__device__ __forceinline__ Flt readlane_aff(const Flt& v, int l) {
+  return Flt{readlane_f(v.a, l), readlane_f(v.b, l), readlane_f(v.c, l), readlane_f(v.d, l),
+             readlane_f(v.e, l), readlane_f(v.f, l), readlane_f(v.g, l)};
+}
+// one lane up across the whole wave (DPP wave_shr:1); lane 0 takes `lane0`
+__device__ __forceinline__ Flt flt_wave_shr1(const Flt& v, const Flt& lane0) {
+  return Flt{dpp_f<0x138>(lane0.a, v.a), dpp_f<0x138>(lane0.b, v.b), dpp_f<0x138>(lane0.c, v.c),
+             dpp_f<0x138>(lane0.d, v.d), dpp_f<0x138>(lane0.e, v.e), dpp_f<0x138>(lane0.f, v.f),
+             dpp_f<0x138>(lane0.g, v.g)};
+}
+__device__ __forceinline__ Aff1 aff_wave_shr1(const Aff1& v, const Aff1& lane0) {
+  return Aff1{dpp_f<0x138>(lane0.a, v.a), dpp_f<0x138>(lane0.b, v.b)};
+}
+
 template <class E>
 __device__ __forceinline__ E wave_inclusive_scan(E v, const E& id) {
   const int rl = (int)(lane_id() & 15);

@@ -531,20 +531,13 @@ __global__ void __launch_bounds__(64 * kLoopWaves, 1) gru_bwd_loop_kernel(BwdLoo
           p_ = coherent_load(ag + (size_t)c * 2);
           q_ = coherent_load(ag + (size_t)c * 2 + 1);
         }
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const float pp = __shfl_up(p_, off, 64), pq = __shfl_up(q_, off, 64);
-          if (lane >= off) {
-            q_ = fmaf(p_, pq, q_);
-            p_ *= pp;
-          }
-        }
-        if (lane == 63) s_tot[wid] = make_float2(p_, q_);
+        const Aff1 f = wave_inclusive_scan(Aff1{p_, q_}, aff_identity1());
+        if (lane == 63) s_tot[wid] = make_float2(f.a, f.b);
         __syncthreads();
         float xg = x;   // after this wave's group
         for (int s2 = wid - sub; s2 < wid; ++s2) xg = fmaf(s_tot[s2].x, xg, s_tot[s2].y);
-        const float pp = __shfl_up(p_, 1, 64), pq = __shfl_up(q_, 1, 64);
-        const float xin = lane == 0 ? xg : fmaf(pp, xg, pq);
+        const Aff1 before = aff_wave_shr1(f, aff_identity1());
+        const float xin = fmaf(before.a, xg, before.b);
         if (live && c >= 0) coherent_store(a.carry + ((size_t)b * nch + c) * D + i, xin);
         for (int s2 = wid - sub; s2 < wid - sub + wpr; ++s2) x = fmaf(s_tot[s2].x, x, s_tot[s2].y);
         __syncthreads();   // the totals are read before the next round writes them

@@ -56,14 +56,6 @@ __device__ __forceinline__ Flt filter_step(float j, float r, float lam) {
   const float j2 = j * j;
   return Flt{j2, 1.f, lam * j2, 1.f + lam, 0.f, r, j};
 }
-__device__ __forceinline__ Flt flt_shfl_up(const Flt& f, int off) {
-  return Flt{__shfl_up(f.a, off, 64), __shfl_up(f.b, off, 64), __shfl_up(f.c, off, 64), __shfl_up(f.d, off, 64),
-             __shfl_up(f.e, off, 64), __shfl_up(f.f, off, 64), __shfl_up(f.g, off, 64)};
-}
-__device__ __forceinline__ Flt flt_shfl(const Flt& f, int src) {
-  return Flt{__shfl(f.a, src, 64), __shfl(f.b, src, 64), __shfl(f.c, src, 64), __shfl(f.d, src, 64),
-             __shfl(f.e, src, 64), __shfl(f.f, src, 64), __shfl(f.g, src, 64)};
-}
 // the rows this wave just wrote to LDS are read back by every lane of the wave
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
@@ -434,16 +426,12 @@ __global__ void __launch_bounds__(64 * kElkWaves, 1) gru_elk_loop_kernel(ElkLoop
           f = Flt{coherent_load(p), coherent_load(p + 1), coherent_load(p + 2), coherent_load(p + 3),
                   coherent_load(p + 4), coherent_load(p + 5), coherent_load(p + 6)};
         }
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const Flt prev = flt_shfl_up(f, off);
-          if (lane >= off) f = compose(f, prev);
-        }
+        f = wave_inclusive_scan(f, flt_identity());
         if (lane == 63) s_tot[wid] = f;
         __syncthreads();
         V3 xg = x;   // entering this wave's group
         for (int s2 = wid - sub; s2 < wid; ++s2) xg = normalized(apply(s_tot[s2], xg));
-        const Flt before = flt_shfl_up(f, 1);
+        const Flt before = flt_wave_shr1(f, flt_identity());
         const V3 xin = lane == 0 ? xg : normalized(apply(before, xg));
         if (live && c < nch) {
           float* cp = a.carry + ((size_t)b * nch + c) * 2 * D + i;
@@ -489,20 +477,13 @@ __global__ void __launch_bounds__(64 * kElkWaves, 1) gru_elk_loop_kernel(ElkLoop
           p_ = coherent_load(ag2 + (size_t)c * 2);
           q_ = coherent_load(ag2 + (size_t)c * 2 + 1);
         }
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const float pp = __shfl_up(p_, off, 64), pq = __shfl_up(q_, off, 64);
-          if (lane >= off) {
-            q_ = fmaf(p_, pq, q_);
-            p_ *= pp;
-          }
-        }
-        if (lane == 63) s_tot2[wid] = make_float2(p_, q_);
+        const Aff1 f = wave_inclusive_scan(Aff1{p_, q_}, aff_identity1());
+        if (lane == 63) s_tot2[wid] = make_float2(f.a, f.b);
         __syncthreads();
         float xg = x;   // after this wave's group
         for (int s2 = wid - sub; s2 < wid; ++s2) xg = fmaf(s_tot2[s2].x, xg, s_tot2[s2].y);
-        const float pp = __shfl_up(p_, 1, 64), pq = __shfl_up(q_, 1, 64);
-        const float xin = lane == 0 ? xg : fmaf(pp, xg, pq);
+        const Aff1 before = aff_wave_shr1(f, aff_identity1());
+        const float xin = fmaf(before.a, xg, before.b);
         if (live && c >= 0) coherent_store(a.carry2 + ((size_t)b * nch + c) * D + i, xin);
         for (int s2 = wid - sub; s2 < wid - sub + wpr; ++s2) x = fmaf(s_tot2[s2].x, x, s_tot2[s2].y);
         __syncthreads();

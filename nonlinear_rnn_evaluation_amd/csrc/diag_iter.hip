@@ -797,25 +797,6 @@ hipError_t launch_diag_newton(int cell, const DiagLoopArgs& a, int grid, hipStre
 // diag_newton_kernel; the backward sweep maps thread t to the (255 - t)-th run of steps
 // so that lane order is reverse time and the same forward scan machinery applies.
 template <> __device__ __forceinline__ Flt identity_of<Flt>() { return flt_identity(); }
-__device__ __forceinline__ Flt shfl_row_shr_aff(const Flt& v, const Flt& id, int s) {
-  Flt o;
-#define PNR_DPP7(C)                                                                 \
-  o.a = dpp_f<C>(id.a, v.a); o.b = dpp_f<C>(id.b, v.b); o.c = dpp_f<C>(id.c, v.c); \
-  o.d = dpp_f<C>(id.d, v.d); o.e = dpp_f<C>(id.e, v.e); o.f = dpp_f<C>(id.f, v.f); \
-  o.g = dpp_f<C>(id.g, v.g);
-  switch (s) {
-    case 1: PNR_DPP7(0x111) break;
-    case 2: PNR_DPP7(0x112) break;
-    case 4: PNR_DPP7(0x114) break;
-    default: PNR_DPP7(0x118) break;
-  }
-#undef PNR_DPP7
-  return o;
-}
-__device__ __forceinline__ Flt readlane_aff(const Flt& v, int l) {
-  return Flt{readlane_f(v.a, l), readlane_f(v.b, l), readlane_f(v.c, l), readlane_f(v.d, l),
-             readlane_f(v.e, l), readlane_f(v.f, l), readlane_f(v.g, l)};
-}
 __device__ __forceinline__ V3 wave_shr1(const V3& x, const V3& lane0) {
   return V3{wave_shr1(x.u, lane0.u), wave_shr1(x.v, lane0.v), wave_shr1(x.n, lane0.n)};
 }
