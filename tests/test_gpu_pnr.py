@@ -149,6 +149,23 @@ def test_fixed_iterations_multi_tile_dense(mode, D, sd):
     np.testing.assert_allclose(_np(got["h"]), ref["states"], rtol=0, atol=1e-10 if sd == WL.DT_F64 else 1e-4)
 
 
+def test_fixed_iterations_dense_full_many_tiles_per_block():
+    """The dense-Jacobian MFMA kernel with several 64-step tiles per block (B = 4,
+    T = 40000: 2500 tiles, more than a full grid has blocks), so that every block loads
+    its next tile while it works on the current one and looks back across many tiles;
+    two Newton iterations against the oracle's loop solver."""
+    T = 40000
+    p = WL.random_problem(WL.CELL_GRU, 4, T, 16, 5, seed=T, x_dtype=WL.DT_F32, state_dtype=WL.DT_F32,
+                          bias_std=0.2, h0_std=0.3, w_std=0.5 / math.sqrt(16))
+    q = _f64(p)
+    print("# dense FULL, 2500 tiles", flush=True)
+    got = _run(WL.CELL_GRU, p, 2, -1.0, WL.JAC_FULL)
+    ref = O.newton_dense(WL.CELL_GRU, q["W"], q["U"], q["b_x"], q["b_h"], q["x"], q["h0"], 2, -1.0, WL.JAC_FULL,
+                         solver="loop")
+    np.testing.assert_allclose(_np(got["h"]), ref["states"], rtol=0, atol=1e-4)
+    np.testing.assert_allclose(got["history"], ref["rhos"], rtol=1e-3, atol=1e-5)
+
+
 # ---------------------------------------------------------------------------------
 # Converged result = sequential evaluation
 @pytest.mark.parametrize("cell,D,mode", [(WL.CELL_GRU, 8, WL.JAC_FULL), (WL.CELL_GRU, 32, WL.JAC_DIAG),
