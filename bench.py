@@ -396,7 +396,7 @@ def run_backward(name, steps, warmup, parity=True):
     dense = w.cell == WL.CELL_GRU
     bytes_call = dense_adjoint_bytes(w, grads["iters"]) if dense else adjoint_bytes(w)
     achieved = bytes_call / (adj_ms * 1e-3) / 1e9 if adj_ms > 0 else 0.0
-    ksrc = CSRC + "diag_iter.hip"
+    ksrc = CSRC + ("dense_bwd.hip" if dense else "diag_iter.hip")
     traffic = None
     pmc_path = os.path.join(ROOT, "profiles", f"newton_kernel_{name}_pmc.json")
     if os.path.exists(pmc_path):
@@ -404,8 +404,7 @@ def run_backward(name, steps, warmup, parity=True):
             pmc = json.load(f)
         if pmc.get("kernel_src_sha") == src_hash(ksrc):
             traffic = pmc.get("bytes_per_launch")
-    kname = ("pnr::gru_bwd_loop_kernel (persistent refinement loop, one read-back per call)" if dense
-             else "pnr::adjoint_diag_kernel")
+    kname = "pnr::gru_bwd_loop_kernel" if dense else "pnr::adjoint_diag_kernel"
     roof = {"kernel": kname, "avg_launch_us": round(adj_ms * 1e3 / launches, 3), "launches_per_step": launches,
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,

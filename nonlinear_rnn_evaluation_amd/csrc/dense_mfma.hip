@@ -161,6 +161,9 @@ __device__ __forceinline__ int next_buffer(int cur, int jac, int nbuf) {
 // Read up to Wn predecessor slots (SV values each, aggregate first) into Win and find
 // the nearest predecessor with a published prefix whose successors (up to this tile)
 // all published their aggregates.  Returns that window index, or -1.  Block-uniform.
+// BATCH loads per thread are issued before any is used: with BATCH * PNR_BLOCK >= Wn * SV
+// the whole window costs one memory round trip.
+template <int BATCH = kLoadBatch>
 __device__ __forceinline__ int window_read(const uint64_t* __restrict__ slots, int tile, int Wn, int SV, int SA,
                                            uint32_t ep, float* __restrict__ Win) {
   __shared__ int s_ok[16][2];
@@ -169,16 +172,16 @@ __device__ __forceinline__ int window_read(const uint64_t* __restrict__ slots, i
   if (tid < Wn) { s_ok[tid][0] = 1; s_ok[tid][1] = 1; }
   __syncthreads();
   // every load of a batch first (indices clamped into the window), then the tag checks
-  for (int j0 = 0; j0 < Wn * SV; j0 += kLoadBatch * PNR_BLOCK) {
-    uint64_t x[kLoadBatch];
+  for (int j0 = 0; j0 < Wn * SV; j0 += BATCH * PNR_BLOCK) {
+    uint64_t x[BATCH];
 #pragma unroll
-    for (int j = 0; j < kLoadBatch; ++j) {
+    for (int j = 0; j < BATCH; ++j) {
       const int idx = min(j0 + tid + j * PNR_BLOCK, Wn * SV - 1);
       const int w = idx / SV, e = idx - w * SV;
       x[j] = __hip_atomic_load(slots + (size_t)(tile - 1 - w) * SV + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 #pragma unroll
-    for (int j = 0; j < kLoadBatch; ++j) {
+    for (int j = 0; j < BATCH; ++j) {
       const int idx = j0 + tid + j * PNR_BLOCK;
       if (idx < Wn * SV) {
         const int w = idx / SV, e = idx - w * SV;
@@ -913,7 +916,8 @@ __device__ __forceinline__ float jac_entry(float z, float al, float be, float ga
   return fmaf(al, uz, fmaf(be, ur, ga * un)) + (diag ? z : 0.f);
 }
 
-__global__ void __launch_bounds__(PNR_BLOCK) dense_full_mfma_kernel(DenseLoopArgs<float> a) {
+// two waves per SIMD (two 4-wave blocks per CU, as its LDS allows): the register budget is 256
+__global__ void __launch_bounds__(PNR_BLOCK, 2) dense_full_mfma_kernel(DenseLoopArgs<float> a) {
   extern __shared__ __align__(16) float lds[];
   Ctrl* ctrl = a.ctrl;
   constexpr int D = kF, LD = kF + 4;
@@ -1118,7 +1122,8 @@ __global__ void __launch_bounds__(PNR_BLOCK) dense_full_mfma_kernel(DenseLoopArg
         // ---- decoupled look-back: apply the aggregates after the nearest prefix to it ----
         uint32_t spins = 0;
         while (true) {
-          const int pw = window_read(a.slots, tile, min(seg, kFWin), kFSlot, kFAgg, ep, Win);
+          const int pw = window_read<(kFWin * kFSlot + PNR_BLOCK - 1) / PNR_BLOCK>(a.slots, tile, min(seg, kFWin),
+                                                                                kFSlot, kFAgg, ep, Win);
           if (pw >= 0) {
             if (tid < D) Vec[tid] = Win[pw * kFSlot + kFAgg + tid];
             __syncthreads();
