@@ -1202,27 +1202,31 @@ __global__ void __launch_bounds__(PNR_BLOCK, 2) dense_full_mfma_kernel(DenseLoop
           }
           xa = ya;
           xb = yb;
+          // the new states go into the staged rows (row s + 1 holds step t0 + s): no global
+          // store or wait inside the chain
           if (m == 0) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int c = 4 * q + i;
-              if (sa < Lv) {
-                float* o = Hnext + ((size_t)b * T + t0 + sa) * D + c;
-                const float v = X[(sa + 1) * LD + c] + xa[i];
-                if (sa == kTL - 1) coherent_store(o, v);
-                else *o = v;
-              }
-              if (sb < Lv) {
-                float* o = Hnext + ((size_t)b * T + t0 + sb) * D + c;
-                const float v = X[(sb + 1) * LD + c] + xb[i];
-                if (sb == kTL - 1) coherent_store(o, v);   // the next tile's halo
-                else *o = v;
-              }
+              X[(sa + 1) * LD + 4 * q + i] += xa[i];
+              X[(sb + 1) * LD + 4 * q + i] += xb[i];
             }
           }
         }
       }
       __syncthreads();
+      // the tile's new states, 16 threads to a row (coalesced), the last step's coherently
+      // (the next tile's halo)
+#pragma unroll
+      for (int j = 0; j < kTL * kF / PNR_BLOCK; ++j) {
+        const int idx = tid + j * PNR_BLOCK, s_ = idx >> 4, c_ = idx & 15;
+        if (s_ < Lv) {
+          float* o = Hnext + ((size_t)b * T + t0 + s_) * D + c_;
+          const float v = X[(s_ + 1) * LD + c_];
+          if (s_ == kTL - 1) coherent_store(o, v);
+          else *o = v;
+        }
+      }
+      __syncthreads();   // the rows are read before the next tile stages its own
     }
     end_pass(a, blk_max, k, cur);
     if (__hip_atomic_load(&ctrl->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) || has_fault(ctrl)) break;
