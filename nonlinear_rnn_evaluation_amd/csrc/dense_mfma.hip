@@ -122,34 +122,30 @@ __device__ __forceinline__ void gates_frag(const v4f (&f)[DM / 16], const float 
   }
 }
 
-// Residual partial -> grid barrier; the last block merges the partials and decides.
-__device__ __forceinline__ void end_pass(const DenseLoopArgs<float>& a, uint32_t blk_max, int k, int cur) {
+// The pass's residual maximum into this iteration's word (the zeroed partials area), the
+// lean grid barrier, then every block reads the word and takes the same decision (stop when
+// rho_k <= tol, on a non-finite rho, or at the residual-only pass after max_iters), which
+// block 0 records.  Returns true when the loop stops or this block's barrier wait ran out.
+__device__ __forceinline__ bool end_pass(const DenseLoopArgs<float>& a, uint32_t blk_max, int k, int cur,
+                                         uint32_t& gen) {
   __shared__ uint32_t s_wmax[PNR_WAVES];
+  __shared__ uint32_t s_bits;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  uint32_t* word = reinterpret_cast<uint32_t*>(a.partials) + k;
   blk_max = wave_max_u32(blk_max);
   if (lane == 0) s_wmax[wid] = blk_max;
   __syncthreads();
   if (tid == 0) {
     uint32_t m = s_wmax[0];
     for (int w = 1; w < PNR_WAVES; ++w) m = max(m, s_wmax[w]);
-    __hip_atomic_store(reinterpret_cast<uint32_t*>(a.partials) + blockIdx.x, m, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+    if (m) __hip_atomic_fetch_max(word, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  Ctrl* ctrl = a.ctrl;
-  grid_barrier(ctrl, [&]() {
-    uint32_t m = 0;
-    for (int i = tid; i < (int)gridDim.x; i += PNR_BLOCK)
-      m = max(m, __hip_atomic_load(reinterpret_cast<uint32_t*>(a.partials) + i, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT));
-    m = wave_max_u32(m);
-    __syncthreads();
-    if (lane == 0) s_wmax[wid] = m;
-    __syncthreads();
-    if (tid == 0) {
-      for (int w = 0; w < PNR_WAVES; ++w) m = max(m, s_wmax[w]);
-      finish_iteration(ctrl, a.rho_hist, bits_to_rho(m), k, cur, a.max_iters, a.tol);
-    }
-  });
+  if (!grid_sync(a.ctrl, gen)) return true;
+  if (tid == 0) s_bits = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const double rho = bits_to_rho(s_bits);
+  if (blockIdx.x == 0 && tid == 0) finish_iteration(a.ctrl, a.rho_hist, rho, k, cur, a.max_iters, a.tol);
+  return !(rho < __builtin_inf()) || rho <= a.tol || k >= a.max_iters;
 }
 
 __device__ __forceinline__ int next_buffer(int cur, int jac, int nbuf) {
@@ -961,6 +957,7 @@ __global__ void __launch_bounds__(PNR_BLOCK, 2) dense_full_mfma_kernel(DenseLoop
   const float bhr = Bh[m], bhz = Bh[D + m], bhn = Bh[2 * D + m];
 
   int cur = -1, jac = -1;
+  uint32_t gen = 0;   // generation of the next grid barrier
   for (int k = 0; k <= a.max_iters; ++k) {
     const bool resid_only = k == a.max_iters;
     if (!resid_only && k % a.jac_every == 0) jac = cur;
@@ -1048,7 +1045,7 @@ __global__ void __launch_bounds__(PNR_BLOCK, 2) dense_full_mfma_kernel(DenseLoop
           xb[i] = xa[i];
         }
         float va = 0.f, vb = 0.f;
-#pragma unroll 1
+#pragma unroll 4
         for (int st = kFPartLen - 1; st >= 0; --st) {
           const int sa = pa * kFPartLen + st, sb = pb * kFPartLen + st;
           float aa[4], ab[4];
@@ -1182,7 +1179,7 @@ __global__ void __launch_bounds__(PNR_BLOCK, 2) dense_full_mfma_kernel(DenseLoop
           xa[i] = m == 0 ? Pin[pa * D + 4 * q + i] : 0.f;
           xb[i] = m == 0 ? Pin[pb * D + 4 * q + i] : 0.f;
         }
-#pragma unroll 1
+#pragma unroll 4
         for (int st = 0; st < kFPartLen; ++st) {
           const int sa = pa * kFPartLen + st, sb = pb * kFPartLen + st;
           const float za = Zv[sa * D + m], ala = Al[sa * D + m], bea = Be[sa * D + m], gaa = Ga[sa * D + m];
@@ -1228,8 +1225,7 @@ __global__ void __launch_bounds__(PNR_BLOCK, 2) dense_full_mfma_kernel(DenseLoop
       }
       __syncthreads();   // the rows are read before the next tile stages its own
     }
-    end_pass(a, blk_max, k, cur);
-    if (__hip_atomic_load(&ctrl->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) || has_fault(ctrl)) break;
+    if (end_pass(a, blk_max, k, cur, gen) || has_fault(ctrl)) break;
     cur = next;
   }
 }
