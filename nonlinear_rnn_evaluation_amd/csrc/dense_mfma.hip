@@ -895,15 +895,60 @@ __global__ void __launch_bounds__(PNR_BLOCK, (RES && TL > 64) ? 1 : 2)
 
 // =====================================================================================
 // Dense 16x16 Jacobian.  LDS: Bh[48] | X[65 LD] | Xj (reuse) | R, Z, Al, Be, Ga [64][16] |
-// Pagg[8][272] | Tot[272] | Tmp[272] | Pin[9][16] | Vec[2][16] | Win[W][288] | Din[16].
+// Pagg[8][336] | Wm[4][336] | Xm[2][336] | Tot[336] | Win[W][288] | Din[16].
 constexpr int kF = 16;
 constexpr int kFAgg = kF * kF + kF;      // aggregate values: M (row-major) then v
 constexpr int kFSlot = kFAgg + kF;       // slot values: aggregate, then prefix
 constexpr int kFWin = 16;
+// Aggregates staged for MFMA operand reads: the rows of M at a stride of kFL floats, then
+// v.  With that stride a row's 4-float run (a b128 read) and a column's 4 entries fall on
+// distinct banks for the 64 lanes.
+constexpr int kFL = kF + 4;
+constexpr int kFMat = kF * kFL + kF;
 __host__ __device__ inline size_t mff_lds_floats(int reuse) {
   const int LD = kF + 4;
   return (size_t)3 * kF + (size_t)(kTL + 1) * LD * (reuse ? 2 : 1) + (size_t)5 * kTL * kF +
-         (size_t)kFParts * kFAgg + 2 * kFAgg + (size_t)(kFParts + 1) * kF + 2 * kF + (size_t)kFWin * kFSlot + kF;
+         (size_t)(kFParts + 4 + 2 + 1) * kFMat + (size_t)kFWin * kFSlot + kF;
+}
+
+// 16x16 operands of v_mfma_f32_16x16x4f32 with k split as 4q + i over the four issues:
+// lane (q, m) holds A[m][4q+i] (an A fragment) and B[4q+i][m] (a B fragment), and the
+// accumulator of A B holds (A B)[4q+i][m] -- the B fragment of the product.
+template <int LDM = kFL>
+__device__ __forceinline__ v4f ld_arow(const float* S, int m, int q) {
+  return *reinterpret_cast<const v4f*>(S + m * LDM + 4 * q);
+}
+__device__ __forceinline__ v4f ld_bcol(const float* S, int m, int q) {
+  v4f b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b[i] = S[(4 * q + i) * kFL + m];
+  return b;
+}
+__device__ __forceinline__ void st_acc(float* S, v4f c, int m, int q) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) S[(4 * q + i) * kFL + m] = c[i];
+}
+__device__ __forceinline__ v4f mm16(v4f a, v4f b, v4f c) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c = mfma4(a[i], b[i], c);
+  return c;
+}
+// (A v)[m] in every lane of row m, from A's fragment and v in LDS
+__device__ __forceinline__ float mv_rows(v4f a, const float* v, int q) {
+  const v4f x = *reinterpret_cast<const v4f*>(v + 4 * q);
+  float s = fmaf(a[0], x[0], fmaf(a[1], x[1], fmaf(a[2], x[2], a[3] * x[3])));
+  s += __shfl_xor(s, 16);
+  s += __shfl_xor(s, 32);
+  return s;
+}
+// d <- M d + v for a staged aggregate (rows at stride LDM, then v), with d in column 0 of a
+// B fragment (lane (q, 0) holds d[4q+i], every other lane zeros); the result has the same form
+template <int LDM>
+__device__ __forceinline__ v4f mv_col0(const float* S, v4f d, int m, int q) {
+  v4f c;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = m == 0 ? S[kF * LDM + 4 * q + i] : 0.f;
+  return mm16(ld_arow<LDM>(S, m, q), d, c);
 }
 
 // Entry J_t[row][col] from the factors of `row` and U_g[row][col] (g = r, z, n).
@@ -917,7 +962,7 @@ __global__ void __launch_bounds__(PNR_BLOCK, 2) dense_full_mfma_kernel(DenseLoop
   extern __shared__ __align__(16) float lds[];
   Ctrl* ctrl = a.ctrl;
   constexpr int D = kF, LD = kF + 4;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 15, q = lane >> 4;
   const int T = a.T;
   const bool reuse = a.nbuf > 2;
@@ -929,12 +974,11 @@ __global__ void __launch_bounds__(PNR_BLOCK, 2) dense_full_mfma_kernel(DenseLoop
   float* Al = Zv + kTL * D;
   float* Be = Al + kTL * D;
   float* Ga = Be + kTL * D;
-  float* Pagg = Ga + kTL * D;
-  float* Tot = Pagg + kFParts * kFAgg;
-  float* Tmp = Tot + kFAgg;
-  float* Pin = Tmp + kFAgg;
-  float* Vec = Pin + (kFParts + 1) * D;
-  float* Win = Vec + 2 * D;
+  float* Pagg = Ga + kTL * D;           // part aggregates
+  float* Wm = Pagg + kFParts * kFMat;   // products of part pairs
+  float* Xm = Wm + 4 * kFMat;           // products of those pairs
+  float* Tot = Xm + 2 * kFMat;          // the tile total
+  float* Win = Tot + kFMat;
   float* Din = Win + kFWin * kFSlot;
 
   for (int i = tid; i < 3 * D; i += PNR_BLOCK) Bh[i] = a.bh ? a.bh[i] : 0.f;
@@ -975,6 +1019,7 @@ __global__ void __launch_bounds__(PNR_BLOCK, 2) dense_full_mfma_kernel(DenseLoop
       if (has_fault(ctrl)) break;
       const int seg = item / a.B, b = item - seg * a.B;
       const int tile = b * a.tiles_per_row + seg;   // slot index: row-major
+      uint64_t* myslot = a.slots + (size_t)tile * kFSlot;
       const int t0 = seg * kTL, Lv = min(kTL, T - t0);
       const float* gxb = a.gx + (size_t)b * T * 3 * D;
       stage_rows(X, Hcur, a.h0, b, t0, T, D, LD);
@@ -1073,76 +1118,75 @@ __global__ void __launch_bounds__(PNR_BLOCK, 2) dense_full_mfma_kernel(DenseLoop
         va += __shfl_xor(va, 32);
         vb += __shfl_xor(vb, 16);
         vb += __shfl_xor(vb, 32);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          Pagg[pa * kFAgg + m * D + 4 * q + i] = xa[i];
-          Pagg[pb * kFAgg + m * D + 4 * q + i] = xb[i];
-        }
+        float* Pa = Pagg + pa * kFMat;
+        float* Pb = Pagg + pb * kFMat;
+        *reinterpret_cast<v4f*>(Pa + m * kFL + 4 * q) = xa;
+        *reinterpret_cast<v4f*>(Pb + m * kFL + 4 * q) = xb;
         if (q == 0) {
-          Pagg[pa * kFAgg + D * D + m] = va;
-          Pagg[pb * kFAgg + D * D + m] = vb;
+          Pa[kF * kFL + m] = va;
+          Pb[kF * kFL + m] = vb;
         }
-      }
-      __syncthreads();
-
-      // ---- tile total: (M, v) <- part_p o (M, v) for p = 1..7 ----
-      for (int i = tid; i < kFAgg; i += PNR_BLOCK) Tot[i] = Pagg[i];
-      __syncthreads();
-#pragma unroll 1
-      for (int p = 1; p < kFParts; ++p) {
-        const float* Mp = Pagg + p * kFAgg;
-        {
-          const int r_ = tid >> 4, c_ = tid & 15;   // 256 threads = 16 x 16 entries
-          float s_ = 0.f;
+        // ---- tile total as a pairwise tree on MFMA ----
+        // level 1, in-wave (the part rows were written by this wave): W = M_b M_a
+        const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+        v4f w4 = mm16(xb, ld_bcol(Pa, m, q), zero4);
+        float vw = mv_rows(xb, Pa + kF * kFL, q) + vb;
+        float* Ww = Wm + wid * kFMat;
+        st_acc(Ww, w4, m, q);
+        if (q == 0) Ww[kF * kFL + m] = vw;
+        __syncthreads();
+        // level 2: waves 0 and 2 form X_0 = W_1 W_0 and X_1 = W_3 W_2 (B: their own W)
+        if (wid == 0 || wid == 2) {
+          const float* Wl = Wm + (wid + 1) * kFMat;
+          const v4f al = ld_arow(Wl, m, q);
+          w4 = mm16(al, w4, zero4);
+          vw = mv_rows(al, Ww + kF * kFL, q) + Wl[kF * kFL + m];
+          float* Xd = Xm + (wid >> 1) * kFMat;
+          st_acc(Xd, w4, m, q);
+          if (q == 0) Xd[kF * kFL + m] = vw;
+        }
+        __syncthreads();
+        // level 3: wave 0 forms the tile total T = X_1 X_0 and publishes it
+        if (wid == 0) {
+          const float* X1 = Xm + kFMat;
+          const v4f al = ld_arow(X1, m, q);
+          const v4f t4 = mm16(al, w4, zero4);
+          const float vt = mv_rows(al, Xm + kF * kFL, q) + X1[kF * kFL + m];
+          st_acc(Tot, t4, m, q);
+          if (q == 0) Tot[kF * kFL + m] = vt;
+          if (seg == 0) {
+            if (q == 0) {
+              slot_put(myslot + kFAgg + m, ep, vt);
+              Din[m] = 0.f;
+            }
+          } else {
 #pragma unroll
-          for (int l = 0; l < D; ++l) s_ = fmaf(Mp[r_ * D + l], Tot[l * D + c_], s_);
-          Tmp[r_ * D + c_] = s_;
-          if (tid < D) {
-            float v_ = Mp[D * D + tid];
-#pragma unroll
-            for (int l = 0; l < D; ++l) v_ = fmaf(Mp[tid * D + l], Tot[D * D + l], v_);
-            Tmp[D * D + tid] = v_;
+            for (int i = 0; i < 4; ++i) slot_put(myslot + (4 * q + i) * kF + m, ep, t4[i]);
+            if (q == 0) slot_put(myslot + kF * kF + m, ep, vt);
           }
         }
-        __syncthreads();
-        for (int i = tid; i < kFAgg; i += PNR_BLOCK) Tot[i] = Tmp[i];
-        __syncthreads();
       }
-      uint64_t* myslot = a.slots + (size_t)tile * kFSlot;
-      if (seg == 0) {
-        if (tid < D) {
-          slot_put(myslot + kFAgg + tid, ep, Tot[D * D + tid]);
-          Din[tid] = 0.f;
-        }
-      } else {
-        for (int i = tid; i < kFAgg; i += PNR_BLOCK) slot_put(myslot + i, ep, Tot[i]);
-        // ---- decoupled look-back: apply the aggregates after the nearest prefix to it ----
+      if (seg > 0) {
+        // ---- decoupled look-back: wave 0 applies the aggregates after the nearest
+        // published prefix, as a chain of MFMA matrix-vector products (d in column 0) ----
         uint32_t spins = 0;
         while (true) {
           const int pw = window_read<(kFWin * kFSlot + PNR_BLOCK - 1) / PNR_BLOCK>(a.slots, tile, min(seg, kFWin),
                                                                                 kFSlot, kFAgg, ep, Win);
           if (pw >= 0) {
-            if (tid < D) Vec[tid] = Win[pw * kFSlot + kFAgg + tid];
-            __syncthreads();
-            int src = 0;
-            for (int w = pw - 1; w >= 0; --w) {
-              if (tid < D) {
-                const float* Mw = Win + w * kFSlot;
-                float v_ = Mw[D * D + tid];
+            if (wid == 0) {
+              v4f d;
 #pragma unroll
-                for (int l = 0; l < D; ++l) v_ = fmaf(Mw[tid * D + l], Vec[src * D + l], v_);
-                Vec[(1 - src) * D + tid] = v_;
+              for (int i = 0; i < 4; ++i) d[i] = m == 0 ? Win[pw * kFSlot + kFAgg + 4 * q + i] : 0.f;
+              for (int w = pw - 1; w >= 0; --w) d = mv_col0<kF>(Win + w * kFSlot, d, m, q);
+              const v4f e = mv_col0<kFL>(Tot, d, m, q);
+              if (m == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  Din[4 * q + i] = d[i];
+                  slot_put(myslot + kFAgg + 4 * q + i, ep, e[i]);
+                }
               }
-              __syncthreads();
-              src = 1 - src;
-            }
-            if (tid < D) Din[tid] = Vec[src * D + tid];
-            __syncthreads();
-            if (tid < D) {
-              float v_ = Tot[D * D + tid];
-#pragma unroll
-              for (int l = 0; l < D; ++l) v_ = fmaf(Tot[tid * D + l], Din[l], v_);
-              slot_put(myslot + kFAgg + tid, ep, v_);
             }
             break;
           }
@@ -1156,29 +1200,18 @@ __global__ void __launch_bounds__(PNR_BLOCK, 2) dense_full_mfma_kernel(DenseLoop
       }
       __syncthreads();
 
-      // ---- increments entering the parts: Pin[p+1] = M_p Pin[p] + v_p ----
-      if (tid < D) Pin[tid] = Din[tid];
-      __syncthreads();
-      for (int p = 0; p < kFParts - 1; ++p) {
-        if (tid < D) {
-          const float* Mp = Pagg + p * kFAgg;
-          float v_ = Mp[D * D + tid];
-#pragma unroll
-          for (int l = 0; l < D; ++l) v_ = fmaf(Mp[tid * D + l], Pin[p * D + l], v_);
-          Pin[(p + 1) * D + tid] = v_;
-        }
-        __syncthreads();
-      }
-
       // ---- fix-up on MFMA: d <- J_t d + r_t with d in column 0; s <- s + d ----
       {
+        // the increments entering this wave's parts, from the one entering the tile:
+        // Pin[2w] = (W_{w-1} .. W_0)(Din) through the tree's products, Pin[2w+1] = part_2w(Pin[2w])
         const int pa = 2 * wid, pb = 2 * wid + 1;
         v4f xa, xb;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          xa[i] = m == 0 ? Pin[pa * D + 4 * q + i] : 0.f;
-          xb[i] = m == 0 ? Pin[pb * D + 4 * q + i] : 0.f;
-        }
+        for (int i = 0; i < 4; ++i) xa[i] = m == 0 ? Din[4 * q + i] : 0.f;
+        if (wid == 1) xa = mv_col0<kFL>(Wm, xa, m, q);
+        if (wid >= 2) xa = mv_col0<kFL>(Xm, xa, m, q);
+        if (wid == 3) xa = mv_col0<kFL>(Wm + 2 * kFMat, xa, m, q);
+        xb = mv_col0<kFL>(Pagg + pa * kFMat, xa, m, q);
 #pragma unroll 4
         for (int st = 0; st < kFPartLen; ++st) {
           const int sa = pa * kFPartLen + st, sb = pb * kFPartLen + st;
