@@ -8,6 +8,9 @@
 // Both operands are K-contiguous.  bf16 inputs run on MFMA (v_mfma_f32_32x32x16_bf16,
 // fp32 accumulate), fp32 inputs on fp32 MFMA; fp64 inputs use an LDS-tiled VALU kernel
 // (the fp64 projections are tiny).
+#include <atomic>
+#include <cmath>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -128,41 +131,53 @@ __global__ void __launch_bounds__(256, 4) gemm_bf16_mfma(GemmArgs g) {
 
 // ---------------------------------------------------------------------------------
 // bf16 MFMA GEMM with direct global -> LDS loads (global_load_lds_dwordx4), for K a
-// multiple of 32.  Waves and MFMA tiles as in gemm_bf16_mfma (each wave 64 x 64 of C), in
-// WM x 2 waves: block tile (64 WM) x 128 -- 256 x 128 for long M, which cuts the operand
-// bytes each CU pulls from L2 per MFMA by a quarter against 128 x 128.
+// multiple of 32.  The block holds WM x WN waves; each wave computes (32 TM) x (32 TN) of
+// C as TM x TN tiles of v_mfma_f32_32x32x16_bf16, so the block tile is (32 TM WM) x
+// (32 TN WN).
+//  * Long M and N (every projection and gradient product of the long workloads): 256 x 384
+//    from 8 waves of 128 x 96, four LDS stages (4 x 40 KB, the whole LDS).  Per K step a
+//    wave reads 4 + 3 fragments for 12 MFMAs, and the block pulls 640 operand rows for
+//    256 x 384 outputs -- a fifth fewer L2 -> LDS bytes per flop than 256 x 256.
+//  * Long M only: 256 x 128 (8 waves of 64 x 64, three stages); otherwise 128 x 128.
 //  * Each lane's 16 B go straight from global memory into LDS (lane l of a load writes
 //    bytes 16l..16l+15 of a 1 KB run), so no registers stage the tiles and no LDS store
 //    instructions are issued.
-//  * NS LDS stages (three, or four for the 256 x 256 tile): loads run NS-1 K steps ahead
-//    of the MFMAs, with one barrier per K step.  Each stage is its own LDS array, so that
-//    the compiler can tell the stage being read from the stages being loaded and waits
-//    only for the loads it needs (with one array indexed by stage it waits for all).
-//    Measured on the long-LSTM projection: 256 x 256 with four stages 1061 TF/s, three
-//    1037, two (two blocks per CU) 841; 256 x 128 with three 912.
+//  * NS LDS stages: loads run NS-1 K steps ahead of the MFMAs, with one barrier per K
+//    step.  Each stage is its own LDS array, so that the compiler can tell the stage being
+//    read from the stages being loaded and waits only for the loads it needs (with one
+//    array indexed by stage it waits for all).
 //  * A tile row is 64 B (32 bf16) with its four 16-B chunks permuted by row bits 2-3.
 //    ds_read_b128 serves 16 lanes per cycle from 64 four-byte banks (measured with the
 //    bank-conflict counter); a fragment read's 16 lanes take 16 consecutive rows at one
 //    chunk, and the permutation puts them on 16 distinct 16-B bank groups.
 //  * Rows past M (or N) read the last row instead (their results are not stored), so
 //    every load is issued unconditionally and the wait counts stay exact.
+//  * Block order: groups of GM row tiles sweep the column tiles together (as in
+//    gemm_bf16_mfma); with 256 x 384 tiles and one block per CU, groups of 64 measured best.
+//  * Measured on the 131072-step LSTM's projection (M 16384, N 131072, K 4096): 256 x 384
+//    in groups of 64 15.0-15.3 ms, against 16.4-16.6 ms for 256 x 256 with 16 waves of
+//    64 x 64 in groups of 32; the gradient products (K 131072, and M 131072) gain 6-11%.
 constexpr int GD_K = 32, GD_ROW = GD_K * 2;   // bytes of one tile row
 
 __device__ __forceinline__ int gd_swz(int row) { return (row >> 2) & 3; }
 
-template <int WM, int WN>
+template <int WM, int WN, int TM, int TN>
 struct GdCfg {
-  static constexpr int BM = 64 * WM, BN = 64 * WN, THREADS = 64 * WM * WN;
-  static constexpr int A_RUNS = BM / 16 / (WM * WN);   // 1 KB runs per wave and stage
-  static constexpr int B_RUNS = BN / 16 / (WM * WN);
-  static constexpr int LOADS = A_RUNS + B_RUNS;        // vmcnt of one stage
+  static constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN, NW = WM * WN, THREADS = 64 * NW;
+  static constexpr int A_RUNS = BM / 16 / NW;   // 1 KB runs per wave and stage
+  static constexpr int B_RUNS = BN / 16 / NW;
+  static constexpr int LOADS = A_RUNS + B_RUNS;   // vmcnt of one stage
+  // the register budget: four waves per SIMD for 64 x 64 wave tiles, two for larger ones
+  static constexpr int MIN_BLOCKS = (TM * TN > 4) ? 1 : 4;
+  static_assert(A_RUNS * 16 * NW == BM && B_RUNS * 16 * NW == BN, "tile rows must split into whole runs per wave");
 };
 
-template <int WM, int WN>
+template <int WM, int WN, int TM, int TN>
 struct GdLoad {
-  const __bf16* pa[GdCfg<WM, WN>::A_RUNS];   // this lane's source rows
-  const __bf16* pb[GdCfg<WM, WN>::B_RUNS];
-  int ka[GdCfg<WM, WN>::A_RUNS], kb[GdCfg<WM, WN>::B_RUNS];   // element offset of its 16-B chunk
+  using C = GdCfg<WM, WN, TM, TN>;
+  const __bf16* pa[C::A_RUNS];   // this lane's source rows
+  const __bf16* pb[C::B_RUNS];
+  int ka[C::A_RUNS], kb[C::B_RUNS];   // element offset of its 16-B chunk
 };
 
 // vmcnt <= n (expcnt and lgkmcnt left at their maxima), then the barrier.  n must fold
@@ -178,50 +193,64 @@ __device__ __forceinline__ void gd_wait_barrier(int n) {
     case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
     case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
     case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
+    case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
+    case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
     default: __builtin_amdgcn_s_waitcnt(0x0F70); break;   // waiting for all is always safe
   }
   asm volatile("s_barrier" ::: "memory");
 }
 
-template <int WM, int WN>
-__device__ __forceinline__ void gd_issue(const GdLoad<WM, WN>& L, int k0, char* sa, char* sb, int wid) {
-  using C = GdCfg<WM, WN>;
-#pragma unroll
-  for (int h = 0; h < C::A_RUNS; ++h)
-    __builtin_amdgcn_global_load_lds(L.pa[h] + k0 + L.ka[h], sa + (C::A_RUNS * wid + h) * 1024, 16, 0, 0);
-#pragma unroll
-  for (int h = 0; h < C::B_RUNS; ++h)
-    __builtin_amdgcn_global_load_lds(L.pb[h] + k0 + L.kb[h], sb + (C::B_RUNS * wid + h) * 1024, 16, 0, 0);
+// The builtins sit in plain (non-template) functions: the host pass of a kernel template
+// rejects a target builtin met while instantiating it, which drops the kernel silently.
+__device__ __forceinline__ int gd_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ void gd_load(const __bf16* src, char* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ floatx16_t gd_mfma(u32x4_t a, u32x4_t b, floatx16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
 }
 
+template <int WM, int WN, int TM, int TN>
+__device__ __forceinline__ void gd_issue(const GdLoad<WM, WN, TM, TN>& L, int k0, char* sa, char* sb, int wid) {
+  using C = GdCfg<WM, WN, TM, TN>;
+#pragma unroll
+  for (int h = 0; h < C::A_RUNS; ++h) gd_load(L.pa[h] + k0 + L.ka[h], sa + (C::A_RUNS * wid + h) * 1024);
+#pragma unroll
+  for (int h = 0; h < C::B_RUNS; ++h) gd_load(L.pb[h] + k0 + L.kb[h], sb + (C::B_RUNS * wid + h) * 1024);
+}
+
+template <int TM, int TN>
 __device__ __forceinline__ void gd_compute(const char* sa, const char* sb, int wm, int wn, int lane,
-                                           floatx16_t (&acc)[2][2]) {
+                                           floatx16_t (&acc)[TM][TN]) {
 #pragma unroll
   for (int ks = 0; ks < GD_K / 16; ++ks) {
     const int kc = ks * 2 + (lane >> 5);
-    bf16x8_t fa[2], fb[2];
+    u32x4_t fa[TM], fb[TN];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-      const int r = wm * 64 + mi * 32 + (lane & 31);
-      fa[mi] = *reinterpret_cast<const bf16x8_t*>(sa + r * GD_ROW + 16 * (kc ^ gd_swz(r)));
+    for (int mi = 0; mi < TM; ++mi) {
+      const int r = wm * 32 * TM + mi * 32 + (lane & 31);
+      fa[mi] = *reinterpret_cast<const u32x4_t*>(sa + r * GD_ROW + 16 * (kc ^ gd_swz(r)));
     }
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int r = wn * 64 + ni * 32 + (lane & 31);
-      fb[ni] = *reinterpret_cast<const bf16x8_t*>(sb + r * GD_ROW + 16 * (kc ^ gd_swz(r)));
+    for (int ni = 0; ni < TN; ++ni) {
+      const int r = wn * 32 * TN + ni * 32 + (lane & 31);
+      fb[ni] = *reinterpret_cast<const u32x4_t*>(sb + r * GD_ROW + 16 * (kc ^ gd_swz(r)));
     }
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+      for (int ni = 0; ni < TN; ++ni) acc[mi][ni] = gd_mfma(fa[mi], fb[ni], acc[mi][ni]);
   }
 }
 
-// Four waves per SIMD: registers held to 128.
-template <int WM, int WN, int NS>
-__global__ void __launch_bounds__((GdCfg<WM, WN>::THREADS), 4) gemm_bf16_dma(GemmArgs g) {
-  using Cf = GdCfg<WM, WN>;
+template <int WM, int WN, int TM, int TN, int NS, int GM>
+__global__ void __launch_bounds__((GdCfg<WM, WN, TM, TN>::THREADS), (GdCfg<WM, WN, TM, TN>::MIN_BLOCKS))
+    gemm_bf16_dma(GemmArgs g) {
+  using Cf = GdCfg<WM, WN, TM, TN>;
   constexpr int SA = Cf::BM * GD_ROW, SB = Cf::BN * GD_ROW;
   static_assert(NS >= 3 && NS <= 4, "three or four stages");
   __shared__ __align__(1024) char sa0[SA], sa1[SA], sa2[SA], sa3[NS > 3 ? SA : 16];
@@ -230,20 +259,22 @@ __global__ void __launch_bounds__((GdCfg<WM, WN>::THREADS), 4) gemm_bf16_dma(Gem
   // loops over stages are unrolled
   char* const stA[4] = {sa0, sa1, sa2, sa3};
   char* const stB[4] = {sb0, sb1, sb2, sb3};
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  // the wave index is made uniform so that each load's LDS address (taken from M0) is
+  // computed once on the scalar unit, not read back from a vector register per load
+  const int tid = threadIdx.x, lane = tid & 63, wid = gd_uniform(tid >> 6);
   const int wm = wid / WN, wn = wid % WN;
   const int z = blockIdx.z;
   const int gx = (int)gridDim.x, gy = (int)gridDim.y;
   const int lin = (int)blockIdx.y * gx + (int)blockIdx.x;
-  const int grp = lin / (GB_GM * gx), loc = lin - grp * GB_GM * gx;
-  const int gm = min(GB_GM, gy - grp * GB_GM);
-  const int i0 = (grp * GB_GM + loc % gm) * Cf::BM, j0 = (loc / gm) * Cf::BN;
+  const int grp = lin / (GM * gx), loc = lin - grp * GM * gx;
+  const int gm = min(GM, gy - grp * GM);
+  const int i0 = (grp * GM + loc % gm) * Cf::BM, j0 = (loc / gm) * Cf::BN;
   const __bf16* A = reinterpret_cast<const __bf16*>(g.A) + (size_t)z * g.sA;
   const __bf16* Bm = reinterpret_cast<const __bf16*>(g.Bm) + (size_t)z * g.sB;
   float* C = reinterpret_cast<float*>(g.C) + (size_t)z * g.sC;
 
   // lane l of a 1 KB run holds tile row 16 run + l/4, physical chunk l%4
-  GdLoad<WM, WN> L;
+  GdLoad<WM, WN, TM, TN> L;
 #pragma unroll
   for (int h = 0; h < Cf::A_RUNS; ++h) {
     const int row = (Cf::A_RUNS * wid + h) * 16 + (lane >> 2);
@@ -257,11 +288,11 @@ __global__ void __launch_bounds__((GdCfg<WM, WN>::THREADS), 4) gemm_bf16_dma(Gem
     L.pb[h] = Bm + (size_t)min(j0 + row, g.N - 1) * g.ldb;
   }
 
-  floatx16_t acc[2][2];
+  floatx16_t acc[TM][TN];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < TM; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < TN; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
@@ -273,17 +304,18 @@ __global__ void __launch_bounds__((GdCfg<WM, WN>::THREADS), 4) gemm_bf16_dma(Gem
   // inside the loop body, so that the loop head is reached with one order of pending
   // loads, and every stage index is a constant.
   constexpr int W = Cf::LOADS;
-  static_assert(W * (NS - 2) <= 8, "wait count beyond the table");
+  static_assert(W * (NS - 2) <= 12, "wait count beyond the table");
   const int nk = g.K / GD_K, kmax = (nk - 1) * GD_K;
 #pragma unroll
-  for (int j = 0; j < NS - 1; ++j) gd_issue<WM, WN>(L, min(j * GD_K, kmax), stA[j], stB[j], wid);
+  for (int j = 0; j < NS - 1; ++j) gd_issue<WM, WN, TM, TN>(L, min(j * GD_K, kmax), stA[j], stB[j], wid);
   int t = 0;
   for (; t + NS <= nk; t += NS) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       gd_wait_barrier(W * (NS - 2));
-      gd_issue<WM, WN>(L, min((t + j + NS - 1) * GD_K, kmax), stA[(j + NS - 1) % NS], stB[(j + NS - 1) % NS], wid);
-      gd_compute(stA[j], stB[j], wm, wn, lane, acc);
+      gd_issue<WM, WN, TM, TN>(L, min((t + j + NS - 1) * GD_K, kmax), stA[(j + NS - 1) % NS],
+                               stB[(j + NS - 1) % NS], wid);
+      gd_compute<TM, TN>(stA[j], stB[j], wm, wn, lane, acc);
     }
   }
   // the last nk - t < NS steps: no more loads, so fewer stay in flight at each wait
@@ -291,24 +323,26 @@ __global__ void __launch_bounds__((GdCfg<WM, WN>::THREADS), 4) gemm_bf16_dma(Gem
   for (int j = 0; j < NS - 1; ++j) {
     if (t + j < nk) {
       gd_wait_barrier(W * (NS - 2 - j));
-      gd_compute(stA[j], stB[j], wm, wn, lane, acc);
+      gd_compute<TM, TN>(stA[j], stB[j], wm, wn, lane, acc);
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);   // no load into LDS outlives the block
 
+  // epilogue: lane holds column (lane & 31) and rows 8 q + 4 (lane >> 5) + e of each tile,
+  // so one store instruction writes two 128-B row segments
   const float* bias = reinterpret_cast<const float*>(g.bias);
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int j = j0 + wn * 64 + ni * 32 + (lane & 31);
+    for (int ni = 0; ni < TN; ++ni) {
+      const int j = j0 + wn * 32 * TN + ni * 32 + (lane & 31);
       if (j >= g.N) continue;
       const float bj = (bias && !g.bias_on_i) ? bias[j] : 0.f;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int i = i0 + wm * 64 + mi * 32 + 8 * q + 4 * (lane >> 5) + e;
+          const int i = i0 + wm * 32 * TM + mi * 32 + 8 * q + 4 * (lane >> 5) + e;
           if (i < g.M) {
             const float bi = (bias && g.bias_on_i) ? bias[i] : 0.f;
             __builtin_nontemporal_store(acc[mi][ni][4 * q + e] + bi + bj, &C[(size_t)i * g.ldc + j]);
@@ -463,21 +497,62 @@ __global__ void __launch_bounds__(256) gemm_generic(GemmArgs g) {
   }
 }
 
+// Compute units of the current device (cached per device; 0 if the query fails).
+static int num_cu() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDev) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+  if (dev < kMaxDev && n > 0) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// 256 x 384 or 256 x 256 tiles for a long product.  Both run one block per CU, so the
+// time goes as (waves of blocks) x (tile area) / (rate per area); the wider tile's rate
+// per area is higher by the factor measured on the long workloads' products: about 1.1
+// at K = 4096 and 1.2 at K >= 16384, where its fixed costs per tile are spread over more
+// K steps.  The wave count decides the rest: a product whose last wave of wide tiles is
+// mostly empty (the 8192-step chunks' projections: 1408 blocks, 5.5 waves) keeps the
+// 256 x 256 tiles.
+static bool wide_tiles_pay(const GemmArgs& g, int ncu) {
+  if (ncu <= 0) return true;
+  const double b3 = (double)((g.M + 255) / 256) * ((g.N + 383) / 384) * g.batch;
+  const double b2 = (double)((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
+  const double eff = g.K >= 16384 ? 1.2 : 1.1;
+  const double c3 = std::ceil(b3 / ncu) * 1.5 / eff, c2 = std::ceil(b2 / ncu);
+  return c3 < c2;
+}
+
 hipError_t launch_gemm(int in_dtype, int out_dtype, const GemmArgs& g, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
   if (in_dtype == PNR_BF16 && out_dtype == PNR_F32 && (g.K % 8) == 0 && (g.lda % 8) == 0 &&
       (g.ldb % 8) == 0 && (g.sA % 8) == 0 && (g.sB % 8) == 0) {
     const bool aligned = ((uintptr_t)g.A % 16) == 0 && ((uintptr_t)g.Bm % 16) == 0;
     if ((g.K % GD_K) == 0 && aligned) {
-      if (g.M >= 1024 && g.N >= 1024) {   // 256 x 256 tiles once both sides fill several
-        dim3 grid((g.N + 255) / 256, (g.M + 255) / 256, g.batch);
-        hipLaunchKernelGGL((gemm_bf16_dma<4, 4, 4>), grid, dim3(GdCfg<4, 4>::THREADS), 0, st, g);
+      if (g.M >= 1024 && g.N >= 1024) {   // 256 x 384 or 256 x 256 once both sides fill several
+        using C3 = GdCfg<2, 4, 4, 3>;
+        using C2 = GdCfg<4, 4, 2, 2>;
+        if (wide_tiles_pay(g, num_cu())) {
+          dim3 grid((g.N + C3::BN - 1) / C3::BN, (g.M + C3::BM - 1) / C3::BM, g.batch);
+          hipLaunchKernelGGL((gemm_bf16_dma<2, 4, 4, 3, 4, 64>), grid, dim3(C3::THREADS), 0, st, g);
+        } else {
+          dim3 grid((g.N + C2::BN - 1) / C2::BN, (g.M + C2::BM - 1) / C2::BM, g.batch);
+          hipLaunchKernelGGL((gemm_bf16_dma<4, 4, 2, 2, 4, GB_GM>), grid, dim3(C2::THREADS), 0, st, g);
+        }
       } else if (g.M >= 1024) {
-        dim3 grid((g.N + 127) / 128, (g.M + 255) / 256, g.batch);
-        hipLaunchKernelGGL((gemm_bf16_dma<4, 2, 3>), grid, dim3(GdCfg<4, 2>::THREADS), 0, st, g);
+        using Cf = GdCfg<4, 2, 2, 2>;
+        dim3 grid((g.N + Cf::BN - 1) / Cf::BN, (g.M + Cf::BM - 1) / Cf::BM, g.batch);
+        hipLaunchKernelGGL((gemm_bf16_dma<4, 2, 2, 2, 3, GB_GM>), grid, dim3(Cf::THREADS), 0, st, g);
       } else {
-        dim3 grid((g.N + 127) / 128, (g.M + 127) / 128, g.batch);
-        hipLaunchKernelGGL((gemm_bf16_dma<2, 2, 3>), grid, dim3(GdCfg<2, 2>::THREADS), 0, st, g);
+        using Cf = GdCfg<2, 2, 2, 2>;
+        dim3 grid((g.N + Cf::BN - 1) / Cf::BN, (g.M + Cf::BM - 1) / Cf::BM, g.batch);
+        hipLaunchKernelGGL((gemm_bf16_dma<2, 2, 2, 2, 3, GB_GM>), grid, dim3(Cf::THREADS), 0, st, g);
       }
       return hipGetLastError();
     }
