@@ -247,7 +247,7 @@ __device__ __forceinline__ void gd_compute(const char* sa, const char* sb, int w
   }
 }
 
-template <int WM, int WN, int TM, int TN, int NS, int GM>
+template <int WM, int WN, int TM, int TN, int NS, int GM, bool STAGED>
 __global__ void __launch_bounds__((GdCfg<WM, WN, TM, TN>::THREADS), (GdCfg<WM, WN, TM, TN>::MIN_BLOCKS))
     gemm_bf16_dma(GemmArgs g) {
   using Cf = GdCfg<WM, WN, TM, TN>;
@@ -328,9 +328,57 @@ __global__ void __launch_bounds__((GdCfg<WM, WN, TM, TN>::THREADS), (GdCfg<WM, W
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);   // no load into LDS outlives the block
 
+  const float* bias = reinterpret_cast<const float*>(g.bias);
+  if constexpr (STAGED) {
+    // Epilogue through LDS, 16 tile rows per round: the waves holding those rows write
+    // them into one B stage array (exactly 16 rows of BN floats), then every thread moves
+    // 16 B of a row to C, so each row leaves as one contiguous run of 4 BN bytes.  Round r
+    // uses stage r % NS: the barriers of the rounds in between order its reads before the
+    // writes of round r + NS.
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    char* const stg[4] = {sb0, sb1, sb2, sb3};
+    const bool vec_ok = (g.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(C) & 15) == 0;
+    __syncthreads();   // every wave is done reading the stages
+#pragma unroll
+    for (int r = 0; r < Cf::BM / 16; ++r) {
+      float* Ls = reinterpret_cast<float*>(stg[r % NS]);
+      // tile rows 16 r .. 16 r + 15: wave row r / (2 TM), MFMA tile (r % (2 TM)) / 2, and
+      // lane groups q = 2 (r & 1) and 2 (r & 1) + 1 of it
+      if (wm == r / (2 * TM)) {
+        const int mi = (r % (2 * TM)) / 2;
+#pragma unroll
+        for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+          for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              Ls[(8 * qq + 4 * (lane >> 5) + e) * Cf::BN + wn * 32 * TN + ni * 32 + (lane & 31)] =
+                  acc[mi][ni][4 * (2 * (r & 1) + qq) + e];
+      }
+      __syncthreads();
+      constexpr int NV = 16 * Cf::BN / 4;
+#pragma unroll
+      for (int v = tid; v < NV; v += Cf::THREADS) {
+        const int rr = v / (Cf::BN / 4), c4 = v - rr * (Cf::BN / 4);
+        const int i = i0 + 16 * r + rr, j = j0 + 4 * c4;
+        if (i >= g.M) continue;
+        f4 x = *reinterpret_cast<const f4*>(&Ls[rr * Cf::BN + 4 * c4]);
+        const float bi = (bias && g.bias_on_i) ? bias[i] : 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] += bi + ((bias && !g.bias_on_i && j + e < g.N) ? bias[j + e] : 0.f);
+        if (j + 3 < g.N && vec_ok) {
+          __builtin_nontemporal_store(x, reinterpret_cast<f4*>(&C[(size_t)i * g.ldc + j]));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j + e < g.N) C[(size_t)i * g.ldc + j + e] = x[e];
+        }
+      }
+    }
+    return;
+  }
   // epilogue: lane holds column (lane & 31) and rows 8 q + 4 (lane >> 5) + e of each tile,
   // so one store instruction writes two 128-B row segments
-  const float* bias = reinterpret_cast<const float*>(g.bias);
 #pragma unroll
   for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
@@ -540,19 +588,19 @@ hipError_t launch_gemm(int in_dtype, int out_dtype, const GemmArgs& g, hipStream
         using C2 = GdCfg<4, 4, 2, 2>;
         if (wide_tiles_pay(g, num_cu())) {
           dim3 grid((g.N + C3::BN - 1) / C3::BN, (g.M + C3::BM - 1) / C3::BM, g.batch);
-          hipLaunchKernelGGL((gemm_bf16_dma<2, 4, 4, 3, 4, 64>), grid, dim3(C3::THREADS), 0, st, g);
+          hipLaunchKernelGGL((gemm_bf16_dma<2, 4, 4, 3, 4, 64, true>), grid, dim3(C3::THREADS), 0, st, g);
         } else {
           dim3 grid((g.N + C2::BN - 1) / C2::BN, (g.M + C2::BM - 1) / C2::BM, g.batch);
-          hipLaunchKernelGGL((gemm_bf16_dma<4, 4, 2, 2, 4, GB_GM>), grid, dim3(C2::THREADS), 0, st, g);
+          hipLaunchKernelGGL((gemm_bf16_dma<4, 4, 2, 2, 4, GB_GM, false>), grid, dim3(C2::THREADS), 0, st, g);
         }
       } else if (g.M >= 1024) {
         using Cf = GdCfg<4, 2, 2, 2>;
         dim3 grid((g.N + Cf::BN - 1) / Cf::BN, (g.M + Cf::BM - 1) / Cf::BM, g.batch);
-        hipLaunchKernelGGL((gemm_bf16_dma<4, 2, 2, 2, 3, GB_GM>), grid, dim3(Cf::THREADS), 0, st, g);
+        hipLaunchKernelGGL((gemm_bf16_dma<4, 2, 2, 2, 3, GB_GM, false>), grid, dim3(Cf::THREADS), 0, st, g);
       } else {
         using Cf = GdCfg<2, 2, 2, 2>;
         dim3 grid((g.N + Cf::BN - 1) / Cf::BN, (g.M + Cf::BM - 1) / Cf::BM, g.batch);
-        hipLaunchKernelGGL((gemm_bf16_dma<2, 2, 2, 2, 3, GB_GM>), grid, dim3(Cf::THREADS), 0, st, g);
+        hipLaunchKernelGGL((gemm_bf16_dma<2, 2, 2, 2, 3, GB_GM, false>), grid, dim3(Cf::THREADS), 0, st, g);
       }
       return hipGetLastError();
     }
