@@ -152,6 +152,8 @@ __global__ void __launch_bounds__(256, 4) gemm_bf16_mfma(GemmArgs g) {
 //    chunk, and the permutation puts them on 16 distinct 16-B bank groups.
 //  * Rows past M (or N) read the last row instead (their results are not stored), so
 //    every load is issued unconditionally and the wait counts stay exact.
+//  * The 256 x 384 and 256 x 256 kernels write C through LDS (16-row rounds through the
+//    free stage arrays), so that each row of the tile leaves as one contiguous run.
 //  * Block order: groups of GM row tiles sweep the column tiles together (as in
 //    gemm_bf16_mfma); with 256 x 384 tiles and one block per CU, groups of 64 measured best.
 //  * Measured on the 131072-step LSTM's projection (M 16384, N 131072, K 4096): 256 x 384
@@ -591,7 +593,7 @@ hipError_t launch_gemm(int in_dtype, int out_dtype, const GemmArgs& g, hipStream
           hipLaunchKernelGGL((gemm_bf16_dma<2, 4, 4, 3, 4, 64, true>), grid, dim3(C3::THREADS), 0, st, g);
         } else {
           dim3 grid((g.N + C2::BN - 1) / C2::BN, (g.M + C2::BM - 1) / C2::BM, g.batch);
-          hipLaunchKernelGGL((gemm_bf16_dma<4, 4, 2, 2, 4, GB_GM, false>), grid, dim3(C2::THREADS), 0, st, g);
+          hipLaunchKernelGGL((gemm_bf16_dma<4, 4, 2, 2, 4, GB_GM, true>), grid, dim3(C2::THREADS), 0, st, g);
         }
       } else if (g.M >= 1024) {
         using Cf = GdCfg<4, 2, 2, 2>;
