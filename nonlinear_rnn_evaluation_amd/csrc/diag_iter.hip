@@ -1183,7 +1183,16 @@ __device__ __forceinline__ typename DeltaOf<typename DiagCell<CELL>::E>::T adjoi
   for (int k = 0; k < K; ++k) {
     load_n(a.hT + off[k], tb, T, vec, N, hv[k]);
     load_n(a.gT + off[k], tb, T, vec, N, gv[k]);
-    p0[k] = tb == 0 ? (a.h0 ? a.h0[(size_t)b * S + k * D + d] : 0.f) : (tb <= T ? a.hT[off[k] + tb - 1] : 0.f);
+  }
+  // the state before this thread's first step is the last of the next lane's run (the
+  // runs go backwards in time with the thread index); only the wave's last lane, whose
+  // neighbour is in the next wave (or in the tile before), reads it from memory
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const float nb = shfl_down_f(hv[k][N - 1], 1);
+    p0[k] = lane != 63 ? nb
+                       : (tb == 0 ? (a.h0 ? a.h0[(size_t)b * S + k * D + d] : 0.f)
+                                  : (tb <= T ? a.hT[off[k] + tb - 1] : 0.f));
   }
   // scan elements mu -> J^T mu + J^T g, latest step first
   E e[N];
