@@ -1160,9 +1160,44 @@ __device__ __forceinline__ void store_n_bf16(__bf16* __restrict__ row, int tb, i
   }
 }
 
-template <int CELL, int N, bool BF16OUT>
+// Staged backward walk (T a multiple of the tile): the next tile's planes (gates, states,
+// loss gradients) go straight from memory into LDS (global_load_lds_dwordx4) while the
+// current tile is computed.  Thread t takes steps (PNR_BLOCK - 1 - t) N .. of its tile, so
+// wave w's threads take one 1-KB run of each plane, run PNR_WAVES - 1 - w; the wave loads
+// exactly that run (lane l writes bytes 16l..16l+15 of it) and reads back only what its
+// own loads brought in, so its own vmcnt wait covers every read and no barrier is needed.
+template <int CELL, int N>
+struct BwdStage {
+  static constexpr int PLANES = DiagCell<CELL>::G + 2 * DiagCell<CELL>::SP;
+  float pl[PLANES][PNR_BLOCK * N];
+};
+
+template <int CELL, int N>
+__device__ __forceinline__ void bwd_stage_issue(const BwdArgs& a, int row, int seg, BwdStage<CELL, N>& st) {
+  using C = DiagCell<CELL>;
+  constexpr int NG = C::G, K = C::SP, TILE = PNR_BLOCK * N;
+  static_assert(N == 4, "one 16-byte load per lane and plane");
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int D = a.D, T = a.T, S = K * D;
+  const int b = row / D, d = row - b * D;
+  const int r0 = (PNR_WAVES - 1 - wid) * 64 * N;   // the wave's run in each plane
+  const size_t tb = (size_t)seg * TILE + r0 + lane * N;
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) lds_load16(a.gx + ((size_t)(b * NG + gg) * D + d) * T + tb, &st.pl[gg][r0]);
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const size_t off = ((size_t)b * S + (size_t)k * D + d) * T;
+    lds_load16(a.hT + off + tb, &st.pl[NG + k][r0]);
+    lds_load16(a.gT + off + tb, &st.pl[NG + K + k][r0]);
+  }
+}
+
+// STAGED: the tile's inputs are read from `st` (this wave's own loads, landed), and the
+// loads of the next tile (nrow, nseg) are issued once they are in registers.
+template <int CELL, int N, bool BF16OUT, bool STAGED>
 __device__ __forceinline__ typename DeltaOf<typename DiagCell<CELL>::E>::T adjoint_tile(
-    const BwdArgs& a, BwdShared<CELL>& sh, int b, int d, int seg, float* acc) {
+    const BwdArgs& a, BwdShared<CELL>& sh, int b, int d, int seg, float* acc, BwdStage<CELL, N>* st, int nrow,
+    int nseg, bool more) {
   using C = DiagCell<CELL>;
   using E = typename C::E;
   using Dl = typename DeltaOf<E>::T;
@@ -1177,12 +1212,30 @@ __device__ __forceinline__ typename DeltaOf<typename DiagCell<CELL>::E>::T adjoi
 #pragma unroll
   for (int k = 0; k < K; ++k) off[k] = ((size_t)b * S + k * D + d) * T;
   float gx[NG][N], hv[K][N], gv[K][N], p0[K];
+  if constexpr (STAGED) {
+    const int i0 = (PNR_BLOCK - 1 - tid) * N;
+    auto rd = [&](const float* p, float* o) {
+      const float4 x = *reinterpret_cast<const float4*>(p + i0);
+      o[0] = x.x; o[1] = x.y; o[2] = x.z; o[3] = x.w;
+    };
 #pragma unroll
-  for (int gg = 0; gg < NG; ++gg) load_n(a.gx + ((size_t)(b * NG + gg) * D + d) * T, tb, T, vec, N, gx[gg]);
+    for (int gg = 0; gg < NG; ++gg) rd(st->pl[gg], gx[gg]);
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    load_n(a.hT + off[k], tb, T, vec, N, hv[k]);
-    load_n(a.gT + off[k], tb, T, vec, N, gv[k]);
+    for (int k = 0; k < K; ++k) {
+      rd(st->pl[NG + k], hv[k]);
+      rd(st->pl[NG + K + k], gv[k]);
+    }
+    // the reads have returned before the next tile's loads may overwrite the stage
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    if (more) bwd_stage_issue<CELL, N>(a, nrow, nseg, *st);
+  } else {
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) load_n(a.gx + ((size_t)(b * NG + gg) * D + d) * T, tb, T, vec, N, gx[gg]);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      load_n(a.hT + off[k], tb, T, vec, N, hv[k]);
+      load_n(a.gT + off[k], tb, T, vec, N, gv[k]);
+    }
   }
   // the state before this thread's first step is the last of the next lane's run (the
   // runs go backwards in time with the thread index); only the wave's last lane, whose
@@ -1280,13 +1333,18 @@ __device__ __forceinline__ typename DeltaOf<typename DiagCell<CELL>::E>::T adjoi
   return mu;
 }
 
-template <int CELL, int N, bool BF16OUT>
+template <int CELL, int N, bool BF16OUT, bool STAGED>
 __global__ void __launch_bounds__(PNR_BLOCK) adjoint_diag_kernel(BwdArgs a) {
   using C = DiagCell<CELL>;
   using Dl = typename DeltaOf<typename C::E>::T;
   constexpr int NA = 3 * C::G;
   __shared__ BwdShared<CELL> sh;
+  // one staged tile (a one-float token when unstaged)
+  __shared__ __align__(16) float stg_raw[STAGED ? BwdStage<CELL, N>::PLANES * PNR_BLOCK * N : 1];
+  BwdStage<CELL, N>* stg = reinterpret_cast<BwdStage<CELL, N>*>(stg_raw);
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int tpr = a.tiles_per_row;
+  if (STAGED && (int)blockIdx.x < a.n_rows) bwd_stage_issue<CELL, N>(a, blockIdx.x, tpr - 1, *stg);
   for (int row = blockIdx.x; row < a.n_rows; row += gridDim.x) {
     const int b = row / a.D, d = row - b * a.D;
     float acc[NA];
@@ -1295,7 +1353,11 @@ __global__ void __launch_bounds__(PNR_BLOCK) adjoint_diag_kernel(BwdArgs a) {
     if (tid == 0) sh.carry = DeltaOf<typename C::E>::zero();
     __syncthreads();
     Dl mu = DeltaOf<typename C::E>::zero();
-    for (int seg = a.tiles_per_row - 1; seg >= 0; --seg) mu = adjoint_tile<CELL, N, BF16OUT>(a, sh, b, d, seg, acc);
+    for (int seg = tpr - 1; seg >= 0; --seg) {
+      const int nrow = seg > 0 ? row : row + (int)gridDim.x, nseg = seg > 0 ? seg - 1 : tpr - 1;
+      if (STAGED) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's staged loads have landed
+      mu = adjoint_tile<CELL, N, BF16OUT, STAGED>(a, sh, b, d, seg, acc, stg, nrow, nseg, nrow < a.n_rows);
+    }
     if (tid == PNR_BLOCK - 1 && a.dh0) {   // this thread's run starts at step 0: mu = dL/dh0
       const int S = C::SP * a.D;
       if constexpr (CELL == PNR_CELL_GRU_DIAG) {
@@ -1318,6 +1380,7 @@ __global__ void __launch_bounds__(PNR_BLOCK) adjoint_diag_kernel(BwdArgs a) {
     }
     __syncthreads();
   }
+  if (STAGED) __builtin_amdgcn_s_waitcnt(0x0F70);   // no staged load outlives the block
 }
 
 constexpr int kAdjN = 4;   // steps per thread
@@ -1325,12 +1388,18 @@ constexpr int kAdjN = 4;   // steps per thread
 int adjoint_items_per_thread() { return kAdjN; }
 
 hipError_t launch_adjoint_diag(int cell, const BwdArgs& a, int num_cu, hipStream_t st) {
+  // the staged walk loads whole tiles, so T must be a multiple of the tile; it pays for the
+  // LSTM (4.79 -> 4.57 ms on the 131072-step backward pass) but not for the GRU, whose
+  // lighter tiles run at higher occupancy unstaged (0.344 ms against 0.373)
+  const bool staged = cell == PNR_CELL_LSTM_DIAG && a.T % (PNR_BLOCK * kAdjN) == 0;
   const void* fn =
       cell == PNR_CELL_GRU_DIAG
-          ? (a.dgx_bf16 ? (const void*)adjoint_diag_kernel<PNR_CELL_GRU_DIAG, kAdjN, true>
-                        : (const void*)adjoint_diag_kernel<PNR_CELL_GRU_DIAG, kAdjN, false>)
-          : (a.dgx_bf16 ? (const void*)adjoint_diag_kernel<PNR_CELL_LSTM_DIAG, kAdjN, true>
-                        : (const void*)adjoint_diag_kernel<PNR_CELL_LSTM_DIAG, kAdjN, false>);
+          ? (a.dgx_bf16 ? (const void*)adjoint_diag_kernel<PNR_CELL_GRU_DIAG, kAdjN, true, false>
+                        : (const void*)adjoint_diag_kernel<PNR_CELL_GRU_DIAG, kAdjN, false, false>)
+          : (a.dgx_bf16 ? (staged ? (const void*)adjoint_diag_kernel<PNR_CELL_LSTM_DIAG, kAdjN, true, true>
+                                  : (const void*)adjoint_diag_kernel<PNR_CELL_LSTM_DIAG, kAdjN, true, false>)
+                        : (staged ? (const void*)adjoint_diag_kernel<PNR_CELL_LSTM_DIAG, kAdjN, false, true>
+                                  : (const void*)adjoint_diag_kernel<PNR_CELL_LSTM_DIAG, kAdjN, false, false>));
   const int per_cu = cached_occupancy(fn, 0);
   if (per_cu < 1) return hipErrorInvalidConfiguration;
   long g = (long)per_cu * num_cu;
