@@ -157,8 +157,9 @@ __global__ void __launch_bounds__(256, 4) gemm_bf16_mfma(GemmArgs g) {
 //  * Block order: groups of GM row tiles sweep the column tiles together (as in
 //    gemm_bf16_mfma); with 256 x 384 tiles and one block per CU, groups of 64 measured best.
 //  * Measured on the 131072-step LSTM's projection (M 16384, N 131072, K 4096): 256 x 384
-//    in groups of 64 15.0-15.3 ms, against 16.4-16.6 ms for 256 x 256 with 16 waves of
-//    64 x 64 in groups of 32; the gradient products (K 131072, and M 131072) gain 6-11%.
+//    in groups of 64 15.0-15.3 ms with 4-byte stores and 14.2-14.3 ms with C through LDS,
+//    against 16.4-16.6 ms for 256 x 256 with 16 waves of 64 x 64 in groups of 32; the
+//    gradient products (K 131072, and M 131072) gain 6-11%.
 constexpr int GD_K = 32, GD_ROW = GD_K * 2;   // bytes of one tile row
 
 __device__ __forceinline__ int gd_swz(int row) { return (row >> 2) & 3; }
